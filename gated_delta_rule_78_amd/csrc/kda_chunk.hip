@@ -1,0 +1,516 @@
+// KDA chunkwise prefill for gfx950: fused chunk loop, segment summaries, segment scan.
+//
+// Mathematics (Kimi K3 reading notes, liuzhao09.github.io/papers/kimi-k3.html, section 2.2,
+// chunk equations; the pieces the page leaves unprinted are derived by unrolling the
+// recurrence inside one chunk). For a chunk of C = 64 rows with entry state S, per key
+// channel G_r = sum_{s<=r} log_alpha_s, Gamma_r = exp(G_r), gamma_C = Gamma_C:
+//   Q~ = Q*Gamma, K~ = K*Gamma, K^ = K/Gamma, K-bar = K*gamma_C/Gamma
+//   A_kk = Diag(beta) StrictTril(K~ K^T),   A_qk = Tril(Q~ K^T)   (incl. diagonal)
+//   V~ = (I + A_kk)^{-1} Diag(beta) (V - K~ S)          (= U - W S of the UT transform)
+//   O  = Q~ S + A_qk V~
+//   S' = Diag(gamma_C) S + K-bar^T V~
+// Section 2.5 (affine pair): a run of chunks maps S_in to S~ + M S_in. SUMMARY blocks run
+// the same loop on the augmented state [S~ | M], entry [0 | I], with zero values for the M
+// columns; a scan composes the pairs into exact entry states; FINISH blocks rerun each segment
+// from its exact entry state and write o.
+//
+// Work decomposition. Value columns are independent given the key-side quantities, so a
+// workgroup owns a lane (b,h), a segment of chunks and NW*16 state columns; each wave owns 16
+// of those columns (its slice of S lives in MFMA accumulators, fp32) and a 1/NW share of the
+// key channels for the per-chunk key-side preparation. Per chunk:
+//   A  (wave-local) load rows of q,k,log_alpha,v (prefetched one chunk ahead), cumulative
+//      log-decay across the 64 lanes (= rows), exponentials, operand tiles to LDS
+//   B  per-wave K~ S and S^T Q~^T on MFMA; Gram tiles on MFMA spread over the waves; wave 0
+//      inverts the four 16x16 diagonal blocks of (I + A_kk) in fp32
+//   D  per-wave: R = beta (V - K~ S), blocked forward substitution with the inverted diagonal
+//      blocks (V~), O^T += V~^T A_qk^T -> o, S <- gamma_C S + K-bar^T V~
+// Three workgroup barriers per chunk.
+#include "kda_device.h"
+#include "kda_internal.h"
+
+namespace kda {
+
+constexpr int kC = 64;  // chunk length
+
+template <class Op, int DK, int NW>
+struct __align__(16) ChunkSmem {
+    typedef typename Op::elem E;
+    static constexpr int P = 16 / (int)sizeof(E);  // 16-byte row padding, in elements
+    static constexpr int LDK = DK + P;             // stride of [*][DK] tiles
+    static constexpr int LDC = kC + P;             // stride of [*][C] tiles
+    static constexpr int LDT = 16 + P;             // stride of the inverted diagonal blocks
+    static constexpr int LDB = 16 * 16 + 4;        // fp32 diagonal blocks (block stride, floats)
+    E q[kC * LDK];          // Q~
+    E k[kC * LDK];          // K~
+    E kh[kC * LDK];         // K^
+    E kbT[DK * LDC];        // K-bar^T
+    E aqk[kC * LDC];        // A_qk (upper 16x16 blocks (0,1) and (2,3) kept at zero)
+    E l[kC * LDC];          // A_kk, off-diagonal 16x16 blocks
+    E td[4 * 16 * LDT];     // (I + L_II)^{-1}, I = 0..3
+    float ld[4 * LDB];      // diagonal blocks of A_kk, fp32
+    float gam[DK];          // gamma_C
+    float beta[kC];
+    E sT[NW][16 * LDK];     // per wave: S^T of its 16 columns (operand precision)
+    E x[NW][16 * LDC];      // per wave: V^T, then X^T and V~^T
+};
+
+template <typename T> struct VecCount { static constexpr int value = 1; };
+
+template <class Op, typename TIn, typename TOut, int DK, int NW>
+__global__ __launch_bounds__(NW * 64) void chunk_kernel(ChunkLaunch p) {
+    typedef ChunkSmem<Op, DK, NW> Sm;
+    typedef typename Op::elem E;
+    constexpr int LDK = Sm::LDK, LDC = Sm::LDC, LDT = Sm::LDT, LDB = Sm::LDB;
+    constexpr int CPW = DK / NW;                       // key channels prepared per wave
+    constexpr int EPV = 16 / (int)sizeof(TIn);         // input elements per 16-byte vector
+    constexpr int NVK = CPW / EPV;                     // vectors per row per key-side tensor
+    constexpr int NVV = 16 / EPV;                      // vectors per row of the wave's 16 v columns
+    constexpr int NM = DK / 16;                        // 16-row tiles of the state
+    static_assert(CPW % EPV == 0 && CPW % 4 == 0, "channel split");
+    __shared__ Sm sm;
+
+    const int tid = threadIdx.x;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keep it scalar
+    const int l = tid & 63;
+    const int l16 = l & 15;
+    const int lq = l >> 4;
+    const int W = NW * 16;
+    const int64_t DV = p.dv;
+
+    // ---- which lane / segment / column block this workgroup owns -------------------------
+    int64_t bid = blockIdx.x;
+    const int64_t nblk = gridDim.x;
+    if ((nblk & 7) == 0) bid = (bid & 7) * (nblk >> 3) + (bid >> 3);  // siblings share an XCD
+    const int ncb_fin = (int)(DV / W);
+    const int ncb_sum = (int)((DV + DK) / W);
+    const int64_t n_fin = p.lanes * p.fin_nseg * ncb_fin;
+    bool summary;
+    int cb, seg;
+    int64_t lane;
+    if (bid < n_fin) {
+        summary = false;
+        cb = (int)(bid % ncb_fin);
+        const int64_t r = bid / ncb_fin;
+        seg = p.fin_seg_lo + (int)(r % p.fin_nseg);
+        lane = r / p.fin_nseg;
+    } else {
+        summary = true;
+        const int64_t b2 = bid - n_fin;
+        cb = (int)(b2 % ncb_sum);
+        const int64_t r = b2 / ncb_sum;
+        seg = p.sum_seg_lo + (int)(r % p.sum_nseg);
+        lane = r / p.sum_nseg;
+    }
+    const int64_t T = p.T;
+    const int64_t nchunks = (T + kC - 1) / kC;
+    const int64_t c_begin = (int64_t)seg * p.chunks_per_seg;
+    const int64_t c_end = c_begin + p.chunks_per_seg < nchunks ? c_begin + p.chunks_per_seg : nchunks;
+
+    const int col0 = cb * W + 16 * w;                  // first column of this wave
+    const bool m_cols = summary && col0 >= DV;         // identity-started M columns
+    const bool has_v = !m_cols;
+    const int ch0 = w * CPW;                           // first key channel this wave prepares
+
+    const TIn* qg = (const TIn*)p.q + lane * T * DK;
+    const TIn* kg = (const TIn*)p.k + lane * T * DK;
+    const TIn* gg = (const TIn*)p.la + lane * T * DK;
+    const TIn* vg = (const TIn*)p.v + lane * T * DV;
+    const TIn* bg = (const TIn*)p.beta + lane * T;
+
+    // ---- entry state into accumulators and into the wave's S^T operand tile ---------------
+    f32x4 Sacc[NM];
+    {
+        const float* entry = nullptr;
+        if (!summary) {
+            if (seg > 0) entry = p.ws_entry + ((lane * p.nseg + seg) * DK) * DV;
+            else if (p.S0) entry = p.S0 + lane * DK * DV;
+        }
+#pragma unroll
+        for (int M = 0; M < NM; ++M) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int c = 16 * M + 4 * lq + r;
+                float s0 = 0.f;
+                if (!summary) {
+                    if (entry) s0 = entry[(int64_t)c * DV + col0 + l16];
+                } else if (m_cols) {
+                    s0 = (c == col0 - DV + l16) ? 1.f : 0.f;
+                }
+                Sacc[M][r] = s0;
+            }
+            store4(&sm.sT[w][l16 * LDK + 16 * M + 4 * lq], Sacc[M][0], Sacc[M][1], Sacc[M][2], Sacc[M][3]);
+        }
+    }
+    // A_qk blocks above the diagonal that the 32-wide K steps touch stay zero for the whole run.
+    for (int i = tid; i < 2 * 256; i += NW * 64) {
+        const int blk = i >> 8, e = i & 255;
+        sm.aqk[(32 * blk + (e >> 4)) * LDC + 32 * blk + 16 + (e & 15)] = Op::cvt(0.f);
+    }
+
+    // ---- prefetch registers: this lane = row l of the chunk -------------------------------
+    uint4 pq[NVK], pk[NVK], pg[NVK], pv[NVV];
+    float pb = 0.f;
+    auto load_chunk = [&](int64_t c) {
+        const int64_t row = c * kC + l;
+        const bool ok = row < T;
+#pragma unroll
+        for (int i = 0; i < NVK; ++i) {
+            const int64_t off = row * DK + ch0 + i * EPV;
+            pq[i] = ok ? *reinterpret_cast<const uint4*>(qg + off) : make_uint4(0, 0, 0, 0);
+            pk[i] = ok ? *reinterpret_cast<const uint4*>(kg + off) : make_uint4(0, 0, 0, 0);
+            pg[i] = ok ? *reinterpret_cast<const uint4*>(gg + off) : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < NVV; ++i)
+            pv[i] = (ok && has_v) ? *reinterpret_cast<const uint4*>(vg + row * DV + col0 + i * EPV)
+                                  : make_uint4(0, 0, 0, 0);
+        if (w == 0) pb = ok ? ld_f(bg + row) : 0.f;
+    };
+    if (c_begin < c_end) load_chunk(c_begin);
+
+    for (int64_t c = c_begin; c < c_end; ++c) {
+        // ================= phase A: key-side preparation (wave-local) =====================
+        {
+            // one 16-byte group of EPV key channels at a time keeps the live set small
+            uint4 cq_[NVK], ck_[NVK], cg_[NVK], cv_[NVV];
+#pragma unroll
+            for (int i = 0; i < NVK; ++i) { cq_[i] = pq[i]; ck_[i] = pk[i]; cg_[i] = pg[i]; }
+#pragma unroll
+            for (int i = 0; i < NVV; ++i) cv_[i] = pv[i];
+            const float bcur = pb;
+            if (c + 1 < c_end) load_chunk(c + 1);
+#pragma unroll
+            for (int i = 0; i < NVK; ++i) {
+                asm volatile("" ::: "memory");
+                float qf[EPV], kf[EPV], G[EPV];
+                unpack16(cq_[i], (const TIn*)nullptr, qf);
+                unpack16(ck_[i], (const TIn*)nullptr, kf);
+                unpack16(cg_[i], (const TIn*)nullptr, G);
+                // inclusive prefix sum over the 64 rows (lanes), in log2 units
+#pragma unroll
+                for (int j = 0; j < EPV; ++j) {
+                    float x = G[j] * kLog2e;
+#pragma unroll
+                    for (int off = 1; off < 64; off <<= 1) {
+                        const float y = __shfl_up(x, off, 64);
+                        if (l >= off) x += y;
+                    }
+                    G[j] = x;
+                }
+                E oq[EPV], ok_[EPV], okh[EPV];
+                const int chg = ch0 + i * EPV;
+#pragma unroll
+                for (int j = 0; j < EPV; ++j) {
+                    const float gC = __builtin_amdgcn_exp2f(__shfl(G[j], 63, 64));
+                    const float gam = __builtin_amdgcn_exp2f(G[j]);
+                    const float kh = kf[j] * __builtin_amdgcn_exp2f(-G[j]);
+                    oq[j] = Op::cvt(qf[j] * gam);
+                    ok_[j] = Op::cvt(kf[j] * gam);
+                    okh[j] = Op::cvt(kh);
+                    sm.kbT[(chg + j) * LDC + l] = Op::cvt(kh * gC);
+                    if (l == 0) sm.gam[chg + j] = gC;
+                }
+                constexpr int EV = 16 / (int)sizeof(E);
+#pragma unroll
+                for (int j = 0; j < EPV; j += EV) {
+                    uint4 a, b, d;
+                    __builtin_memcpy(&a, &oq[j], 16);
+                    __builtin_memcpy(&b, &ok_[j], 16);
+                    __builtin_memcpy(&d, &okh[j], 16);
+                    *reinterpret_cast<uint4*>(&sm.q[l * LDK + chg + j]) = a;
+                    *reinterpret_cast<uint4*>(&sm.k[l * LDK + chg + j]) = b;
+                    *reinterpret_cast<uint4*>(&sm.kh[l * LDK + chg + j]) = d;
+                }
+            }
+            if (w == 0) sm.beta[l] = bcur;
+#pragma unroll
+            for (int i = 0; i < NVV; ++i) {
+                float vf[EPV];
+                unpack16(cv_[i], (const TIn*)nullptr, vf);
+#pragma unroll
+                for (int n = 0; n < EPV; ++n) sm.x[w][(i * EPV + n) * LDC + l] = Op::cvt(vf[n]);
+            }
+        }
+        __syncthreads();
+
+        // ================= phase B: state products, Gram tiles, diagonal inverses ==========
+        f32x4 Y[4], Ot[4];
+#pragma unroll
+        for (int I = 0; I < 4; ++I) { Y[I] = f32x4{0.f, 0.f, 0.f, 0.f}; Ot[I] = Y[I]; }
+#pragma unroll
+        for (int ks = 0; ks < DK / 32; ++ks) {
+            asm volatile("" ::: "memory");  // bound how many fragments the scheduler hoists
+            const auto sf = Op::load32(&sm.sT[w][l16 * LDK + 32 * ks + 8 * lq]);
+#pragma unroll
+            for (int I = 0; I < 4; ++I) {
+                const auto a = Op::load32(&sm.k[(16 * I + l16) * LDK + 32 * ks + 8 * lq]);
+                Y[I] = Op::mma32(a, sf, Y[I]);
+                if (!summary) {
+                    const auto b = Op::load32(&sm.q[(16 * I + l16) * LDK + 32 * ks + 8 * lq]);
+                    Ot[I] = Op::mma32(sf, b, Ot[I]);
+                }
+            }
+        }
+        if (w == 0) {
+            // diagonal blocks of A_kk (fp32, strictly lower, rows scaled by beta), then invert
+#pragma unroll
+            for (int I = 0; I < 4; ++I) {
+                asm volatile("" ::: "memory");
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < DK / 32; ++ks) {
+                    const auto a = Op::load32(&sm.k[(16 * I + l16) * LDK + 32 * ks + 8 * lq]);
+                    const auto b = Op::load32(&sm.kh[(16 * I + l16) * LDK + 32 * ks + 8 * lq]);
+                    acc = Op::mma32(a, b, acc);
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int i = 4 * lq + r;
+                    sm.ld[I * LDB + i * 16 + l16] = (l16 < i) ? sm.beta[16 * I + i] * acc[r] : 0.f;
+                }
+            }
+            wave_lds_sync();
+            // lane (I = l / 16, j = l % 16) solves column j of (I + L_II)^{-1} by forward substitution
+            const float* Lb = &sm.ld[lq * LDB];
+            float tc[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) tc[i] = 0.f;
+            // row i+1 of L_II is loaded while row i is consumed; the compiler barrier keeps at
+            // most two rows in registers
+            float4 cur[4], nxt[4];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                if (i + 1 < 16) {
+#pragma unroll
+                    for (int mb = 0; mb < (i + 4) / 4; ++mb)
+                        nxt[mb] = *reinterpret_cast<const float4*>(&Lb[(i + 1) * 16 + 4 * mb]);
+                }
+                asm volatile("" ::: "memory");
+                float s = 0.f;
+#pragma unroll
+                for (int mb = 0; mb < (i + 3) / 4; ++mb)
+                    s += cur[mb].x * tc[4 * mb] + cur[mb].y * tc[4 * mb + 1] + cur[mb].z * tc[4 * mb + 2] +
+                         cur[mb].w * tc[4 * mb + 3];
+                tc[i] = (i == l16) ? 1.f : ((i < l16) ? 0.f : -s);
+#pragma unroll
+                for (int mb = 0; mb < 4; ++mb) cur[mb] = nxt[mb];
+            }
+#pragma unroll
+            for (int i = 0; i < 16; ++i) sm.td[(lq * 16 + i) * LDT + l16] = Op::cvt(tc[i]);
+        } else {
+            // off-diagonal A_kk blocks (6), then A_qk blocks (10, FINISH only)
+            const int ntiles = summary ? 6 : 16;
+            for (int idx = w - 1; idx < ntiles; idx += NW - 1) {
+                int I, J;
+                const bool is_kk = idx < 6;
+                if (is_kk) {
+                    I = idx < 1 ? 1 : (idx < 3 ? 2 : 3);
+                    J = idx - (I * (I - 1)) / 2;
+                } else {
+                    const int t = idx - 6;
+                    I = t < 1 ? 0 : (t < 3 ? 1 : (t < 6 ? 2 : 3));
+                    J = t - (I * (I + 1)) / 2;
+                }
+                const E* A = is_kk ? sm.k : sm.q;
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < DK / 32; ++ks) {
+                    const auto a = Op::load32(&A[(16 * I + l16) * LDK + 32 * ks + 8 * lq]);
+                    const auto b = Op::load32(&sm.kh[(16 * J + l16) * LDK + 32 * ks + 8 * lq]);
+                    acc = Op::mma32(a, b, acc);
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int i = 16 * I + 4 * lq + r;
+                    const int j = 16 * J + l16;
+                    if (is_kk) sm.l[i * LDC + j] = Op::cvt(sm.beta[i] * acc[r]);
+                    else sm.aqk[i * LDC + j] = Op::cvt(j <= i ? acc[r] : 0.f);
+                }
+            }
+        }
+        __syncthreads();
+
+        // ================= phase D: per-wave solve, output, state update ====================
+        E* xw = sm.x[w];
+        {
+            f32x4 R[4];
+#pragma unroll
+            for (int I = 0; I < 4; ++I) {
+                const int i0 = 16 * I + 4 * lq;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float vv = ld_f(&xw[l16 * LDC + i0 + r]);
+                    R[I][r] = sm.beta[i0 + r] * (vv - Y[I][r]);
+                }
+            }
+            // (I + A_kk) V~ = R, block rows I = 0..3
+#pragma unroll
+            for (int I = 0; I < 4; ++I) {
+                f32x4 X = R[I];
+                if (I > 0) {
+                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+                    const int rowL = (16 * I + l16) * LDC;
+                    if (I == 1) {
+                        acc = Op::mma16(Op::load16(&sm.l[rowL + 4 * lq]), Op::load16(&xw[l16 * LDC + 4 * lq]), acc);
+                    } else {
+                        acc = Op::mma32(Op::load32(&sm.l[rowL + 8 * lq]), Op::load32(&xw[l16 * LDC + 8 * lq]), acc);
+                        if (I == 3) {
+                            // A fresh accumulator: one accumulation chain never mixes MFMA shapes
+                            // (a 16x16x16 reading as SrcC the result of a 16x16x32 issued just
+                            // before it was observed to see the stale value).
+                            f32x4 acc16 = {0.f, 0.f, 0.f, 0.f};
+                            acc16 = Op::mma16(Op::load16(&sm.l[rowL + 32 + 4 * lq]),
+                                              Op::load16(&xw[l16 * LDC + 32 + 4 * lq]), acc16);
+                            acc = acc + acc16;
+                        }
+                    }
+                    X = X - acc;
+                }
+                E* xi = &xw[l16 * LDC + 16 * I + 4 * lq];
+                store4(xi, X[0], X[1], X[2], X[3]);
+                wave_lds_sync();
+                f32x4 vt = {0.f, 0.f, 0.f, 0.f};
+                vt = Op::mma16(Op::load16(&sm.td[(I * 16 + l16) * LDT + 4 * lq]), Op::load16(xi), vt);
+                store4(xi, vt[0], vt[1], vt[2], vt[3]);
+                wave_lds_sync();
+            }
+        }
+        if (!summary) {
+            TOut* og = (TOut*)p.o + lane * T * DV;
+#pragma unroll
+            for (int I = 0; I < 4; ++I) {
+                asm volatile("" ::: "memory");
+#pragma unroll
+                for (int ks = 0; ks < (I < 2 ? 1 : 2); ++ks) {
+                    const auto a = Op::load32(&xw[l16 * LDC + 32 * ks + 8 * lq]);
+                    const auto b = Op::load32(&sm.aqk[(16 * I + l16) * LDC + 32 * ks + 8 * lq]);
+                    Ot[I] = Op::mma32(a, b, Ot[I]);
+                }
+                const int64_t row = c * kC + 16 * I + l16;
+                if (row < T) store4(og + row * DV + col0 + 4 * lq, Ot[I][0], Ot[I][1], Ot[I][2], Ot[I][3]);
+            }
+        }
+#pragma unroll
+        for (int M = 0; M < NM; ++M) {
+            asm volatile("" ::: "memory");
+            const float4 g4 = *reinterpret_cast<const float4*>(&sm.gam[16 * M + 4 * lq]);
+            f32x4 acc = Sacc[M];
+            acc[0] *= g4.x; acc[1] *= g4.y; acc[2] *= g4.z; acc[3] *= g4.w;
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                const auto a = Op::load32(&sm.kbT[(16 * M + l16) * LDC + 32 * ks + 8 * lq]);
+                const auto b = Op::load32(&xw[l16 * LDC + 32 * ks + 8 * lq]);
+                acc = Op::mma32(a, b, acc);
+            }
+            Sacc[M] = acc;
+            store4(&sm.sT[w][l16 * LDK + 16 * M + 4 * lq], acc[0], acc[1], acc[2], acc[3]);
+        }
+        __syncthreads();
+    }
+
+    // ---- exit state ------------------------------------------------------------------------
+    float* dst = nullptr;
+    int64_t ld_dst = DV;
+    if (summary) {
+        dst = p.ws_pair + (lane * p.nseg + seg) * DK * (DV + DK);
+        ld_dst = DV + DK;
+    } else if (seg == p.nseg - 1) {
+        dst = p.S_T ? p.S_T + lane * DK * DV : nullptr;
+    } else if (seg == 0) {
+        dst = p.ws_entry + ((lane * p.nseg + 1) * DK) * DV;
+    }
+    if (dst) {
+#pragma unroll
+        for (int M = 0; M < NM; ++M)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) dst[(int64_t)(16 * M + 4 * lq + r) * ld_dst + col0 + l16] = Sacc[M][r];
+    }
+}
+
+// Exact entry states: entry_{s+1} = S~_s + M_s entry_s for s = 1 .. nseg-2 (entry_1 was written by
+// the FINISH pass of segment 0). One workgroup per (lane, 16 value columns), fp32 throughout.
+template <int DK>
+__global__ __launch_bounds__(256) void segment_scan_kernel(ChunkLaunch p) {
+    __shared__ float Es[DK][17];
+    const int64_t DV = p.dv;
+    const int ncb = (int)(DV / 16);
+    const int64_t lane = blockIdx.x / ncb;
+    const int cb = blockIdx.x % ncb;
+    const int n = threadIdx.x & 15;
+    const int cr = threadIdx.x >> 4;
+    constexpr int RPT = DK / 16;
+    const int64_t LDP = DV + DK;
+    for (int i = 0; i < RPT; ++i) {
+        const int c = cr + 16 * i;
+        Es[c][n] = p.ws_entry[((lane * p.nseg + 1) * DK + c) * DV + 16 * cb + n];
+    }
+    for (int s = 1; s + 1 < p.nseg; ++s) {
+        __syncthreads();
+        const float* P = p.ws_pair + (lane * p.nseg + s) * DK * LDP;
+        float out[RPT];
+        for (int i = 0; i < RPT; ++i) {
+            const int c = cr + 16 * i;
+            const float* Prow = P + c * LDP;
+            float acc = Prow[16 * cb + n];
+            for (int m = 0; m < DK; m += 4) {
+                const float4 mr = *reinterpret_cast<const float4*>(Prow + DV + m);
+                acc += mr.x * Es[m][n] + mr.y * Es[m + 1][n] + mr.z * Es[m + 2][n] + mr.w * Es[m + 3][n];
+            }
+            out[i] = acc;
+        }
+        __syncthreads();
+        float* dst = p.ws_entry + (lane * p.nseg + s + 1) * DK * DV;
+        for (int i = 0; i < RPT; ++i) {
+            const int c = cr + 16 * i;
+            Es[c][n] = out[i];
+            dst[(int64_t)c * DV + 16 * cb + n] = out[i];
+        }
+    }
+}
+
+__global__ void copy_or_zero_kernel(float* dst, const float* src, int64_t n) {
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+        dst[i] = src ? src[i] : 0.f;
+}
+
+template <class Op, typename TIn, typename TOut, int DK, int NW>
+static hipError_t launch_t(const ChunkLaunch& a, hipStream_t st) {
+    const int W = NW * 16;
+    const int64_t blocks = a.lanes * ((int64_t)a.fin_nseg * (a.dv / W) + (int64_t)a.sum_nseg * ((a.dv + DK) / W));
+    if (blocks <= 0) return hipSuccess;
+    hipLaunchKernelGGL((chunk_kernel<Op, TIn, TOut, DK, NW>), dim3((unsigned)blocks), dim3(NW * 64), 0, st, a);
+    return hipGetLastError();
+}
+
+template <typename TOut>
+static hipError_t launch_o(const ChunkLaunch& a, hipStream_t st) {
+    if (!a.in_bf16) return launch_t<OpF32, float, TOut, 64, 4>(a, st);  // fp32 path: dk = 64
+    if (a.dk == 128) {
+        if (a.nw == 8) return launch_t<OpBF16, bf16_t, TOut, 128, 8>(a, st);
+        return launch_t<OpBF16, bf16_t, TOut, 128, 4>(a, st);
+    }
+    if (a.nw == 8) return launch_t<OpBF16, bf16_t, TOut, 64, 8>(a, st);
+    return launch_t<OpBF16, bf16_t, TOut, 64, 4>(a, st);
+}
+
+hipError_t launch_chunk(const ChunkLaunch& a, hipStream_t st) {
+    return a.out_bf16 ? launch_o<bf16_t>(a, st) : launch_o<float>(a, st);
+}
+
+hipError_t launch_segment_scan(const ChunkLaunch& a, hipStream_t st) {
+    if (a.nseg <= 2) return hipSuccess;
+    const int64_t blocks = a.lanes * (a.dv / 16);
+    if (a.dk == 128) hipLaunchKernelGGL(segment_scan_kernel<128>, dim3((unsigned)blocks), dim3(256), 0, st, a);
+    else hipLaunchKernelGGL(segment_scan_kernel<64>, dim3((unsigned)blocks), dim3(256), 0, st, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_copy_or_zero(float* dst, const float* src, int64_t n, hipStream_t st) {
+    if (n <= 0) return hipSuccess;
+    int64_t blocks = (n + 255) / 256;
+    if (blocks > 4096) blocks = 4096;
+    hipLaunchKernelGGL(copy_or_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, st, dst, src, n);
+    return hipGetLastError();
+}
+
+}  // namespace kda

@@ -1,0 +1,117 @@
+// KDA single-token decode step for gfx950.
+//
+// One token of the recurrence in section 2.2 of the Kimi K3 reading notes
+// (liuzhao09.github.io/papers/kimi-k3.html):
+//   S' = Diag(alpha) S                           (decay, alpha = exp(log_alpha) per key channel)
+//   r  = S'^T k,   p = S'^T q                     (two reductions over the key dimension)
+//   delta = beta (v - r)
+//   S'' = S' + k delta^T                          (written back in place)
+//   o  = S''^T q = p + (k^T q) delta              (read after the write)
+// The fp32 state is ~99% of the bytes, so the kernel is HBM-bound: each state slab is read once
+// and written once with 16-byte coalesced accesses and kept in registers in between.
+//
+// Work mapping: one workgroup of 256 threads per (sequence, head). Thread t owns column quad
+// t % NQ (4 value columns, float4) and rows rg, rg + NRG, ... with rg = t / NQ, so each wave's
+// loads cover whole consecutive rows.
+#include "kda_device.h"
+#include "kda_internal.h"
+
+namespace kda {
+
+template <int DK, int DV, typename TIn, typename TOut>
+__global__ __launch_bounds__(256) void decode_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k,
+                                                     const TIn* __restrict__ v, const TIn* __restrict__ la,
+                                                     const TIn* __restrict__ beta, float* __restrict__ S,
+                                                     TOut* __restrict__ o, int64_t lanes) {
+    constexpr int NQ = DV / 4;        // column quads
+    constexpr int NRG = 256 / NQ;     // row groups
+    constexpr int RPT = DK / NRG;     // rows per thread
+    static_assert(RPT * NRG == DK, "shape");
+    __shared__ float red[NRG][NQ][9];
+    __shared__ float kq_part[NRG];
+
+    const int t = threadIdx.x;
+    const int cq = t % NQ;
+    const int rg = t / NQ;
+
+    for (int64_t lane = blockIdx.x; lane < lanes; lane += gridDim.x) {
+        float* Sl = S + lane * (int64_t)(DK * DV);
+        const TIn* ql = q + lane * DK;
+        const TIn* kl = k + lane * DK;
+        const TIn* lal = la + lane * DK;
+        const TIn* vl = v + lane * DV;
+
+        float4 s[RPT];
+#pragma unroll
+        for (int i = 0; i < RPT; ++i)
+            s[i] = *reinterpret_cast<const float4*>(Sl + (int64_t)(rg + NRG * i) * DV + 4 * cq);
+
+        float kr[RPT], qr[RPT];
+        float rs[4] = {0.f, 0.f, 0.f, 0.f}, ps[4] = {0.f, 0.f, 0.f, 0.f};
+        float kq = 0.f;
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) {
+            const int row = rg + NRG * i;
+            kr[i] = ld_f(kl + row);
+            qr[i] = ld_f(ql + row);
+            const float a = __builtin_amdgcn_exp2f(ld_f(lal + row) * kLog2e);
+            s[i].x *= a; s[i].y *= a; s[i].z *= a; s[i].w *= a;
+            rs[0] += kr[i] * s[i].x; rs[1] += kr[i] * s[i].y; rs[2] += kr[i] * s[i].z; rs[3] += kr[i] * s[i].w;
+            ps[0] += qr[i] * s[i].x; ps[1] += qr[i] * s[i].y; ps[2] += qr[i] * s[i].z; ps[3] += qr[i] * s[i].w;
+            kq += kr[i] * qr[i];
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) { red[rg][cq][j] = rs[j]; red[rg][cq][4 + j] = ps[j]; }
+        if (cq == 0) kq_part[rg] = kq;
+        __syncthreads();
+        float r4[4] = {0.f, 0.f, 0.f, 0.f}, p4[4] = {0.f, 0.f, 0.f, 0.f};
+        float kqt = 0.f;
+#pragma unroll
+        for (int g = 0; g < NRG; ++g) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) { r4[j] += red[g][cq][j]; p4[j] += red[g][cq][4 + j]; }
+            kqt += kq_part[g];
+        }
+        const float b = ld_f(beta + lane);
+        float d4[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) d4[j] = b * (ld_f(vl + 4 * cq + j) - r4[j]);
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) {
+            s[i].x += kr[i] * d4[0]; s[i].y += kr[i] * d4[1]; s[i].z += kr[i] * d4[2]; s[i].w += kr[i] * d4[3];
+            *reinterpret_cast<float4*>(Sl + (int64_t)(rg + NRG * i) * DV + 4 * cq) = s[i];
+        }
+        if (rg == 0) {
+            TOut* ol = o + lane * DV + 4 * cq;
+            store4(ol, p4[0] + kqt * d4[0], p4[1] + kqt * d4[1], p4[2] + kqt * d4[2], p4[3] + kqt * d4[3]);
+        }
+        __syncthreads();  // red[] is reused by the next lane of a grid-stride loop
+    }
+}
+
+template <int DK, int DV, typename TIn, typename TOut>
+static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t st) {
+    const int64_t lanes = a.N * a.H;
+    const int64_t grid = lanes < (int64_t)1 << 30 ? lanes : (int64_t)1 << 30;
+    hipLaunchKernelGGL((decode_kernel<DK, DV, TIn, TOut>), dim3((unsigned)grid), dim3(256), 0, st,
+                       (const TIn*)a.q, (const TIn*)a.k, (const TIn*)a.v, (const TIn*)a.la, (const TIn*)a.beta,
+                       a.S, (TOut*)a.o, lanes);
+    return hipGetLastError();
+}
+
+template <int DK, int DV>
+static hipError_t launch_decode_d(const DecodeArgs& a, hipStream_t st) {
+    if (a.in_bf16 && a.out_bf16) return launch_decode_t<DK, DV, bf16_t, bf16_t>(a, st);
+    if (a.in_bf16) return launch_decode_t<DK, DV, bf16_t, float>(a, st);
+    if (a.out_bf16) return launch_decode_t<DK, DV, float, bf16_t>(a, st);
+    return launch_decode_t<DK, DV, float, float>(a, st);
+}
+
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t st) {
+    if (a.dk == 128 && a.dv == 128) return launch_decode_d<128, 128>(a, st);
+    if (a.dk == 128 && a.dv == 64) return launch_decode_d<128, 64>(a, st);
+    if (a.dk == 64 && a.dv == 128) return launch_decode_d<64, 128>(a, st);
+    return launch_decode_d<64, 64>(a, st);
+}
+
+}  // namespace kda

@@ -1,0 +1,130 @@
+/*
+ * kda.h -- C ABI of the Kimi Delta Attention (KDA) hot path for AMD Instinct MI355X (gfx950).
+ *
+ * The operation (Kimi K3 reading notes, liuzhao09.github.io/papers/kimi-k3.html, section 2.2,
+ * state recurrence equation): per (batch b, head h) lane a fixed-size state S in R^{dk x dv}
+ * (rows are key channels) evolves token by token as
+ *
+ *     S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T,   o_t = S_t^T q_t,
+ *
+ * with per-channel retention alpha_t = exp(log_alpha_t) in (0,1]^{dk} and write strength beta_t.
+ * Prefill evaluates it in the chunkwise form of the same section (cumulative decay
+ * gamma^{i->j}, UT transform, causal matrix including the diagonal); decode applies one step.
+ * The carried initial / final state is the KDA checkpoint restored at a prefix-cache hit
+ * (section 2.5, Figure 12).
+ *
+ * Conventions shared by every entry point
+ *  - All data pointers are DEVICE pointers, owned by the caller, who allocates and frees them.
+ *    The library never allocates device memory, never synchronises and keeps no per-call state.
+ *  - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default stream). A returned
+ *    KDA_OK means the work was enqueued; a kernel fault surfaces at the caller's next sync.
+ *  - Arguments are validated before any device work. On any error nothing is enqueued and
+ *    no output is touched. No entry point aborts or throws.
+ *  - Element types: kda_dtype. Inputs q,k,v,log_alpha,beta share `in_dtype`; the output o
+ *    uses `out_dtype`; states (S0, S_T, S) are always fp32.
+ *  - q and k are used as given (the library does not L2-normalise them); no 1/sqrt(d) scale.
+ *  - Every tensor is dense and row-major with the last dimension contiguous; tensor base
+ *    pointers must be 16-byte aligned (beta: aligned to its element size).
+ *  - Decay domain: log_alpha must lie in [-5, 0] (the lower bound g_min = -5 of the decay
+ *    equation in section 2.2). Prefill additionally requires every per-channel sum of
+ *    log_alpha over one 64-token chunk to be >= -80 (true whenever log_alpha >= -1.25); outside
+ *    this range results are undefined (no check is made: it would need a pass over the data).
+ */
+#ifndef KDA_H
+#define KDA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum kda_status {
+    KDA_OK = 0,
+    KDA_ERR_INVALID_ARG = -1, /* null/negative/misaligned/overlapping argument            */
+    KDA_ERR_UNSUPPORTED = -2, /* well-formed but not implemented (e.g. dk not in {64,128}) */
+    KDA_ERR_WORKSPACE = -3,   /* workspace missing or smaller than the query reports      */
+    KDA_ERR_HIP = -4          /* the HIP runtime reported an error while enqueuing        */
+} kda_status;
+
+typedef enum kda_dtype {
+    KDA_F32 = 0,  /* IEEE fp32                                    */
+    KDA_BF16 = 1  /* bfloat16 (round-to-nearest-even on output)   */
+} kda_dtype;
+
+/* Shape and types of one chunkwise prefill call. */
+typedef struct kda_chunk_desc {
+    int64_t B;          /* batch, >= 1                                                   */
+    int64_t H;          /* heads, >= 1                                                   */
+    int64_t T;          /* tokens per lane, >= 0 (any value; a ragged last chunk is fine) */
+    int64_t dk;         /* key dimension: 64 or 128                                      */
+    int64_t dv;         /* value dimension: 64 or 128                                    */
+    int32_t chunk;      /* chunk length C: must be 64                                    */
+    int32_t in_dtype;   /* kda_dtype of q,k,v,log_alpha,beta (KDA_F32 needs dk == 64)    */
+    int32_t out_dtype;  /* kda_dtype of o                                                */
+    int32_t segments;   /* sequence segments per lane: 0 = library's choice, n >= 1 = n  */
+} kda_chunk_desc;
+
+/* Shape and types of one decode step over N independent sequences. */
+typedef struct kda_decode_desc {
+    int64_t N;          /* sequences, >= 1                 */
+    int64_t H;          /* heads, >= 1                     */
+    int64_t dk;         /* key dimension: 64 or 128        */
+    int64_t dv;         /* value dimension: 64 or 128      */
+    int32_t in_dtype;   /* kda_dtype of q,k,v,log_alpha,beta */
+    int32_t out_dtype;  /* kda_dtype of o                  */
+} kda_decode_desc;
+
+/*
+ * Bytes of device workspace kda_chunk_fwd needs for `desc` (0 when the call needs none, and
+ * 0 for an invalid desc). The workspace holds per-segment affine pairs (M, S~) with
+ * S_out = S~ + M S_in and the exact entry state of each segment (section 2.5 of the Kimi K3
+ * reading notes: segment transforms compose associatively, and a prefix scan gives every
+ * segment its entry state).
+ */
+size_t kda_chunk_fwd_workspace_bytes(const kda_chunk_desc* desc);
+
+/*
+ * Chunkwise KDA prefill: kda_chunk_fwd(q,k,v,log_alpha,beta,S0) -> (o, S_T).
+ *   q, k, log_alpha : [B,H,T,dk] in_dtype      v : [B,H,T,dv] in_dtype
+ *   beta            : [B,H,T]    in_dtype      o : [B,H,T,dv] out_dtype (written)
+ *   S0              : [B,H,dk,dv] fp32 entry state, or NULL for the zero state
+ *   S_T             : [B,H,dk,dv] fp32 state after token T-1 (written), or NULL to skip;
+ *                     may be the same pointer as S0 (in-place update), must not partially
+ *                     overlap it
+ *   workspace       : at least kda_chunk_fwd_workspace_bytes(desc) bytes (may be NULL if 0)
+ * o must not overlap any input. T == 0 writes S_T = S0 (or zeros) and touches nothing else.
+ * Source: section 2.2 (recurrence and chunk equations) and section 2.5 (affine pair,
+ * in-device sequence split) of the Kimi K3 reading notes.
+ */
+kda_status kda_chunk_fwd(const kda_chunk_desc* desc,
+                         const void* q, const void* k, const void* v,
+                         const void* log_alpha, const void* beta,
+                         const float* S0, void* o, float* S_T,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * One KDA decode step: kda_decode_step(q,k,v,log_alpha,beta,S) -> (o, S').
+ *   q, k, log_alpha : [N,H,dk] in_dtype        v : [N,H,dv] in_dtype
+ *   beta            : [N,H]    in_dtype        o : [N,H,dv] out_dtype (written)
+ *   S               : [N,H,dk,dv] fp32, read and overwritten in place with S'
+ * o must not overlap S or any input. Source: the recurrence of section 2.2 (one token), and
+ * section 2.5's decode regime (a fixed-size state, one launch per step, no KV growth).
+ */
+kda_status kda_decode_step(const kda_decode_desc* desc,
+                           const void* q, const void* k, const void* v,
+                           const void* log_alpha, const void* beta,
+                           float* S, void* o, void* stream);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char* kda_status_string(int32_t status);
+
+/* Static version string of the library, e.g. "kda-gfx950 0.1.0". */
+const char* kda_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H */

@@ -1,0 +1,114 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports every function
+``include/kda.h`` declares, and rejects bad arguments before any device work."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import gated_delta_rule_78_amd as kda
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE, HIP = 0, -1, -2, -3, -4
+FAKE = 0x7F0000000000  # never dereferenced: every call below fails validation first
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(kda.LIB_PATH):
+        from gated_delta_rule_78_amd import build
+        build.build()
+    return kda.library()
+
+
+def test_header_declares_the_boundary():
+    assert declared_functions() == ["kda_chunk_fwd", "kda_chunk_fwd_workspace_bytes", "kda_decode_step",
+                                    "kda_status_string", "kda_version"]
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings_and_version(lib):
+    for code in (OK, INVALID, UNSUPPORTED, WORKSPACE, HIP):
+        s = lib.kda_status_string(code).decode()
+        assert s.startswith("KDA_")
+    assert lib.kda_status_string(12345).decode() == "unknown kda_status"
+    assert lib.kda_version().decode().startswith("kda-gfx950")
+
+
+def _desc(B=1, H=2, T=128, dk=128, dv=128, chunk=64, ind=1, outd=1, seg=0):
+    return kda.ChunkDesc(B, H, T, dk, dv, chunk, ind, outd, seg)
+
+
+def _chunk(lib, d, q=FAKE, k=FAKE + (1 << 30), v=FAKE + (2 << 30), la=FAKE + (3 << 30), beta=FAKE + (4 << 30),
+           S0=None, o=FAKE + (5 << 30), ST=None, ws=None, ws_bytes=0):
+    P = ctypes.c_void_p
+    return lib.kda_chunk_fwd(None if d is None else ctypes.byref(d), P(q), P(k), P(v), P(la), P(beta), P(S0), P(o),
+                             P(ST), P(ws), ws_bytes, None)
+
+
+def test_chunk_rejects_bad_descriptors(lib):
+    assert _chunk(lib, None) == INVALID
+    assert _chunk(lib, _desc(B=0)) == INVALID
+    assert _chunk(lib, _desc(T=-1)) == INVALID
+    assert _chunk(lib, _desc(seg=-2)) == INVALID
+    assert _chunk(lib, _desc(ind=7)) == INVALID
+    assert _chunk(lib, _desc(chunk=32)) == UNSUPPORTED
+    assert _chunk(lib, _desc(dk=96)) == UNSUPPORTED
+    assert _chunk(lib, _desc(dv=256)) == UNSUPPORTED
+    assert _chunk(lib, _desc(ind=0, dk=128)) == UNSUPPORTED   # the fp32 path is dk = 64 only
+
+
+def test_chunk_rejects_bad_pointers(lib):
+    assert _chunk(lib, _desc(), q=0) == INVALID
+    assert _chunk(lib, _desc(), o=0) == INVALID
+    assert _chunk(lib, _desc(), q=FAKE + 8) == INVALID               # misaligned
+    assert _chunk(lib, _desc(), S0=FAKE + (6 << 30) + 4) == INVALID  # misaligned state
+    assert _chunk(lib, _desc(), o=FAKE + 64) == INVALID              # o overlaps q
+    S = FAKE + (6 << 30)
+    assert _chunk(lib, _desc(), S0=S, ST=S + 1024) == INVALID        # partial state overlap
+    assert _chunk(lib, _desc(), S0=S, ST=S + (1 << 28), o=S + 16) == INVALID  # o overlaps S0
+
+
+def test_workspace_query_and_check(lib):
+    lanes, dk, dv = 2, 128, 128
+    d = _desc(B=1, H=lanes, T=64 * 40, seg=4)
+    need = lib.kda_chunk_fwd_workspace_bytes(ctypes.byref(d))
+    assert need == lanes * 4 * dk * (2 * dv + dk) * 4
+    assert _chunk(lib, d) == WORKSPACE
+    assert _chunk(lib, d, ws=FAKE + (7 << 30), ws_bytes=need - 1) == WORKSPACE
+    assert _chunk(lib, d, ws=FAKE + (7 << 30) + 8, ws_bytes=need) == INVALID   # misaligned workspace
+    assert _chunk(lib, d, ws=FAKE + 32, ws_bytes=need) == INVALID              # workspace overlaps q
+    assert lib.kda_chunk_fwd_workspace_bytes(ctypes.byref(_desc(seg=1))) == 0
+    assert lib.kda_chunk_fwd_workspace_bytes(ctypes.byref(_desc(dk=96))) == 0
+    assert lib.kda_chunk_fwd_workspace_bytes(None) == 0
+
+
+def _decode(lib, d, q=FAKE, k=FAKE + (1 << 30), v=FAKE + (2 << 30), la=FAKE + (3 << 30), beta=FAKE + (4 << 30),
+            S=FAKE + (5 << 30), o=FAKE + (6 << 30)):
+    P = ctypes.c_void_p
+    return lib.kda_decode_step(None if d is None else ctypes.byref(d), P(q), P(k), P(v), P(la), P(beta), P(S),
+                               P(o), None)
+
+
+def test_decode_rejects_bad_arguments(lib):
+    d = kda.DecodeDesc(4, 2, 128, 128, 1, 1)
+    assert _decode(lib, None) == INVALID
+    assert _decode(lib, kda.DecodeDesc(0, 2, 128, 128, 1, 1)) == INVALID
+    assert _decode(lib, kda.DecodeDesc(4, 2, 80, 128, 1, 1)) == UNSUPPORTED
+    assert _decode(lib, kda.DecodeDesc(4, 2, 128, 128, 3, 1)) == INVALID
+    assert _decode(lib, d, S=0) == INVALID
+    assert _decode(lib, d, S=FAKE + (5 << 30) + 4) == INVALID           # misaligned state
+    assert _decode(lib, d, o=FAKE + (5 << 30) + 64) == INVALID          # o overlaps S
+    assert _decode(lib, d, q=FAKE + (5 << 30) + 256) == INVALID         # input overlaps S

@@ -1,0 +1,159 @@
+"""GPU parity of kda_chunk_fwd (chunkwise prefill, section 2.2 of the Kimi K3 reading notes;
+sequence split by affine pairs, section 2.5) against the fp64 token-by-token oracle."""
+import numpy as np
+import pytest
+import torch
+
+import gated_delta_rule_78_amd as kda
+from gated_delta_rule_78_amd import synth
+from tests.parity import TOL_O, TOL_S, assert_close, host32, oracle_prefill, rel_l2_per_lane, say
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0") if torch.cuda.is_available() else None
+BF16, F32 = torch.bfloat16, torch.float32
+
+
+def run_and_check(tag, B, H, T, dk, dv, dt, odt=None, s0_std=None, segments=0, la_range=synth.LOG_ALPHA_RANGE,
+                  seed=1000):
+    say("%s: B=%d H=%d T=%d dk=%d dv=%d in=%s out=%s S0=%s segments=%d log_alpha=%s" %
+        (tag, B, H, T, dk, dv, dt, odt, s0_std, segments, la_range))
+    q, k, v, la, beta, S0 = synth.prefill_inputs(B, H, T, dk, dv, dt, device=DEV, seed_base=seed, s0_std=s0_std,
+                                                 log_alpha_range=la_range)
+    o, S_T = kda.chunk_fwd(q, k, v, la, beta, S0, out_dtype=odt, segments=segments)
+    torch.cuda.synchronize()
+    o_ref, S_ref = oracle_prefill(q, k, v, la, beta, S0)
+    assert_close(tag, dt, host32(o).reshape(B * H, T, dv), o_ref, host32(S_T).reshape(B * H, dk, dv), S_ref)
+    return o, S_T
+
+
+def test_fp32_small_workload():
+    """fp32 path: B=1, H=1, T=256, d=64, S0=0 (tolerance 1e-4)."""
+    w = synth.PREFILL_FP32_SMALL
+    run_and_check("fp32 small", w.B, w.H, w.T, w.d, w.d, F32)
+
+
+@pytest.mark.parametrize("T", [1, 15, 16, 17, 63, 64, 65, 127, 130, 200])
+def test_ragged_lengths_bf16(T):
+    run_and_check("ragged", 1, 3, T, 128, 128, BF16, seed=2000 + T)
+
+
+@pytest.mark.parametrize("T", [1, 65, 200])
+def test_ragged_lengths_fp32(T):
+    run_and_check("ragged fp32", 1, 2, T, 64, 64, F32, seed=2100 + T)
+
+
+@pytest.mark.parametrize("dk,dv", [(64, 64), (64, 128), (128, 64), (128, 128)])
+@pytest.mark.parametrize("odt", [BF16, F32])
+def test_shapes_and_prefix_state(dk, dv, odt):
+    run_and_check("shapes", 2, 3, 333, dk, dv, BF16, odt=odt, s0_std=0.5, seed=3000 + dk + dv)
+
+
+@pytest.mark.parametrize("segments", [2, 3, 5])
+def test_segment_split_slow_decay(segments):
+    """The sequence split must give the same result as one pass; slow decay keeps the carried
+    state (and so the affine pairs M) significant across segments."""
+    run_and_check("segments", 1, 4, 64 * 23 + 17, 128, 128, BF16, s0_std=0.3, segments=segments,
+                  la_range=(-0.02, 0.0), seed=4000 + segments)
+
+
+def test_segment_split_no_decay_channels():
+    """alpha = 1 on every channel (log_alpha = 0): M carries the entry state undamped."""
+    run_and_check("segments alpha=1", 1, 2, 64 * 12, 64, 64, BF16, s0_std=0.3, segments=4, la_range=(0.0, 0.0),
+                  seed=4100)
+
+
+def test_full_decay_contract_edge():
+    """log_alpha down to -1.25 (a 64-chunk sum can reach -80, the edge of the kernel's contract)."""
+    run_and_check("decay edge", 1, 2, 640, 128, 128, BF16, la_range=(-1.25, -1.0), seed=4200)
+
+
+def test_bf16_8k_workload_all_heads():
+    """B=1, H=32, T=8192, d=128, bf16 in / fp32 state, S0=0: every head against the oracle."""
+    w = synth.PREFILL_BF16_8K
+    run_and_check("bf16 8k", w.B, w.H, w.T, w.d, w.d, w.dtype)
+
+
+def test_prefix_64k_workload_sampled_lanes():
+    """B=4, H=32, T=65536 with S0 ~ N(0, 0.02): the full launch; 6 lanes checked end to end."""
+    w = synth.PREFILL_BF16_PREFIX_64K
+    say("prefix 64k: B=%d H=%d T=%d" % (w.B, w.H, w.T))
+    q, k, v, la, beta, S0 = synth.workload_inputs(w, device=DEV)
+    o, S_T = kda.chunk_fwd(q, k, v, la, beta, S0)
+    torch.cuda.synchronize()
+    lanes = [0, 31, 32, 77, 100, 127]
+    bh = lambda t: t.reshape((w.B * w.H,) + tuple(t.shape[2:]))[lanes]
+    o_ref, S_ref = oracle_prefill(bh(q)[:, None], bh(k)[:, None], bh(v)[:, None], bh(la)[:, None],
+                                  bh(beta)[:, None], bh(S0)[:, None])
+    assert_close("prefix 64k", BF16, host32(bh(o)), o_ref, host32(bh(S_T)), S_ref)
+
+
+def test_long_1m_workload_sampled():
+    """B=1, H=32, T=1,048,576 (sequence split across CUs): the full launch; two heads checked
+    (final state, and outputs on the last 2048 tokens plus 64 spread rows)."""
+    w = synth.PREFILL_BF16_1M
+    say("long 1M: H=%d T=%d" % (w.H, w.T))
+    q, k, v, la, beta, _ = synth.workload_inputs(w, device=DEV)
+    o, S_T = kda.chunk_fwd(q, k, v, la, beta)
+    torch.cuda.synchronize()
+    heads = [3, 30]
+    rows = sorted(set(list(range(0, w.T, w.T // 64)) + list(range(w.T - 2048, w.T))))
+    o_ref, S_ref = oracle_prefill(q[:, heads], k[:, heads], v[:, heads], la[:, heads], beta[:, heads], None,
+                                  rows=rows)
+    o_gpu = host32(o[0, heads][:, rows])
+    assert_close("long 1M", BF16, o_gpu, o_ref, host32(S_T[0, heads]), S_ref)
+
+
+def test_split_resume_at_prefix_hit():
+    """Prefix-cache hit at B=2560 (Figure 12): run [0, 2560), restore the state, continue;
+    equals a one-shot run."""
+    B, H, T, d, Bhit = 1, 8, 4000, 128, 2560
+    q, k, v, la, beta, S0 = synth.prefill_inputs(B, H, T, d, d, BF16, device=DEV, seed_base=5000, s0_std=0.1,
+                                                 log_alpha_range=(-0.05, 0.0))
+    o_full, S_full = kda.chunk_fwd(q, k, v, la, beta, S0, out_dtype=F32)
+    cut = lambda x, a, b: x[:, :, a:b].contiguous()
+    o_a, S_B = kda.chunk_fwd(cut(q, 0, Bhit), cut(k, 0, Bhit), cut(v, 0, Bhit), cut(la, 0, Bhit),
+                             cut(beta, 0, Bhit), S0, out_dtype=F32)
+    o_b, S_end = kda.chunk_fwd(cut(q, Bhit, T), cut(k, Bhit, T), cut(v, Bhit, T), cut(la, Bhit, T),
+                               cut(beta, Bhit, T), S_B, out_dtype=F32)
+    torch.cuda.synchronize()
+    # the two calls may split their sequences differently, so agreement is to tolerance
+    assert np.abs(host32(o_a) - host32(o_full[:, :, :Bhit])).max() <= TOL_O[BF16]
+    assert np.abs(host32(o_b) - host32(o_full[:, :, Bhit:])).max() <= TOL_O[BF16]
+    assert rel_l2_per_lane(host32(S_end).reshape(H, -1), host32(S_full).reshape(H, -1)) <= TOL_S[BF16]
+
+
+def test_identity_decay_no_write():
+    """alpha = 1, beta = 0: S_T = S0 and o_t = S0^T q_t."""
+    B, H, T, d = 1, 2, 200, 128
+    q, k, v, la, beta, S0 = synth.prefill_inputs(B, H, T, d, d, BF16, device=DEV, seed_base=5100, s0_std=0.5)
+    la.zero_()
+    beta.zero_()
+    o, S_T = kda.chunk_fwd(q, k, v, la, beta, S0, out_dtype=F32)
+    torch.cuda.synchronize()
+    ref = torch.matmul(q.double().cpu(), S0.double().cpu()).numpy()
+    assert np.abs(host32(o) - ref).max() <= TOL_O[BF16]
+    # the state passes through exactly (gamma = 1, no write)
+    assert torch.equal(S_T, S0)
+
+
+def test_in_place_state_and_empty_sequence():
+    B, H, T, d = 1, 2, 100, 64
+    q, k, v, la, beta, S0 = synth.prefill_inputs(B, H, T, d, d, BF16, device=DEV, seed_base=5200, s0_std=0.2)
+    _, S_ref = kda.chunk_fwd(q, k, v, la, beta, S0.clone())
+    S = S0.clone()
+    kda.chunk_fwd(q, k, v, la, beta, S, S_T=S)
+    e = lambda x: x[:, :, :0].contiguous()
+    S_empty = torch.full_like(S0, 7.0)
+    kda.chunk_fwd(e(q), e(k), e(v), e(la), e(beta), S0, S_T=S_empty)
+    torch.cuda.synchronize()
+    assert torch.equal(S, S_ref)
+    assert torch.equal(S_empty, S0)
+
+
+def test_run_to_run_determinism():
+    B, H, T, d = 1, 4, 1500, 128
+    q, k, v, la, beta, S0 = synth.prefill_inputs(B, H, T, d, d, BF16, device=DEV, seed_base=5300, s0_std=0.1)
+    a = kda.chunk_fwd(q, k, v, la, beta, S0, segments=3)
+    b = kda.chunk_fwd(q, k, v, la, beta, S0, segments=3)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
