@@ -1,0 +1,192 @@
+"""Benchmark of the KDA hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload prefill_8k|prefill_64k|prefill_1m|fp32_small]
+                    [--decode-steps 1000] [--no-cpu-baseline] [--copy-probe-mib M]
+
+One step = one kda_chunk_fwd call over the named prefill workload (default: bf16, B=1, H=32,
+T=8192, d=128, C=64, S0=0), inputs already resident in HBM. The decode regime is measured in
+the same run: `--decode-steps` chained kda_decode_step calls over 256 sequences x 32 heads
+(fp32 state, bf16 tokens, each step its own pre-generated tokens). Times come from HIP events
+recorded on the stream the library launches on.
+
+Prints one JSON line. `value` is prefill tokens/s (B*T / seconds per call). `roofline` is the
+prefill call against HBM bandwidth with algorithmic bytes; `decode` carries the decode
+figures and its own roofline; `cpu_baseline` is the fp64 oracle timed on this host.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
+FP32_PEAK_TFLOPS = 157.3       # MI355X fp32 vector/matrix, published
+
+# Algorithmic work per token-head of chunkwise prefill (C = 64, dk = dv = d):
+#   flops  6*dk*dv + C*(3*dk + 2*dv) + C^2/3      (state products, Gram/UT/causal halves)
+#   bytes  q,k,log_alpha,v (4*d elements in) + beta (1) + o (d elements out)
+# plus one fp32 state read (S0, when given) and one fp32 state write (S_T) per head.
+def prefill_alg(B, H, T, d, in_bytes, out_bytes, has_s0, C=64):
+    flops_tok = 6 * d * d + C * (5 * d) + C * C / 3.0
+    bytes_tok = 4 * d * in_bytes + in_bytes + d * out_bytes
+    state = d * d * 4 * (2 if has_s0 else 1)
+    return B * H * T * flops_tok, B * H * (T * bytes_tok + state)
+
+
+# Decode per (sequence, head): fp32 state read + write, q,k,log_alpha,v in, beta, o out.
+def decode_alg(N, H, d, in_bytes=2, out_bytes=2):
+    flops = 7 * d * d
+    bytes_ = 2 * d * d * 4 + 4 * d * in_bytes + in_bytes + d * out_bytes
+    return N * H * flops, N * H * bytes_
+
+
+WORKLOADS = {
+    "prefill_8k": "PREFILL_BF16_8K",
+    "prefill_64k": "PREFILL_BF16_PREFIX_64K",
+    "prefill_1m": "PREFILL_BF16_1M",
+    "fp32_small": "PREFILL_FP32_SMALL",
+}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="prefill_8k", choices=sorted(WORKLOADS))
+    ap.add_argument("--segments", type=int, default=0, help="0 = the library's plan")
+    ap.add_argument("--decode-steps", type=int, default=1000)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-lanes", type=int, default=32, help="lanes of the CPU-baseline sample")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="also run one plain device copy of this size (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (--gpus %d refused)" % args.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import gated_delta_rule_78_amd as kda
+    from gated_delta_rule_78_amd import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    w = getattr(synth, WORKLOADS[args.workload])
+    print("bench: generating %s" % w.name, file=sys.stderr, flush=True)
+    q, k, v, la, beta, S0 = synth.workload_inputs(w, device=dev)
+    out_dtype = w.dtype
+    o = torch.empty(w.B, w.H, w.T, w.d, device=dev, dtype=out_dtype)
+    S_T = torch.empty(w.B, w.H, w.d, w.d, device=dev, dtype=torch.float32)
+    nbytes = kda.chunk_workspace_bytes(q, v, segments=args.segments)
+    ws = torch.empty(max(nbytes, 16), device=dev, dtype=torch.uint8)
+
+    def step():
+        kda.chunk_fwd(q, k, v, la, beta, S0, out_dtype=out_dtype, segments=args.segments, o=o, S_T=S_T,
+                      workspace=ws, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    ms_per_step = total_ms / args.steps
+    call_ms = float(np.mean([s.elapsed_time(e) for s, e in zip(starts, ends)]))
+    tokens = w.B * w.T
+    in_b = 2 if w.dtype == torch.bfloat16 else 4
+    flops, abytes = prefill_alg(w.B, w.H, w.T, w.d, in_b, in_b, S0 is not None)
+    achieved_gbs = abytes / (call_ms * 1e-3) / 1e9
+    tflops = flops / (call_ms * 1e-3) / 1e12
+    mm_peak = BF16_PEAK_TFLOPS if w.dtype == torch.bfloat16 else FP32_PEAK_TFLOPS
+
+    if args.copy_probe_mib:
+        n = args.copy_probe_mib * (1 << 20) // 4
+        src = torch.ones(n, device=dev, dtype=torch.float32)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    # ---------------- decode regime ----------------
+    decode = None
+    if args.decode_steps > 0:
+        dw = synth.DECODE_BF16_256x32
+        print("bench: decode %s" % dw.name, file=sys.stderr, flush=True)
+        S = synth.decode_state(dw.N, dw.H, dw.d, dw.d, dw.s_std, device=dev)
+        toks = [synth.decode_tokens(dw.N, dw.H, dw.d, dw.d, dw.dtype, device=dev, seed=4000 + i)
+                for i in range(min(args.decode_steps, 1000))]
+        od = torch.empty(dw.N, dw.H, dw.d, device=dev, dtype=dw.dtype)
+        for i in range(3):
+            kda.decode_step(*toks[i], S, o=od, stream=stream)
+        torch.cuda.synchronize()
+        d0 = torch.cuda.Event(enable_timing=True)
+        d1 = torch.cuda.Event(enable_timing=True)
+        d0.record(stream)
+        for i in range(args.decode_steps):
+            kda.decode_step(*toks[i % len(toks)], S, o=od, stream=stream)
+        d1.record(stream)
+        torch.cuda.synchronize()
+        dms = d0.elapsed_time(d1) / args.decode_steps
+        dfl, dby = decode_alg(dw.N, dw.H, dw.d)
+        dgbs = dby / (dms * 1e-3) / 1e9
+        decode = {"workload": dw.name, "metric": "KDA decode tokens/s", "value": dw.N / (dms * 1e-3),
+                  "unit": "tokens/s", "steps": args.decode_steps, "ms_per_step": dms,
+                  "roofline": {"bound": "hbm", "achieved": dgbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                               "frac": dgbs / HBM_PEAK_GBS, "traffic": None},
+                  "alg_bytes_per_step": dby, "alg_flops_per_step": dfl}
+        del toks
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle import native
+        L = min(args.cpu_lanes, w.B * w.H)
+        print("bench: cpu baseline (oracle) on %d lanes x %d tokens" % (L, w.T), file=sys.stderr, flush=True)
+        f = lambda x: x.reshape((-1,) + tuple(x.shape[2:]))[:L].float().cpu().numpy()
+        a = [f(q), f(k), f(v), f(la), f(beta)]
+        s0 = None if S0 is None else f(S0)
+        threads = native.default_threads()
+        t0 = time.perf_counter()
+        native.kda_fwd(*a, s0, threads=threads)
+        dt = time.perf_counter() - t0
+        # tokens/s of the whole workload at the sampled rate (lanes are independent)
+        whole_s = dt * (w.B * w.H) / L          # lanes are independent: scale the sample to the workload
+        cpu = {"value": w.B * w.T / whole_s, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+               "sample": "%d of %d lanes x %d tokens (fp64 token loop), %.2f s" % (L, w.B * w.H, w.T, dt)}
+
+    line = {
+        "metric": "KDA prefill tokens/s", "value": tokens / (call_ms * 1e-3), "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == torch.bfloat16 else "f32", "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "T": w.T, "dk": w.d, "dv": w.d, "chunk": 64,
+                   "s0": S0 is not None, "segments": args.segments or "auto", "workspace_bytes": nbytes},
+        "roofline": {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved_gbs / HBM_PEAK_GBS, "traffic": None},
+        "mfma": {"alg_tflops": tflops, "peak_tflops": mm_peak, "frac": tflops / mm_peak},
+        "alg_bytes_per_call": abytes, "alg_flops_per_call": flops, "call_ms": call_ms,
+        "decode": decode, "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -125,21 +125,23 @@ __global__ __launch_bounds__(NW * 64) void chunk_kernel(ChunkLaunch p) {
             if (seg > 0) entry = p.ws_entry + ((lane * p.nseg + seg) * DK) * DV;
             else if (p.S0) entry = p.S0 + lane * DK * DV;
         }
+        if (entry) {
+            // all loads issued together, one wait
+            const float* e = entry + col0 + l16;
 #pragma unroll
-        for (int M = 0; M < NM; ++M) {
+            for (int M = 0; M < NM; ++M)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int c = 16 * M + 4 * lq + r;
-                float s0 = 0.f;
-                if (!summary) {
-                    if (entry) s0 = entry[(int64_t)c * DV + col0 + l16];
-                } else if (m_cols) {
-                    s0 = (c == col0 - DV + l16) ? 1.f : 0.f;
-                }
-                Sacc[M][r] = s0;
-            }
-            store4(&sm.sT[w][l16 * LDK + 16 * M + 4 * lq], Sacc[M][0], Sacc[M][1], Sacc[M][2], Sacc[M][3]);
+                for (int r = 0; r < 4; ++r) Sacc[M][r] = e[(int64_t)(16 * M + 4 * lq + r) * DV];
+        } else {
+            const int diag = m_cols ? col0 - (int)DV + l16 : -1;  // identity columns of M
+#pragma unroll
+            for (int M = 0; M < NM; ++M)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) Sacc[M][r] = (16 * M + 4 * lq + r == diag) ? 1.f : 0.f;
         }
+#pragma unroll
+        for (int M = 0; M < NM; ++M)
+            store4(&sm.sT[w][l16 * LDK + 16 * M + 4 * lq], Sacc[M][0], Sacc[M][1], Sacc[M][2], Sacc[M][3]);
     }
     // A_qk blocks above the diagonal that the 32-wide K steps touch stay zero for the whole run.
     for (int i = tid; i < 2 * 256; i += NW * 64) {
@@ -186,40 +188,30 @@ __global__ __launch_bounds__(NW * 64) void chunk_kernel(ChunkLaunch p) {
                 unpack16(cq_[i], (const TIn*)nullptr, qf);
                 unpack16(ck_[i], (const TIn*)nullptr, kf);
                 unpack16(cg_[i], (const TIn*)nullptr, G);
-                // inclusive prefix sum over the 64 rows (lanes), in log2 units
+                // cumulative log-decay over the 64 rows (= lanes), in log2 units
 #pragma unroll
-                for (int j = 0; j < EPV; ++j) {
-                    float x = G[j] * kLog2e;
-#pragma unroll
-                    for (int off = 1; off < 64; off <<= 1) {
-                        const float y = __shfl_up(x, off, 64);
-                        if (l >= off) x += y;
-                    }
-                    G[j] = x;
-                }
-                E oq[EPV], ok_[EPV], okh[EPV];
+                for (int j = 0; j < EPV; ++j) G[j] = wave_prefix_sum(G[j] * kLog2e);
+                float oq[EPV], ok_[EPV], okh[EPV];
                 const int chg = ch0 + i * EPV;
 #pragma unroll
                 for (int j = 0; j < EPV; ++j) {
-                    const float gC = __builtin_amdgcn_exp2f(__shfl(G[j], 63, 64));
+                    const float gC = __builtin_amdgcn_exp2f(lane_value(G[j], 63));  // gamma_C, wave-uniform
                     const float gam = __builtin_amdgcn_exp2f(G[j]);
                     const float kh = kf[j] * __builtin_amdgcn_exp2f(-G[j]);
-                    oq[j] = Op::cvt(qf[j] * gam);
-                    ok_[j] = Op::cvt(kf[j] * gam);
-                    okh[j] = Op::cvt(kh);
+                    oq[j] = qf[j] * gam;
+                    ok_[j] = kf[j] * gam;
+                    okh[j] = kh;
                     sm.kbT[(chg + j) * LDC + l] = Op::cvt(kh * gC);
-                    if (l == 0) sm.gam[chg + j] = gC;
+                    if (l == j) sm.gam[chg + j] = gC;
                 }
-                constexpr int EV = 16 / (int)sizeof(E);
-#pragma unroll
-                for (int j = 0; j < EPV; j += EV) {
-                    uint4 a, b, d;
-                    __builtin_memcpy(&a, &oq[j], 16);
-                    __builtin_memcpy(&b, &ok_[j], 16);
-                    __builtin_memcpy(&d, &okh[j], 16);
-                    *reinterpret_cast<uint4*>(&sm.q[l * LDK + chg + j]) = a;
-                    *reinterpret_cast<uint4*>(&sm.k[l * LDK + chg + j]) = b;
-                    *reinterpret_cast<uint4*>(&sm.kh[l * LDK + chg + j]) = d;
+                if constexpr (EPV == 8) {
+                    store8(&sm.q[l * LDK + chg], oq);
+                    store8(&sm.k[l * LDK + chg], ok_);
+                    store8(&sm.kh[l * LDK + chg], okh);
+                } else {
+                    store4(&sm.q[l * LDK + chg], oq[0], oq[1], oq[2], oq[3]);
+                    store4(&sm.k[l * LDK + chg], ok_[0], ok_[1], ok_[2], ok_[3]);
+                    store4(&sm.kh[l * LDK + chg], okh[0], okh[1], okh[2], okh[3]);
                 }
             }
             if (w == 0) sm.beta[l] = bcur;

@@ -39,15 +39,59 @@ __device__ __forceinline__ void unpack16(uint4 u, const float*, float* out) {
 }
 template <typename T> struct ElemsPer16 { static constexpr int value = 16 / sizeof(T); };
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Two floats to two bfloat16 (round to nearest even) in one 32-bit word, low half = a.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    const f32x2 v = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
 // Store 4 consecutive floats as storage type T (8 bytes for bf16, 16 bytes for fp32).
 __device__ __forceinline__ void store4(bf16_t* p, float a, float b, float c, float d) {
     uint2 u;
-    u.x = (uint32_t)f32_to_bf16_bits(a) | ((uint32_t)f32_to_bf16_bits(b) << 16);
-    u.y = (uint32_t)f32_to_bf16_bits(c) | ((uint32_t)f32_to_bf16_bits(d) << 16);
+    u.x = pack_bf16x2(a, b);
+    u.y = pack_bf16x2(c, d);
     *reinterpret_cast<uint2*>(p) = u;
 }
 __device__ __forceinline__ void store4(float* p, float a, float b, float c, float d) {
     *reinterpret_cast<float4*>(p) = make_float4(a, b, c, d);
+}
+
+// Store 8 consecutive floats (16 bytes for bf16, 32 bytes for fp32).
+__device__ __forceinline__ void store8(bf16_t* p, const float* x) {
+    uint4 u;
+    u.x = pack_bf16x2(x[0], x[1]); u.y = pack_bf16x2(x[2], x[3]);
+    u.z = pack_bf16x2(x[4], x[5]); u.w = pack_bf16x2(x[6], x[7]);
+    *reinterpret_cast<uint4*>(p) = u;
+}
+__device__ __forceinline__ void store8(float* p, const float* x) {
+    *reinterpret_cast<float4*>(p) = make_float4(x[0], x[1], x[2], x[3]);
+    *reinterpret_cast<float4*>(p + 4) = make_float4(x[4], x[5], x[6], x[7]);
+}
+
+// Lane shuffle within a wave via DPP; lanes whose source is outside the pattern read 0.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_f32(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, ROW_MASK, 0xf, true));
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave: Hillis-Steele inside each 16-lane row
+// (row_shr 1, 2, 4, 8), then row 0's total into rows 1 and 3 (row_bcast:15) and lane 31's
+// total into rows 2 and 3 (row_bcast:31).
+__device__ __forceinline__ float wave_prefix_sum(float x) {
+    x += dpp_f32<0x111, 0xf>(x);
+    x += dpp_f32<0x112, 0xf>(x);
+    x += dpp_f32<0x114, 0xf>(x);
+    x += dpp_f32<0x118, 0xf>(x);
+    x += dpp_f32<0x142, 0xa>(x);
+    x += dpp_f32<0x143, 0xc>(x);
+    return x;
+}
+
+__device__ __forceinline__ float lane_value(float x, int lane) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), lane));
 }
 
 // Order this wave's LDS writes before its later LDS reads (all lanes of the wave).
