@@ -32,14 +32,24 @@ int64_t elem_bytes(int32_t d) { return d == KDA_BF16 ? 2 : 4; }
 struct Plan {
     int nseg;
     int64_t chunks_per_seg;
-    int nw_pass1, nw_pass2;
+    int nw, nt;  // waves per workgroup, 16-column state tiles per wave
     size_t ws_bytes;
 };
 
-int pick_nw(int64_t dk, int64_t dv) {
-    // 8 waves (128 columns) per workgroup share one key-side preparation between twice as many
-    // state columns; measured faster than 4 waves whenever the column counts divide.
-    return ((dv % 128 == 0) && ((dv + dk) % 128 == 0)) ? 8 : 4;
+// Workgroup shape: 128 state columns per workgroup (4 waves x 2 tiles) wherever 128 divides
+// both the value width and the augmented width, else 4 waves x 1 tile (64 columns).
+void pick_shape(const kda_chunk_desc* d, int* nw, int* nt) {
+    const bool w128 = (d->dv % 128 == 0) && ((d->dv + d->dk) % 128 == 0) && d->dk == 128;
+    // dk = dv = 128: eight waves, one 16-column state tile each (measured faster than four
+    // waves holding two tiles: more waves hide the LDS and exp latency of the chunk prologue).
+    *nw = w128 ? 8 : 4;
+    *nt = 1;
+    // Launch-shape override for tuning sweeps: KDA_NW=8 (8 waves x 1 tile), 4 (4 x 1) or 4x2.
+    if (const char* e = getenv("KDA_NW")) {
+        if (!strcmp(e, "8") && w128) { *nw = 8; *nt = 1; }
+        else if (!strcmp(e, "4")) { *nw = 4; *nt = 1; }
+        else if (!strcmp(e, "4x2") && w128) { *nw = 4; *nt = 2; }
+    }
 }
 
 Plan make_plan(const kda_chunk_desc* d) {
@@ -63,20 +73,13 @@ Plan make_plan(const kda_chunk_desc* d) {
     nseg = nchunks > 0 ? (nchunks + cps - 1) / cps : 1;  // no empty segment
     p.nseg = (int)nseg;
     p.chunks_per_seg = cps;
-    p.nw_pass1 = p.nw_pass2 = pick_nw(d->dk, d->dv);
+    pick_shape(d, &p.nw, &p.nt);
     if (nseg == 1) {
         p.ws_bytes = 0;
     } else {
         p.ws_bytes = (size_t)lanes * (size_t)nseg * (size_t)d->dk * (size_t)(2 * d->dv + d->dk) * sizeof(float);
     }
-    if (d->in_dtype == KDA_F32) { p.nw_pass1 = p.nw_pass2 = 4; }
-    // Launch-shape override for tuning sweeps: KDA_NW=4|8 waves per workgroup (8 only where
-    // 128 columns divide the value width and the augmented width).
-    if (const char* e = getenv("KDA_NW")) {
-        const int nw = atoi(e);
-        const bool ok8 = (d->dv % 128 == 0) && ((d->dv + d->dk) % 128 == 0) && d->in_dtype == KDA_BF16;
-        if (nw == 4 || (nw == 8 && ok8)) p.nw_pass1 = p.nw_pass2 = nw;
-    }
+    if (d->in_dtype == KDA_F32) { p.nw = 4; p.nt = 1; }
     return p;
 }
 
@@ -88,6 +91,9 @@ kda_status check_chunk_desc(const kda_chunk_desc* d) {
     if (d->chunk != kChunk) return KDA_ERR_UNSUPPORTED;
     if ((d->dk != 64 && d->dk != 128) || (d->dv != 64 && d->dv != 128)) return KDA_ERR_UNSUPPORTED;
     if (d->in_dtype == KDA_F32 && d->dk != 64) return KDA_ERR_UNSUPPORTED;
+    // the bf16 kernel addresses one lane's rows with 32-bit buffer offsets
+    if (d->in_dtype == KDA_BF16 && d->T * (d->dk > d->dv ? d->dk : d->dv) * 4 >= ((int64_t)1 << 31))
+        return KDA_ERR_UNSUPPORTED;
     // element counts must fit comfortably in 64-bit byte offsets
     const double elems = (double)d->B * (double)d->H * (double)(d->T > 0 ? d->T : 1) * (double)(d->dk + d->dv);
     if (elems > 1e17) return KDA_ERR_INVALID_ARG;
@@ -171,19 +177,18 @@ kda_status kda_chunk_fwd(const kda_chunk_desc* d, const void* q, const void* k, 
     a.ws_pair = plan.ws_bytes ? ws : nullptr;
     a.ws_entry = plan.ws_bytes ? ws + (size_t)lanes * plan.nseg * d->dk * (d->dv + d->dk) : nullptr;
 
+    a.nw = plan.nw;
+    a.nt = plan.nt;
     if (plan.nseg == 1) {
-        a.nw = plan.nw_pass1;
         a.fin_seg_lo = 0; a.fin_nseg = 1; a.sum_seg_lo = 0; a.sum_nseg = 0;
         return kda::launch_chunk(a, st) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
     }
     // pass 1: segment 0 from the known entry state; summaries of the middle segments
-    a.nw = plan.nw_pass1;
     a.fin_seg_lo = 0; a.fin_nseg = 1; a.sum_seg_lo = 1; a.sum_nseg = plan.nseg - 2;
     if (kda::launch_chunk(a, st) != hipSuccess) return KDA_ERR_HIP;
     // exact entry state of every later segment
     if (kda::launch_segment_scan(a, st) != hipSuccess) return KDA_ERR_HIP;
     // pass 2: every later segment from its exact entry state
-    a.nw = plan.nw_pass2;
     a.fin_seg_lo = 1; a.fin_nseg = plan.nseg - 1; a.sum_seg_lo = 0; a.sum_nseg = 0;
     return kda::launch_chunk(a, st) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }

@@ -1,4 +1,5 @@
-// KDA chunkwise prefill for gfx950: fused chunk loop, segment summaries, segment scan.
+// KDA chunkwise prefill for gfx950: generic fused chunk loop (used for fp32 inputs), segment
+// scan, state copy. bf16 inputs use the register-resident kernel in kda_prefill_bf16.hip.
 //
 // Mathematics (Kimi K3 reading notes, liuzhao09.github.io/papers/kimi-k3.html, section 2.2,
 // chunk equations; the pieces the page leaves unprinted are derived by unrolling the
@@ -474,19 +475,10 @@ static hipError_t launch_t(const ChunkLaunch& a, hipStream_t st) {
     return hipGetLastError();
 }
 
-template <typename TOut>
-static hipError_t launch_o(const ChunkLaunch& a, hipStream_t st) {
-    if (!a.in_bf16) return launch_t<OpF32, float, TOut, 64, 4>(a, st);  // fp32 path: dk = 64
-    if (a.dk == 128) {
-        if (a.nw == 8) return launch_t<OpBF16, bf16_t, TOut, 128, 8>(a, st);
-        return launch_t<OpBF16, bf16_t, TOut, 128, 4>(a, st);
-    }
-    if (a.nw == 8) return launch_t<OpBF16, bf16_t, TOut, 64, 8>(a, st);
-    return launch_t<OpBF16, bf16_t, TOut, 64, 4>(a, st);
-}
-
 hipError_t launch_chunk(const ChunkLaunch& a, hipStream_t st) {
-    return a.out_bf16 ? launch_o<bf16_t>(a, st) : launch_o<float>(a, st);
+    if (a.in_bf16) return launch_prefill_bf16(a, st);
+    // fp32 path (dk = 64): the generic kernel on fp32 MFMA
+    return a.out_bf16 ? launch_t<OpF32, float, bf16_t, 64, 4>(a, st) : launch_t<OpF32, float, float, 64, 4>(a, st);
 }
 
 hipError_t launch_segment_scan(const ChunkLaunch& a, hipStream_t st) {

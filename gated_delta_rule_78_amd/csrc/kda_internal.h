@@ -20,7 +20,8 @@ struct DecodeArgs {
 struct ChunkLaunch {
     int64_t lanes, T, dk, dv;
     bool in_bf16, out_bf16;
-    int nw;                 // waves per workgroup (16 value columns per wave)
+    int nw;                 // waves per workgroup
+    int nt;                 // 16-column state tiles per wave (bf16 kernel: 1 or 2)
     int nseg;               // segments per lane
     int64_t chunks_per_seg;
     int fin_seg_lo, fin_nseg;   // FINISH segments [fin_seg_lo, fin_seg_lo + fin_nseg)
@@ -35,6 +36,8 @@ struct ChunkLaunch {
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st);
 hipError_t launch_chunk(const ChunkLaunch& a, hipStream_t st);
+// bf16-input prefill (register-resident state path), called by launch_chunk.
+hipError_t launch_prefill_bf16(const ChunkLaunch& a, hipStream_t st);
 // entry_{s+1} = S~_s + M_s entry_s for s in [1, nseg-1), entry_1 already stored.
 hipError_t launch_segment_scan(const ChunkLaunch& a, hipStream_t st);
 // dst[i] = src ? src[i] : 0 for n floats (graph-capture safe replacement for memcpy/memset).

@@ -57,7 +57,8 @@ typedef enum kda_dtype {
 typedef struct kda_chunk_desc {
     int64_t B;          /* batch, >= 1                                                   */
     int64_t H;          /* heads, >= 1                                                   */
-    int64_t T;          /* tokens per lane, >= 0 (any value; a ragged last chunk is fine) */
+    int64_t T;          /* tokens per lane, >= 0; a ragged last chunk is fine; bf16 inputs
+                           need T * max(dk,dv) * 4 < 2^31 (T < 4,194,304 at d = 128)     */
     int64_t dk;         /* key dimension: 64 or 128                                      */
     int64_t dv;         /* value dimension: 64 or 128                                    */
     int32_t chunk;      /* chunk length C: must be 64                                    */
