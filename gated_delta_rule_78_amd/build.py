@@ -12,12 +12,15 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libkda.so")
-SOURCES = ["kda_abi.cpp", "kda_decode.hip", "kda_chunk.hip", "kda_prefill_bf16.hip"]
+SOURCES = ["kda_abi.cpp", "kda_decode.hip", "kda_chunk.hip", "kda_intra.hip", "kda_inter.hip", "kda_scan.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 COMMON = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
           # Packed fp32 arithmetic (v_pk_*_f32) stays off in all device code.
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          # MFMA results in architectural VGPRs: the state accumulators are also read by VALU
+          # code every chunk, and the AGPR form costs a v_accvgpr move per such read.
+          "-mllvm", "-amdgpu-mfma-vgpr-form",
           "-I", os.path.join(ROOT, "include"), "-I", CSRC]
 
 

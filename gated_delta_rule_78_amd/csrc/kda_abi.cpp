@@ -8,6 +8,7 @@
 #include <string.h>
 
 #include "kda_internal.h"
+#include "kda_record.h"
 
 namespace {
 
@@ -28,58 +29,58 @@ bool overlaps(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi && a.hi > a.
 bool valid_dtype(int32_t d) { return d == KDA_F32 || d == KDA_BF16; }
 int64_t elem_bytes(int32_t d) { return d == KDA_BF16 ? 2 : 4; }
 
-// Segments per lane and chunks per segment for a prefill call.
+// Segments per lane, chunks per segment and workspace of a prefill call.
 struct Plan {
     int nseg;
-    int64_t chunks_per_seg;
-    int nw, nt;  // waves per workgroup, 16-column state tiles per wave
+    int64_t nchunks, chunks_per_seg;
+    size_t rec_bytes;    // intra-chunk records (bf16 path): [lanes][nchunks]
+    size_t pair_bytes;   // affine pairs [lanes][nseg][dk][dv + dk] (nseg > 1)
+    size_t entry_bytes;  // entry states [lanes][nseg][dk][dv] (nseg > 1)
     size_t ws_bytes;
 };
 
-// Workgroup shape: 128 state columns per workgroup (4 waves x 2 tiles) wherever 128 divides
-// both the value width and the augmented width, else 4 waves x 1 tile (64 columns).
-void pick_shape(const kda_chunk_desc* d, int* nw, int* nt) {
-    const bool w128 = (d->dv % 128 == 0) && ((d->dv + d->dk) % 128 == 0) && d->dk == 128;
-    // dk = dv = 128: eight waves, one 16-column state tile each (measured faster than four
-    // waves holding two tiles: more waves hide the LDS and exp latency of the chunk prologue).
-    *nw = w128 ? 8 : 4;
-    *nt = 1;
-    // Launch-shape override for tuning sweeps: KDA_NW=8 (8 waves x 1 tile), 4 (4 x 1) or 4x2.
-    if (const char* e = getenv("KDA_NW")) {
-        if (!strcmp(e, "8") && w128) { *nw = 8; *nt = 1; }
-        else if (!strcmp(e, "4")) { *nw = 4; *nt = 1; }
-        else if (!strcmp(e, "4x2") && w128) { *nw = 4; *nt = 2; }
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Sequence split of the bf16 state pass. One state-pass workgroup occupies a compute unit; with
+// n segments, pass 1 runs segment 0 plus n - 2 summaries per lane, pass 2 the n - 1 later
+// segments, each pass taking chunks_per_seg steps per round of kTargetBlocks workgroups. Pick the
+// n with the fewest sequential chunk steps (the segment scan adds about two per segment).
+int64_t auto_segments(int64_t lanes, int64_t nchunks) {
+    int64_t best = 1;
+    int64_t best_cost = nchunks * ceil_div(lanes, kTargetBlocks);
+    const int64_t nmax = nchunks / 4 < 64 ? nchunks / 4 : 64;
+    for (int64_t n = 3; n <= nmax; ++n) {
+        const int64_t cps = ceil_div(nchunks, n);
+        const int64_t nn = ceil_div(nchunks, cps);
+        if (nn < 3) continue;
+        const int64_t rounds = ceil_div(lanes * (nn - 1), kTargetBlocks);
+        const int64_t cost = cps * 2 * rounds + 2 * (nn - 2);
+        if (cost < best_cost) { best_cost = cost; best = nn; }
     }
+    return best;
 }
 
 Plan make_plan(const kda_chunk_desc* d) {
     Plan p{};
     const int64_t lanes = d->B * d->H;
     const int64_t nchunks = (d->T + kChunk - 1) / kChunk;
+    p.nchunks = nchunks;
     int64_t nseg = 1;
-    if (d->segments > 0) {
-        nseg = d->segments;
-    } else if (d->in_dtype == KDA_BF16 && lanes < kTargetBlocks && nchunks >= 16) {
-        // Too few lanes to fill the chip: split each sequence into segments (at least 8 chunks
-        // each) so that lanes x segments is about one workgroup per compute unit.
-        nseg = kTargetBlocks / lanes;
-        if (nseg > nchunks / 8) nseg = nchunks / 8;
-        if (nseg < 1) nseg = 1;
-    }
+    if (d->in_dtype == KDA_BF16 && nchunks > 0) nseg = d->segments > 0 ? d->segments : auto_segments(lanes, nchunks);
     if (nseg > nchunks) nseg = nchunks > 0 ? nchunks : 1;
-    if (d->in_dtype == KDA_F32) nseg = 1;  // the fp32 path runs one pass
-    int64_t cps = nchunks > 0 ? (nchunks + nseg - 1) / nseg : 1;
+    int64_t cps = nchunks > 0 ? ceil_div(nchunks, nseg) : 1;
     if (cps < 1) cps = 1;
-    nseg = nchunks > 0 ? (nchunks + cps - 1) / cps : 1;  // no empty segment
+    nseg = nchunks > 0 ? ceil_div(nchunks, cps) : 1;  // no empty segment
     p.nseg = (int)nseg;
     p.chunks_per_seg = cps;
-    pick_shape(d, &p.nw, &p.nt);
-    if (nseg == 1) {
-        p.ws_bytes = 0;
-    } else {
-        p.ws_bytes = (size_t)lanes * (size_t)nseg * (size_t)d->dk * (size_t)(2 * d->dv + d->dk) * sizeof(float);
+    if (d->in_dtype == KDA_BF16 && nchunks > 0) {
+        p.rec_bytes = (size_t)lanes * (size_t)nchunks * (size_t)kda::record_bytes(d->dk, d->dv);
+        if (nseg > 1) {
+            p.pair_bytes = (size_t)lanes * (size_t)nseg * (size_t)(d->dk * (d->dv + d->dk)) * sizeof(float);
+            p.entry_bytes = (size_t)lanes * (size_t)nseg * (size_t)(d->dk * d->dv) * sizeof(float);
+        }
     }
-    if (d->in_dtype == KDA_F32) { p.nw = 4; p.nt = 1; }
+    p.ws_bytes = p.rec_bytes + p.pair_bytes + p.entry_bytes;
     return p;
 }
 
@@ -169,28 +170,40 @@ kda_status kda_chunk_fwd(const kda_chunk_desc* d, const void* q, const void* k, 
 
     kda::ChunkLaunch a{};
     a.lanes = lanes; a.T = d->T; a.dk = d->dk; a.dv = d->dv;
+    a.nchunks = plan.nchunks;
     a.in_bf16 = d->in_dtype == KDA_BF16; a.out_bf16 = d->out_dtype == KDA_BF16;
     a.nseg = plan.nseg; a.chunks_per_seg = plan.chunks_per_seg;
     a.q = q; a.k = k; a.v = v; a.la = log_alpha; a.beta = beta;
     a.S0 = S0; a.o = o; a.S_T = S_T;
-    float* ws = static_cast<float*>(workspace);
-    a.ws_pair = plan.ws_bytes ? ws : nullptr;
-    a.ws_entry = plan.ws_bytes ? ws + (size_t)lanes * plan.nseg * d->dk * (d->dv + d->dk) : nullptr;
-
-    a.nw = plan.nw;
-    a.nt = plan.nt;
-    if (plan.nseg == 1) {
+    if (!a.in_bf16) {
         a.fin_seg_lo = 0; a.fin_nseg = 1; a.sum_seg_lo = 0; a.sum_nseg = 0;
         return kda::launch_chunk(a, st) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
     }
+
+    // bf16: records of every chunk (state independent, fully parallel) ...
+    unsigned char* ws = static_cast<unsigned char*>(workspace);
+    kda::IntraArgs ia{};
+    ia.lanes = lanes; ia.T = d->T; ia.nchunks = plan.nchunks; ia.dk = d->dk; ia.dv = d->dv;
+    ia.q = q; ia.k = k; ia.v = v; ia.la = log_alpha; ia.beta = beta;
+    ia.rec = ws;
+    if (kda::launch_intra(ia, st) != hipSuccess) return KDA_ERR_HIP;
+    a.rec = ws;
+    a.ws_pair = plan.pair_bytes ? reinterpret_cast<float*>(ws + plan.rec_bytes) : nullptr;
+    a.ws_entry = plan.entry_bytes ? reinterpret_cast<float*>(ws + plan.rec_bytes + plan.pair_bytes) : nullptr;
+
+    // ... then the sequential state pass
+    if (plan.nseg == 1) {
+        a.fin_seg_lo = 0; a.fin_nseg = 1; a.sum_seg_lo = 0; a.sum_nseg = 0;
+        return kda::launch_inter(a, st) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+    }
     // pass 1: segment 0 from the known entry state; summaries of the middle segments
     a.fin_seg_lo = 0; a.fin_nseg = 1; a.sum_seg_lo = 1; a.sum_nseg = plan.nseg - 2;
-    if (kda::launch_chunk(a, st) != hipSuccess) return KDA_ERR_HIP;
+    if (kda::launch_inter(a, st) != hipSuccess) return KDA_ERR_HIP;
     // exact entry state of every later segment
     if (kda::launch_segment_scan(a, st) != hipSuccess) return KDA_ERR_HIP;
     // pass 2: every later segment from its exact entry state
     a.fin_seg_lo = 1; a.fin_nseg = plan.nseg - 1; a.sum_seg_lo = 0; a.sum_nseg = 0;
-    return kda::launch_chunk(a, st) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+    return kda::launch_inter(a, st) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
 kda_status kda_decode_step(const kda_decode_desc* d, const void* q, const void* k, const void* v,

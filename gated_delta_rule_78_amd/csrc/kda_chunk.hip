@@ -420,47 +420,6 @@ __global__ __launch_bounds__(NW * 64) void chunk_kernel(ChunkLaunch p) {
     }
 }
 
-// Exact entry states: entry_{s+1} = S~_s + M_s entry_s for s = 1 .. nseg-2 (entry_1 was written by
-// the FINISH pass of segment 0). One workgroup per (lane, 16 value columns), fp32 throughout.
-template <int DK>
-__global__ __launch_bounds__(256) void segment_scan_kernel(ChunkLaunch p) {
-    __shared__ float Es[DK][17];
-    const int64_t DV = p.dv;
-    const int ncb = (int)(DV / 16);
-    const int64_t lane = blockIdx.x / ncb;
-    const int cb = blockIdx.x % ncb;
-    const int n = threadIdx.x & 15;
-    const int cr = threadIdx.x >> 4;
-    constexpr int RPT = DK / 16;
-    const int64_t LDP = DV + DK;
-    for (int i = 0; i < RPT; ++i) {
-        const int c = cr + 16 * i;
-        Es[c][n] = p.ws_entry[((lane * p.nseg + 1) * DK + c) * DV + 16 * cb + n];
-    }
-    for (int s = 1; s + 1 < p.nseg; ++s) {
-        __syncthreads();
-        const float* P = p.ws_pair + (lane * p.nseg + s) * DK * LDP;
-        float out[RPT];
-        for (int i = 0; i < RPT; ++i) {
-            const int c = cr + 16 * i;
-            const float* Prow = P + c * LDP;
-            float acc = Prow[16 * cb + n];
-            for (int m = 0; m < DK; m += 4) {
-                const float4 mr = *reinterpret_cast<const float4*>(Prow + DV + m);
-                acc += mr.x * Es[m][n] + mr.y * Es[m + 1][n] + mr.z * Es[m + 2][n] + mr.w * Es[m + 3][n];
-            }
-            out[i] = acc;
-        }
-        __syncthreads();
-        float* dst = p.ws_entry + (lane * p.nseg + s + 1) * DK * DV;
-        for (int i = 0; i < RPT; ++i) {
-            const int c = cr + 16 * i;
-            Es[c][n] = out[i];
-            dst[(int64_t)c * DV + 16 * cb + n] = out[i];
-        }
-    }
-}
-
 __global__ void copy_or_zero_kernel(float* dst, const float* src, int64_t n) {
     for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
         dst[i] = src ? src[i] : 0.f;
@@ -476,17 +435,8 @@ static hipError_t launch_t(const ChunkLaunch& a, hipStream_t st) {
 }
 
 hipError_t launch_chunk(const ChunkLaunch& a, hipStream_t st) {
-    if (a.in_bf16) return launch_prefill_bf16(a, st);
     // fp32 path (dk = 64): the generic kernel on fp32 MFMA
     return a.out_bf16 ? launch_t<OpF32, float, bf16_t, 64, 4>(a, st) : launch_t<OpF32, float, float, 64, 4>(a, st);
-}
-
-hipError_t launch_segment_scan(const ChunkLaunch& a, hipStream_t st) {
-    if (a.nseg <= 2) return hipSuccess;
-    const int64_t blocks = a.lanes * (a.dv / 16);
-    if (a.dk == 128) hipLaunchKernelGGL(segment_scan_kernel<128>, dim3((unsigned)blocks), dim3(256), 0, st, a);
-    else hipLaunchKernelGGL(segment_scan_kernel<64>, dim3((unsigned)blocks), dim3(256), 0, st, a);
-    return hipGetLastError();
 }
 
 hipError_t launch_copy_or_zero(float* dst, const float* src, int64_t n, hipStream_t st) {

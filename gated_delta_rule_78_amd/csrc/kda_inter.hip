@@ -1,0 +1,302 @@
+// KDA inter-chunk state pass for gfx950: the sequential part of chunkwise prefill (Kimi K3
+// reading notes, liuzhao09.github.io/papers/kimi-k3.html, section 2.2 chunk equations; section
+// 2.5 affine pair for the sequence split). For each chunk of a lane, with the chunk's record
+// (kda_record.h) and entry state S:
+//   V~ = U - W S,   O = Q~ S + A_qk V~,   S <- Diag(gamma_C) S + K-^T V~
+// (the record holds -W, so V~ is one MFMA accumulation started from U).
+//
+// One workgroup (4 waves) per (lane, segment) walks the segment's chunks in order. The fp32 state
+// stays in MFMA accumulators: wave w owns 16*NT state columns, rows = key channels. Records
+// stream HBM -> LDS with direct-to-LDS buffer loads (each wave a quarter of the blocks), double
+// buffered one chunk ahead; every operand read from LDS is one conflict-free 16-byte fragment
+// read. The chunk loop is bound by that record stream; the stores of a chunk's output are issued
+// one chunk late, so that the wait for the next record copies does not also wait for them.
+//
+// Roles (one launch may mix them, see ChunkLaunch):
+//   FINISH  columns [0, dv): exact entry state in, o written, exit state stored as asked.
+//   SUMMARY columns [0, dv + dk) = [S~ | M] with entry [0 | I] and U = 0 on the M columns: the
+//           affine pair S_out = S~ + M S_in of the segment, no o.
+#include "kda_internal.h"
+#include "kda_mfma.h"
+#include "kda_record.h"
+
+namespace kda {
+namespace {
+
+constexpr int kC = 64;
+constexpr int kThreads = 256;
+
+// Four output values in storage form (bf16: 8 bytes; fp32: 16 bytes) and their buffer store.
+__device__ __forceinline__ void store_out(__amdgpu_buffer_rsrc_t r, uint32_t off, f32x4 x, bf16_t*) {
+    typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
+    const u32x2 u = {pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
+    __builtin_amdgcn_raw_buffer_store_b64(u, r, (int)off, 0, 0);
+}
+__device__ __forceinline__ void store_out(__amdgpu_buffer_rsrc_t r, uint32_t off, f32x4 x, float*) {
+    typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), r, (int)off, 0, 0);
+}
+
+template <int DK, int DV>
+struct __align__(16) InterSmem {
+    unsigned char rec[2][RecordLayout<DK, DV>::BYTES];
+};
+
+// Copy this wave's share (blocks w, w + 4, ...) of the blocks of one chunk record that a role
+// reads (FINISH: all; SUMMARY: all but Q~ and A_qk) into an LDS buffer: one direct-to-LDS buffer
+// load per 1 KiB block; the descriptor covers the lane's records, offsets stay scalar. Every wave
+// issues the same count: indices past the end repeat the last block (the same bytes to the same
+// place), which keeps the copy free of branches.
+template <int DK, int DV, bool FIN>
+__device__ __forceinline__ void copy_record(__amdgpu_buffer_rsrc_t rsrc, uint32_t chunk_off, unsigned char* dst, int w, int l) {
+    typedef RecordLayout<DK, DV> R;
+    constexpr int NSKIP = 4 * R::NKS;
+    constexpr int NLOAD = FIN ? R::BLOCKS : R::BLOCKS - NSKIP - 6;
+#pragma unroll
+    for (int i = 0; i < (NLOAD + 3) / 4; ++i) {
+        const int b = w + 4 * i < NLOAD ? w + 4 * i : NLOAD - 1;
+        const int blk = FIN ? b : (b < R::Q ? b : (b < R::Q + 2 * R::NM ? b + NSKIP : b + NSKIP + 6));
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(dst + blk * 1024), 16, (unsigned)(l * 16),
+                                                 chunk_off + (uint32_t)(blk * 1024), 0, 0);
+    }
+}
+
+// One chunk for state tiles G0 .. G0 + NTG - 1 of this wave (columns col0 + 16 nt + l16).
+template <typename TOut, int DK, int DV, int NT, int G0, int NTG, bool FIN>
+__device__ __forceinline__ void chunk_step(const unsigned char* rbuf, f32x4 (&S)[NT][DK / 16], int col0,
+                                           f32x4 (&Opend)[NT][4]) {
+    typedef RecordLayout<DK, DV> R;
+    constexpr int NKS = R::NKS, NM = R::NM, NV = R::NV;
+    const int l = threadIdx.x & 63;
+    const int lq = l >> 4;
+    const unsigned char* rb = rbuf + l * 16;
+#define KDA_FRAG(b) read16(rb + (b) * 1024)
+
+    // V~ = U + (-W) S (rows = tokens 16I + 4lq + r; U = 0 on SUMMARY's M columns) and, for
+    // FINISH, O^T = S^T Q~^T. k steps outer: each step converts its slice of S once and issues
+    // 4 NTG (+ 4 NTG) independent MFMAs.
+    f32x4 Vt[NTG][4], Ot[NTG][4];
+#pragma unroll
+    for (int nt = 0; nt < NTG; ++nt) {
+        const int n = col0 / 16 + G0 + nt;
+        if (FIN || n < NV) {
+            const bf16x8 u0 = KDA_FRAG(R::u(n, 0));
+            const bf16x8 u1 = KDA_FRAG(R::u(n, 1));
+            Vt[nt][0] = unpack4f(lo4(u0)); Vt[nt][1] = unpack4f(hi4(u0));
+            Vt[nt][2] = unpack4f(lo4(u1)); Vt[nt][3] = unpack4f(hi4(u1));
+        } else {
+#pragma unroll
+            for (int I = 0; I < 4; ++I) Vt[nt][I] = kZero4;
+        }
+#pragma unroll
+        for (int I = 0; I < 4; ++I) Ot[nt][I] = kZero4;
+    }
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+        bf16x8 sk[NTG];
+#pragma unroll
+        for (int nt = 0; nt < NTG; ++nt) sk[nt] = cat(cvt4(S[G0 + nt][2 * ks]), cvt4(S[G0 + nt][2 * ks + 1]));
+        bf16x8 wa[4], qb[4];
+#pragma unroll
+        for (int I = 0; I < 4; ++I) {
+            wa[I] = KDA_FRAG(R::w(I, ks));
+            if (FIN) qb[I] = KDA_FRAG(R::q(I, ks));
+        }
+#pragma unroll
+        for (int I = 0; I < 4; ++I)
+#pragma unroll
+            for (int nt = 0; nt < NTG; ++nt) Vt[nt][I] = mma32(wa[I], sk[nt], Vt[nt][I]);
+        if (FIN) {
+#pragma unroll
+            for (int I = 0; I < 4; ++I)
+#pragma unroll
+                for (int nt = 0; nt < NTG; ++nt) Ot[nt][I] = mma32(sk[nt], qb[I], Ot[nt][I]);
+        }
+    }
+    // V~ as K32 B operands over tokens 0..31 (v01) and 32..63 (v23)
+    bf16x8 v01[NTG], v23[NTG];
+#pragma unroll
+    for (int nt = 0; nt < NTG; ++nt) {
+        v01[nt] = cat(cvt4(Vt[nt][0]), cvt4(Vt[nt][1]));
+        v23[nt] = cat(cvt4(Vt[nt][2]), cvt4(Vt[nt][3]));
+    }
+    if (FIN) {
+#pragma unroll
+        for (int I = 0; I < 4; ++I) {
+            const bf16x8 a0 = KDA_FRAG(R::a(I, 0));
+#pragma unroll
+            for (int nt = 0; nt < NTG; ++nt) Ot[nt][I] = mma32(v01[nt], a0, Ot[nt][I]);
+            if (I >= 2) {
+                const bf16x8 a1 = KDA_FRAG(R::a(I, 1));
+#pragma unroll
+                for (int nt = 0; nt < NTG; ++nt) Ot[nt][I] = mma32(v23[nt], a1, Ot[nt][I]);
+            }
+            // O^T tile: rows = columns 4lq + r, column = token 16I + l16 (stored next iteration)
+#pragma unroll
+            for (int nt = 0; nt < NTG; ++nt) Opend[G0 + nt][I] = Ot[nt][I];
+        }
+    }
+    // S <- Diag(gamma_C) S + K-^T V~, in two sweeps of independent MFMAs
+    const float* gam = reinterpret_cast<const float*>(rbuf + R::G * 1024);
+#pragma unroll
+    for (int M = 0; M < NM; ++M) {
+        const f32x4 g4 = *reinterpret_cast<const f32x4*>(&gam[16 * M + 4 * lq]);
+        const bf16x8 k0 = KDA_FRAG(R::k(M, 0));
+#pragma unroll
+        for (int nt = 0; nt < NTG; ++nt) S[G0 + nt][M] = mma32(k0, v01[nt], g4 * S[G0 + nt][M]);
+    }
+#pragma unroll
+    for (int M = 0; M < NM; ++M) {
+        const bf16x8 k1 = KDA_FRAG(R::k(M, 1));
+#pragma unroll
+        for (int nt = 0; nt < NTG; ++nt) S[G0 + nt][M] = mma32(k1, v23[nt], S[G0 + nt][M]);
+    }
+#undef KDA_FRAG
+}
+
+template <typename TOut, int DK, int DV, int NT, bool FIN>
+__device__ __forceinline__ void run_segment(const ChunkLaunch& p, InterSmem<DK, DV>& sm, int64_t lane, int seg) {
+    typedef RecordLayout<DK, DV> R;
+    constexpr int NM = R::NM;
+    constexpr int BYTES = R::BYTES;
+    const int tid = threadIdx.x;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l = tid & 63;
+    const int l16 = l & 15;
+    const int lq = l >> 4;
+    const int64_t DVl = DV;
+
+    const int64_t nchunks = p.nchunks;
+    const int64_t c_begin = (int64_t)seg * p.chunks_per_seg;
+    const int64_t c_end = c_begin + p.chunks_per_seg < nchunks ? c_begin + p.chunks_per_seg : nchunks;
+    const int col0 = w * 16 * NT;   // FINISH: in [0, dv); SUMMARY: in [0, dv + dk)
+
+    // ---- entry state: S[nt][M] holds rows 16M + 4lq + r, column col0 + 16nt + l16 ----------
+    f32x4 S[NT][NM];
+    {
+        if (FIN) {
+            const float* entry = nullptr;
+            if (seg > 0) entry = p.ws_entry + ((lane * p.nseg + seg) * DK) * DVl;
+            else if (p.S0) entry = p.S0 + lane * DK * DVl;
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+                for (int M = 0; M < NM; ++M)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        S[nt][M][r] = entry ? entry[(16 * M + 4 * lq + r) * DVl + col0 + 16 * nt + l16] : 0.f;
+        } else {
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+                const int diag = col0 + 16 * nt + l16 - DV;   // M column -> its unit row
+#pragma unroll
+                for (int M = 0; M < NM; ++M)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) S[nt][M][r] = (16 * M + 4 * lq + r == diag) ? 1.f : 0.f;
+            }
+        }
+    }
+
+    const __amdgpu_buffer_rsrc_t rrec =
+        make_rsrc(p.rec + lane * nchunks * (int64_t)BYTES, (uint32_t)(nchunks * (int64_t)BYTES));
+    const __amdgpu_buffer_rsrc_t ro =
+        make_rsrc(FIN ? (const TOut*)p.o + lane * p.T * DVl : nullptr, FIN ? (uint32_t)(p.T * DVl * sizeof(TOut)) : 0u);
+
+    // Output of the previous chunk, stored one iteration late: vmcnt counts loads and stores
+    // alike, so stores issued right after the wait complete in the shadow of the next chunk
+    // instead of being waited for with its copies.
+    f32x4 Opend[NT][4];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int I = 0; I < 4; ++I) Opend[nt][I] = kZero4;
+
+    if (c_begin < c_end) copy_record<DK, DV, FIN>(rrec, (uint32_t)(c_begin * BYTES), sm.rec[0], w, l);
+    for (int64_t c = c_begin; c < c_end; ++c) {
+        const int buf = (int)((c - c_begin) & 1);
+        __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0): this wave's copies of chunk c landed
+        __syncthreads();                        // ... and everyone's; buffer buf^1 is free again
+        if (FIN && c > c_begin) {
+#pragma unroll
+            for (int I = 0; I < 4; ++I) {
+                const uint32_t row = (uint32_t)((c - 1) * kC + 16 * I + l16);
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt)
+                    store_out(ro, (row * (uint32_t)DV + col0 + 16 * nt + 4 * lq) * (uint32_t)sizeof(TOut), Opend[nt][I],
+                              (TOut*)nullptr);
+            }
+        }
+        if (c + 1 < c_end) copy_record<DK, DV, FIN>(rrec, (uint32_t)((c + 1) * BYTES), sm.rec[buf ^ 1], w, l);
+        chunk_step<TOut, DK, DV, NT, 0, NT, FIN>(sm.rec[buf], S, col0, Opend);
+    }
+    if (FIN && c_begin < c_end) {
+#pragma unroll
+        for (int I = 0; I < 4; ++I) {
+            const uint32_t row = (uint32_t)((c_end - 1) * kC + 16 * I + l16);
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+                store_out(ro, (row * (uint32_t)DV + col0 + 16 * nt + 4 * lq) * (uint32_t)sizeof(TOut), Opend[nt][I],
+                          (TOut*)nullptr);
+        }
+    }
+
+    // ---- exit state --------------------------------------------------------------------------
+    float* dst = nullptr;
+    int64_t ld_dst = DVl;
+    if (!FIN) {
+        dst = p.ws_pair + (lane * p.nseg + seg) * DK * (DVl + DK);
+        ld_dst = DVl + DK;
+    } else if (seg == p.nseg - 1) {
+        dst = p.S_T ? p.S_T + lane * DK * DVl : nullptr;
+    } else if (seg == 0) {
+        dst = p.ws_entry + ((lane * p.nseg + 1) * DK) * DVl;
+    }
+    if (dst) {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+            for (int M = 0; M < NM; ++M)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    dst[(int64_t)(16 * M + 4 * lq + r) * ld_dst + col0 + 16 * nt + l16] = S[nt][M][r];
+    }
+}
+
+template <typename TOut, int DK, int DV>
+__global__ __launch_bounds__(kThreads, 1) void inter_kernel(ChunkLaunch p) {
+    __shared__ InterSmem<DK, DV> sm;
+    const int64_t bid = blockIdx.x;
+    const int64_t n_fin = p.lanes * p.fin_nseg;
+    if (bid < n_fin) {
+        const int64_t lane = uniform64(bid / p.fin_nseg);
+        const int seg = (int)uniform64(p.fin_seg_lo + bid % p.fin_nseg);
+        run_segment<TOut, DK, DV, DV / 64, true>(p, sm, lane, seg);
+    } else {
+        const int64_t b2 = bid - n_fin;
+        const int64_t lane = uniform64(b2 / p.sum_nseg);
+        const int seg = (int)uniform64(p.sum_seg_lo + b2 % p.sum_nseg);
+        run_segment<TOut, DK, DV, (DV + DK) / 64, false>(p, sm, lane, seg);
+    }
+}
+
+template <typename TOut, int DK, int DV>
+hipError_t launch_t(const ChunkLaunch& a, hipStream_t st) {
+    const int64_t blocks = a.lanes * ((int64_t)a.fin_nseg + (int64_t)a.sum_nseg);
+    if (blocks <= 0) return hipSuccess;
+    hipLaunchKernelGGL((inter_kernel<TOut, DK, DV>), dim3((unsigned)blocks), dim3(kThreads), 0, st, a);
+    return hipGetLastError();
+}
+
+template <typename TOut>
+hipError_t launch_o(const ChunkLaunch& a, hipStream_t st) {
+    if (a.dk == 128) return a.dv == 128 ? launch_t<TOut, 128, 128>(a, st) : launch_t<TOut, 128, 64>(a, st);
+    return a.dv == 128 ? launch_t<TOut, 64, 128>(a, st) : launch_t<TOut, 64, 64>(a, st);
+}
+
+}  // namespace
+
+hipError_t launch_inter(const ChunkLaunch& a, hipStream_t st) {
+    return a.out_bf16 ? launch_o<bf16_t>(a, st) : launch_o<float>(a, st);
+}
+
+}  // namespace kda

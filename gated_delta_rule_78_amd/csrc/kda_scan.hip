@@ -1,0 +1,103 @@
+// Segment scan of the sequence split (Kimi K3 reading notes, liuzhao09.github.io/papers/kimi-k3.html,
+// section 2.5: a segment acts on the state as the affine map S_out = S~ + M S_in, and such maps
+// compose associatively). Given entry_1 (the exit state of segment 0) and the pairs (S~_s, M_s)
+// of the middle segments, it forms the exact entry states entry_{s+1} = S~_s + M_s entry_s for
+// s = 1 .. nseg - 2, in fp32.
+//
+// One workgroup (4 waves) per (lane, 16 state columns). The current entry tile (dk x 16) lives in
+// LDS, transposed; each step is a (dk x dk) x (dk x 16) product on the fp32 MFMA (16x16x4): wave w
+// owns dk/64 output row tiles, its A operands (rows of M_s) stream from the workspace one step
+// ahead. Within a lane group the k index runs contiguously (k = (dk/4) lq + j for the j-th MFMA),
+// the same for A and B, so each lane reads its operands as whole 16-byte vectors.
+#include "kda_internal.h"
+#include "kda_mfma.h"
+
+namespace kda {
+namespace {
+
+template <int DK>
+__global__ __launch_bounds__(256) void segment_scan_kernel(ChunkLaunch p) {
+    constexpr int TPW = DK / 64;   // 16-row output tiles per wave
+    constexpr int KJ = DK / 4;     // k values per lane group
+    constexpr int LDE = DK + 4;
+    __shared__ __align__(16) float Et[16][LDE];   // Et[column][row] of the current entry tile
+
+    const int64_t DV = p.dv;
+    const int64_t LDP = DV + DK;
+    const int ncb = (int)(DV / 16);
+    const int64_t lane = uniform64(blockIdx.x / ncb);
+    const int cb = (int)uniform64(blockIdx.x % ncb);
+    const int tid = threadIdx.x;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l = tid & 63;
+    const int l16 = l & 15;
+    const int lq = l >> 4;
+    const int64_t col = 16 * cb + l16;
+    const int nseg = p.nseg;
+
+    const float* e1 = p.ws_entry + (lane * nseg + 1) * DK * DV;
+    for (int i = tid; i < DK * 16; i += 256) Et[i & 15][i >> 4] = e1[(int64_t)(i >> 4) * DV + 16 * cb + (i & 15)];
+
+    // operands of step s: A = rows 16 (TPW w + t) + l16 of M_s, k = KJ lq .. KJ lq + KJ - 1;
+    // st = S~_s at the tile's accumulator positions
+    f32x4 a[TPW][KJ / 4], st[TPW];
+    auto load_step = [&](int s, f32x4 (*aa)[KJ / 4], f32x4* ss) {
+        const float* P = p.ws_pair + (lane * nseg + s) * DK * LDP;
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) {
+            const int row0 = 16 * (TPW * w + t);
+            const float* Arow = P + (int64_t)(row0 + l16) * LDP + DV + KJ * lq;
+#pragma unroll
+            for (int j4 = 0; j4 < KJ / 4; ++j4) aa[t][j4] = *reinterpret_cast<const f32x4*>(Arow + 4 * j4);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) ss[t][r] = P[(int64_t)(row0 + 4 * lq + r) * LDP + col];
+        }
+    };
+    if (nseg > 2) load_step(1, a, st);
+    __syncthreads();
+    for (int s = 1; s + 1 < nseg; ++s) {
+        f32x4 an[TPW][KJ / 4], stn[TPW];
+        if (s + 2 < nseg) load_step(s + 1, an, stn);
+        f32x4 acc[TPW];
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) acc[t] = st[t];
+#pragma unroll
+        for (int j4 = 0; j4 < KJ / 4; ++j4) {
+            const f32x4 b = *reinterpret_cast<const f32x4*>(&Et[l16][KJ * lq + 4 * j4]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+#pragma unroll
+                for (int t = 0; t < TPW; ++t) acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[t][j4][e], b[e], acc[t], 0, 0, 0);
+        }
+        __syncthreads();   // every wave has read the old entry tile
+        float* dst = p.ws_entry + (lane * nseg + s + 1) * DK * DV;
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) {
+            const int row0 = 16 * (TPW * w + t);
+            *reinterpret_cast<f32x4*>(&Et[l16][row0 + 4 * lq]) = acc[t];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) dst[(int64_t)(row0 + 4 * lq + r) * DV + col] = acc[t][r];
+        }
+        __syncthreads();
+        if (s + 2 < nseg) {
+#pragma unroll
+            for (int t = 0; t < TPW; ++t) {
+                st[t] = stn[t];
+#pragma unroll
+                for (int j4 = 0; j4 < KJ / 4; ++j4) a[t][j4] = an[t][j4];
+            }
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_segment_scan(const ChunkLaunch& a, hipStream_t st) {
+    if (a.nseg <= 2) return hipSuccess;
+    const int64_t blocks = a.lanes * (a.dv / 16);
+    if (a.dk == 128) hipLaunchKernelGGL(segment_scan_kernel<128>, dim3((unsigned)blocks), dim3(256), 0, st, a);
+    else hipLaunchKernelGGL(segment_scan_kernel<64>, dim3((unsigned)blocks), dim3(256), 0, st, a);
+    return hipGetLastError();
+}
+
+}  // namespace kda

@@ -79,10 +79,16 @@ typedef struct kda_decode_desc {
 
 /*
  * Bytes of device workspace kda_chunk_fwd needs for `desc` (0 when the call needs none, and
- * 0 for an invalid desc). The workspace holds per-segment affine pairs (M, S~) with
- * S_out = S~ + M S_in and the exact entry state of each segment (section 2.5 of the Kimi K3
- * reading notes: segment transforms compose associatively, and a prefix scan gives every
- * segment its entry state).
+ * 0 for an invalid desc). For bf16 inputs the workspace holds, in this order:
+ *  - one record per 64-token chunk of every (b,h) lane: the chunk's state-independent factors
+ *    W = (I+A_kk)^{-1} Diag(beta) K~, U = (I+A_kk)^{-1} Diag(beta) V, Q~, K- = K gamma_C / Gamma,
+ *    A_qk and gamma_C (the UT transform and decay factors of section 2.2 of the Kimi K3 reading
+ *    notes), (12 dk/32 + 7 + 2 dv/16) KiB per chunk, about 1.1x the bytes of q, k, v and
+ *    log_alpha together;
+ *  - with more than one sequence segment per lane, per-segment affine pairs (M, S~) with
+ *    S_out = S~ + M S_in and the exact entry state of each segment (section 2.5: segment
+ *    transforms compose associatively, and a prefix scan gives every segment its entry state).
+ * The fp32 path needs no workspace.
  */
 size_t kda_chunk_fwd_workspace_bytes(const kda_chunk_desc* desc);
 

@@ -81,16 +81,26 @@ def test_chunk_rejects_bad_pointers(lib):
     assert _chunk(lib, _desc(), S0=S, ST=S + (1 << 28), o=S + 16) == INVALID  # o overlaps S0
 
 
+def record_bytes(dk, dv):
+    """Bytes of one chunk record as include/kda.h documents them: W, Q~ and K- blocks (dk/32 * 4
+    KiB each), six A_qk blocks, U (dv/16 * 2 KiB) and one block of gamma_C."""
+    return (12 * (dk // 32) + 7 + 2 * (dv // 16)) * 1024
+
+
 def test_workspace_query_and_check(lib):
-    lanes, dk, dv = 2, 128, 128
-    d = _desc(B=1, H=lanes, T=64 * 40, seg=4)
+    lanes, dk, dv, nchunks, nseg = 2, 128, 128, 40, 4
+    d = _desc(B=1, H=lanes, T=64 * nchunks, seg=nseg)
     need = lib.kda_chunk_fwd_workspace_bytes(ctypes.byref(d))
-    assert need == lanes * 4 * dk * (2 * dv + dk) * 4
+    assert need == lanes * nchunks * record_bytes(dk, dv) + lanes * nseg * dk * (2 * dv + dk) * 4
     assert _chunk(lib, d) == WORKSPACE
     assert _chunk(lib, d, ws=FAKE + (7 << 30), ws_bytes=need - 1) == WORKSPACE
     assert _chunk(lib, d, ws=FAKE + (7 << 30) + 8, ws_bytes=need) == INVALID   # misaligned workspace
     assert _chunk(lib, d, ws=FAKE + 32, ws_bytes=need) == INVALID              # workspace overlaps q
-    assert lib.kda_chunk_fwd_workspace_bytes(ctypes.byref(_desc(seg=1))) == 0
+    # one segment: records only; a ragged tail counts as a whole chunk
+    one = _desc(B=2, H=3, T=64 * 5 + 1, dk=64, dv=128, seg=1)
+    assert lib.kda_chunk_fwd_workspace_bytes(ctypes.byref(one)) == 6 * 6 * record_bytes(64, 128)
+    assert lib.kda_chunk_fwd_workspace_bytes(ctypes.byref(_desc(ind=0, dk=64, dv=64))) == 0   # fp32 path
+    assert lib.kda_chunk_fwd_workspace_bytes(ctypes.byref(_desc(T=0))) == 0
     assert lib.kda_chunk_fwd_workspace_bytes(ctypes.byref(_desc(dk=96))) == 0
     assert lib.kda_chunk_fwd_workspace_bytes(None) == 0
 
