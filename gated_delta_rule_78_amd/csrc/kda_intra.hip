@@ -2,8 +2,10 @@
 // depend on the recurrent state (Kimi K3 reading notes, liuzhao09.github.io/papers/kimi-k3.html,
 // section 2.2: cumulative decay Gamma, the decay-weighted Gram tiles and the UT transform).
 //
-// One workgroup (4 waves) per (lane, chunk); every chunk of every lane is independent, so the grid
-// is large and the kernel is bound by HBM traffic, not by latency. Output: the chunk's record
+// Every chunk of every lane is independent. A persistent grid of two workgroups (4 waves each) per
+// compute unit walks the (lane, chunk) pairs, loading the next chunk's raw rows into registers
+// while it works on the current one, so the kernel is bound by HBM traffic, not by latency. Input
+// loads are row-contiguous (64 bytes per row per wave). Output: the chunk's record
 // (kda_record.h) in the workspace. Steps, with G = cumsum(log alpha) over the chunk's rows:
 //   1. per wave, 32 key channels: G^T = g^T U (U[s][t] = (s <= t)) on the MFMA, Gamma = exp(G);
 //      Q~ = Q Gamma, K~ = K Gamma, K^ = K / Gamma, K- = K gamma_C / Gamma, all from fp32 factors
@@ -100,24 +102,8 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs p) {
     const int l16 = l & 15;
     const int lq = l >> 4;
 
-    const int64_t c = uniform64(blockIdx.x % p.nchunks);
-    const int64_t lane = uniform64(blockIdx.x / p.nchunks);
     const int64_t T = p.T;
-    unsigned char* rec = p.rec + (lane * p.nchunks + c) * (int64_t)R::BYTES;
-    auto blk = [&](int b) -> unsigned char* { return rec + b * 1024 + l * 16; };
-
-    const bf16_t* qg = (const bf16_t*)p.q + lane * T * DK;
-    const bf16_t* kg = (const bf16_t*)p.k + lane * T * DK;
-    const bf16_t* gg = (const bf16_t*)p.la + lane * T * DK;
-    const bf16_t* vg = (const bf16_t*)p.v + lane * T * DV;
-    const bf16_t* bg = (const bf16_t*)p.beta + lane * T;
-    const __amdgpu_buffer_rsrc_t rq = make_rsrc(qg, (uint32_t)(T * DK * 2));
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kg, (uint32_t)(T * DK * 2));
-    const __amdgpu_buffer_rsrc_t rg = make_rsrc(gg, (uint32_t)(T * DK * 2));
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vg, (uint32_t)(T * DV * 2));
-    const __amdgpu_buffer_rsrc_t rb = make_rsrc(bg, (uint32_t)(T * 2));
-    const uint32_t row0 = (uint32_t)(c * kC);   // rows at or past T read as zeros
-
+    const int64_t total = p.lanes * p.nchunks;
     unsigned char* reg = sm.region[w];
     bf16_t* stA = reinterpret_cast<bf16_t*>(reg);                    // g, then K- (token-major)
     unsigned char* stB = reg + Cfg::STAGE_A;                         // v, then blocks
@@ -128,39 +114,77 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs p) {
     const bool kw = w < NKS;          // this wave prepares key channels 32w .. 32w + 31
     const bool vw = Cfg::has_v(w);    // this wave solves value tiles vt0 .. vt0 + VPW - 1
     const int vc0 = 16 * Cfg::vt0(w);
+    constexpr int LPR = 2 * VPW;      // lanes per row of the value stage load
+    // Lane's 16-byte slice of a q/k row: rows (lq = 0, 1) and (2, 3) then trade halves with one
+    // permlane16 swap per dword pair, which leaves each lane its fragment channels
+    // 32w + 16h + 4lq .. +3 for h = 0, 1.
+    const int qk_off = 8 * (((lq & 1) << 1) | (lq >> 1));
+
+    // Raw inputs of one chunk, loaded one chunk ahead. Rows at or past T read as zeros.
+    uint4 pq[4], pk[4], pg[4], pv[LPR];
+    uint32_t pb = 0;
+#define KDA_INTRA_LOAD(tt)                                                                          \
+    do {                                                                                            \
+        const int64_t c_ = uniform64((tt) % p.nchunks);                                             \
+        const int64_t lane_ = uniform64((tt) / p.nchunks);                                          \
+        const uint32_t r0_ = (uint32_t)(c_ * kC);                                                   \
+        if (kw) {                                                                                   \
+            const __amdgpu_buffer_rsrc_t rq_ = make_rsrc((const bf16_t*)p.q + lane_ * T * DK, (uint32_t)(T * DK * 2)); \
+            const __amdgpu_buffer_rsrc_t rk_ = make_rsrc((const bf16_t*)p.k + lane_ * T * DK, (uint32_t)(T * DK * 2)); \
+            const __amdgpu_buffer_rsrc_t rg_ = make_rsrc((const bf16_t*)p.la + lane_ * T * DK, (uint32_t)(T * DK * 2)); \
+            _Pragma("unroll") for (int I_ = 0; I_ < 4; ++I_) {                                      \
+                const uint32_t o_ = ((r0_ + 16 * I_ + l16) * DK + 32 * w + qk_off) * 2;               \
+                pq[I_] = buf_load16(rq_, o_);                                                       \
+                pk[I_] = buf_load16(rk_, o_);                                                       \
+                pg[I_] = buf_load16(rg_, ((r0_ + 16 * I_ + (l >> 2)) * DK + 32 * w + 8 * (l & 3)) * 2); \
+            }                                                                                       \
+        }                                                                                           \
+        if (vw) {                                                                                   \
+            const __amdgpu_buffer_rsrc_t rv_ = make_rsrc((const bf16_t*)p.v + lane_ * T * DV, (uint32_t)(T * DV * 2)); \
+            _Pragma("unroll") for (int i_ = 0; i_ < LPR; ++i_)                                      \
+                pv[i_] = buf_load16(rv_, ((r0_ + i_ * (64 / LPR) + l / LPR) * DV + vc0 + 8 * (l % LPR)) * 2); \
+        }                                                                                           \
+        if (w == 0) {                                                                               \
+            const __amdgpu_buffer_rsrc_t rb_ = make_rsrc((const bf16_t*)p.beta + lane_ * T, (uint32_t)(T * 2)); \
+            pb = buf_load2(rb_, (r0_ + l) * 2);                                                     \
+        }                                                                                           \
+    } while (0)
+
+    // Persistent: workgroup b takes chunks b, b + gridDim.x, ... of the flattened (lane, chunk)
+    // index, so the loads of the next chunk overlap the Gram tiles and solve of this one.
+    int64_t t = blockIdx.x;
+    if (t < total) KDA_INTRA_LOAD(t);
+    for (; t < total; t += gridDim.x) {
+    const int64_t c = uniform64(t % p.nchunks);
+    const int64_t lane = uniform64(t / p.nchunks);
+    unsigned char* rec = p.rec + (lane * p.nchunks + c) * (int64_t)R::BYTES;
+    auto blk = [&](int b) -> unsigned char* { return rec + b * 1024 + l * 16; };
 
     // ================= phase 1: decay and scaled operands (wave-local) =========================
     i16x4 vacc[VPW][4];     // V rows 16I + 4lq + e, column vc0 + 16j + l16 (accumulator layout)
     i16x4 kacc[2][4];       // K~ rows 16I + 4lq + e, channel 32w + 16h + l16
     {
         uint2 qv[2][4], kv[2][4];
-        uint4 gs[4], vs[2 * VPW];
-        if (kw) {
-#pragma unroll
-            for (int h = 0; h < 2; ++h)
-#pragma unroll
-                for (int I = 0; I < 4; ++I) {
-                    const uint32_t off = ((row0 + 16 * I + l16) * DK + 32 * w + 16 * h + 4 * lq) * 2;
-                    qv[h][I] = buf_load8(rq, off);
-                    kv[h][I] = buf_load8(rk, off);
-                }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) gs[i] = buf_load16(rg, ((row0 + l) * DK + 32 * w + 8 * i) * 2);
-        }
-        if (vw) {
-#pragma unroll
-            for (int i = 0; i < 2 * VPW; ++i) vs[i] = buf_load16(rv, ((row0 + l) * DV + vc0 + 8 * i) * 2);
-        }
-        if (w == 0) sm.beta[l] = __uint_as_float(buf_load2(rb, (row0 + l) * 2) << 16);
-        if (kw) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(&stA[l * LDG + 8 * i]) = gs[i];
-        }
         bf16_t* vst = reinterpret_cast<bf16_t*>(stB);
+        if (kw) {
+#pragma unroll
+            for (int I = 0; I < 4; ++I) {
+                *reinterpret_cast<uint4*>(&stA[(16 * I + (l >> 2)) * LDG + 8 * (l & 3)]) = pg[I];
+                typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
+                const u32x2 sq0 = __builtin_amdgcn_permlane16_swap(pq[I].x, pq[I].z, false, false);
+                const u32x2 sq1 = __builtin_amdgcn_permlane16_swap(pq[I].y, pq[I].w, false, false);
+                const u32x2 sk0 = __builtin_amdgcn_permlane16_swap(pk[I].x, pk[I].z, false, false);
+                const u32x2 sk1 = __builtin_amdgcn_permlane16_swap(pk[I].y, pk[I].w, false, false);
+                qv[0][I] = make_uint2(sq0[0], sq1[0]); qv[1][I] = make_uint2(sq0[1], sq1[1]);
+                kv[0][I] = make_uint2(sk0[0], sk1[0]); kv[1][I] = make_uint2(sk0[1], sk1[1]);
+            }
+        }
         if (vw) {
 #pragma unroll
-            for (int i = 0; i < 2 * VPW; ++i) *reinterpret_cast<uint4*>(&vst[l * LDVS + 8 * i]) = vs[i];
+            for (int i = 0; i < LPR; ++i) *reinterpret_cast<uint4*>(&vst[(i * (64 / LPR) + l / LPR) * LDVS + 8 * (l % LPR)]) = pv[i];
         }
+        if (w == 0) sm.beta[l] = __uint_as_float(pb << 16);
+        if (t + gridDim.x < total) KDA_INTRA_LOAD(t + gridDim.x);
         wave_lds_sync();
         if (vw) {
 #pragma unroll
@@ -170,7 +194,6 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs p) {
                     vacc[j][I] = tr_read(&vst[(16 * I + 4 * lq + (l16 >> 2)) * LDVS + 16 * j + 4 * (l16 & 3)]);
         }
         if (kw) {
-            uint2 qt[2][4], kt[2][4], kh[2][4];
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 bf16x8 ga[2];
@@ -206,24 +229,17 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs p) {
                         oh[r] = kf[r] * igam;
                         ob[r] = oh[r] * gC[r];
                     }
-                    qt[h][I] = __builtin_bit_cast(uint2, cvt4(oq));
-                    kt[h][I] = __builtin_bit_cast(uint2, cvt4(ok));
-                    kh[h][I] = __builtin_bit_cast(uint2, cvt4(oh));
+                    // fragment blocks (I, ks = w): register elements e < 4 come from h = 0, e >= 4
+                    // from h = 1, i.e. bytes 8h .. 8h + 7 of the lane's 16
+                    const i16x4 bq = cvt4(oq);
+                    *reinterpret_cast<i16x4*>(lblk(w, 0, I) + l * 16 + 8 * h) = bq;
+                    *reinterpret_cast<i16x4*>(lblk(w, 1, I) + l * 16 + 8 * h) = cvt4(ok);
+                    *reinterpret_cast<i16x4*>(lblk(w, 2, I) + l * 16 + 8 * h) = cvt4(oh);
+                    *reinterpret_cast<i16x4*>(blk(R::q(I, w)) + 8 * h) = bq;
                     // K- token-major into the g stage columns 16h.. (already consumed above)
                     *reinterpret_cast<uint2*>(&stA[(16 * I + l16) * LDG + 16 * h + 4 * lq]) =
                         __builtin_bit_cast(uint2, cvt4(ob));
                 }
-            }
-            // fragment blocks (I, ks = w): e < 4 from h = 0, e >= 4 from h = 1
-#pragma unroll
-            for (int I = 0; I < 4; ++I) {
-                const uint4 bq = make_uint4(qt[0][I].x, qt[0][I].y, qt[1][I].x, qt[1][I].y);
-                const uint4 bk = make_uint4(kt[0][I].x, kt[0][I].y, kt[1][I].x, kt[1][I].y);
-                const uint4 bh = make_uint4(kh[0][I].x, kh[0][I].y, kh[1][I].x, kh[1][I].y);
-                *reinterpret_cast<uint4*>(lblk(w, 0, I) + l * 16) = bq;
-                *reinterpret_cast<uint4*>(lblk(w, 1, I) + l * 16) = bk;
-                *reinterpret_cast<uint4*>(lblk(w, 2, I) + l * 16) = bh;
-                *reinterpret_cast<uint4*>(blk(R::q(I, w))) = bq;
             }
             wave_lds_sync();
             // K- blocks (M = 2w + h, half): K-[32 half + k(e)][16M + l16]
@@ -372,12 +388,29 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs p) {
             }
         }
     }
+    __syncthreads();   // the next chunk rewrites the stages, beta and the A_kk blocks
+    }
+#undef KDA_INTRA_LOAD
+}
+
+// Resident workgroups for the persistent grid: two per compute unit (the LDS budget).
+int resident_workgroups() {
+    static int cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 512;
+    if (cached[dev] == 0) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+        cached[dev] = 2 * cus;
+    }
+    return cached[dev];
 }
 
 template <int DK, int DV>
 hipError_t launch_dd(const IntraArgs& a, hipStream_t st) {
-    const int64_t blocks = a.lanes * a.nchunks;
+    int64_t blocks = a.lanes * a.nchunks;
     if (blocks <= 0) return hipSuccess;
+    if (blocks > resident_workgroups()) blocks = resident_workgroups();
     hipLaunchKernelGGL((intra_kernel<DK, DV>), dim3((unsigned)blocks), dim3(256), 0, st, a);
     return hipGetLastError();
 }

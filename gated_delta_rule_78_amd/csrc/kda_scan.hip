@@ -6,8 +6,8 @@
 //
 // One workgroup (4 waves) per (lane, 16 state columns). The current entry tile (dk x 16) lives in
 // LDS, transposed; each step is a (dk x dk) x (dk x 16) product on the fp32 MFMA (16x16x4): wave w
-// owns dk/64 output row tiles, its A operands (rows of M_s) stream from the workspace one step
-// ahead. Within a lane group the k index runs contiguously (k = (dk/4) lq + j for the j-th MFMA),
+// owns dk/64 output row tiles, its A operands (rows of M_s) stream from the workspace three
+// steps ahead. Within a lane group the k index runs contiguously (k = (dk/4) lq + j for the j-th MFMA),
 // the same for A and B, so each lane reads its operands as whole 16-byte vectors.
 #include "kda_internal.h"
 #include "kda_mfma.h"
@@ -25,8 +25,20 @@ __global__ __launch_bounds__(256) void segment_scan_kernel(ChunkLaunch p) {
     const int64_t DV = p.dv;
     const int64_t LDP = DV + DK;
     const int ncb = (int)(DV / 16);
-    const int64_t lane = uniform64(blockIdx.x / ncb);
-    const int cb = (int)uniform64(blockIdx.x % ncb);
+    // Workgroups are dealt to the 8 XCDs round-robin by block index. When the lane count allows,
+    // the ncb workgroups of a lane get indices that are equal mod 8, so they share one XCD's L2
+    // and each M_s is read from HBM once per lane.
+    int64_t lane, cb;
+    const int64_t bid = blockIdx.x;
+    if ((p.lanes & 7) == 0) {
+        cb = (bid >> 3) % ncb;
+        lane = (bid / (8 * ncb)) * 8 + (bid & 7);
+    } else {
+        cb = bid % ncb;
+        lane = bid / ncb;
+    }
+    lane = uniform64(lane);
+    cb = uniform64(cb);
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l = tid & 63;
@@ -53,11 +65,14 @@ __global__ __launch_bounds__(256) void segment_scan_kernel(ChunkLaunch p) {
             for (int r = 0; r < 4; ++r) ss[t][r] = P[(int64_t)(row0 + 4 * lq + r) * LDP + col];
         }
     };
+    // Operands three steps ahead: the loads of step s + 3 are in flight while steps s .. s + 2
+    // compute (the chain of a step is short next to a memory round trip).
+    f32x4 a1[TPW][KJ / 4], st1[TPW], a2[TPW][KJ / 4], st2[TPW];
     if (nseg > 2) load_step(1, a, st);
+    if (nseg > 3) load_step(2, a1, st1);
+    if (nseg > 4) load_step(3, a2, st2);
     __syncthreads();
     for (int s = 1; s + 1 < nseg; ++s) {
-        f32x4 an[TPW][KJ / 4], stn[TPW];
-        if (s + 2 < nseg) load_step(s + 1, an, stn);
         f32x4 acc[TPW];
 #pragma unroll
         for (int t = 0; t < TPW; ++t) acc[t] = st[t];
@@ -69,6 +84,14 @@ __global__ __launch_bounds__(256) void segment_scan_kernel(ChunkLaunch p) {
 #pragma unroll
                 for (int t = 0; t < TPW; ++t) acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[t][j4][e], b[e], acc[t], 0, 0, 0);
         }
+        // rotate the prefetched operands and start the loads of step s + 3
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) {
+            st[t] = st1[t]; st1[t] = st2[t];
+#pragma unroll
+            for (int j4 = 0; j4 < KJ / 4; ++j4) { a[t][j4] = a1[t][j4]; a1[t][j4] = a2[t][j4]; }
+        }
+        if (s + 4 < nseg) load_step(s + 3, a2, st2);
         __syncthreads();   // every wave has read the old entry tile
         float* dst = p.ws_entry + (lane * nseg + s + 1) * DK * DV;
 #pragma unroll
@@ -79,14 +102,6 @@ __global__ __launch_bounds__(256) void segment_scan_kernel(ChunkLaunch p) {
             for (int r = 0; r < 4; ++r) dst[(int64_t)(row0 + 4 * lq + r) * DV + col] = acc[t][r];
         }
         __syncthreads();
-        if (s + 2 < nseg) {
-#pragma unroll
-            for (int t = 0; t < TPW; ++t) {
-                st[t] = stn[t];
-#pragma unroll
-                for (int j4 = 0; j4 < KJ / 4; ++j4) a[t][j4] = an[t][j4];
-            }
-        }
     }
 }
 
