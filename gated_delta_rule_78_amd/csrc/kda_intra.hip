@@ -4,16 +4,25 @@
 //
 // Every chunk of every lane is independent. A persistent grid of two workgroups (4 waves each) per
 // compute unit walks the (lane, chunk) pairs, loading the next chunk's raw rows into registers
-// while it works on the current one, so the kernel is bound by HBM traffic, not by latency. Input
+// while it solves the current one (and while the other workgroup on the compute unit runs), so
+// the kernel is bound by HBM traffic, not by latency. Input
 // loads are row-contiguous (64 bytes per row per wave). Output: the chunk's record
 // (kda_record.h) in the workspace. Steps, with G = cumsum(log alpha) over the chunk's rows:
-//   1. per wave, 32 key channels: G^T = g^T U (U[s][t] = (s <= t)) on the MFMA, Gamma = exp(G);
-//      Q~ = Q Gamma, K~ = K Gamma, K^ = K / Gamma, K- = K gamma_C / Gamma, all from fp32 factors
-//      rounded once to bf16. Q~ and K- go straight to the record; Q~, K~, K^ go to LDS as
-//      fragment blocks.
-//   2. Gram tiles from the LDS blocks: the diagonal blocks of A_kk = Diag(beta) StrictTril(K~K^^T)
-//      in fp32 (wave 0, which then inverts I + A_kk's four 16x16 diagonal blocks by substitution),
-//      its off-diagonal blocks in bf16 (wave 1) and A_qk = Tril(Q~K^^T) into the record (waves 2-3).
+//   1. per wave, 32 key channels: G^T = g^T U (U[s][t] = (s <= t)) on the MFMA. Decay factors are
+//      taken against reference points so that none exceeds e^80 over the whole domain
+//      log alpha in [-5, 0] (decay lower-bound equation of section 2.2, with the 16-token
+//      sub-tiles of Figure 3): for the Gram tiles, relative to the start of each 16-token block,
+//      G_ref(I) = G at token 16I - 1, i.e. Q~_I = Q e^{G - G_ref(I)}, K~_I = K e^{G - G_ref(I)}
+//      (<= 1) and K^_I = K e^{G_ref(I) - G} (<= e^{16*5}); for the record, relative to the chunk
+//      start: Q~ = Q e^{G}, K~ = K e^{G} and K- = K e^{G_C - G} (all <= 1). Factors are fp32,
+//      rounded once to bf16. Q~ and K- go to the record; the block-relative Q~, K~, K^ go to LDS
+//      as fragment blocks.
+//   2. Gram tiles from the LDS blocks. A diagonal 16x16 block uses one reference point; an
+//      off-diagonal block (I > J) rescales K^_J channel-wise by f_IJ = e^{G_ref(I) - G_ref(J)}
+//      (<= 1). The diagonal blocks of A_kk = Diag(beta) StrictTril(K~K^^T) are formed in fp32
+//      (wave 0, which then inverts I + A_kk's four 16x16 diagonal blocks by substitution); waves
+//      1-3 take two off-diagonal block pairs each, rescaling K^_J once for both the A_kk block (bf16,
+//      to LDS) and the A_qk = Tril(Q~K^^T) block (to the record), then the diagonal A_qk blocks.
 //   3. blocked forward substitution (I + A_kk) [W | U] = Diag(beta) [K~ | V] on the MFMA, 16
 //      columns per tile, right-hand sides and results in registers; U goes to the record, -W is
 //      transposed through LDS into fragment order.
@@ -49,17 +58,35 @@ struct SolveOps {
 // (I + A_kk) X = Diag(beta) R for one 16-column tile; R and X in accumulator layout (rows
 // 16I + 4lq + r). X_I = T_I (beta R_I - sum_{J<I} A_IJ X_J). Products of different MFMA shapes
 // go to separate accumulators and are combined on the VALU.
-__device__ __forceinline__ void ut_solve(const SolveOps& o, i16x4 r0, i16x4 r1, i16x4 r2, i16x4 r3,
+__device__ __forceinline__ void ut_solve(const SolveOps& o, f32x4 r0, f32x4 r1, f32x4 r2, f32x4 r3,
                                          f32x4& X0, f32x4& X1, f32x4& X2, f32x4& X3) {
-    X0 = mma16(o.t0, cvt4(o.b0 * unpack4f(r0)), kZero4);
+    X0 = mma16(o.t0, cvt4(o.b0 * r0), kZero4);
     const i16x4 x0 = cvt4(X0);
-    const f32x4 y1 = o.b1 * unpack4f(r1) - mma16(o.a10, x0, kZero4);
+    const f32x4 y1 = o.b1 * r1 - mma16(o.a10, x0, kZero4);
     X1 = mma16(o.t1, cvt4(y1), kZero4);
     const bf16x8 x01 = cat(x0, cvt4(X1));
-    const f32x4 y2 = o.b2 * unpack4f(r2) - mma32(o.a2, x01, kZero4);
+    const f32x4 y2 = o.b2 * r2 - mma32(o.a2, x01, kZero4);
     X2 = mma16(o.t2, cvt4(y2), kZero4);
-    const f32x4 y3 = o.b3 * unpack4f(r3) - mma32(o.a3, x01, kZero4) - mma16(o.a32, cvt4(X2), kZero4);
+    const f32x4 y3 = o.b3 * r3 - mma32(o.a3, x01, kZero4) - mma16(o.a32, cvt4(X2), kZero4);
     X3 = mma16(o.t3, cvt4(y3), kZero4);
+}
+
+// Make a loaded value "used" at this point: the wait for its load is placed here, not at its
+// real use. vmcnt counts loads and stores in issue order, so waiting for a prefetch at the top of
+// the next chunk would also wait for every record store issued after it.
+__device__ __forceinline__ void pin(uint4& v) { asm volatile("" : "+v"(v.x), "+v"(v.y), "+v"(v.z), "+v"(v.w)); }
+__device__ __forceinline__ void pin(uint32_t& v) { asm volatile("" : "+v"(v)); }
+
+// Pair index of an off-diagonal block (I > J): (1,0) (2,0) (2,1) (3,0) (3,1) (3,2).
+__host__ __device__ constexpr int pair_index(int I, int J) { return I * (I - 1) / 2 + J; }
+
+// A K32 operand fragment of K^ (block J) scaled channel-wise by f_IJ (channels of the fragment:
+// 32ks + 16(e/4) + 4lq + e%4), re-rounded to bf16: the reference point moves from block J's start
+// to block I's start, and every factor stays <= 1.
+__device__ __forceinline__ bf16x8 scale_frag(bf16x8 a, const bf16_t* f, int ks, int lq) {
+    const f32x4 f0 = unpack4f(read8(f + 32 * ks + 4 * lq));
+    const f32x4 f1 = unpack4f(read8(f + 32 * ks + 16 + 4 * lq));
+    return cat(cvt4(unpack4f(lo4(a)) * f0), cvt4(unpack4f(hi4(a)) * f1));
 }
 
 template <int DK, int DV>
@@ -87,6 +114,7 @@ struct __align__(16) IntraSmem {
     bf16_t akk[6][256];         // off-diagonal blocks (I, J), I > J, as K16 A fragments
     bf16_t tinv[4][16 * 24];    // (I + A_kk,II)^{-1}, row-major, 24-element rows
     float beta[kC];
+    bf16_t fij[6][DK];          // exp(G_ref(I) - G_ref(J)) per channel for the pairs I > J
 };
 
 template <int DK, int DV>
@@ -111,7 +139,7 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs p) {
         return sm.region[ks] + Cfg::STAGE_A + (X * 4 + I) * 1024;
     };
 
-    const bool kw = w < NKS;          // this wave prepares key channels 32w .. 32w + 31
+    const bool kw = NKS == 4 || w < NKS;   // this wave prepares key channels 32w .. 32w + 31
     const bool vw = Cfg::has_v(w);    // this wave solves value tiles vt0 .. vt0 + VPW - 1
     const int vc0 = 16 * Cfg::vt0(w);
     constexpr int LPR = 2 * VPW;      // lanes per row of the value stage load
@@ -125,13 +153,15 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs p) {
     uint32_t pb = 0;
 #define KDA_INTRA_LOAD(tt)                                                                          \
     do {                                                                                            \
-        const int64_t c_ = uniform64((tt) % p.nchunks);                                             \
-        const int64_t lane_ = uniform64((tt) / p.nchunks);                                          \
+        const bool ok_ = (tt) < total;   /* past the end: empty descriptors, zeros, no traffic */   \
+        const int64_t c_ = ok_ ? uniform64((tt) % p.nchunks) : 0;                                   \
+        const int64_t lane_ = ok_ ? uniform64((tt) / p.nchunks) : 0;                                \
         const uint32_t r0_ = (uint32_t)(c_ * kC);                                                   \
+        const uint32_t nk_ = ok_ ? (uint32_t)(T * DK * 2) : 0u, nv_ = ok_ ? (uint32_t)(T * DV * 2) : 0u; \
         if (kw) {                                                                                   \
-            const __amdgpu_buffer_rsrc_t rq_ = make_rsrc((const bf16_t*)p.q + lane_ * T * DK, (uint32_t)(T * DK * 2)); \
-            const __amdgpu_buffer_rsrc_t rk_ = make_rsrc((const bf16_t*)p.k + lane_ * T * DK, (uint32_t)(T * DK * 2)); \
-            const __amdgpu_buffer_rsrc_t rg_ = make_rsrc((const bf16_t*)p.la + lane_ * T * DK, (uint32_t)(T * DK * 2)); \
+            const __amdgpu_buffer_rsrc_t rq_ = make_rsrc((const bf16_t*)p.q + lane_ * T * DK, nk_);   \
+            const __amdgpu_buffer_rsrc_t rk_ = make_rsrc((const bf16_t*)p.k + lane_ * T * DK, nk_);   \
+            const __amdgpu_buffer_rsrc_t rg_ = make_rsrc((const bf16_t*)p.la + lane_ * T * DK, nk_);  \
             _Pragma("unroll") for (int I_ = 0; I_ < 4; ++I_) {                                      \
                 const uint32_t o_ = ((r0_ + 16 * I_ + l16) * DK + 32 * w + qk_off) * 2;               \
                 pq[I_] = buf_load16(rq_, o_);                                                       \
@@ -140,12 +170,12 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs p) {
             }                                                                                       \
         }                                                                                           \
         if (vw) {                                                                                   \
-            const __amdgpu_buffer_rsrc_t rv_ = make_rsrc((const bf16_t*)p.v + lane_ * T * DV, (uint32_t)(T * DV * 2)); \
+            const __amdgpu_buffer_rsrc_t rv_ = make_rsrc((const bf16_t*)p.v + lane_ * T * DV, nv_);   \
             _Pragma("unroll") for (int i_ = 0; i_ < LPR; ++i_)                                      \
                 pv[i_] = buf_load16(rv_, ((r0_ + i_ * (64 / LPR) + l / LPR) * DV + vc0 + 8 * (l % LPR)) * 2); \
         }                                                                                           \
         if (w == 0) {                                                                               \
-            const __amdgpu_buffer_rsrc_t rb_ = make_rsrc((const bf16_t*)p.beta + lane_ * T, (uint32_t)(T * 2)); \
+            const __amdgpu_buffer_rsrc_t rb_ = make_rsrc((const bf16_t*)p.beta + lane_ * T, ok_ ? (uint32_t)(T * 2) : 0u); \
             pb = buf_load2(rb_, (r0_ + l) * 2);                                                     \
         }                                                                                           \
     } while (0)
@@ -153,7 +183,14 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs p) {
     // Persistent: workgroup b takes chunks b, b + gridDim.x, ... of the flattened (lane, chunk)
     // index, so the loads of the next chunk overlap the Gram tiles and solve of this one.
     int64_t t = blockIdx.x;
-    if (t < total) KDA_INTRA_LOAD(t);
+    KDA_INTRA_LOAD(t);
+    // taken here too, so that the loop head (which merges this path with the loop's back edge)
+    // carries no wait for loads
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { pin(pq[i]); pin(pk[i]); pin(pg[i]); }
+#pragma unroll
+    for (int i = 0; i < LPR; ++i) pin(pv[i]);
+    pin(pb);
     for (; t < total; t += gridDim.x) {
     const int64_t c = uniform64(t % p.nchunks);
     const int64_t lane = uniform64(t / p.nchunks);
@@ -162,7 +199,7 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs p) {
 
     // ================= phase 1: decay and scaled operands (wave-local) =========================
     i16x4 vacc[VPW][4];     // V rows 16I + 4lq + e, column vc0 + 16j + l16 (accumulator layout)
-    i16x4 kacc[2][4];       // K~ rows 16I + 4lq + e, channel 32w + 16h + l16
+    i16x4 kacc[2][4];       // K~ (chunk-relative) rows 16I + 4lq + e, channel 32w + 16h + l16
     {
         uint2 qv[2][4], kv[2][4];
         bf16_t* vst = reinterpret_cast<bf16_t*>(stB);
@@ -184,7 +221,9 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs p) {
             for (int i = 0; i < LPR; ++i) *reinterpret_cast<uint4*>(&vst[(i * (64 / LPR) + l / LPR) * LDVS + 8 * (l % LPR)]) = pv[i];
         }
         if (w == 0) sm.beta[l] = __uint_as_float(pb << 16);
-        if (t + gridDim.x < total) KDA_INTRA_LOAD(t + gridDim.x);
+        // the next chunk's rows load while this one is processed (the prefetch registers are free
+        // again once consumed above)
+        KDA_INTRA_LOAD(t + gridDim.x);
         wave_lds_sync();
         if (vw) {
 #pragma unroll
@@ -194,6 +233,7 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs p) {
                     vacc[j][I] = tr_read(&vst[(16 * I + 4 * lq + (l16 >> 2)) * LDVS + 16 * j + 4 * (l16 & 3)]);
         }
         if (kw) {
+            float pcol[2][4];   // exp(G_ref(I)) of channel 32w + 16h + l16
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 bf16x8 ga[2];
@@ -202,44 +242,98 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs p) {
                     const bf16_t* b0 = &stA[(32 * s + 4 * lq + (l16 >> 2)) * LDG + 16 * h + 4 * (l16 & 3)];
                     ga[s] = cat(tr_read(b0), tr_read(b0 + 16 * LDG));
                 }
-                // D[r] = G for channel 32w + 16h + 4lq + r at token 16I + l16
+                // D[r] = G for channel 32w + 16h + 4lq + r at token 16I + l16. The constant
+                // operands are rebuilt here (a few VALU ops) rather than held across the chunk
+                // loop: the empty asm hides that their inputs are loop-invariant.
+                int lqv = lq, l16v = l16;
+                asm volatile("" : "+v"(lqv), "+v"(l16v));
                 f32x4 G[4];
 #pragma unroll
                 for (int I = 0; I < 4; ++I) {
-                    G[I] = mma32(ga[0], ufrag(I, 0, lq, l16), kZero4);
-                    if (I >= 2) G[I] = mma32(ga[1], ufrag(I, 1, lq, l16), G[I]);
+                    G[I] = mma32(ga[0], ufrag(I, 0, lqv, l16v), kZero4);
+                    if (I >= 2) G[I] = mma32(ga[1], ufrag(I, 1, lqv, l16v), G[I]);
                 }
-                f32x4 gC;   // gamma_C of the lane's four channels (lane 15 of the row holds token 63)
+                // Reference points: G_ref(I) = G at token 16I - 1 (0 for I = 0), broadcast from
+                // lane 15 of the row that holds tile I - 1; gC = G at token 63. Every factor between
+                // reference points is a product of the block decays D_J = e^{G_ref(J+1) - G_ref(J)}
+                // and the tail E = e^{gC - G_ref(3)}, all <= 1: P_I = e^{G_ref(I)} (P_0 = 1),
+                // Q_I = e^{gC - G_ref(I)}, f_IJ = e^{G_ref(I) - G_ref(J)}, gamma_C = Q_0.
+                f32x4 Gref[4], P[4], Qt[4], D[3];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) gC[r] = row_bcast15(__builtin_amdgcn_exp2f(G[3][r] * kLog2e));
+                for (int r = 0; r < 4; ++r) {
+                    Gref[0][r] = 0.f;
+                    Gref[1][r] = row_bcast15(G[0][r]);
+                    Gref[2][r] = row_bcast15(G[1][r]);
+                    Gref[3][r] = row_bcast15(G[2][r]);
+                    const float gC = row_bcast15(G[3][r]);
+                    D[0][r] = __builtin_amdgcn_exp2f(Gref[1][r] * kLog2e);
+                    D[1][r] = __builtin_amdgcn_exp2f((Gref[2][r] - Gref[1][r]) * kLog2e);
+                    D[2][r] = __builtin_amdgcn_exp2f((Gref[3][r] - Gref[2][r]) * kLog2e);
+                    Qt[3][r] = __builtin_amdgcn_exp2f((gC - Gref[3][r]) * kLog2e);
+                    P[0][r] = 1.f;
+                    P[1][r] = D[0][r];
+                    P[2][r] = D[0][r] * D[1][r];
+                    P[3][r] = P[2][r] * D[2][r];
+                    Qt[2][r] = Qt[3][r] * D[2][r];
+                    Qt[1][r] = Qt[2][r] * D[1][r];
+                    Qt[0][r] = Qt[1][r] * D[0][r];
+                }
                 if (l16 == 15)
-                    *reinterpret_cast<f32x4*>(rec + R::G * 1024 + (32 * w + 16 * h + 4 * lq) * 4) = gC;
+                    *reinterpret_cast<f32x4*>(rec + R::G * 1024 + (32 * w + 16 * h + 4 * lq) * 4) = Qt[0];
+                if (l16 == 0) {   // f_IJ for the lane's four channels
+                    const int cc = 32 * w + 16 * h + 4 * lq;
+                    *reinterpret_cast<i16x4*>(&sm.fij[pair_index(1, 0)][cc]) = cvt4(D[0]);
+                    *reinterpret_cast<i16x4*>(&sm.fij[pair_index(2, 1)][cc]) = cvt4(D[1]);
+                    *reinterpret_cast<i16x4*>(&sm.fij[pair_index(3, 2)][cc]) = cvt4(D[2]);
+                    *reinterpret_cast<i16x4*>(&sm.fij[pair_index(2, 0)][cc]) = cvt4(P[2]);
+                    *reinterpret_cast<i16x4*>(&sm.fij[pair_index(3, 1)][cc]) = cvt4(D[1] * D[2]);
+                    *reinterpret_cast<i16x4*>(&sm.fij[pair_index(3, 0)][cc]) = cvt4(P[3]);
+                }
 #pragma unroll
                 for (int I = 0; I < 4; ++I) {
                     const f32x4 qf = unpack4f(__builtin_bit_cast(i16x4, qv[h][I]));
                     const f32x4 kf = unpack4f(__builtin_bit_cast(i16x4, kv[h][I]));
-                    f32x4 oq, ok, oh, ob;
+                    f32x4 oq, ok, oh, ob, orq;
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        const float g2 = G[I][r] * kLog2e;
-                        const float gam = __builtin_amdgcn_exp2f(g2);
-                        const float igam = __builtin_amdgcn_exp2f(-g2);
-                        oq[r] = qf[r] * gam;
-                        ok[r] = kf[r] * gam;
-                        oh[r] = kf[r] * igam;
-                        ob[r] = oh[r] * gC[r];
+                        // within the 16-token block: e1 = exp(G - G_ref) <= 1, e2 = 1/e1 <= e^80
+                        const float d2 = (G[I][r] - Gref[I][r]) * kLog2e;
+                        const float e1 = __builtin_amdgcn_exp2f(d2);
+                        const float e2 = __builtin_amdgcn_exp2f(-d2);
+                        oq[r] = qf[r] * e1;
+                        ok[r] = kf[r] * e1;
+                        oh[r] = kf[r] * e2;
+                        // record factors relative to the chunk start, each <= 1
+                        orq[r] = oq[r] * P[I][r];
+                        ob[r] = oh[r] * Qt[I][r];
                     }
                     // fragment blocks (I, ks = w): register elements e < 4 come from h = 0, e >= 4
                     // from h = 1, i.e. bytes 8h .. 8h + 7 of the lane's 16
-                    const i16x4 bq = cvt4(oq);
-                    *reinterpret_cast<i16x4*>(lblk(w, 0, I) + l * 16 + 8 * h) = bq;
+                    *reinterpret_cast<i16x4*>(lblk(w, 0, I) + l * 16 + 8 * h) = cvt4(oq);
                     *reinterpret_cast<i16x4*>(lblk(w, 1, I) + l * 16 + 8 * h) = cvt4(ok);
                     *reinterpret_cast<i16x4*>(lblk(w, 2, I) + l * 16 + 8 * h) = cvt4(oh);
-                    *reinterpret_cast<i16x4*>(blk(R::q(I, w)) + 8 * h) = bq;
+                    *reinterpret_cast<i16x4*>(blk(R::q(I, w)) + 8 * h) = cvt4(orq);
                     // K- token-major into the g stage columns 16h.. (already consumed above)
                     *reinterpret_cast<uint2*>(&stA[(16 * I + l16) * LDG + 16 * h + 4 * lq]) =
                         __builtin_bit_cast(uint2, cvt4(ob));
                 }
+                // P_I of channel 32w + 16h + l16 (the accumulator-layout column of the solve):
+                // P_I of local channel 16h + 4lq' + r' sits in every lane of row lq'
+                {
+                    const int src = ((l16 >> 2) << 4) * 4;   // byte address of lane 16 (l16 / 4)
+                    pcol[h][0] = 1.f;
+#pragma unroll
+                    for (int I = 1; I < 4; ++I) {
+                        float v[4];
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            v[r] = __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(P[I][r])));
+                        const int rr = l16 & 3;
+                        pcol[h][I] = rr == 0 ? v[0] : (rr == 1 ? v[1] : (rr == 2 ? v[2] : v[3]));
+                    }
+                }
+                // one 16-channel tile at a time: interleaving the two would double the live set
+                __builtin_amdgcn_sched_barrier(0);
             }
             wave_lds_sync();
             // K- blocks (M = 2w + h, half): K-[32 half + k(e)][16M + l16]
@@ -253,12 +347,13 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs p) {
             // K~ in accumulator layout from its own blocks: the 8-byte chunk addressed by lane
             // (lq, l16) is K~[16I + 4lq + l16/4][32w + 16h + 4(l16%4) ..], i.e. block lane
             // (l16 % 4, 4lq + l16/4), half h.
+            // (block-relative there; times exp(G_ref(I)) of the column's channel: chunk-relative)
 #pragma unroll
             for (int h = 0; h < 2; ++h)
 #pragma unroll
                 for (int I = 0; I < 4; ++I)
-                    kacc[h][I] = tr_read(reinterpret_cast<const bf16_t*>(
-                        lblk(w, 1, I) + ((l16 & 3) * 16 + 4 * lq + (l16 >> 2)) * 16 + 8 * h));
+                    kacc[h][I] = cvt4(pcol[h][I] * unpack4f(tr_read(reinterpret_cast<const bf16_t*>(
+                        lblk(w, 1, I) + ((l16 & 3) * 16 + 4 * lq + (l16 >> 2)) * 16 + 8 * h))));
         }
     }
     __syncthreads();
@@ -305,45 +400,52 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs p) {
         r1.z = pack_bf16x2(t[12], t[13]); r1.w = pack_bf16x2(t[14], t[15]);
         *reinterpret_cast<uint4*>(&sm.tinv[lq][i * 24]) = r0;
         *reinterpret_cast<uint4*>(&sm.tinv[lq][i * 24 + 8]) = r1;
-    } else if (w == 1) {
-        // off-diagonal blocks transposed: lane holds A_kk[16I + l16][16J + 4lq + r]
-#pragma unroll
-        for (int I = 1; I < 4; ++I)
-#pragma unroll
-            for (int J = 0; J < I; ++J) {
-                f32x4 acc = kZero4;
-#pragma unroll
-                for (int ks = 0; ks < NKS; ++ks)
-                    acc = mma32(read16(lblk(ks, 2, J) + l * 16), read16(lblk(ks, 1, I) + l * 16), acc);
-                const float b = sm.beta[16 * I + l16];
-                *reinterpret_cast<i16x4*>(&sm.akk[I * (I - 1) / 2 + J][l * 4]) = cvt4(acc * b);
-            }
     } else {
-        // A_qk transposed, lane holds A_qk[16I + l16][16J + 4lq + r] (j <= i kept); wave 2 writes
-        // the record blocks (0,0), (1,0), (2,0), wave 3 (2,1), (3,0), (3,1)
-        auto qk = [&](int I, int J) -> i16x4 {
+        // Waves 1-3: two off-diagonal block pairs (I > J) each, with K^_J rescaled once per pair
+        // and used for both A_kk and A_qk (transposed: the lane holds X[16I + l16][16J + 4lq + r],
+        // so the A_kk blocks are K16 A operands as computed and the A_qk blocks are record
+        // halves); then the diagonal A_qk blocks (j <= i kept). Record block A(I, h) holds
+        // J = 2h in bytes 0..7 and J = 2h + 1 in bytes 8..15 of each lane's 16.
+        const int I0 = w == 1 ? 1 : (w == 2 ? 2 : 3), J0 = w == 1 ? 0 : (w == 2 ? 1 : 1);
+        const int I1 = w == 1 ? 2 : 3, J1 = w == 1 ? 0 : (w == 2 ? 0 : 2);
+#pragma unroll
+        for (int pr = 0; pr < 2; ++pr) {
+            const int I = pr ? I1 : I0, J = pr ? J1 : J0;
+            const bf16_t* f = sm.fij[pair_index(I, J)];
+            f32x4 akk = kZero4, aqk = kZero4;
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) {
+                const bf16x8 a = scale_frag(read16(lblk(ks, 2, J) + l * 16), f, ks, lq);
+                akk = mma32(a, read16(lblk(ks, 1, I) + l * 16), akk);
+                aqk = mma32(a, read16(lblk(ks, 0, I) + l * 16), aqk);
+            }
+            *reinterpret_cast<i16x4*>(&sm.akk[pair_index(I, J)][l * 4]) = cvt4(akk * sm.beta[16 * I + l16]);
+            *reinterpret_cast<i16x4*>(blk(R::a(I, J >> 1)) + 8 * (J & 1)) = cvt4(aqk);
+        }
+        // diagonal A_qk blocks: wave 1 takes I = 0, 1, wave 2 I = 2, wave 3 I = 3; the wave that
+        // writes I = 0 (I = 2) also zeroes the J = 1 (J = 3) half of record block A(0,0) (A(2,1))
+        const int nd = w == 1 ? 2 : 1;
+        for (int d = 0; d < nd; ++d) {
+            const int I = w == 1 ? d : w;
             f32x4 acc = kZero4;
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks)
-                acc = mma32(read16(lblk(ks, 2, J) + l * 16), read16(lblk(ks, 0, I) + l * 16), acc);
-            if (J == I) {
+                acc = mma32(read16(lblk(ks, 2, I) + l * 16), read16(lblk(ks, 0, I) + l * 16), acc);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) acc[r] = (4 * lq + r <= l16) ? acc[r] : 0.f;
-            }
-            return cvt4(acc);
-        };
-        const i16x4 z = {0, 0, 0, 0};
-        if (w == 2) {
-            *reinterpret_cast<bf16x8*>(blk(R::a(0, 0))) = cat(qk(0, 0), z);
-            *reinterpret_cast<bf16x8*>(blk(R::a(1, 0))) = cat(qk(1, 0), qk(1, 1));
-            *reinterpret_cast<bf16x8*>(blk(R::a(2, 0))) = cat(qk(2, 0), qk(2, 1));
-        } else {
-            *reinterpret_cast<bf16x8*>(blk(R::a(2, 1))) = cat(qk(2, 2), z);
-            *reinterpret_cast<bf16x8*>(blk(R::a(3, 0))) = cat(qk(3, 0), qk(3, 1));
-            *reinterpret_cast<bf16x8*>(blk(R::a(3, 1))) = cat(qk(3, 2), qk(3, 3));
+            for (int r = 0; r < 4; ++r) acc[r] = (4 * lq + r <= l16) ? acc[r] : 0.f;
+            *reinterpret_cast<i16x4*>(blk(R::a(I, I >> 1)) + 8 * (I & 1)) = cvt4(acc);
+            if ((I & 1) == 0) *reinterpret_cast<uint2*>(blk(R::a(I, I >> 1)) + 8) = make_uint2(0u, 0u);
         }
     }
     __syncthreads();
+
+    // the next chunk's rows have had the Gram phase to arrive; take them now, before this
+    // chunk's solve issues its record stores
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { pin(pq[i]); pin(pk[i]); pin(pg[i]); }
+#pragma unroll
+    for (int i = 0; i < LPR; ++i) pin(pv[i]);
+    pin(pb);
 
     // ================= phase 3: (I + A_kk) [W | U] = Diag(beta) [K~ | V] =========================
     {
@@ -364,7 +466,8 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs p) {
 #pragma unroll
             for (int j = 0; j < VPW; ++j) {
                 f32x4 X[4];
-                ut_solve(ops, vacc[j][0], vacc[j][1], vacc[j][2], vacc[j][3], X[0], X[1], X[2], X[3]);
+                ut_solve(ops, unpack4f(vacc[j][0]), unpack4f(vacc[j][1]), unpack4f(vacc[j][2]), unpack4f(vacc[j][3]),
+                         X[0], X[1], X[2], X[3]);
                 const int n = vc0 / 16 + j;
                 *reinterpret_cast<bf16x8*>(blk(R::u(n, 0))) = cat(cvt4(X[0]), cvt4(X[1]));
                 *reinterpret_cast<bf16x8*>(blk(R::u(n, 1))) = cat(cvt4(X[2]), cvt4(X[3]));
@@ -375,7 +478,8 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs p) {
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 f32x4 X[4];
-                ut_solve(ops, kacc[h][0], kacc[h][1], kacc[h][2], kacc[h][3], X[0], X[1], X[2], X[3]);
+                ut_solve(ops, unpack4f(kacc[h][0]), unpack4f(kacc[h][1]), unpack4f(kacc[h][2]), unpack4f(kacc[h][3]),
+                         X[0], X[1], X[2], X[3]);
 #pragma unroll
                 for (int I = 0; I < 4; ++I)   // the record holds -W
                     *reinterpret_cast<i16x4*>(&wt[(16 * h + l16) * LDW + 16 * I + 4 * lq]) = cvt4(-X[I]);

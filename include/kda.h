@@ -26,9 +26,10 @@
  *  - Every tensor is dense and row-major with the last dimension contiguous; tensor base
  *    pointers must be 16-byte aligned (beta: aligned to its element size).
  *  - Decay domain: log_alpha must lie in [-5, 0] (the lower bound g_min = -5 of the decay
- *    equation in section 2.2). Prefill additionally requires every per-channel sum of
- *    log_alpha over one 64-token chunk to be >= -80 (true whenever log_alpha >= -1.25); outside
- *    this range results are undefined (no check is made: it would need a pass over the data).
+ *    equation in section 2.2); bf16 prefill and decode accept the whole domain. The fp32
+ *    prefill path (dk = 64) additionally requires every per-channel sum of log_alpha over one
+ *    64-token chunk to be >= -80 (true whenever log_alpha >= -1.25). Outside these ranges
+ *    results are undefined (no check is made: it would need a pass over the data).
  */
 #ifndef KDA_H
 #define KDA_H

@@ -63,8 +63,38 @@ def test_segment_split_no_decay_channels():
 
 
 def test_full_decay_contract_edge():
-    """log_alpha down to -1.25 (a 64-chunk sum can reach -80, the edge of the kernel's contract)."""
+    """log_alpha in [-1.25, -1] (a 64-token chunk sum near -80, the former chunk-start limit)."""
     run_and_check("decay edge", 1, 2, 640, 128, 128, BF16, la_range=(-1.25, -1.0), seed=4200)
+
+
+@pytest.mark.parametrize("dk,dv", [(128, 128), (64, 128), (128, 64), (64, 64)])
+def test_full_decay_domain(dk, dv):
+    """log_alpha over the whole domain [-5, 0] (decay lower-bound equation of section 2.2): a
+    64-token chunk's cumulative decay reaches -320, past what a chunk-start reference allows."""
+    run_and_check("decay domain", 1, 3, 64 * 9 + 21, dk, dv, BF16, s0_std=0.3, la_range=(-5.0, 0.0),
+                  seed=4300 + dk + dv)
+
+
+def test_strongest_decay_everywhere():
+    """log_alpha = -5 on every channel and token: each token's write is nearly all that is left."""
+    run_and_check("decay -5", 1, 2, 64 * 5 + 9, 128, 128, BF16, s0_std=0.3, la_range=(-5.0, -5.0), seed=4400)
+
+
+@pytest.mark.parametrize("segments", [1, 4])
+def test_decay_domain_mixed_channels(segments):
+    """Even channels at the strongest decay, odd channels almost without decay, carried state,
+    with and without a sequence split: both extremes inside one Gram tile and one state."""
+    B, H, T, d = 1, 4, 64 * 17 + 5, 128
+    say("decay mixed channels: B=%d H=%d T=%d d=%d segments=%d" % (B, H, T, d, segments))
+    q, k, v, la, beta, S0 = synth.prefill_inputs(B, H, T, d, d, BF16, device=DEV, seed_base=4500, s0_std=0.3)
+    g = torch.Generator(device="cpu").manual_seed(4501)
+    strong = -5.0 + 0.5 * torch.rand(B, H, T, d // 2, generator=g)
+    weak = -0.01 * torch.rand(B, H, T, d // 2, generator=g)
+    la = torch.stack([strong, weak], dim=-1).reshape(B, H, T, d).to(BF16).to(DEV)
+    o, S_T = kda.chunk_fwd(q, k, v, la, beta, S0, segments=segments)
+    torch.cuda.synchronize()
+    o_ref, S_ref = oracle_prefill(q, k, v, la, beta, S0)
+    assert_close("decay mixed", BF16, host32(o).reshape(B * H, T, d), o_ref, host32(S_T).reshape(B * H, d, d), S_ref)
 
 
 def test_bf16_8k_workload_all_heads():

@@ -134,6 +134,18 @@ def test_beta0_closed_form_decay():
     assert np.abs(o[0] - o_cf).max() < 1e-13 and np.abs(S[0] - S_cf).max() < 1e-13
 
 
+def test_beta0_closed_form_full_decay_domain():
+    """beta = 0 over the whole decay domain log alpha in [-5, 0] (decay lower-bound equation):
+    the closed form of the test above, with cumulative decays down to about -300."""
+    q, k, v, la, beta, S0 = _rand_inputs(1, 130, 6, 4, la_lo=-5.0, la_hi=0.0)
+    beta[:] = 0.0
+    o, S = native.kda_fwd(q, k, v, la, beta, S0)
+    gam = np.exp(np.cumsum(la[0].astype(np.float64), axis=0))
+    o_cf = (gam * q[0]) @ S0[0].astype(np.float64)
+    S_cf = gam[-1][:, None] * S0[0]
+    assert np.abs(o[0] - o_cf).max() < 1e-13 and np.abs(S[0] - S_cf).max() < 1e-13
+
+
 def test_beta1_unit_key_recall():
     """beta = 1 and ||k|| = 1: after the write S_t^T k_t = v_t, whatever alpha and the old state;
     reading with q_t = k_t therefore returns v_t exactly (up to rounding)."""
