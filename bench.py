@@ -1,13 +1,15 @@
 """Benchmark of the KDA hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload prefill_8k|prefill_64k|prefill_1m|fp32_small]
-                    [--decode-steps 1000] [--no-cpu-baseline] [--copy-probe-mib M]
+                    [--decode-steps 1000] [--no-cpu-baseline] [--no-packed] [--copy-probe-mib M]
 
 One step = one kda_chunk_fwd call over the named prefill workload (default: bf16, B=1, H=32,
 T=8192, d=128, C=64, S0=0), inputs already resident in HBM. The decode regime is measured in
 the same run: `--decode-steps` chained kda_decode_step calls over 256 sequences x 32 heads
-(fp32 state, bf16 tokens, each step its own pre-generated tokens). Times come from HIP events
-recorded on the stream the library launches on.
+(fp32 state, bf16 tokens, each step its own pre-generated tokens), and so is a packed batch of
+12 variable-length sequences (8192 tokens per head, 32 heads) with state checkpoints every 512
+tokens (kda_chunk_fwd_varlen). Times come from HIP events recorded on the stream the library
+launches on.
 
 Prints one JSON line. `value` is prefill tokens/s (B*T / seconds per call). `roofline` is the
 prefill call (all of its kernels: intra-chunk records, state passes, segment scan) against HBM
@@ -94,6 +96,7 @@ def main():
     ap.add_argument("--segments", type=int, default=0, help="0 = the library's plan")
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-packed", action="store_true", help="skip the packed variable-length batch")
     ap.add_argument("--cpu-lanes", type=int, default=32, help="lanes of the CPU-baseline sample")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run one plain device copy of this size (counter calibration)")
@@ -157,6 +160,49 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+
+    # ---------------- packed variable-length batch with checkpoints ----------------
+    packed = None
+    if not args.no_packed:
+        pw = synth.PACKED_BF16_8K
+        lens = synth.PACKED_BF16_8K_LENS
+        E = 512
+        print("bench: packed %s" % pw.name, file=sys.stderr, flush=True)
+        pq, pk, pv, pla, pbeta, cu, _ = synth.packed_inputs(lens, pw.H, pw.d, pw.d, pw.dtype, device=dev)
+        N = len(lens)
+        n_ck = sum(n // E for n in lens)
+        po = torch.empty_like(pv)
+        pS = torch.empty(N, pw.H, pw.d, pw.d, device=dev, dtype=torch.float32)
+        pck = torch.empty(pw.T // E, pw.H, pw.d, pw.d, device=dev, dtype=torch.float32)
+        poff = torch.empty(N + 1, device=dev, dtype=torch.int32)
+        pws = torch.empty(max(kda.varlen_workspace_bytes(N, pw.H, pw.T, max(lens), pw.d, pw.d, ckpt_every=E), 16),
+                          device=dev, dtype=torch.uint8)
+
+        def pstep():
+            kda.chunk_fwd_varlen(pq, pk, pv, pla, pbeta, cu, None, max_len=max(lens), ckpt_every=E, o=po, S_T=pS,
+                                 S_ckpt=pck, ckpt_offsets=poff, workspace=pws, stream=stream)
+
+        for _ in range(args.warmup):
+            pstep()
+        torch.cuda.synchronize()
+        p0 = torch.cuda.Event(enable_timing=True)
+        p1 = torch.cuda.Event(enable_timing=True)
+        p0.record(stream)
+        for _ in range(args.steps):
+            pstep()
+        p1.record(stream)
+        torch.cuda.synchronize()
+        pms = p0.elapsed_time(p1) / args.steps
+        _, pby = prefill_alg(1, pw.H, pw.T, pw.d, 2, 2, False)
+        pby += (N - 1) * pw.H * pw.d * pw.d * 4 + n_ck * pw.H * pw.d * pw.d * 4   # S_T per lane, checkpoints
+        pgbs = pby / (pms * 1e-3) / 1e9
+        packed = {"workload": pw.name, "lengths": list(lens), "metric": "KDA packed prefill tokens/s",
+                  "value": pw.T / (pms * 1e-3), "unit": "tokens/s", "ms_per_step": pms, "ckpt_every": E,
+                  "checkpoints_per_call": n_ck,
+                  "roofline": {"bound": "hbm", "achieved": pgbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                               "frac": pgbs / HBM_PEAK_GBS, "traffic": None},
+                  "alg_bytes_per_call": pby}
+        del pq, pk, pv, pla, pbeta, po, pws
 
     # ---------------- decode regime ----------------
     decode = None
@@ -222,7 +268,7 @@ def main():
                      "traffic": measured_traffic("call", w.name, PREFILL_SOURCES)},
         "mfma": {"alg_tflops": tflops, "peak_tflops": mm_peak, "frac": tflops / mm_peak},
         "alg_bytes_per_call": abytes, "alg_flops_per_call": flops, "call_ms": call_ms,
-        "decode": decode, "cpu_baseline": cpu,
+        "decode": decode, "packed": packed, "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
 

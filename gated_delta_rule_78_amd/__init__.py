@@ -6,6 +6,8 @@ Every step of the computation runs in the library's HIP kernels. There is no fal
 library is missing or fails, the call raises.
 
     chunk_fwd(q, k, v, log_alpha, beta, S0=None) -> (o, S_T)     chunkwise prefill
+    chunk_fwd_varlen(q, k, v, log_alpha, beta, cu_seqlens, ...)   packed variable-length batch,
+        -> (o, S_T, S_ckpt, ckpt_offsets)                         state checkpoints every E tokens
     decode_step(q, k, v, log_alpha, beta, S) -> o                 one token, S updated in place
 """
 import ctypes
@@ -13,7 +15,8 @@ import os
 
 import torch
 
-__all__ = ["chunk_fwd", "decode_step", "chunk_workspace_bytes", "library", "KDAError", "LIB_PATH"]
+__all__ = ["chunk_fwd", "chunk_fwd_varlen", "decode_step", "chunk_workspace_bytes", "varlen_workspace_bytes",
+           "library", "KDAError", "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkda.so")
 
@@ -25,6 +28,13 @@ class ChunkDesc(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int64), ("H", ctypes.c_int64), ("T", ctypes.c_int64), ("dk", ctypes.c_int64),
                 ("dv", ctypes.c_int64), ("chunk", ctypes.c_int32), ("in_dtype", ctypes.c_int32),
                 ("out_dtype", ctypes.c_int32), ("segments", ctypes.c_int32)]
+
+
+class VarlenDesc(ctypes.Structure):
+    _fields_ = [("N", ctypes.c_int64), ("H", ctypes.c_int64), ("T", ctypes.c_int64), ("max_len", ctypes.c_int64),
+                ("dk", ctypes.c_int64), ("dv", ctypes.c_int64), ("chunk", ctypes.c_int32), ("in_dtype", ctypes.c_int32),
+                ("out_dtype", ctypes.c_int32), ("segments", ctypes.c_int32), ("ckpt_every", ctypes.c_int32),
+                ("packed", ctypes.c_int32)]
 
 
 class DecodeDesc(ctypes.Structure):
@@ -54,6 +64,11 @@ def library():
         lib.kda_chunk_fwd_workspace_bytes.restype = ctypes.c_size_t
         lib.kda_chunk_fwd.argtypes = [ctypes.POINTER(ChunkDesc), P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
         lib.kda_chunk_fwd.restype = ctypes.c_int32
+        lib.kda_chunk_fwd_varlen_workspace_bytes.argtypes = [ctypes.POINTER(VarlenDesc)]
+        lib.kda_chunk_fwd_varlen_workspace_bytes.restype = ctypes.c_size_t
+        lib.kda_chunk_fwd_varlen.argtypes = [ctypes.POINTER(VarlenDesc), P, P, P, P, P, P, P, P, P, P, P, P,
+                                             ctypes.c_size_t, P]
+        lib.kda_chunk_fwd_varlen.restype = ctypes.c_int32
         lib.kda_decode_step.argtypes = [ctypes.POINTER(DecodeDesc), P, P, P, P, P, P, P, P]
         lib.kda_decode_step.restype = ctypes.c_int32
         lib.kda_status_string.argtypes = [ctypes.c_int32]
@@ -131,6 +146,87 @@ def chunk_fwd(q, k, v, log_alpha, beta, S0=None, *, out_dtype=None, segments=0, 
                            _ptr(o), _ptr(S_T), _ptr(workspace), ws_bytes, _stream(dev, stream))
     _check("kda_chunk_fwd", st)
     return o, S_T
+
+
+def _varlen_desc(N, H, T, max_len, dk, dv, out_dtype, segments, ckpt_every, packed):
+    return VarlenDesc(N, H, T, max_len, dk, dv, 64, KDA_BF16, _DTYPES[out_dtype], int(segments), int(ckpt_every),
+                      int(packed))
+
+
+def varlen_workspace_bytes(N, H, T, max_len, dk, dv, *, segments=0, ckpt_every=0, packed=True,
+                           out_dtype=torch.bfloat16):
+    d = _varlen_desc(N, H, T, max_len, dk, dv, out_dtype, segments, ckpt_every, packed)
+    return int(library().kda_chunk_fwd_varlen_workspace_bytes(ctypes.byref(d)))
+
+
+def chunk_fwd_varlen(q, k, v, log_alpha, beta, cu_seqlens=None, S0=None, *, max_len=None, N=None, ckpt_every=0,
+                     out_dtype=None, segments=0, o=None, S_T=None, S_ckpt=None, ckpt_offsets=None,
+                     store_state=True, workspace=None, stream=None):
+    """KDA prefill over a batch of sequences with state checkpoints, through ``kda_chunk_fwd_varlen``.
+
+    Packed (``cu_seqlens`` given, int32 [N+1] on the device): q, k, log_alpha [H,T,dk], v [H,T,dv],
+    beta [H,T], bf16; sequence s is rows cu_seqlens[s]:cu_seqlens[s+1] of every head.
+    ``max_len`` bounds every length (default T); ``N`` defaults to len(cu_seqlens) - 1.
+    Equal lengths (``cu_seqlens`` None): tensors [N,H,T,...] as ``chunk_fwd``.
+    S0, S_T: [N,H,dk,dv] fp32. With ``ckpt_every`` = E > 0, the state after every E tokens of each
+    sequence goes to S_ckpt[ckpt_offsets[s] + j - 1, h] (S_ckpt: [K, H, dk, dv] fp32 with
+    K = T // E packed or N * (T // E) otherwise) and ckpt_offsets (int32 [N+1]) is written.
+    Returns (o, S_T, S_ckpt, ckpt_offsets); the last two are None when E = 0. S_ckpt is returned
+    at its capacity K; its first ckpt_offsets[N] entries are written (the count is only known on
+    the device, and reading it would synchronise).
+    """
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("chunk_fwd_varlen runs on the GPU; got a tensor on %s" % dev)
+    if q.dtype != torch.bfloat16:
+        raise ValueError("chunk_fwd_varlen takes bf16 inputs (got %s)" % q.dtype)
+    out_dtype = out_dtype or q.dtype
+    packed = cu_seqlens is not None
+    dk, dv = q.shape[-1], v.shape[-1]
+    if packed:
+        H, T = q.shape[0], q.shape[1]
+        _check_tensor("cu_seqlens", cu_seqlens, dev, torch.int32, (cu_seqlens.numel(),))
+        N = cu_seqlens.numel() - 1 if N is None else N
+        if N < 1 or cu_seqlens.numel() != N + 1:
+            raise ValueError("cu_seqlens must have N + 1 >= 2 entries")
+        lead, slead = (H, T), (N, H)
+        max_len = T if max_len is None else int(max_len)
+        n_ck = T // ckpt_every if ckpt_every else 0
+    else:
+        N, H, T = q.shape[0], q.shape[1], q.shape[2]
+        lead, slead = (N, H, T), (N, H)
+        max_len = T
+        n_ck = N * (T // ckpt_every) if ckpt_every else 0
+    for name, t, shape in (("q", q, lead + (dk,)), ("k", k, lead + (dk,)), ("log_alpha", log_alpha, lead + (dk,)),
+                           ("v", v, lead + (dv,)), ("beta", beta, lead)):
+        _check_tensor(name, t, dev, torch.bfloat16, shape)
+    if S0 is not None:
+        _check_tensor("S0", S0, dev, torch.float32, slead + (dk, dv))
+    if o is None:
+        o = torch.empty(lead + (dv,), device=dev, dtype=out_dtype)
+    else:
+        _check_tensor("o", o, dev, out_dtype, lead + (dv,))
+    if S_T is None and store_state:
+        S_T = torch.empty(slead + (dk, dv), device=dev, dtype=torch.float32)
+    if ckpt_every:
+        if S_ckpt is None:
+            S_ckpt = torch.empty(max(n_ck, 1), H, dk, dv, device=dev, dtype=torch.float32)
+        if ckpt_offsets is None:
+            ckpt_offsets = torch.empty(N + 1, device=dev, dtype=torch.int32)
+    desc = _varlen_desc(N, H, T, max_len, dk, dv, out_dtype, segments, ckpt_every, packed)
+    lib = library()
+    need = int(lib.kda_chunk_fwd_varlen_workspace_bytes(ctypes.byref(desc)))
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, device=dev, dtype=torch.uint8)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.kda_chunk_fwd_varlen(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
+                                  _ptr(cu_seqlens), _ptr(S0), _ptr(o), _ptr(S_T),
+                                  _ptr(S_ckpt if ckpt_every else None), _ptr(ckpt_offsets if ckpt_every else None),
+                                  _ptr(workspace), ws_bytes, _stream(dev, stream))
+    _check("kda_chunk_fwd_varlen", st)
+    if not ckpt_every:
+        return o, S_T, None, None
+    return o, S_T, S_ckpt[:n_ck], ckpt_offsets
 
 
 def decode_step(q, k, v, log_alpha, beta, S, *, out_dtype=None, o=None, stream=None):

@@ -29,13 +29,22 @@ bool overlaps(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi && a.hi > a.
 bool valid_dtype(int32_t d) { return d == KDA_F32 || d == KDA_BF16; }
 int64_t elem_bytes(int32_t d) { return d == KDA_BF16 ? 2 : 4; }
 
+// What a bf16 prefill call covers, for planning: `lanes` (batch or sequence, head) pairs whose
+// longest one has `max_chunks` chunks, and `slots` record slots in all.
+struct Geometry {
+    int64_t lanes, max_chunks, slots, dk, dv;
+    int32_t in_dtype, segments;
+    int64_t tab_slots;   // slot-table entries (packed batches), 0 otherwise
+};
+
 // Segments per lane, chunks per segment and workspace of a prefill call.
 struct Plan {
     int nseg;
     int64_t nchunks, chunks_per_seg;
-    size_t rec_bytes;    // intra-chunk records (bf16 path): [lanes][nchunks]
+    size_t rec_bytes;    // intra-chunk records (bf16 path): one per slot
     size_t pair_bytes;   // affine pairs [lanes][nseg][dk][dv + dk] (nseg > 1)
     size_t entry_bytes;  // entry states [lanes][nseg][dk][dv] (nseg > 1)
+    size_t tab_bytes;    // slot table (packed batches)
     size_t ws_bytes;
 };
 
@@ -60,28 +69,33 @@ int64_t auto_segments(int64_t lanes, int64_t nchunks) {
     return best;
 }
 
-Plan make_plan(const kda_chunk_desc* d) {
+Plan make_plan(const Geometry& g) {
     Plan p{};
-    const int64_t lanes = d->B * d->H;
-    const int64_t nchunks = (d->T + kChunk - 1) / kChunk;
+    const int64_t nchunks = g.max_chunks;
     p.nchunks = nchunks;
     int64_t nseg = 1;
-    if (d->in_dtype == KDA_BF16 && nchunks > 0) nseg = d->segments > 0 ? d->segments : auto_segments(lanes, nchunks);
+    if (g.in_dtype == KDA_BF16 && nchunks > 0) nseg = g.segments > 0 ? g.segments : auto_segments(g.lanes, nchunks);
     if (nseg > nchunks) nseg = nchunks > 0 ? nchunks : 1;
     int64_t cps = nchunks > 0 ? ceil_div(nchunks, nseg) : 1;
     if (cps < 1) cps = 1;
-    nseg = nchunks > 0 ? ceil_div(nchunks, cps) : 1;  // no empty segment
+    nseg = nchunks > 0 ? ceil_div(nchunks, cps) : 1;  // no segment past the longest lane
     p.nseg = (int)nseg;
     p.chunks_per_seg = cps;
-    if (d->in_dtype == KDA_BF16 && nchunks > 0) {
-        p.rec_bytes = (size_t)lanes * (size_t)nchunks * (size_t)kda::record_bytes(d->dk, d->dv);
+    if (g.in_dtype == KDA_BF16 && nchunks > 0) {
+        p.rec_bytes = (size_t)g.slots * (size_t)kda::record_bytes(g.dk, g.dv);
         if (nseg > 1) {
-            p.pair_bytes = (size_t)lanes * (size_t)nseg * (size_t)(d->dk * (d->dv + d->dk)) * sizeof(float);
-            p.entry_bytes = (size_t)lanes * (size_t)nseg * (size_t)(d->dk * d->dv) * sizeof(float);
+            p.pair_bytes = (size_t)g.lanes * (size_t)nseg * (size_t)(g.dk * (g.dv + g.dk)) * sizeof(float);
+            p.entry_bytes = (size_t)g.lanes * (size_t)nseg * (size_t)(g.dk * g.dv) * sizeof(float);
         }
+        p.tab_bytes = (size_t)g.tab_slots * sizeof(kda::SlotEntry);
     }
-    p.ws_bytes = p.rec_bytes + p.pair_bytes + p.entry_bytes;
+    p.ws_bytes = p.rec_bytes + p.pair_bytes + p.entry_bytes + p.tab_bytes;
     return p;
+}
+
+Geometry fixed_geometry(const kda_chunk_desc* d) {
+    const int64_t nchunks = ceil_div(d->T, kChunk);
+    return Geometry{d->B * d->H, nchunks, d->B * d->H * nchunks, d->dk, d->dv, d->in_dtype, d->segments, 0};
 }
 
 kda_status check_chunk_desc(const kda_chunk_desc* d) {
@@ -98,7 +112,75 @@ kda_status check_chunk_desc(const kda_chunk_desc* d) {
     // element counts must fit comfortably in 64-bit byte offsets
     const double elems = (double)d->B * (double)d->H * (double)(d->T > 0 ? d->T : 1) * (double)(d->dk + d->dv);
     if (elems > 1e17) return KDA_ERR_INVALID_ARG;
+    // the intra-chunk kernel numbers its chunks with 32 bits
+    if (d->in_dtype == KDA_BF16 && (double)d->B * (double)d->H * (double)ceil_div(d->T, kChunk) >= 2147483648.0)
+        return KDA_ERR_UNSUPPORTED;
     return KDA_OK;
+}
+
+kda_status check_varlen_desc(const kda_varlen_desc* d) {
+    if (!d) return KDA_ERR_INVALID_ARG;
+    if (d->N < 1 || d->H < 1 || d->T < 0 || d->max_len < 0 || d->dk < 1 || d->dv < 1 || d->segments < 0 ||
+        d->ckpt_every < 0 || (d->packed != 0 && d->packed != 1))
+        return KDA_ERR_INVALID_ARG;
+    if (d->ckpt_every % kChunk != 0) return KDA_ERR_INVALID_ARG;
+    if (!valid_dtype(d->in_dtype) || !valid_dtype(d->out_dtype)) return KDA_ERR_INVALID_ARG;
+    if (d->chunk != kChunk) return KDA_ERR_UNSUPPORTED;
+    if ((d->dk != 64 && d->dk != 128) || (d->dv != 64 && d->dv != 128)) return KDA_ERR_UNSUPPORTED;
+    if (d->in_dtype != KDA_BF16) return KDA_ERR_UNSUPPORTED;
+    // the state pass addresses one sequence's output rows with 32-bit offsets; slot rows are int32
+    const int64_t dmax = d->dk > d->dv ? d->dk : d->dv;
+    const int64_t longest = d->packed ? d->max_len : d->T;
+    if (longest * dmax * 4 >= ((int64_t)1 << 31) || d->T >= ((int64_t)1 << 31) - 64) return KDA_ERR_UNSUPPORTED;
+    const double elems = (double)d->N * (double)d->H * (double)(d->T > 0 ? d->T : 1) * (double)(d->dk + d->dv);
+    if (elems > 1e17) return KDA_ERR_INVALID_ARG;
+    // the intra-chunk kernel numbers its chunk slots with 32 bits
+    const double items = d->packed ? (double)d->H * (double)(d->T / kChunk + d->N)
+                                   : (double)d->N * (double)d->H * (double)ceil_div(d->T, kChunk);
+    if (items >= 2147483648.0) return KDA_ERR_UNSUPPORTED;
+    return KDA_OK;
+}
+
+// Packed batch: T/64 + N record slots per head (the lengths are only known on the device).
+// Equal lengths: the fixed-length geometry with B = N.
+Geometry varlen_geometry(const kda_varlen_desc* d) {
+    if (!d->packed) {
+        const int64_t nchunks = ceil_div(d->T, kChunk);
+        return Geometry{d->N * d->H, nchunks, d->N * d->H * nchunks, d->dk, d->dv, d->in_dtype, d->segments, 0};
+    }
+    const int64_t max_len = d->max_len < d->T ? d->max_len : d->T;
+    const int64_t max_chunks = ceil_div(max_len, kChunk);
+    const int64_t slots = d->T / kChunk + d->N;
+    return Geometry{d->N * d->H, max_chunks, d->H * slots, d->dk, d->dv, d->in_dtype, d->segments, slots};
+}
+
+// bf16 prefill after validation: records of every chunk (state independent, fully parallel),
+// then the sequential state pass, split in two passes around the segment scan when the plan
+// has more than one segment per lane.
+kda_status run_bf16(kda::ChunkLaunch& a, const Plan& plan, unsigned char* ws, hipStream_t st) {
+    kda::IntraArgs ia{};
+    ia.lanes = a.lanes; ia.T = a.T; ia.nchunks = a.nchunks; ia.dk = a.dk; ia.dv = a.dv;
+    ia.q = a.q; ia.k = a.k; ia.v = a.v; ia.la = a.la; ia.beta = a.beta;
+    ia.rec = ws;
+    ia.map = a.map;
+    ia.slot_tab = a.map.cu ? reinterpret_cast<const kda::SlotEntry*>(ws + plan.rec_bytes + plan.pair_bytes + plan.entry_bytes)
+                           : nullptr;
+    if (kda::launch_intra(ia, st) != hipSuccess) return KDA_ERR_HIP;
+    a.rec = ws;
+    a.ws_pair = plan.pair_bytes ? reinterpret_cast<float*>(ws + plan.rec_bytes) : nullptr;
+    a.ws_entry = plan.entry_bytes ? reinterpret_cast<float*>(ws + plan.rec_bytes + plan.pair_bytes) : nullptr;
+    if (plan.nseg == 1) {
+        a.fin_seg_lo = 0; a.fin_nseg = 1; a.sum_seg_lo = 0; a.sum_nseg = 0;
+        return kda::launch_inter(a, st) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+    }
+    // pass 1: segment 0 from the known entry state; summaries of the middle segments
+    a.fin_seg_lo = 0; a.fin_nseg = 1; a.sum_seg_lo = 1; a.sum_nseg = plan.nseg - 2;
+    if (kda::launch_inter(a, st) != hipSuccess) return KDA_ERR_HIP;
+    // exact entry state of every later segment
+    if (kda::launch_segment_scan(a, st) != hipSuccess) return KDA_ERR_HIP;
+    // pass 2: every later segment from its exact entry state
+    a.fin_seg_lo = 1; a.fin_nseg = plan.nseg - 1; a.sum_seg_lo = 0; a.sum_nseg = 0;
+    return kda::launch_inter(a, st) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
 }  // namespace
@@ -120,7 +202,7 @@ const char* kda_version(void) { return "kda-gfx950 0.1.0"; }
 
 size_t kda_chunk_fwd_workspace_bytes(const kda_chunk_desc* d) {
     if (check_chunk_desc(d) != KDA_OK) return 0;
-    return make_plan(d).ws_bytes;
+    return make_plan(fixed_geometry(d)).ws_bytes;
 }
 
 kda_status kda_chunk_fwd(const kda_chunk_desc* d, const void* q, const void* k, const void* v,
@@ -156,7 +238,7 @@ kda_status kda_chunk_fwd(const kda_chunk_desc* d, const void* q, const void* k, 
     if (S0 && overlaps(ro, range_of(S0, state_bytes))) return KDA_ERR_INVALID_ARG;
     if (S_T && overlaps(ro, range_of(S_T, state_bytes))) return KDA_ERR_INVALID_ARG;
 
-    const Plan plan = make_plan(d);
+    const Plan plan = make_plan(fixed_geometry(d));
     if (plan.ws_bytes > 0) {
         if (!workspace || workspace_bytes < plan.ws_bytes) return KDA_ERR_WORKSPACE;
         if (!aligned(workspace, 16)) return KDA_ERR_INVALID_ARG;
@@ -175,35 +257,106 @@ kda_status kda_chunk_fwd(const kda_chunk_desc* d, const void* q, const void* k, 
     a.nseg = plan.nseg; a.chunks_per_seg = plan.chunks_per_seg;
     a.q = q; a.k = k; a.v = v; a.la = log_alpha; a.beta = beta;
     a.S0 = S0; a.o = o; a.S_T = S_T;
+    a.map.H = d->H;
     if (!a.in_bf16) {
         a.fin_seg_lo = 0; a.fin_nseg = 1; a.sum_seg_lo = 0; a.sum_nseg = 0;
         return kda::launch_chunk(a, st) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
     }
+    return run_bf16(a, plan, static_cast<unsigned char*>(workspace), st);
+}
 
-    // bf16: records of every chunk (state independent, fully parallel) ...
-    unsigned char* ws = static_cast<unsigned char*>(workspace);
-    kda::IntraArgs ia{};
-    ia.lanes = lanes; ia.T = d->T; ia.nchunks = plan.nchunks; ia.dk = d->dk; ia.dv = d->dv;
-    ia.q = q; ia.k = k; ia.v = v; ia.la = log_alpha; ia.beta = beta;
-    ia.rec = ws;
-    if (kda::launch_intra(ia, st) != hipSuccess) return KDA_ERR_HIP;
-    a.rec = ws;
-    a.ws_pair = plan.pair_bytes ? reinterpret_cast<float*>(ws + plan.rec_bytes) : nullptr;
-    a.ws_entry = plan.entry_bytes ? reinterpret_cast<float*>(ws + plan.rec_bytes + plan.pair_bytes) : nullptr;
+size_t kda_chunk_fwd_varlen_workspace_bytes(const kda_varlen_desc* d) {
+    if (check_varlen_desc(d) != KDA_OK) return 0;
+    return make_plan(varlen_geometry(d)).ws_bytes;
+}
 
-    // ... then the sequential state pass
-    if (plan.nseg == 1) {
-        a.fin_seg_lo = 0; a.fin_nseg = 1; a.sum_seg_lo = 0; a.sum_nseg = 0;
-        return kda::launch_inter(a, st) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+kda_status kda_chunk_fwd_varlen(const kda_varlen_desc* d, const void* q, const void* k, const void* v,
+                                const void* log_alpha, const void* beta, const int32_t* cu_seqlens,
+                                const float* S0, void* o, float* S_T, float* S_ckpt, int32_t* ckpt_offsets,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+    const kda_status ds = check_varlen_desc(d);
+    if (ds != KDA_OK) return ds;
+    const bool packed = d->packed != 0;
+    if (packed != (cu_seqlens != nullptr)) return KDA_ERR_INVALID_ARG;
+    const int64_t lanes = d->N * d->H;
+    const int64_t row_lanes = packed ? d->H : lanes;   // row blocks of the row-major tensors
+    const int64_t eout = elem_bytes(d->out_dtype);
+    const int64_t state_bytes = lanes * d->dk * d->dv * (int64_t)sizeof(float);
+    const int64_t ck_states = d->ckpt_every > 0 ? (packed ? d->T / d->ckpt_every : d->N * (d->T / d->ckpt_every)) * d->H : 0;
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+
+    if (S0 && !aligned(S0, 16)) return KDA_ERR_INVALID_ARG;
+    if (S_T && !aligned(S_T, 16)) return KDA_ERR_INVALID_ARG;
+    if (S0 && S_T && S0 != S_T && overlaps(range_of(S0, state_bytes), range_of(S_T, state_bytes)))
+        return KDA_ERR_INVALID_ARG;
+    if (d->ckpt_every > 0) {
+        if (ck_states > 0 && (!S_ckpt || !aligned(S_ckpt, 16))) return KDA_ERR_INVALID_ARG;
+        if (packed && !ckpt_offsets) return KDA_ERR_INVALID_ARG;
     }
-    // pass 1: segment 0 from the known entry state; summaries of the middle segments
-    a.fin_seg_lo = 0; a.fin_nseg = 1; a.sum_seg_lo = 1; a.sum_nseg = plan.nseg - 2;
-    if (kda::launch_inter(a, st) != hipSuccess) return KDA_ERR_HIP;
-    // exact entry state of every later segment
-    if (kda::launch_segment_scan(a, st) != hipSuccess) return KDA_ERR_HIP;
-    // pass 2: every later segment from its exact entry state
-    a.fin_seg_lo = 1; a.fin_nseg = plan.nseg - 1; a.sum_seg_lo = 0; a.sum_nseg = 0;
-    return kda::launch_inter(a, st) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+    if (cu_seqlens && !aligned(cu_seqlens, 4)) return KDA_ERR_INVALID_ARG;
+    if (ckpt_offsets && !aligned(ckpt_offsets, 4)) return KDA_ERR_INVALID_ARG;
+    const Range rck = range_of(S_ckpt, ck_states * d->dk * d->dv * (int64_t)sizeof(float));
+    const Range rcko = range_of(ckpt_offsets, d->ckpt_every > 0 && ckpt_offsets ? (d->N + 1) * 4 : 0);
+    const Range rcu = range_of(cu_seqlens, packed ? (d->N + 1) * 4 : 0);
+    const Range rs0 = range_of(S0, S0 ? state_bytes : 0), rst = range_of(S_T, S_T ? state_bytes : 0);
+    const Range outs[] = {rck, rcko};
+    for (const Range& r : outs)
+        if (overlaps(r, rs0) || overlaps(r, rst) || overlaps(r, rcu)) return KDA_ERR_INVALID_ARG;
+    if (overlaps(rck, rcko) || overlaps(rcu, rst)) return KDA_ERR_INVALID_ARG;
+
+    const Geometry g = varlen_geometry(d);
+    const Plan plan = make_plan(g);
+    kda::VarlenPrep vp{};
+    vp.cu = cu_seqlens; vp.N = d->N; vp.rows = d->T; vp.max_len = packed ? d->max_len : d->T;
+    vp.ck_off = d->ckpt_every > 0 ? ckpt_offsets : nullptr; vp.ck_every = d->ckpt_every;
+
+    if (plan.nchunks == 0) {   // every sequence is empty
+        if (vp.ck_off && kda::launch_varlen_prep(vp, st) != hipSuccess) return KDA_ERR_HIP;
+        if (!S_T || S_T == S0) return KDA_OK;
+        return kda::launch_copy_or_zero(S_T, S0, state_bytes / 4, st) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+    }
+
+    if (!q || !k || !v || !log_alpha || !beta || !o) return KDA_ERR_INVALID_ARG;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(log_alpha, 16) || !aligned(o, 16) ||
+        !aligned(beta, 2))
+        return KDA_ERR_INVALID_ARG;
+    const int64_t nrow = row_lanes * d->T;
+    const Range ro = range_of(o, nrow * d->dv * eout);
+    const Range rin[] = {range_of(q, nrow * d->dk * 2), range_of(k, nrow * d->dk * 2), range_of(v, nrow * d->dv * 2),
+                         range_of(log_alpha, nrow * d->dk * 2), range_of(beta, nrow * 2), rcu};
+    for (const Range& r : rin)
+        if (overlaps(ro, r) || overlaps(rck, r) || overlaps(rcko, r)) return KDA_ERR_INVALID_ARG;
+    if (overlaps(ro, rs0) || overlaps(ro, rst) || overlaps(ro, rck) || overlaps(ro, rcko)) return KDA_ERR_INVALID_ARG;
+
+    if (!workspace || workspace_bytes < plan.ws_bytes) return KDA_ERR_WORKSPACE;
+    if (!aligned(workspace, 16)) return KDA_ERR_INVALID_ARG;
+    const Range rw = range_of(workspace, (int64_t)plan.ws_bytes);
+    if (overlaps(rw, ro) || overlaps(rw, rs0) || overlaps(rw, rst) || overlaps(rw, rck) || overlaps(rw, rcko))
+        return KDA_ERR_INVALID_ARG;
+    for (const Range& r : rin)
+        if (overlaps(rw, r)) return KDA_ERR_INVALID_ARG;
+
+    unsigned char* ws = static_cast<unsigned char*>(workspace);
+    kda::ChunkLaunch a{};
+    a.lanes = lanes; a.T = d->T; a.dk = d->dk; a.dv = d->dv;
+    a.nchunks = plan.nchunks;
+    a.in_bf16 = true; a.out_bf16 = d->out_dtype == KDA_BF16;
+    a.nseg = plan.nseg; a.chunks_per_seg = plan.chunks_per_seg;
+    a.q = q; a.k = k; a.v = v; a.la = log_alpha; a.beta = beta;
+    a.S0 = S0; a.o = o; a.S_T = S_T;
+    a.map.H = d->H;
+    if (packed) {
+        a.map.cu = cu_seqlens; a.map.H = d->H; a.map.rows = d->T; a.map.max_len = d->max_len;
+        a.map.slots = g.tab_slots;
+        vp.slots = g.tab_slots;
+        vp.slot_tab = reinterpret_cast<kda::SlotEntry*>(ws + plan.rec_bytes + plan.pair_bytes + plan.entry_bytes);
+    }
+    if (d->ckpt_every > 0 && ck_states > 0) {
+        a.ckpt = S_ckpt; a.ck_chunks = d->ckpt_every / kChunk; a.ck_cap = ck_states;
+        a.ck_per_lane = d->T / d->ckpt_every; a.ck_off = ckpt_offsets;
+    }
+    if ((packed || vp.ck_off) && kda::launch_varlen_prep(vp, st) != hipSuccess) return KDA_ERR_HIP;
+    return run_bf16(a, plan, ws, st);
 }
 
 kda_status kda_decode_step(const kda_decode_desc* d, const void* q, const void* k, const void* v,

@@ -12,6 +12,10 @@
 // read. The chunk loop is bound by that record stream; the stores of a chunk's output are issued
 // one chunk late, so that the wait for the next record copies does not also wait for them.
 //
+// A lane is one (batch, head) pair of a fixed-length batch or one (sequence, head) pair of a packed
+// batch of variable-length sequences (ChunkLaunch::map); a FINISH segment also stores the state
+// at every checkpoint interval it closes.
+//
 // Roles (one launch may mix them, see ChunkLaunch):
 //   FINISH  columns [0, dv): exact entry state in, o written, exit state stored as asked.
 //   SUMMARY columns [0, dv + dk) = [S~ | M] with entry [0 | I] and U = 0 on the M columns: the
@@ -44,7 +48,7 @@ struct __align__(16) InterSmem {
 
 // Copy this wave's share (blocks w, w + 4, ...) of the blocks of one chunk record that a role
 // reads (FINISH: all; SUMMARY: all but Q~ and A_qk) into an LDS buffer: one direct-to-LDS buffer
-// load per 1 KiB block; the descriptor covers the lane's records, offsets stay scalar. Every wave
+// load per 1 KiB block; the descriptor covers the chunk's record, offsets stay scalar. Every wave
 // issues the same count: indices past the end repeat the last block (the same bytes to the same
 // place), which keeps the copy free of branches.
 template <int DK, int DV, bool FIN>
@@ -166,9 +170,37 @@ __device__ __forceinline__ void run_segment(const ChunkLaunch& p, InterSmem<DK, 
     const int lq = l >> 4;
     const int64_t DVl = DV;
 
-    const int64_t nchunks = p.nchunks;
-    const int64_t c_begin = (int64_t)seg * p.chunks_per_seg;
-    const int64_t c_end = c_begin + p.chunks_per_seg < nchunks ? c_begin + p.chunks_per_seg : nchunks;
+    // ---- where the lane's rows, records and checkpoints are (see SeqMap) ---------------------
+    int64_t row_base, len, slot0, ck_base = 0, ck_stride = 1;
+    if (p.map.cu) {
+        const int64_t s = uniform64(lane / p.map.H), h = uniform64(lane % p.map.H);
+        const int64_t rows = p.map.rows;
+        int64_t c0 = p.map.cu[s], c1 = p.map.cu[s + 1];
+        c0 = c0 < 0 ? 0 : (c0 > rows ? rows : c0);
+        c1 = c1 < c0 ? c0 : (c1 > rows ? rows : c1);
+        len = c1 - c0 < p.map.max_len ? c1 - c0 : p.map.max_len;
+        row_base = h * rows + c0;
+        slot0 = h * p.map.slots + (c0 >> 6) + s;
+        if (p.ckpt) { ck_base = (int64_t)p.ck_off[s] * p.map.H + h; ck_stride = p.map.H; }
+    } else {
+        len = p.T;
+        row_base = lane * p.T;
+        slot0 = lane * p.nchunks;
+        if (p.ckpt) {   // sequence s = lane / H has its checkpoints at rows s * ck_per_lane + j - 1
+            const int64_t s = uniform64(lane / p.map.H), h = uniform64(lane % p.map.H);
+            ck_base = s * p.ck_per_lane * p.map.H + h;
+            ck_stride = p.map.H;
+        }
+    }
+    row_base = uniform64(row_base); len = uniform64(len); slot0 = uniform64(slot0);
+    ck_base = uniform64(ck_base); ck_stride = uniform64(ck_stride);
+    const int64_t nchunks = (len + kC - 1) / kC;
+    // the last segment runs to the lane's last chunk (a packed batch plans with its longest
+    // sequence); segments past a short lane's end are empty
+    int64_t c_begin = (int64_t)seg * p.chunks_per_seg;
+    int64_t c_end = seg == p.nseg - 1 ? nchunks : c_begin + p.chunks_per_seg;
+    if (c_end > nchunks) c_end = nchunks;
+    if (c_begin > c_end) c_begin = c_end;
     const int col0 = w * 16 * NT;   // FINISH: in [0, dv); SUMMARY: in [0, dv + dk)
 
     // ---- entry state: S[nt][M] holds rows 16M + 4lq + r, column col0 + 16nt + l16 ----------
@@ -197,10 +229,28 @@ __device__ __forceinline__ void run_segment(const ChunkLaunch& p, InterSmem<DK, 
         }
     }
 
-    const __amdgpu_buffer_rsrc_t rrec =
-        make_rsrc(p.rec + lane * nchunks * (int64_t)BYTES, (uint32_t)(nchunks * (int64_t)BYTES));
+    // one descriptor per chunk record: a lane's records may exceed 32-bit offsets
+    const unsigned char* rec0 = p.rec + slot0 * (int64_t)BYTES;
     const __amdgpu_buffer_rsrc_t ro =
-        make_rsrc(FIN ? (const TOut*)p.o + lane * p.T * DVl : nullptr, FIN ? (uint32_t)(p.T * DVl * sizeof(TOut)) : 0u);
+        make_rsrc(FIN ? (const TOut*)p.o + row_base * DVl : nullptr, FIN ? (uint32_t)(len * DVl * sizeof(TOut)) : 0u);
+    // State checkpoint after chunk cc when it closes a checkpoint interval inside the lane
+    // (FINISH only: the state is exact there). Stored right after the wait at the top of the
+    // next iteration, like the output, so that the wait does not cover these stores.
+    // (a macro, not a lambda: a lambda capturing the state array would put it in scratch)
+#define KDA_CKPT_STORE(cc)                                                                          \
+    do {                                                                                            \
+        const int64_t cc_ = (cc);                                                                   \
+        if (FIN && p.ckpt && (cc_ + 1) % p.ck_chunks == 0 && (cc_ + 1) * kC <= len) {               \
+            const int64_t idx_ = ck_base + ((cc_ + 1) / p.ck_chunks - 1) * ck_stride;               \
+            if (idx_ < p.ck_cap) {                                                                  \
+                float* dst_ = p.ckpt + idx_ * DK * DVl;                                             \
+                _Pragma("unroll") for (int nt = 0; nt < NT; ++nt)                                   \
+                _Pragma("unroll") for (int M = 0; M < NM; ++M)                                      \
+                _Pragma("unroll") for (int r = 0; r < 4; ++r)                                       \
+                    dst_[(int64_t)(16 * M + 4 * lq + r) * DVl + col0 + 16 * nt + l16] = S[nt][M][r]; \
+            }                                                                                       \
+        }                                                                                           \
+    } while (0)
 
     // Output of the previous chunk, stored one iteration late: vmcnt counts loads and stores
     // alike, so stores issued right after the wait complete in the shadow of the next chunk
@@ -211,12 +261,13 @@ __device__ __forceinline__ void run_segment(const ChunkLaunch& p, InterSmem<DK, 
 #pragma unroll
         for (int I = 0; I < 4; ++I) Opend[nt][I] = kZero4;
 
-    if (c_begin < c_end) copy_record<DK, DV, FIN>(rrec, (uint32_t)(c_begin * BYTES), sm.rec[0], w, l);
+    if (c_begin < c_end) copy_record<DK, DV, FIN>(make_rsrc(rec0 + c_begin * BYTES, BYTES), 0u, sm.rec[0], w, l);
     for (int64_t c = c_begin; c < c_end; ++c) {
         const int buf = (int)((c - c_begin) & 1);
         __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0): this wave's copies of chunk c landed
         __syncthreads();                        // ... and everyone's; buffer buf^1 is free again
         if (FIN && c > c_begin) {
+            KDA_CKPT_STORE(c - 1);
 #pragma unroll
             for (int I = 0; I < 4; ++I) {
                 const uint32_t row = (uint32_t)((c - 1) * kC + 16 * I + l16);
@@ -226,10 +277,11 @@ __device__ __forceinline__ void run_segment(const ChunkLaunch& p, InterSmem<DK, 
                               (TOut*)nullptr);
             }
         }
-        if (c + 1 < c_end) copy_record<DK, DV, FIN>(rrec, (uint32_t)((c + 1) * BYTES), sm.rec[buf ^ 1], w, l);
+        if (c + 1 < c_end) copy_record<DK, DV, FIN>(make_rsrc(rec0 + (c + 1) * BYTES, BYTES), 0u, sm.rec[buf ^ 1], w, l);
         chunk_step<TOut, DK, DV, NT, 0, NT, FIN>(sm.rec[buf], S, col0, Opend);
     }
     if (FIN && c_begin < c_end) {
+        KDA_CKPT_STORE(c_end - 1);
 #pragma unroll
         for (int I = 0; I < 4; ++I) {
             const uint32_t row = (uint32_t)((c_end - 1) * kC + 16 * I + l16);
@@ -240,6 +292,7 @@ __device__ __forceinline__ void run_segment(const ChunkLaunch& p, InterSmem<DK, 
         }
     }
 
+#undef KDA_CKPT_STORE
     // ---- exit state --------------------------------------------------------------------------
     float* dst = nullptr;
     int64_t ld_dst = DVl;

@@ -14,9 +14,29 @@ struct DecodeArgs {
     void* o;
 };
 
+// Where the rows of one lane live. Fixed-length batches: lane = b*H + h owns rows
+// [lane*T, lane*T + T) of q, k, v, log_alpha, beta and o, and records [lane*nchunks, ...).
+// Packed variable-length batches (cu != NULL): lane = s*H + h, sequence s is rows
+// [cu[s], cu[s+1]) of head h's block of `rows` rows, and its chunk c has record slot
+// h*slots + cu[s]/64 + s + c (a slot index that never collides, whatever the lengths).
+struct SeqMap {
+    const int32_t* cu;      // [N + 1] device cumulative lengths, or NULL for equal lengths T
+    int64_t H;              // heads (lanes = N * H; set in both modes)
+    int64_t rows;           // packed rows per head (cu != NULL) or T
+    int64_t max_len;        // longest sequence processed (longer ones are cut to it)
+    int64_t slots;          // record slots per head (cu != NULL) or per lane (= nchunks)
+};
+
+// Per-chunk slot table entry of a packed batch: first row of the chunk inside its head's block
+// and the number of valid rows (0 for a slot no chunk owns).
+struct SlotEntry {
+    int32_t row0, nrows;
+};
+
 // One launch of the chunk kernels. Blocks [0, n_fin) run FINISH work (exact entry state, write
 // o and, for the last segment, S_T); the following n_sum blocks run SUMMARY work (affine pair
-// of a segment, no o). Every segment covers `chunks_per_seg` chunks of 64 tokens.
+// of a segment, no o). Every segment covers `chunks_per_seg` chunks of 64 tokens; the last
+// segment of a lane runs to the lane's last chunk.
 struct ChunkLaunch {
     int64_t lanes, T, dk, dv;
     int64_t nchunks;
@@ -29,16 +49,36 @@ struct ChunkLaunch {
     const float* S0;        // entry state of segment 0 (NULL = zero)
     void* o;
     float* S_T;             // exit state of the last segment (NULL = not stored)
-    const unsigned char* rec;   // [lanes][nchunks] intra-chunk records (bf16 path)
+    const unsigned char* rec;   // intra-chunk records (bf16 path), see SeqMap
     float* ws_pair;         // [lanes][nseg][dk][dv + dk]   affine pairs [S~ | M]
     float* ws_entry;        // [lanes][nseg][dk][dv]        exact entry state of each segment
+    SeqMap map;
+    // State checkpoints (bf16 path): after every ck_chunks chunks of a lane (s, h), the state
+    // goes to ckpt[(ck_off[s] + j - 1) * H + h] (packed) or ckpt[(s * ck_per_lane + j - 1) * H + h]
+    // (equal lengths), dk x dv fp32 each, with H = map.H; indices at or beyond ck_cap states are
+    // dropped.
+    float* ckpt;            // NULL = no checkpoints
+    int64_t ck_chunks, ck_cap, ck_per_lane;
+    const int32_t* ck_off;  // [N + 1] (packed batches)
 };
 
-// The intra-chunk kernel over every chunk of every lane (bf16 inputs).
+// The intra-chunk kernel over every record slot (bf16 inputs): slots = map.slots per head of
+// map.H heads (packed) or per lane of `lanes` lanes (fixed).
 struct IntraArgs {
     int64_t lanes, T, nchunks, dk, dv;
     const void *q, *k, *v, *la, *beta;
-    unsigned char* rec;     // [lanes][nchunks] records, record_bytes(dk, dv) each
+    unsigned char* rec;     // record_bytes(dk, dv) per slot
+    const SlotEntry* slot_tab;  // [map.slots] for a packed batch, NULL for a fixed one
+    SeqMap map;
+};
+
+// Slot table and checkpoint offsets of a packed batch.
+struct VarlenPrep {
+    const int32_t* cu;
+    int64_t N, rows, max_len, slots;
+    SlotEntry* slot_tab;    // [slots]
+    int32_t* ck_off;        // [N + 1] or NULL
+    int64_t ck_every;       // tokens per checkpoint (> 0 when ck_off is set)
 };
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st);
@@ -49,6 +89,7 @@ hipError_t launch_intra(const IntraArgs& a, hipStream_t st);
 hipError_t launch_inter(const ChunkLaunch& a, hipStream_t st);
 // entry_{s+1} = S~_s + M_s entry_s for s in [1, nseg-1), entry_1 already stored.
 hipError_t launch_segment_scan(const ChunkLaunch& a, hipStream_t st);
+hipError_t launch_varlen_prep(const VarlenPrep& a, hipStream_t st);
 // dst[i] = src ? src[i] : 0 for n floats (graph-capture safe replacement for memcpy/memset).
 hipError_t launch_copy_or_zero(float* dst, const float* src, int64_t n, hipStream_t st);
 

@@ -3,7 +3,9 @@
 // section 2.2: cumulative decay Gamma, the decay-weighted Gram tiles and the UT transform).
 //
 // Every chunk of every lane is independent. A persistent grid of two workgroups (4 waves each) per
-// compute unit walks the (lane, chunk) pairs, loading the next chunk's raw rows into registers
+// compute unit walks the record slots (the chunks of every lane; for a packed batch of
+// variable-length sequences, the chunk slots of every head, which a small table maps to rows),
+// loading the next chunk's raw rows into registers
 // while it solves the current one (and while the other workgroup on the compute unit runs), so
 // the kernel is bound by HBM traffic, not by latency. Input
 // loads are row-contiguous (64 bytes per row per wave). Output: the chunk's record
@@ -117,7 +119,7 @@ struct __align__(16) IntraSmem {
     bf16_t fij[6][DK];          // exp(G_ref(I) - G_ref(J)) per channel for the pairs I > J
 };
 
-template <int DK, int DV>
+template <int DK, int DV, bool PACKED>
 __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs p) {
     typedef IntraCfg<DK, DV> Cfg;
     typedef RecordLayout<DK, DV> R;
@@ -130,8 +132,11 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs p) {
     const int l16 = l & 15;
     const int lq = l >> 4;
 
-    const int64_t T = p.T;
-    const int64_t total = p.lanes * p.nchunks;
+    // work items: record slots, `slots` per head (packed batch) or per lane (fixed length),
+    // fewer than 2^31 in all; `rows` rows of every row-major input per head / lane
+    const uint32_t slots = (uint32_t)(PACKED ? p.map.slots : p.nchunks);
+    const int64_t rows = PACKED ? p.map.rows : p.T;
+    const uint32_t total = (uint32_t)((PACKED ? p.map.H : p.lanes) * (int64_t)slots);
     unsigned char* reg = sm.region[w];
     bf16_t* stA = reinterpret_cast<bf16_t*>(reg);                    // g, then K- (token-major)
     unsigned char* stB = reg + Cfg::STAGE_A;                         // v, then blocks
@@ -148,42 +153,66 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs p) {
     // 32w + 16h + 4lq .. +3 for h = 0, 1.
     const int qk_off = 8 * (((lq & 1) << 1) | (lq >> 1));
 
-    // Raw inputs of one chunk, loaded one chunk ahead. Rows at or past T read as zeros.
+    // Raw inputs of one chunk, loaded one chunk ahead. Rows past the chunk's valid rows (the end
+    // of the sequence) read as zeros: every descriptor starts at the chunk's first row and
+    // covers its valid rows only.
     uint4 pq[4], pk[4], pg[4], pv[LPR];
     uint32_t pb = 0;
-#define KDA_INTRA_LOAD(tt)                                                                          \
+    // per-lane byte offsets inside a chunk. Row offsets stay in the vector offset, the part of
+    // the address the buffer range check sees (the scalar offset is not range-checked); the
+    // empty asm in the load stops the compiler from hoisting one register per row group.
+    const uint32_t qk_voff = (l16 * DK + 32 * w + qk_off) * 2;
+    const uint32_t g_voff = ((l >> 2) * DK + 32 * w + 8 * (l & 3)) * 2;
+    const uint32_t v_voff = ((l / LPR) * DV + vc0 + 8 * (l % LPR)) * 2;
+#define KDA_INTRA_LOAD(ok, hh, jj)                                                                  \
     do {                                                                                            \
-        const bool ok_ = (tt) < total;   /* past the end: empty descriptors, zeros, no traffic */   \
-        const int64_t c_ = ok_ ? uniform64((tt) % p.nchunks) : 0;                                   \
-        const int64_t lane_ = ok_ ? uniform64((tt) / p.nchunks) : 0;                                \
-        const uint32_t r0_ = (uint32_t)(c_ * kC);                                                   \
-        const uint32_t nk_ = ok_ ? (uint32_t)(T * DK * 2) : 0u, nv_ = ok_ ? (uint32_t)(T * DV * 2) : 0u; \
+        int64_t row_ = 0;                /* first row of the chunk in the row-major tensors */     \
+        uint32_t n_ = 0;                 /* valid rows; 0 past the end: zeros, no traffic */       \
+        if (ok) {                                                                                   \
+            if (PACKED) {                                                                           \
+                const SlotEntry e_ = p.slot_tab[jj];                                                \
+                row_ = (int64_t)(hh) * rows + e_.row0;                                              \
+                n_ = (uint32_t)e_.nrows;                                                            \
+            } else {                                                                                \
+                row_ = (int64_t)(hh) * rows + (int64_t)(jj) * kC;                                   \
+                n_ = (uint32_t)(rows - (int64_t)(jj) * kC < kC ? rows - (int64_t)(jj) * kC : kC);   \
+            }                                                                                       \
+        }                                                                                           \
         if (kw) {                                                                                   \
-            const __amdgpu_buffer_rsrc_t rq_ = make_rsrc((const bf16_t*)p.q + lane_ * T * DK, nk_);   \
-            const __amdgpu_buffer_rsrc_t rk_ = make_rsrc((const bf16_t*)p.k + lane_ * T * DK, nk_);   \
-            const __amdgpu_buffer_rsrc_t rg_ = make_rsrc((const bf16_t*)p.la + lane_ * T * DK, nk_);  \
+            const uint32_t nk_ = n_ * (DK * 2);                                                     \
+            const __amdgpu_buffer_rsrc_t rq_ = make_rsrc((const bf16_t*)p.q + row_ * DK, nk_);       \
+            const __amdgpu_buffer_rsrc_t rk_ = make_rsrc((const bf16_t*)p.k + row_ * DK, nk_);       \
+            const __amdgpu_buffer_rsrc_t rg_ = make_rsrc((const bf16_t*)p.la + row_ * DK, nk_);      \
+            uint32_t qo_ = qk_voff, go_ = g_voff;                                                   \
+            asm volatile("" : "+v"(qo_), "+v"(go_));   /* keeps the row offsets below in the loop */ \
             _Pragma("unroll") for (int I_ = 0; I_ < 4; ++I_) {                                      \
-                const uint32_t o_ = ((r0_ + 16 * I_ + l16) * DK + 32 * w + qk_off) * 2;               \
-                pq[I_] = buf_load16(rq_, o_);                                                       \
-                pk[I_] = buf_load16(rk_, o_);                                                       \
-                pg[I_] = buf_load16(rg_, ((r0_ + 16 * I_ + (l >> 2)) * DK + 32 * w + 8 * (l & 3)) * 2); \
+                pq[I_] = buf_load16(rq_, qo_ + 16 * I_ * DK * 2);                                   \
+                pk[I_] = buf_load16(rk_, qo_ + 16 * I_ * DK * 2);                                   \
+                pg[I_] = buf_load16(rg_, go_ + 16 * I_ * DK * 2);                                   \
             }                                                                                       \
         }                                                                                           \
         if (vw) {                                                                                   \
-            const __amdgpu_buffer_rsrc_t rv_ = make_rsrc((const bf16_t*)p.v + lane_ * T * DV, nv_);   \
+            const __amdgpu_buffer_rsrc_t rv_ = make_rsrc((const bf16_t*)p.v + row_ * DV, n_ * (DV * 2)); \
+            uint32_t vo_ = v_voff;                                                                  \
+            asm volatile("" : "+v"(vo_));                                                           \
             _Pragma("unroll") for (int i_ = 0; i_ < LPR; ++i_)                                      \
-                pv[i_] = buf_load16(rv_, ((r0_ + i_ * (64 / LPR) + l / LPR) * DV + vc0 + 8 * (l % LPR)) * 2); \
+                pv[i_] = buf_load16(rv_, vo_ + i_ * (64 / LPR) * DV * 2);                           \
         }                                                                                           \
         if (w == 0) {                                                                               \
-            const __amdgpu_buffer_rsrc_t rb_ = make_rsrc((const bf16_t*)p.beta + lane_ * T, ok_ ? (uint32_t)(T * 2) : 0u); \
-            pb = buf_load2(rb_, (r0_ + l) * 2);                                                     \
+            const __amdgpu_buffer_rsrc_t rb_ = make_rsrc((const bf16_t*)p.beta + row_, n_ * 2);     \
+            pb = buf_load2(rb_, l * 2);                                                             \
         }                                                                                           \
     } while (0)
 
     // Persistent: workgroup b takes chunks b, b + gridDim.x, ... of the flattened (lane, chunk)
     // index, so the loads of the next chunk overlap the Gram tiles and solve of this one.
-    int64_t t = blockIdx.x;
-    KDA_INTRA_LOAD(t);
+    // Item t is (head or lane t / slots, slot t % slots); the pair advances by the grid size
+    // without dividing again.
+    const uint32_t G = gridDim.x;
+    const uint32_t step_h = G / slots, step_j = G % slots;
+    uint32_t t = blockIdx.x;
+    uint32_t hn = t / slots, jn = t % slots;   // the item whose rows are (being) loaded
+    KDA_INTRA_LOAD(t < total, hn, jn);
     // taken here too, so that the loop head (which merges this path with the loop's back edge)
     // carries no wait for loads
 #pragma unroll
@@ -191,10 +220,10 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs p) {
 #pragma unroll
     for (int i = 0; i < LPR; ++i) pin(pv[i]);
     pin(pb);
-    for (; t < total; t += gridDim.x) {
-    const int64_t c = uniform64(t % p.nchunks);
-    const int64_t lane = uniform64(t / p.nchunks);
-    unsigned char* rec = p.rec + (lane * p.nchunks + c) * (int64_t)R::BYTES;
+    for (; t < total; t += G) {
+    unsigned char* rec = p.rec + (int64_t)t * R::BYTES;
+    jn += step_j; hn += step_h;
+    if (jn >= slots) { jn -= slots; ++hn; }
     auto blk = [&](int b) -> unsigned char* { return rec + b * 1024 + l * 16; };
 
     // ================= phase 1: decay and scaled operands (wave-local) =========================
@@ -223,7 +252,7 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs p) {
         if (w == 0) sm.beta[l] = __uint_as_float(pb << 16);
         // the next chunk's rows load while this one is processed (the prefetch registers are free
         // again once consumed above)
-        KDA_INTRA_LOAD(t + gridDim.x);
+        KDA_INTRA_LOAD(t + G < total, hn, jn);
         wave_lds_sync();
         if (vw) {
 #pragma unroll
@@ -512,10 +541,13 @@ int resident_workgroups() {
 
 template <int DK, int DV>
 hipError_t launch_dd(const IntraArgs& a, hipStream_t st) {
-    int64_t blocks = a.lanes * a.nchunks;
+    int64_t blocks = a.slot_tab ? a.map.H * a.map.slots : a.lanes * a.nchunks;
     if (blocks <= 0) return hipSuccess;
     if (blocks > resident_workgroups()) blocks = resident_workgroups();
-    hipLaunchKernelGGL((intra_kernel<DK, DV>), dim3((unsigned)blocks), dim3(256), 0, st, a);
+    if (a.slot_tab)
+        hipLaunchKernelGGL((intra_kernel<DK, DV, true>), dim3((unsigned)blocks), dim3(256), 0, st, a);
+    else
+        hipLaunchKernelGGL((intra_kernel<DK, DV, false>), dim3((unsigned)blocks), dim3(256), 0, st, a);
     return hipGetLastError();
 }
 

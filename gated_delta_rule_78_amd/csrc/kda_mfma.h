@@ -76,13 +76,15 @@ __device__ __forceinline__ float row_bcast15(float x) {
 }
 
 // Raw buffer access (gfx9 descriptor): an offset at or beyond num_records reads zeros and drops
-// stores, so rows past the end of a sequence need neither clamping nor branches.
+// stores, so rows past the end of a sequence need neither clamping nor branches. The address is
+// base + voffset (per lane) + soffset (uniform), but only voffset is range-checked against
+// num_records: an offset that must read as zero past the end belongs in voffset.
 constexpr int32_t kBufFlags = 0x00020000;
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufFlags);
 }
-__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t soff = 0) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, (int)soff, 0));
 }
 __device__ __forceinline__ uint2 buf_load8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
     return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0));

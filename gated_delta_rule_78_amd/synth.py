@@ -102,6 +102,42 @@ def workload_inputs(w: PrefillWorkload, device="cpu", seed_base: int = 1000, T: 
                           w.s0_std, log_alpha_range)
 
 
+# Packed batch standing in for a prefill batch of mixed request lengths: 8192 tokens per head in
+# 12 sequences (lengths from a few tens to 2.5K, three of them multiples of 512, most ragged),
+# 32 heads, d = 128, checkpoints every 512 tokens (the 512-token hash blocks of a prefix cache).
+PACKED_BF16_8K_LENS = (2500, 1536, 1024, 900, 700, 512, 413, 300, 150, 90, 40, 27)
+PACKED_BF16_8K = PrefillWorkload("prefill bf16 packed 12 seqs (8192 tokens) H=32 d=128 C=64, checkpoints every 512",
+                                 12, 32, 8192, 128, torch.bfloat16)
+
+
+def packed_inputs(lens, H: int, dk: int, dv: int, dtype, device="cpu", seed_base: int = 5000,
+                  s0_std: Optional[float] = None, log_alpha_range: Tuple[float, float] = LOG_ALPHA_RANGE):
+    """A packed batch: sequence s (length lens[s]) is rows cu[s]..cu[s+1]-1 of every head.
+    Returns q,k,log_alpha [H,T,dk]; v [H,T,dv]; beta [H,T]; cu_seqlens int32 [N+1];
+    S0 [N,H,dk,dv] fp32 or None. Lane (s, h) is seeded with seed_base + s*H + h."""
+    N = len(lens)
+    cu = [0]
+    for n in lens:
+        cu.append(cu[-1] + int(n))
+    T = cu[-1]
+    q = torch.empty(H, T, dk, dtype=dtype, device=device)
+    k = torch.empty_like(q)
+    la = torch.empty_like(q)
+    v = torch.empty(H, T, dv, dtype=dtype, device=device)
+    beta = torch.empty(H, T, dtype=dtype, device=device)
+    S0 = None if s0_std is None else torch.empty(N, H, dk, dv, dtype=torch.float32, device=device)
+    for s in range(N):
+        a, b = cu[s], cu[s + 1]
+        for h in range(H):
+            seed = seed_base + s * H + h
+            lq, lk, lv, lla, lb = lane_inputs(b - a, dk, dv, dtype, seed, device, log_alpha_range)
+            q[h, a:b], k[h, a:b], v[h, a:b], la[h, a:b], beta[h, a:b] = lq, lk, lv, lla, lb
+            if S0 is not None:
+                S0[s, h] = torch.randn(dk, dv, generator=_gen(device, seed + 7_000_000), device=device,
+                                       dtype=torch.float32) * s0_std
+    return q, k, v, la, beta, torch.tensor(cu, dtype=torch.int32, device=device), S0
+
+
 def decode_state(N: int, H: int, dk: int, dv: int, std: float, device="cpu", seed: int = 3000):
     """Fixed-size fp32 state [N,H,dk,dv] ~ N(0, std)."""
     return torch.randn(N, H, dk, dv, generator=_gen(device, seed), device=device, dtype=torch.float32) * std

@@ -112,6 +112,73 @@ kda_status kda_chunk_fwd(const kda_chunk_desc* desc,
                          const float* S0, void* o, float* S_T,
                          void* workspace, size_t workspace_bytes, void* stream);
 
+/* Shape and types of one prefill call over a batch of sequences with checkpoints. */
+typedef struct kda_varlen_desc {
+    int64_t N;          /* sequences, >= 1                                                */
+    int64_t H;          /* heads, >= 1                                                    */
+    int64_t T;          /* packed: rows per head (= cu_seqlens[N]); else tokens per
+                           sequence. >= 0                                                 */
+    int64_t max_len;    /* packed: bound on every sequence length (plans the sequence
+                           split); ignored otherwise. max_len * max(dk,dv) * 4 < 2^31     */
+    int64_t dk;         /* key dimension: 64 or 128                                       */
+    int64_t dv;         /* value dimension: 64 or 128                                     */
+    int32_t chunk;      /* chunk length C: must be 64                                     */
+    int32_t in_dtype;   /* must be KDA_BF16                                               */
+    int32_t out_dtype;  /* kda_dtype of o                                                 */
+    int32_t segments;   /* sequence segments per lane: 0 = library's choice, n >= 1 = n   */
+    int32_t ckpt_every; /* 0 = no checkpoints, else a positive multiple of 64 (e.g. 512)  */
+    int32_t packed;     /* 1: sequences packed along T, described by cu_seqlens;
+                           0: N sequences of T tokens in kda_chunk_fwd's layout (B = N)   */
+} kda_varlen_desc;
+
+/* Bytes of device workspace kda_chunk_fwd_varlen needs for `desc` (0 for an invalid desc).
+ * The same records, affine pairs and entry states as kda_chunk_fwd's workspace; a packed
+ * batch lays out records in T/64 + N chunk slots per head (sequence s's chunk c in slot
+ * cu_seqlens[s]/64 + s + c, which never collide whatever the lengths) and adds a table of
+ * 8 bytes per slot. */
+size_t kda_chunk_fwd_varlen_workspace_bytes(const kda_varlen_desc* desc);
+
+/*
+ * Chunkwise KDA prefill over a batch of sequences, with state checkpoints:
+ * kda_chunk_fwd_varlen(q,k,v,log_alpha,beta,cu_seqlens,S0) -> (o, S_T, S_ckpt, ckpt_offsets).
+ * Each (sequence s, head h) pair is an independent lane computing exactly what
+ * kda_chunk_fwd computes for one lane (its chunks start at the sequence's first token).
+ *  packed = 1: q, k, log_alpha : [H,T,dk] bf16   v : [H,T,dv] bf16   beta : [H,T] bf16
+ *              o : [H,T,dv] out_dtype. Sequence s is rows cu_seqlens[s] .. cu_seqlens[s+1]-1
+ *              of every head (the [1,H,T,d] tensors of kda_chunk_fwd with the sequences
+ *              back to back along T). cu_seqlens: DEVICE int32 [N+1], cu_seqlens[0] = 0,
+ *              non-decreasing, cu_seqlens[N] = T, every length <= max_len. The library reads
+ *              it on the device only. Lengths that break these rules give undefined numbers but
+ *              no access outside the tensors (rows are clamped into [0, T], lengths cut to
+ *              max_len; o rows past a cut length are left untouched).
+ *  packed = 0: cu_seqlens must be NULL; tensors as kda_chunk_fwd with B = N.
+ *  S0, S_T    : [N,H,dk,dv] fp32 as in kda_chunk_fwd (S0 NULL = zero state, S_T NULL = skip,
+ *               S_T may be S0).
+ *  Checkpoints (ckpt_every = E > 0): after every E tokens of a sequence (tokens counted from
+ *  the sequence's first row, i.e. from the state S0 stands for), the state of every head is
+ *  written: for sequence s and j = 1 .. floor(len_s / E), the state after its first j*E tokens
+ *  goes to S_ckpt[(ckpt_offsets[s] + j - 1) * H + h] (dk x dv fp32 each): one checkpoint holds
+ *  all heads of a sequence at one endpoint, the unit a prefix cache restores. ckpt_offsets
+ *  (DEVICE int32 [N+1], written) receives the exclusive prefix sum of floor(len_s / E), its
+ *  last entry the total. S_ckpt must hold floor(T/E) * H states (packed) or N * floor(T/E) * H
+ *  (packed = 0); checkpoints beyond that capacity are dropped. With packed = 0, ckpt_offsets
+ *  may be NULL (its values are s * floor(T/E)); with packed = 1 it is required.
+ *  With E = 0, S_ckpt and ckpt_offsets are ignored.
+ *  workspace  : at least kda_chunk_fwd_varlen_workspace_bytes(desc) bytes.
+ * No output may overlap an input or another output (S_T = S0 aside). A call whose sequences
+ * are all empty writes S_T = S0 (or zeros) and the offsets, nothing else.
+ * Source: section 2.5 of the Kimi K3 reading notes and its Figure 12 (a prefix cache with
+ * 6144-token physical blocks and 512-token hash blocks keeps KDA checkpoints only at the
+ * hash-queryable endpoints; a hit at boundary B restores the checkpoint and continues prefill
+ * from B); the per-lane arithmetic is section 2.2's, as in kda_chunk_fwd.
+ */
+kda_status kda_chunk_fwd_varlen(const kda_varlen_desc* desc,
+                                const void* q, const void* k, const void* v,
+                                const void* log_alpha, const void* beta,
+                                const int32_t* cu_seqlens, const float* S0, void* o, float* S_T,
+                                float* S_ckpt, int32_t* ckpt_offsets,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
 /*
  * One KDA decode step: kda_decode_step(q,k,v,log_alpha,beta,S) -> (o, S').
  *   q, k, log_alpha : [N,H,dk] in_dtype        v : [N,H,dv] in_dtype

@@ -16,7 +16,7 @@
  *
  * Inputs are fp32 arrays (a bf16 or fp32 value widens to fp32 exactly); every operation runs in
  * fp64. Layouts: q,k,log_alpha [BH][T][dk]; v [BH][T][dv]; beta [BH][T]; S0 [BH][dk][dv]
- * (NULL = zero state); o [BH][nrows][dv]; S_T [BH][dk][dv].
+ * (NULL = zero state); o [BH][nrows][dv]; S_T [BH][dk][dv]; checkpoints [BH][T/E][dk][dv].
  * Columns of the value dimension evolve independently (column j of S and o only ever meets
  * column j of v), so the work is split over (lane, column block) with identical arithmetic.
  */
@@ -30,7 +30,7 @@
 static int run_task(int64_t T, int64_t dk, int64_t dv, int64_t j0, int64_t j1,
                     const float* q, const float* k, const float* v, const float* la,
                     const float* beta, const float* S0, const int64_t* rows, int64_t nrows,
-                    double* o, double* ST)
+                    double* o, double* ST, int64_t ckpt_every, double* ckpt)
 {
     const int64_t w = j1 - j0;
     double* S = (double*)malloc(sizeof(double) * (size_t)(dk * w));
@@ -74,6 +74,12 @@ static int run_task(int64_t T, int64_t dk, int64_t dv, int64_t j0, int64_t j1,
             }
             for (int64_t j = 0; j < w; ++j) o[orow * dv + j0 + j] = r[j];
         }
+        /* checkpoint: the state after tokens 0..t when t + 1 is a multiple of ckpt_every */
+        if (ckpt && ckpt_every > 0 && (t + 1) % ckpt_every == 0) {
+            double* dst = ckpt + ((t + 1) / ckpt_every - 1) * dk * dv;
+            for (int64_t c = 0; c < dk; ++c)
+                for (int64_t j = 0; j < w; ++j) dst[c * dv + j0 + j] = S[c * w + j];
+        }
     }
     if (ST)
         for (int64_t c = 0; c < dk; ++c)
@@ -83,13 +89,15 @@ static int run_task(int64_t T, int64_t dk, int64_t dv, int64_t j0, int64_t j1,
 }
 
 /* Returns 0 on success, -1 on bad arguments or allocation failure. `rows` (sorted, strictly
- * increasing, each in [0,T)) selects which tokens' outputs are stored; NULL stores all T. */
+ * increasing, each in [0,T)) selects which tokens' outputs are stored; NULL stores all T.
+ * With ckpt_every = E > 0 and ckpt != NULL, ckpt [BH][T/E][dk][dv] receives the state after the
+ * first j*E tokens, j = 1 .. T/E (the prefix-cache checkpoints of section 2.5 / Figure 12). */
 int kda_oracle_fwd(int64_t BH, int64_t T, int64_t dk, int64_t dv,
                    const float* q, const float* k, const float* v, const float* log_alpha,
                    const float* beta, const float* S0, const int64_t* rows, int64_t nrows,
-                   double* o, double* S_T, int nthreads)
+                   double* o, double* S_T, int64_t ckpt_every, double* ckpt, int nthreads)
 {
-    if (BH < 0 || T < 0 || dk <= 0 || dv <= 0) return -1;
+    if (BH < 0 || T < 0 || dk <= 0 || dv <= 0 || ckpt_every < 0) return -1;
     if (T > 0 && (!q || !k || !v || !log_alpha || !beta)) return -1;
     if (rows) {
         for (int64_t i = 0; i < nrows; ++i)
@@ -98,6 +106,7 @@ int kda_oracle_fwd(int64_t BH, int64_t T, int64_t dk, int64_t dv,
     const int64_t nblk = (dv + COLS_PER_TASK - 1) / COLS_PER_TASK;
     const int64_t ntask = BH * nblk;
     const int64_t orows = rows ? nrows : T;
+    const int64_t nck = ckpt_every > 0 ? T / ckpt_every : 0;
     int failed = 0;
 #pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads > 0 ? nthreads : 1) reduction(| : failed)
     for (int64_t task = 0; task < ntask; ++task) {
@@ -107,7 +116,8 @@ int kda_oracle_fwd(int64_t BH, int64_t T, int64_t dk, int64_t dv,
         const int64_t xo = lane * T * dk, vo = lane * T * dv;
         failed |= run_task(T, dk, dv, j0, j1, q + xo, k + xo, v + vo, log_alpha + xo, beta + lane * T,
                            S0 ? S0 + lane * dk * dv : NULL, rows, nrows,
-                           o ? o + lane * orows * dv : NULL, S_T ? S_T + lane * dk * dv : NULL) != 0;
+                           o ? o + lane * orows * dv : NULL, S_T ? S_T + lane * dk * dv : NULL,
+                           ckpt_every, ckpt ? ckpt + lane * nck * dk * dv : NULL) != 0;
     }
     return failed ? -1 : 0;
 }

@@ -30,8 +30,9 @@ def lib():
 
 
 def test_header_declares_the_boundary():
-    assert declared_functions() == ["kda_chunk_fwd", "kda_chunk_fwd_workspace_bytes", "kda_decode_step",
-                                    "kda_status_string", "kda_version"]
+    assert declared_functions() == ["kda_chunk_fwd", "kda_chunk_fwd_varlen", "kda_chunk_fwd_varlen_workspace_bytes",
+                                    "kda_chunk_fwd_workspace_bytes", "kda_decode_step", "kda_status_string",
+                                    "kda_version"]
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -122,3 +123,54 @@ def test_decode_rejects_bad_arguments(lib):
     assert _decode(lib, d, S=FAKE + (5 << 30) + 4) == INVALID           # misaligned state
     assert _decode(lib, d, o=FAKE + (5 << 30) + 64) == INVALID          # o overlaps S
     assert _decode(lib, d, q=FAKE + (5 << 30) + 256) == INVALID         # input overlaps S
+
+
+# ---- packed variable-length batches with checkpoints (kda_chunk_fwd_varlen) ----
+
+def _vdesc(N=3, H=2, T=640, max_len=512, dk=128, dv=128, chunk=64, ind=1, outd=1, seg=0, ck=0, packed=1):
+    return kda.VarlenDesc(N, H, T, max_len, dk, dv, chunk, ind, outd, seg, ck, packed)
+
+
+def _varlen(lib, d, cu=FAKE + (6 << 30), S0=None, ST=None, ckpt=None, ckoff=None, ws=FAKE + (8 << 30),
+            ws_bytes=1 << 40, q=FAKE, o=FAKE + (5 << 30)):
+    P = ctypes.c_void_p
+    return lib.kda_chunk_fwd_varlen(None if d is None else ctypes.byref(d), P(q), P(FAKE + (1 << 30)),
+                                    P(FAKE + (2 << 30)), P(FAKE + (3 << 30)), P(FAKE + (4 << 30)), P(cu), P(S0),
+                                    P(o), P(ST), P(ckpt), P(ckoff), P(ws), ws_bytes, None)
+
+
+def test_varlen_rejects_bad_arguments(lib):
+    assert _varlen(lib, None) == INVALID
+    assert _varlen(lib, _vdesc(), cu=None) == INVALID                      # packed needs cu_seqlens
+    assert _varlen(lib, _vdesc(packed=0)) == INVALID                       # equal lengths take no cu_seqlens
+    assert _varlen(lib, _vdesc(packed=2)) == INVALID
+    assert _varlen(lib, _vdesc(ck=100)) == INVALID                         # not a multiple of 64
+    assert _varlen(lib, _vdesc(ck=-64)) == INVALID
+    assert _varlen(lib, _vdesc(ind=0)) == UNSUPPORTED                      # bf16 inputs only
+    assert _varlen(lib, _vdesc(chunk=32)) == UNSUPPORTED
+    assert _varlen(lib, _vdesc(dk=96)) == UNSUPPORTED
+    assert _varlen(lib, _vdesc(max_len=1 << 22)) == UNSUPPORTED            # 32-bit output offsets
+    assert _varlen(lib, _vdesc(N=0)) == INVALID
+    assert _varlen(lib, _vdesc(ck=512)) == INVALID                         # checkpoints need S_ckpt ...
+    assert _varlen(lib, _vdesc(ck=512), ckpt=FAKE + (9 << 30)) == INVALID  # ... and (packed) the offsets
+    assert _varlen(lib, _vdesc(), cu=FAKE + (6 << 30) + 2) == INVALID      # misaligned cu_seqlens
+    assert _varlen(lib, _vdesc(), o=FAKE + 64) == INVALID                  # o overlaps q
+    assert _varlen(lib, _vdesc(ck=512), ckpt=FAKE + (9 << 30), ckoff=FAKE + (9 << 30) + 64) == INVALID  # overlap
+
+
+def test_varlen_workspace_query_and_check(lib):
+    N, H, T, dk, dv = 3, 2, 640, 128, 128
+    d = _vdesc(N=N, H=H, T=T, max_len=512, seg=1)
+    need = lib.kda_chunk_fwd_varlen_workspace_bytes(ctypes.byref(d))
+    slots = T // 64 + N   # chunk slots per head: sequence s's chunk c sits in slot cu[s]/64 + s + c
+    assert need == H * slots * record_bytes(dk, dv) + slots * 8
+    # with a split of the longest sequence (8 chunks) into 4 segments: affine pairs and entries per lane
+    d4 = _vdesc(N=N, H=H, T=T, max_len=512, seg=4)
+    assert lib.kda_chunk_fwd_varlen_workspace_bytes(ctypes.byref(d4)) == need + N * H * 4 * dk * (2 * dv + dk) * 4
+    assert _varlen(lib, d, ws=None, ws_bytes=0) == WORKSPACE
+    assert _varlen(lib, d, ws_bytes=need - 1) == WORKSPACE
+    assert _varlen(lib, d, ws=FAKE + (8 << 30) + 8, ws_bytes=need) == INVALID
+    # equal lengths: the fixed-length call's workspace with B = N
+    e = _vdesc(N=N, H=H, T=T, seg=1, packed=0)
+    assert lib.kda_chunk_fwd_varlen_workspace_bytes(ctypes.byref(e)) == N * H * (T // 64) * record_bytes(dk, dv)
+    assert lib.kda_chunk_fwd_varlen_workspace_bytes(ctypes.byref(_vdesc(ind=0))) == 0
