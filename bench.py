@@ -196,12 +196,38 @@ def main():
         _, pby = prefill_alg(1, pw.H, pw.T, pw.d, 2, 2, False)
         pby += (N - 1) * pw.H * pw.d * pw.d * 4 + n_ck * pw.H * pw.d * pw.d * 4   # S_T per lane, checkpoints
         pgbs = pby / (pms * 1e-3) / 1e9
+
+        # the same call with the fused prologue (decay from z) and epilogue (gate, RMSNorm)
+        gz, gA, ggate, gw = synth.gating_inputs((pw.H, pw.T), pw.H, pw.d, pw.d, pw.dtype, device=dev)
+
+        def fstep():
+            kda.chunk_fwd_varlen(pq, pk, pv, None, pbeta, cu, None, max_len=max(lens), ckpt_every=E, o=po, S_T=pS,
+                                 S_ckpt=pck, ckpt_offsets=poff, workspace=pws, stream=stream, z=gz, A_log=gA,
+                                 gate=ggate, norm_weight=gw)
+
+        for _ in range(args.warmup):
+            fstep()
+        torch.cuda.synchronize()
+        p0.record(stream)
+        for _ in range(args.steps):
+            fstep()
+        p1.record(stream)
+        torch.cuda.synchronize()
+        fms = p0.elapsed_time(p1) / args.steps
+        fby = pby + pw.H * pw.T * pw.d * 2          # the gate rows (z replaces log_alpha)
+        fgbs = fby / (fms * 1e-3) / 1e9
+        del gz, gA, ggate, gw
         packed = {"workload": pw.name, "lengths": list(lens), "metric": "KDA packed prefill tokens/s",
                   "value": pw.T / (pms * 1e-3), "unit": "tokens/s", "ms_per_step": pms, "ckpt_every": E,
                   "checkpoints_per_call": n_ck,
                   "roofline": {"bound": "hbm", "achieved": pgbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                "frac": pgbs / HBM_PEAK_GBS, "traffic": None},
-                  "alg_bytes_per_call": pby}
+                  "alg_bytes_per_call": pby,
+                  "fused_gating": {"what": "decay from z (g = -5 sigmoid(e^A z)) and y = sigmoid(gate) RMSNorm(o)",
+                                   "value": pw.T / (fms * 1e-3), "unit": "tokens/s", "ms_per_step": fms,
+                                   "roofline": {"bound": "hbm", "achieved": fgbs, "peak": HBM_PEAK_GBS,
+                                                "unit": "GB/s", "frac": fgbs / HBM_PEAK_GBS, "traffic": None},
+                                   "alg_bytes_per_call": fby}}
         del pq, pk, pv, pla, pbeta, po, pws
 
     # ---------------- decode regime ----------------

@@ -37,6 +37,11 @@ class VarlenDesc(ctypes.Structure):
                 ("packed", ctypes.c_int32)]
 
 
+class Gating(ctypes.Structure):
+    _fields_ = [("z", ctypes.c_void_p), ("A_log", ctypes.c_void_p), ("g_min", ctypes.c_float), ("eps", ctypes.c_float),
+                ("gate", ctypes.c_void_p), ("norm_weight", ctypes.c_void_p)]
+
+
 class DecodeDesc(ctypes.Structure):
     _fields_ = [("N", ctypes.c_int64), ("H", ctypes.c_int64), ("dk", ctypes.c_int64), ("dv", ctypes.c_int64),
                 ("in_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32)]
@@ -66,11 +71,14 @@ def library():
         lib.kda_chunk_fwd.restype = ctypes.c_int32
         lib.kda_chunk_fwd_varlen_workspace_bytes.argtypes = [ctypes.POINTER(VarlenDesc)]
         lib.kda_chunk_fwd_varlen_workspace_bytes.restype = ctypes.c_size_t
-        lib.kda_chunk_fwd_varlen.argtypes = [ctypes.POINTER(VarlenDesc), P, P, P, P, P, P, P, P, P, P, P, P,
-                                             ctypes.c_size_t, P]
+        lib.kda_chunk_fwd_varlen.argtypes = [ctypes.POINTER(VarlenDesc), P, P, P, P, P, P, P, P, P, P, P,
+                                             ctypes.POINTER(Gating), P, ctypes.c_size_t, P]
         lib.kda_chunk_fwd_varlen.restype = ctypes.c_int32
         lib.kda_decode_step.argtypes = [ctypes.POINTER(DecodeDesc), P, P, P, P, P, P, P, P]
         lib.kda_decode_step.restype = ctypes.c_int32
+        lib.kda_decode_step_gated.argtypes = [ctypes.POINTER(DecodeDesc), P, P, P, P, P, ctypes.POINTER(Gating), P, P,
+                                              P]
+        lib.kda_decode_step_gated.restype = ctypes.c_int32
         lib.kda_status_string.argtypes = [ctypes.c_int32]
         lib.kda_status_string.restype = ctypes.c_char_p
         lib.kda_version.argtypes = []
@@ -148,6 +156,24 @@ def chunk_fwd(q, k, v, log_alpha, beta, S0=None, *, out_dtype=None, segments=0, 
     return o, S_T
 
 
+def _gating(dev, H, dv, dtype, lead, z, A_log, g_min, gate, norm_weight, eps):
+    """kda_gating for the fused prologue (z, A_log, g_min) and epilogue (gate, norm_weight, eps),
+    or None when neither is asked for."""
+    if z is None and gate is None:
+        return None
+    if z is not None:
+        _check_tensor("z", z, dev, dtype, z.shape)
+        if tuple(z.shape[:-1]) != tuple(lead):
+            raise ValueError("z must have the shape of log_alpha")
+        _check_tensor("A_log", A_log, dev, torch.float32, (H,))
+    if gate is not None:
+        _check_tensor("gate", gate, dev, dtype, tuple(lead) + (dv,))
+        if norm_weight is not None:
+            _check_tensor("norm_weight", norm_weight, dev, torch.float32, (dv,))
+    return Gating(_ptr(z), _ptr(A_log) if z is not None else None, float(g_min), float(eps), _ptr(gate),
+                  _ptr(norm_weight) if gate is not None else None)
+
+
 def _varlen_desc(N, H, T, max_len, dk, dv, out_dtype, segments, ckpt_every, packed):
     return VarlenDesc(N, H, T, max_len, dk, dv, 64, KDA_BF16, _DTYPES[out_dtype], int(segments), int(ckpt_every),
                       int(packed))
@@ -161,6 +187,7 @@ def varlen_workspace_bytes(N, H, T, max_len, dk, dv, *, segments=0, ckpt_every=0
 
 def chunk_fwd_varlen(q, k, v, log_alpha, beta, cu_seqlens=None, S0=None, *, max_len=None, N=None, ckpt_every=0,
                      out_dtype=None, segments=0, o=None, S_T=None, S_ckpt=None, ckpt_offsets=None,
+                     z=None, A_log=None, g_min=-5.0, gate=None, norm_weight=None, eps=1e-6,
                      store_state=True, workspace=None, stream=None):
     """KDA prefill over a batch of sequences with state checkpoints, through ``kda_chunk_fwd_varlen``.
 
@@ -174,6 +201,9 @@ def chunk_fwd_varlen(q, k, v, log_alpha, beta, cu_seqlens=None, S0=None, *, max_
     Returns (o, S_T, S_ckpt, ckpt_offsets); the last two are None when E = 0. S_ckpt is returned
     at its capacity K; its first ckpt_offsets[N] entries are written (the count is only known on
     the device, and reading it would synchronise).
+    Fused prologue: with ``z`` (shape of log_alpha, which may then be None) and ``A_log`` [H] fp32,
+    the log decay is g_min * sigmoid(exp(A_log[h]) * z). Fused epilogue: with ``gate`` (shape of
+    v), o receives sigmoid(gate) * norm_weight * o / sqrt(mean(o^2) + eps).
     """
     dev = q.device
     if dev.type != "cuda":
@@ -199,7 +229,10 @@ def chunk_fwd_varlen(q, k, v, log_alpha, beta, cu_seqlens=None, S0=None, *, max_
         n_ck = N * (T // ckpt_every) if ckpt_every else 0
     for name, t, shape in (("q", q, lead + (dk,)), ("k", k, lead + (dk,)), ("log_alpha", log_alpha, lead + (dk,)),
                            ("v", v, lead + (dv,)), ("beta", beta, lead)):
+        if t is None and name == "log_alpha" and z is not None:
+            continue
         _check_tensor(name, t, dev, torch.bfloat16, shape)
+    gating = _gating(dev, H, dv, torch.bfloat16, lead, z, A_log, g_min, gate, norm_weight, eps)
     if S0 is not None:
         _check_tensor("S0", S0, dev, torch.float32, slead + (dk, dv))
     if o is None:
@@ -222,6 +255,7 @@ def chunk_fwd_varlen(q, k, v, log_alpha, beta, cu_seqlens=None, S0=None, *, max_
     st = lib.kda_chunk_fwd_varlen(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
                                   _ptr(cu_seqlens), _ptr(S0), _ptr(o), _ptr(S_T),
                                   _ptr(S_ckpt if ckpt_every else None), _ptr(ckpt_offsets if ckpt_every else None),
+                                  None if gating is None else ctypes.byref(gating),
                                   _ptr(workspace), ws_bytes, _stream(dev, stream))
     _check("kda_chunk_fwd_varlen", st)
     if not ckpt_every:
@@ -229,10 +263,12 @@ def chunk_fwd_varlen(q, k, v, log_alpha, beta, cu_seqlens=None, S0=None, *, max_
     return o, S_T, S_ckpt[:n_ck], ckpt_offsets
 
 
-def decode_step(q, k, v, log_alpha, beta, S, *, out_dtype=None, o=None, stream=None):
+def decode_step(q, k, v, log_alpha, beta, S, *, out_dtype=None, o=None, z=None, A_log=None, g_min=-5.0, gate=None,
+                norm_weight=None, eps=1e-6, stream=None):
     """One KDA decode step through ``kda_decode_step``; S ([N,H,dk,dv] fp32) is updated in place.
 
-    q, k, log_alpha: [N,H,dk]; v: [N,H,dv]; beta: [N,H]. Returns o [N,H,dv]."""
+    q, k, log_alpha: [N,H,dk]; v: [N,H,dv]; beta: [N,H]. Returns o [N,H,dv]. With ``z`` or
+    ``gate``, the fused prologue / epilogue of ``chunk_fwd_varlen`` (``kda_decode_step_gated``)."""
     dev = q.device
     if dev.type != "cuda":
         raise ValueError("decode_step runs on the GPU; got a tensor on %s" % dev)
@@ -244,14 +280,23 @@ def decode_step(q, k, v, log_alpha, beta, S, *, out_dtype=None, o=None, stream=N
     out_dtype = out_dtype or dt
     for name, t, shape in (("q", q, (N, H, dk)), ("k", k, (N, H, dk)), ("log_alpha", log_alpha, (N, H, dk)),
                            ("v", v, (N, H, dv)), ("beta", beta, (N, H))):
+        if t is None and name == "log_alpha" and z is not None:
+            continue
         _check_tensor(name, t, dev, dt, shape)
+    gating = _gating(dev, H, dv, dt, (N, H), z, A_log, g_min, gate, norm_weight, eps)
     _check_tensor("S", S, dev, torch.float32, (N, H, dk, dv))
     if o is None:
         o = torch.empty(N, H, dv, device=dev, dtype=out_dtype)
     else:
         _check_tensor("o", o, dev, out_dtype, (N, H, dv))
     desc = DecodeDesc(N, H, dk, dv, _DTYPES[dt], _DTYPES[out_dtype])
-    st = library().kda_decode_step(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
-                                   _ptr(S), _ptr(o), _stream(dev, stream))
-    _check("kda_decode_step", st)
+    if gating is None:
+        st = library().kda_decode_step(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
+                                       _ptr(S), _ptr(o), _stream(dev, stream))
+        _check("kda_decode_step", st)
+    else:
+        st = library().kda_decode_step_gated(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha),
+                                             _ptr(beta), ctypes.byref(gating), _ptr(S), _ptr(o),
+                                             _stream(dev, stream))
+        _check("kda_decode_step_gated", st)
     return o

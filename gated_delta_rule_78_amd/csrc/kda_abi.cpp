@@ -118,6 +118,29 @@ kda_status check_chunk_desc(const kda_chunk_desc* d) {
     return KDA_OK;
 }
 
+// Checks the kda_gating fields that are set; the tensors' extents are checked by the caller.
+kda_status check_gating(const kda_gating* g) {
+    if (!g) return KDA_OK;
+    if (g->z) {
+        if (!g->A_log || !aligned(g->A_log, 4) || !aligned(g->z, 16)) return KDA_ERR_INVALID_ARG;
+        if (!(g->g_min < 0.f) || g->g_min < -3.0e38f) return KDA_ERR_INVALID_ARG;   // NaN fails too
+    }
+    if (g->gate) {
+        if (!(g->eps > 0.f) || g->eps > 3.0e38f || !aligned(g->gate, 16)) return KDA_ERR_INVALID_ARG;
+        if (g->norm_weight && !aligned(g->norm_weight, 16)) return KDA_ERR_INVALID_ARG;
+    }
+    return KDA_OK;
+}
+
+kda::Gating to_gating(const kda_gating* g) {
+    kda::Gating r{};
+    if (g) {
+        r.z = g->z; r.A_log = g->A_log; r.g_min = g->g_min;
+        r.gate = g->gate; r.norm_w = g->norm_weight; r.eps = g->eps;
+    }
+    return r;
+}
+
 kda_status check_varlen_desc(const kda_varlen_desc* d) {
     if (!d) return KDA_ERR_INVALID_ARG;
     if (d->N < 1 || d->H < 1 || d->T < 0 || d->max_len < 0 || d->dk < 1 || d->dv < 1 || d->segments < 0 ||
@@ -163,6 +186,7 @@ kda_status run_bf16(kda::ChunkLaunch& a, const Plan& plan, unsigned char* ws, hi
     ia.q = a.q; ia.k = a.k; ia.v = a.v; ia.la = a.la; ia.beta = a.beta;
     ia.rec = ws;
     ia.map = a.map;
+    ia.gt = a.gt;
     ia.slot_tab = a.map.cu ? reinterpret_cast<const kda::SlotEntry*>(ws + plan.rec_bytes + plan.pair_bytes + plan.entry_bytes)
                            : nullptr;
     if (kda::launch_intra(ia, st) != hipSuccess) return KDA_ERR_HIP;
@@ -273,9 +297,13 @@ size_t kda_chunk_fwd_varlen_workspace_bytes(const kda_varlen_desc* d) {
 kda_status kda_chunk_fwd_varlen(const kda_varlen_desc* d, const void* q, const void* k, const void* v,
                                 const void* log_alpha, const void* beta, const int32_t* cu_seqlens,
                                 const float* S0, void* o, float* S_T, float* S_ckpt, int32_t* ckpt_offsets,
-                                void* workspace, size_t workspace_bytes, void* stream) {
+                                const kda_gating* gating, void* workspace, size_t workspace_bytes, void* stream) {
     const kda_status ds = check_varlen_desc(d);
     if (ds != KDA_OK) return ds;
+    const kda_status gs = check_gating(gating);
+    if (gs != KDA_OK) return gs;
+    const void* z = gating ? gating->z : nullptr;
+    const void* gate = gating ? gating->gate : nullptr;
     const bool packed = d->packed != 0;
     if (packed != (cu_seqlens != nullptr)) return KDA_ERR_INVALID_ARG;
     const int64_t lanes = d->N * d->H;
@@ -316,14 +344,17 @@ kda_status kda_chunk_fwd_varlen(const kda_varlen_desc* d, const void* q, const v
         return kda::launch_copy_or_zero(S_T, S0, state_bytes / 4, st) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
     }
 
-    if (!q || !k || !v || !log_alpha || !beta || !o) return KDA_ERR_INVALID_ARG;
+    if (!q || !k || !v || (!log_alpha && !z) || !beta || !o) return KDA_ERR_INVALID_ARG;
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(log_alpha, 16) || !aligned(o, 16) ||
         !aligned(beta, 2))
         return KDA_ERR_INVALID_ARG;
     const int64_t nrow = row_lanes * d->T;
     const Range ro = range_of(o, nrow * d->dv * eout);
     const Range rin[] = {range_of(q, nrow * d->dk * 2), range_of(k, nrow * d->dk * 2), range_of(v, nrow * d->dv * 2),
-                         range_of(log_alpha, nrow * d->dk * 2), range_of(beta, nrow * 2), rcu};
+                         range_of(z ? nullptr : log_alpha, z ? 0 : nrow * d->dk * 2), range_of(beta, nrow * 2), rcu,
+                         range_of(z, z ? nrow * d->dk * 2 : 0), range_of(gate, gate ? nrow * d->dv * 2 : 0),
+                         range_of(z ? gating->A_log : nullptr, z ? d->H * 4 : 0),
+                         range_of(gate ? gating->norm_weight : nullptr, gate && gating->norm_weight ? d->dv * 4 : 0)};
     for (const Range& r : rin)
         if (overlaps(ro, r) || overlaps(rck, r) || overlaps(rcko, r)) return KDA_ERR_INVALID_ARG;
     if (overlaps(ro, rs0) || overlaps(ro, rst) || overlaps(ro, rck) || overlaps(ro, rcko)) return KDA_ERR_INVALID_ARG;
@@ -345,6 +376,7 @@ kda_status kda_chunk_fwd_varlen(const kda_varlen_desc* d, const void* q, const v
     a.q = q; a.k = k; a.v = v; a.la = log_alpha; a.beta = beta;
     a.S0 = S0; a.o = o; a.S_T = S_T;
     a.map.H = d->H;
+    a.gt = to_gating(gating);
     if (packed) {
         a.map.cu = cu_seqlens; a.map.H = d->H; a.map.rows = d->T; a.map.max_len = d->max_len;
         a.map.slots = g.tab_slots;
@@ -359,13 +391,18 @@ kda_status kda_chunk_fwd_varlen(const kda_varlen_desc* d, const void* q, const v
     return run_bf16(a, plan, ws, st);
 }
 
-kda_status kda_decode_step(const kda_decode_desc* d, const void* q, const void* k, const void* v,
-                           const void* log_alpha, const void* beta, float* S, void* o, void* stream) {
+kda_status kda_decode_step_gated(const kda_decode_desc* d, const void* q, const void* k, const void* v,
+                                 const void* log_alpha, const void* beta, const kda_gating* gating, float* S,
+                                 void* o, void* stream) {
     if (!d) return KDA_ERR_INVALID_ARG;
     if (d->N < 1 || d->H < 1 || d->dk < 1 || d->dv < 1) return KDA_ERR_INVALID_ARG;
     if (!valid_dtype(d->in_dtype) || !valid_dtype(d->out_dtype)) return KDA_ERR_INVALID_ARG;
     if ((d->dk != 64 && d->dk != 128) || (d->dv != 64 && d->dv != 128)) return KDA_ERR_UNSUPPORTED;
-    if (!q || !k || !v || !log_alpha || !beta || !S || !o) return KDA_ERR_INVALID_ARG;
+    const kda_status gs = check_gating(gating);
+    if (gs != KDA_OK) return gs;
+    const void* z = gating ? gating->z : nullptr;
+    const void* gate = gating ? gating->gate : nullptr;
+    if (!q || !k || !v || (!log_alpha && !z) || !beta || !S || !o) return KDA_ERR_INVALID_ARG;
     const int64_t ein = elem_bytes(d->in_dtype), eout = elem_bytes(d->out_dtype);
     if (!aligned(S, 16) || !aligned(o, (uintptr_t)eout) || !aligned(q, (uintptr_t)ein) ||
         !aligned(k, (uintptr_t)ein) || !aligned(v, (uintptr_t)ein) || !aligned(log_alpha, (uintptr_t)ein) ||
@@ -377,16 +414,26 @@ kda_status kda_decode_step(const kda_decode_desc* d, const void* q, const void* 
     const Range ro = range_of(o, lanes * d->dv * eout);
     const Range others[] = {range_of(S, lanes * d->dk * d->dv * 4), range_of(q, lanes * d->dk * ein),
                             range_of(k, lanes * d->dk * ein), range_of(v, lanes * d->dv * ein),
-                            range_of(log_alpha, lanes * d->dk * ein), range_of(beta, lanes * ein)};
+                            range_of(z ? nullptr : log_alpha, z ? 0 : lanes * d->dk * ein),
+                            range_of(beta, lanes * ein),
+                            range_of(z, z ? lanes * d->dk * ein : 0), range_of(gate, gate ? lanes * d->dv * ein : 0),
+                            range_of(z ? gating->A_log : nullptr, z ? d->H * 4 : 0),
+                            range_of(gate ? gating->norm_weight : nullptr, gate && gating->norm_weight ? d->dv * 4 : 0)};
     for (const Range& r : others)
         if (overlaps(ro, r)) return KDA_ERR_INVALID_ARG;
-    for (int i = 1; i < 6; ++i)
+    for (int i = 1; i < (int)(sizeof(others) / sizeof(others[0])); ++i)
         if (overlaps(others[0], others[i])) return KDA_ERR_INVALID_ARG;
     kda::DecodeArgs a{};
     a.N = d->N; a.H = d->H; a.dk = d->dk; a.dv = d->dv;
     a.in_bf16 = d->in_dtype == KDA_BF16; a.out_bf16 = d->out_dtype == KDA_BF16;
     a.q = q; a.k = k; a.v = v; a.la = log_alpha; a.beta = beta; a.S = S; a.o = o;
+    a.gt = to_gating(gating);
     return kda::launch_decode(a, reinterpret_cast<hipStream_t>(stream)) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+kda_status kda_decode_step(const kda_decode_desc* d, const void* q, const void* k, const void* v,
+                           const void* log_alpha, const void* beta, float* S, void* o, void* stream) {
+    return kda_decode_step_gated(d, q, k, v, log_alpha, beta, nullptr, S, o, stream);
 }
 
 }  // extern "C"

@@ -18,11 +18,17 @@
 
 namespace kda {
 
+// Fused prologue / epilogue (Gating): alpha = exp(g_min * sigmoid(exp(A_h) * z)) replaces
+// exp(log_alpha); o is replaced by sigmoid(gate) * w * o / sqrt(mean(o^2) + eps).
+__device__ __forceinline__ float sigmoidf_fast(float x) {
+    return __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-x * kLog2e));
+}
+
 template <int DK, int DV, typename TIn, typename TOut>
 __global__ __launch_bounds__(256) void decode_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k,
                                                      const TIn* __restrict__ v, const TIn* __restrict__ la,
                                                      const TIn* __restrict__ beta, float* __restrict__ S,
-                                                     TOut* __restrict__ o, int64_t lanes) {
+                                                     TOut* __restrict__ o, int64_t lanes, int64_t H, Gating gt) {
     constexpr int NQ = DV / 4;        // column quads
     constexpr int NRG = 256 / NQ;     // row groups
     constexpr int RPT = DK / NRG;     // rows per thread
@@ -38,8 +44,9 @@ __global__ __launch_bounds__(256) void decode_kernel(const TIn* __restrict__ q, 
         float* Sl = S + lane * (int64_t)(DK * DV);
         const TIn* ql = q + lane * DK;
         const TIn* kl = k + lane * DK;
-        const TIn* lal = la + lane * DK;
+        const TIn* lal = (gt.z ? (const TIn*)gt.z : la) + lane * DK;
         const TIn* vl = v + lane * DV;
+        const float eA = gt.z ? __builtin_amdgcn_exp2f(gt.A_log[lane % H] * kLog2e) : 0.f;
 
         float4 s[RPT];
 #pragma unroll
@@ -54,7 +61,8 @@ __global__ __launch_bounds__(256) void decode_kernel(const TIn* __restrict__ q, 
             const int row = rg + NRG * i;
             kr[i] = ld_f(kl + row);
             qr[i] = ld_f(ql + row);
-            const float a = __builtin_amdgcn_exp2f(ld_f(lal + row) * kLog2e);
+            const float x = ld_f(lal + row);
+            const float a = __builtin_amdgcn_exp2f((gt.z ? gt.g_min * sigmoidf_fast(eA * x) : x) * kLog2e);
             s[i].x *= a; s[i].y *= a; s[i].z *= a; s[i].w *= a;
             rs[0] += kr[i] * s[i].x; rs[1] += kr[i] * s[i].y; rs[2] += kr[i] * s[i].z; rs[3] += kr[i] * s[i].w;
             ps[0] += qr[i] * s[i].x; ps[1] += qr[i] * s[i].y; ps[2] += qr[i] * s[i].z; ps[3] += qr[i] * s[i].w;
@@ -81,9 +89,20 @@ __global__ __launch_bounds__(256) void decode_kernel(const TIn* __restrict__ q, 
             s[i].x += kr[i] * d4[0]; s[i].y += kr[i] * d4[1]; s[i].z += kr[i] * d4[2]; s[i].w += kr[i] * d4[3];
             *reinterpret_cast<float4*>(Sl + (int64_t)(rg + NRG * i) * DV + 4 * cq) = s[i];
         }
-        if (rg == 0) {
+        if (rg == 0) {   // threads 0 .. NQ-1 of wave 0 hold the whole output row
             TOut* ol = o + lane * DV + 4 * cq;
-            store4(ol, p4[0] + kqt * d4[0], p4[1] + kqt * d4[1], p4[2] + kqt * d4[2], p4[3] + kqt * d4[3]);
+            float y[4] = {p4[0] + kqt * d4[0], p4[1] + kqt * d4[1], p4[2] + kqt * d4[2], p4[3] + kqt * d4[3]};
+            if (gt.gate) {
+                float ss = y[0] * y[0] + y[1] * y[1] + y[2] * y[2] + y[3] * y[3];
+#pragma unroll
+                for (int m = 1; m < NQ; m <<= 1) ss += __shfl_xor(ss, m);
+                const float rstd = __builtin_amdgcn_rsqf(ss * (1.f / (float)DV) + gt.eps);
+                const TIn* gl = (const TIn*)gt.gate + lane * DV + 4 * cq;
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    y[j] *= rstd * (gt.norm_w ? gt.norm_w[4 * cq + j] : 1.f) * sigmoidf_fast(ld_f(gl + j));
+            }
+            store4(ol, y[0], y[1], y[2], y[3]);
         }
         __syncthreads();  // red[] is reused by the next lane of a grid-stride loop
     }
@@ -95,7 +114,7 @@ static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t st) {
     const int64_t grid = lanes < (int64_t)1 << 30 ? lanes : (int64_t)1 << 30;
     hipLaunchKernelGGL((decode_kernel<DK, DV, TIn, TOut>), dim3((unsigned)grid), dim3(256), 0, st,
                        (const TIn*)a.q, (const TIn*)a.k, (const TIn*)a.v, (const TIn*)a.la, (const TIn*)a.beta,
-                       a.S, (TOut*)a.o, lanes);
+                       a.S, (TOut*)a.o, lanes, a.H, a.gt);
     return hipGetLastError();
 }
 

@@ -16,6 +16,9 @@
 // batch of variable-length sequences (ChunkLaunch::map); a FINISH segment also stores the state
 // at every checkpoint interval it closes.
 //
+// With a fused epilogue (ChunkLaunch::gt.gate), FINISH stores y = sigmoid(gate) * w * o * rstd(o)
+// instead of o (the per-head RMSNorm and output gate that follow the core in section 2.2).
+//
 // Roles (one launch may mix them, see ChunkLaunch):
 //   FINISH  columns [0, dv): exact entry state in, o written, exit state stored as asked.
 //   SUMMARY columns [0, dv + dk) = [S~ | M] with entry [0 | I] and U = 0 on the M columns: the
@@ -44,7 +47,19 @@ __device__ __forceinline__ void store_out(__amdgpu_buffer_rsrc_t r, uint32_t off
 template <int DK, int DV>
 struct __align__(16) InterSmem {
     unsigned char rec[2][RecordLayout<DK, DV>::BYTES];
+    float ssq[2][4][64];    // fused epilogue: per-wave partial sums of o^2 per token, by chunk parity
 };
+
+// Fused epilogue of one output tile: y = sigmoid(gate) * w * o * rstd for 4 columns of a token.
+__device__ __forceinline__ f32x4 gated_norm(f32x4 o, uint2 g, f32x4 w, float rstd) {
+    const float gv[4] = {__uint_as_float(g.x << 16), __uint_as_float(g.x & 0xffff0000u),
+                         __uint_as_float(g.y << 16), __uint_as_float(g.y & 0xffff0000u)};
+    f32x4 y;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+        y[r] = o[r] * rstd * w[r] * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-gv[r] * kLog2e));
+    return y;
+}
 
 // Copy this wave's share (blocks w, w + 4, ...) of the blocks of one chunk record that a role
 // reads (FINISH: all; SUMMARY: all but Q~ and A_qk) into an LDS buffer: one direct-to-LDS buffer
@@ -261,6 +276,60 @@ __device__ __forceinline__ void run_segment(const ChunkLaunch& p, InterSmem<DK, 
 #pragma unroll
         for (int I = 0; I < 4; ++I) Opend[nt][I] = kZero4;
 
+    // Fused epilogue (FINISH with a gate): the gate rows of a chunk load one iteration ahead of
+    // their use, like the records; per-token sums of o^2 meet in LDS across the four waves.
+    const bool gated = FIN && p.gt.gate != nullptr;
+    const __amdgpu_buffer_rsrc_t rgt =
+        make_rsrc(gated ? (const bf16_t*)p.gt.gate + row_base * DVl : nullptr, gated ? (uint32_t)(len * DVl * 2) : 0u);
+    f32x4 nw[NT];
+    uint2 gpend[NT][4];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        nw[nt] = f32x4{1.f, 1.f, 1.f, 1.f};
+        if (gated && p.gt.norm_w) nw[nt] = *reinterpret_cast<const f32x4*>(p.gt.norm_w + col0 + 16 * nt + 4 * lq);
+#pragma unroll
+        for (int I = 0; I < 4; ++I) gpend[nt][I] = make_uint2(0u, 0u);
+    }
+    const float inv_dv = 1.f / (float)DV;
+    // sum of o^2 over the lane's columns, then over the four 16-lane rows, into LDS
+#define KDA_EPI_PARTIAL(cc)                                                                         \
+    do {                                                                                            \
+        _Pragma("unroll") for (int I = 0; I < 4; ++I) {                                             \
+            float ss_ = 0.f;                                                                        \
+            _Pragma("unroll") for (int nt = 0; nt < NT; ++nt)                                       \
+                _Pragma("unroll") for (int r = 0; r < 4; ++r) ss_ += Opend[nt][I][r] * Opend[nt][I][r]; \
+            ss_ += __shfl_xor(ss_, 16);                                                             \
+            ss_ += __shfl_xor(ss_, 32);                                                             \
+            if (lq == 0) sm.ssq[(cc) & 1][w][16 * I + l16] = ss_;                                   \
+        }                                                                                           \
+    } while (0)
+    // store the output of chunk cc (after a barrier that made every wave's partial sums visible)
+#define KDA_STORE_O(cc)                                                                             \
+    do {                                                                                            \
+        _Pragma("unroll") for (int I = 0; I < 4; ++I) {                                             \
+            const uint32_t row = (uint32_t)((cc) * kC + 16 * I + l16);                              \
+            float rstd_ = 0.f;                                                                      \
+            if (gated) {                                                                            \
+                const float* ps_ = &sm.ssq[(cc) & 1][0][16 * I + l16];                              \
+                rstd_ = __builtin_amdgcn_rsqf((ps_[0] + ps_[64] + ps_[128] + ps_[192]) * inv_dv + p.gt.eps); \
+            }                                                                                       \
+            _Pragma("unroll") for (int nt = 0; nt < NT; ++nt) {                                     \
+                const f32x4 y_ = gated ? gated_norm(Opend[nt][I], gpend[nt][I], nw[nt], rstd_) : Opend[nt][I]; \
+                store_out(ro, (row * (uint32_t)DV + col0 + 16 * nt + 4 * lq) * (uint32_t)sizeof(TOut), y_, \
+                          (TOut*)nullptr);                                                          \
+            }                                                                                       \
+        }                                                                                           \
+    } while (0)
+    // gate rows of chunk cc for the lane's output tiles
+#define KDA_LOAD_GATE(cc)                                                                           \
+    do {                                                                                            \
+        if (gated) {                                                                                \
+            _Pragma("unroll") for (int I = 0; I < 4; ++I)                                           \
+                _Pragma("unroll") for (int nt = 0; nt < NT; ++nt)                                   \
+                    gpend[nt][I] = buf_load8(rgt, (((uint32_t)((cc) * kC) + 16 * I + l16) * (uint32_t)DV + col0 + 16 * nt + 4 * lq) * 2u); \
+        }                                                                                           \
+    } while (0)
+
     if (c_begin < c_end) copy_record<DK, DV, FIN>(make_rsrc(rec0 + c_begin * BYTES, BYTES), 0u, sm.rec[0], w, l);
     for (int64_t c = c_begin; c < c_end; ++c) {
         const int buf = (int)((c - c_begin) & 1);
@@ -268,29 +337,24 @@ __device__ __forceinline__ void run_segment(const ChunkLaunch& p, InterSmem<DK, 
         __syncthreads();                        // ... and everyone's; buffer buf^1 is free again
         if (FIN && c > c_begin) {
             KDA_CKPT_STORE(c - 1);
-#pragma unroll
-            for (int I = 0; I < 4; ++I) {
-                const uint32_t row = (uint32_t)((c - 1) * kC + 16 * I + l16);
-#pragma unroll
-                for (int nt = 0; nt < NT; ++nt)
-                    store_out(ro, (row * (uint32_t)DV + col0 + 16 * nt + 4 * lq) * (uint32_t)sizeof(TOut), Opend[nt][I],
-                              (TOut*)nullptr);
-            }
+            KDA_STORE_O(c - 1);
         }
         if (c + 1 < c_end) copy_record<DK, DV, FIN>(make_rsrc(rec0 + (c + 1) * BYTES, BYTES), 0u, sm.rec[buf ^ 1], w, l);
+        KDA_LOAD_GATE(c);
         chunk_step<TOut, DK, DV, NT, 0, NT, FIN>(sm.rec[buf], S, col0, Opend);
+        if (gated) KDA_EPI_PARTIAL(c);
     }
     if (FIN && c_begin < c_end) {
         KDA_CKPT_STORE(c_end - 1);
-#pragma unroll
-        for (int I = 0; I < 4; ++I) {
-            const uint32_t row = (uint32_t)((c_end - 1) * kC + 16 * I + l16);
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt)
-                store_out(ro, (row * (uint32_t)DV + col0 + 16 * nt + 4 * lq) * (uint32_t)sizeof(TOut), Opend[nt][I],
-                          (TOut*)nullptr);
+        if (gated) {
+            __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0): the last chunk's gate rows
+            __syncthreads();                        // every wave's partial sums of the last chunk
         }
+        KDA_STORE_O(c_end - 1);
     }
+#undef KDA_EPI_PARTIAL
+#undef KDA_STORE_O
+#undef KDA_LOAD_GATE
 
 #undef KDA_CKPT_STORE
     // ---- exit state --------------------------------------------------------------------------

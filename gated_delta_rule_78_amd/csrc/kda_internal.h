@@ -6,12 +6,23 @@
 
 namespace kda {
 
+// Fused prologue / epilogue (kda_gating), all NULL when not asked for: with z, the log decay is
+// g_min * sigmoid(exp(A_log[h]) * z); with gate, o receives sigmoid(gate) * w * o * rstd(o).
+struct Gating {
+    const void* z;
+    const float* A_log;
+    float g_min, eps;
+    const void* gate;
+    const float* norm_w;
+};
+
 struct DecodeArgs {
     int64_t N, H, dk, dv;
     bool in_bf16, out_bf16;
     const void *q, *k, *v, *la, *beta;
     float* S;
     void* o;
+    Gating gt;
 };
 
 // Where the rows of one lane live. Fixed-length batches: lane = b*H + h owns rows
@@ -60,6 +71,7 @@ struct ChunkLaunch {
     float* ckpt;            // NULL = no checkpoints
     int64_t ck_chunks, ck_cap, ck_per_lane;
     const int32_t* ck_off;  // [N + 1] (packed batches)
+    Gating gt;              // the epilogue fields are read by the state pass
 };
 
 // The intra-chunk kernel over every record slot (bf16 inputs): slots = map.slots per head of
@@ -70,6 +82,7 @@ struct IntraArgs {
     unsigned char* rec;     // record_bytes(dk, dv) per slot
     const SlotEntry* slot_tab;  // [map.slots] for a packed batch, NULL for a fixed one
     SeqMap map;
+    Gating gt;              // the prologue fields are read by the intra-chunk kernel
 };
 
 // Slot table and checkpoint offsets of a packed batch.

@@ -91,6 +91,21 @@ __device__ __forceinline__ bf16x8 scale_frag(bf16x8 a, const bf16_t* f, int ks, 
     return cat(cvt4(unpack4f(lo4(a)) * f0), cvt4(unpack4f(hi4(a)) * f1));
 }
 
+// Fused decay prologue on 8 packed bf16 pre-activations z: g = g_min * sigmoid(eA * z) with
+// eA = exp(A_h), in fp32, rounded back to bf16 (the form a bf16 log_alpha input has).
+__device__ __forceinline__ uint4 decay_from_z(uint4 zr, float eA, float g_min) {
+    const uint32_t w[4] = {zr.x, zr.y, zr.z, zr.w};
+    uint32_t o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float z0 = __uint_as_float(w[i] << 16), z1 = __uint_as_float(w[i] & 0xffff0000u);
+        const float s0 = __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-eA * z0 * kLog2e));
+        const float s1 = __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-eA * z1 * kLog2e));
+        o[i] = pack_bf16x2(g_min * s0, g_min * s1);
+    }
+    return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
 template <int DK, int DV>
 struct IntraCfg {
     static constexpr int NKS = DK / 32;                    // waves 0..NKS-1 own 32 key channels each
@@ -119,7 +134,7 @@ struct __align__(16) IntraSmem {
     bf16_t fij[6][DK];          // exp(G_ref(I) - G_ref(J)) per channel for the pairs I > J
 };
 
-template <int DK, int DV, bool PACKED>
+template <int DK, int DV, bool PACKED, bool ZPRO>
 __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs p) {
     typedef IntraCfg<DK, DV> Cfg;
     typedef RecordLayout<DK, DV> R;
@@ -158,6 +173,9 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs p) {
     // covers its valid rows only.
     uint4 pq[4], pk[4], pg[4], pv[LPR];
     uint32_t pb = 0;
+    // the decay rows: log_alpha, or the pre-activation z of the fused prologue
+    const bf16_t* gsrc = (const bf16_t*)(ZPRO ? p.gt.z : p.la);
+    const int64_t nheads = p.map.H > 0 ? p.map.H : 1;
     // per-lane byte offsets inside a chunk. Row offsets stay in the vector offset, the part of
     // the address the buffer range check sees (the scalar offset is not range-checked); the
     // empty asm in the load stops the compiler from hoisting one register per row group.
@@ -182,7 +200,7 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs p) {
             const uint32_t nk_ = n_ * (DK * 2);                                                     \
             const __amdgpu_buffer_rsrc_t rq_ = make_rsrc((const bf16_t*)p.q + row_ * DK, nk_);       \
             const __amdgpu_buffer_rsrc_t rk_ = make_rsrc((const bf16_t*)p.k + row_ * DK, nk_);       \
-            const __amdgpu_buffer_rsrc_t rg_ = make_rsrc((const bf16_t*)p.la + row_ * DK, nk_);      \
+            const __amdgpu_buffer_rsrc_t rg_ = make_rsrc(gsrc + row_ * DK, nk_);                    \
             uint32_t qo_ = qk_voff, go_ = g_voff;                                                   \
             asm volatile("" : "+v"(qo_), "+v"(go_));   /* keeps the row offsets below in the loop */ \
             _Pragma("unroll") for (int I_ = 0; I_ < 4; ++I_) {                                      \
@@ -222,6 +240,15 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs p) {
     pin(pb);
     for (; t < total; t += G) {
     unsigned char* rec = p.rec + (int64_t)t * R::BYTES;
+    // exp(A_h) of this chunk's head for the fused decay prologue (head = lane % H for a fixed batch)
+    const float eA = ZPRO ? __builtin_amdgcn_exp2f(p.gt.A_log[PACKED ? hn : hn % nheads] * kLog2e) : 0.f;
+    // valid rows of this chunk: with the fused prologue, padded rows (zeros, so z = 0) must not
+    // decay, g = 0 there rather than g_min / 2
+    uint32_t nrows = kC;
+    if (ZPRO) {
+        if (PACKED) nrows = (uint32_t)p.slot_tab[jn].nrows;
+        else nrows = (uint32_t)(rows - (int64_t)jn * kC < kC ? rows - (int64_t)jn * kC : kC);
+    }
     jn += step_j; hn += step_h;
     if (jn >= slots) { jn -= slots; ++hn; }
     auto blk = [&](int b) -> unsigned char* { return rec + b * 1024 + l * 16; };
@@ -235,7 +262,8 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs p) {
         if (kw) {
 #pragma unroll
             for (int I = 0; I < 4; ++I) {
-                *reinterpret_cast<uint4*>(&stA[(16 * I + (l >> 2)) * LDG + 8 * (l & 3)]) = pg[I];
+                *reinterpret_cast<uint4*>(&stA[(16 * I + (l >> 2)) * LDG + 8 * (l & 3)]) =
+                    !ZPRO ? pg[I] : decay_from_z(pg[I], eA, 16u * I + (l >> 2) < nrows ? p.gt.g_min : 0.f);
                 typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
                 const u32x2 sq0 = __builtin_amdgcn_permlane16_swap(pq[I].x, pq[I].z, false, false);
                 const u32x2 sq1 = __builtin_amdgcn_permlane16_swap(pq[I].y, pq[I].w, false, false);
@@ -544,10 +572,14 @@ hipError_t launch_dd(const IntraArgs& a, hipStream_t st) {
     int64_t blocks = a.slot_tab ? a.map.H * a.map.slots : a.lanes * a.nchunks;
     if (blocks <= 0) return hipSuccess;
     if (blocks > resident_workgroups()) blocks = resident_workgroups();
-    if (a.slot_tab)
-        hipLaunchKernelGGL((intra_kernel<DK, DV, true>), dim3((unsigned)blocks), dim3(256), 0, st, a);
-    else
-        hipLaunchKernelGGL((intra_kernel<DK, DV, false>), dim3((unsigned)blocks), dim3(256), 0, st, a);
+    const dim3 grid((unsigned)blocks), block(256);
+    if (a.slot_tab) {
+        if (a.gt.z) hipLaunchKernelGGL((intra_kernel<DK, DV, true, true>), grid, block, 0, st, a);
+        else hipLaunchKernelGGL((intra_kernel<DK, DV, true, false>), grid, block, 0, st, a);
+    } else {
+        if (a.gt.z) hipLaunchKernelGGL((intra_kernel<DK, DV, false, true>), grid, block, 0, st, a);
+        else hipLaunchKernelGGL((intra_kernel<DK, DV, false, false>), grid, block, 0, st, a);
+    }
     return hipGetLastError();
 }
 

@@ -138,6 +138,19 @@ def packed_inputs(lens, H: int, dk: int, dv: int, dtype, device="cpu", seed_base
     return q, k, v, la, beta, torch.tensor(cu, dtype=torch.int32, device=device), S0
 
 
+def gating_inputs(lead, H: int, dk: int, dv: int, dtype, device="cpu", seed: int = 6000):
+    """Inputs of the fused prologue / epilogue around the core, for rows shaped `lead` (e.g. (H, T)
+    packed or (N, H) decode): z [*lead, dk] ~ N(-3, 1.5^2) (so that g = -5 sigmoid(e^A z) sits
+    mostly in [-0.5, 0) with a tail toward -5), A_log [H] ~ U[-0.5, 0.5] fp32, gate [*lead, dv]
+    ~ N(0, 1), norm_weight [dv] = 1 + 0.1 N(0, 1) fp32."""
+    g = _gen(device, seed)
+    z = (torch.randn(*lead, dk, generator=g, device=device) * 1.5 - 3.0).to(dtype)
+    A_log = torch.rand(H, generator=g, device=device) - 0.5
+    gate = torch.randn(*lead, dv, generator=g, device=device).to(dtype)
+    w = 1.0 + 0.1 * torch.randn(dv, generator=g, device=device)
+    return z, A_log, gate, w
+
+
 def decode_state(N: int, H: int, dk: int, dv: int, std: float, device="cpu", seed: int = 3000):
     """Fixed-size fp32 state [N,H,dk,dv] ~ N(0, std)."""
     return torch.randn(N, H, dk, dv, generator=_gen(device, seed), device=device, dtype=torch.float32) * std

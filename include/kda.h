@@ -112,6 +112,32 @@ kda_status kda_chunk_fwd(const kda_chunk_desc* desc,
                          const float* S0, void* o, float* S_T,
                          void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Optional fused prologue and epilogue around the KDA core (section 2.2 of the Kimi K3 reading
+ * notes: the decay lower-bound equation, and the per-head RMSNorm with the full-rank sigmoid
+ * output gate that follow the core). Only their elementwise parts: the projections that produce
+ * z and the gate pre-activation, and W_o after the gate, are the caller's.
+ *  Prologue (z != NULL): the per-channel log decay is computed from the decay pre-activation z
+ *    (same shape and type as log_alpha, which is then ignored and may be NULL) as
+ *        g = g_min * sigmoid(exp(A_log[h]) * z),   alpha = exp(g),
+ *    in fp32; g_min < 0 (K3 uses -5; every g then lies in (g_min, 0), inside the decay domain when
+ *    g_min >= -5). The bf16 prefill rounds g to bf16 before its cumulative sum, as a bf16
+ *    log_alpha input would be; decode keeps it in fp32.
+ *  Epilogue (gate != NULL): o receives, instead of the core output o_t,
+ *        y_t = sigmoid(gate_t) * norm_weight * o_t / sqrt(mean(o_t^2) + eps)
+ *    per (token, head), the mean over the dv columns of the head (gate: same shape and type as v;
+ *    norm_weight: [dv] fp32 shared by the heads, NULL = ones; eps > 0), computed from the fp32
+ *    core output before o is rounded.
+ */
+typedef struct kda_gating {
+    const void* z;              /* decay pre-activation, or NULL = use log_alpha              */
+    const float* A_log;         /* [H] fp32 head-wise log scale (required with z)            */
+    float g_min;                /* decay lower bound, < 0 (required with z)                   */
+    float eps;                  /* RMSNorm epsilon, > 0 (required with gate)                  */
+    const void* gate;           /* gate pre-activation W_g x, or NULL = no epilogue           */
+    const float* norm_weight;   /* [dv] fp32 RMSNorm weight, or NULL = ones                   */
+} kda_gating;
+
 /* Shape and types of one prefill call over a batch of sequences with checkpoints. */
 typedef struct kda_varlen_desc {
     int64_t N;          /* sequences, >= 1                                                */
@@ -164,6 +190,8 @@ size_t kda_chunk_fwd_varlen_workspace_bytes(const kda_varlen_desc* desc);
  *  (packed = 0); checkpoints beyond that capacity are dropped. With packed = 0, ckpt_offsets
  *  may be NULL (its values are s * floor(T/E)); with packed = 1 it is required.
  *  With E = 0, S_ckpt and ckpt_offsets are ignored.
+ *  gating     : fused prologue / epilogue (see kda_gating), or NULL for none; the head of
+ *               A_log[h] is the lane's head in both layouts.
  *  workspace  : at least kda_chunk_fwd_varlen_workspace_bytes(desc) bytes.
  * No output may overlap an input or another output (S_T = S0 aside). A call whose sequences
  * are all empty writes S_T = S0 (or zeros) and the offsets, nothing else.
@@ -176,7 +204,7 @@ kda_status kda_chunk_fwd_varlen(const kda_varlen_desc* desc,
                                 const void* q, const void* k, const void* v,
                                 const void* log_alpha, const void* beta,
                                 const int32_t* cu_seqlens, const float* S0, void* o, float* S_T,
-                                float* S_ckpt, int32_t* ckpt_offsets,
+                                float* S_ckpt, int32_t* ckpt_offsets, const kda_gating* gating,
                                 void* workspace, size_t workspace_bytes, void* stream);
 
 /*
@@ -191,6 +219,16 @@ kda_status kda_decode_step(const kda_decode_desc* desc,
                            const void* q, const void* k, const void* v,
                            const void* log_alpha, const void* beta,
                            float* S, void* o, void* stream);
+
+/*
+ * kda_decode_step with the fused prologue / epilogue of kda_gating (z [N,H,dk] in_dtype replaces
+ * log_alpha, which may then be NULL; gate [N,H,dv] in_dtype). gating == NULL is kda_decode_step.
+ * Source: as kda_decode_step, plus the decay lower-bound and output-gate equations of section 2.2.
+ */
+kda_status kda_decode_step_gated(const kda_decode_desc* desc,
+                                 const void* q, const void* k, const void* v,
+                                 const void* log_alpha, const void* beta, const kda_gating* gating,
+                                 float* S, void* o, void* stream);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* kda_status_string(int32_t status);

@@ -31,8 +31,8 @@ def lib():
 
 def test_header_declares_the_boundary():
     assert declared_functions() == ["kda_chunk_fwd", "kda_chunk_fwd_varlen", "kda_chunk_fwd_varlen_workspace_bytes",
-                                    "kda_chunk_fwd_workspace_bytes", "kda_decode_step", "kda_status_string",
-                                    "kda_version"]
+                                    "kda_chunk_fwd_workspace_bytes", "kda_decode_step", "kda_decode_step_gated",
+                                    "kda_status_string", "kda_version"]
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -132,11 +132,12 @@ def _vdesc(N=3, H=2, T=640, max_len=512, dk=128, dv=128, chunk=64, ind=1, outd=1
 
 
 def _varlen(lib, d, cu=FAKE + (6 << 30), S0=None, ST=None, ckpt=None, ckoff=None, ws=FAKE + (8 << 30),
-            ws_bytes=1 << 40, q=FAKE, o=FAKE + (5 << 30)):
+            ws_bytes=1 << 40, q=FAKE, o=FAKE + (5 << 30), la=FAKE + (3 << 30), gating=None):
     P = ctypes.c_void_p
     return lib.kda_chunk_fwd_varlen(None if d is None else ctypes.byref(d), P(q), P(FAKE + (1 << 30)),
-                                    P(FAKE + (2 << 30)), P(FAKE + (3 << 30)), P(FAKE + (4 << 30)), P(cu), P(S0),
-                                    P(o), P(ST), P(ckpt), P(ckoff), P(ws), ws_bytes, None)
+                                    P(FAKE + (2 << 30)), P(la), P(FAKE + (4 << 30)), P(cu), P(S0),
+                                    P(o), P(ST), P(ckpt), P(ckoff), None if gating is None else ctypes.byref(gating),
+                                    P(ws), ws_bytes, None)
 
 
 def test_varlen_rejects_bad_arguments(lib):
@@ -174,3 +175,28 @@ def test_varlen_workspace_query_and_check(lib):
     e = _vdesc(N=N, H=H, T=T, seg=1, packed=0)
     assert lib.kda_chunk_fwd_varlen_workspace_bytes(ctypes.byref(e)) == N * H * (T // 64) * record_bytes(dk, dv)
     assert lib.kda_chunk_fwd_varlen_workspace_bytes(ctypes.byref(_vdesc(ind=0))) == 0
+
+
+def test_gating_rejects_bad_arguments(lib):
+    G = kda.Gating
+    z, A, gate, w = FAKE + (10 << 30), FAKE + (11 << 30), FAKE + (12 << 30), FAKE + (13 << 30)
+    d = _vdesc()
+    assert _varlen(lib, d, la=None) == INVALID                                        # no decay input at all
+    assert _varlen(lib, d, la=None, gating=G(z, None, -5.0, 0.0, None, None)) == INVALID   # z without A_log
+    assert _varlen(lib, d, la=None, gating=G(z, A, 0.0, 0.0, None, None)) == INVALID       # g_min must be < 0
+    assert _varlen(lib, d, la=None, gating=G(z, A, float("nan"), 0.0, None, None)) == INVALID
+    assert _varlen(lib, d, la=None, gating=G(z + 8, A, -5.0, 0.0, None, None)) == INVALID  # misaligned z
+    assert _varlen(lib, d, gating=G(None, None, 0.0, 0.0, gate, None)) == INVALID          # eps must be > 0
+    assert _varlen(lib, d, gating=G(None, None, 0.0, 1e-6, gate, w + 4)) == INVALID        # misaligned weight
+    assert _varlen(lib, d, gating=G(None, None, 0.0, 1e-6, FAKE + (5 << 30), None)) == INVALID  # gate overlaps o
+    # a valid gating passes validation and stops at the missing workspace
+    assert _varlen(lib, d, la=None, ws=None, ws_bytes=0, gating=G(z, A, -5.0, 1e-6, gate, w)) == WORKSPACE
+    dd = kda.DecodeDesc(4, 2, 128, 128, 1, 1)
+    P = ctypes.c_void_p
+    call = lambda la, g: lib.kda_decode_step_gated(ctypes.byref(dd), P(FAKE), P(FAKE + (1 << 30)), P(FAKE + (2 << 30)),
+                                                   P(la), P(FAKE + (4 << 30)), None if g is None else ctypes.byref(g),
+                                                   P(FAKE + (5 << 30)), P(FAKE + (6 << 30)), None)
+    assert call(None, None) == INVALID
+    assert call(None, G(z, None, -5.0, 0.0, None, None)) == INVALID
+    assert call(FAKE + (3 << 30), G(None, None, 0.0, -1.0, gate, None)) == INVALID
+    assert call(FAKE + (3 << 30), G(None, None, 0.0, 1e-6, FAKE + (6 << 30), None)) == INVALID   # gate overlaps o
