@@ -97,6 +97,7 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-packed", action="store_true", help="skip the packed variable-length batch")
+    ap.add_argument("--no-backward", action="store_true", help="skip the backward of the prefill workload")
     ap.add_argument("--cpu-lanes", type=int, default=32, help="lanes of the CPU-baseline sample")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run one plain device copy of this size (counter calibration)")
@@ -230,6 +231,42 @@ def main():
                                    "alg_bytes_per_call": fby}}
         del pq, pk, pv, pla, pbeta, po, pws
 
+    # ---------------- backward (training) of the same prefill workload ----------------
+    bwd = None
+    if not args.no_backward and w.dtype == torch.bfloat16:
+        print("bench: backward %s" % w.name, file=sys.stderr, flush=True)
+        g = torch.Generator(device=dev)
+        g.manual_seed(17)
+        dO = torch.randn(w.B, w.H, w.T, w.d, generator=g, device=dev).to(out_dtype)
+        dST = torch.randn(w.B, w.H, w.d, w.d, generator=g, device=dev) * 0.1
+        bws = torch.empty(max(kda.chunk_bwd_workspace_bytes(q, v, args.segments, out_dtype), 16), device=dev,
+                          dtype=torch.uint8)
+
+        def bstep():
+            kda.chunk_bwd(q, k, v, la, beta, S0, dO, dST, segments=args.segments, workspace=bws, stream=stream)
+
+        for _ in range(max(1, args.warmup)):
+            bstep()
+        torch.cuda.synchronize()
+        b0 = torch.cuda.Event(enable_timing=True)
+        b1 = torch.cuda.Event(enable_timing=True)
+        nb = max(1, args.steps // 4)
+        b0.record(stream)
+        for _ in range(nb):
+            bstep()
+        b1.record(stream)
+        torch.cuda.synchronize()
+        bms = b0.elapsed_time(b1) / nb
+        # bytes: the forward's inputs, dO in, fp32 gradients of q, k, v, log_alpha, beta out, states
+        bby = w.B * w.H * (w.T * (4 * w.d * in_b + in_b + w.d * in_b + 4 * w.d * 4 + 4) + 3 * w.d * w.d * 4)
+        bgbs = bby / (bms * 1e-3) / 1e9
+        bwd = {"workload": w.name + ", backward (forward recompute included)", "metric": "KDA backward tokens/s",
+               "value": tokens / (bms * 1e-3), "unit": "tokens/s", "ms_per_step": bms, "steps": nb,
+               "roofline": {"bound": "hbm", "achieved": bgbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                            "frac": bgbs / HBM_PEAK_GBS, "traffic": None},
+               "alg_bytes_per_call": bby, "workspace_bytes": int(bws.numel())}
+        del dO, bws
+
     # ---------------- decode regime ----------------
     decode = None
     if args.decode_steps > 0:
@@ -294,7 +331,7 @@ def main():
                      "traffic": measured_traffic("call", w.name, PREFILL_SOURCES)},
         "mfma": {"alg_tflops": tflops, "peak_tflops": mm_peak, "frac": tflops / mm_peak},
         "alg_bytes_per_call": abytes, "alg_flops_per_call": flops, "call_ms": call_ms,
-        "decode": decode, "packed": packed, "cpu_baseline": cpu,
+        "decode": decode, "packed": packed, "backward": bwd, "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
 

@@ -8,6 +8,7 @@ library is missing or fails, the call raises.
     chunk_fwd(q, k, v, log_alpha, beta, S0=None) -> (o, S_T)     chunkwise prefill
     chunk_fwd_varlen(q, k, v, log_alpha, beta, cu_seqlens, ...)   packed variable-length batch,
         -> (o, S_T, S_ckpt, ckpt_offsets)                         state checkpoints every E tokens
+    chunk_bwd(q, k, v, log_alpha, beta, S0, dO, dS_T) -> grads    backward of chunkwise prefill
     decode_step(q, k, v, log_alpha, beta, S) -> o                 one token, S updated in place
 """
 import ctypes
@@ -15,7 +16,7 @@ import os
 
 import torch
 
-__all__ = ["chunk_fwd", "chunk_fwd_varlen", "decode_step", "chunk_workspace_bytes", "varlen_workspace_bytes",
+__all__ = ["chunk_fwd", "chunk_fwd_varlen", "chunk_bwd", "chunk_bwd_workspace_bytes", "decode_step", "chunk_workspace_bytes", "varlen_workspace_bytes",
            "library", "KDAError", "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkda.so")
@@ -74,6 +75,10 @@ def library():
         lib.kda_chunk_fwd_varlen.argtypes = [ctypes.POINTER(VarlenDesc), P, P, P, P, P, P, P, P, P, P, P,
                                              ctypes.POINTER(Gating), P, ctypes.c_size_t, P]
         lib.kda_chunk_fwd_varlen.restype = ctypes.c_int32
+        lib.kda_chunk_bwd_workspace_bytes.argtypes = [ctypes.POINTER(ChunkDesc)]
+        lib.kda_chunk_bwd_workspace_bytes.restype = ctypes.c_size_t
+        lib.kda_chunk_bwd.argtypes = [ctypes.POINTER(ChunkDesc)] + [P] * 15 + [ctypes.c_size_t, P]
+        lib.kda_chunk_bwd.restype = ctypes.c_int32
         lib.kda_decode_step.argtypes = [ctypes.POINTER(DecodeDesc), P, P, P, P, P, P, P, P]
         lib.kda_decode_step.restype = ctypes.c_int32
         lib.kda_decode_step_gated.argtypes = [ctypes.POINTER(DecodeDesc), P, P, P, P, P, ctypes.POINTER(Gating), P, P,
@@ -261,6 +266,51 @@ def chunk_fwd_varlen(q, k, v, log_alpha, beta, cu_seqlens=None, S0=None, *, max_
     if not ckpt_every:
         return o, S_T, None, None
     return o, S_T, S_ckpt[:n_ck], ckpt_offsets
+
+
+def chunk_bwd_workspace_bytes(q, v, segments=0, out_dtype=None):
+    d = _chunk_desc(q, v, segments, out_dtype or q.dtype)
+    return int(library().kda_chunk_bwd_workspace_bytes(ctypes.byref(d)))
+
+
+def chunk_bwd(q, k, v, log_alpha, beta, S0, dO, dS_T=None, *, segments=0, workspace=None, stream=None):
+    """Backward of chunkwise prefill through ``kda_chunk_bwd`` (bf16 inputs).
+
+    Inputs as ``chunk_fwd``; dO [B,H,T,dv] (bf16 or fp32: the forward's output type), dS_T
+    [B,H,dk,dv] fp32 or None. Returns fp32 (dq, dk, dv, dlog_alpha, dbeta, dS0)."""
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("chunk_bwd runs on the GPU; got a tensor on %s" % dev)
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    if q.dtype != torch.bfloat16:
+        raise ValueError("chunk_bwd takes bf16 inputs (got %s)" % q.dtype)
+    for name, t, shape in (("q", q, (B, H, T, dk)), ("k", k, (B, H, T, dk)), ("log_alpha", log_alpha, (B, H, T, dk)),
+                           ("v", v, (B, H, T, dv)), ("beta", beta, (B, H, T))):
+        _check_tensor(name, t, dev, torch.bfloat16, shape)
+    if S0 is not None:
+        _check_tensor("S0", S0, dev, torch.float32, (B, H, dk, dv))
+    if dO.dtype not in _DTYPES:
+        raise ValueError("unsupported dO dtype %s" % dO.dtype)
+    _check_tensor("dO", dO, dev, dO.dtype, (B, H, T, dv))
+    if dS_T is not None:
+        _check_tensor("dS_T", dS_T, dev, torch.float32, (B, H, dk, dv))
+    f32 = dict(device=dev, dtype=torch.float32)
+    dq, dk_, dla = (torch.empty(B, H, T, dk, **f32) for _ in range(3))
+    dv_ = torch.empty(B, H, T, dv, **f32)
+    dbeta = torch.empty(B, H, T, **f32)
+    dS0 = torch.empty(B, H, dk, dv, **f32)
+    desc = _chunk_desc(q, v, segments, dO.dtype)
+    lib = library()
+    need = int(lib.kda_chunk_bwd_workspace_bytes(ctypes.byref(desc)))
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, device=dev, dtype=torch.uint8)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.kda_chunk_bwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S0),
+                           _ptr(dO), _ptr(dS_T), _ptr(dq), _ptr(dk_), _ptr(dv_), _ptr(dla), _ptr(dbeta), _ptr(dS0),
+                           _ptr(workspace), ws_bytes, _stream(dev, stream))
+    _check("kda_chunk_bwd", st)
+    return dq, dk_, dv_, dla, dbeta, dS0
 
 
 def decode_step(q, k, v, log_alpha, beta, S, *, out_dtype=None, o=None, z=None, A_log=None, g_min=-5.0, gate=None,

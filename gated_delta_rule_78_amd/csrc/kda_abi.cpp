@@ -207,6 +207,32 @@ kda_status run_bf16(kda::ChunkLaunch& a, const Plan& plan, unsigned char* ws, hi
     return kda::launch_inter(a, st) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
+// Backward workspace, in order: the forward's own workspace (records, pairs, entries), every
+// chunk's exit state, the forward's output (discarded), then the backward's per-chunk scratch.
+struct BwdPlan {
+    Plan fwd;
+    int64_t ck_stride;
+    size_t ckpt_off, o_off, prep_off, gst_off, dvt_off, gscr_off, ws_bytes;
+};
+
+BwdPlan make_bwd_plan(const kda_chunk_desc* d) {
+    BwdPlan b{};
+    b.fwd = make_plan(fixed_geometry(d));
+    const int64_t lanes = d->B * d->H;
+    const int64_t nchunks = ceil_div(d->T, kChunk);
+    const size_t chunks = (size_t)(lanes * nchunks);
+    b.ck_stride = d->T / kChunk;
+    auto align = [](size_t x) { return (x + 255) & ~(size_t)255; };
+    b.ckpt_off = align(b.fwd.ws_bytes);
+    b.o_off = align(b.ckpt_off + (size_t)(lanes * b.ck_stride * d->dk * d->dv) * 4);
+    b.prep_off = align(b.o_off + (size_t)(lanes * d->T * d->dv) * (size_t)elem_bytes(d->out_dtype));
+    b.gst_off = align(b.prep_off + chunks * kda::bwd_prep_floats(d->dk, d->dv) * 4);
+    b.dvt_off = align(b.gst_off + chunks * (size_t)(d->dk * d->dv) * 4);
+    b.gscr_off = align(b.dvt_off + chunks * (size_t)(kChunk * d->dv) * 4);
+    b.ws_bytes = b.gscr_off + chunks * kda::bwd_grad_floats(d->dk, d->dv) * 4;
+    return b;
+}
+
 }  // namespace
 
 extern "C" {
@@ -389,6 +415,86 @@ kda_status kda_chunk_fwd_varlen(const kda_varlen_desc* d, const void* q, const v
     }
     if ((packed || vp.ck_off) && kda::launch_varlen_prep(vp, st) != hipSuccess) return KDA_ERR_HIP;
     return run_bf16(a, plan, ws, st);
+}
+
+size_t kda_chunk_bwd_workspace_bytes(const kda_chunk_desc* d) {
+    if (check_chunk_desc(d) != KDA_OK || d->in_dtype != KDA_BF16 || d->T == 0) return 0;
+    return make_bwd_plan(d).ws_bytes;
+}
+
+kda_status kda_chunk_bwd(const kda_chunk_desc* d, const void* q, const void* k, const void* v,
+                         const void* log_alpha, const void* beta, const float* S0, const void* dO,
+                         const float* dS_T, float* dq, float* dk, float* dv, float* dlog_alpha, float* dbeta,
+                         float* dS0, void* workspace, size_t workspace_bytes, void* stream) {
+    const kda_status ds = check_chunk_desc(d);
+    if (ds != KDA_OK) return ds;
+    if (d->in_dtype != KDA_BF16) return KDA_ERR_UNSUPPORTED;
+    const int64_t lanes = d->B * d->H;
+    const int64_t eout = elem_bytes(d->out_dtype);
+    const int64_t state_bytes = lanes * d->dk * d->dv * 4;
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    if ((S0 && !aligned(S0, 16)) || (dS_T && !aligned(dS_T, 16)) || (dS0 && !aligned(dS0, 16)))
+        return KDA_ERR_INVALID_ARG;
+    const Range rs0 = range_of(S0, S0 ? state_bytes : 0), rdst = range_of(dS_T, dS_T ? state_bytes : 0);
+    const Range rds0 = range_of(dS0, dS0 ? state_bytes : 0);
+    if (overlaps(rds0, rs0) || overlaps(rds0, rdst)) return KDA_ERR_INVALID_ARG;
+    if (d->T == 0) {   // no tokens: dS0 = dS_T
+        if (!dS0) return KDA_OK;
+        return kda::launch_copy_or_zero(dS0, dS_T, state_bytes / 4, st) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+    }
+    if (!q || !k || !v || !log_alpha || !beta || !dO || !dq || !dk || !dv || !dlog_alpha || !dbeta)
+        return KDA_ERR_INVALID_ARG;
+    const void* ins[] = {q, k, v, log_alpha, dO, dq, dk, dv, dlog_alpha, dbeta};
+    for (const void* p : ins)
+        if (!aligned(p, 4)) return KDA_ERR_INVALID_ARG;
+    if (!aligned(beta, 2)) return KDA_ERR_INVALID_ARG;
+    const int64_t nk = lanes * d->T * d->dk, nv = lanes * d->T * d->dv, nt = lanes * d->T;
+    const Range rin[] = {range_of(q, nk * 2), range_of(k, nk * 2), range_of(v, nv * 2), range_of(log_alpha, nk * 2),
+                         range_of(beta, nt * 2), range_of(dO, nv * eout), rs0, rdst};
+    const Range rout[] = {range_of(dq, nk * 4), range_of(dk, nk * 4), range_of(dv, nv * 4),
+                          range_of(dlog_alpha, nk * 4), range_of(dbeta, nt * 4), rds0};
+    for (int i = 0; i < 6; ++i) {
+        for (const Range& r : rin)
+            if (overlaps(rout[i], r)) return KDA_ERR_INVALID_ARG;
+        for (int j = i + 1; j < 6; ++j)
+            if (overlaps(rout[i], rout[j])) return KDA_ERR_INVALID_ARG;
+    }
+    const BwdPlan bp = make_bwd_plan(d);
+    if (!workspace || workspace_bytes < bp.ws_bytes) return KDA_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return KDA_ERR_INVALID_ARG;
+    const Range rw = range_of(workspace, (int64_t)bp.ws_bytes);
+    for (const Range& r : rin)
+        if (overlaps(rw, r)) return KDA_ERR_INVALID_ARG;
+    for (const Range& r : rout)
+        if (overlaps(rw, r)) return KDA_ERR_INVALID_ARG;
+
+    unsigned char* ws = static_cast<unsigned char*>(workspace);
+    // forward recompute: every chunk's exit state into the workspace (lane-major checkpoints)
+    kda::ChunkLaunch a{};
+    a.lanes = lanes; a.T = d->T; a.dk = d->dk; a.dv = d->dv;
+    a.nchunks = bp.fwd.nchunks;
+    a.in_bf16 = true; a.out_bf16 = d->out_dtype == KDA_BF16;
+    a.nseg = bp.fwd.nseg; a.chunks_per_seg = bp.fwd.chunks_per_seg;
+    a.q = q; a.k = k; a.v = v; a.la = log_alpha; a.beta = beta;
+    a.S0 = S0; a.o = ws + bp.o_off; a.S_T = nullptr;
+    a.map.H = 1;   // checkpoint j of lane l at index l * ck_per_lane + j - 1
+    if (bp.ck_stride > 0) {
+        a.ckpt = reinterpret_cast<float*>(ws + bp.ckpt_off);
+        a.ck_chunks = 1; a.ck_cap = lanes * bp.ck_stride; a.ck_per_lane = bp.ck_stride;
+    }
+    const kda_status fs = run_bf16(a, bp.fwd, ws, st);
+    if (fs != KDA_OK) return fs;
+    kda::BwdArgs b{};
+    b.lanes = lanes; b.T = d->T; b.nchunks = bp.fwd.nchunks; b.dk = d->dk; b.dv = d->dv;
+    b.q = q; b.k = k; b.v = v; b.la = log_alpha; b.beta = beta; b.S0 = S0;
+    b.dO = dO; b.dO_bf16 = d->out_dtype == KDA_BF16; b.dST = dS_T;
+    b.ckpt = reinterpret_cast<const float*>(ws + bp.ckpt_off); b.ck_stride = bp.ck_stride;
+    b.prep = reinterpret_cast<float*>(ws + bp.prep_off);
+    b.gst = reinterpret_cast<float*>(ws + bp.gst_off);
+    b.dvt = reinterpret_cast<float*>(ws + bp.dvt_off);
+    b.gscr = reinterpret_cast<float*>(ws + bp.gscr_off);
+    b.dq = dq; b.dk_ = dk; b.dv_ = dv; b.dla = dlog_alpha; b.dbeta = dbeta; b.dS0 = dS0;
+    return kda::launch_bwd(b, st) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
 kda_status kda_decode_step_gated(const kda_decode_desc* d, const void* q, const void* k, const void* v,

@@ -94,6 +94,27 @@ struct VarlenPrep {
     int64_t ck_every;       // tokens per checkpoint (> 0 when ck_off is set)
 };
 
+// Backward of chunkwise prefill (bf16 inputs, fp32 gradients), after a forward recompute that
+// stored every chunk's exit state in ckpt ([lanes][ck_stride] states, dk x dv each).
+struct BwdArgs {
+    int64_t lanes, T, nchunks, dk, dv;
+    const void *q, *k, *v, *la, *beta;   // bf16 [lanes][T][d]
+    const float* S0;                      // [lanes][dk][dv] or NULL (zero)
+    const void* dO;                       // [lanes][T][dv], bf16 or fp32
+    bool dO_bf16;
+    const float* dST;                     // [lanes][dk][dv] or NULL (zero)
+    const float* ckpt;                    // forward exit state of chunk c at [lane * ck_stride + c]
+    int64_t ck_stride;
+    float* prep;                          // [lanes * nchunks][bwd_prep_floats]
+    float* gst;                           // [lanes * nchunks][dk][dv]  exit-state gradient of each chunk
+    float* dvt;                           // [lanes * nchunks][64][dv]  dV~ of each chunk
+    float* gscr;                          // [lanes * nchunks][bwd_grad_floats]
+    float *dq, *dk_, *dv_, *dla, *dbeta, *dS0;   // outputs (dS0 may be NULL)
+};
+size_t bwd_prep_floats(int64_t dk, int64_t dv);
+size_t bwd_grad_floats(int64_t dk, int64_t dv);
+hipError_t launch_bwd(const BwdArgs& a, hipStream_t st);
+
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st);
 // fp32-input prefill (one pass, generic chunk kernel).
 hipError_t launch_chunk(const ChunkLaunch& a, hipStream_t st);

@@ -207,6 +207,31 @@ kda_status kda_chunk_fwd_varlen(const kda_varlen_desc* desc,
                                 float* S_ckpt, int32_t* ckpt_offsets, const kda_gating* gating,
                                 void* workspace, size_t workspace_bytes, void* stream);
 
+/* Bytes of device workspace kda_chunk_bwd needs for `desc` (0 for an invalid desc, fp32 inputs or
+ * T = 0). It holds the forward's workspace, the state after every 64-token chunk (fp32), the
+ * recomputed output, and per-chunk fp32 scratch (about 0.5 MiB per chunk of a lane at d = 128). */
+size_t kda_chunk_bwd_workspace_bytes(const kda_chunk_desc* desc);
+
+/*
+ * Backward of chunkwise KDA prefill (training): for L with dL/do = dO and dL/dS_T = dS_T, writes
+ * dL/dq, dL/dk, dL/dv, dL/dlog_alpha, dL/dbeta and dL/dS0.
+ *   inputs as kda_chunk_fwd (in_dtype must be KDA_BF16; S0 NULL = zero state)
+ *   dO              : [B,H,T,dv] out_dtype        dS_T : [B,H,dk,dv] fp32, or NULL (zero)
+ *   dq, dk, dlog_alpha : [B,H,T,dk] fp32 (written)   dv : [B,H,T,dv] fp32   dbeta : [B,H,T] fp32
+ *   dS0             : [B,H,dk,dv] fp32 (written), or NULL to skip
+ *   workspace       : at least kda_chunk_bwd_workspace_bytes(desc) bytes, 256-byte aligned
+ * The call recomputes the forward (with a state checkpoint after every chunk) and then runs the
+ * reverse pass; gradient outputs must not overlap each other, the inputs or the workspace.
+ * Source: the pages print no backward; section 2.2 of the Kimi K3 reading notes gives the
+ * recurrence and chunk equations this differentiates, and says training uses chunkwise KDA.
+ */
+kda_status kda_chunk_bwd(const kda_chunk_desc* desc,
+                         const void* q, const void* k, const void* v,
+                         const void* log_alpha, const void* beta, const float* S0,
+                         const void* dO, const float* dS_T,
+                         float* dq, float* dk, float* dv, float* dlog_alpha, float* dbeta, float* dS0,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
 /*
  * One KDA decode step: kda_decode_step(q,k,v,log_alpha,beta,S) -> (o, S').
  *   q, k, log_alpha : [N,H,dk] in_dtype        v : [N,H,dv] in_dtype

@@ -30,7 +30,8 @@ def lib():
 
 
 def test_header_declares_the_boundary():
-    assert declared_functions() == ["kda_chunk_fwd", "kda_chunk_fwd_varlen", "kda_chunk_fwd_varlen_workspace_bytes",
+    assert declared_functions() == ["kda_chunk_bwd", "kda_chunk_bwd_workspace_bytes", "kda_chunk_fwd",
+                                    "kda_chunk_fwd_varlen", "kda_chunk_fwd_varlen_workspace_bytes",
                                     "kda_chunk_fwd_workspace_bytes", "kda_decode_step", "kda_decode_step_gated",
                                     "kda_status_string", "kda_version"]
 
@@ -200,3 +201,28 @@ def test_gating_rejects_bad_arguments(lib):
     assert call(None, G(z, None, -5.0, 0.0, None, None)) == INVALID
     assert call(FAKE + (3 << 30), G(None, None, 0.0, -1.0, gate, None)) == INVALID
     assert call(FAKE + (3 << 30), G(None, None, 0.0, 1e-6, FAKE + (6 << 30), None)) == INVALID   # gate overlaps o
+
+
+def test_backward_rejects_bad_arguments(lib):
+    d = _desc(B=1, H=2, T=256)
+    P = ctypes.c_void_p
+    base = [FAKE + (i << 30) for i in range(14)]   # q k v la beta S0 dO dS_T dq dk dv dla dbeta dS0
+
+    def call(desc, ptrs, ws=FAKE + (20 << 30), ws_bytes=1 << 40):
+        return lib.kda_chunk_bwd(None if desc is None else ctypes.byref(desc), *[P(p) for p in ptrs], P(ws), ws_bytes,
+                                 None)
+    assert call(None, base) == INVALID
+    assert call(_desc(ind=0, dk=64, dv=64), base) == UNSUPPORTED        # bf16 inputs only
+    assert call(d, base[:8] + [None] + base[9:]) == INVALID             # dq missing
+    bad = list(base)
+    bad[9] = base[8] + 64                                                # dk overlaps dq
+    assert call(d, bad) == INVALID
+    bad = list(base)
+    bad[10] = base[2]                                                    # dv overlaps v
+    assert call(d, bad) == INVALID
+    assert call(d, base, ws=None, ws_bytes=0) == WORKSPACE
+    need = lib.kda_chunk_bwd_workspace_bytes(ctypes.byref(d))
+    assert need > lib.kda_chunk_fwd_workspace_bytes(ctypes.byref(d))
+    assert call(d, base, ws_bytes=need - 1) == WORKSPACE
+    assert call(d, base, ws=FAKE + (20 << 30) + 16, ws_bytes=need) == INVALID   # 256-byte alignment
+    assert lib.kda_chunk_bwd_workspace_bytes(ctypes.byref(_desc(T=0))) == 0
