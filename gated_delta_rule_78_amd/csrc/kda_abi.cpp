@@ -35,6 +35,7 @@ struct Geometry {
     int64_t lanes, max_chunks, slots, dk, dv;
     int32_t in_dtype, segments;
     int64_t tab_slots;   // slot-table entries (packed batches), 0 otherwise
+    int64_t long_lanes;  // lanes that can have max_chunks chunks (plans the sequence split)
 };
 
 // Segments per lane, chunks per segment and workspace of a prefill call.
@@ -74,7 +75,7 @@ Plan make_plan(const Geometry& g) {
     const int64_t nchunks = g.max_chunks;
     p.nchunks = nchunks;
     int64_t nseg = 1;
-    if (g.in_dtype == KDA_BF16 && nchunks > 0) nseg = g.segments > 0 ? g.segments : auto_segments(g.lanes, nchunks);
+    if (g.in_dtype == KDA_BF16 && nchunks > 0) nseg = g.segments > 0 ? g.segments : auto_segments(g.long_lanes, nchunks);
     if (nseg > nchunks) nseg = nchunks > 0 ? nchunks : 1;
     int64_t cps = nchunks > 0 ? ceil_div(nchunks, nseg) : 1;
     if (cps < 1) cps = 1;
@@ -95,7 +96,8 @@ Plan make_plan(const Geometry& g) {
 
 Geometry fixed_geometry(const kda_chunk_desc* d) {
     const int64_t nchunks = ceil_div(d->T, kChunk);
-    return Geometry{d->B * d->H, nchunks, d->B * d->H * nchunks, d->dk, d->dv, d->in_dtype, d->segments, 0};
+    return Geometry{d->B * d->H, nchunks, d->B * d->H * nchunks, d->dk, d->dv, d->in_dtype, d->segments, 0,
+                    d->B * d->H};
 }
 
 kda_status check_chunk_desc(const kda_chunk_desc* d) {
@@ -169,12 +171,18 @@ kda_status check_varlen_desc(const kda_varlen_desc* d) {
 Geometry varlen_geometry(const kda_varlen_desc* d) {
     if (!d->packed) {
         const int64_t nchunks = ceil_div(d->T, kChunk);
-        return Geometry{d->N * d->H, nchunks, d->N * d->H * nchunks, d->dk, d->dv, d->in_dtype, d->segments, 0};
+        return Geometry{d->N * d->H, nchunks, d->N * d->H * nchunks, d->dk, d->dv, d->in_dtype, d->segments, 0,
+                        d->N * d->H};
     }
     const int64_t max_len = d->max_len < d->T ? d->max_len : d->T;
     const int64_t max_chunks = ceil_div(max_len, kChunk);
     const int64_t slots = d->T / kChunk + d->N;
-    return Geometry{d->N * d->H, max_chunks, d->H * slots, d->dk, d->dv, d->in_dtype, d->segments, slots};
+    // The split is planned as if every lane had max_chunks chunks: with few long sequences a
+    // split would shorten their chain, but the scan and the summary pass still run over every
+    // lane (measured: 12 sequences x 32 heads, 8192 tokens, longest 2500: 0.31 ms unsplit,
+    // 0.39 ms in 3 segments).
+    return Geometry{d->N * d->H, max_chunks, d->H * slots, d->dk, d->dv, d->in_dtype, d->segments, slots,
+                    d->N * d->H};
 }
 
 // bf16 prefill after validation: records of every chunk (state independent, fully parallel),

@@ -173,7 +173,7 @@ __device__ __forceinline__ void chunk_step(const unsigned char* rbuf, f32x4 (&S)
 #undef KDA_FRAG
 }
 
-template <typename TOut, int DK, int DV, int NT, bool FIN>
+template <typename TOut, int DK, int DV, int NT, bool FIN, bool GATED>
 __device__ __forceinline__ void run_segment(const ChunkLaunch& p, InterSmem<DK, DV>& sm, int64_t lane, int seg) {
     typedef RecordLayout<DK, DV> R;
     constexpr int NM = R::NM;
@@ -278,7 +278,7 @@ __device__ __forceinline__ void run_segment(const ChunkLaunch& p, InterSmem<DK, 
 
     // Fused epilogue (FINISH with a gate): the gate rows of a chunk load one iteration ahead of
     // their use, like the records; per-token sums of o^2 meet in LDS across the four waves.
-    const bool gated = FIN && p.gt.gate != nullptr;
+    constexpr bool gated = FIN && GATED;
     const __amdgpu_buffer_rsrc_t rgt =
         make_rsrc(gated ? (const bf16_t*)p.gt.gate + row_base * DVl : nullptr, gated ? (uint32_t)(len * DVl * 2) : 0u);
     f32x4 nw[NT];
@@ -379,7 +379,7 @@ __device__ __forceinline__ void run_segment(const ChunkLaunch& p, InterSmem<DK, 
     }
 }
 
-template <typename TOut, int DK, int DV>
+template <typename TOut, int DK, int DV, bool GATED>
 __global__ __launch_bounds__(kThreads, 1) void inter_kernel(ChunkLaunch p) {
     __shared__ InterSmem<DK, DV> sm;
     const int64_t bid = blockIdx.x;
@@ -387,12 +387,12 @@ __global__ __launch_bounds__(kThreads, 1) void inter_kernel(ChunkLaunch p) {
     if (bid < n_fin) {
         const int64_t lane = uniform64(bid / p.fin_nseg);
         const int seg = (int)uniform64(p.fin_seg_lo + bid % p.fin_nseg);
-        run_segment<TOut, DK, DV, DV / 64, true>(p, sm, lane, seg);
+        run_segment<TOut, DK, DV, DV / 64, true, GATED>(p, sm, lane, seg);
     } else {
         const int64_t b2 = bid - n_fin;
         const int64_t lane = uniform64(b2 / p.sum_nseg);
         const int seg = (int)uniform64(p.sum_seg_lo + b2 % p.sum_nseg);
-        run_segment<TOut, DK, DV, (DV + DK) / 64, false>(p, sm, lane, seg);
+        run_segment<TOut, DK, DV, (DV + DK) / 64, false, false>(p, sm, lane, seg);
     }
 }
 
@@ -400,7 +400,10 @@ template <typename TOut, int DK, int DV>
 hipError_t launch_t(const ChunkLaunch& a, hipStream_t st) {
     const int64_t blocks = a.lanes * ((int64_t)a.fin_nseg + (int64_t)a.sum_nseg);
     if (blocks <= 0) return hipSuccess;
-    hipLaunchKernelGGL((inter_kernel<TOut, DK, DV>), dim3((unsigned)blocks), dim3(kThreads), 0, st, a);
+    if (a.gt.gate)
+        hipLaunchKernelGGL((inter_kernel<TOut, DK, DV, true>), dim3((unsigned)blocks), dim3(kThreads), 0, st, a);
+    else
+        hipLaunchKernelGGL((inter_kernel<TOut, DK, DV, false>), dim3((unsigned)blocks), dim3(kThreads), 0, st, a);
     return hipGetLastError();
 }
 
