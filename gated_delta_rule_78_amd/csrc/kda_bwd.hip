@@ -54,6 +54,7 @@ __device__ __forceinline__ float ldin(const bf16_t* p, int64_t i) { return bf16_
 __device__ __forceinline__ float ldo(const bf16_t* p, int64_t i) { return bf16_bits_to_f32(p[i]); }
 __device__ __forceinline__ float ldo(const float* p, int64_t i) { return p[i]; }
 __device__ __forceinline__ float fexp(float x) { return __builtin_amdgcn_exp2f(x * kLog2e); }
+__device__ __forceinline__ f32x4 kZero4f() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
 // Rows [0, nrows) of the chunk into LDS as fp32 (zeros past the end), and the cumulative decay.
 template <int DK>
@@ -143,198 +144,391 @@ __global__ __launch_bounds__(kT) void bwd_prep_kernel(BwdArgs a) {
     for (int ch = threadIdx.x; ch < DK; ch += kT) sc[L::GAM + ch] = fexp(sm.G[kC - 1][ch]);
 }
 
-// Reverse state pass for value columns [j0, j0 + 32) of one lane.
+// Reverse state pass for value columns [j0, j0 + 32) of one lane. Per chunk the factors the pass
+// reads (K-, Q~, W, A_qk, gamma) and the lane's dO block are staged in LDS with 16-byte loads
+// (rows padded by 4 floats against bank conflicts), and each thread computes a small register
+// tile of dV~ and of the new Gx from 16-byte LDS reads.
+template <int DK, int DV>
+struct __align__(16) StateSmem {
+    static constexpr int LK = DK + 4, LB = 32 + 4, LA = kC + 4;
+    float KB[kC][LK], QT[kC][LK], W[kC][LK];
+    float AQK[kC][LA];
+    float dO[kC][LB], X[kC][LB];
+    float Gx[DK][LB];
+    float gam[DK];
+};
+
+// cooperative copy of a rows x cols fp32 block (cols % 4 == 0) from a row-major source with row
+// stride `ld_src` into LDS rows of stride `ld_dst`
+__device__ __forceinline__ void stage(float* dst, int ld_dst, const float* src, int64_t ld_src, int rows, int cols) {
+    const int q4 = cols / 4;
+    for (int e = threadIdx.x; e < rows * q4; e += kT) {
+        const int r = e / q4, c = (e % q4) * 4;
+        *reinterpret_cast<float4*>(dst + r * ld_dst + c) = *reinterpret_cast<const float4*>(src + r * ld_src + c);
+    }
+}
+
 template <int DK, int DV, typename TO>
 __global__ __launch_bounds__(kT) void bwd_state_kernel(BwdArgs a) {
     typedef BwdLayout<DK, DV> L;
+    typedef StateSmem<DK, DV> SS;
     constexpr int NB = 32;
-    __shared__ float Gx[DK][NB];
-    __shared__ float X[kC][NB];
+    extern __shared__ __align__(16) unsigned char smem_raw[];
+    SS& sm = *reinterpret_cast<SS*>(smem_raw);
     const int nblk = DV / NB;
-    const int64_t lane = blockIdx.x / nblk;
-    const int j0 = (int)(blockIdx.x % nblk) * NB;
+    // the column blocks of a lane run on one XCD (block index = lane mod 8 there) when the lane
+    // count allows, so they share the lane's factors in that XCD's L2
+    int64_t lane, cb;
+    if (a.lanes % 8 == 0) {
+        const int64_t bid = blockIdx.x;
+        cb = (bid >> 3) % nblk;
+        lane = (bid / (8 * nblk)) * 8 + (bid & 7);
+    } else {
+        lane = blockIdx.x / nblk;
+        cb = blockIdx.x % nblk;
+    }
+    const int j0 = (int)cb * NB;
     const TO* dO = (const TO*)a.dO;
     for (int e = threadIdx.x; e < DK * NB; e += kT) {
         const int ch = e / NB, j = e % NB;
-        Gx[ch][j] = a.dST ? a.dST[(lane * DK + ch) * DV + j0 + j] : 0.f;
+        sm.Gx[ch][j] = a.dST ? a.dST[(lane * DK + ch) * DV + j0 + j] : 0.f;
     }
-    __syncthreads();
+    // thread tiles: dV~ rows 2xr .. 2xr+1, columns 4xc .. 4xc+3; Gx rows 4gr .. 4gr+3, same columns
+    const int xc = (threadIdx.x & 7) * 4;
+    const int xr = (threadIdx.x >> 3) * 2;
+    const int gr = (threadIdx.x >> 3) * (DK / 32);
     for (int64_t c = a.nchunks - 1; c >= 0; --c) {
         const float* sc = a.prep + (lane * a.nchunks + c) * L::PREP;
         float* gst = a.gst + (lane * a.nchunks + c) * (int64_t)(DK * DV);
         float* dvt = a.dvt + (lane * a.nchunks + c) * (int64_t)(kC * DV);
         const int nrows = (int)(a.T - c * kC < kC ? a.T - c * kC : kC);
         const int64_t orow = lane * a.T + c * kC;
-        for (int e = threadIdx.x; e < DK * NB; e += kT) {
-            const int ch = e / NB, j = e % NB;
-            gst[ch * DV + j0 + j] = Gx[ch][j];
-        }
-        // dV~ = K- Gx + A_qk^T dO
+        __syncthreads();   // the previous chunk is done with every staged array
+        stage(&sm.KB[0][0], SS::LK, sc + L::KB, DK, kC, DK);
+        stage(&sm.QT[0][0], SS::LK, sc + L::QT, DK, kC, DK);
+        stage(&sm.W[0][0], SS::LK, sc + L::W, DK, kC, DK);
+        stage(&sm.AQK[0][0], SS::LA, sc + L::AQK, kC, kC, kC);
         for (int e = threadIdx.x; e < kC * NB; e += kT) {
             const int t = e / NB, j = e % NB;
-            float x = 0.f;
-            for (int ch = 0; ch < DK; ++ch) x += sc[L::KB + t * DK + ch] * Gx[ch][j];
-            for (int i = t; i < nrows; ++i) x += sc[L::AQK + i * kC + t] * ldo(dO, (orow + i) * DV + j0 + j);
-            X[t][j] = x;
-            dvt[t * DV + j0 + j] = x;
+            sm.dO[t][j] = t < nrows ? ldo(dO, (orow + t) * DV + j0 + j) : 0.f;
+        }
+        for (int ch = threadIdx.x; ch < DK; ch += kT) sm.gam[ch] = sc[L::GAM + ch];
+        for (int e = threadIdx.x; e < DK * NB; e += kT) {
+            const int ch = e / NB, j = e % NB;
+            gst[ch * DV + j0 + j] = sm.Gx[ch][j];
+        }
+        __syncthreads();
+        // dV~ = K- Gx + A_qk^T dO
+        {
+            f32x4 x0 = kZero4f(), x1 = kZero4f();
+            for (int ch = 0; ch < DK; ch += 4) {
+                const f32x4 k0 = *reinterpret_cast<const f32x4*>(&sm.KB[xr][ch]);
+                const f32x4 k1 = *reinterpret_cast<const f32x4*>(&sm.KB[xr + 1][ch]);
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const f32x4 g = *reinterpret_cast<const f32x4*>(&sm.Gx[ch + u][xc]);
+                    x0 += k0[u] * g;
+                    x1 += k1[u] * g;
+                }
+            }
+            for (int i = xr; i < kC; ++i) {
+                const f32x4 d = *reinterpret_cast<const f32x4*>(&sm.dO[i][xc]);
+                x0 += sm.AQK[i][xr] * d;
+                if (i > xr) x1 += sm.AQK[i][xr + 1] * d;
+            }
+            *reinterpret_cast<f32x4*>(&sm.X[xr][xc]) = x0;
+            *reinterpret_cast<f32x4*>(&sm.X[xr + 1][xc]) = x1;
+            *reinterpret_cast<f32x4*>(dvt + xr * DV + j0 + xc) = x0;
+            *reinterpret_cast<f32x4*>(dvt + (xr + 1) * DV + j0 + xc) = x1;
         }
         __syncthreads();
         // Gx <- Diag(gamma) Gx + Q~^T dO - W^T dV~
-        float gn[DK * NB / kT];
+        f32x4 gn[DK / 32];
 #pragma unroll
-        for (int r = 0; r < DK * NB / kT; ++r) {
-            const int e = threadIdx.x + r * kT;
-            const int ch = e / NB, j = e % NB;
-            float g = sc[L::GAM + ch] * Gx[ch][j];
-#pragma nounroll
-            for (int t = 0; t < nrows; ++t) g += sc[L::QT + t * DK + ch] * ldo(dO, (orow + t) * DV + j0 + j);
-#pragma nounroll
-            for (int t = 0; t < kC; ++t) g -= sc[L::W + t * DK + ch] * X[t][j];
-            gn[r] = g;
+        for (int r = 0; r < DK / 32; ++r)
+            gn[r] = sm.gam[gr + r] * *reinterpret_cast<const f32x4*>(&sm.Gx[gr + r][xc]);
+        for (int t = 0; t < kC; ++t) {
+            const f32x4 d = *reinterpret_cast<const f32x4*>(&sm.dO[t][xc]);
+            const f32x4 x = *reinterpret_cast<const f32x4*>(&sm.X[t][xc]);
+#pragma unroll
+            for (int r = 0; r < DK / 32; ++r) gn[r] += sm.QT[t][gr + r] * d - sm.W[t][gr + r] * x;
         }
         __syncthreads();
 #pragma unroll
-        for (int r = 0; r < DK * NB / kT; ++r) {
-            const int e = threadIdx.x + r * kT;
-            Gx[e / NB][e % NB] = gn[r];
-        }
-        __syncthreads();
+        for (int r = 0; r < DK / 32; ++r) *reinterpret_cast<f32x4*>(&sm.Gx[gr + r][xc]) = gn[r];
     }
+    __syncthreads();
     if (a.dS0)
         for (int e = threadIdx.x; e < DK * NB; e += kT) {
             const int ch = e / NB, j = e % NB;
-            a.dS0[(lane * DK + ch) * DV + j0 + j] = Gx[ch][j];
+            a.dS0[(lane * DK + ch) * DV + j0 + j] = sm.Gx[ch][j];
         }
 }
 
+// Gradient kernel LDS arena, reused by phase (offsets in floats; rows padded by 4 floats):
+//   phase 1 (twice, one half of the value columns each): S_h, Gx_h [DK][NH+4], W [64][DK+4],
+//           dO_h, dV~_h, V~_h [64][NH+4]
+//   phase 2: dA_kk [64][68] at 0 (kept), then T [64][68], dW [64][DK+4], dV~ [64][DV+4] for
+//           dX = T^T [dW | dV~], then dX_K [64][DK+4], dX_V [64][DV+4], W, U for dA_kk
+//   phase 3: dA_kk, dA_qk [64][68], K, Q, G [64][DK+4] for the pairwise terms; then dG over Q
 template <int DK, int DV>
-struct __align__(16) GradSmem {
-    float K[kC][DK], Q[kC][DK], G[kC][DK];
-    float dAqk[kC][kC + 1], dAkk[kC][kC + 1];   // dAkk first holds T
-    float beta[kC];
-    float dlgam[DK];                             // gamma dgamma + sum_t dK-_t K-_t, joins row 63
+struct GradArena {
+    static constexpr int NH = DV / 2, LH = NH + 4, LK = DK + 4, LV = DV + 4, LA = kC + 4;
+    // phase 1
+    static constexpr int P1_S = 0, P1_GX = P1_S + DK * LH, P1_W = P1_GX + DK * LH, P1_DO = P1_W + kC * LK,
+                         P1_DVT = P1_DO + kC * LH, P1_VT = P1_DVT + kC * LH, P1_END = P1_VT + kC * LH;
+    // phase 2 / 3
+    static constexpr int AKK = 0, P2_T = AKK + kC * LA, P2_DW = P2_T + kC * LA, P2_DVT = P2_DW + kC * LK,
+                         P2A_END = P2_DVT + kC * LV;
+    static constexpr int P2_XK = AKK + kC * LA, P2_XV = P2_XK + kC * LK, P2_W = P2_XV + kC * LV,
+                         P2_U = P2_W + kC * LK, P2B_END = P2_U + kC * LV;
+    static constexpr int AQK = AKK + kC * LA, P3_K = AQK + kC * LA, P3_Q = P3_K + kC * LK, P3_G = P3_Q + kC * LK,
+                         P3_END = P3_G + kC * LK;
+    static constexpr int SMALL = (P1_END > P2B_END ? (P1_END > P3_END ? P1_END : P3_END)
+                                                   : (P2B_END > P3_END ? P2B_END : P3_END));
+    static constexpr int BETA = SMALL, DLGAM = BETA + kC, TOTAL = DLGAM + DK;
+    static_assert(P2A_END <= TOTAL && TOTAL * 4 <= 160 * 1024, "arena fits the LDS of a CU");
 };
 
 template <int DK, int DV, typename TO>
 __global__ __launch_bounds__(kT) void bwd_grad_kernel(BwdArgs a) {
     typedef BwdLayout<DK, DV> L;
-    constexpr int CG = DK / 4;        // channels per thread: thread = (row t, channel group of CG)
-    constexpr int VG = DV / 4;
+    typedef GradArena<DK, DV> A;
+    constexpr int NH = A::NH, LH = A::LH, LK = A::LK, LV = A::LV, LA = A::LA;
+    constexpr int CG = DK / 4;        // channels per thread: thread = (row t, channel group)
+    constexpr int VG = DV / 4;        // value columns per thread
     extern __shared__ __align__(16) unsigned char smem_raw[];
-    GradSmem<DK, DV>& sm = *reinterpret_cast<GradSmem<DK, DV>*>(smem_raw);
+    float* ar = reinterpret_cast<float*>(smem_raw);
+    float* beta = ar + A::BETA;
+    float* dlgam = ar + A::DLGAM;     // gamma dgamma + sum_t dK-_t K-_t (joins row 63 of dG)
     const int64_t lane = blockIdx.x / a.nchunks, c = blockIdx.x % a.nchunks;
     const int64_t row0 = lane * a.T + c * kC;
     const int nrows = (int)(a.T - c * kC < kC ? a.T - c * kC : kC);
     const float* sc = a.prep + (int64_t)blockIdx.x * L::PREP;
-    float* gs = a.gscr + (int64_t)blockIdx.x * L::GRAD;
     const float* Gx = a.gst + (int64_t)blockIdx.x * (DK * DV);
     const float* dVt = a.dvt + (int64_t)blockIdx.x * (kC * DV);
     // entry state: S0 (or zero) for the first chunk, else the forward's state after chunk c - 1
     const float* S = c == 0 ? (a.S0 ? a.S0 + lane * (int64_t)(DK * DV) : nullptr)
                             : a.ckpt + (lane * a.ck_stride + c - 1) * (int64_t)(DK * DV);
     const TO* dO = (const TO*)a.dO;
-    load_chunk_kgq<DK>(a, row0, nrows, sm.K, sm.Q, sm.G, sm.beta);
+    const int tid = threadIdx.x;
+    const int t = tid >> 2;                  // row of this thread in the (row, group) tiles
+    const int c0 = (tid & 3) * CG;           // its channels
+    const int j0 = (tid & 3) * VG;           // its value columns
+    if (tid < kC) beta[tid] = tid < nrows ? ldin((const bf16_t*)a.beta, row0 + tid) : 0.f;
 
-    const int t = threadIdx.x >> 2;          // row of this thread
-    const int c0 = (threadIdx.x & 3) * CG;   // its channels c0 .. c0 + CG - 1
-    const int j0 = (threadIdx.x & 3) * VG;   // its value columns
-    auto dO_at = [&](int tt, int j) -> float { return tt < nrows ? ldo(dO, (row0 + tt) * DV + j) : 0.f; };
-    auto S_at = [&](int ch, int j) -> float { return S ? S[ch * DV + j] : 0.f; };
+    // ---------------- phase 1: V~ = U - W S, and the products over the value columns ----------
+    float accQ[CG], accK[CG], accW[CG], aqk[16];
+    float dgam = 0.f;
+#pragma unroll
+    for (int u = 0; u < CG; ++u) { accQ[u] = 0.f; accK[u] = 0.f; accW[u] = 0.f; }
+#pragma unroll
+    for (int u = 0; u < 16; ++u) aqk[u] = 0.f;
+    float* sS = ar + A::P1_S;
+    float* sGx = ar + A::P1_GX;
+    float* sW = ar + A::P1_W;
+    float* sdO = ar + A::P1_DO;
+    float* sdVt = ar + A::P1_DVT;
+    float* sVt = ar + A::P1_VT;
+    stage(sW, LK, sc + L::W, DK, kC, DK);
+    for (int h = 0; h < 2; ++h) {
+        const int jh = h * NH;
+        if (S) stage(sS, LH, S + jh, DV, DK, NH);
+        else
+            for (int e = tid; e < DK * LH; e += kT) sS[e] = 0.f;
+        stage(sGx, LH, Gx + jh, DV, DK, NH);
+        stage(sdVt, LH, dVt + jh, DV, kC, NH);
+        for (int e = tid; e < kC * NH; e += kT) {
+            const int tt = e / NH, j = e % NH;
+            sdO[tt * LH + j] = tt < nrows ? ldo(dO, (row0 + tt) * DV + jh + j) : 0.f;
+        }
+        __syncthreads();
+        {   // V~_h: thread tile of VR rows x 4 columns (NH / 4 column groups, kT / (NH / 4) row groups)
+            constexpr int NCG = NH / 4, VR = kC * NCG / kT;
+            const int vr = (tid / NCG) * VR, vc = (tid % NCG) * 4;
+            f32x4 acc[VR];
+#pragma unroll
+            for (int r = 0; r < VR; ++r) acc[r] = *reinterpret_cast<const f32x4*>(sc + L::U + (vr + r) * DV + jh + vc);
+            for (int ch = 0; ch < DK; ch += 4) {
+                f32x4 s4[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) s4[u] = *reinterpret_cast<const f32x4*>(sS + (ch + u) * LH + vc);
+#pragma unroll
+                for (int r = 0; r < VR; ++r) {
+                    const f32x4 w4 = *reinterpret_cast<const f32x4*>(sW + (vr + r) * LK + ch);
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) acc[r] -= w4[u] * s4[u];
+                }
+            }
+#pragma unroll
+            for (int r = 0; r < VR; ++r) *reinterpret_cast<f32x4*>(sVt + (vr + r) * LH + vc) = acc[r];
+        }
+        if (tid < DK) {
+            float sacc = 0.f;
+            for (int j = 0; j < NH; ++j) sacc += sGx[tid * LH + j] * sS[tid * LH + j];
+            dgam += sacc;
+        }
+        __syncthreads();
+        // dQ~ += dO S^T, dW -= dV~ S^T, dK- += V~ Gx^T (rows t, channels c0 ..)
+        for (int j = 0; j < NH; j += 4) {
+            const f32x4 o4 = *reinterpret_cast<const f32x4*>(sdO + t * LH + j);
+            const f32x4 d4 = *reinterpret_cast<const f32x4*>(sdVt + t * LH + j);
+            const f32x4 v4 = *reinterpret_cast<const f32x4*>(sVt + t * LH + j);
+#pragma unroll
+            for (int u = 0; u < CG; ++u) {
+                const f32x4 s4 = *reinterpret_cast<const f32x4*>(sS + (c0 + u) * LH + j);
+                const f32x4 g4 = *reinterpret_cast<const f32x4*>(sGx + (c0 + u) * LH + j);
+                accQ[u] += o4[0] * s4[0] + o4[1] * s4[1] + o4[2] * s4[2] + o4[3] * s4[3];
+                accW[u] -= d4[0] * s4[0] + d4[1] * s4[1] + d4[2] * s4[2] + d4[3] * s4[3];
+                accK[u] += v4[0] * g4[0] + v4[1] * g4[1] + v4[2] * g4[2] + v4[3] * g4[3];
+            }
+        }
+        // dA_qk[t][16 g + u] += dO_t . V~_(16 g + u) over this half (lower triangle used later)
+        {
+            const int jg = (tid & 3) * 16;
+            for (int j = 0; j < NH; j += 4) {
+                const f32x4 o4 = *reinterpret_cast<const f32x4*>(sdO + t * LH + j);
+#pragma unroll
+                for (int u = 0; u < 16; ++u) {
+                    const f32x4 v4 = *reinterpret_cast<const f32x4*>(sVt + (jg + u) * LH + j);
+                    aqk[u] += o4[0] * v4[0] + o4[1] * v4[1] + o4[2] * v4[2] + o4[3] * v4[3];
+                }
+            }
+        }
+        __syncthreads();
+    }
+    if (tid < DK) dlgam[tid] = sc[L::GAM + tid] * dgam;
 
-    // V~ = U - W S
-    for (int e = threadIdx.x; e < kC * DV; e += kT) {
-        const int tt = e / DV, j = e % DV;
-        float x = sc[L::U + e];
-        for (int ch = 0; ch < DK; ++ch) x -= sc[L::W + tt * DK + ch] * S_at(ch, j);
-        gs[L::VT + e] = x;
-    }
-    // T into the dAkk slot; dgamma-part of dlgam
-    for (int e = threadIdx.x; e < kC * kC; e += kT) sm.dAkk[e / kC][e % kC] = sc[L::T + e];
-    for (int ch = threadIdx.x; ch < DK; ch += kT) {
-        float s = 0.f;
-        for (int j = 0; j < DV; ++j) s += Gx[ch * DV + j] * S_at(ch, j);
-        sm.dlgam[ch] = sc[L::GAM + ch] * s;
-    }
+    // ---------------- phase 2: [dX_K | dX_V] = T^T [dW | dV~], then dA_kk ---------------------
+    float* sAkk = ar + A::AKK;
+    float* sT = ar + A::P2_T;
+    float* sdW = ar + A::P2_DW;
+    float* sdV2 = ar + A::P2_DVT;
+    stage(sT, LA, sc + L::T, kC, kC, kC);
+    stage(sdV2, LV, dVt, DV, kC, DV);
+#pragma unroll
+    for (int u = 0; u < CG; ++u) sdW[t * LK + c0 + u] = accW[u];
     __syncthreads();
-    // dA_qk = Tril(dO V~^T)
-    for (int e = threadIdx.x; e < kC * kC; e += kT) {
-        const int i = e / kC, j = e % kC;
-        float x = 0.f;
-        if (j <= i)
-            for (int jj = 0; jj < DV; ++jj) x += dO_at(i, jj) * gs[L::VT + j * DV + jj];
-        sm.dAqk[i][j] = x;
+    float xk[CG], xv[VG];
+#pragma unroll
+    for (int u = 0; u < CG; ++u) xk[u] = 0.f;
+#pragma unroll
+    for (int u = 0; u < VG; ++u) xv[u] = 0.f;
+    for (int m = t; m < kC; ++m) {
+        const float tm = sT[m * LA + t];
+#pragma unroll
+        for (int u = 0; u < CG; u += 4) {
+            const f32x4 w4 = *reinterpret_cast<const f32x4*>(sdW + m * LK + c0 + u);
+            xk[u] += tm * w4[0]; xk[u + 1] += tm * w4[1]; xk[u + 2] += tm * w4[2]; xk[u + 3] += tm * w4[3];
+        }
+#pragma unroll
+        for (int u = 0; u < VG; u += 4) {
+            const f32x4 v4 = *reinterpret_cast<const f32x4*>(sdV2 + m * LV + j0 + u);
+            xv[u] += tm * v4[0]; xv[u + 1] += tm * v4[1]; xv[u + 2] += tm * v4[2]; xv[u + 3] += tm * v4[3];
+        }
     }
-    // per (t, channel group): dQ~ = dO S^T, dK- = V~ Gx^T, dW = -dV~ S^T
-    float dq[CG], dk[CG], dG[CG];
+    // dv = beta dX_V; dbeta gets dX_V . V
     float dbeta = 0.f;
-    for (int u = 0; u < CG; ++u) {
-        const int ch = c0 + u;
-        float xq = 0.f, xb = 0.f, xw = 0.f;
-        for (int j = 0; j < DV; ++j) {
-            const float s = S_at(ch, j);
-            xq += dO_at(t, j) * s;
-            xb += gs[L::VT + t * DV + j] * Gx[ch * DV + j];
-            xw -= dVt[t * DV + j] * s;
+    if (t < nrows) {
+        const int64_t r = row0 + t;
+#pragma unroll
+        for (int u = 0; u < VG; ++u) {
+            a.dv_[r * DV + j0 + u] = beta[t] * xv[u];
+            dbeta += xv[u] * ldin((const bf16_t*)a.v, r * DV + j0 + u);
         }
-        const float eg = fexp(sm.G[t][ch]);
-        const float kb = sc[L::KB + t * DK + ch];
-        dq[u] = xq * eg;
-        dk[u] = xb * fexp(sm.G[kC - 1][ch] - sm.G[t][ch]);
-        dG[u] = xq * sm.Q[t][ch] * eg - xb * kb;
-        gs[L::DW + t * DK + ch] = xw;
-        atomicAdd(&sm.dlgam[ch], xb * kb);
     }
+    __syncthreads();   // T, dW, dV~ are done; the dA_kk operands take their place
+    float* sXK = ar + A::P2_XK;
+    float* sXV = ar + A::P2_XV;
+    float* sW2 = ar + A::P2_W;
+    float* sU = ar + A::P2_U;
+#pragma unroll
+    for (int u = 0; u < CG; ++u) sXK[t * LK + c0 + u] = xk[u];
+#pragma unroll
+    for (int u = 0; u < VG; ++u) sXV[t * LV + j0 + u] = xv[u];
+    stage(sW2, LK, sc + L::W, DK, kC, DK);
+    stage(sU, LV, sc + L::U, DV, kC, DV);
     __syncthreads();
-    // [dX_K | dX_V] = T^T [dW | dV~]
-    for (int u = 0; u < CG; ++u) {
-        const int ch = c0 + u;
-        float x = 0.f;
-        for (int m = t; m < kC; ++m) x += sm.dAkk[m][t] * gs[L::DW + m * DK + ch];
-        gs[L::XK + t * DK + ch] = x;
-        const float kt = sm.K[t][ch] * fexp(sm.G[t][ch]);   // K~
-        dk[u] += sm.beta[t] * x * fexp(sm.G[t][ch]);
-        dG[u] += sm.beta[t] * x * kt;
-        dbeta += x * kt;
-    }
-    float dv[VG];
-    for (int u = 0; u < VG; ++u) {
-        const int j = j0 + u;
-        float x = 0.f;
-        for (int m = t; m < kC; ++m) x += sm.dAkk[m][t] * dVt[m * DV + j];
-        gs[L::XV + t * DV + j] = x;
-        dv[u] = sm.beta[t] * x;
-        if (t < nrows) dbeta += x * ldin((const bf16_t*)a.v, (row0 + t) * DV + j);
-    }
-    __syncthreads();
-    // dA_kk = -(dX_K W^T + dX_V U^T), strictly below the diagonal (replaces T)
-    for (int e = threadIdx.x; e < kC * kC; e += kT) {
-        const int i = e / kC, j = e % kC;
-        float x = 0.f;
-        if (j < i) {
-            for (int ch = 0; ch < DK; ++ch) x -= gs[L::XK + i * DK + ch] * sc[L::W + j * DK + ch];
-            for (int jj = 0; jj < DV; ++jj) x -= gs[L::XV + i * DV + jj] * sc[L::U + j * DV + jj];
+    {   // dA_kk[i][16 g + u] = -(dX_K,i . W_(16g+u) + dX_V,i . U_(16g+u)) for j < i
+        const int i = t, jg = (tid & 3) * 16;
+        float acc[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) acc[u] = 0.f;
+        for (int ch = 0; ch < DK; ch += 4) {
+            const f32x4 x4 = *reinterpret_cast<const f32x4*>(sXK + i * LK + ch);
+#pragma unroll
+            for (int u = 0; u < 16; ++u) {
+                const f32x4 w4 = *reinterpret_cast<const f32x4*>(sW2 + (jg + u) * LK + ch);
+                acc[u] -= x4[0] * w4[0] + x4[1] * w4[1] + x4[2] * w4[2] + x4[3] * w4[3];
+            }
         }
-        sm.dAkk[i][j] = x;
+        for (int jj = 0; jj < DV; jj += 4) {
+            const f32x4 x4 = *reinterpret_cast<const f32x4*>(sXV + i * LV + jj);
+#pragma unroll
+            for (int u = 0; u < 16; ++u) {
+                const f32x4 u4 = *reinterpret_cast<const f32x4*>(sU + (jg + u) * LV + jj);
+                acc[u] -= x4[0] * u4[0] + x4[1] * u4[1] + x4[2] * u4[2] + x4[3] * u4[3];
+            }
+        }
+        __syncthreads();   // everyone has read dX / W / U before dA_qk and K, Q, G land on them
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+            sAkk[i * LA + jg + u] = jg + u < i ? acc[u] : 0.f;
+            ar[A::AQK + i * LA + jg + u] = jg + u <= i ? aqk[u] : 0.f;
+        }
+    }
+
+    // ---------------- phase 3: decay factors, pairwise terms, reverse cumsum -----------------
+    float* sK = ar + A::P3_K;
+    float* sQ = ar + A::P3_Q;
+    float* sG = ar + A::P3_G;
+    const float* sAqk = ar + A::AQK;
+    {
+        const bf16_t* k = (const bf16_t*)a.k;
+        const bf16_t* q = (const bf16_t*)a.q;
+        const bf16_t* la = (const bf16_t*)a.la;
+        for (int e = tid; e < kC * DK; e += kT) {
+            const int tt = e / DK, ch = e % DK;
+            const bool ok = tt < nrows;
+            sK[tt * LK + ch] = ok ? ldin(k, (row0 + tt) * DK + ch) : 0.f;
+            sQ[tt * LK + ch] = ok ? ldin(q, (row0 + tt) * DK + ch) : 0.f;
+            sG[tt * LK + ch] = ok ? ldin(la, (row0 + tt) * DK + ch) : 0.f;
+        }
     }
     __syncthreads();
-    // pairwise terms: row sums (this thread's row t against j <= t) and column sums (rows i >= t)
+    for (int ch = tid; ch < DK; ch += kT) {   // G = inclusive cumsum of log_alpha down the rows
+        float acc = 0.f;
+        for (int tt = 0; tt < kC; ++tt) { acc += sG[tt * LK + ch]; sG[tt * LK + ch] = acc; }
+    }
+    __syncthreads();
+    float dq[CG], dk[CG], dG[CG];
+    const float bt = beta[t];
+#pragma unroll
     for (int u = 0; u < CG; ++u) {
         const int ch = c0 + u;
-        const float kt = sm.K[t][ch], qt = sm.Q[t][ch], gt = sm.G[t][ch], bt = sm.beta[t];
+        const float gt = sG[t * LK + ch], kt = sK[t * LK + ch], qt = sQ[t * LK + ch];
+        const float eg = fexp(gt);
+        const float kbf = fexp(sG[(kC - 1) * LK + ch] - gt);   // K- = K kbf
+        dq[u] = accQ[u] * eg;
+        dk[u] = accK[u] * kbf + bt * xk[u] * eg;
+        dG[u] = accQ[u] * qt * eg - accK[u] * kt * kbf + bt * xk[u] * kt * eg;
+        dbeta += xk[u] * kt * eg;
+        atomicAdd(&dlgam[ch], accK[u] * kt * kbf);
+        // pairwise: row sums against j <= t, column sums against rows i >= t
         float rq = 0.f, rk = 0.f, rg = 0.f, rb = 0.f, ck = 0.f, cg = 0.f;
         for (int j = 0; j <= t; ++j) {
-            const float e = fexp(gt - sm.G[j][ch]);
-            const float aq = sm.dAqk[t][j], ak = j < t ? sm.dAkk[t][j] : 0.f;
-            const float kj = sm.K[j][ch] * e;
+            const float e = fexp(gt - sG[j * LK + ch]);
+            const float aq = sAqk[t * LA + j], ak = sAkk[t * LA + j];
+            const float kj = sK[j * LK + ch] * e;
             rq += aq * kj;
             rk += bt * ak * kj;
             rg += (aq * qt + bt * ak * kt) * kj;
             rb += ak * kt * kj;
         }
         for (int i = t; i < kC; ++i) {
-            const float e = fexp(sm.G[i][ch] - gt);
-            const float aq = sm.dAqk[i][t], ak = i > t ? sm.dAkk[i][t] : 0.f;
-            const float w = (aq * sm.Q[i][ch] + sm.beta[i] * ak * sm.K[i][ch]) * e;
+            const float e = fexp(sG[i * LK + ch] - gt);
+            const float aq = sAqk[i * LA + t], ak = sAkk[i * LA + t];
+            const float w = (aq * sQ[i * LK + ch] + beta[i] * ak * sK[i * LK + ch]) * e;
             ck += w;
             cg += w * kt;
         }
@@ -344,25 +538,26 @@ __global__ __launch_bounds__(kT) void bwd_grad_kernel(BwdArgs a) {
         dbeta += rb;
     }
     __syncthreads();
-    // dG into LDS (reusing Q), dgamma's share on row 63, then reverse cumsum per channel
-    for (int u = 0; u < CG; ++u) sm.Q[t][c0 + u] = dG[u] + (t == kC - 1 ? sm.dlgam[c0 + u] : 0.f);
+    // dG into LDS over Q, dgamma's share on row 63, then the reverse cumsum per channel
+#pragma unroll
+    for (int u = 0; u < CG; ++u) sQ[t * LK + c0 + u] = dG[u] + (t == kC - 1 ? dlgam[c0 + u] : 0.f);
     __syncthreads();
-    for (int ch = threadIdx.x; ch < DK; ch += kT) {
+    for (int ch = tid; ch < DK; ch += kT) {
         float acc = 0.f;
-        for (int tt = kC - 1; tt >= 0; --tt) { acc += sm.Q[tt][ch]; sm.Q[tt][ch] = acc; }
+        for (int tt = kC - 1; tt >= 0; --tt) { acc += sQ[tt * LK + ch]; sQ[tt * LK + ch] = acc; }
     }
     __syncthreads();
     dbeta += __shfl_xor(dbeta, 1);
     dbeta += __shfl_xor(dbeta, 2);
     if (t < nrows) {
         const int64_t r = row0 + t;
+#pragma unroll
         for (int u = 0; u < CG; ++u) {
             a.dq[r * DK + c0 + u] = dq[u];
             a.dk_[r * DK + c0 + u] = dk[u];
-            a.dla[r * DK + c0 + u] = sm.Q[t][c0 + u];
+            a.dla[r * DK + c0 + u] = sQ[t * LK + c0 + u];
         }
-        for (int u = 0; u < VG; ++u) a.dv_[r * DV + j0 + u] = dv[u];
-        if ((threadIdx.x & 3) == 0) a.dbeta[r] = dbeta;
+        if ((tid & 3) == 0) a.dbeta[r] = dbeta;
     }
 }
 
@@ -370,12 +565,16 @@ template <int DK, int DV, typename TO>
 hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
     const int64_t chunks = a.lanes * a.nchunks;
     if (chunks <= 0) return hipSuccess;
-    const size_t prep_smem = sizeof(PrepSmem<DK, DV>), grad_smem = sizeof(GradSmem<DK, DV>);
+    const size_t prep_smem = sizeof(PrepSmem<DK, DV>), grad_smem = GradArena<DK, DV>::TOTAL * sizeof(float);
     hipFuncSetAttribute((const void*)bwd_prep_kernel<DK, DV>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)prep_smem);
     hipFuncSetAttribute((const void*)bwd_grad_kernel<DK, DV, TO>, hipFuncAttributeMaxDynamicSharedMemorySize,
                         (int)grad_smem);
     hipLaunchKernelGGL((bwd_prep_kernel<DK, DV>), dim3((unsigned)chunks), dim3(kT), prep_smem, st, a);
-    hipLaunchKernelGGL((bwd_state_kernel<DK, DV, TO>), dim3((unsigned)(a.lanes * (DV / 32))), dim3(kT), 0, st, a);
+    const size_t state_smem = sizeof(StateSmem<DK, DV>);
+    hipFuncSetAttribute((const void*)bwd_state_kernel<DK, DV, TO>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                        (int)state_smem);
+    hipLaunchKernelGGL((bwd_state_kernel<DK, DV, TO>), dim3((unsigned)(a.lanes * (DV / 32))), dim3(kT), state_smem, st,
+                       a);
     hipLaunchKernelGGL((bwd_grad_kernel<DK, DV, TO>), dim3((unsigned)chunks), dim3(kT), grad_smem, st, a);
     return hipGetLastError();
 }
