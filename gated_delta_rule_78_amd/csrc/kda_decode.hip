@@ -10,9 +10,9 @@
 // The fp32 state is ~99% of the bytes, so the kernel is HBM-bound: each state slab is read once
 // and written once with 16-byte coalesced accesses and kept in registers in between.
 //
-// Work mapping: one workgroup of 256 threads per (sequence, head). Thread t owns column quad
-// t % NQ (4 value columns, float4) and rows rg, rg + NRG, ... with rg = t / NQ, so each wave's
-// loads cover whole consecutive rows.
+// Work mapping: one workgroup of 256 threads per (sequence, head, block of NC value columns).
+// Thread t owns column quad t % NQ (4 value columns, float4) of the block and rows rg, rg + NRG,
+// ... with rg = t / NQ, so each wave's loads cover whole row segments.
 #include "kda_device.h"
 #include "kda_internal.h"
 
@@ -24,23 +24,26 @@ __device__ __forceinline__ float sigmoidf_fast(float x) {
     return __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-x * kLog2e));
 }
 
-template <int DK, int DV, typename TIn, typename TOut>
+template <int DK, int DV, int NC, typename TIn, typename TOut>
 __global__ __launch_bounds__(256) void decode_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k,
                                                      const TIn* __restrict__ v, const TIn* __restrict__ la,
                                                      const TIn* __restrict__ beta, float* __restrict__ S,
                                                      TOut* __restrict__ o, int64_t lanes, int64_t H, Gating gt) {
-    constexpr int NQ = DV / 4;        // column quads
+    constexpr int NQ = NC / 4;        // column quads of this workgroup's block
     constexpr int NRG = 256 / NQ;     // row groups
     constexpr int RPT = DK / NRG;     // rows per thread
-    static_assert(RPT * NRG == DK, "shape");
-    __shared__ float red[NRG][NQ][9];
-    __shared__ float kq_part[NRG];
+    constexpr int NB = DV / NC;       // column blocks per (sequence, head)
+    constexpr int RGW = 64 / NQ;      // row groups per wave
+    static_assert(RPT * NRG == DK && NB * NC == DV && RGW >= 1, "shape");
+    __shared__ float red[4][NQ][9];   // per-wave partial sums: r (4), p (4), k^T q
 
     const int t = threadIdx.x;
     const int cq = t % NQ;
     const int rg = t / NQ;
 
-    for (int64_t lane = blockIdx.x; lane < lanes; lane += gridDim.x) {
+    for (int64_t item = blockIdx.x; item < lanes * NB; item += gridDim.x) {
+        const int64_t lane = item / NB;
+        const int col0 = (int)(item % NB) * NC + 4 * cq;   // this thread's first column
         float* Sl = S + lane * (int64_t)(DK * DV);
         const TIn* ql = q + lane * DK;
         const TIn* kl = k + lane * DK;
@@ -48,10 +51,13 @@ __global__ __launch_bounds__(256) void decode_kernel(const TIn* __restrict__ q, 
         const TIn* vl = v + lane * DV;
         const float eA = gt.z ? __builtin_amdgcn_exp2f(gt.A_log[lane % H] * kLog2e) : 0.f;
 
+        // the state streams through once per step: non-temporal loads and stores
         float4 s[RPT];
 #pragma unroll
-        for (int i = 0; i < RPT; ++i)
-            s[i] = *reinterpret_cast<const float4*>(Sl + (int64_t)(rg + NRG * i) * DV + 4 * cq);
+        for (int i = 0; i < RPT; ++i) {
+            const f32x4 x = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(Sl + (int64_t)(rg + NRG * i) * DV + col0));
+            s[i] = make_float4(x[0], x[1], x[2], x[3]);
+        }
 
         float kr[RPT], qr[RPT];
         float rs[4] = {0.f, 0.f, 0.f, 0.f}, ps[4] = {0.f, 0.f, 0.f, 0.f};
@@ -68,54 +74,78 @@ __global__ __launch_bounds__(256) void decode_kernel(const TIn* __restrict__ q, 
             ps[0] += qr[i] * s[i].x; ps[1] += qr[i] * s[i].y; ps[2] += qr[i] * s[i].z; ps[3] += qr[i] * s[i].w;
             kq += kr[i] * qr[i];
         }
+        // sums over the rows: first across the row groups of a wave (lanes NQ apart), then
+        // across the four waves through LDS
 #pragma unroll
-        for (int j = 0; j < 4; ++j) { red[rg][cq][j] = rs[j]; red[rg][cq][4 + j] = ps[j]; }
-        if (cq == 0) kq_part[rg] = kq;
+        for (int m = NQ; m < 64; m <<= 1) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) { rs[j] += __shfl_xor(rs[j], m); ps[j] += __shfl_xor(ps[j], m); }
+            kq += __shfl_xor(kq, m);
+        }
+        const int wv = t >> 6;
+        if ((t & 63) < NQ) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) { red[wv][cq][j] = rs[j]; red[wv][cq][4 + j] = ps[j]; }
+            red[wv][cq][8] = kq;
+        }
         __syncthreads();
         float r4[4] = {0.f, 0.f, 0.f, 0.f}, p4[4] = {0.f, 0.f, 0.f, 0.f};
         float kqt = 0.f;
 #pragma unroll
-        for (int g = 0; g < NRG; ++g) {
+        for (int g = 0; g < 4; ++g) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) { r4[j] += red[g][cq][j]; p4[j] += red[g][cq][4 + j]; }
-            kqt += kq_part[g];
+            kqt += red[g][cq][8];
         }
         const float b = ld_f(beta + lane);
         float d4[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) d4[j] = b * (ld_f(vl + 4 * cq + j) - r4[j]);
+        for (int j = 0; j < 4; ++j) d4[j] = b * (ld_f(vl + col0 + j) - r4[j]);
 #pragma unroll
         for (int i = 0; i < RPT; ++i) {
             s[i].x += kr[i] * d4[0]; s[i].y += kr[i] * d4[1]; s[i].z += kr[i] * d4[2]; s[i].w += kr[i] * d4[3];
-            *reinterpret_cast<float4*>(Sl + (int64_t)(rg + NRG * i) * DV + 4 * cq) = s[i];
+            __builtin_nontemporal_store(f32x4{s[i].x, s[i].y, s[i].z, s[i].w},
+                                        reinterpret_cast<f32x4*>(Sl + (int64_t)(rg + NRG * i) * DV + col0));
         }
-        if (rg == 0) {   // threads 0 .. NQ-1 of wave 0 hold the whole output row
-            TOut* ol = o + lane * DV + 4 * cq;
+        if (rg == 0) {   // threads 0 .. NQ-1 of wave 0 hold the block's output columns
+            TOut* ol = o + lane * DV + col0;
             float y[4] = {p4[0] + kqt * d4[0], p4[1] + kqt * d4[1], p4[2] + kqt * d4[2], p4[3] + kqt * d4[3]};
-            if (gt.gate) {
+            if (NC == DV && gt.gate) {   // the epilogue needs the whole row: launched with NC = DV
                 float ss = y[0] * y[0] + y[1] * y[1] + y[2] * y[2] + y[3] * y[3];
 #pragma unroll
                 for (int m = 1; m < NQ; m <<= 1) ss += __shfl_xor(ss, m);
                 const float rstd = __builtin_amdgcn_rsqf(ss * (1.f / (float)DV) + gt.eps);
-                const TIn* gl = (const TIn*)gt.gate + lane * DV + 4 * cq;
+                const TIn* gl = (const TIn*)gt.gate + lane * DV + col0;
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
-                    y[j] *= rstd * (gt.norm_w ? gt.norm_w[4 * cq + j] : 1.f) * sigmoidf_fast(ld_f(gl + j));
+                    y[j] *= rstd * (gt.norm_w ? gt.norm_w[col0 + j] : 1.f) * sigmoidf_fast(ld_f(gl + j));
             }
             store4(ol, y[0], y[1], y[2], y[3]);
         }
-        __syncthreads();  // red[] is reused by the next lane of a grid-stride loop
+        __syncthreads();  // red[] is reused by the next item of a grid-stride loop
     }
+}
+
+// Columns per workgroup: a (sequence, head) state splits into independent column blocks (each
+// column of S only meets its own column of v), which keeps fewer registers per thread and more
+// workgroups in flight; the fused epilogue normalises a whole row, so it keeps NC = DV.
+constexpr int kDecodeCols = 64;
+
+template <int DK, int DV, int NC, typename TIn, typename TOut>
+static hipError_t launch_decode_nc(const DecodeArgs& a, hipStream_t st) {
+    const int64_t items = a.N * a.H * (DV / NC);
+    const int64_t grid = items < (int64_t)1 << 30 ? items : (int64_t)1 << 30;
+    hipLaunchKernelGGL((decode_kernel<DK, DV, NC, TIn, TOut>), dim3((unsigned)grid), dim3(256), 0, st,
+                       (const TIn*)a.q, (const TIn*)a.k, (const TIn*)a.v, (const TIn*)a.la, (const TIn*)a.beta,
+                       a.S, (TOut*)a.o, a.N * a.H, a.H, a.gt);
+    return hipGetLastError();
 }
 
 template <int DK, int DV, typename TIn, typename TOut>
 static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t st) {
-    const int64_t lanes = a.N * a.H;
-    const int64_t grid = lanes < (int64_t)1 << 30 ? lanes : (int64_t)1 << 30;
-    hipLaunchKernelGGL((decode_kernel<DK, DV, TIn, TOut>), dim3((unsigned)grid), dim3(256), 0, st,
-                       (const TIn*)a.q, (const TIn*)a.k, (const TIn*)a.v, (const TIn*)a.la, (const TIn*)a.beta,
-                       a.S, (TOut*)a.o, lanes, a.H, a.gt);
-    return hipGetLastError();
+    constexpr int NC = kDecodeCols < DV ? kDecodeCols : DV;
+    if (a.gt.gate || NC == DV) return launch_decode_nc<DK, DV, DV, TIn, TOut>(a, st);
+    return launch_decode_nc<DK, DV, NC, TIn, TOut>(a, st);
 }
 
 template <int DK, int DV>
