@@ -277,7 +277,7 @@ def main():
                 for i in range(min(args.decode_steps, 1000))]
         od = torch.empty(dw.N, dw.H, dw.d, device=dev, dtype=dw.dtype)
         for i in range(3):
-            kda.decode_step(*toks[i], S, o=od, stream=stream)
+            kda.decode_step(*toks[i % len(toks)], S, o=od, stream=stream)
         torch.cuda.synchronize()
         d0 = torch.cuda.Event(enable_timing=True)
         d1 = torch.cuda.Event(enable_timing=True)
