@@ -84,6 +84,7 @@ struct __align__(16) PrepSmem {
     float K[kC][DK], Q[kC][DK], G[kC][DK];
     float A[kC][kC + 1], T[kC][kC + 1];
     float beta[kC];
+    float Vx[DV > DK ? kC : 1][DV > DK ? DV : 4];   // beta V when it does not fit over Q
 };
 
 template <int DK, int DV>
@@ -95,53 +96,106 @@ __global__ __launch_bounds__(kT) void bwd_prep_kernel(BwdArgs a) {
     const int64_t row0 = lane * a.T + c * kC;
     const int nrows = (int)(a.T - c * kC < kC ? a.T - c * kC : kC);
     float* sc = a.prep + (int64_t)blockIdx.x * L::PREP;
+    const int tid = threadIdx.x;
     load_chunk_kgq<DK>(a, row0, nrows, sm.K, sm.Q, sm.G, sm.beta);
 
-    // A_kk (i > j, beta-scaled) and A_qk (i >= j)
-    for (int e = threadIdx.x; e < kC * kC; e += kT) {
-        const int i = e / kC, j = e % kC;
-        float akk = 0.f, aqk = 0.f;
-        if (j <= i) {
-            for (int ch = 0; ch < DK; ++ch) {
-                const float f = sm.K[j][ch] * fexp(sm.G[i][ch] - sm.G[j][ch]);
-                akk += sm.K[i][ch] * f;
-                aqk += sm.Q[i][ch] * f;
+    // A_kk (i > j, beta-scaled) and A_qk (i >= j): thread = (row i, columns 16 g .. 16 g + 15)
+    {
+        const int i = tid >> 2, jg = (tid & 3) * 16;
+        float akk[16], aqk[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) { akk[u] = 0.f; aqk[u] = 0.f; }
+        if (jg <= i) {
+            for (int ch = 0; ch < DK; ch += 4) {
+                const f32x4 ki = *reinterpret_cast<const f32x4*>(&sm.K[i][ch]);
+                const f32x4 qi = *reinterpret_cast<const f32x4*>(&sm.Q[i][ch]);
+                const f32x4 gi = *reinterpret_cast<const f32x4*>(&sm.G[i][ch]);
+#pragma unroll
+                for (int u = 0; u < 16; ++u) {
+                    if (jg + u > i) break;
+                    const f32x4 kj = *reinterpret_cast<const f32x4*>(&sm.K[jg + u][ch]);
+                    const f32x4 gj = *reinterpret_cast<const f32x4*>(&sm.G[jg + u][ch]);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float f = kj[e] * fexp(gi[e] - gj[e]);
+                        akk[u] += ki[e] * f;
+                        aqk[u] += qi[e] * f;
+                    }
+                }
             }
         }
-        sm.A[i][j] = j < i ? sm.beta[i] * akk : 0.f;
-        sc[L::AQK + e] = aqk;
-    }
-    __syncthreads();
-    // T = (I + A)^{-1}, unit lower triangular: one column per thread, rows in order
-    if (threadIdx.x < kC) {
-        const int j = threadIdx.x;
-        for (int i = 0; i < kC; ++i) {
-            float v = i == j ? 1.f : 0.f;
-            if (i > j)
-                for (int m = j; m < i; ++m) v -= sm.A[i][m] * sm.T[m][j];
-            sm.T[i][j] = i >= j ? v : 0.f;
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+            const int j = jg + u;
+            sm.A[i][j] = j < i ? sm.beta[i] * akk[u] : 0.f;
+            sc[L::AQK + i * kC + j] = j <= i ? aqk[u] : 0.f;
         }
     }
-    __syncthreads();
-    for (int e = threadIdx.x; e < kC * kC; e += kT) sc[L::T + e] = sm.T[e / kC][e % kC];
-    // W = T Diag(beta) K e^G,  Q~ = Q e^G,  K- = K e^{G_63 - G}
-    for (int e = threadIdx.x; e < kC * DK; e += kT) {
+    // Q~ = Q e^G, K- = K e^{G_63 - G}, gamma
+    for (int e = tid; e < kC * DK; e += kT) {
         const int t = e / DK, ch = e % DK;
-        float w = 0.f;
-        for (int m = 0; m <= t; ++m) w += sm.T[t][m] * sm.beta[m] * sm.K[m][ch] * fexp(sm.G[m][ch]);
-        sc[L::W + e] = w;
         sc[L::QT + e] = sm.Q[t][ch] * fexp(sm.G[t][ch]);
         sc[L::KB + e] = sm.K[t][ch] * fexp(sm.G[kC - 1][ch] - sm.G[t][ch]);
     }
-    // U = T Diag(beta) V
+    for (int ch = tid; ch < DK; ch += kT) sc[L::GAM + ch] = fexp(sm.G[kC - 1][ch]);
+    __syncthreads();
+    // right-hand sides in place: K <- Diag(beta) K e^G, and Diag(beta) V over Q (or its own
+    // array when dv > dk), rows of DV floats
+    float* Vs = DV <= DK ? &sm.Q[0][0] : &sm.Vx[0][0];
     const bf16_t* v = (const bf16_t*)a.v;
-    for (int e = threadIdx.x; e < kC * DV; e += kT) {
-        const int t = e / DV, j = e % DV;
-        float u = 0.f;
-        for (int m = 0; m <= t && m < nrows; ++m) u += sm.T[t][m] * sm.beta[m] * ldin(v, (lane * a.T + c * kC + m) * DV + j);
-        sc[L::U + e] = u;
+    for (int e = tid; e < kC * DK; e += kT) {
+        const int t = e / DK, ch = e % DK;
+        sm.K[t][ch] *= sm.beta[t] * fexp(sm.G[t][ch]);
     }
-    for (int ch = threadIdx.x; ch < DK; ch += kT) sc[L::GAM + ch] = fexp(sm.G[kC - 1][ch]);
+    for (int e = tid; e < kC * DV; e += kT) {
+        const int t = e / DV, j = e % DV;
+        Vs[t * DV + j] = t < nrows ? sm.beta[t] * ldin(v, (row0 + t) * DV + j) : 0.f;
+    }
+    // T = (I + A)^{-1}, unit lower triangular: thread j keeps column j in registers, rows in order
+    if (tid < kC) {
+        const int j = tid;
+        float col[kC];
+#pragma unroll
+        for (int i = 0; i < kC; ++i) {
+            float x = i == j ? 1.f : 0.f;
+#pragma unroll
+            for (int m = 0; m < i; ++m) x -= sm.A[i][m] * col[m];
+            col[i] = i >= j ? x : 0.f;
+        }
+#pragma unroll
+        for (int i = 0; i < kC; ++i) sm.T[i][j] = col[i];
+    }
+    __syncthreads();
+    for (int e = tid; e < kC * kC; e += kT) sc[L::T + e] = sm.T[e / kC][e % kC];
+    // W = T (beta K e^G), U = T (beta V): thread = (row t, channel / column group)
+    {
+        constexpr int CG = DK / 4, VG = DV / 4;
+        const int t = tid >> 2, c0 = (tid & 3) * CG, j0 = (tid & 3) * VG;
+        float w[CG], u[VG];
+#pragma unroll
+        for (int x = 0; x < CG; ++x) w[x] = 0.f;
+#pragma unroll
+        for (int x = 0; x < VG; ++x) u[x] = 0.f;
+        for (int m = 0; m <= t; ++m) {
+            const float tm = sm.T[t][m];
+#pragma unroll
+            for (int x = 0; x < CG; x += 4) {
+                const f32x4 k4 = *reinterpret_cast<const f32x4*>(&sm.K[m][c0 + x]);
+                w[x] += tm * k4[0]; w[x + 1] += tm * k4[1]; w[x + 2] += tm * k4[2]; w[x + 3] += tm * k4[3];
+            }
+#pragma unroll
+            for (int x = 0; x < VG; x += 4) {
+                const f32x4 v4 = *reinterpret_cast<const f32x4*>(Vs + m * DV + j0 + x);
+                u[x] += tm * v4[0]; u[x + 1] += tm * v4[1]; u[x + 2] += tm * v4[2]; u[x + 3] += tm * v4[3];
+            }
+        }
+#pragma unroll
+        for (int x = 0; x < CG; x += 4)
+            *reinterpret_cast<f32x4*>(sc + L::W + t * DK + c0 + x) = f32x4{w[x], w[x + 1], w[x + 2], w[x + 3]};
+#pragma unroll
+        for (int x = 0; x < VG; x += 4)
+            *reinterpret_cast<f32x4*>(sc + L::U + t * DV + j0 + x) = f32x4{u[x], u[x + 1], u[x + 2], u[x + 3]};
+    }
 }
 
 // Reverse state pass for value columns [j0, j0 + 32) of one lane. Per chunk the factors the pass
@@ -501,41 +555,59 @@ __global__ __launch_bounds__(kT) void bwd_grad_kernel(BwdArgs a) {
         for (int tt = 0; tt < kC; ++tt) { acc += sG[tt * LK + ch]; sG[tt * LK + ch] = acc; }
     }
     __syncthreads();
-    float dq[CG], dk[CG], dG[CG];
+    float dq[CG], dk[CG], dG[CG], gt[CG], kt[CG], qt[CG];
     const float bt = beta[t];
 #pragma unroll
-    for (int u = 0; u < CG; ++u) {
-        const int ch = c0 + u;
-        const float gt = sG[t * LK + ch], kt = sK[t * LK + ch], qt = sQ[t * LK + ch];
-        const float eg = fexp(gt);
-        const float kbf = fexp(sG[(kC - 1) * LK + ch] - gt);   // K- = K kbf
-        dq[u] = accQ[u] * eg;
-        dk[u] = accK[u] * kbf + bt * xk[u] * eg;
-        dG[u] = accQ[u] * qt * eg - accK[u] * kt * kbf + bt * xk[u] * kt * eg;
-        dbeta += xk[u] * kt * eg;
-        atomicAdd(&dlgam[ch], accK[u] * kt * kbf);
-        // pairwise: row sums against j <= t, column sums against rows i >= t
-        float rq = 0.f, rk = 0.f, rg = 0.f, rb = 0.f, ck = 0.f, cg = 0.f;
-        for (int j = 0; j <= t; ++j) {
-            const float e = fexp(gt - sG[j * LK + ch]);
-            const float aq = sAqk[t * LA + j], ak = sAkk[t * LA + j];
-            const float kj = sK[j * LK + ch] * e;
-            rq += aq * kj;
-            rk += bt * ak * kj;
-            rg += (aq * qt + bt * ak * kt) * kj;
-            rb += ak * kt * kj;
+    for (int u = 0; u < CG; u += 4) {
+        const f32x4 g4 = *reinterpret_cast<const f32x4*>(sG + t * LK + c0 + u);
+        const f32x4 k4 = *reinterpret_cast<const f32x4*>(sK + t * LK + c0 + u);
+        const f32x4 q4 = *reinterpret_cast<const f32x4*>(sQ + t * LK + c0 + u);
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(sG + (kC - 1) * LK + c0 + u);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            gt[u + e] = g4[e]; kt[u + e] = k4[e]; qt[u + e] = q4[e];
+            const float eg = fexp(g4[e]);
+            const float kbf = fexp(l4[e] - g4[e]);   // K- = K kbf
+            dq[u + e] = accQ[u + e] * eg;
+            dk[u + e] = accK[u + e] * kbf + bt * xk[u + e] * eg;
+            dG[u + e] = accQ[u + e] * q4[e] * eg - accK[u + e] * k4[e] * kbf + bt * xk[u + e] * k4[e] * eg;
+            dbeta += xk[u + e] * k4[e] * eg;
+            atomicAdd(&dlgam[c0 + u + e], accK[u + e] * k4[e] * kbf);
         }
-        for (int i = t; i < kC; ++i) {
-            const float e = fexp(sG[i * LK + ch] - gt);
-            const float aq = sAqk[i * LA + t], ak = sAkk[i * LA + t];
-            const float w = (aq * sQ[i * LK + ch] + beta[i] * ak * sK[i * LK + ch]) * e;
-            ck += w;
-            cg += w * kt;
+    }
+    // pairwise terms. Row sums: this thread's row t against rows j <= t (A_qk and A_kk of row t);
+    // column sums: rows i >= t against row t (their column t). The factors of a (row, row) pair
+    // are read once; the 32 channels come in 16-byte reads.
+    for (int j = 0; j <= t; ++j) {
+        const float aq = sAqk[t * LA + j], bak = bt * sAkk[t * LA + j], ak = sAkk[t * LA + j];
+#pragma unroll
+        for (int u = 0; u < CG; u += 4) {
+            const f32x4 g4 = *reinterpret_cast<const f32x4*>(sG + j * LK + c0 + u);
+            const f32x4 k4 = *reinterpret_cast<const f32x4*>(sK + j * LK + c0 + u);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float kj = k4[e] * fexp(gt[u + e] - g4[e]);
+                dq[u + e] += aq * kj;
+                dk[u + e] += bak * kj;
+                dG[u + e] += (aq * qt[u + e] + bak * kt[u + e]) * kj;
+                dbeta += ak * kt[u + e] * kj;
+            }
         }
-        dq[u] += rq;
-        dk[u] += rk + ck;
-        dG[u] += rg - cg;
-        dbeta += rb;
+    }
+    for (int i = t; i < kC; ++i) {
+        const float aq = sAqk[i * LA + t], bak = beta[i] * sAkk[i * LA + t];
+#pragma unroll
+        for (int u = 0; u < CG; u += 4) {
+            const f32x4 g4 = *reinterpret_cast<const f32x4*>(sG + i * LK + c0 + u);
+            const f32x4 k4 = *reinterpret_cast<const f32x4*>(sK + i * LK + c0 + u);
+            const f32x4 q4 = *reinterpret_cast<const f32x4*>(sQ + i * LK + c0 + u);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float wv = (aq * q4[e] + bak * k4[e]) * fexp(g4[e] - gt[u + e]);
+                dk[u + e] += wv;
+                dG[u + e] -= wv * kt[u + e];
+            }
+        }
     }
     __syncthreads();
     // dG into LDS over Q, dgamma's share on row 63, then the reverse cumsum per channel
