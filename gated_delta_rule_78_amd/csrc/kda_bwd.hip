@@ -637,16 +637,24 @@ template <int DK, int DV, typename TO>
 hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
     const int64_t chunks = a.lanes * a.nchunks;
     if (chunks <= 0) return hipSuccess;
-    const size_t prep_smem = sizeof(PrepSmem<DK, DV>), grad_smem = GradArena<DK, DV>::TOTAL * sizeof(float);
-    hipFuncSetAttribute((const void*)bwd_prep_kernel<DK, DV>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)prep_smem);
-    hipFuncSetAttribute((const void*)bwd_grad_kernel<DK, DV, TO>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                        (int)grad_smem);
+    const size_t prep_smem = sizeof(PrepSmem<DK, DV>), state_smem = sizeof(StateSmem<DK, DV>);
+    const size_t grad_smem = GradArena<DK, DV>::TOTAL * sizeof(float);
+    // each kernel takes more than the default dynamic LDS limit: raise it, and stop at the first
+    // error (a later launch would otherwise hide it)
+    hipError_t e = hipFuncSetAttribute((const void*)bwd_prep_kernel<DK, DV>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)prep_smem);
+    if (e == hipSuccess)
+        e = hipFuncSetAttribute((const void*)bwd_state_kernel<DK, DV, TO>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                (int)state_smem);
+    if (e == hipSuccess)
+        e = hipFuncSetAttribute((const void*)bwd_grad_kernel<DK, DV, TO>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                (int)grad_smem);
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_prep_kernel<DK, DV>), dim3((unsigned)chunks), dim3(kT), prep_smem, st, a);
-    const size_t state_smem = sizeof(StateSmem<DK, DV>);
-    hipFuncSetAttribute((const void*)bwd_state_kernel<DK, DV, TO>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                        (int)state_smem);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_state_kernel<DK, DV, TO>), dim3((unsigned)(a.lanes * (DV / 32))), dim3(kT), state_smem, st,
                        a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_grad_kernel<DK, DV, TO>), dim3((unsigned)chunks), dim3(kT), grad_smem, st, a);
     return hipGetLastError();
 }

@@ -28,6 +28,8 @@
 //   3. blocked forward substitution (I + A_kk) [W | U] = Diag(beta) [K~ | V] on the MFMA, 16
 //      columns per tile, right-hand sides and results in registers; U goes to the record, -W is
 //      transposed through LDS into fragment order.
+#include <atomic>
+
 #include "kda_internal.h"
 #include "kda_mfma.h"
 #include "kda_record.h"
@@ -554,17 +556,20 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs p) {
 #undef KDA_INTRA_LOAD
 }
 
-// Resident workgroups for the persistent grid: two per compute unit (the LDS budget).
+// Resident workgroups for the persistent grid: two per compute unit (the LDS budget). Cached
+// per device; concurrent first calls from several host threads store the same value.
 int resident_workgroups() {
-    static int cached[64];
+    static std::atomic<int> cached[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 512;
-    if (cached[dev] == 0) {
+    int n = cached[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
         int cus = 0;
         if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
-        cached[dev] = 2 * cus;
+        n = 2 * cus;
+        cached[dev].store(n, std::memory_order_relaxed);
     }
-    return cached[dev];
+    return n;
 }
 
 template <int DK, int DV>
