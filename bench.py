@@ -91,7 +91,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="prefill_8k", choices=sorted(WORKLOADS))
     ap.add_argument("--segments", type=int, default=0, help="0 = the library's plan")
     ap.add_argument("--decode-steps", type=int, default=1000)

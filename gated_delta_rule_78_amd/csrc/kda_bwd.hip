@@ -29,7 +29,8 @@ namespace kda {
 namespace {
 
 constexpr int kC = 64;
-constexpr int kT = 256;   // threads per workgroup
+constexpr int kT = 256;   // threads per workgroup (prep, state pass)
+constexpr int kTG = 512;  // threads of the gradient kernel: two waves per SIMD on its LDS arena
 
 // Per-chunk fp32 scratch written by the prep kernel (offsets in floats).
 template <int DK, int DV>
@@ -56,28 +57,92 @@ __device__ __forceinline__ float ldo(const float* p, int64_t i) { return p[i]; }
 __device__ __forceinline__ float fexp(float x) { return __builtin_amdgcn_exp2f(x * kLog2e); }
 __device__ __forceinline__ f32x4 kZero4f() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
-// Rows [0, nrows) of the chunk into LDS as fp32 (zeros past the end), and the cumulative decay.
-template <int DK>
-__device__ void load_chunk_kgq(const BwdArgs& a, int64_t row0, int nrows, float (*Ks)[DK], float (*Qs)[DK],
-                               float (*Gs)[DK], float* bs) {
-    const bf16_t* k = (const bf16_t*)a.k;
-    const bf16_t* q = (const bf16_t*)a.q;
-    const bf16_t* la = (const bf16_t*)a.la;
-    for (int e = threadIdx.x; e < kC * DK; e += kT) {
-        const int t = e / DK, c = e % DK;
-        const bool ok = t < nrows;
-        Ks[t][c] = ok ? ldin(k, (row0 + t) * DK + c) : 0.f;
-        Qs[t][c] = ok ? ldin(q, (row0 + t) * DK + c) : 0.f;
-        Gs[t][c] = ok ? ldin(la, (row0 + t) * DK + c) : 0.f;
-    }
-    if (threadIdx.x < kC) bs[threadIdx.x] = threadIdx.x < nrows ? ldin((const bf16_t*)a.beta, row0 + threadIdx.x) : 0.f;
-    __syncthreads();
-    for (int c = threadIdx.x; c < DK; c += kT) {   // inclusive cumulative sum down the rows
-        float acc = 0.f;
-        for (int t = 0; t < kC; ++t) { acc += Gs[t][c]; Gs[t][c] = acc; }
-    }
-    __syncthreads();
+// Workgroup barrier that orders LDS accesses only: outstanding global loads stay in flight across
+// it. The backward kernels never read back, inside a workgroup, what they write to global memory,
+// so LDS is the only memory their barriers have to order.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
+
+template <int V>
+struct IntC { static constexpr int value = V; };
+
+// Register tiles for cooperative global -> LDS copies by NT threads: every thread issues all of
+// its loads before its first LDS write, so a block costs one memory round trip instead of one per
+// element. Piece e of a block goes to thread e mod NT.
+template <int ROWS, int COLS, int NT>
+struct F32Tile {   // fp32 block, 16-byte pieces
+    static constexpr int Q = COLS / 4, N = ROWS * Q, PER = (N + NT - 1) / NT;
+    static_assert(COLS % 4 == 0, "fp32 tile columns");
+    f32x4 r[PER];
+    __device__ __forceinline__ void load(const float* src, int64_t ld) {
+#pragma unroll
+        for (int u = 0; u < PER; ++u) {
+            const int e = threadIdx.x + u * NT;
+            if (N % NT == 0 || e < N) r[u] = *reinterpret_cast<const f32x4*>(src + (e / Q) * ld + (e % Q) * 4);
+        }
+    }
+    // keep = false stores zeros (a missing operand read from a stand-in address)
+    __device__ __forceinline__ void store(float* dst, int ld, bool keep = true) const {
+#pragma unroll
+        for (int u = 0; u < PER; ++u) {
+            const int e = threadIdx.x + u * NT;
+            if (N % NT == 0 || e < N) *reinterpret_cast<f32x4*>(dst + (e / Q) * ld + (e % Q) * 4) = keep ? r[u] : kZero4f();
+        }
+    }
+};
+
+// Rows [0, nrows) of a bf16 or fp32 row-major block as fp32, in pieces of 8 elements (16 bytes of
+// bf16, 32 of fp32). Rows past nrows read the last valid row (no branch, hence no wait at the
+// load) and are stored as zeros; an optional per-row factor scales what is stored.
+template <int ROWS, int COLS, int NT, typename TI>
+struct InTile {
+    static constexpr int Q = COLS / 8, N = ROWS * Q, PER = (N + NT - 1) / NT, W = sizeof(TI) / 2;
+    static_assert(COLS % 8 == 0 && (sizeof(TI) == 2 || sizeof(TI) == 4), "input tile");
+    uint4 r[PER * W];
+    int nrows;
+    __device__ __forceinline__ void load(const TI* src, int64_t ld, int nrows_) {
+        nrows = nrows_;
+#pragma unroll
+        for (int u = 0; u < PER; ++u) {
+            const int e = threadIdx.x + u * NT, row = e / Q, rr = row < nrows_ ? row : nrows_ - 1;
+            const uint4* p = reinterpret_cast<const uint4*>(src + rr * ld + (e % Q) * 8);
+            if (N % NT == 0 || e < N)
+#pragma unroll
+                for (int w = 0; w < W; ++w) r[u * W + w] = p[w];
+        }
+    }
+    __device__ __forceinline__ void store(float* dst, int ld, const float* rowscale = nullptr) const {
+#pragma unroll
+        for (int u = 0; u < PER; ++u) {
+            const int e = threadIdx.x + u * NT, row = e / Q;
+            if (!(N % NT == 0 || e < N)) continue;
+            const float f = row < nrows ? (rowscale ? rowscale[row] : 1.f) : 0.f;
+            float x[8];
+            if (W == 1) {
+                const uint4 v = r[u * W];
+                const unsigned h[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    x[2 * i] = __uint_as_float(h[i] << 16);
+                    x[2 * i + 1] = __uint_as_float(h[i] & 0xffff0000u);
+                }
+            } else {
+#pragma unroll
+                for (int w = 0; w < W; ++w) {
+                    const uint4 v = r[u * W + w];
+                    x[4 * w] = __uint_as_float(v.x); x[4 * w + 1] = __uint_as_float(v.y);
+                    x[4 * w + 2] = __uint_as_float(v.z); x[4 * w + 3] = __uint_as_float(v.w);
+                }
+            }
+            float* d = dst + row * ld + (e % Q) * 8;
+            *reinterpret_cast<f32x4*>(d) = f32x4{f * x[0], f * x[1], f * x[2], f * x[3]};
+            *reinterpret_cast<f32x4*>(d + 4) = f32x4{f * x[4], f * x[5], f * x[6], f * x[7]};
+        }
+    }
+};
 
 template <int DK, int DV>
 struct __align__(16) PrepSmem {
@@ -97,7 +162,27 @@ __global__ __launch_bounds__(kT) void bwd_prep_kernel(BwdArgs a) {
     const int nrows = (int)(a.T - c * kC < kC ? a.T - c * kC : kC);
     float* sc = a.prep + (int64_t)blockIdx.x * L::PREP;
     const int tid = threadIdx.x;
-    load_chunk_kgq<DK>(a, row0, nrows, sm.K, sm.Q, sm.G, sm.beta);
+    // K, Q, log_alpha and V of the chunk in one round trip; V stays in registers until its LDS
+    // place is free
+    InTile<kC, DK, kT, bf16_t> tk, tq, tg;
+    InTile<kC, DV, kT, bf16_t> tv;
+    tk.load((const bf16_t*)a.k + row0 * DK, DK, nrows);
+    tq.load((const bf16_t*)a.q + row0 * DK, DK, nrows);
+    tg.load((const bf16_t*)a.la + row0 * DK, DK, nrows);
+    tv.load((const bf16_t*)a.v + row0 * DV, DV, nrows);
+    if (tid < kC) {
+        const float b = ldin((const bf16_t*)a.beta, row0 + (tid < nrows ? tid : nrows - 1));
+        sm.beta[tid] = tid < nrows ? b : 0.f;
+    }
+    tk.store(&sm.K[0][0], DK);
+    tq.store(&sm.Q[0][0], DK);
+    tg.store(&sm.G[0][0], DK);
+    lds_barrier();
+    for (int c = tid; c < DK; c += kT) {   // G = inclusive cumulative sum of log_alpha down the rows
+        float acc = 0.f;
+        for (int t = 0; t < kC; ++t) { acc += sm.G[t][c]; sm.G[t][c] = acc; }
+    }
+    lds_barrier();
 
     // A_kk (i > j, beta-scaled) and A_qk (i >= j): thread = (row i, columns 16 g .. 16 g + 15)
     {
@@ -138,19 +223,15 @@ __global__ __launch_bounds__(kT) void bwd_prep_kernel(BwdArgs a) {
         sc[L::KB + e] = sm.K[t][ch] * fexp(sm.G[kC - 1][ch] - sm.G[t][ch]);
     }
     for (int ch = tid; ch < DK; ch += kT) sc[L::GAM + ch] = fexp(sm.G[kC - 1][ch]);
-    __syncthreads();
+    lds_barrier();
     // right-hand sides in place: K <- Diag(beta) K e^G, and Diag(beta) V over Q (or its own
     // array when dv > dk), rows of DV floats
     float* Vs = DV <= DK ? &sm.Q[0][0] : &sm.Vx[0][0];
-    const bf16_t* v = (const bf16_t*)a.v;
     for (int e = tid; e < kC * DK; e += kT) {
         const int t = e / DK, ch = e % DK;
         sm.K[t][ch] *= sm.beta[t] * fexp(sm.G[t][ch]);
     }
-    for (int e = tid; e < kC * DV; e += kT) {
-        const int t = e / DV, j = e % DV;
-        Vs[t * DV + j] = t < nrows ? sm.beta[t] * ldin(v, (row0 + t) * DV + j) : 0.f;
-    }
+    tv.store(Vs, DV, sm.beta);
     // T = (I + A)^{-1}, unit lower triangular: thread j keeps column j in registers, rows in order
     if (tid < kC) {
         const int j = tid;
@@ -165,7 +246,7 @@ __global__ __launch_bounds__(kT) void bwd_prep_kernel(BwdArgs a) {
 #pragma unroll
         for (int i = 0; i < kC; ++i) sm.T[i][j] = col[i];
     }
-    __syncthreads();
+    lds_barrier();
     for (int e = tid; e < kC * kC; e += kT) sc[L::T + e] = sm.T[e / kC][e % kC];
     // W = T (beta K e^G), U = T (beta V): thread = (row t, channel / column group)
     {
@@ -199,9 +280,10 @@ __global__ __launch_bounds__(kT) void bwd_prep_kernel(BwdArgs a) {
 }
 
 // Reverse state pass for value columns [j0, j0 + 32) of one lane. Per chunk the factors the pass
-// reads (K-, Q~, W, A_qk, gamma) and the lane's dO block are staged in LDS with 16-byte loads
-// (rows padded by 4 floats against bank conflicts), and each thread computes a small register
-// tile of dV~ and of the new Gx from 16-byte LDS reads.
+// reads (K-, Q~, W, A_qk, gamma) and the lane's dO block are staged in LDS (rows padded by 4
+// floats against bank conflicts), and each thread computes a small register tile of dV~ and of the
+// new Gx from 16-byte LDS reads. The chunk before the current one is loaded into registers while
+// the current one computes; the barriers order LDS only, so that load stays in flight across them.
 template <int DK, int DV>
 struct __align__(16) StateSmem {
     static constexpr int LK = DK + 4, LB = 32 + 4, LA = kC + 4;
@@ -212,21 +294,53 @@ struct __align__(16) StateSmem {
     float gam[DK];
 };
 
-// cooperative copy of a rows x cols fp32 block (cols % 4 == 0) from a row-major source with row
-// stride `ld_src` into LDS rows of stride `ld_dst`
-__device__ __forceinline__ void stage(float* dst, int ld_dst, const float* src, int64_t ld_src, int rows, int cols) {
-    const int q4 = cols / 4;
-    for (int e = threadIdx.x; e < rows * q4; e += kT) {
-        const int r = e / q4, c = (e % q4) * 4;
-        *reinterpret_cast<float4*>(dst + r * ld_dst + c) = *reinterpret_cast<const float4*>(src + r * ld_src + c);
+// one thread's share of a chunk's state-pass operands, held in registers between the global load
+// and the LDS store (kT threads; element e of a block goes to thread e mod kT)
+template <int DK, typename TO>
+struct StateFetch {
+    static constexpr int NB = 32;
+    static constexpr int NF = kC * DK / 4 / kT;   // float4s of one [64][DK] factor
+    static constexpr int NA = kC * kC / 4 / kT;   // float4s of A_qk
+    static constexpr int ND = kC * NB / kT;       // dO elements
+    f32x4 kb[NF], qt[NF], w[NF], aqk[NA];
+    f32x4 gam;
+    TO dO[ND];     // raw, converted when stored to LDS
+    int nrows;
+
+    template <typename L>
+    __device__ __forceinline__ void load(const float* sc, const TO* dO_, int64_t orow, int nrows, int j0, int dv) {
+        constexpr int Q = DK / 4;
+        this->nrows = nrows;
+#pragma unroll
+        for (int u = 0; u < NF; ++u) {
+            const int e = threadIdx.x + u * kT, r = e / Q, c = (e % Q) * 4;
+            kb[u] = *reinterpret_cast<const f32x4*>(sc + L::KB + r * DK + c);
+            qt[u] = *reinterpret_cast<const f32x4*>(sc + L::QT + r * DK + c);
+            w[u] = *reinterpret_cast<const f32x4*>(sc + L::W + r * DK + c);
+        }
+#pragma unroll
+        for (int u = 0; u < NA; ++u) {
+            const int e = threadIdx.x + u * kT;
+            aqk[u] = *reinterpret_cast<const f32x4*>(sc + L::AQK + e * 4);
+        }
+        if ((int)threadIdx.x < DK / 4) gam = *reinterpret_cast<const f32x4*>(sc + L::GAM + threadIdx.x * 4);
+#pragma unroll
+        for (int u = 0; u < ND; ++u) {
+            // rows past the end read the last row (no branch, so no wait); they are zeroed when
+            // the raw values go to LDS, so nothing here waits for the loads to land
+            const int e = threadIdx.x + u * kT, t = e / NB, j = e % NB, tr = t < nrows ? t : nrows - 1;
+            dO[u] = dO_[(orow + tr) * dv + j0 + j];
+        }
     }
-}
+};
 
 template <int DK, int DV, typename TO>
 __global__ __launch_bounds__(kT) void bwd_state_kernel(BwdArgs a) {
     typedef BwdLayout<DK, DV> L;
     typedef StateSmem<DK, DV> SS;
-    constexpr int NB = 32;
+    typedef StateFetch<DK, TO> F;
+    constexpr int NB = F::NB;
+    static_assert(DV % NB == 0 && (kC * DK / 4) % kT == 0 && (kC * kC / 4) % kT == 0, "state tiles");
     extern __shared__ __align__(16) unsigned char smem_raw[];
     SS& sm = *reinterpret_cast<SS*>(smem_raw);
     const int nblk = DV / NB;
@@ -247,31 +361,49 @@ __global__ __launch_bounds__(kT) void bwd_state_kernel(BwdArgs a) {
         const int ch = e / NB, j = e % NB;
         sm.Gx[ch][j] = a.dST ? a.dST[(lane * DK + ch) * DV + j0 + j] : 0.f;
     }
+    auto chunk_rows = [&](int64_t c) { return (int)(a.T - c * kC < kC ? a.T - c * kC : kC); };
+    F f;
+    {
+        const int64_t c = a.nchunks - 1;
+        f.template load<L>(a.prep + (lane * a.nchunks + c) * L::PREP, dO, lane * a.T + c * kC, chunk_rows(c), j0, DV);
+    }
     // thread tiles: dV~ rows 2xr .. 2xr+1, columns 4xc .. 4xc+3; Gx rows 4gr .. 4gr+3, same columns
     const int xc = (threadIdx.x & 7) * 4;
     const int xr = (threadIdx.x >> 3) * 2;
     const int gr = (threadIdx.x >> 3) * (DK / 32);
     for (int64_t c = a.nchunks - 1; c >= 0; --c) {
-        const float* sc = a.prep + (lane * a.nchunks + c) * L::PREP;
         float* gst = a.gst + (lane * a.nchunks + c) * (int64_t)(DK * DV);
         float* dvt = a.dvt + (lane * a.nchunks + c) * (int64_t)(kC * DV);
-        const int nrows = (int)(a.T - c * kC < kC ? a.T - c * kC : kC);
-        const int64_t orow = lane * a.T + c * kC;
-        __syncthreads();   // the previous chunk is done with every staged array
-        stage(&sm.KB[0][0], SS::LK, sc + L::KB, DK, kC, DK);
-        stage(&sm.QT[0][0], SS::LK, sc + L::QT, DK, kC, DK);
-        stage(&sm.W[0][0], SS::LK, sc + L::W, DK, kC, DK);
-        stage(&sm.AQK[0][0], SS::LA, sc + L::AQK, kC, kC, kC);
-        for (int e = threadIdx.x; e < kC * NB; e += kT) {
-            const int t = e / NB, j = e % NB;
-            sm.dO[t][j] = t < nrows ? ldo(dO, (orow + t) * DV + j0 + j) : 0.f;
+        lds_barrier();   // the previous chunk is done with every staged array; its Gx is in place
+        {
+            constexpr int Q = DK / 4;
+#pragma unroll
+            for (int u = 0; u < F::NF; ++u) {
+                const int e = threadIdx.x + u * kT, r = e / Q, cc = (e % Q) * 4;
+                *reinterpret_cast<f32x4*>(&sm.KB[r][cc]) = f.kb[u];
+                *reinterpret_cast<f32x4*>(&sm.QT[r][cc]) = f.qt[u];
+                *reinterpret_cast<f32x4*>(&sm.W[r][cc]) = f.w[u];
+            }
+#pragma unroll
+            for (int u = 0; u < F::NA; ++u) {
+                const int e = threadIdx.x + u * kT, r = (e * 4) / kC, cc = (e * 4) % kC;
+                *reinterpret_cast<f32x4*>(&sm.AQK[r][cc]) = f.aqk[u];
+            }
+            if ((int)threadIdx.x < DK / 4) *reinterpret_cast<f32x4*>(&sm.gam[threadIdx.x * 4]) = f.gam;
+#pragma unroll
+            for (int u = 0; u < F::ND; ++u) {
+                const int e = threadIdx.x + u * kT;
+                sm.dO[e / NB][e % NB] = e / NB < f.nrows ? ldo(&f.dO[u], 0) : 0.f;
+            }
         }
-        for (int ch = threadIdx.x; ch < DK; ch += kT) sm.gam[ch] = sc[L::GAM + ch];
         for (int e = threadIdx.x; e < DK * NB; e += kT) {
             const int ch = e / NB, j = e % NB;
             gst[ch * DV + j0 + j] = sm.Gx[ch][j];
         }
-        __syncthreads();
+        if (c > 0)   // the next chunk's operands travel while this one computes
+            f.template load<L>(a.prep + (lane * a.nchunks + c - 1) * L::PREP, dO, lane * a.T + (c - 1) * kC,
+                               chunk_rows(c - 1), j0, DV);
+        lds_barrier();
         // dV~ = K- Gx + A_qk^T dO
         {
             f32x4 x0 = kZero4f(), x1 = kZero4f();
@@ -295,7 +427,7 @@ __global__ __launch_bounds__(kT) void bwd_state_kernel(BwdArgs a) {
             *reinterpret_cast<f32x4*>(dvt + xr * DV + j0 + xc) = x0;
             *reinterpret_cast<f32x4*>(dvt + (xr + 1) * DV + j0 + xc) = x1;
         }
-        __syncthreads();
+        lds_barrier();
         // Gx <- Diag(gamma) Gx + Q~^T dO - W^T dV~
         f32x4 gn[DK / 32];
 #pragma unroll
@@ -307,11 +439,11 @@ __global__ __launch_bounds__(kT) void bwd_state_kernel(BwdArgs a) {
 #pragma unroll
             for (int r = 0; r < DK / 32; ++r) gn[r] += sm.QT[t][gr + r] * d - sm.W[t][gr + r] * x;
         }
-        __syncthreads();
+        lds_barrier();
 #pragma unroll
         for (int r = 0; r < DK / 32; ++r) *reinterpret_cast<f32x4*>(&sm.Gx[gr + r][xc]) = gn[r];
     }
-    __syncthreads();
+    lds_barrier();
     if (a.dS0)
         for (int e = threadIdx.x; e < DK * NB; e += kT) {
             const int ch = e / NB, j = e % NB;
@@ -345,12 +477,14 @@ struct GradArena {
 };
 
 template <int DK, int DV, typename TO>
-__global__ __launch_bounds__(kT) void bwd_grad_kernel(BwdArgs a) {
+__global__ __launch_bounds__(kTG) void bwd_grad_kernel(BwdArgs a) {
     typedef BwdLayout<DK, DV> L;
     typedef GradArena<DK, DV> A;
     constexpr int NH = A::NH, LH = A::LH, LK = A::LK, LV = A::LV, LA = A::LA;
-    constexpr int CG = DK / 4;        // channels per thread: thread = (row t, channel group)
-    constexpr int VG = DV / 4;        // value columns per thread
+    constexpr int NGR = kTG / kC;     // threads per row
+    constexpr int CG = DK / NGR;      // channels per thread: thread = (row t, channel group)
+    constexpr int VG = DV / NGR;      // value columns per thread
+    constexpr int JG = kC / NGR;      // columns of A_qk / A_kk per thread
     extern __shared__ __align__(16) unsigned char smem_raw[];
     float* ar = reinterpret_cast<float*>(smem_raw);
     float* beta = ar + A::BETA;
@@ -366,43 +500,72 @@ __global__ __launch_bounds__(kT) void bwd_grad_kernel(BwdArgs a) {
                             : a.ckpt + (lane * a.ck_stride + c - 1) * (int64_t)(DK * DV);
     const TO* dO = (const TO*)a.dO;
     const int tid = threadIdx.x;
-    const int t = tid >> 2;                  // row of this thread in the (row, group) tiles
-    const int c0 = (tid & 3) * CG;           // its channels
-    const int j0 = (tid & 3) * VG;           // its value columns
+    const int t = tid / NGR;                 // row of this thread in the (row, group) tiles
+    const int gi = tid % NGR;
+    const int c0 = gi * CG;                  // its channels
+    const int j0 = gi * VG;                  // its value columns
     if (tid < kC) beta[tid] = tid < nrows ? ldin((const bf16_t*)a.beta, row0 + tid) : 0.f;
 
     // ---------------- phase 1: V~ = U - W S, and the products over the value columns ----------
-    float accQ[CG], accK[CG], accW[CG], aqk[16];
+    float accQ[CG], accK[CG], accW[CG], aqk[JG];
     float dgam = 0.f;
 #pragma unroll
     for (int u = 0; u < CG; ++u) { accQ[u] = 0.f; accK[u] = 0.f; accW[u] = 0.f; }
 #pragma unroll
-    for (int u = 0; u < 16; ++u) aqk[u] = 0.f;
+    for (int u = 0; u < JG; ++u) aqk[u] = 0.f;
     float* sS = ar + A::P1_S;
     float* sGx = ar + A::P1_GX;
     float* sW = ar + A::P1_W;
     float* sdO = ar + A::P1_DO;
     float* sdVt = ar + A::P1_DVT;
     float* sVt = ar + A::P1_VT;
-    stage(sW, LK, sc + L::W, DK, kC, DK);
-    for (int h = 0; h < 2; ++h) {
-        const int jh = h * NH;
-        if (S) stage(sS, LH, S + jh, DV, DK, NH);
-        else
-            for (int e = tid; e < DK * LH; e += kT) sS[e] = 0.f;
-        stage(sGx, LH, Gx + jh, DV, DK, NH);
-        stage(sdVt, LH, dVt + jh, DV, kC, NH);
-        for (int e = tid; e < kC * NH; e += kT) {
-            const int tt = e / NH, j = e % NH;
-            sdO[tt * LH + j] = tt < nrows ? ldo(dO, (row0 + tt) * DV + jh + j) : 0.f;
-        }
-        __syncthreads();
-        {   // V~_h: thread tile of VR rows x 4 columns (NH / 4 column groups, kT / (NH / 4) row groups)
-            constexpr int NCG = NH / 4, VR = kC * NCG / kT;
-            const int vr = (tid / NCG) * VR, vc = (tid % NCG) * 4;
-            f32x4 acc[VR];
+    // operands of each phase are loaded into registers during the phase before it
+    F32Tile<kC, DK, kTG> tw;
+    F32Tile<DK, NH, kTG> ts, tgx;
+    F32Tile<kC, NH, kTG> tdv;
+    InTile<kC, NH, kTG, TO> tdo;
+    F32Tile<kC, kC, kTG> tT;
+    F32Tile<kC, DV, kTG> tdv2;
+    const float* Ssrc = S ? S : Gx;   // a stand-in of the same shape when there is no entry state
+    // V~_h tiles: VR rows x 4 columns per thread (NH / 4 column groups); U is their starting value
+    constexpr int NCG = NH / 4, VR = kC * NCG / kTG;
+    const int vr = (tid / NCG) * VR, vc = (tid % NCG) * 4;
+    f32x4 uin[VR];
+    auto load_uin = [&](int jh) {
 #pragma unroll
-            for (int r = 0; r < VR; ++r) acc[r] = *reinterpret_cast<const f32x4*>(sc + L::U + (vr + r) * DV + jh + vc);
+        for (int r = 0; r < VR; ++r) uin[r] = *reinterpret_cast<const f32x4*>(sc + L::U + (vr + r) * DV + jh + vc);
+    };
+    tw.load(sc + L::W, DK);
+    ts.load(Ssrc, DV);
+    tgx.load(Gx, DV);
+    tdv.load(dVt, DV);
+    tdo.load(dO + row0 * DV, DV, nrows);
+    load_uin(0);
+    tw.store(sW, LK);
+    // the two halves are written out (no loop) so that the registers a prefetch fills are the ones
+    // the next half reads, with no copies that would wait for the loads
+    auto half = [&](auto hc) {
+        constexpr int h = decltype(hc)::value, jh = h * NH;
+        ts.store(sS, LH, S != nullptr);
+        tgx.store(sGx, LH);
+        tdv.store(sdVt, LH);
+        tdo.store(sdO, LH);
+        f32x4 acc[VR];
+#pragma unroll
+        for (int r = 0; r < VR; ++r) acc[r] = uin[r];
+        lds_barrier();
+        if constexpr (h == 0) {
+            ts.load(Ssrc + NH, DV);
+            tgx.load(Gx + NH, DV);
+            tdv.load(dVt + NH, DV);
+            tdo.load(dO + row0 * DV + NH, DV, nrows);
+            load_uin(NH);
+        } else {
+            tT.load(sc + L::T, kC);
+            tdv2.load(dVt, DV);
+        }
+        {   // V~_h: thread tile of VR rows x 4 columns, starting from U
+#pragma unroll 2
             for (int ch = 0; ch < DK; ch += 4) {
                 f32x4 s4[4];
 #pragma unroll
@@ -419,11 +582,13 @@ __global__ __launch_bounds__(kT) void bwd_grad_kernel(BwdArgs a) {
         }
         if (tid < DK) {
             float sacc = 0.f;
+#pragma unroll 4
             for (int j = 0; j < NH; ++j) sacc += sGx[tid * LH + j] * sS[tid * LH + j];
             dgam += sacc;
         }
-        __syncthreads();
+        lds_barrier();
         // dQ~ += dO S^T, dW -= dV~ S^T, dK- += V~ Gx^T (rows t, channels c0 ..)
+#pragma unroll 1
         for (int j = 0; j < NH; j += 4) {
             const f32x4 o4 = *reinterpret_cast<const f32x4*>(sdO + t * LH + j);
             const f32x4 d4 = *reinterpret_cast<const f32x4*>(sdVt + t * LH + j);
@@ -437,20 +602,23 @@ __global__ __launch_bounds__(kT) void bwd_grad_kernel(BwdArgs a) {
                 accK[u] += v4[0] * g4[0] + v4[1] * g4[1] + v4[2] * g4[2] + v4[3] * g4[3];
             }
         }
-        // dA_qk[t][16 g + u] += dO_t . V~_(16 g + u) over this half (lower triangle used later)
+        // dA_qk[t][JG g + u] += dO_t . V~_(JG g + u) over this half (lower triangle used later)
         {
-            const int jg = (tid & 3) * 16;
+            const int jg = gi * JG;
+#pragma unroll 1
             for (int j = 0; j < NH; j += 4) {
                 const f32x4 o4 = *reinterpret_cast<const f32x4*>(sdO + t * LH + j);
 #pragma unroll
-                for (int u = 0; u < 16; ++u) {
+                for (int u = 0; u < JG; ++u) {
                     const f32x4 v4 = *reinterpret_cast<const f32x4*>(sVt + (jg + u) * LH + j);
                     aqk[u] += o4[0] * v4[0] + o4[1] * v4[1] + o4[2] * v4[2] + o4[3] * v4[3];
                 }
             }
         }
-        __syncthreads();
-    }
+        lds_barrier();
+    };
+    half(IntC<0>{});
+    half(IntC<1>{});
     if (tid < DK) dlgam[tid] = sc[L::GAM + tid] * dgam;
 
     // ---------------- phase 2: [dX_K | dX_V] = T^T [dW | dV~], then dA_kk ---------------------
@@ -458,11 +626,15 @@ __global__ __launch_bounds__(kT) void bwd_grad_kernel(BwdArgs a) {
     float* sT = ar + A::P2_T;
     float* sdW = ar + A::P2_DW;
     float* sdV2 = ar + A::P2_DVT;
-    stage(sT, LA, sc + L::T, kC, kC, kC);
-    stage(sdV2, LV, dVt, DV, kC, DV);
+    tT.store(sT, LA);
+    tdv2.store(sdV2, LV);
 #pragma unroll
     for (int u = 0; u < CG; ++u) sdW[t * LK + c0 + u] = accW[u];
-    __syncthreads();
+    lds_barrier();
+    F32Tile<kC, DK, kTG> tw2;
+    F32Tile<kC, DV, kTG> tu;
+    tw2.load(sc + L::W, DK);
+    tu.load(sc + L::U, DV);
     float xk[CG], xv[VG];
 #pragma unroll
     for (int u = 0; u < CG; ++u) xk[u] = 0.f;
@@ -491,7 +663,7 @@ __global__ __launch_bounds__(kT) void bwd_grad_kernel(BwdArgs a) {
             dbeta += xv[u] * ldin((const bf16_t*)a.v, r * DV + j0 + u);
         }
     }
-    __syncthreads();   // T, dW, dV~ are done; the dA_kk operands take their place
+    lds_barrier();   // T, dW, dV~ are done; the dA_kk operands take their place
     float* sXK = ar + A::P2_XK;
     float* sXV = ar + A::P2_XV;
     float* sW2 = ar + A::P2_W;
@@ -500,18 +672,22 @@ __global__ __launch_bounds__(kT) void bwd_grad_kernel(BwdArgs a) {
     for (int u = 0; u < CG; ++u) sXK[t * LK + c0 + u] = xk[u];
 #pragma unroll
     for (int u = 0; u < VG; ++u) sXV[t * LV + j0 + u] = xv[u];
-    stage(sW2, LK, sc + L::W, DK, kC, DK);
-    stage(sU, LV, sc + L::U, DV, kC, DV);
-    __syncthreads();
-    {   // dA_kk[i][16 g + u] = -(dX_K,i . W_(16g+u) + dX_V,i . U_(16g+u)) for j < i
-        const int i = t, jg = (tid & 3) * 16;
-        float acc[16];
+    tw2.store(sW2, LK);
+    tu.store(sU, LV);
+    lds_barrier();
+    InTile<kC, DK, kTG, bf16_t> tk, tq, tg;
+    tk.load((const bf16_t*)a.k + row0 * DK, DK, nrows);
+    tq.load((const bf16_t*)a.q + row0 * DK, DK, nrows);
+    tg.load((const bf16_t*)a.la + row0 * DK, DK, nrows);
+    {   // dA_kk[i][JG g + u] = -(dX_K,i . W_(JG g+u) + dX_V,i . U_(JG g+u)) for j < i
+        const int i = t, jg = gi * JG;
+        float acc[JG];
 #pragma unroll
-        for (int u = 0; u < 16; ++u) acc[u] = 0.f;
+        for (int u = 0; u < JG; ++u) acc[u] = 0.f;
         for (int ch = 0; ch < DK; ch += 4) {
             const f32x4 x4 = *reinterpret_cast<const f32x4*>(sXK + i * LK + ch);
 #pragma unroll
-            for (int u = 0; u < 16; ++u) {
+            for (int u = 0; u < JG; ++u) {
                 const f32x4 w4 = *reinterpret_cast<const f32x4*>(sW2 + (jg + u) * LK + ch);
                 acc[u] -= x4[0] * w4[0] + x4[1] * w4[1] + x4[2] * w4[2] + x4[3] * w4[3];
             }
@@ -519,14 +695,14 @@ __global__ __launch_bounds__(kT) void bwd_grad_kernel(BwdArgs a) {
         for (int jj = 0; jj < DV; jj += 4) {
             const f32x4 x4 = *reinterpret_cast<const f32x4*>(sXV + i * LV + jj);
 #pragma unroll
-            for (int u = 0; u < 16; ++u) {
+            for (int u = 0; u < JG; ++u) {
                 const f32x4 u4 = *reinterpret_cast<const f32x4*>(sU + (jg + u) * LV + jj);
                 acc[u] -= x4[0] * u4[0] + x4[1] * u4[1] + x4[2] * u4[2] + x4[3] * u4[3];
             }
         }
-        __syncthreads();   // everyone has read dX / W / U before dA_qk and K, Q, G land on them
+        lds_barrier();   // everyone has read dX / W / U before dA_qk and K, Q, G land on them
 #pragma unroll
-        for (int u = 0; u < 16; ++u) {
+        for (int u = 0; u < JG; ++u) {
             sAkk[i * LA + jg + u] = jg + u < i ? acc[u] : 0.f;
             ar[A::AQK + i * LA + jg + u] = jg + u <= i ? aqk[u] : 0.f;
         }
@@ -537,24 +713,15 @@ __global__ __launch_bounds__(kT) void bwd_grad_kernel(BwdArgs a) {
     float* sQ = ar + A::P3_Q;
     float* sG = ar + A::P3_G;
     const float* sAqk = ar + A::AQK;
-    {
-        const bf16_t* k = (const bf16_t*)a.k;
-        const bf16_t* q = (const bf16_t*)a.q;
-        const bf16_t* la = (const bf16_t*)a.la;
-        for (int e = tid; e < kC * DK; e += kT) {
-            const int tt = e / DK, ch = e % DK;
-            const bool ok = tt < nrows;
-            sK[tt * LK + ch] = ok ? ldin(k, (row0 + tt) * DK + ch) : 0.f;
-            sQ[tt * LK + ch] = ok ? ldin(q, (row0 + tt) * DK + ch) : 0.f;
-            sG[tt * LK + ch] = ok ? ldin(la, (row0 + tt) * DK + ch) : 0.f;
-        }
-    }
-    __syncthreads();
-    for (int ch = tid; ch < DK; ch += kT) {   // G = inclusive cumsum of log_alpha down the rows
+    tk.store(sK, LK);
+    tq.store(sQ, LK);
+    tg.store(sG, LK);
+    lds_barrier();
+    for (int ch = tid; ch < DK; ch += kTG) {   // G = inclusive cumsum of log_alpha down the rows
         float acc = 0.f;
         for (int tt = 0; tt < kC; ++tt) { acc += sG[tt * LK + ch]; sG[tt * LK + ch] = acc; }
     }
-    __syncthreads();
+    lds_barrier();
     float dq[CG], dk[CG], dG[CG], gt[CG], kt[CG], qt[CG];
     const float bt = beta[t];
 #pragma unroll
@@ -609,18 +776,18 @@ __global__ __launch_bounds__(kT) void bwd_grad_kernel(BwdArgs a) {
             }
         }
     }
-    __syncthreads();
+    lds_barrier();
     // dG into LDS over Q, dgamma's share on row 63, then the reverse cumsum per channel
 #pragma unroll
     for (int u = 0; u < CG; ++u) sQ[t * LK + c0 + u] = dG[u] + (t == kC - 1 ? dlgam[c0 + u] : 0.f);
-    __syncthreads();
-    for (int ch = tid; ch < DK; ch += kT) {
+    lds_barrier();
+    for (int ch = tid; ch < DK; ch += kTG) {
         float acc = 0.f;
         for (int tt = kC - 1; tt >= 0; --tt) { acc += sQ[tt * LK + ch]; sQ[tt * LK + ch] = acc; }
     }
-    __syncthreads();
-    dbeta += __shfl_xor(dbeta, 1);
-    dbeta += __shfl_xor(dbeta, 2);
+    lds_barrier();
+#pragma unroll
+    for (int m = 1; m < NGR; m <<= 1) dbeta += __shfl_xor(dbeta, m);
     if (t < nrows) {
         const int64_t r = row0 + t;
 #pragma unroll
@@ -629,7 +796,7 @@ __global__ __launch_bounds__(kT) void bwd_grad_kernel(BwdArgs a) {
             a.dk_[r * DK + c0 + u] = dk[u];
             a.dla[r * DK + c0 + u] = sQ[t * LK + c0 + u];
         }
-        if ((tid & 3) == 0) a.dbeta[r] = dbeta;
+        if (gi == 0) a.dbeta[r] = dbeta;
     }
 }
 
@@ -655,7 +822,7 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
     hipLaunchKernelGGL((bwd_state_kernel<DK, DV, TO>), dim3((unsigned)(a.lanes * (DV / 32))), dim3(kT), state_smem, st,
                        a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_grad_kernel<DK, DV, TO>), dim3((unsigned)chunks), dim3(kT), grad_smem, st, a);
+    hipLaunchKernelGGL((bwd_grad_kernel<DK, DV, TO>), dim3((unsigned)chunks), dim3(kTG), grad_smem, st, a);
     return hipGetLastError();
 }
 
