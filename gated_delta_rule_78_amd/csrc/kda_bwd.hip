@@ -279,50 +279,62 @@ __global__ __launch_bounds__(kT) void bwd_prep_kernel(BwdArgs a) {
     }
 }
 
-// Reverse state pass for value columns [j0, j0 + 32) of one lane. Per chunk the factors the pass
-// reads (K-, Q~, W, A_qk, gamma) and the lane's dO block are staged in LDS (rows padded by 4
-// floats against bank conflicts), and each thread computes a small register tile of dV~ and of the
-// new Gx from 16-byte LDS reads. The chunk before the current one is loaded into registers while
-// the current one computes; the barriers order LDS only, so that load stays in flight across them.
+// Reverse state pass for value columns [j0, j0 + 32) of one lane, on the fp32 matrix cores
+// (16x16x4 MFMA). Per chunk, walking backwards:
+//     dV~ = K- Gx + A_qk^T dO                     (64 x 32; wave w owns rows 16w .. 16w + 15)
+//     Gx  <- Diag(gamma) Gx + Q~^T dO - W^T dV~   (DK x 32; wave w owns rows DK/4 w ..)
+// Gx lives in the waves' accumulator registers for the whole pass. Every MFMA operand sits in LDS
+// with the contraction index contiguous (K- as is; Q~, W, A_qk, dO and dV~ transposed while
+// staged or stored), so a lane fetches its next four k values of an operand in one 16-byte read.
+// In a 16x16x4 step lane l = r + 16 g supplies row (or column) r at k = g; the k values a lane
+// walks through are assigned as kb + 4 g + q for step q of a block of 16, the same on both sides.
+// The chunk before the current one is loaded into registers while the current one computes; the
+// barriers order LDS only, so that load stays in flight across them.
 template <int DK, int DV>
 struct __align__(16) StateSmem {
-    static constexpr int LK = DK + 4, LB = 32 + 4, LA = kC + 4;
-    float KB[kC][LK], QT[kC][LK], W[kC][LK];
-    float AQK[kC][LA];
-    float dO[kC][LB], X[kC][LB];
-    float Gx[DK][LB];
+    static constexpr int NB = 32, LK = DK + 4, LS = kC + 4;
+    float KB[kC][LK];     // K- [t][ch]
+    float QTT[DK][LS];    // Q~^T [ch][s]
+    float WTN[DK][LS];    // -W^T [ch][s]
+    float AQT[kC][LS];    // A_qk^T [t][s]
+    float dOT[NB][LS];    // dO^T [j][s]
+    float dVT[NB][LS];    // dV~^T [j][s]
+    float GxT[NB][LK];    // Gx^T [j][ch]
     float gam[DK];
 };
 
 // one thread's share of a chunk's state-pass operands, held in registers between the global load
-// and the LDS store (kT threads; element e of a block goes to thread e mod kT)
+// and the LDS store. A [64][n] factor is read in blocks of 16 rows x 16 columns, one block per
+// wave and instruction: lane l takes row 16 (b mod 4) + (l mod 16) and the four columns from
+// 16 (b / 4) + 4 (l / 16), so the transposed LDS stores of a half-wave fall in distinct banks.
 template <int DK, typename TO>
 struct StateFetch {
     static constexpr int NB = 32;
     static constexpr int NF = kC * DK / 4 / kT;   // float4s of one [64][DK] factor
     static constexpr int NA = kC * kC / 4 / kT;   // float4s of A_qk
     static constexpr int ND = kC * NB / kT;       // dO elements
+    static_assert(kT == 256, "four waves");
     f32x4 kb[NF], qt[NF], w[NF], aqk[NA];
     f32x4 gam;
     TO dO[ND];     // raw, converted when stored to LDS
     int nrows;
 
+    static __device__ __forceinline__ int blk_row(int u) { return 16 * (((threadIdx.x >> 6) + 4 * u) & 3) + (threadIdx.x & 15); }
+    static __device__ __forceinline__ int blk_col(int u) { return 16 * (((threadIdx.x >> 6) + 4 * u) >> 2) + 4 * ((threadIdx.x >> 4) & 3); }
+
     template <typename L>
     __device__ __forceinline__ void load(const float* sc, const TO* dO_, int64_t orow, int nrows, int j0, int dv) {
-        constexpr int Q = DK / 4;
         this->nrows = nrows;
 #pragma unroll
         for (int u = 0; u < NF; ++u) {
-            const int e = threadIdx.x + u * kT, r = e / Q, c = (e % Q) * 4;
-            kb[u] = *reinterpret_cast<const f32x4*>(sc + L::KB + r * DK + c);
-            qt[u] = *reinterpret_cast<const f32x4*>(sc + L::QT + r * DK + c);
-            w[u] = *reinterpret_cast<const f32x4*>(sc + L::W + r * DK + c);
+            const int off = blk_row(u) * DK + blk_col(u);
+            kb[u] = *reinterpret_cast<const f32x4*>(sc + L::KB + off);
+            qt[u] = *reinterpret_cast<const f32x4*>(sc + L::QT + off);
+            w[u] = *reinterpret_cast<const f32x4*>(sc + L::W + off);
         }
 #pragma unroll
-        for (int u = 0; u < NA; ++u) {
-            const int e = threadIdx.x + u * kT;
-            aqk[u] = *reinterpret_cast<const f32x4*>(sc + L::AQK + e * 4);
-        }
+        for (int u = 0; u < NA; ++u)
+            aqk[u] = *reinterpret_cast<const f32x4*>(sc + L::AQK + blk_row(u) * kC + blk_col(u));
         if ((int)threadIdx.x < DK / 4) gam = *reinterpret_cast<const f32x4*>(sc + L::GAM + threadIdx.x * 4);
 #pragma unroll
         for (int u = 0; u < ND; ++u) {
@@ -332,7 +344,37 @@ struct StateFetch {
             dO[u] = dO_[(orow + tr) * dv + j0 + j];
         }
     }
+
+    template <typename SS>
+    __device__ __forceinline__ void store(SS& sm) const {
+#pragma unroll
+        for (int u = 0; u < NF; ++u) {
+            const int r = blk_row(u), c = blk_col(u);
+            *reinterpret_cast<f32x4*>(&sm.KB[r][c]) = kb[u];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                sm.QTT[c + i][r] = qt[u][i];
+                sm.WTN[c + i][r] = -w[u][i];
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < NA; ++u) {
+            const int r = blk_row(u), c = blk_col(u);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sm.AQT[c + i][r] = aqk[u][i];
+        }
+        if ((int)threadIdx.x < DK / 4) *reinterpret_cast<f32x4*>(&sm.gam[threadIdx.x * 4]) = gam;
+#pragma unroll
+        for (int u = 0; u < ND; ++u) {
+            const int e = threadIdx.x + u * kT;
+            sm.dOT[e % NB][e / NB] = e / NB < nrows ? ldo(&dO[u], 0) : 0.f;
+        }
+    }
 };
+
+__device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
 
 template <int DK, int DV, typename TO>
 __global__ __launch_bounds__(kT) void bwd_state_kernel(BwdArgs a) {
@@ -340,7 +382,8 @@ __global__ __launch_bounds__(kT) void bwd_state_kernel(BwdArgs a) {
     typedef StateSmem<DK, DV> SS;
     typedef StateFetch<DK, TO> F;
     constexpr int NB = F::NB;
-    static_assert(DV % NB == 0 && (kC * DK / 4) % kT == 0 && (kC * kC / 4) % kT == 0, "state tiles");
+    constexpr int RT = DK / 64;   // 16-row tiles of Gx per wave
+    static_assert(DV % NB == 0 && DK % 64 == 0 && (kC * DK / 4) % kT == 0 && (kC * kC / 4) % kT == 0, "state tiles");
     extern __shared__ __align__(16) unsigned char smem_raw[];
     SS& sm = *reinterpret_cast<SS*>(smem_raw);
     const int nblk = DV / NB;
@@ -357,98 +400,120 @@ __global__ __launch_bounds__(kT) void bwd_state_kernel(BwdArgs a) {
     }
     const int j0 = (int)cb * NB;
     const TO* dO = (const TO*)a.dO;
-    for (int e = threadIdx.x; e < DK * NB; e += kT) {
-        const int ch = e / NB, j = e % NB;
-        sm.Gx[ch][j] = a.dST ? a.dST[(lane * DK + ch) * DV + j0 + j] : 0.f;
-    }
+    const int wv = threadIdx.x >> 6, lr = threadIdx.x & 15, lg = (threadIdx.x >> 4) & 3;
+    // Gx accumulators: gx[rt][ct][i] = Gx[gr0 + 16 rt + 4 lg + i][16 ct + lr]
+    const int gr0 = wv * (DK / 4);
+    f32x4 gx[RT][2];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int ch = gr0 + 16 * rt + 4 * lg + i, j = 16 * ct + lr;
+                gx[rt][ct][i] = a.dST ? a.dST[(lane * DK + ch) * DV + j0 + j] : 0.f;
+            }
+    auto put_gxt = [&]() {
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct)
+                *reinterpret_cast<f32x4*>(&sm.GxT[16 * ct + lr][gr0 + 16 * rt + 4 * lg]) = gx[rt][ct];
+    };
+    put_gxt();
     auto chunk_rows = [&](int64_t c) { return (int)(a.T - c * kC < kC ? a.T - c * kC : kC); };
     F f;
     {
         const int64_t c = a.nchunks - 1;
         f.template load<L>(a.prep + (lane * a.nchunks + c) * L::PREP, dO, lane * a.T + c * kC, chunk_rows(c), j0, DV);
     }
-    // thread tiles: dV~ rows 2xr .. 2xr+1, columns 4xc .. 4xc+3; Gx rows 4gr .. 4gr+3, same columns
-    const int xc = (threadIdx.x & 7) * 4;
-    const int xr = (threadIdx.x >> 3) * 2;
-    const int gr = (threadIdx.x >> 3) * (DK / 32);
     for (int64_t c = a.nchunks - 1; c >= 0; --c) {
         float* gst = a.gst + (lane * a.nchunks + c) * (int64_t)(DK * DV);
         float* dvt = a.dvt + (lane * a.nchunks + c) * (int64_t)(kC * DV);
-        lds_barrier();   // the previous chunk is done with every staged array; its Gx is in place
-        {
-            constexpr int Q = DK / 4;
+        lds_barrier();   // the previous chunk is done with every staged array; its Gx^T is in place
+        f.store(sm);
+        // the state gradient entering this chunk (from its end), for the gradient kernel
 #pragma unroll
-            for (int u = 0; u < F::NF; ++u) {
-                const int e = threadIdx.x + u * kT, r = e / Q, cc = (e % Q) * 4;
-                *reinterpret_cast<f32x4*>(&sm.KB[r][cc]) = f.kb[u];
-                *reinterpret_cast<f32x4*>(&sm.QT[r][cc]) = f.qt[u];
-                *reinterpret_cast<f32x4*>(&sm.W[r][cc]) = f.w[u];
-            }
+        for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-            for (int u = 0; u < F::NA; ++u) {
-                const int e = threadIdx.x + u * kT, r = (e * 4) / kC, cc = (e * 4) % kC;
-                *reinterpret_cast<f32x4*>(&sm.AQK[r][cc]) = f.aqk[u];
-            }
-            if ((int)threadIdx.x < DK / 4) *reinterpret_cast<f32x4*>(&sm.gam[threadIdx.x * 4]) = f.gam;
+            for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
-            for (int u = 0; u < F::ND; ++u) {
-                const int e = threadIdx.x + u * kT;
-                sm.dO[e / NB][e % NB] = e / NB < f.nrows ? ldo(&f.dO[u], 0) : 0.f;
-            }
-        }
-        for (int e = threadIdx.x; e < DK * NB; e += kT) {
-            const int ch = e / NB, j = e % NB;
-            gst[ch * DV + j0 + j] = sm.Gx[ch][j];
-        }
+                for (int i = 0; i < 4; ++i)
+                    gst[(gr0 + 16 * rt + 4 * lg + i) * DV + j0 + 16 * ct + lr] = gx[rt][ct][i];
         if (c > 0)   // the next chunk's operands travel while this one computes
             f.template load<L>(a.prep + (lane * a.nchunks + c - 1) * L::PREP, dO, lane * a.T + (c - 1) * kC,
                                chunk_rows(c - 1), j0, DV);
         lds_barrier();
-        // dV~ = K- Gx + A_qk^T dO
+        // dV~ rows 16 wv .. 16 wv + 15 = K- Gx + A_qk^T dO (A_qk^T[t][s] = 0 for s < t)
         {
-            f32x4 x0 = kZero4f(), x1 = kZero4f();
-            for (int ch = 0; ch < DK; ch += 4) {
-                const f32x4 k0 = *reinterpret_cast<const f32x4*>(&sm.KB[xr][ch]);
-                const f32x4 k1 = *reinterpret_cast<const f32x4*>(&sm.KB[xr + 1][ch]);
+            f32x4 dv[2] = {kZero4f(), kZero4f()};
+            const int t0 = 16 * wv;
+            for (int kb = 0; kb < DK; kb += 16) {
+                const f32x4 x = *reinterpret_cast<const f32x4*>(&sm.KB[t0 + lr][kb + 4 * lg]);
+                const f32x4 y0 = *reinterpret_cast<const f32x4*>(&sm.GxT[lr][kb + 4 * lg]);
+                const f32x4 y1 = *reinterpret_cast<const f32x4*>(&sm.GxT[16 + lr][kb + 4 * lg]);
 #pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const f32x4 g = *reinterpret_cast<const f32x4*>(&sm.Gx[ch + u][xc]);
-                    x0 += k0[u] * g;
-                    x1 += k1[u] * g;
+                for (int q = 0; q < 4; ++q) {
+                    dv[0] = mfma4(x[q], y0[q], dv[0]);
+                    dv[1] = mfma4(x[q], y1[q], dv[1]);
                 }
             }
-            for (int i = xr; i < kC; ++i) {
-                const f32x4 d = *reinterpret_cast<const f32x4*>(&sm.dO[i][xc]);
-                x0 += sm.AQK[i][xr] * d;
-                if (i > xr) x1 += sm.AQK[i][xr + 1] * d;
+            for (int kb = t0; kb < kC; kb += 16) {
+                const f32x4 x = *reinterpret_cast<const f32x4*>(&sm.AQT[t0 + lr][kb + 4 * lg]);
+                const f32x4 y0 = *reinterpret_cast<const f32x4*>(&sm.dOT[lr][kb + 4 * lg]);
+                const f32x4 y1 = *reinterpret_cast<const f32x4*>(&sm.dOT[16 + lr][kb + 4 * lg]);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    dv[0] = mfma4(x[q], y0[q], dv[0]);
+                    dv[1] = mfma4(x[q], y1[q], dv[1]);
+                }
             }
-            *reinterpret_cast<f32x4*>(&sm.X[xr][xc]) = x0;
-            *reinterpret_cast<f32x4*>(&sm.X[xr + 1][xc]) = x1;
-            *reinterpret_cast<f32x4*>(dvt + xr * DV + j0 + xc) = x0;
-            *reinterpret_cast<f32x4*>(dvt + (xr + 1) * DV + j0 + xc) = x1;
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct) {
+                *reinterpret_cast<f32x4*>(&sm.dVT[16 * ct + lr][t0 + 4 * lg]) = dv[ct];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) dvt[(t0 + 4 * lg + i) * DV + j0 + 16 * ct + lr] = dv[ct][i];
+            }
         }
         lds_barrier();
         // Gx <- Diag(gamma) Gx + Q~^T dO - W^T dV~
-        f32x4 gn[DK / 32];
 #pragma unroll
-        for (int r = 0; r < DK / 32; ++r)
-            gn[r] = sm.gam[gr + r] * *reinterpret_cast<const f32x4*>(&sm.Gx[gr + r][xc]);
-        for (int t = 0; t < kC; ++t) {
-            const f32x4 d = *reinterpret_cast<const f32x4*>(&sm.dO[t][xc]);
-            const f32x4 x = *reinterpret_cast<const f32x4*>(&sm.X[t][xc]);
-#pragma unroll
-            for (int r = 0; r < DK / 32; ++r) gn[r] += sm.QT[t][gr + r] * d - sm.W[t][gr + r] * x;
+        for (int rt = 0; rt < RT; ++rt) {
+            const f32x4 g4 = *reinterpret_cast<const f32x4*>(&sm.gam[gr0 + 16 * rt + 4 * lg]);
+            gx[rt][0] *= g4;
+            gx[rt][1] *= g4;
         }
-        lds_barrier();
+        for (int kb = 0; kb < kC; kb += 16) {
+            f32x4 xq[RT], xw[RT];
 #pragma unroll
-        for (int r = 0; r < DK / 32; ++r) *reinterpret_cast<f32x4*>(&sm.Gx[gr + r][xc]) = gn[r];
+            for (int rt = 0; rt < RT; ++rt) {
+                xq[rt] = *reinterpret_cast<const f32x4*>(&sm.QTT[gr0 + 16 * rt + lr][kb + 4 * lg]);
+                xw[rt] = *reinterpret_cast<const f32x4*>(&sm.WTN[gr0 + 16 * rt + lr][kb + 4 * lg]);
+            }
+            const f32x4 o0 = *reinterpret_cast<const f32x4*>(&sm.dOT[lr][kb + 4 * lg]);
+            const f32x4 o1 = *reinterpret_cast<const f32x4*>(&sm.dOT[16 + lr][kb + 4 * lg]);
+            const f32x4 v0 = *reinterpret_cast<const f32x4*>(&sm.dVT[lr][kb + 4 * lg]);
+            const f32x4 v1 = *reinterpret_cast<const f32x4*>(&sm.dVT[16 + lr][kb + 4 * lg]);
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt) {
+                    gx[rt][0] = mfma4(xq[rt][q], o0[q], gx[rt][0]);
+                    gx[rt][1] = mfma4(xq[rt][q], o1[q], gx[rt][1]);
+                    gx[rt][0] = mfma4(xw[rt][q], v0[q], gx[rt][0]);
+                    gx[rt][1] = mfma4(xw[rt][q], v1[q], gx[rt][1]);
+                }
+        }
+        put_gxt();   // nothing reads Gx^T between the dV~ products above and the next chunk's
     }
-    lds_barrier();
     if (a.dS0)
-        for (int e = threadIdx.x; e < DK * NB; e += kT) {
-            const int ch = e / NB, j = e % NB;
-            a.dS0[(lane * DK + ch) * DV + j0 + j] = sm.Gx[ch][j];
-        }
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    a.dS0[(lane * DK + gr0 + 16 * rt + 4 * lg + i) * DV + j0 + 16 * ct + lr] = gx[rt][ct][i];
 }
 
 // Gradient kernel LDS arena, reused by phase (offsets in floats; rows padded by 4 floats):
