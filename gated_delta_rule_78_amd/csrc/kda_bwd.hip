@@ -572,12 +572,21 @@ __global__ __launch_bounds__(kTG) void bwd_grad_kernel(BwdArgs a) {
     if (tid < kC) beta[tid] = tid < nrows ? ldin((const bf16_t*)a.beta, row0 + tid) : 0.f;
 
     // ---------------- phase 1: V~ = U - W S, and the products over the value columns ----------
-    float accQ[CG], accK[CG], accW[CG], aqk[JG];
+    // fp32 16x16x4 MFMA tiles (lane l = lr + 16 lg supplies row / column lr at k = lg; the k
+    // values of a block of 16 are kb + 4 lg + q at step q, on both operands). Wave w owns rows
+    // t0 = 16 (w mod 4) of every product and a quarter of the columns given by w / 4:
+    //   V~_h     cols vb + 16 ct (NVT tiles)    dQ~, dW, dK- cols cm + 16 ct (NCT tiles)
+    //   dA_qk    cols sb + 16 ct (2 tiles)
+    // An accumulator tile holds rows t0 + 4 lg + i, i = 0..3, of column lr.
+    constexpr int NCT = DK / 32, NVT = NH / 32;
+    const int wv = tid >> 6, lr = tid & 15, lg = (tid >> 4) & 3;
+    const int t0 = 16 * (wv & 3), vb = (NH / 2) * (wv >> 2), cm = (DK / 2) * (wv >> 2), sb = 32 * (wv >> 2);
+    f32x4 mq[NCT], mw[NCT], mk[NCT], mqk[2];
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) { mq[ct] = kZero4f(); mw[ct] = kZero4f(); mk[ct] = kZero4f(); }
+    mqk[0] = kZero4f();
+    mqk[1] = kZero4f();
     float dgam = 0.f;
-#pragma unroll
-    for (int u = 0; u < CG; ++u) { accQ[u] = 0.f; accK[u] = 0.f; accW[u] = 0.f; }
-#pragma unroll
-    for (int u = 0; u < JG; ++u) aqk[u] = 0.f;
     float* sS = ar + A::P1_S;
     float* sGx = ar + A::P1_GX;
     float* sW = ar + A::P1_W;
@@ -592,13 +601,13 @@ __global__ __launch_bounds__(kTG) void bwd_grad_kernel(BwdArgs a) {
     F32Tile<kC, kC, kTG> tT;
     F32Tile<kC, DV, kTG> tdv2;
     const float* Ssrc = S ? S : Gx;   // a stand-in of the same shape when there is no entry state
-    // V~_h tiles: VR rows x 4 columns per thread (NH / 4 column groups); U is their starting value
-    constexpr int NCG = NH / 4, VR = kC * NCG / kTG;
-    const int vr = (tid / NCG) * VR, vc = (tid % NCG) * 4;
-    f32x4 uin[VR];
+    // U_h in the V~_h tile layout (V~ = U - W S), loaded with the half's tiles
+    f32x4 uin[NVT];
     auto load_uin = [&](int jh) {
 #pragma unroll
-        for (int r = 0; r < VR; ++r) uin[r] = *reinterpret_cast<const f32x4*>(sc + L::U + (vr + r) * DV + jh + vc);
+        for (int ct = 0; ct < NVT; ++ct)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) uin[ct][i] = sc[L::U + (t0 + 4 * lg + i) * DV + jh + vb + 16 * ct + lr];
     };
     tw.load(sc + L::W, DK);
     ts.load(Ssrc, DV);
@@ -615,9 +624,10 @@ __global__ __launch_bounds__(kTG) void bwd_grad_kernel(BwdArgs a) {
         tgx.store(sGx, LH);
         tdv.store(sdVt, LH);
         tdo.store(sdO, LH);
-        f32x4 acc[VR];
+        f32x4 acc[NVT];
 #pragma unroll
-        for (int r = 0; r < VR; ++r) acc[r] = uin[r];
+        for (int ct = 0; ct < NVT; ++ct) acc[ct] = kZero4f();
+        const f32x4 u0 = uin[0], u1 = uin[NVT - 1];
         lds_barrier();
         if constexpr (h == 0) {
             ts.load(Ssrc + NH, DV);
@@ -629,21 +639,22 @@ __global__ __launch_bounds__(kTG) void bwd_grad_kernel(BwdArgs a) {
             tT.load(sc + L::T, kC);
             tdv2.load(dVt, DV);
         }
-        {   // V~_h: thread tile of VR rows x 4 columns, starting from U
+        {   // W S_h for rows t0 .., columns vb + 16 ct; S_h's column is strided in LDS (4 reads)
 #pragma unroll 2
-            for (int ch = 0; ch < DK; ch += 4) {
-                f32x4 s4[4];
+            for (int kb = 0; kb < DK; kb += 16) {
+                const f32x4 x = *reinterpret_cast<const f32x4*>(sW + (t0 + lr) * LK + kb + 4 * lg);
 #pragma unroll
-                for (int u = 0; u < 4; ++u) s4[u] = *reinterpret_cast<const f32x4*>(sS + (ch + u) * LH + vc);
+                for (int q = 0; q < 4; ++q)
 #pragma unroll
-                for (int r = 0; r < VR; ++r) {
-                    const f32x4 w4 = *reinterpret_cast<const f32x4*>(sW + (vr + r) * LK + ch);
-#pragma unroll
-                    for (int u = 0; u < 4; ++u) acc[r] -= w4[u] * s4[u];
-                }
+                    for (int ct = 0; ct < NVT; ++ct)
+                        acc[ct] = mfma4(x[q], sS[(kb + 4 * lg + q) * LH + vb + 16 * ct + lr], acc[ct]);
             }
 #pragma unroll
-            for (int r = 0; r < VR; ++r) *reinterpret_cast<f32x4*>(sVt + (vr + r) * LH + vc) = acc[r];
+            for (int ct = 0; ct < NVT; ++ct) {
+                const f32x4 uu = ct == 0 ? u0 : u1;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) sVt[(t0 + 4 * lg + i) * LH + vb + 16 * ct + lr] = uu[i] - acc[ct][i];
+            }
         }
         if (tid < DK) {
             float sacc = 0.f;
@@ -652,32 +663,30 @@ __global__ __launch_bounds__(kTG) void bwd_grad_kernel(BwdArgs a) {
             dgam += sacc;
         }
         lds_barrier();
-        // dQ~ += dO S^T, dW -= dV~ S^T, dK- += V~ Gx^T (rows t, channels c0 ..)
+        // dQ~ += dO S^T, dW += dV~ S^T (negated when stored), dK- += V~ Gx^T, dA_qk += dO V~^T
 #pragma unroll 1
-        for (int j = 0; j < NH; j += 4) {
-            const f32x4 o4 = *reinterpret_cast<const f32x4*>(sdO + t * LH + j);
-            const f32x4 d4 = *reinterpret_cast<const f32x4*>(sdVt + t * LH + j);
-            const f32x4 v4 = *reinterpret_cast<const f32x4*>(sVt + t * LH + j);
+        for (int kb = 0; kb < NH; kb += 16) {
+            const f32x4 xo = *reinterpret_cast<const f32x4*>(sdO + (t0 + lr) * LH + kb + 4 * lg);
+            const f32x4 xd = *reinterpret_cast<const f32x4*>(sdVt + (t0 + lr) * LH + kb + 4 * lg);
+            const f32x4 xv = *reinterpret_cast<const f32x4*>(sVt + (t0 + lr) * LH + kb + 4 * lg);
+            f32x4 ys[NCT], yg[NCT], yv[2];
 #pragma unroll
-            for (int u = 0; u < CG; ++u) {
-                const f32x4 s4 = *reinterpret_cast<const f32x4*>(sS + (c0 + u) * LH + j);
-                const f32x4 g4 = *reinterpret_cast<const f32x4*>(sGx + (c0 + u) * LH + j);
-                accQ[u] += o4[0] * s4[0] + o4[1] * s4[1] + o4[2] * s4[2] + o4[3] * s4[3];
-                accW[u] -= d4[0] * s4[0] + d4[1] * s4[1] + d4[2] * s4[2] + d4[3] * s4[3];
-                accK[u] += v4[0] * g4[0] + v4[1] * g4[1] + v4[2] * g4[2] + v4[3] * g4[3];
+            for (int ct = 0; ct < NCT; ++ct) {
+                ys[ct] = *reinterpret_cast<const f32x4*>(sS + (cm + 16 * ct + lr) * LH + kb + 4 * lg);
+                yg[ct] = *reinterpret_cast<const f32x4*>(sGx + (cm + 16 * ct + lr) * LH + kb + 4 * lg);
             }
-        }
-        // dA_qk[t][JG g + u] += dO_t . V~_(JG g + u) over this half (lower triangle used later)
-        {
-            const int jg = gi * JG;
-#pragma unroll 1
-            for (int j = 0; j < NH; j += 4) {
-                const f32x4 o4 = *reinterpret_cast<const f32x4*>(sdO + t * LH + j);
 #pragma unroll
-                for (int u = 0; u < JG; ++u) {
-                    const f32x4 v4 = *reinterpret_cast<const f32x4*>(sVt + (jg + u) * LH + j);
-                    aqk[u] += o4[0] * v4[0] + o4[1] * v4[1] + o4[2] * v4[2] + o4[3] * v4[3];
+            for (int ct = 0; ct < 2; ++ct) yv[ct] = *reinterpret_cast<const f32x4*>(sVt + (sb + 16 * ct + lr) * LH + kb + 4 * lg);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+#pragma unroll
+                for (int ct = 0; ct < NCT; ++ct) {
+                    mq[ct] = mfma4(xo[q], ys[ct][q], mq[ct]);
+                    mw[ct] = mfma4(xd[q], ys[ct][q], mw[ct]);
+                    mk[ct] = mfma4(xv[q], yg[ct][q], mk[ct]);
                 }
+                mqk[0] = mfma4(xo[q], yv[0][q], mqk[0]);
+                mqk[1] = mfma4(xo[q], yv[1][q], mqk[1]);
             }
         }
         lds_barrier();
@@ -685,6 +694,29 @@ __global__ __launch_bounds__(kTG) void bwd_grad_kernel(BwdArgs a) {
     half(IntC<0>{});
     half(IntC<1>{});
     if (tid < DK) dlgam[tid] = sc[L::GAM + tid] * dgam;
+    // dQ~ and dK- go from the tile layout to the (row t, channels c0 ..) layout of phase 3
+    // through the free phase-1 space
+    float accQ[CG], accK[CG];
+    {
+        float* xq = ar;
+        float* xk = ar + kC * LK;
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                xq[(t0 + 4 * lg + i) * LK + cm + 16 * ct + lr] = mq[ct][i];
+                xk[(t0 + 4 * lg + i) * LK + cm + 16 * ct + lr] = mk[ct][i];
+            }
+        lds_barrier();
+#pragma unroll
+        for (int u = 0; u < CG; u += 4) {
+            const f32x4 q4 = *reinterpret_cast<const f32x4*>(xq + t * LK + c0 + u);
+            const f32x4 k4 = *reinterpret_cast<const f32x4*>(xk + t * LK + c0 + u);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) { accQ[u + e] = q4[e]; accK[u + e] = k4[e]; }
+        }
+        lds_barrier();
+    }
 
     // ---------------- phase 2: [dX_K | dX_V] = T^T [dW | dV~], then dA_kk ---------------------
     float* sAkk = ar + A::AKK;
@@ -694,7 +726,9 @@ __global__ __launch_bounds__(kTG) void bwd_grad_kernel(BwdArgs a) {
     tT.store(sT, LA);
     tdv2.store(sdV2, LV);
 #pragma unroll
-    for (int u = 0; u < CG; ++u) sdW[t * LK + c0 + u] = accW[u];
+    for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sdW[(t0 + 4 * lg + i) * LK + cm + 16 * ct + lr] = -mw[ct][i];
     lds_barrier();
     F32Tile<kC, DK, kTG> tw2;
     F32Tile<kC, DV, kTG> tu;
@@ -767,10 +801,14 @@ __global__ __launch_bounds__(kTG) void bwd_grad_kernel(BwdArgs a) {
         }
         lds_barrier();   // everyone has read dX / W / U before dA_qk and K, Q, G land on them
 #pragma unroll
-        for (int u = 0; u < JG; ++u) {
-            sAkk[i * LA + jg + u] = jg + u < i ? acc[u] : 0.f;
-            ar[A::AQK + i * LA + jg + u] = jg + u <= i ? aqk[u] : 0.f;
-        }
+        for (int u = 0; u < JG; ++u) sAkk[i * LA + jg + u] = jg + u < i ? acc[u] : 0.f;
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int r = t0 + 4 * lg + e, col = sb + 16 * ct + lr;
+                ar[A::AQK + r * LA + col] = col <= r ? mqk[ct][e] : 0.f;
+            }
     }
 
     // ---------------- phase 3: decay factors, pairwise terms, reverse cumsum -----------------
