@@ -94,6 +94,33 @@ struct F32Tile {   // fp32 block, 16-byte pieces
     }
 };
 
+// fp32 block stored transposed into LDS (dst[c][r] = src[r][c]). Each wave instruction covers 16
+// rows x 16 columns: lane l takes row 16 rb + (l mod 16) and the four columns from
+// 16 cb + 4 (l / 16), so with a destination row stride of 4 mod 32 floats the transposed stores of
+// a half-wave fall in distinct banks.
+template <int ROWS, int COLS, int NT>
+struct F32TileT {
+    static constexpr int RB = ROWS / 16, NBLK = RB * (COLS / 16), NW = NT / 64, PER = NBLK / NW;
+    static_assert(ROWS % 16 == 0 && COLS % 16 == 0 && NBLK % NW == 0, "transposed tile");
+    f32x4 r[PER];
+    static __device__ __forceinline__ int row(int u) {
+        return 16 * (((int)(threadIdx.x >> 6) + NW * u) % RB) + (threadIdx.x & 15);
+    }
+    static __device__ __forceinline__ int col(int u) {
+        return 16 * (((int)(threadIdx.x >> 6) + NW * u) / RB) + 4 * ((threadIdx.x >> 4) & 3);
+    }
+    __device__ __forceinline__ void load(const float* src, int64_t ld) {
+#pragma unroll
+        for (int u = 0; u < PER; ++u) r[u] = *reinterpret_cast<const f32x4*>(src + row(u) * ld + col(u));
+    }
+    __device__ __forceinline__ void store_t(float* dst, int ld) const {
+#pragma unroll
+        for (int u = 0; u < PER; ++u)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) dst[(col(u) + i) * ld + row(u)] = r[u][i];
+    }
+};
+
 // Rows [0, nrows) of a bf16 or fp32 row-major block as fp32, in pieces of 8 elements (16 bytes of
 // bf16, 32 of fp32). Rows past nrows read the last valid row (no branch, hence no wait at the
 // load) and are stored as zeros; an optional per-row factor scales what is stored.
@@ -519,7 +546,7 @@ __global__ __launch_bounds__(kT) void bwd_state_kernel(BwdArgs a) {
 // Gradient kernel LDS arena, reused by phase (offsets in floats; rows padded by 4 floats):
 //   phase 1 (twice, one half of the value columns each): S_h, Gx_h [DK][NH+4], W [64][DK+4],
 //           dO_h, dV~_h, V~_h [64][NH+4]
-//   phase 2: dA_kk [64][68] at 0 (kept), then T [64][68], dW [64][DK+4], dV~ [64][DV+4] for
+//   phase 2: dA_kk [64][68] at 0 (kept), then T^T [64][68], dW^T [DK][68], dV~^T [DV][68] for
 //           dX = T^T [dW | dV~], then dX_K [64][DK+4], dX_V [64][DV+4], W, U for dA_kk
 //   phase 3: dA_kk, dA_qk [64][68], K, Q, G [64][DK+4] for the pairwise terms; then dG over Q
 template <int DK, int DV>
@@ -529,15 +556,15 @@ struct GradArena {
     static constexpr int P1_S = 0, P1_GX = P1_S + DK * LH, P1_W = P1_GX + DK * LH, P1_DO = P1_W + kC * LK,
                          P1_DVT = P1_DO + kC * LH, P1_VT = P1_DVT + kC * LH, P1_END = P1_VT + kC * LH;
     // phase 2 / 3
-    static constexpr int AKK = 0, P2_T = AKK + kC * LA, P2_DW = P2_T + kC * LA, P2_DVT = P2_DW + kC * LK,
-                         P2A_END = P2_DVT + kC * LV;
+    static constexpr int AKK = 0, P2_T = AKK + kC * LA, P2_DW = P2_T + kC * LA, P2_DVT = P2_DW + DK * LA,
+                         P2A_END = P2_DVT + DV * LA;
     static constexpr int P2_XK = AKK + kC * LA, P2_XV = P2_XK + kC * LK, P2_W = P2_XV + kC * LV,
                          P2_U = P2_W + kC * LK, P2B_END = P2_U + kC * LV;
     static constexpr int AQK = AKK + kC * LA, P3_K = AQK + kC * LA, P3_Q = P3_K + kC * LK, P3_G = P3_Q + kC * LK,
                          P3_END = P3_G + kC * LK;
     static constexpr int SMALL = (P1_END > P2B_END ? (P1_END > P3_END ? P1_END : P3_END)
                                                    : (P2B_END > P3_END ? P2B_END : P3_END));
-    static constexpr int BETA = SMALL, DLGAM = BETA + kC, TOTAL = DLGAM + DK;
+    static constexpr int BETA = SMALL, DLGAM = BETA + kC, DB = DLGAM + DK, TOTAL = DB + kC;
     static_assert(P2A_END <= TOTAL && TOTAL * 4 <= 160 * 1024, "arena fits the LDS of a CU");
 };
 
@@ -554,6 +581,7 @@ __global__ __launch_bounds__(kTG) void bwd_grad_kernel(BwdArgs a) {
     float* ar = reinterpret_cast<float*>(smem_raw);
     float* beta = ar + A::BETA;
     float* dlgam = ar + A::DLGAM;     // gamma dgamma + sum_t dK-_t K-_t (joins row 63 of dG)
+    float* sdb = ar + A::DB;          // dX_V . V per row (joins dbeta)
     const int64_t lane = blockIdx.x / a.nchunks, c = blockIdx.x % a.nchunks;
     const int64_t row0 = lane * a.T + c * kC;
     const int nrows = (int)(a.T - c * kC < kC ? a.T - c * kC : kC);
@@ -598,8 +626,8 @@ __global__ __launch_bounds__(kTG) void bwd_grad_kernel(BwdArgs a) {
     F32Tile<DK, NH, kTG> ts, tgx;
     F32Tile<kC, NH, kTG> tdv;
     InTile<kC, NH, kTG, TO> tdo;
-    F32Tile<kC, kC, kTG> tT;
-    F32Tile<kC, DV, kTG> tdv2;
+    F32TileT<kC, kC, kTG> tT;
+    F32TileT<kC, DV, kTG> tdv2;
     const float* Ssrc = S ? S : Gx;   // a stand-in of the same shape when there is no entry state
     // U_h in the V~_h tile layout (V~ = U - W S), loaded with the half's tiles
     f32x4 uin[NVT];
@@ -719,58 +747,76 @@ __global__ __launch_bounds__(kTG) void bwd_grad_kernel(BwdArgs a) {
     }
 
     // ---------------- phase 2: [dX_K | dX_V] = T^T [dW | dV~], then dA_kk ---------------------
+    // MFMA tiles as in phase 1, every operand k-contiguous in LDS: T^T [t][m], dW^T [ch][m] and
+    // dV~^T [j][m] for dX; dX_K [i][ch], dX_V [i][jj], W [j][ch], U [j][jj] for dA_kk
+    constexpr int NXV = DV / 32;   // dX_V column tiles per wave
+    const int xb = (DV / 2) * (wv >> 2);
     float* sAkk = ar + A::AKK;
-    float* sT = ar + A::P2_T;
-    float* sdW = ar + A::P2_DW;
-    float* sdV2 = ar + A::P2_DVT;
-    tT.store(sT, LA);
-    tdv2.store(sdV2, LV);
+    float* sTT = ar + A::P2_T;
+    float* sdWT = ar + A::P2_DW;
+    float* sdVT = ar + A::P2_DVT;
+    tT.store_t(sTT, LA);
+    tdv2.store_t(sdVT, LA);
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sdW[(t0 + 4 * lg + i) * LK + cm + 16 * ct + lr] = -mw[ct][i];
+    for (int ct = 0; ct < NCT; ++ct) *reinterpret_cast<f32x4*>(sdWT + (cm + 16 * ct + lr) * LA + t0 + 4 * lg) = -mw[ct];
+    if (tid < kC) sdb[tid] = 0.f;
     lds_barrier();
     F32Tile<kC, DK, kTG> tw2;
     F32Tile<kC, DV, kTG> tu;
     tw2.load(sc + L::W, DK);
     tu.load(sc + L::U, DV);
-    float xk[CG], xv[VG];
+    f32x4 mxk[NCT], mxv[NXV];
 #pragma unroll
-    for (int u = 0; u < CG; ++u) xk[u] = 0.f;
+    for (int ct = 0; ct < NCT; ++ct) mxk[ct] = kZero4f();
 #pragma unroll
-    for (int u = 0; u < VG; ++u) xv[u] = 0.f;
-    for (int m = t; m < kC; ++m) {
-        const float tm = sT[m * LA + t];
+    for (int ct = 0; ct < NXV; ++ct) mxv[ct] = kZero4f();
+    for (int kb = t0; kb < kC; kb += 16) {   // T^T[t][m] = 0 for m < t
+        const f32x4 x = *reinterpret_cast<const f32x4*>(sTT + (t0 + lr) * LA + kb + 4 * lg);
+        f32x4 yw[NCT], yv[NXV];
 #pragma unroll
-        for (int u = 0; u < CG; u += 4) {
-            const f32x4 w4 = *reinterpret_cast<const f32x4*>(sdW + m * LK + c0 + u);
-            xk[u] += tm * w4[0]; xk[u + 1] += tm * w4[1]; xk[u + 2] += tm * w4[2]; xk[u + 3] += tm * w4[3];
-        }
+        for (int ct = 0; ct < NCT; ++ct) yw[ct] = *reinterpret_cast<const f32x4*>(sdWT + (cm + 16 * ct + lr) * LA + kb + 4 * lg);
 #pragma unroll
-        for (int u = 0; u < VG; u += 4) {
-            const f32x4 v4 = *reinterpret_cast<const f32x4*>(sdV2 + m * LV + j0 + u);
-            xv[u] += tm * v4[0]; xv[u + 1] += tm * v4[1]; xv[u + 2] += tm * v4[2]; xv[u + 3] += tm * v4[3];
-        }
-    }
-    // dv = beta dX_V; dbeta gets dX_V . V
-    float dbeta = 0.f;
-    if (t < nrows) {
-        const int64_t r = row0 + t;
+        for (int ct = 0; ct < NXV; ++ct) yv[ct] = *reinterpret_cast<const f32x4*>(sdVT + (xb + 16 * ct + lr) * LA + kb + 4 * lg);
 #pragma unroll
-        for (int u = 0; u < VG; ++u) {
-            a.dv_[r * DV + j0 + u] = beta[t] * xv[u];
-            dbeta += xv[u] * ldin((const bf16_t*)a.v, r * DV + j0 + u);
+        for (int q = 0; q < 4; ++q) {
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) mxk[ct] = mfma4(x[q], yw[ct][q], mxk[ct]);
+#pragma unroll
+            for (int ct = 0; ct < NXV; ++ct) mxv[ct] = mfma4(x[q], yv[ct][q], mxv[ct]);
         }
     }
-    lds_barrier();   // T, dW, dV~ are done; the dA_kk operands take their place
+    {   // dv = beta dX_V; dbeta gets dX_V . V (row sums over the 16 lanes of a tile, then LDS)
+        float pb[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ct = 0; ct < NXV; ++ct)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = t0 + 4 * lg + i, j = xb + 16 * ct + lr;
+                if (r < nrows) {
+                    a.dv_[(row0 + r) * DV + j] = beta[r] * mxv[ct][i];
+                    pb[i] += mxv[ct][i] * ldin((const bf16_t*)a.v, (row0 + r) * DV + j);
+                }
+            }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+#pragma unroll
+            for (int m = 1; m < 16; m <<= 1) pb[i] += __shfl_xor(pb[i], m);
+            if (lr == 0) atomicAdd(&sdb[t0 + 4 * lg + i], pb[i]);
+        }
+    }
+    lds_barrier();   // T^T, dW^T, dV~^T are done; the dA_kk operands take their place
     float* sXK = ar + A::P2_XK;
     float* sXV = ar + A::P2_XV;
     float* sW2 = ar + A::P2_W;
     float* sU = ar + A::P2_U;
 #pragma unroll
-    for (int u = 0; u < CG; ++u) sXK[t * LK + c0 + u] = xk[u];
+    for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-    for (int u = 0; u < VG; ++u) sXV[t * LV + j0 + u] = xv[u];
+        for (int i = 0; i < 4; ++i) sXK[(t0 + 4 * lg + i) * LK + cm + 16 * ct + lr] = mxk[ct][i];
+#pragma unroll
+    for (int ct = 0; ct < NXV; ++ct)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sXV[(t0 + 4 * lg + i) * LV + xb + 16 * ct + lr] = mxv[ct][i];
     tw2.store(sW2, LK);
     tu.store(sU, LV);
     lds_barrier();
@@ -778,35 +824,44 @@ __global__ __launch_bounds__(kTG) void bwd_grad_kernel(BwdArgs a) {
     tk.load((const bf16_t*)a.k + row0 * DK, DK, nrows);
     tq.load((const bf16_t*)a.q + row0 * DK, DK, nrows);
     tg.load((const bf16_t*)a.la + row0 * DK, DK, nrows);
-    {   // dA_kk[i][JG g + u] = -(dX_K,i . W_(JG g+u) + dX_V,i . U_(JG g+u)) for j < i
-        const int i = t, jg = gi * JG;
-        float acc[JG];
+    float xk[CG];   // dX_K in the (row t, channels c0 ..) layout of phase 3
 #pragma unroll
-        for (int u = 0; u < JG; ++u) acc[u] = 0.f;
-        for (int ch = 0; ch < DK; ch += 4) {
-            const f32x4 x4 = *reinterpret_cast<const f32x4*>(sXK + i * LK + ch);
+    for (int u = 0; u < CG; u += 4) {
+        const f32x4 x4 = *reinterpret_cast<const f32x4*>(sXK + t * LK + c0 + u);
 #pragma unroll
-            for (int u = 0; u < JG; ++u) {
-                const f32x4 w4 = *reinterpret_cast<const f32x4*>(sW2 + (jg + u) * LK + ch);
-                acc[u] -= x4[0] * w4[0] + x4[1] * w4[1] + x4[2] * w4[2] + x4[3] * w4[3];
+        for (int e = 0; e < 4; ++e) xk[u + e] = x4[e];
+    }
+    {   // dA_kk tiles (rows t0 .., columns sb + 16 ct) = -(dX_K W^T + dX_V U^T), kept for j < i
+        f32x4 akk[2] = {kZero4f(), kZero4f()};
+#pragma unroll 2
+        for (int kb = 0; kb < DK; kb += 16) {
+            const f32x4 x = *reinterpret_cast<const f32x4*>(sXK + (t0 + lr) * LK + kb + 4 * lg);
+            const f32x4 y0 = *reinterpret_cast<const f32x4*>(sW2 + (sb + lr) * LK + kb + 4 * lg);
+            const f32x4 y1 = *reinterpret_cast<const f32x4*>(sW2 + (sb + 16 + lr) * LK + kb + 4 * lg);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                akk[0] = mfma4(x[q], y0[q], akk[0]);
+                akk[1] = mfma4(x[q], y1[q], akk[1]);
             }
         }
-        for (int jj = 0; jj < DV; jj += 4) {
-            const f32x4 x4 = *reinterpret_cast<const f32x4*>(sXV + i * LV + jj);
+#pragma unroll 2
+        for (int kb = 0; kb < DV; kb += 16) {
+            const f32x4 x = *reinterpret_cast<const f32x4*>(sXV + (t0 + lr) * LV + kb + 4 * lg);
+            const f32x4 y0 = *reinterpret_cast<const f32x4*>(sU + (sb + lr) * LV + kb + 4 * lg);
+            const f32x4 y1 = *reinterpret_cast<const f32x4*>(sU + (sb + 16 + lr) * LV + kb + 4 * lg);
 #pragma unroll
-            for (int u = 0; u < JG; ++u) {
-                const f32x4 u4 = *reinterpret_cast<const f32x4*>(sU + (jg + u) * LV + jj);
-                acc[u] -= x4[0] * u4[0] + x4[1] * u4[1] + x4[2] * u4[2] + x4[3] * u4[3];
+            for (int q = 0; q < 4; ++q) {
+                akk[0] = mfma4(x[q], y0[q], akk[0]);
+                akk[1] = mfma4(x[q], y1[q], akk[1]);
             }
         }
         lds_barrier();   // everyone has read dX / W / U before dA_qk and K, Q, G land on them
-#pragma unroll
-        for (int u = 0; u < JG; ++u) sAkk[i * LA + jg + u] = jg + u < i ? acc[u] : 0.f;
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int r = t0 + 4 * lg + e, col = sb + 16 * ct + lr;
+                sAkk[r * LA + col] = col < r ? -akk[ct][e] : 0.f;
                 ar[A::AQK + r * LA + col] = col <= r ? mqk[ct][e] : 0.f;
             }
     }
@@ -826,6 +881,7 @@ __global__ __launch_bounds__(kTG) void bwd_grad_kernel(BwdArgs a) {
     }
     lds_barrier();
     float dq[CG], dk[CG], dG[CG], gt[CG], kt[CG], qt[CG];
+    float dbeta = 0.f;
     const float bt = beta[t];
 #pragma unroll
     for (int u = 0; u < CG; u += 4) {
@@ -899,7 +955,7 @@ __global__ __launch_bounds__(kTG) void bwd_grad_kernel(BwdArgs a) {
             a.dk_[r * DK + c0 + u] = dk[u];
             a.dla[r * DK + c0 + u] = sQ[t * LK + c0 + u];
         }
-        if (gi == 0) a.dbeta[r] = dbeta;
+        if (gi == 0) a.dbeta[r] = dbeta + sdb[t];
     }
 }
 
