@@ -31,6 +31,7 @@ namespace {
 constexpr int kC = 64;
 constexpr int kT = 256;   // threads per workgroup (prep, state pass)
 constexpr int kTG = 512;  // threads of the gradient kernel: two waves per SIMD on its LDS arena
+constexpr int kTP = 512;  // threads of the prep kernel, likewise
 
 // Per-chunk fp32 scratch written by the prep kernel (offsets in floats).
 template <int DK, int DV>
@@ -180,7 +181,7 @@ struct __align__(16) PrepSmem {
 };
 
 template <int DK, int DV>
-__global__ __launch_bounds__(kT) void bwd_prep_kernel(BwdArgs a) {
+__global__ __launch_bounds__(kTP) void bwd_prep_kernel(BwdArgs a) {
     typedef BwdLayout<DK, DV> L;
     extern __shared__ __align__(16) unsigned char smem_raw[];
     PrepSmem<DK, DV>& sm = *reinterpret_cast<PrepSmem<DK, DV>*>(smem_raw);
@@ -191,8 +192,8 @@ __global__ __launch_bounds__(kT) void bwd_prep_kernel(BwdArgs a) {
     const int tid = threadIdx.x;
     // K, Q, log_alpha and V of the chunk in one round trip; V stays in registers until its LDS
     // place is free
-    InTile<kC, DK, kT, bf16_t> tk, tq, tg;
-    InTile<kC, DV, kT, bf16_t> tv;
+    InTile<kC, DK, kTP, bf16_t> tk, tq, tg;
+    InTile<kC, DV, kTP, bf16_t> tv;
     tk.load((const bf16_t*)a.k + row0 * DK, DK, nrows);
     tq.load((const bf16_t*)a.q + row0 * DK, DK, nrows);
     tg.load((const bf16_t*)a.la + row0 * DK, DK, nrows);
@@ -205,25 +206,26 @@ __global__ __launch_bounds__(kT) void bwd_prep_kernel(BwdArgs a) {
     tq.store(&sm.Q[0][0], DK);
     tg.store(&sm.G[0][0], DK);
     lds_barrier();
-    for (int c = tid; c < DK; c += kT) {   // G = inclusive cumulative sum of log_alpha down the rows
+    for (int c = tid; c < DK; c += kTP) {   // G = inclusive cumulative sum of log_alpha down the rows
         float acc = 0.f;
         for (int t = 0; t < kC; ++t) { acc += sm.G[t][c]; sm.G[t][c] = acc; }
     }
     lds_barrier();
 
-    // A_kk (i > j, beta-scaled) and A_qk (i >= j): thread = (row i, columns 16 g .. 16 g + 15)
+    // A_kk (i > j, beta-scaled) and A_qk (i >= j): thread = (row i, columns JA g .. JA g + JA - 1)
     {
-        const int i = tid >> 2, jg = (tid & 3) * 16;
-        float akk[16], aqk[16];
+        constexpr int NG = kTP / kC, JA = kC / NG;
+        const int i = tid / NG, jg = (tid % NG) * JA;
+        float akk[JA], aqk[JA];
 #pragma unroll
-        for (int u = 0; u < 16; ++u) { akk[u] = 0.f; aqk[u] = 0.f; }
+        for (int u = 0; u < JA; ++u) { akk[u] = 0.f; aqk[u] = 0.f; }
         if (jg <= i) {
             for (int ch = 0; ch < DK; ch += 4) {
                 const f32x4 ki = *reinterpret_cast<const f32x4*>(&sm.K[i][ch]);
                 const f32x4 qi = *reinterpret_cast<const f32x4*>(&sm.Q[i][ch]);
                 const f32x4 gi = *reinterpret_cast<const f32x4*>(&sm.G[i][ch]);
 #pragma unroll
-                for (int u = 0; u < 16; ++u) {
+                for (int u = 0; u < JA; ++u) {
                     if (jg + u > i) break;
                     const f32x4 kj = *reinterpret_cast<const f32x4*>(&sm.K[jg + u][ch]);
                     const f32x4 gj = *reinterpret_cast<const f32x4*>(&sm.G[jg + u][ch]);
@@ -237,30 +239,16 @@ __global__ __launch_bounds__(kT) void bwd_prep_kernel(BwdArgs a) {
             }
         }
 #pragma unroll
-        for (int u = 0; u < 16; ++u) {
+        for (int u = 0; u < JA; ++u) {
             const int j = jg + u;
             sm.A[i][j] = j < i ? sm.beta[i] * akk[u] : 0.f;
             sc[L::AQK + i * kC + j] = j <= i ? aqk[u] : 0.f;
         }
     }
-    // Q~ = Q e^G, K- = K e^{G_63 - G}, gamma
-    for (int e = tid; e < kC * DK; e += kT) {
-        const int t = e / DK, ch = e % DK;
-        sc[L::QT + e] = sm.Q[t][ch] * fexp(sm.G[t][ch]);
-        sc[L::KB + e] = sm.K[t][ch] * fexp(sm.G[kC - 1][ch] - sm.G[t][ch]);
-    }
-    for (int ch = tid; ch < DK; ch += kT) sc[L::GAM + ch] = fexp(sm.G[kC - 1][ch]);
     lds_barrier();
-    // right-hand sides in place: K <- Diag(beta) K e^G, and Diag(beta) V over Q (or its own
-    // array when dv > dk), rows of DV floats
-    float* Vs = DV <= DK ? &sm.Q[0][0] : &sm.Vx[0][0];
-    for (int e = tid; e < kC * DK; e += kT) {
-        const int t = e / DK, ch = e % DK;
-        sm.K[t][ch] *= sm.beta[t] * fexp(sm.G[t][ch]);
-    }
-    tv.store(Vs, DV, sm.beta);
-    // T = (I + A)^{-1}, unit lower triangular: thread j keeps column j in registers, rows in order
     if (tid < kC) {
+        // wave 0: T = (I + A)^{-1}, unit lower triangular; thread j keeps column j in registers
+        // and walks the rows in order
         const int j = tid;
         float col[kC];
 #pragma unroll
@@ -272,13 +260,30 @@ __global__ __launch_bounds__(kT) void bwd_prep_kernel(BwdArgs a) {
         }
 #pragma unroll
         for (int i = 0; i < kC; ++i) sm.T[i][j] = col[i];
+    } else {
+        // the other waves meanwhile: Q~ = Q e^G, K- = K e^{G_63 - G}, gamma
+        for (int e = tid - kC; e < kC * DK; e += kTP - kC) {
+            const int t = e / DK, ch = e % DK;
+            sc[L::QT + e] = sm.Q[t][ch] * fexp(sm.G[t][ch]);
+            sc[L::KB + e] = sm.K[t][ch] * fexp(sm.G[kC - 1][ch] - sm.G[t][ch]);
+        }
+        for (int ch = tid - kC; ch < DK; ch += kTP - kC) sc[L::GAM + ch] = fexp(sm.G[kC - 1][ch]);
     }
     lds_barrier();
-    for (int e = tid; e < kC * kC; e += kT) sc[L::T + e] = sm.T[e / kC][e % kC];
+    // right-hand sides in place: K <- Diag(beta) K e^G, and Diag(beta) V over Q (or its own
+    // array when dv > dk), rows of DV floats
+    float* Vs = DV <= DK ? &sm.Q[0][0] : &sm.Vx[0][0];
+    for (int e = tid; e < kC * DK; e += kTP) {
+        const int t = e / DK, ch = e % DK;
+        sm.K[t][ch] *= sm.beta[t] * fexp(sm.G[t][ch]);
+    }
+    tv.store(Vs, DV, sm.beta);
+    for (int e = tid; e < kC * kC; e += kTP) sc[L::T + e] = sm.T[e / kC][e % kC];
+    lds_barrier();
     // W = T (beta K e^G), U = T (beta V): thread = (row t, channel / column group)
     {
-        constexpr int CG = DK / 4, VG = DV / 4;
-        const int t = tid >> 2, c0 = (tid & 3) * CG, j0 = (tid & 3) * VG;
+        constexpr int NG = kTP / kC, CG = DK / NG, VG = DV / NG;
+        const int t = tid / NG, c0 = (tid % NG) * CG, j0 = (tid % NG) * VG;
         float w[CG], u[VG];
 #pragma unroll
         for (int x = 0; x < CG; ++x) w[x] = 0.f;
@@ -976,7 +981,7 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
         e = hipFuncSetAttribute((const void*)bwd_grad_kernel<DK, DV, TO>, hipFuncAttributeMaxDynamicSharedMemorySize,
                                 (int)grad_smem);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_prep_kernel<DK, DV>), dim3((unsigned)chunks), dim3(kT), prep_smem, st, a);
+    hipLaunchKernelGGL((bwd_prep_kernel<DK, DV>), dim3((unsigned)chunks), dim3(kTP), prep_smem, st, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_state_kernel<DK, DV, TO>), dim3((unsigned)(a.lanes * (DV / 32))), dim3(kT), state_smem, st,
                        a);
