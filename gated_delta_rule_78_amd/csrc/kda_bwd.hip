@@ -58,14 +58,8 @@ __device__ __forceinline__ float ldo(const float* p, int64_t i) { return p[i]; }
 __device__ __forceinline__ float fexp(float x) { return __builtin_amdgcn_exp2f(x * kLog2e); }
 __device__ __forceinline__ f32x4 kZero4f() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
-// Workgroup barrier that orders LDS accesses only: outstanding global loads stay in flight across
-// it. The backward kernels never read back, inside a workgroup, what they write to global memory,
-// so LDS is the only memory their barriers have to order.
-__device__ __forceinline__ void lds_barrier() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
+// The backward kernels never read back, inside a workgroup, what they write to global memory, so
+// their barriers order LDS only (lds_barrier) and prefetches stay in flight across them.
 
 template <int V>
 struct IntC { static constexpr int value = V; };

@@ -146,4 +146,13 @@ struct OpF32 {
     __device__ static __forceinline__ elem cvt(float x) { return x; }
 };
 
+// Workgroup barrier that orders LDS accesses only. __syncthreads() also waits for every
+// outstanding global load and store of the wave; this one lets a prefetch stay in flight across
+// it. For kernels whose workgroups never read back, through global memory, what they wrote there.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 }  // namespace kda
