@@ -21,7 +21,10 @@
 //   bwd_state_kernel   one workgroup per (lane, 32 value columns), chunks in reverse: Gx of every
 //                      chunk, dV~, and dS0
 //   bwd_grad_kernel    one workgroup per chunk: dq, dk, dv, dlog_alpha, dbeta
-// Plain fp32 loops over LDS / L2-resident scratch: correctness first, one workgroup per CU.
+// All arithmetic is fp32. The matrix products (the state pass, V~ and the value-column products,
+// T^T [dW | dV~], dA_kk) run on the fp32 matrix cores (16x16x4 MFMA) from LDS operands laid out
+// contiguous along the contraction index; the pairwise decay terms and the inverse run on the
+// VALU. One workgroup per CU (each kernel's LDS arena takes most of it).
 #include "kda_device.h"
 #include "kda_internal.h"
 
