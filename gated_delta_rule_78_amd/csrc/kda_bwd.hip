@@ -18,7 +18,7 @@
 //
 // Three kernels after a forward recompute that stores every chunk's entry state:
 //   bwd_prep_kernel    one workgroup per chunk: T, W, U, Q~, K-, A_qk, gamma (fp32 scratch)
-//   bwd_state_kernel   one workgroup per (lane, 32 value columns), chunks in reverse: Gx of every
+//   bwd_state_kernel   one workgroup per (lane, 16 or 32 value columns), chunks in reverse: Gx of every
 //                      chunk, dV~, and dS0
 //   bwd_grad_kernel    one workgroup per chunk: dq, dk, dv, dlog_alpha, dbeta
 // All arithmetic is fp32. The matrix products (the state pass, V~ and the value-column products,
@@ -308,10 +308,10 @@ __global__ __launch_bounds__(kTP) void bwd_prep_kernel(BwdArgs a) {
     }
 }
 
-// Reverse state pass for value columns [j0, j0 + 32) of one lane, on the fp32 matrix cores
+// Reverse state pass for value columns [j0, j0 + NB) of one lane (NB = 16 or 32), on the fp32 matrix cores
 // (16x16x4 MFMA). Per chunk, walking backwards:
-//     dV~ = K- Gx + A_qk^T dO                     (64 x 32; wave w owns rows 16w .. 16w + 15)
-//     Gx  <- Diag(gamma) Gx + Q~^T dO - W^T dV~   (DK x 32; wave w owns rows DK/4 w ..)
+//     dV~ = K- Gx + A_qk^T dO                     (64 x NB; wave w owns rows 16w .. 16w + 15)
+//     Gx  <- Diag(gamma) Gx + Q~^T dO - W^T dV~   (DK x NB; wave w owns rows DK/4 w ..)
 // Gx lives in the waves' accumulator registers for the whole pass. Every MFMA operand sits in LDS
 // with the contraction index contiguous (K- as is; Q~, W, A_qk, dO and dV~ transposed while
 // staged or stored), so a lane fetches its next four k values of an operand in one 16-byte read.
@@ -319,9 +319,9 @@ __global__ __launch_bounds__(kTP) void bwd_prep_kernel(BwdArgs a) {
 // walks through are assigned as kb + 4 g + q for step q of a block of 16, the same on both sides.
 // The chunk before the current one is loaded into registers while the current one computes; the
 // barriers order LDS only, so that load stays in flight across them.
-template <int DK, int DV>
+template <int DK, int NB>
 struct __align__(16) StateSmem {
-    static constexpr int NB = 32, LK = DK + 4, LS = kC + 4;
+    static constexpr int LK = DK + 4, LS = kC + 4;
     float KB[kC][LK];     // K- [t][ch]
     float QTT[DK][LS];    // Q~^T [ch][s]
     float WTN[DK][LS];    // -W^T [ch][s]
@@ -336,9 +336,8 @@ struct __align__(16) StateSmem {
 // and the LDS store. A [64][n] factor is read in blocks of 16 rows x 16 columns, one block per
 // wave and instruction: lane l takes row 16 (b mod 4) + (l mod 16) and the four columns from
 // 16 (b / 4) + 4 (l / 16), so the transposed LDS stores of a half-wave fall in distinct banks.
-template <int DK, typename TO>
+template <int DK, typename TO, int NB>
 struct StateFetch {
-    static constexpr int NB = 32;
     static constexpr int NF = kC * DK / 4 / kT;   // float4s of one [64][DK] factor
     static constexpr int NA = kC * kC / 4 / kT;   // float4s of A_qk
     static constexpr int ND = kC * NB / kT;       // dO elements
@@ -405,13 +404,13 @@ __device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
-template <int DK, int DV, typename TO>
+template <int DK, int DV, typename TO, int NB>
 __global__ __launch_bounds__(kT) void bwd_state_kernel(BwdArgs a) {
     typedef BwdLayout<DK, DV> L;
-    typedef StateSmem<DK, DV> SS;
-    typedef StateFetch<DK, TO> F;
-    constexpr int NB = F::NB;
+    typedef StateSmem<DK, NB> SS;
+    typedef StateFetch<DK, TO, NB> F;
     constexpr int RT = DK / 64;   // 16-row tiles of Gx per wave
+    constexpr int CT = NB / 16;   // 16-column tiles of the block
     static_assert(DV % NB == 0 && DK % 64 == 0 && (kC * DK / 4) % kT == 0 && (kC * kC / 4) % kT == 0, "state tiles");
     extern __shared__ __align__(16) unsigned char smem_raw[];
     SS& sm = *reinterpret_cast<SS*>(smem_raw);
@@ -432,11 +431,11 @@ __global__ __launch_bounds__(kT) void bwd_state_kernel(BwdArgs a) {
     const int wv = threadIdx.x >> 6, lr = threadIdx.x & 15, lg = (threadIdx.x >> 4) & 3;
     // Gx accumulators: gx[rt][ct][i] = Gx[gr0 + 16 rt + 4 lg + i][16 ct + lr]
     const int gr0 = wv * (DK / 4);
-    f32x4 gx[RT][2];
+    f32x4 gx[RT][CT];
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct)
+        for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int ch = gr0 + 16 * rt + 4 * lg + i, j = 16 * ct + lr;
@@ -446,7 +445,7 @@ __global__ __launch_bounds__(kT) void bwd_state_kernel(BwdArgs a) {
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-            for (int ct = 0; ct < 2; ++ct)
+            for (int ct = 0; ct < CT; ++ct)
                 *reinterpret_cast<f32x4*>(&sm.GxT[16 * ct + lr][gr0 + 16 * rt + 4 * lg]) = gx[rt][ct];
     };
     put_gxt();
@@ -465,7 +464,7 @@ __global__ __launch_bounds__(kT) void bwd_state_kernel(BwdArgs a) {
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-            for (int ct = 0; ct < 2; ++ct)
+            for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
                     gst[(gr0 + 16 * rt + 4 * lg + i) * DV + j0 + 16 * ct + lr] = gx[rt][ct][i];
@@ -475,30 +474,32 @@ __global__ __launch_bounds__(kT) void bwd_state_kernel(BwdArgs a) {
         lds_barrier();
         // dV~ rows 16 wv .. 16 wv + 15 = K- Gx + A_qk^T dO (A_qk^T[t][s] = 0 for s < t)
         {
-            f32x4 dv[2] = {kZero4f(), kZero4f()};
+            f32x4 dv[CT];
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) dv[ct] = kZero4f();
             const int t0 = 16 * wv;
             for (int kb = 0; kb < DK; kb += 16) {
                 const f32x4 x = *reinterpret_cast<const f32x4*>(&sm.KB[t0 + lr][kb + 4 * lg]);
-                const f32x4 y0 = *reinterpret_cast<const f32x4*>(&sm.GxT[lr][kb + 4 * lg]);
-                const f32x4 y1 = *reinterpret_cast<const f32x4*>(&sm.GxT[16 + lr][kb + 4 * lg]);
+                f32x4 y[CT];
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    dv[0] = mfma4(x[q], y0[q], dv[0]);
-                    dv[1] = mfma4(x[q], y1[q], dv[1]);
-                }
+                for (int ct = 0; ct < CT; ++ct) y[ct] = *reinterpret_cast<const f32x4*>(&sm.GxT[16 * ct + lr][kb + 4 * lg]);
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+#pragma unroll
+                    for (int ct = 0; ct < CT; ++ct) dv[ct] = mfma4(x[q], y[ct][q], dv[ct]);
             }
             for (int kb = t0; kb < kC; kb += 16) {
                 const f32x4 x = *reinterpret_cast<const f32x4*>(&sm.AQT[t0 + lr][kb + 4 * lg]);
-                const f32x4 y0 = *reinterpret_cast<const f32x4*>(&sm.dOT[lr][kb + 4 * lg]);
-                const f32x4 y1 = *reinterpret_cast<const f32x4*>(&sm.dOT[16 + lr][kb + 4 * lg]);
+                f32x4 y[CT];
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    dv[0] = mfma4(x[q], y0[q], dv[0]);
-                    dv[1] = mfma4(x[q], y1[q], dv[1]);
-                }
+                for (int ct = 0; ct < CT; ++ct) y[ct] = *reinterpret_cast<const f32x4*>(&sm.dOT[16 * ct + lr][kb + 4 * lg]);
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+#pragma unroll
+                    for (int ct = 0; ct < CT; ++ct) dv[ct] = mfma4(x[q], y[ct][q], dv[ct]);
             }
 #pragma unroll
-            for (int ct = 0; ct < 2; ++ct) {
+            for (int ct = 0; ct < CT; ++ct) {
                 *reinterpret_cast<f32x4*>(&sm.dVT[16 * ct + lr][t0 + 4 * lg]) = dv[ct];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) dvt[(t0 + 4 * lg + i) * DV + j0 + 16 * ct + lr] = dv[ct][i];
@@ -509,8 +510,8 @@ __global__ __launch_bounds__(kT) void bwd_state_kernel(BwdArgs a) {
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
             const f32x4 g4 = *reinterpret_cast<const f32x4*>(&sm.gam[gr0 + 16 * rt + 4 * lg]);
-            gx[rt][0] *= g4;
-            gx[rt][1] *= g4;
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) gx[rt][ct] *= g4;
         }
         for (int kb = 0; kb < kC; kb += 16) {
             f32x4 xq[RT], xw[RT];
@@ -519,18 +520,20 @@ __global__ __launch_bounds__(kT) void bwd_state_kernel(BwdArgs a) {
                 xq[rt] = *reinterpret_cast<const f32x4*>(&sm.QTT[gr0 + 16 * rt + lr][kb + 4 * lg]);
                 xw[rt] = *reinterpret_cast<const f32x4*>(&sm.WTN[gr0 + 16 * rt + lr][kb + 4 * lg]);
             }
-            const f32x4 o0 = *reinterpret_cast<const f32x4*>(&sm.dOT[lr][kb + 4 * lg]);
-            const f32x4 o1 = *reinterpret_cast<const f32x4*>(&sm.dOT[16 + lr][kb + 4 * lg]);
-            const f32x4 v0 = *reinterpret_cast<const f32x4*>(&sm.dVT[lr][kb + 4 * lg]);
-            const f32x4 v1 = *reinterpret_cast<const f32x4*>(&sm.dVT[16 + lr][kb + 4 * lg]);
+            f32x4 o[CT], v[CT];
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) {
+                o[ct] = *reinterpret_cast<const f32x4*>(&sm.dOT[16 * ct + lr][kb + 4 * lg]);
+                v[ct] = *reinterpret_cast<const f32x4*>(&sm.dVT[16 * ct + lr][kb + 4 * lg]);
+            }
 #pragma unroll
             for (int q = 0; q < 4; ++q)
 #pragma unroll
                 for (int rt = 0; rt < RT; ++rt) {
-                    gx[rt][0] = mfma4(xq[rt][q], o0[q], gx[rt][0]);
-                    gx[rt][1] = mfma4(xq[rt][q], o1[q], gx[rt][1]);
-                    gx[rt][0] = mfma4(xw[rt][q], v0[q], gx[rt][0]);
-                    gx[rt][1] = mfma4(xw[rt][q], v1[q], gx[rt][1]);
+#pragma unroll
+                    for (int ct = 0; ct < CT; ++ct) gx[rt][ct] = mfma4(xq[rt][q], o[ct][q], gx[rt][ct]);
+#pragma unroll
+                    for (int ct = 0; ct < CT; ++ct) gx[rt][ct] = mfma4(xw[rt][q], v[ct][q], gx[rt][ct]);
                 }
         }
         put_gxt();   // nothing reads Gx^T between the dV~ products above and the next chunk's
@@ -539,7 +542,7 @@ __global__ __launch_bounds__(kT) void bwd_state_kernel(BwdArgs a) {
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-            for (int ct = 0; ct < 2; ++ct)
+            for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
                     a.dS0[(lane * DK + gr0 + 16 * rt + 4 * lg + i) * DV + j0 + 16 * ct + lr] = gx[rt][ct][i];
@@ -965,23 +968,30 @@ template <int DK, int DV, typename TO>
 hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
     const int64_t chunks = a.lanes * a.nchunks;
     if (chunks <= 0) return hipSuccess;
-    const size_t prep_smem = sizeof(PrepSmem<DK, DV>), state_smem = sizeof(StateSmem<DK, DV>);
+    // state pass: blocks of 16 value columns when blocks of 32 would leave compute units idle
+    const bool narrow = a.lanes * (DV / 32) < resident_workgroups() / 2;
+    const size_t prep_smem = sizeof(PrepSmem<DK, DV>);
+    const size_t state_smem = narrow ? sizeof(StateSmem<DK, 16>) : sizeof(StateSmem<DK, 32>);
+    const void* state_fn = narrow ? (const void*)bwd_state_kernel<DK, DV, TO, 16> : (const void*)bwd_state_kernel<DK, DV, TO, 32>;
     const size_t grad_smem = GradArena<DK, DV>::TOTAL * sizeof(float);
     // each kernel takes more than the default dynamic LDS limit: raise it, and stop at the first
     // error (a later launch would otherwise hide it)
     hipError_t e = hipFuncSetAttribute((const void*)bwd_prep_kernel<DK, DV>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)prep_smem);
     if (e == hipSuccess)
-        e = hipFuncSetAttribute((const void*)bwd_state_kernel<DK, DV, TO>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                (int)state_smem);
+        e = hipFuncSetAttribute(state_fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)state_smem);
     if (e == hipSuccess)
         e = hipFuncSetAttribute((const void*)bwd_grad_kernel<DK, DV, TO>, hipFuncAttributeMaxDynamicSharedMemorySize,
                                 (int)grad_smem);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_prep_kernel<DK, DV>), dim3((unsigned)chunks), dim3(kTP), prep_smem, st, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_state_kernel<DK, DV, TO>), dim3((unsigned)(a.lanes * (DV / 32))), dim3(kT), state_smem, st,
-                       a);
+    if (narrow)
+        hipLaunchKernelGGL((bwd_state_kernel<DK, DV, TO, 16>), dim3((unsigned)(a.lanes * (DV / 16))), dim3(kT),
+                           state_smem, st, a);
+    else
+        hipLaunchKernelGGL((bwd_state_kernel<DK, DV, TO, 32>), dim3((unsigned)(a.lanes * (DV / 32))), dim3(kT),
+                           state_smem, st, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_grad_kernel<DK, DV, TO>), dim3((unsigned)chunks), dim3(kTG), grad_smem, st, a);
     return hipGetLastError();

@@ -556,22 +556,6 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs p) {
 #undef KDA_INTRA_LOAD
 }
 
-// Resident workgroups for the persistent grid: two per compute unit (the LDS budget). Cached
-// per device; concurrent first calls from several host threads store the same value.
-int resident_workgroups() {
-    static std::atomic<int> cached[64];
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 512;
-    int n = cached[dev].load(std::memory_order_relaxed);
-    if (n == 0) {
-        int cus = 0;
-        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
-        n = 2 * cus;
-        cached[dev].store(n, std::memory_order_relaxed);
-    }
-    return n;
-}
-
 template <int DK, int DV>
 hipError_t launch_dd(const IntraArgs& a, hipStream_t st) {
     int64_t blocks = a.slot_tab ? a.map.H * a.map.slots : a.lanes * a.nchunks;
@@ -589,6 +573,22 @@ hipError_t launch_dd(const IntraArgs& a, hipStream_t st) {
 }
 
 }  // namespace
+
+// Resident workgroups for the persistent grid: two per compute unit (the LDS budget). Cached
+// per device; concurrent first calls from several host threads store the same value.
+int resident_workgroups() {
+    static std::atomic<int> cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 512;
+    int n = cached[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+        n = 2 * cus;
+        cached[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
 
 hipError_t launch_intra(const IntraArgs& a, hipStream_t st) {
     if (a.dk == 128) return a.dv == 128 ? launch_dd<128, 128>(a, st) : launch_dd<128, 64>(a, st);

@@ -67,6 +67,12 @@ def test_bwd_full_decay_domain():
     run_bwd("bwd full decay", 1, 2, 192, 128, 128, la_range=(-5.0, 0.0), seed=7300)
 
 
+def test_bwd_many_lanes():
+    """64 lanes: the reverse state pass takes blocks of 32 value columns here (it narrows them to
+    16 when there are too few lanes to fill the GPU, as in the other cases)."""
+    run_bwd("bwd 64 lanes", 2, 32, 130, 128, 128, seed=7500)
+
+
 def test_bwd_longer_sequence():
     """1024 tokens (16 chunks; the forward recompute splits the sequence into segments)."""
     run_bwd("bwd 1K", 1, 4, 1024, 128, 128, seed=7400)
