@@ -906,11 +906,17 @@ __global__ __launch_bounds__(kTG) void bwd_grad_kernel(BwdArgs a) {
             atomicAdd(&dlgam[c0 + u + e], accK[u + e] * k4[e] * kbf);
         }
     }
-    // pairwise terms. Row sums: this thread's row t against rows j <= t (A_qk and A_kk of row t);
-    // column sums: rows i >= t against row t (their column t). The factors of a (row, row) pair
-    // are read once; the 32 channels come in 16-byte reads.
+    // pairwise terms, per channel c of this thread (E_ij = exp(G_i - G_j), i >= j):
+    //   row sums     rq = sum_{j<=t} A_qk[t][j] K_j E_tj,   rk = sum_{j<t} A_kk[t][j] K_j E_tj
+    //   column sums  cc = sum_{i>=t} (A_qk[i][t] Q_i + beta_i A_kk[i][t] K_i) E_it
+    // then dq += rq, dk += beta_t rk + cc, dG += Q_t rq + beta_t K_t rk - K_t cc and
+    // dbeta += K_t . rk. The factors of a (row, row) pair are read once; the channels come in
+    // 16-byte reads.
+    float rq[CG], rk[CG], cc[CG];
+#pragma unroll
+    for (int u = 0; u < CG; ++u) { rq[u] = 0.f; rk[u] = 0.f; cc[u] = 0.f; }
     for (int j = 0; j <= t; ++j) {
-        const float aq = sAqk[t * LA + j], bak = bt * sAkk[t * LA + j], ak = sAkk[t * LA + j];
+        const float aq = sAqk[t * LA + j], ak = sAkk[t * LA + j];
 #pragma unroll
         for (int u = 0; u < CG; u += 4) {
             const f32x4 g4 = *reinterpret_cast<const f32x4*>(sG + j * LK + c0 + u);
@@ -918,10 +924,8 @@ __global__ __launch_bounds__(kTG) void bwd_grad_kernel(BwdArgs a) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const float kj = k4[e] * fexp(gt[u + e] - g4[e]);
-                dq[u + e] += aq * kj;
-                dk[u + e] += bak * kj;
-                dG[u + e] += (aq * qt[u + e] + bak * kt[u + e]) * kj;
-                dbeta += ak * kt[u + e] * kj;
+                rq[u + e] += aq * kj;
+                rk[u + e] += ak * kj;
             }
         }
     }
@@ -933,12 +937,15 @@ __global__ __launch_bounds__(kTG) void bwd_grad_kernel(BwdArgs a) {
             const f32x4 k4 = *reinterpret_cast<const f32x4*>(sK + i * LK + c0 + u);
             const f32x4 q4 = *reinterpret_cast<const f32x4*>(sQ + i * LK + c0 + u);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float wv = (aq * q4[e] + bak * k4[e]) * fexp(g4[e] - gt[u + e]);
-                dk[u + e] += wv;
-                dG[u + e] -= wv * kt[u + e];
-            }
+            for (int e = 0; e < 4; ++e) cc[u + e] += (aq * q4[e] + bak * k4[e]) * fexp(g4[e] - gt[u + e]);
         }
+    }
+#pragma unroll
+    for (int u = 0; u < CG; ++u) {
+        dq[u] += rq[u];
+        dk[u] += bt * rk[u] + cc[u];
+        dG[u] += qt[u] * rq[u] + kt[u] * (bt * rk[u] - cc[u]);
+        dbeta += kt[u] * rk[u];
     }
     lds_barrier();
     // dG into LDS over Q, dgamma's share on row 63, then the reverse cumsum per channel
