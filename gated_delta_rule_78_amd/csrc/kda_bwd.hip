@@ -67,6 +67,12 @@ __device__ __forceinline__ f32x4 kZero4f() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 template <int V>
 struct IntC { static constexpr int value = V; };
 
+// fp32 16x16x4 MFMA step: lane l = r + 16 g supplies A[r][g] and B[g][r]; the accumulator holds
+// rows 4 g .. 4 g + 3 of column r
+__device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
 // Register tiles for cooperative global -> LDS copies by NT threads: every thread issues all of
 // its loads before its first LDS write, so a block costs one memory round trip instead of one per
 // element. Piece e of a block goes to thread e mod NT.
@@ -171,7 +177,8 @@ struct InTile {
 
 template <int DK, int DV>
 struct __align__(16) PrepSmem {
-    float K[kC][DK], Q[kC][DK], G[kC][DK];
+    static constexpr int LP = DK + 4;   // padded rows: 16-byte reads of 8 rows fall in distinct banks
+    float K[kC][LP], Q[kC][LP], G[kC][LP];
     float A[kC][kC + 1], T[kC][kC + 1];
     float beta[kC];
     float Vx[DV > DK ? kC : 1][DV > DK ? DV : 4];   // beta V when it does not fit over Q
@@ -199,9 +206,9 @@ __global__ __launch_bounds__(kTP) void bwd_prep_kernel(BwdArgs a) {
         const float b = ldin((const bf16_t*)a.beta, row0 + (tid < nrows ? tid : nrows - 1));
         sm.beta[tid] = tid < nrows ? b : 0.f;
     }
-    tk.store(&sm.K[0][0], DK);
-    tq.store(&sm.Q[0][0], DK);
-    tg.store(&sm.G[0][0], DK);
+    tk.store(&sm.K[0][0], PrepSmem<DK, DV>::LP);
+    tq.store(&sm.Q[0][0], PrepSmem<DK, DV>::LP);
+    tg.store(&sm.G[0][0], PrepSmem<DK, DV>::LP);
     lds_barrier();
     for (int c = tid; c < DK; c += kTP) {   // G = inclusive cumulative sum of log_alpha down the rows
         float acc = 0.f;
@@ -209,26 +216,26 @@ __global__ __launch_bounds__(kTP) void bwd_prep_kernel(BwdArgs a) {
     }
     lds_barrier();
 
-    // A_kk (i > j, beta-scaled) and A_qk (i >= j): thread = (row i, columns JA g .. JA g + JA - 1)
-    {
-        constexpr int NG = kTP / kC, JA = kC / NG;
-        const int i = tid / NG, jg = (tid % NG) * JA;
-        float akk[JA], aqk[JA];
-#pragma unroll
-        for (int u = 0; u < JA; ++u) { akk[u] = 0.f; aqk[u] = 0.f; }
-        if (jg <= i) {
+    // A_kk (i > j, beta-scaled) and A_qk (i >= j) by 16 x 16 blocks. A diagonal block forms the
+    // factors exp(G_i - G_j) pair by pair; an off-diagonal block (I > J) splits them at r = 16 I,
+    // the first row of block I, as exp(G_i - G_r) exp(G_r - G_j), both <= 1 since j < r <= i
+    // (so the whole decay domain stays in range), and runs on the fp32 MFMA with the factors
+    // folded into its operands.
+    {   // diagonal blocks: thread = (row i, columns jd and jd + 1 of its block)
+        const int i = tid >> 3, jd = (i & ~15) + 2 * (tid & 7);
+        float akk[2] = {0.f, 0.f}, aqk[2] = {0.f, 0.f};
+        if (jd <= i) {
             for (int ch = 0; ch < DK; ch += 4) {
                 const f32x4 ki = *reinterpret_cast<const f32x4*>(&sm.K[i][ch]);
                 const f32x4 qi = *reinterpret_cast<const f32x4*>(&sm.Q[i][ch]);
                 const f32x4 gi = *reinterpret_cast<const f32x4*>(&sm.G[i][ch]);
 #pragma unroll
-                for (int u = 0; u < JA; ++u) {
-                    if (jg + u > i) break;
-                    const f32x4 kj = *reinterpret_cast<const f32x4*>(&sm.K[jg + u][ch]);
-                    const f32x4 gj = *reinterpret_cast<const f32x4*>(&sm.G[jg + u][ch]);
+                for (int u = 0; u < 2; ++u) {
+                    const f32x4 kj = *reinterpret_cast<const f32x4*>(&sm.K[jd + u][ch]);
+                    const f32x4 gj = *reinterpret_cast<const f32x4*>(&sm.G[jd + u][ch]);
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        const float f = kj[e] * fexp(gi[e] - gj[e]);
+                        const float f = kj[e] * fexp(gi[e] - gj[e]);   // jd + 1 > i: never stored
                         akk[u] += ki[e] * f;
                         aqk[u] += qi[e] * f;
                     }
@@ -236,10 +243,40 @@ __global__ __launch_bounds__(kTP) void bwd_prep_kernel(BwdArgs a) {
             }
         }
 #pragma unroll
-        for (int u = 0; u < JA; ++u) {
-            const int j = jg + u;
+        for (int u = 0; u < 2; ++u) {
+            const int j = jd + u;
             sm.A[i][j] = j < i ? sm.beta[i] * akk[u] : 0.f;
             sc[L::AQK + i * kC + j] = j <= i ? aqk[u] : 0.f;
+        }
+        for (int j = (i & ~15) + 16 + (tid & 7); j < kC; j += 8) sc[L::AQK + i * kC + j] = 0.f;   // above
+    }
+    {   // off-diagonal blocks (I, J), I > J: one per wave for waves 0 .. 5
+        const int wv = tid >> 6, lr = tid & 15, lg = (tid >> 4) & 3;
+        if (wv < 6) {
+            const int I = wv < 1 ? 1 : (wv < 3 ? 2 : 3), J = wv - (I * (I - 1)) / 2;
+            const int r = 16 * I, ia = r + lr, jb = 16 * J + lr;
+            f32x4 ckk = kZero4f(), cqk = kZero4f();
+            for (int kb = 0; kb < DK; kb += 16) {
+                const int k0 = kb + 4 * lg;
+                const f32x4 ka = *reinterpret_cast<const f32x4*>(&sm.K[ia][k0]);
+                const f32x4 qa = *reinterpret_cast<const f32x4*>(&sm.Q[ia][k0]);
+                const f32x4 ga = *reinterpret_cast<const f32x4*>(&sm.G[ia][k0]);
+                const f32x4 gr = *reinterpret_cast<const f32x4*>(&sm.G[r][k0]);
+                const f32x4 kbv = *reinterpret_cast<const f32x4*>(&sm.K[jb][k0]);
+                const f32x4 gbv = *reinterpret_cast<const f32x4*>(&sm.G[jb][k0]);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const float fa = fexp(ga[q] - gr[q]), fb = kbv[q] * fexp(gr[q] - gbv[q]);
+                    ckk = mfma4(ka[q] * fa, fb, ckk);
+                    cqk = mfma4(qa[q] * fa, fb, cqk);
+                }
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int row = r + 4 * lg + e, col = 16 * J + lr;
+                sm.A[row][col] = sm.beta[row] * ckk[e];
+                sc[L::AQK + row * kC + col] = cqk[e];
+            }
         }
     }
     lds_barrier();
@@ -399,10 +436,6 @@ struct StateFetch {
         }
     }
 };
-
-__device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
-}
 
 template <int DK, int DV, typename TO, int NB>
 __global__ __launch_bounds__(kT) void bwd_state_kernel(BwdArgs a) {
