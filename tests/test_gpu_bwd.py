@@ -73,6 +73,25 @@ def test_bwd_many_lanes():
     run_bwd("bwd 64 lanes", 2, 32, 130, 128, 128, seed=7500)
 
 
+def test_bwd_full_workload_sampled_lanes():
+    """The 8K workload in the configuration the benchmark times (B=1, H=32, T=8192, d=128, bf16,
+    library plan, dS_T given): every gradient of heads 0 and 31 against the oracle, one lane at a
+    time (the oracle keeps all 8192 states of a lane)."""
+    w = synth.PREFILL_BF16_8K
+    say("bwd 8K: %s, heads 0 and 31 against the oracle" % w.name)
+    q, k, v, la, beta, S0 = synth.workload_inputs(w, device=DEV)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(17)
+    dO = torch.randn(w.B, w.H, w.T, w.d, generator=g, device=DEV).to(BF16)
+    dST = torch.randn(w.B, w.H, w.d, w.d, generator=g, device=DEV) * 0.1
+    got = kda.chunk_bwd(q, k, v, la, beta, S0, dO, dST)
+    torch.cuda.synchronize()
+    for h in (0, w.H - 1):
+        f = lambda x: None if x is None else host32(x[:, h:h + 1]).reshape((1,) + tuple(x.shape[2:]))
+        ref = backward.kda_bwd(f(q), f(k), f(v), f(la), f(beta), f(S0), f(dO), f(dST))
+        check_grads("bwd 8K head %d" % h, [x[:, h:h + 1] for x in got], ref, 1)
+
+
 def test_bwd_longer_sequence():
     """1024 tokens (16 chunks; the forward recompute splits the sequence into segments)."""
     run_bwd("bwd 1K", 1, 4, 1024, 128, 128, seed=7400)
