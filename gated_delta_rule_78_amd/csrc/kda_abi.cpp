@@ -220,7 +220,7 @@ kda_status run_bf16(kda::ChunkLaunch& a, const Plan& plan, unsigned char* ws, hi
 struct BwdPlan {
     Plan fwd;
     int64_t ck_stride;
-    size_t ckpt_off, o_off, prep_off, gst_off, dvt_off, gscr_off, ws_bytes;
+    size_t ckpt_off, o_off, prep_off, gst_off, dvt_off, ws_bytes;
 };
 
 BwdPlan make_bwd_plan(const kda_chunk_desc* d) {
@@ -236,8 +236,7 @@ BwdPlan make_bwd_plan(const kda_chunk_desc* d) {
     b.prep_off = align(b.o_off + (size_t)(lanes * d->T * d->dv) * (size_t)elem_bytes(d->out_dtype));
     b.gst_off = align(b.prep_off + chunks * kda::bwd_prep_floats(d->dk, d->dv) * 4);
     b.dvt_off = align(b.gst_off + chunks * (size_t)(d->dk * d->dv) * 4);
-    b.gscr_off = align(b.dvt_off + chunks * (size_t)(kChunk * d->dv) * 4);
-    b.ws_bytes = b.gscr_off + chunks * kda::bwd_grad_floats(d->dk, d->dv) * 4;
+    b.ws_bytes = b.dvt_off + chunks * (size_t)(kChunk * d->dv) * 4;
     return b;
 }
 
@@ -500,7 +499,6 @@ kda_status kda_chunk_bwd(const kda_chunk_desc* d, const void* q, const void* k, 
     b.prep = reinterpret_cast<float*>(ws + bp.prep_off);
     b.gst = reinterpret_cast<float*>(ws + bp.gst_off);
     b.dvt = reinterpret_cast<float*>(ws + bp.dvt_off);
-    b.gscr = reinterpret_cast<float*>(ws + bp.gscr_off);
     b.dq = dq; b.dk_ = dk; b.dv_ = dv; b.dla = dlog_alpha; b.dbeta = dbeta; b.dS0 = dS0;
     return kda::launch_bwd(b, st) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }

@@ -47,12 +47,6 @@ struct BwdLayout {
     static constexpr int AQK = KB + kC * DK;          // [64][64]
     static constexpr int GAM = AQK + kC * kC;         // [DK] gamma
     static constexpr int PREP = GAM + DK;
-    // gradient-kernel scratch
-    static constexpr int VT = 0;                      // [64][DV] V~
-    static constexpr int DW = VT + kC * DV;           // [64][DK]
-    static constexpr int XK = DW + kC * DK;           // [64][DK] dX_K
-    static constexpr int XV = XK + kC * DK;           // [64][DV] dX_V
-    static constexpr int GRAD = XV + kC * DV;
 };
 
 __device__ __forceinline__ float ldin(const bf16_t* p, int64_t i) { return bf16_bits_to_f32(p[i]); }
@@ -1145,10 +1139,6 @@ hipError_t launch_bwd_o(const BwdArgs& a, hipStream_t st) {
 size_t bwd_prep_floats(int64_t dk, int64_t dv) {
     return dk == 128 ? (dv == 128 ? BwdLayout<128, 128>::PREP : BwdLayout<128, 64>::PREP)
                      : (dv == 128 ? BwdLayout<64, 128>::PREP : BwdLayout<64, 64>::PREP);
-}
-size_t bwd_grad_floats(int64_t dk, int64_t dv) {
-    return dk == 128 ? (dv == 128 ? BwdLayout<128, 128>::GRAD : BwdLayout<128, 64>::GRAD)
-                     : (dv == 128 ? BwdLayout<64, 128>::GRAD : BwdLayout<64, 64>::GRAD);
 }
 
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t st) {

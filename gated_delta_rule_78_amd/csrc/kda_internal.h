@@ -108,11 +108,9 @@ struct BwdArgs {
     float* prep;                          // [lanes * nchunks][bwd_prep_floats]
     float* gst;                           // [lanes * nchunks][dk][dv]  exit-state gradient of each chunk
     float* dvt;                           // [lanes * nchunks][64][dv]  dV~ of each chunk
-    float* gscr;                          // [lanes * nchunks][bwd_grad_floats]
     float *dq, *dk_, *dv_, *dla, *dbeta, *dS0;   // outputs (dS0 may be NULL)
 };
 size_t bwd_prep_floats(int64_t dk, int64_t dv);
-size_t bwd_grad_floats(int64_t dk, int64_t dv);
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t st);
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st);

@@ -209,7 +209,8 @@ kda_status kda_chunk_fwd_varlen(const kda_varlen_desc* desc,
 
 /* Bytes of device workspace kda_chunk_bwd needs for `desc` (0 for an invalid desc, fp32 inputs or
  * T = 0). It holds the forward's workspace, the state after every 64-token chunk (fp32), the
- * recomputed output, and per-chunk fp32 scratch (about 0.5 MiB per chunk of a lane at d = 128). */
+ * recomputed output, and per-chunk fp32 scratch (with the checkpoint about 0.32 MiB per chunk of
+ * a lane at d = 128). */
 size_t kda_chunk_bwd_workspace_bytes(const kda_chunk_desc* desc);
 
 /*
