@@ -173,7 +173,8 @@ template <int DK, int DV>
 struct __align__(16) PrepSmem {
     static constexpr int LP = DK + 4;   // padded rows: 16-byte reads of 8 rows fall in distinct banks
     float K[kC][LP], Q[kC][LP], G[kC][LP];
-    float A[kC][kC + 1], T[kC][kC + 1];
+    float A[kC][kC + 1], T[kC][kC + 4];   // T rows 16-byte aligned for the MFMA operand reads
+    float Y[3][16][17];                   // block products of the inverse's substitution levels
     float beta[kC];
     float Vx[DV > DK ? kC : 1][DV > DK ? DV : 4];   // beta V when it does not fit over Q
 };
@@ -274,28 +275,58 @@ __global__ __launch_bounds__(kTP) void bwd_prep_kernel(BwdArgs a) {
         }
     }
     lds_barrier();
-    if (tid < kC) {
-        // wave 0: T = (I + A)^{-1}, unit lower triangular; thread j keeps column j in registers
-        // and walks the rows in order
-        const int j = tid;
-        float col[kC];
+    // T = (I + A_kk)^{-1} (unit lower triangular) by 16 x 16 blocks: waves 0-3 invert the diagonal
+    // blocks (one column per lane in registers, rows in order) while waves 4-7 write Q~, K- and
+    // gamma; then block forward substitution T_IJ = -T_II sum_{J <= K < I} A_IK T_KJ, one level
+    // of I - J at a time, on the fp32 MFMA.
+    const int wv = tid >> 6, lr = tid & 15, lg = (tid >> 4) & 3;
+    if (wv < 4) {
+        const int o = 16 * wv, j = lr;
+        float col[16];
 #pragma unroll
-        for (int i = 0; i < kC; ++i) {
+        for (int i = 0; i < 16; ++i) {
             float x = i == j ? 1.f : 0.f;
 #pragma unroll
-            for (int m = 0; m < i; ++m) x -= sm.A[i][m] * col[m];
+            for (int m = 0; m < i; ++m) x -= sm.A[o + i][o + m] * col[m];
             col[i] = i >= j ? x : 0.f;
         }
+        if ((tid & 63) < 16)
 #pragma unroll
-        for (int i = 0; i < kC; ++i) sm.T[i][j] = col[i];
+            for (int i = 0; i < 16; ++i) sm.T[o + i][o + j] = col[i];
+        for (int e = tid & 63; e < 16 * (kC - o - 16); e += 64) sm.T[o + e / (kC - o - 16)][o + 16 + e % (kC - o - 16)] = 0.f;
     } else {
-        // the other waves meanwhile: Q~ = Q e^G, K- = K e^{G_63 - G}, gamma
-        for (int e = tid - kC; e < kC * DK; e += kTP - kC) {
+        // Q~ = Q e^G, K- = K e^{G_63 - G}, gamma
+        for (int e = tid - 256; e < kC * DK; e += kTP - 256) {
             const int t = e / DK, ch = e % DK;
             sc[L::QT + e] = sm.Q[t][ch] * fexp(sm.G[t][ch]);
             sc[L::KB + e] = sm.K[t][ch] * fexp(sm.G[kC - 1][ch] - sm.G[t][ch]);
         }
-        for (int ch = tid - kC; ch < DK; ch += kTP - kC) sc[L::GAM + ch] = fexp(sm.G[kC - 1][ch]);
+        for (int ch = tid - 256; ch < DK; ch += kTP - 256) sc[L::GAM + ch] = fexp(sm.G[kC - 1][ch]);
+    }
+    lds_barrier();
+#pragma unroll
+    for (int d = 1; d <= 3; ++d) {
+        const bool job = wv < 4 - d;
+        const int J = wv, I = wv + d;
+        if (job) {   // Y = sum_K A_IK T_KJ
+            f32x4 y = kZero4f();
+            for (int K = J; K < I; ++K)
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    y = mfma4(sm.A[16 * I + lr][16 * K + 4 * lg + q], sm.T[16 * K + 4 * lg + q][16 * J + lr], y);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sm.Y[wv][4 * lg + e][lr] = y[e];
+        }
+        lds_barrier();
+        if (job) {   // T_IJ = -T_II Y
+            f32x4 t4 = kZero4f();
+            const f32x4 x = *reinterpret_cast<const f32x4*>(&sm.T[16 * I + lr][16 * I + 4 * lg]);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) t4 = mfma4(x[q], sm.Y[wv][4 * lg + q][lr], t4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sm.T[16 * I + 4 * lg + e][16 * J + lr] = -t4[e];
+        }
+        lds_barrier();
     }
     lds_barrier();
     // right-hand sides in place: K <- Diag(beta) K e^G, and Diag(beta) V over Q (or its own
@@ -308,34 +339,35 @@ __global__ __launch_bounds__(kTP) void bwd_prep_kernel(BwdArgs a) {
     tv.store(Vs, DV, sm.beta);
     for (int e = tid; e < kC * kC; e += kTP) sc[L::T + e] = sm.T[e / kC][e % kC];
     lds_barrier();
-    // W = T (beta K e^G), U = T (beta V): thread = (row t, channel / column group)
+    // W = T (beta K e^G), U = T (beta V) as 16x16x4 MFMA tiles: wave w takes rows 16 (w mod 4) and
+    // half of the columns of each (T[t][m] = 0 past the diagonal block, so m stops there)
     {
-        constexpr int NG = kTP / kC, CG = DK / NG, VG = DV / NG;
-        const int t = tid / NG, c0 = (tid % NG) * CG, j0 = (tid % NG) * VG;
-        float w[CG], u[VG];
+        constexpr int NWT = DK / 32, NUT = DV / 32;
+        const int rb = 16 * (wv & 3), cw = (DK / 2) * (wv >> 2), cu = (DV / 2) * (wv >> 2);
+        f32x4 aw[NWT], au[NUT];
 #pragma unroll
-        for (int x = 0; x < CG; ++x) w[x] = 0.f;
+        for (int ct = 0; ct < NWT; ++ct) aw[ct] = kZero4f();
 #pragma unroll
-        for (int x = 0; x < VG; ++x) u[x] = 0.f;
-        for (int m = 0; m <= t; ++m) {
-            const float tm = sm.T[t][m];
+        for (int ct = 0; ct < NUT; ++ct) au[ct] = kZero4f();
+        for (int kb = 0; kb <= rb; kb += 16) {
+            const f32x4 x = *reinterpret_cast<const f32x4*>(&sm.T[rb + lr][kb + 4 * lg]);
 #pragma unroll
-            for (int x = 0; x < CG; x += 4) {
-                const f32x4 k4 = *reinterpret_cast<const f32x4*>(&sm.K[m][c0 + x]);
-                w[x] += tm * k4[0]; w[x + 1] += tm * k4[1]; w[x + 2] += tm * k4[2]; w[x + 3] += tm * k4[3];
-            }
+            for (int q = 0; q < 4; ++q) {
+                const int m = kb + 4 * lg + q;
 #pragma unroll
-            for (int x = 0; x < VG; x += 4) {
-                const f32x4 v4 = *reinterpret_cast<const f32x4*>(Vs + m * DV + j0 + x);
-                u[x] += tm * v4[0]; u[x + 1] += tm * v4[1]; u[x + 2] += tm * v4[2]; u[x + 3] += tm * v4[3];
+                for (int ct = 0; ct < NWT; ++ct) aw[ct] = mfma4(x[q], sm.K[m][cw + 16 * ct + lr], aw[ct]);
+#pragma unroll
+                for (int ct = 0; ct < NUT; ++ct) au[ct] = mfma4(x[q], Vs[m * DV + cu + 16 * ct + lr], au[ct]);
             }
         }
 #pragma unroll
-        for (int x = 0; x < CG; x += 4)
-            *reinterpret_cast<f32x4*>(sc + L::W + t * DK + c0 + x) = f32x4{w[x], w[x + 1], w[x + 2], w[x + 3]};
+        for (int e = 0; e < 4; ++e) {
+            const int t = rb + 4 * lg + e;
 #pragma unroll
-        for (int x = 0; x < VG; x += 4)
-            *reinterpret_cast<f32x4*>(sc + L::U + t * DV + j0 + x) = f32x4{u[x], u[x + 1], u[x + 2], u[x + 3]};
+            for (int ct = 0; ct < NWT; ++ct) sc[L::W + t * DK + cw + 16 * ct + lr] = aw[ct][e];
+#pragma unroll
+            for (int ct = 0; ct < NUT; ++ct) sc[L::U + t * DV + cu + 16 * ct + lr] = au[ct][e];
+        }
     }
 }
 
