@@ -52,7 +52,8 @@ def decode_alg(N, H, d, in_bytes=2, out_bytes=2):
 # Measured HBM traffic (rocprofv3 FETCH_SIZE / WRITE_SIZE, calibrated) comes from the committed
 # profile summary; a figure is used only while the kernel sources it was taken on are unchanged.
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_prefill_8k_and_decode.md")
-PREFILL_SOURCES = ["kda_intra.hip", "kda_inter.hip", "kda_scan.hip", "kda_record.h", "kda_mfma.h", "kda_abi.cpp"]
+PREFILL_SOURCES = ["kda_intra.hip", "kda_inter.hip", "kda_scan.hip", "kda_record.h", "kda_mfma.h", "kda_device.h",
+                   "kda_plan.h", "kda_plan.cpp"]
 DECODE_SOURCES = ["kda_decode.hip", "kda_device.h"]
 
 

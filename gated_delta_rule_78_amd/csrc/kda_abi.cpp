@@ -8,12 +8,17 @@
 #include <string.h>
 
 #include "kda_internal.h"
+#include "kda_plan.h"
 #include "kda_record.h"
 
 namespace {
 
-constexpr int64_t kChunk = 64;
-constexpr int64_t kTargetBlocks = 256;  // one workgroup per compute unit
+using kda::kChunk;
+using kda::Geometry;
+using kda::Plan;
+using kda::ceil_div;
+using kda::make_plan;
+using kda::run_bf16;
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
@@ -28,71 +33,6 @@ bool overlaps(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi && a.hi > a.
 
 bool valid_dtype(int32_t d) { return d == KDA_F32 || d == KDA_BF16; }
 int64_t elem_bytes(int32_t d) { return d == KDA_BF16 ? 2 : 4; }
-
-// What a bf16 prefill call covers, for planning: `lanes` (batch or sequence, head) pairs whose
-// longest one has `max_chunks` chunks, and `slots` record slots in all.
-struct Geometry {
-    int64_t lanes, max_chunks, slots, dk, dv;
-    int32_t in_dtype, segments;
-    int64_t tab_slots;   // slot-table entries (packed batches), 0 otherwise
-    int64_t long_lanes;  // lanes that can have max_chunks chunks (plans the sequence split)
-};
-
-// Segments per lane, chunks per segment and workspace of a prefill call.
-struct Plan {
-    int nseg;
-    int64_t nchunks, chunks_per_seg;
-    size_t rec_bytes;    // intra-chunk records (bf16 path): one per slot
-    size_t pair_bytes;   // affine pairs [lanes][nseg][dk][dv + dk] (nseg > 1)
-    size_t entry_bytes;  // entry states [lanes][nseg][dk][dv] (nseg > 1)
-    size_t tab_bytes;    // slot table (packed batches)
-    size_t ws_bytes;
-};
-
-int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
-
-// Sequence split of the bf16 state pass. One state-pass workgroup occupies a compute unit; with
-// n segments, pass 1 runs segment 0 plus n - 2 summaries per lane, pass 2 the n - 1 later
-// segments, each pass taking chunks_per_seg steps per round of kTargetBlocks workgroups. Pick the
-// n with the fewest sequential chunk steps (the segment scan adds about two per segment).
-int64_t auto_segments(int64_t lanes, int64_t nchunks) {
-    int64_t best = 1;
-    int64_t best_cost = nchunks * ceil_div(lanes, kTargetBlocks);
-    const int64_t nmax = nchunks / 4 < 64 ? nchunks / 4 : 64;
-    for (int64_t n = 3; n <= nmax; ++n) {
-        const int64_t cps = ceil_div(nchunks, n);
-        const int64_t nn = ceil_div(nchunks, cps);
-        if (nn < 3) continue;
-        const int64_t rounds = ceil_div(lanes * (nn - 1), kTargetBlocks);
-        const int64_t cost = cps * 2 * rounds + 2 * (nn - 2);
-        if (cost < best_cost) { best_cost = cost; best = nn; }
-    }
-    return best;
-}
-
-Plan make_plan(const Geometry& g) {
-    Plan p{};
-    const int64_t nchunks = g.max_chunks;
-    p.nchunks = nchunks;
-    int64_t nseg = 1;
-    if (g.in_dtype == KDA_BF16 && nchunks > 0) nseg = g.segments > 0 ? g.segments : auto_segments(g.long_lanes, nchunks);
-    if (nseg > nchunks) nseg = nchunks > 0 ? nchunks : 1;
-    int64_t cps = nchunks > 0 ? ceil_div(nchunks, nseg) : 1;
-    if (cps < 1) cps = 1;
-    nseg = nchunks > 0 ? ceil_div(nchunks, cps) : 1;  // no segment past the longest lane
-    p.nseg = (int)nseg;
-    p.chunks_per_seg = cps;
-    if (g.in_dtype == KDA_BF16 && nchunks > 0) {
-        p.rec_bytes = (size_t)g.slots * (size_t)kda::record_bytes(g.dk, g.dv);
-        if (nseg > 1) {
-            p.pair_bytes = (size_t)g.lanes * (size_t)nseg * (size_t)(g.dk * (g.dv + g.dk)) * sizeof(float);
-            p.entry_bytes = (size_t)g.lanes * (size_t)nseg * (size_t)(g.dk * g.dv) * sizeof(float);
-        }
-        p.tab_bytes = (size_t)g.tab_slots * sizeof(kda::SlotEntry);
-    }
-    p.ws_bytes = p.rec_bytes + p.pair_bytes + p.entry_bytes + p.tab_bytes;
-    return p;
-}
 
 Geometry fixed_geometry(const kda_chunk_desc* d) {
     const int64_t nchunks = ceil_div(d->T, kChunk);
@@ -183,36 +123,6 @@ Geometry varlen_geometry(const kda_varlen_desc* d) {
     // 0.39 ms in 3 segments).
     return Geometry{d->N * d->H, max_chunks, d->H * slots, d->dk, d->dv, d->in_dtype, d->segments, slots,
                     d->N * d->H};
-}
-
-// bf16 prefill after validation: records of every chunk (state independent, fully parallel),
-// then the sequential state pass, split in two passes around the segment scan when the plan
-// has more than one segment per lane.
-kda_status run_bf16(kda::ChunkLaunch& a, const Plan& plan, unsigned char* ws, hipStream_t st) {
-    kda::IntraArgs ia{};
-    ia.lanes = a.lanes; ia.T = a.T; ia.nchunks = a.nchunks; ia.dk = a.dk; ia.dv = a.dv;
-    ia.q = a.q; ia.k = a.k; ia.v = a.v; ia.la = a.la; ia.beta = a.beta;
-    ia.rec = ws;
-    ia.map = a.map;
-    ia.gt = a.gt;
-    ia.slot_tab = a.map.cu ? reinterpret_cast<const kda::SlotEntry*>(ws + plan.rec_bytes + plan.pair_bytes + plan.entry_bytes)
-                           : nullptr;
-    if (kda::launch_intra(ia, st) != hipSuccess) return KDA_ERR_HIP;
-    a.rec = ws;
-    a.ws_pair = plan.pair_bytes ? reinterpret_cast<float*>(ws + plan.rec_bytes) : nullptr;
-    a.ws_entry = plan.entry_bytes ? reinterpret_cast<float*>(ws + plan.rec_bytes + plan.pair_bytes) : nullptr;
-    if (plan.nseg == 1) {
-        a.fin_seg_lo = 0; a.fin_nseg = 1; a.sum_seg_lo = 0; a.sum_nseg = 0;
-        return kda::launch_inter(a, st) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
-    }
-    // pass 1: segment 0 from the known entry state; summaries of the middle segments
-    a.fin_seg_lo = 0; a.fin_nseg = 1; a.sum_seg_lo = 1; a.sum_nseg = plan.nseg - 2;
-    if (kda::launch_inter(a, st) != hipSuccess) return KDA_ERR_HIP;
-    // exact entry state of every later segment
-    if (kda::launch_segment_scan(a, st) != hipSuccess) return KDA_ERR_HIP;
-    // pass 2: every later segment from its exact entry state
-    a.fin_seg_lo = 1; a.fin_nseg = plan.nseg - 1; a.sum_seg_lo = 0; a.sum_nseg = 0;
-    return kda::launch_inter(a, st) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
 // Backward workspace, in order: the forward's own workspace (records, pairs, entries), every

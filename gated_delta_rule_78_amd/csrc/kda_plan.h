@@ -1,0 +1,45 @@
+// Launch plan and dispatch of a bf16 prefill call (fixed-length or packed): how many sequence
+// segments each lane's state pass is split into, the workspace that plan needs, and the launch
+// sequence intra-chunk kernel -> state pass (-> segment scan -> state pass). Internal to the
+// library; the C ABI validates arguments before it plans.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "kda.h"
+#include "kda_internal.h"
+
+namespace kda {
+
+constexpr int64_t kChunk = 64;
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// What a bf16 prefill call covers, for planning: `lanes` (batch or sequence, head) pairs whose
+// longest one has `max_chunks` chunks, and `slots` record slots in all.
+struct Geometry {
+    int64_t lanes, max_chunks, slots, dk, dv;
+    int32_t in_dtype, segments;
+    int64_t tab_slots;   // slot-table entries (packed batches), 0 otherwise
+    int64_t long_lanes;  // lanes that can have max_chunks chunks (plans the sequence split)
+};
+
+// Segments per lane, chunks per segment and workspace of a prefill call.
+struct Plan {
+    int nseg;
+    int64_t nchunks, chunks_per_seg;
+    size_t rec_bytes;    // intra-chunk records (bf16 path): one per slot
+    size_t pair_bytes;   // affine pairs [lanes][nseg][dk][dv + dk] (nseg > 1)
+    size_t entry_bytes;  // entry states [lanes][nseg][dk][dv] (nseg > 1)
+    size_t tab_bytes;    // slot table (packed batches)
+    size_t ws_bytes;
+};
+
+Plan make_plan(const Geometry& g);
+
+// Launch a validated bf16 prefill on `st`: `a` carries the call's tensors and geometry, `ws` the
+// workspace of `plan` (at least plan.ws_bytes). Returns KDA_ERR_HIP if a launch fails.
+kda_status run_bf16(ChunkLaunch& a, const Plan& plan, unsigned char* ws, hipStream_t st);
+
+}  // namespace kda
