@@ -277,7 +277,7 @@ def main():
         toks = [synth.decode_tokens(dw.N, dw.H, dw.d, dw.d, dw.dtype, device=dev, seed=4000 + i)
                 for i in range(min(args.decode_steps, 1000))]
         od = torch.empty(dw.N, dw.H, dw.d, device=dev, dtype=dw.dtype)
-        for i in range(3):
+        for i in range(max(args.warmup, 3)):   # untimed, like the prefill's warm-up calls
             kda.decode_step(*toks[i % len(toks)], S, o=od, stream=stream)
         torch.cuda.synchronize()
         d0 = torch.cuda.Event(enable_timing=True)
