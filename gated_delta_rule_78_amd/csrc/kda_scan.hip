@@ -6,9 +6,11 @@
 //
 // One workgroup (4 waves) per (lane, 16 state columns). The current entry tile (dk x 16) lives in
 // LDS, transposed; each step is a (dk x dk) x (dk x 16) product on the fp32 MFMA (16x16x4): wave w
-// owns dk/64 output row tiles, its A operands (rows of M_s) stream from the workspace three
-// steps ahead. Within a lane group the k index runs contiguously (k = (dk/4) lq + j for the j-th MFMA),
-// the same for A and B, so each lane reads its operands as whole 16-byte vectors.
+// owns dk/64 output row tiles, its A operands (rows of M_s) stream from the workspace two
+// steps ahead. The k index of the e-th value of a lane's j-th 16-byte vector is 16 j + 4 lq + e,
+// the same for A and B: each lane reads whole 16-byte vectors, and the four lane groups of a row
+// read 64 contiguous bytes per instruction (a blocked k = (dk/4) lq + .. layout made every
+// instruction touch four times as many cache lines).
 #include "kda_internal.h"
 #include "kda_mfma.h"
 
@@ -47,10 +49,22 @@ __global__ __launch_bounds__(256) void segment_scan_kernel(ChunkLaunch p) {
     const int64_t col = 16 * cb + l16;
     const int nseg = p.nseg;
 
+    // entry tile: every load issued before the first LDS store (one memory round trip)
     const float* e1 = p.ws_entry + (lane * nseg + 1) * DK * DV;
-    for (int i = tid; i < DK * 16; i += 256) Et[i & 15][i >> 4] = e1[(int64_t)(i >> 4) * DV + 16 * cb + (i & 15)];
+    constexpr int NE = DK * 16 / 256;
+    float ev[NE];
+#pragma unroll
+    for (int u = 0; u < NE; ++u) {
+        const int i = tid + 256 * u;
+        ev[u] = e1[(int64_t)(i >> 4) * DV + 16 * cb + (i & 15)];
+    }
+#pragma unroll
+    for (int u = 0; u < NE; ++u) {
+        const int i = tid + 256 * u;
+        Et[i & 15][i >> 4] = ev[u];
+    }
 
-    // operands of step s: A = rows 16 (TPW w + t) + l16 of M_s, k = KJ lq .. KJ lq + KJ - 1;
+    // operands of step s: A = rows 16 (TPW w + t) + l16 of M_s, k = 16 j4 + 4 lq + e;
     // st = S~_s at the tile's accumulator positions
     f32x4 a[TPW][KJ / 4], st[TPW];
     auto load_step = [&](int s, f32x4 (*aa)[KJ / 4], f32x4* ss) {
@@ -58,51 +72,52 @@ __global__ __launch_bounds__(256) void segment_scan_kernel(ChunkLaunch p) {
 #pragma unroll
         for (int t = 0; t < TPW; ++t) {
             const int row0 = 16 * (TPW * w + t);
-            const float* Arow = P + (int64_t)(row0 + l16) * LDP + DV + KJ * lq;
+            const float* Arow = P + (int64_t)(row0 + l16) * LDP + DV + 4 * lq;
 #pragma unroll
-            for (int j4 = 0; j4 < KJ / 4; ++j4) aa[t][j4] = *reinterpret_cast<const f32x4*>(Arow + 4 * j4);
+            for (int j4 = 0; j4 < KJ / 4; ++j4) aa[t][j4] = *reinterpret_cast<const f32x4*>(Arow + 16 * j4);
 #pragma unroll
             for (int r = 0; r < 4; ++r) ss[t][r] = P[(int64_t)(row0 + 4 * lq + r) * LDP + col];
         }
     };
-    // Operands three steps ahead: the loads of step s + 3 are in flight while steps s .. s + 2
-    // compute (the chain of a step is short next to a memory round trip).
+    // Operands two steps ahead in three buffers: at the top of step s, before its products, the
+    // loads of step s + 2 go into the buffer step s - 1 has released, so they are issued while
+    // this step's MFMA chain runs. The loop is unrolled by three so that no buffer is ever copied
+    // (a register copy would wait for the loads filling its source).
     f32x4 a1[TPW][KJ / 4], st1[TPW], a2[TPW][KJ / 4], st2[TPW];
     if (nseg > 2) load_step(1, a, st);
     if (nseg > 3) load_step(2, a1, st1);
-    if (nseg > 4) load_step(3, a2, st2);
-    __syncthreads();
-    for (int s = 1; s + 1 < nseg; ++s) {
-        f32x4 acc[TPW];
-#pragma unroll
-        for (int t = 0; t < TPW; ++t) acc[t] = st[t];
-#pragma unroll
-        for (int j4 = 0; j4 < KJ / 4; ++j4) {
-            const f32x4 b = *reinterpret_cast<const f32x4*>(&Et[l16][KJ * lq + 4 * j4]);
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-#pragma unroll
-                for (int t = 0; t < TPW; ++t) acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[t][j4][e], b[e], acc[t], 0, 0, 0);
-        }
-        // rotate the prefetched operands and start the loads of step s + 3
-#pragma unroll
-        for (int t = 0; t < TPW; ++t) {
-            st[t] = st1[t]; st1[t] = st2[t];
-#pragma unroll
-            for (int j4 = 0; j4 < KJ / 4; ++j4) { a[t][j4] = a1[t][j4]; a1[t][j4] = a2[t][j4]; }
-        }
-        if (s + 4 < nseg) load_step(s + 3, a2, st2);
-        __syncthreads();   // every wave has read the old entry tile
-        float* dst = p.ws_entry + (lane * nseg + s + 1) * DK * DV;
-#pragma unroll
-        for (int t = 0; t < TPW; ++t) {
-            const int row0 = 16 * (TPW * w + t);
-            *reinterpret_cast<f32x4*>(&Et[l16][row0 + 4 * lq]) = acc[t];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) dst[(int64_t)(row0 + 4 * lq + r) * DV + col] = acc[t][r];
-        }
-        __syncthreads();
+    // Barriers below order the LDS tile only: a full barrier would also wait for the operand
+    // loads in flight for later steps. The entry states stored here are read by a later kernel.
+    lds_barrier();
+    // (a macro, not a lambda, so that the operand arrays stay in registers)
+#define KDA_SCAN_STEP(S_, A_, ST_, NA_, NST_)                                                       \
+    do {                                                                                            \
+        const int s_ = (S_);                                                                        \
+        if (s_ + 3 < nseg) load_step(s_ + 2, NA_, NST_);                                            \
+        f32x4 acc[TPW];                                                                             \
+        _Pragma("unroll") for (int t = 0; t < TPW; ++t) acc[t] = ST_[t];                            \
+        _Pragma("unroll") for (int j4 = 0; j4 < KJ / 4; ++j4) {                                     \
+            const f32x4 b = *reinterpret_cast<const f32x4*>(&Et[l16][16 * j4 + 4 * lq]);           \
+            _Pragma("unroll") for (int e = 0; e < 4; ++e)                                           \
+            _Pragma("unroll") for (int t = 0; t < TPW; ++t)                                         \
+                acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(A_[t][j4][e], b[e], acc[t], 0, 0, 0); \
+        }                                                                                           \
+        lds_barrier();   /* every wave has read the old entry tile */                               \
+        float* dst = p.ws_entry + (lane * nseg + s_ + 1) * DK * DV;                                 \
+        _Pragma("unroll") for (int t = 0; t < TPW; ++t) {                                           \
+            const int row0 = 16 * (TPW * w + t);                                                    \
+            *reinterpret_cast<f32x4*>(&Et[l16][row0 + 4 * lq]) = acc[t];                            \
+            _Pragma("unroll") for (int r = 0; r < 4; ++r)                                           \
+                dst[(int64_t)(row0 + 4 * lq + r) * DV + col] = acc[t][r];                           \
+        }                                                                                           \
+        lds_barrier();                                                                              \
+    } while (0)
+    for (int s = 1; s + 1 < nseg; s += 3) {
+        KDA_SCAN_STEP(s, a, st, a2, st2);
+        if (s + 2 < nseg) KDA_SCAN_STEP(s + 1, a1, st1, a, st);
+        if (s + 3 < nseg) KDA_SCAN_STEP(s + 2, a2, st2, a1, st1);
     }
+#undef KDA_SCAN_STEP
 }
 
 }  // namespace
