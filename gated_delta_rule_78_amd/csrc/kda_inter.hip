@@ -50,6 +50,27 @@ struct __align__(16) InterSmem {
     float ssq[2][4][64];    // fused epilogue: per-wave partial sums of o^2 per token, by chunk parity
 };
 
+// Store two 16-column output tiles of one token row (accumulator layout: lane (lq, l16) holds
+// columns 4 lq .. 4 lq + 3 of each tile for token l16). One permlane16 swap per register trades
+// rows 1 <-> 0 and 3 <-> 2 between the tiles, after which lane lq holds the 8 consecutive columns
+// starting at 16 (lq & 1) + 8 (lq >> 1): a 16-byte store per lane, and every token row written in
+// whole 64-byte pieces (two 8-byte stores per lane wrote 32-byte pieces).
+__device__ __forceinline__ void store_out_pair(__amdgpu_buffer_rsrc_t r, uint32_t row_off, uint32_t col, f32x4 x, f32x4 y,
+                                               int lq, bf16_t*) {
+    typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
+    typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
+    f32x4 a, b;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const u32x2 sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(x[i]), __float_as_uint(y[i]), false, false);
+        a[i] = __uint_as_float(sw[0]);
+        b[i] = __uint_as_float(sw[1]);
+    }
+    const u32x4 u = {pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]), pack_bf16x2(b[0], b[1]), pack_bf16x2(b[2], b[3])};
+    const uint32_t c = col + 16u * (uint32_t)(lq & 1) + 8u * (uint32_t)(lq >> 1);
+    __builtin_amdgcn_raw_buffer_store_b128(u, r, (int)((row_off + c) * 2u), 0, 0);
+}
+
 // Fused epilogue of one output tile: y = sigmoid(gate) * w * o * rstd for 4 columns of a token.
 __device__ __forceinline__ f32x4 gated_norm(f32x4 o, uint2 g, f32x4 w, float rstd) {
     const float gv[4] = {__uint_as_float(g.x << 16), __uint_as_float(g.x & 0xffff0000u),
@@ -313,10 +334,17 @@ __device__ __forceinline__ void run_segment(const ChunkLaunch& p, InterSmem<DK, 
                 const float* ps_ = &sm.ssq[(cc) & 1][0][16 * I + l16];                              \
                 rstd_ = __builtin_amdgcn_rsqf((ps_[0] + ps_[64] + ps_[128] + ps_[192]) * inv_dv + p.gt.eps); \
             }                                                                                       \
-            _Pragma("unroll") for (int nt = 0; nt < NT; ++nt) {                                     \
-                const f32x4 y_ = gated ? gated_norm(Opend[nt][I], gpend[nt][I], nw[nt], rstd_) : Opend[nt][I]; \
-                store_out(ro, (row * (uint32_t)DV + col0 + 16 * nt + 4 * lq) * (uint32_t)sizeof(TOut), y_, \
-                          (TOut*)nullptr);                                                          \
+            f32x4 y_[NT];                                                                           \
+            _Pragma("unroll") for (int nt = 0; nt < NT; ++nt)                                       \
+                y_[nt] = gated ? gated_norm(Opend[nt][I], gpend[nt][I], nw[nt], rstd_) : Opend[nt][I]; \
+            if constexpr (sizeof(TOut) == 2 && NT % 2 == 0) {                                       \
+                _Pragma("unroll") for (int nt = 0; nt < NT; nt += 2)                                \
+                    store_out_pair(ro, row * (uint32_t)DV, (uint32_t)(col0 + 16 * nt), y_[nt], y_[nt + 1], lq, \
+                                   (bf16_t*)nullptr);                                               \
+            } else {                                                                                \
+                _Pragma("unroll") for (int nt = 0; nt < NT; ++nt)                                   \
+                    store_out(ro, (row * (uint32_t)DV + col0 + 16 * nt + 4 * lq) * (uint32_t)sizeof(TOut), y_[nt], \
+                              (TOut*)nullptr);                                                      \
             }                                                                                       \
         }                                                                                           \
     } while (0)
