@@ -88,12 +88,23 @@ __device__ __forceinline__ f32x4 gated_norm(f32x4 o, uint2 g, f32x4 w, float rst
 // issues the same count: indices past the end repeat the last block (the same bytes to the same
 // place), which keeps the copy free of branches.
 template <int DK, int DV, bool FIN>
+struct CopyPlan {
+    typedef RecordLayout<DK, DV> R;
+    static constexpr int NSKIP = 4 * R::NKS;
+    static constexpr int NLOAD = FIN ? R::BLOCKS : R::BLOCKS - NSKIP - 6;
+    static constexpr int ITERS = (NLOAD + 3) / 4;                 // loads per wave
+    static constexpr int PART = (ITERS + R::NKS - 1) / R::NKS;   // loads per k step of a chunk
+};
+
+// Loads I0 .. I1 - 1 of this wave's share (all of them by default).
+template <int DK, int DV, bool FIN, int I0 = 0, int I1 = CopyPlan<DK, DV, FIN>::ITERS>
 __device__ __forceinline__ void copy_record(__amdgpu_buffer_rsrc_t rsrc, uint32_t chunk_off, unsigned char* dst, int w, int l) {
     typedef RecordLayout<DK, DV> R;
-    constexpr int NSKIP = 4 * R::NKS;
-    constexpr int NLOAD = FIN ? R::BLOCKS : R::BLOCKS - NSKIP - 6;
+    constexpr int NSKIP = CopyPlan<DK, DV, FIN>::NSKIP;
+    constexpr int NLOAD = CopyPlan<DK, DV, FIN>::NLOAD;
+    constexpr int IEND = I1 < (NLOAD + 3) / 4 ? I1 : (NLOAD + 3) / 4;
 #pragma unroll
-    for (int i = 0; i < (NLOAD + 3) / 4; ++i) {
+    for (int i = I0; i < IEND; ++i) {
         const int b = w + 4 * i < NLOAD ? w + 4 * i : NLOAD - 1;
         const int blk = FIN ? b : (b < R::Q ? b : (b < R::Q + 2 * R::NM ? b + NSKIP : b + NSKIP + 6));
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(dst + blk * 1024), 16, (unsigned)(l * 16),
@@ -102,9 +113,14 @@ __device__ __forceinline__ void copy_record(__amdgpu_buffer_rsrc_t rsrc, uint32_
 }
 
 // One chunk for state tiles G0 .. G0 + NTG - 1 of this wave (columns col0 + 16 nt + l16).
+// The next chunk's record copy (when `copy`) is issued in parts, one after each k step of the
+// first products: issued in one piece before them, its stalls (the copies queue behind the
+// record stream) kept the wave from starting the products for about a microsecond per chunk.
 template <typename TOut, int DK, int DV, int NT, int G0, int NTG, bool FIN>
 __device__ __forceinline__ void chunk_step(const unsigned char* rbuf, f32x4 (&S)[NT][DK / 16], int col0,
-                                           f32x4 (&Opend)[NT][4]) {
+                                           f32x4 (&Opend)[NT][4], bool copy, __amdgpu_buffer_rsrc_t crs,
+                                           unsigned char* cdst, int w) {
+    typedef CopyPlan<DK, DV, FIN> CP;
     typedef RecordLayout<DK, DV> R;
     constexpr int NKS = R::NKS, NM = R::NM, NV = R::NV;
     const int l = threadIdx.x & 63;
@@ -151,6 +167,12 @@ __device__ __forceinline__ void chunk_step(const unsigned char* rbuf, f32x4 (&S)
             for (int I = 0; I < 4; ++I)
 #pragma unroll
                 for (int nt = 0; nt < NTG; ++nt) Ot[nt][I] = mma32(sk[nt], qb[I], Ot[nt][I]);
+        }
+        if (copy) {
+            if (ks == 0) copy_record<DK, DV, FIN, 0, CP::PART>(crs, 0u, cdst, w, l);
+            if (ks == 1) copy_record<DK, DV, FIN, CP::PART, 2 * CP::PART>(crs, 0u, cdst, w, l);
+            if (ks == 2) copy_record<DK, DV, FIN, 2 * CP::PART, 3 * CP::PART>(crs, 0u, cdst, w, l);
+            if (ks == 3) copy_record<DK, DV, FIN, 3 * CP::PART, 4 * CP::PART>(crs, 0u, cdst, w, l);
         }
     }
     // V~ as K32 B operands over tokens 0..31 (v01) and 32..63 (v23)
@@ -367,9 +389,9 @@ __device__ __forceinline__ void run_segment(const ChunkLaunch& p, InterSmem<DK, 
             KDA_CKPT_STORE(c - 1);
             KDA_STORE_O(c - 1);
         }
-        if (c + 1 < c_end) copy_record<DK, DV, FIN>(make_rsrc(rec0 + (c + 1) * BYTES, BYTES), 0u, sm.rec[buf ^ 1], w, l);
         KDA_LOAD_GATE(c);
-        chunk_step<TOut, DK, DV, NT, 0, NT, FIN>(sm.rec[buf], S, col0, Opend);
+        chunk_step<TOut, DK, DV, NT, 0, NT, FIN>(sm.rec[buf], S, col0, Opend, c + 1 < c_end,
+                                                 make_rsrc(rec0 + (c + 1) * BYTES, BYTES), sm.rec[buf ^ 1], w);
         if (gated) KDA_EPI_PARTIAL(c);
     }
     if (FIN && c_begin < c_end) {
