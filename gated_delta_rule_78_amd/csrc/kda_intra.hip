@@ -224,14 +224,22 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs p) {
         }                                                                                           \
     } while (0)
 
-    // Persistent: workgroup b takes chunks b, b + gridDim.x, ... of the flattened (lane, chunk)
-    // index, so the loads of the next chunk overlap the Gram tiles and solve of this one.
-    // Item t is (head or lane t / slots, slot t % slots); the pair advances by the grid size
-    // without dividing again.
+    // Persistent: workgroup b takes items b, b + gridDim.x, ..., so the loads of the next chunk
+    // overlap the Gram tiles and solve of this one. Item u -> (head or lane h, slot j). Packed
+    // batch: head-major, in slot order. Fixed length: chunk-major from the last chunk down, lanes
+    // fastest: the records written last, the ones still in the last-level cache when the state
+    // pass starts, are then the first chunks of every lane, which the state pass reads first (in
+    // lane-major order only the last-written lanes found theirs there, and the first pass waited
+    // for the others).
     const uint32_t G = gridDim.x;
-    const uint32_t step_h = G / slots, step_j = G % slots;
+    const uint32_t nl = (uint32_t)(PACKED ? 1 : p.lanes);
+    auto item_of = [&](uint32_t u, uint32_t& h, uint32_t& j) {
+        if (PACKED) { h = u / slots; j = u % slots; }
+        else { h = u % nl; j = slots - 1u - u / nl; }
+    };
     uint32_t t = blockIdx.x;
-    uint32_t hn = t / slots, jn = t % slots;   // the item whose rows are (being) loaded
+    uint32_t hn = 0, jn = 0;   // the item whose rows are (being) loaded
+    if (t < total) item_of(t, hn, jn);
     KDA_INTRA_LOAD(t < total, hn, jn);
     // taken here too, so that the loop head (which merges this path with the loop's back edge)
     // carries no wait for loads
@@ -241,18 +249,18 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs p) {
     for (int i = 0; i < LPR; ++i) pin(pv[i]);
     pin(pb);
     for (; t < total; t += G) {
-    unsigned char* rec = p.rec + (int64_t)t * R::BYTES;
+    const uint32_t hc = hn, jc = jn;   // this item
+    unsigned char* rec = p.rec + ((int64_t)hc * slots + jc) * R::BYTES;
     // exp(A_h) of this chunk's head for the fused decay prologue (head = lane % H for a fixed batch)
-    const float eA = ZPRO ? __builtin_amdgcn_exp2f(p.gt.A_log[PACKED ? hn : hn % nheads] * kLog2e) : 0.f;
+    const float eA = ZPRO ? __builtin_amdgcn_exp2f(p.gt.A_log[PACKED ? hc : hc % nheads] * kLog2e) : 0.f;
     // valid rows of this chunk: with the fused prologue, padded rows (zeros, so z = 0) must not
     // decay, g = 0 there rather than g_min / 2
     uint32_t nrows = kC;
     if (ZPRO) {
-        if (PACKED) nrows = (uint32_t)p.slot_tab[jn].nrows;
-        else nrows = (uint32_t)(rows - (int64_t)jn * kC < kC ? rows - (int64_t)jn * kC : kC);
+        if (PACKED) nrows = (uint32_t)p.slot_tab[jc].nrows;
+        else nrows = (uint32_t)(rows - (int64_t)jc * kC < kC ? rows - (int64_t)jc * kC : kC);
     }
-    jn += step_j; hn += step_h;
-    if (jn >= slots) { jn -= slots; ++hn; }
+    if (t + G < total) item_of(t + G, hn, jn);   // the next item
     auto blk = [&](int b) -> unsigned char* { return rec + b * 1024 + l * 16; };
 
     // ================= phase 1: decay and scaled operands (wave-local) =========================
