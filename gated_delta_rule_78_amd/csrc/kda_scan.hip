@@ -4,10 +4,11 @@
 // of the middle segments, it forms the exact entry states entry_{s+1} = S~_s + M_s entry_s for
 // s = 1 .. nseg - 2, in fp32.
 //
-// One workgroup (4 waves) per (lane, 16 state columns). The current entry tile (dk x 16) lives in
-// LDS, transposed; each step is a (dk x dk) x (dk x 16) product on the fp32 MFMA (16x16x4): wave w
-// owns dk/64 output row tiles, its A operands (rows of M_s) stream from the workspace two
-// steps ahead. The k index of the e-th value of a lane's j-th 16-byte vector is 16 j + 4 lq + e,
+// One workgroup per (lane, 16 state columns), one wave per 16-row output tile (8 waves at dk = 128,
+// two per SIMD, so that one wave's operand-load issue overlaps the other's products). The current
+// entry tile (dk x 16) lives in LDS, transposed; each step is a (dk x dk) x (dk x 16) product on
+// the fp32 MFMA (16x16x4), its A operands (rows of M_s) streaming from the workspace two steps
+// ahead. The k index of the e-th value of a lane's j-th 16-byte vector is 16 j + 4 lq + e,
 // the same for A and B: each lane reads whole 16-byte vectors, and the four lane groups of a row
 // read 64 contiguous bytes per instruction (a blocked k = (dk/4) lq + .. layout made every
 // instruction touch four times as many cache lines).
@@ -18,8 +19,9 @@ namespace kda {
 namespace {
 
 template <int DK>
-__global__ __launch_bounds__(256) void segment_scan_kernel(ChunkLaunch p) {
-    constexpr int TPW = DK / 64;   // 16-row output tiles per wave
+__global__ __launch_bounds__(DK == 128 ? 512 : 256) void segment_scan_kernel(ChunkLaunch p) {
+    constexpr int NTH = DK == 128 ? 512 : 256;   // one 16-row output tile per wave
+    constexpr int TPW = DK / (16 * (NTH / 64));   // 16-row output tiles per wave
     constexpr int KJ = DK / 4;     // k values per lane group
     constexpr int LDE = DK + 4;
     __shared__ __align__(16) float Et[16][LDE];   // Et[column][row] of the current entry tile
@@ -51,16 +53,16 @@ __global__ __launch_bounds__(256) void segment_scan_kernel(ChunkLaunch p) {
 
     // entry tile: every load issued before the first LDS store (one memory round trip)
     const float* e1 = p.ws_entry + (lane * nseg + 1) * DK * DV;
-    constexpr int NE = DK * 16 / 256;
+    constexpr int NE = DK * 16 / NTH;
     float ev[NE];
 #pragma unroll
     for (int u = 0; u < NE; ++u) {
-        const int i = tid + 256 * u;
+        const int i = tid + NTH * u;
         ev[u] = e1[(int64_t)(i >> 4) * DV + 16 * cb + (i & 15)];
     }
 #pragma unroll
     for (int u = 0; u < NE; ++u) {
-        const int i = tid + 256 * u;
+        const int i = tid + NTH * u;
         Et[i & 15][i >> 4] = ev[u];
     }
 
@@ -125,7 +127,7 @@ __global__ __launch_bounds__(256) void segment_scan_kernel(ChunkLaunch p) {
 hipError_t launch_segment_scan(const ChunkLaunch& a, hipStream_t st) {
     if (a.nseg <= 2) return hipSuccess;
     const int64_t blocks = a.lanes * (a.dv / 16);
-    if (a.dk == 128) hipLaunchKernelGGL(segment_scan_kernel<128>, dim3((unsigned)blocks), dim3(256), 0, st, a);
+    if (a.dk == 128) hipLaunchKernelGGL(segment_scan_kernel<128>, dim3((unsigned)blocks), dim3(512), 0, st, a);
     else hipLaunchKernelGGL(segment_scan_kernel<64>, dim3((unsigned)blocks), dim3(256), 0, st, a);
     return hipGetLastError();
 }
