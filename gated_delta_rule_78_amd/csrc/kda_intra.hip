@@ -40,15 +40,25 @@ namespace {
 constexpr int kC = 64;
 
 // Constant operand of the prefix-sum MFMA: U[s][t] = (s <= t) in the K32 placement, for token
-// tile I (t = 16 I + l16) and k window ks (s = 32 ks + 16 (e/4) + 4 lq + e%4).
-__device__ __forceinline__ bf16x8 ufrag(int I, int ks, int lq, int l16) {
-    i16x8 u;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const int s = 32 * ks + 16 * (e >> 2) + 4 * lq + (e & 3);
-        u[e] = (s <= 16 * I + l16) ? (short)0x3F80 : (short)0;
+// tile I (t = 16 I + l16) and k window ks (s = 32 ks + 16 (e/4) + 4 lq + e%4). Its six fragments
+// hold a single lane-dependent 4-element pattern, P[e] = (4 lq + e <= l16); every other half is
+// all ones or all zeros: (I, ks) = (0, 0) and (2, 1) are [P | 0], (1, 0) and (3, 1) are [1 | P],
+// (2, 0) and (3, 0) are [1 | 1].
+struct UFrags {
+    bf16x8 p0, onep, ones;   // [P | 0], [1 | P], [1 | 1]
+    __device__ __forceinline__ bf16x8 get(int I, int ks) const {
+        return ks == 0 ? (I == 0 ? p0 : (I == 1 ? onep : ones)) : (I == 2 ? p0 : onep);
     }
-    return __builtin_bit_cast(bf16x8, u);
+};
+__device__ __forceinline__ UFrags ufrags(int lq, int l16) {
+    i16x4 pv, one, zero;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        pv[e] = (4 * lq + e <= l16) ? (short)0x3F80 : (short)0;
+        one[e] = (short)0x3F80;
+        zero[e] = 0;
+    }
+    return UFrags{cat(pv, zero), cat(one, pv), cat(one, one)};
 }
 
 // Operands of the blocked substitution for one chunk: A_kk's off-diagonal blocks as A fragments,
@@ -314,11 +324,12 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs p) {
                 // loop: the empty asm hides that their inputs are loop-invariant.
                 int lqv = lq, l16v = l16;
                 asm volatile("" : "+v"(lqv), "+v"(l16v));
+                const UFrags uf = ufrags(lqv, l16v);
                 f32x4 G[4];
 #pragma unroll
                 for (int I = 0; I < 4; ++I) {
-                    G[I] = mma32(ga[0], ufrag(I, 0, lqv, l16v), kZero4);
-                    if (I >= 2) G[I] = mma32(ga[1], ufrag(I, 1, lqv, l16v), G[I]);
+                    G[I] = mma32(ga[0], uf.get(I, 0), kZero4);
+                    if (I >= 2) G[I] = mma32(ga[1], uf.get(I, 1), G[I]);
                 }
                 // Reference points: G_ref(I) = G at token 16I - 1 (0 for I = 0), broadcast from
                 // lane 15 of the row that holds tile I - 1; gC = G at token 63. Every factor between
