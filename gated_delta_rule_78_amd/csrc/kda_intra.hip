@@ -298,9 +298,6 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs p) {
             for (int i = 0; i < LPR; ++i) *reinterpret_cast<uint4*>(&vst[(i * (64 / LPR) + l / LPR) * LDVS + 8 * (l % LPR)]) = pv[i];
         }
         if (w == 0) sm.beta[l] = __uint_as_float(pb << 16);
-        // the next chunk's rows load while this one is processed (the prefetch registers are free
-        // again once consumed above)
-        KDA_INTRA_LOAD(t + G < total, hn, jn);
         wave_lds_sync();
         if (vw) {
 #pragma unroll
@@ -311,6 +308,7 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs p) {
         }
         if (kw) {
             float pcol[2][4];   // exp(G_ref(I)) of channel 32w + 16h + l16
+            i16x4 qrec[4];      // the h = 0 half of each Q~ record block, stored with the h = 1 half
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 bf16x8 ga[2];
@@ -390,7 +388,8 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs p) {
                     *reinterpret_cast<i16x4*>(lblk(w, 0, I) + l * 16 + 8 * h) = cvt4(oq);
                     *reinterpret_cast<i16x4*>(lblk(w, 1, I) + l * 16 + 8 * h) = cvt4(ok);
                     *reinterpret_cast<i16x4*>(lblk(w, 2, I) + l * 16 + 8 * h) = cvt4(oh);
-                    *reinterpret_cast<i16x4*>(blk(R::q(I, w)) + 8 * h) = cvt4(orq);
+                    if (h == 0) qrec[I] = cvt4(orq);
+                    else *reinterpret_cast<bf16x8*>(blk(R::q(I, w))) = cat(qrec[I], cvt4(orq));
                     // K- token-major into the g stage columns 16h.. (already consumed above)
                     *reinterpret_cast<uint2*>(&stA[(16 * I + l16) * LDG + 16 * h + 4 * lq]) =
                         __builtin_bit_cast(uint2, cvt4(ob));
@@ -434,6 +433,10 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs p) {
                         lblk(w, 1, I) + ((l16 & 3) * 16 + 4 * lq + (l16 >> 2)) * 16 + 8 * h))));
         }
     }
+    // the next chunk's rows load during the Gram phase: issued here rather than right after this
+    // chunk's staging, they no longer queue behind the previous chunk's record stores at the top of
+    // the chunk, and their registers stay free through the decay phase
+    KDA_INTRA_LOAD(t + G < total, hn, jn);
     __syncthreads();
 
     // ================= phase 2: Gram tiles ====================================================
