@@ -55,20 +55,21 @@ struct __align__(16) InterSmem {
 // rows 1 <-> 0 and 3 <-> 2 between the tiles, after which lane lq holds the 8 consecutive columns
 // starting at 16 (lq & 1) + 8 (lq >> 1): a 16-byte store per lane, and every token row written in
 // whole 64-byte pieces (two 8-byte stores per lane wrote 32-byte pieces).
-__device__ __forceinline__ void store_out_pair(__amdgpu_buffer_rsrc_t r, uint32_t row_off, uint32_t col, f32x4 x, f32x4 y,
-                                               int lq, bf16_t*) {
+__device__ __forceinline__ void swap_pair(f32x4 x, f32x4 y, f32x4& a, f32x4& b) {
     typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
-    typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
-    f32x4 a, b;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const u32x2 sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(x[i]), __float_as_uint(y[i]), false, false);
         a[i] = __uint_as_float(sw[0]);
         b[i] = __uint_as_float(sw[1]);
     }
+}
+// first of the lane's 8 consecutive columns within a pair of tiles, after swap_pair
+__device__ __forceinline__ uint32_t pair_col(int lq) { return 16u * (uint32_t)(lq & 1) + 8u * (uint32_t)(lq >> 1); }
+__device__ __forceinline__ void store_bf16x8(__amdgpu_buffer_rsrc_t r, uint32_t elem_off, f32x4 a, f32x4 b) {
+    typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
     const u32x4 u = {pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]), pack_bf16x2(b[0], b[1]), pack_bf16x2(b[2], b[3])};
-    const uint32_t c = col + 16u * (uint32_t)(lq & 1) + 8u * (uint32_t)(lq >> 1);
-    __builtin_amdgcn_raw_buffer_store_b128(u, r, (int)((row_off + c) * 2u), 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(u, r, (int)(elem_off * 2u), 0, 0);
 }
 
 // Fused epilogue of one output tile: y = sigmoid(gate) * w * o * rstd for 4 columns of a token.
@@ -324,14 +325,31 @@ __device__ __forceinline__ void run_segment(const ChunkLaunch& p, InterSmem<DK, 
     constexpr bool gated = FIN && GATED;
     const __amdgpu_buffer_rsrc_t rgt =
         make_rsrc(gated ? (const bf16_t*)p.gt.gate + row_base * DVl : nullptr, gated ? (uint32_t)(len * DVl * 2) : 0u);
+    // bf16 output with an even tile count leaves in 16-byte row pieces (the layout swap_pair leaves):
+    // the gate rows are then loaded in the same pieces and the epilogue applied after the swap
+    constexpr bool PAIRED = sizeof(TOut) == 2 && NT % 2 == 0;
+    constexpr int NP = NT / 2 > 0 ? NT / 2 : 1;
     f32x4 nw[NT];
     uint2 gpend[NT][4];
+    f32x4 nwp[NP][2];    // PAIRED: weights of the lane's 8 columns of each tile pair
+    uint4 gq[NP][4];     // PAIRED: gate values of those columns, one 16-byte piece per token row
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
         nw[nt] = f32x4{1.f, 1.f, 1.f, 1.f};
         if (gated && p.gt.norm_w) nw[nt] = *reinterpret_cast<const f32x4*>(p.gt.norm_w + col0 + 16 * nt + 4 * lq);
 #pragma unroll
         for (int I = 0; I < 4; ++I) gpend[nt][I] = make_uint2(0u, 0u);
+    }
+#pragma unroll
+    for (int np = 0; np < NP; ++np) {
+        nwp[np][0] = nwp[np][1] = f32x4{1.f, 1.f, 1.f, 1.f};
+        if (PAIRED && gated && p.gt.norm_w) {
+            const float* wp = p.gt.norm_w + col0 + 32 * np + pair_col(lq);
+            nwp[np][0] = *reinterpret_cast<const f32x4*>(wp);
+            nwp[np][1] = *reinterpret_cast<const f32x4*>(wp + 4);
+        }
+#pragma unroll
+        for (int I = 0; I < 4; ++I) gq[np][I] = make_uint4(0u, 0u, 0u, 0u);
     }
     const float inv_dv = 1.f / (float)DV;
     // sum of o^2 over the lane's columns, then over the four 16-lane rows, into LDS
@@ -356,24 +374,33 @@ __device__ __forceinline__ void run_segment(const ChunkLaunch& p, InterSmem<DK, 
                 const float* ps_ = &sm.ssq[(cc) & 1][0][16 * I + l16];                              \
                 rstd_ = __builtin_amdgcn_rsqf((ps_[0] + ps_[64] + ps_[128] + ps_[192]) * inv_dv + p.gt.eps); \
             }                                                                                       \
-            f32x4 y_[NT];                                                                           \
-            _Pragma("unroll") for (int nt = 0; nt < NT; ++nt)                                       \
-                y_[nt] = gated ? gated_norm(Opend[nt][I], gpend[nt][I], nw[nt], rstd_) : Opend[nt][I]; \
-            if constexpr (sizeof(TOut) == 2 && NT % 2 == 0) {                                       \
-                _Pragma("unroll") for (int nt = 0; nt < NT; nt += 2)                                \
-                    store_out_pair(ro, row * (uint32_t)DV, (uint32_t)(col0 + 16 * nt), y_[nt], y_[nt + 1], lq, \
-                                   (bf16_t*)nullptr);                                               \
+            if constexpr (PAIRED) {                                                                 \
+                _Pragma("unroll") for (int np = 0; np < NP; ++np) {                                 \
+                    f32x4 a_, b_;                                                                   \
+                    swap_pair(Opend[2 * np][I], Opend[2 * np + 1][I], a_, b_);                      \
+                    if (gated) {                                                                    \
+                        a_ = gated_norm(a_, make_uint2(gq[np][I].x, gq[np][I].y), nwp[np][0], rstd_); \
+                        b_ = gated_norm(b_, make_uint2(gq[np][I].z, gq[np][I].w), nwp[np][1], rstd_); \
+                    }                                                                               \
+                    store_bf16x8(ro, row * (uint32_t)DV + (uint32_t)(col0 + 32 * np) + pair_col(lq), a_, b_); \
+                }                                                                                   \
             } else {                                                                                \
-                _Pragma("unroll") for (int nt = 0; nt < NT; ++nt)                                   \
-                    store_out(ro, (row * (uint32_t)DV + col0 + 16 * nt + 4 * lq) * (uint32_t)sizeof(TOut), y_[nt], \
+                _Pragma("unroll") for (int nt = 0; nt < NT; ++nt) {                                 \
+                    const f32x4 y_ = gated ? gated_norm(Opend[nt][I], gpend[nt][I], nw[nt], rstd_) : Opend[nt][I]; \
+                    store_out(ro, (row * (uint32_t)DV + col0 + 16 * nt + 4 * lq) * (uint32_t)sizeof(TOut), y_, \
                               (TOut*)nullptr);                                                      \
+                }                                                                                   \
             }                                                                                       \
         }                                                                                           \
     } while (0)
     // gate rows of chunk cc for the lane's output tiles
 #define KDA_LOAD_GATE(cc)                                                                           \
     do {                                                                                            \
-        if (gated) {                                                                                \
+        if (gated && PAIRED) {                                                                      \
+            _Pragma("unroll") for (int I = 0; I < 4; ++I)                                           \
+                _Pragma("unroll") for (int np = 0; np < NP; ++np)                                   \
+                    gq[np][I] = buf_load16(rgt, (((uint32_t)((cc) * kC) + 16 * I + l16) * (uint32_t)DV + col0 + 32 * np + pair_col(lq)) * 2u); \
+        } else if (gated) {                                                                         \
             _Pragma("unroll") for (int I = 0; I < 4; ++I)                                           \
                 _Pragma("unroll") for (int nt = 0; nt < NT; ++nt)                                   \
                     gpend[nt][I] = buf_load8(rgt, (((uint32_t)((cc) * kC) + 16 * I + l16) * (uint32_t)DV + col0 + 16 * nt + 4 * lq) * 2u); \
