@@ -413,27 +413,38 @@ struct StateFetch {
     static __device__ __forceinline__ int blk_row(int u) { return 16 * (((threadIdx.x >> 6) + 4 * u) & 3) + (threadIdx.x & 15); }
     static __device__ __forceinline__ int blk_col(int u) { return 16 * (((threadIdx.x >> 6) + 4 * u) >> 2) + 4 * ((threadIdx.x >> 4) & 3); }
 
+    // The loads of one chunk as a flat list: [0, NF) K-, [NF, 2NF) Q~, [2NF, 3NF) W, then A_qk,
+    // gamma and dO. load_part issues entries [LO, HI); a chunk's loads go out in three parts
+    // between the state pass's products (issued in one piece they stalled the wave for about half
+    // of each chunk's time).
+    static constexpr int NLD = 3 * NF + NA + 1 + ND;
+    template <typename L, int LO, int HI>
+    __device__ __forceinline__ void load_part(const float* sc, const TO* dO_, int64_t orow, int nrows_, int j0, int dv) {
+        if (LO == 0) nrows = nrows_;
+#pragma unroll
+        for (int i = LO; i < (HI < NLD ? HI : NLD); ++i) {
+            if (i < 3 * NF) {
+                const int u = i % NF, f = i / NF;
+                const int off = blk_row(u) * DK + blk_col(u);
+                const f32x4 x = *reinterpret_cast<const f32x4*>(sc + (f == 0 ? L::KB : (f == 1 ? L::QT : L::W)) + off);
+                if (f == 0) kb[u] = x; else if (f == 1) qt[u] = x; else w[u] = x;
+            } else if (i < 3 * NF + NA) {
+                const int u = i - 3 * NF;
+                aqk[u] = *reinterpret_cast<const f32x4*>(sc + L::AQK + blk_row(u) * kC + blk_col(u));
+            } else if (i == 3 * NF + NA) {
+                if ((int)threadIdx.x < DK / 4) gam = *reinterpret_cast<const f32x4*>(sc + L::GAM + threadIdx.x * 4);
+            } else {
+                // rows past the end read the last row (no branch, so no wait); they are zeroed when
+                // the raw values go to LDS, so nothing here waits for the loads to land
+                const int u = i - (3 * NF + NA + 1);
+                const int e = threadIdx.x + u * kT, t = e / NB, j = e % NB, tr = t < nrows_ ? t : nrows_ - 1;
+                dO[u] = dO_[(orow + tr) * dv + j0 + j];
+            }
+        }
+    }
     template <typename L>
-    __device__ __forceinline__ void load(const float* sc, const TO* dO_, int64_t orow, int nrows, int j0, int dv) {
-        this->nrows = nrows;
-#pragma unroll
-        for (int u = 0; u < NF; ++u) {
-            const int off = blk_row(u) * DK + blk_col(u);
-            kb[u] = *reinterpret_cast<const f32x4*>(sc + L::KB + off);
-            qt[u] = *reinterpret_cast<const f32x4*>(sc + L::QT + off);
-            w[u] = *reinterpret_cast<const f32x4*>(sc + L::W + off);
-        }
-#pragma unroll
-        for (int u = 0; u < NA; ++u)
-            aqk[u] = *reinterpret_cast<const f32x4*>(sc + L::AQK + blk_row(u) * kC + blk_col(u));
-        if ((int)threadIdx.x < DK / 4) gam = *reinterpret_cast<const f32x4*>(sc + L::GAM + threadIdx.x * 4);
-#pragma unroll
-        for (int u = 0; u < ND; ++u) {
-            // rows past the end read the last row (no branch, so no wait); they are zeroed when
-            // the raw values go to LDS, so nothing here waits for the loads to land
-            const int e = threadIdx.x + u * kT, t = e / NB, j = e % NB, tr = t < nrows ? t : nrows - 1;
-            dO[u] = dO_[(orow + tr) * dv + j0 + j];
-        }
+    __device__ __forceinline__ void load(const float* sc, const TO* dO_, int64_t orow, int nrows_, int j0, int dv) {
+        load_part<L, 0, NLD>(sc, dO_, orow, nrows_, j0, dv);
     }
 
     template <typename SS>
@@ -527,9 +538,12 @@ __global__ __launch_bounds__(kT) void bwd_state_kernel(BwdArgs a) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
                     gst[(gr0 + 16 * rt + 4 * lg + i) * DV + j0 + 16 * ct + lr] = gx[rt][ct][i];
-        if (c > 0)   // the next chunk's operands travel while this one computes
-            f.template load<L>(a.prep + (lane * a.nchunks + c - 1) * L::PREP, dO, lane * a.T + (c - 1) * kC,
-                               chunk_rows(c - 1), j0, DV);
+        // the next chunk's operands travel while this one computes, in three parts
+        constexpr int P1 = F::NLD / 3, P2 = 2 * F::NLD / 3;
+        const float* nsc = a.prep + (lane * a.nchunks + c - 1) * L::PREP;
+        const int64_t norow = lane * a.T + (c - 1) * kC;
+        const int nrows_next = c > 0 ? chunk_rows(c - 1) : 1;
+        if (c > 0) f.template load_part<L, 0, P1>(nsc, dO, norow, nrows_next, j0, DV);
         lds_barrier();
         // dV~ rows 16 wv .. 16 wv + 15 = K- Gx + A_qk^T dO (A_qk^T[t][s] = 0 for s < t)
         {
@@ -557,6 +571,7 @@ __global__ __launch_bounds__(kT) void bwd_state_kernel(BwdArgs a) {
 #pragma unroll
                     for (int ct = 0; ct < CT; ++ct) dv[ct] = mfma4(x[q], y[ct][q], dv[ct]);
             }
+            if (c > 0) f.template load_part<L, P1, P2>(nsc, dO, norow, nrows_next, j0, DV);
 #pragma unroll
             for (int ct = 0; ct < CT; ++ct) {
                 *reinterpret_cast<f32x4*>(&sm.dVT[16 * ct + lr][t0 + 4 * lg]) = dv[ct];
@@ -595,6 +610,7 @@ __global__ __launch_bounds__(kT) void bwd_state_kernel(BwdArgs a) {
                     for (int ct = 0; ct < CT; ++ct) gx[rt][ct] = mfma4(xw[rt][q], v[ct][q], gx[rt][ct]);
                 }
         }
+        if (c > 0) f.template load_part<L, P2, F::NLD>(nsc, dO, norow, nrows_next, j0, DV);
         put_gxt();   // nothing reads Gx^T between the dV~ products above and the next chunk's
     }
     if (a.dS0)
