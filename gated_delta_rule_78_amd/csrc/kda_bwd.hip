@@ -1120,9 +1120,15 @@ __global__ __launch_bounds__(kTG) void bwd_grad_kernel(BwdArgs a) {
         }
     }
     lds_barrier();
-    // dG into LDS over Q, dgamma's share on row 63, then the reverse cumsum per channel
+    // dG into LDS over Q, dgamma's share on row 63, then the reverse cumsum per channel. dq and dk
+    // go to LDS too (over K and G: this thread's own row and channels, which only it has read),
+    // so that all three leave in whole rows below.
 #pragma unroll
-    for (int u = 0; u < CG; ++u) sQ[t * LK + c0 + u] = dG[u] + (t == kC - 1 ? dlgam[c0 + u] : 0.f);
+    for (int u = 0; u < CG; ++u) {
+        sQ[t * LK + c0 + u] = dG[u] + (t == kC - 1 ? dlgam[c0 + u] : 0.f);
+        sK[t * LK + c0 + u] = dq[u];
+        sG[t * LK + c0 + u] = dk[u];
+    }
     lds_barrier();
     for (int ch = tid; ch < DK; ch += kTG) {
         float acc = 0.f;
@@ -1131,15 +1137,19 @@ __global__ __launch_bounds__(kTG) void bwd_grad_kernel(BwdArgs a) {
     lds_barrier();
 #pragma unroll
     for (int m = 1; m < NGR; m <<= 1) dbeta += __shfl_xor(dbeta, m);
-    if (t < nrows) {
-        const int64_t r = row0 + t;
+    if (t < nrows && gi == 0) a.dbeta[row0 + t] = dbeta + sdb[t];
+    // dq, dk, dlog_alpha row by row: consecutive lanes write consecutive channels, so every store
+    // instruction covers whole rows (thread-per-(row, channel group) stores scattered 4-byte words
+    // over 8 rows and took about a fifth of the kernel's time)
 #pragma unroll
-        for (int u = 0; u < CG; ++u) {
-            a.dq[r * DK + c0 + u] = dq[u];
-            a.dk_[r * DK + c0 + u] = dk[u];
-            a.dla[r * DK + c0 + u] = sQ[t * LK + c0 + u];
+    for (int v = 0; v < kC * DK / kTG; ++v) {
+        const int f = tid + kTG * v, r = f / DK, ch = f % DK;
+        if (r < nrows) {
+            const int64_t o = (row0 + r) * DK + ch;
+            a.dq[o] = sK[r * LK + ch];
+            a.dk_[o] = sG[r * LK + ch];
+            a.dla[o] = sQ[r * LK + ch];
         }
-        if (gi == 0) a.dbeta[r] = dbeta + sdb[t];
     }
 }
 
