@@ -5,10 +5,10 @@
 // Every chunk of every lane is independent. A persistent grid of two workgroups (4 waves each) per
 // compute unit walks the record slots (the chunks of every lane; for a packed batch of
 // variable-length sequences, the chunk slots of every head, which a small table maps to rows),
-// loading the next chunk's raw rows into registers
-// while it solves the current one (and while the other workgroup on the compute unit runs), so
-// the kernel is bound by HBM traffic, not by latency. Input
-// loads are row-contiguous (64 bytes per row per wave). Output: the chunk's record
+// loading the next chunk's raw rows into registers while it solves the current one (and while
+// the other workgroup on the compute unit runs). A chunk still costs a workgroup about 8 us, most
+// of it dependent-instruction and LDS latency, of which the two workgroups per compute unit (the
+// LDS budget) hide part. Input loads are row-contiguous (64 bytes per row per wave). Output: the chunk's record
 // (kda_record.h) in the workspace. Steps, with G = cumsum(log alpha) over the chunk's rows:
 //   1. per wave, 32 key channels: G^T = g^T U (U[s][t] = (s <= t)) on the MFMA. Decay factors are
 //      taken against reference points so that none exceeds e^80 over the whole domain
