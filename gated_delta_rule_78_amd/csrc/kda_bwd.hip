@@ -211,44 +211,25 @@ __global__ __launch_bounds__(kTP) void bwd_prep_kernel(BwdArgs a) {
     }
     lds_barrier();
 
-    // A_kk (i > j, beta-scaled) and A_qk (i >= j) by 16 x 16 blocks. A diagonal block forms the
-    // factors exp(G_i - G_j) pair by pair; an off-diagonal block (I > J) splits them at r = 16 I,
-    // the first row of block I, as exp(G_i - G_r) exp(G_r - G_j), both <= 1 since j < r <= i
-    // (so the whole decay domain stays in range), and runs on the fp32 MFMA with the factors
-    // folded into its operands.
-    {   // diagonal blocks: thread = (row i, columns jd and jd + 1 of its block)
-        const int i = tid >> 3, jd = (i & ~15) + 2 * (tid & 7);
-        float akk[2] = {0.f, 0.f}, aqk[2] = {0.f, 0.f};
-        if (jd <= i) {
-            for (int ch = 0; ch < DK; ch += 4) {
-                const f32x4 ki = *reinterpret_cast<const f32x4*>(&sm.K[i][ch]);
-                const f32x4 qi = *reinterpret_cast<const f32x4*>(&sm.Q[i][ch]);
-                const f32x4 gi = *reinterpret_cast<const f32x4*>(&sm.G[i][ch]);
-#pragma unroll
-                for (int u = 0; u < 2; ++u) {
-                    const f32x4 kj = *reinterpret_cast<const f32x4*>(&sm.K[jd + u][ch]);
-                    const f32x4 gj = *reinterpret_cast<const f32x4*>(&sm.G[jd + u][ch]);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const float f = kj[e] * fexp(gi[e] - gj[e]);   // jd + 1 > i: never stored
-                        akk[u] += ki[e] * f;
-                        aqk[u] += qi[e] * f;
-                    }
-                }
-            }
-        }
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int j = jd + u;
-            sm.A[i][j] = j < i ? sm.beta[i] * akk[u] : 0.f;
-            sc[L::AQK + i * kC + j] = j <= i ? aqk[u] : 0.f;
-        }
-        for (int j = (i & ~15) + 16 + (tid & 7); j < kC; j += 8) sc[L::AQK + i * kC + j] = 0.f;   // above
+    // A_kk (i > j, beta-scaled) and A_qk (i >= j) by 16 x 16 blocks (I, J), I >= J, each on the fp32
+    // MFMA with the factors exp(G_i - G_j) split at r = 16 I, the first row of block I, as
+    // exp(G_i - G_r) exp(G_r - G_j) and folded into the operands. Off the diagonal both factors are
+    // <= 1 (j < r <= i), so the whole decay domain stays in range; on a diagonal block the second
+    // is at most e^{15 * 5} (the per-step bound of the decay), still inside the fp32 range.
+    {   // A_qk above the diagonal blocks is zero: thread = (row i, every 8th column from the next block)
+        const int i = tid >> 3;
+        for (int j = (i & ~15) + 16 + (tid & 7); j < kC; j += 8) sc[L::AQK + i * kC + j] = 0.f;
     }
-    {   // off-diagonal blocks (I, J), I > J: one per wave for waves 0 .. 5
+    {   // 16 x 16 blocks (I, J), I >= J, on the fp32 MFMA: the six off-diagonal blocks on waves 0 .. 5,
+        // the four diagonal blocks two each on waves 6 and 7. Inside a diagonal block the second
+        // factor exp(G_r - G_j) is >= 1 but at most e^{15 * 5}, far inside the fp32 range; the
+        // entries above the diagonal (whose product is not bounded) are masked out.
         const int wv = tid >> 6, lr = tid & 15, lg = (tid >> 4) & 3;
-        if (wv < 6) {
-            const int I = wv < 1 ? 1 : (wv < 3 ? 2 : 3), J = wv - (I * (I - 1)) / 2;
+        const int njobs = wv < 6 ? 1 : 2;
+        for (int jn = 0; jn < njobs; ++jn) {
+            int I, J;
+            if (wv < 6) { I = wv < 1 ? 1 : (wv < 3 ? 2 : 3); J = wv - (I * (I - 1)) / 2; }
+            else { I = 2 * (wv - 6) + jn; J = I; }
             const int r = 16 * I, ia = r + lr, jb = 16 * J + lr;
             f32x4 ckk = kZero4f(), cqk = kZero4f();
             for (int kb = 0; kb < DK; kb += 16) {
@@ -269,8 +250,8 @@ __global__ __launch_bounds__(kTP) void bwd_prep_kernel(BwdArgs a) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int row = r + 4 * lg + e, col = 16 * J + lr;
-                sm.A[row][col] = sm.beta[row] * ckk[e];
-                sc[L::AQK + row * kC + col] = cqk[e];
+                sm.A[row][col] = col < row ? sm.beta[row] * ckk[e] : 0.f;   // always true off the diagonal
+                sc[L::AQK + row * kC + col] = col <= row ? cqk[e] : 0.f;
             }
         }
     }

@@ -67,6 +67,12 @@ def test_bwd_full_decay_domain():
     run_bwd("bwd full decay", 1, 2, 192, 128, 128, la_range=(-5.0, 0.0), seed=7300)
 
 
+def test_bwd_strongest_decay_everywhere():
+    """log_alpha = -5 on every channel and step (the contract's bound): inside a diagonal 16-token
+    block the prep kernel's split decay factors then reach e^-75 and e^75."""
+    run_bwd("bwd log_alpha = -5", 1, 2, 192, 128, 128, la_range=(-5.0, -5.0), seed=7350)
+
+
 def test_bwd_many_lanes():
     """64 lanes: the reverse state pass takes blocks of 32 value columns here (it narrows them to
     16 when there are too few lanes to fill the GPU, as in the other cases)."""
