@@ -941,7 +941,7 @@ __global__ __launch_bounds__(kTG) void bwd_grad_kernel(BwdArgs a) {
         for (int tt = 0; tt < kC; ++tt) { acc += sG[tt * LK + ch]; sG[tt * LK + ch] = acc; }
     }
     lds_barrier();
-    float dq[CG], dk[CG], dG[CG], gt[CG], kt[CG], qt[CG];
+    float dq[CG], dk[CG], dG[CG];
     float dbeta = 0.f;
     const float bt = beta[t];
 #pragma unroll
@@ -952,7 +952,6 @@ __global__ __launch_bounds__(kTG) void bwd_grad_kernel(BwdArgs a) {
         const f32x4 l4 = *reinterpret_cast<const f32x4*>(sG + (kC - 1) * LK + c0 + u);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            gt[u + e] = g4[e]; kt[u + e] = k4[e]; qt[u + e] = q4[e];
             const float eg = fexp(g4[e]);
             const float kbf = fexp(l4[e] - g4[e]);   // K- = K kbf
             dq[u + e] = accQ[u + e] * eg;
@@ -966,80 +965,47 @@ __global__ __launch_bounds__(kTG) void bwd_grad_kernel(BwdArgs a) {
     //   row sums     rq = sum_{j<=t} A_qk[t][j] K_j E_tj,   rk = sum_{j<t} A_kk[t][j] K_j E_tj
     //   column sums  cc = sum_{i>=t} (A_qk[i][t] Q_i + beta_i A_kk[i][t] K_i) E_it
     // then dq += rq, dk += beta_t rk + cc, dG += Q_t rq + beta_t K_t rk - K_t cc and
-    // dbeta += K_t . rk. Pairs in the same 16-row block: per thread, pair by pair below. Pairs in
-    // different blocks: fp32 MFMA further down, with E split at a block boundary r between them,
-    // exp(G_i - G_r) exp(G_r - G_j), both <= 1.
-    float rq[CG], rk[CG], cc[CG];
-#pragma unroll
-    for (int u = 0; u < CG; ++u) { rq[u] = 0.f; rk[u] = 0.f; cc[u] = 0.f; }
-    for (int j = t & ~15; j <= t; ++j) {
-        const float aq = sAqk[t * LA + j], ak = sAkk[t * LA + j];
-#pragma unroll
-        for (int u = 0; u < CG; u += 4) {
-            const f32x4 g4 = *reinterpret_cast<const f32x4*>(sG + j * LK + c0 + u);
-            const f32x4 k4 = *reinterpret_cast<const f32x4*>(sK + j * LK + c0 + u);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float kj = k4[e] * fexp(gt[u + e] - g4[e]);
-                rq[u + e] += aq * kj;
-                rk[u + e] += ak * kj;
-            }
-        }
-    }
-    for (int i = t; i <= (t | 15); ++i) {
-        const float aq = sAqk[i * LA + t], bak = beta[i] * sAkk[i * LA + t];
-#pragma unroll
-        for (int u = 0; u < CG; u += 4) {
-            const f32x4 g4 = *reinterpret_cast<const f32x4*>(sG + i * LK + c0 + u);
-            const f32x4 k4 = *reinterpret_cast<const f32x4*>(sK + i * LK + c0 + u);
-            const f32x4 q4 = *reinterpret_cast<const f32x4*>(sQ + i * LK + c0 + u);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) cc[u + e] += (aq * q4[e] + bak * k4[e]) * fexp(g4[e] - gt[u + e]);
-        }
-    }
-#pragma unroll
-    for (int u = 0; u < CG; ++u) {
-        dq[u] += rq[u];
-        dk[u] += bt * rk[u] + cc[u];
-        dG[u] += qt[u] * rq[u] + kt[u] * (bt * rk[u] - cc[u]);
-        dbeta += kt[u] * rk[u];
-    }
-    {   // pairs in different blocks. Wave w takes channel tile ct (16 channels, column lr of its
-        // tiles); with DK = 128 every wave does both kinds of job, with DK = 64 waves 0-3 the row
-        // blocks and 4-7 the column blocks.
-        //   rows of block I = 1..3, r = 16 I:  [Rq | Rk] = exp(G_i - G_r) (A[I rows, j < r] Khat_r),
+    // dbeta += K_t . rk, all by 16-row blocks on the fp32 MFMA below.
+    {   // By 16-row blocks, with E split at a reference row r. Wave w takes channel tile ct (16
+        // channels, column lr of its tiles); with DK = 128 every wave does both kinds of job, with
+        // DK = 64 waves 0-3 the row blocks and 4-7 the column blocks.
+        //   rows of block I = 0..3, r = 16 I:  [Rq | Rk] = exp(G_i - G_r) (A[I rows, j < r + 16] Khat_r),
         //                                      Khat_r[j] = K_j exp(G_r - G_j)
-        //   rows of block J = 0..2, r = 16 (J + 1):
+        //   rows of block J = 0..2, r = 16 (J + 1), the later blocks:
         //       Cc = exp(G_r - G_t) (A_qk[i >= r, t]^T Qchk_r + (beta A_kk)[i >= r, t]^T Kchk_r),
         //       Qchk_r[i] = Q_i exp(G_i - G_r), Kchk_r[i] = K_i exp(G_i - G_r)
+        //   rows of block J = 0..3, r = 16 J, the block itself: the same with i in [r, r + 16).
+        // Off the diagonal both factors are <= 1. Inside a diagonal block one of them is >= 1 but at
+        // most e^{15 * 5}; the entries of A above the diagonal, whose products it does not bound,
+        // are zero in LDS.
         constexpr int NCTc = DK / 16;
         const bool rows_job = NCTc == 8 || wv < 4, cols_job = NCTc == 8 || wv >= 4;
         const int ch = 16 * (wv % NCTc) + lr;
-        f32x4 mrq[3], mrk[3], mcc[3];
+        f32x4 mrq[4], mrk[4], mcc[3], mcd[4];
 #pragma unroll
-        for (int I = 1; I <= 3; ++I) {
-            mrq[I - 1] = kZero4f();
-            mrk[I - 1] = kZero4f();
+        for (int I = 0; I <= 3; ++I) {
+            mrq[I] = kZero4f();
+            mrk[I] = kZero4f();
             if (!rows_job) continue;
             const int r = 16 * I;
             const float gr = sG[r * LK + ch];
 #pragma unroll 1
-            for (int kb = 0; kb < r; kb += 16) {
+            for (int kb = 0; kb <= r; kb += 16) {
                 const f32x4 xq = *reinterpret_cast<const f32x4*>(sAqk + (r + lr) * LA + kb + 4 * lg);
                 const f32x4 xk = *reinterpret_cast<const f32x4*>(sAkk + (r + lr) * LA + kb + 4 * lg);
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     const int j = kb + 4 * lg + q;
                     const float bj = sK[j * LK + ch] * fexp(gr - sG[j * LK + ch]);
-                    mrq[I - 1] = mfma4(xq[q], bj, mrq[I - 1]);
-                    mrk[I - 1] = mfma4(xk[q], bj, mrk[I - 1]);
+                    mrq[I] = mfma4(xq[q], bj, mrq[I]);
+                    mrk[I] = mfma4(xk[q], bj, mrk[I]);
                 }
             }
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const float f = fexp(sG[(r + 4 * lg + e) * LK + ch] - gr);
-                mrq[I - 1][e] *= f;
-                mrk[I - 1][e] *= f;
+                mrq[I][e] *= f;
+                mrk[I][e] *= f;
             }
         }
 #pragma unroll
@@ -1061,6 +1027,22 @@ __global__ __launch_bounds__(kTG) void bwd_grad_kernel(BwdArgs a) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) mcc[J][e] *= fexp(gr - sG[(16 * J + 4 * lg + e) * LK + ch]);
         }
+#pragma unroll
+        for (int J = 0; J <= 3; ++J) {   // the diagonal blocks of the column sums
+            mcd[J] = kZero4f();
+            if (!cols_job) continue;
+            const int r = 16 * J, tc = r + lr;
+            const float gr = sG[r * LK + ch];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int i = r + 4 * lg + q;
+                const float f = fexp(sG[i * LK + ch] - gr);
+                mcd[J] = mfma4(sAqk[i * LA + tc], sQ[i * LK + ch] * f, mcd[J]);
+                mcd[J] = mfma4(beta[i] * sAkk[i * LA + tc], sK[i * LK + ch] * f, mcd[J]);
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) mcd[J][e] *= fexp(gr - sG[(r + 4 * lg + e) * LK + ch]);
+        }
         // this thread's K_t and Q_t again (not kept in registers across the jobs above)
         float kt2[CG], qt2[CG];
 #pragma unroll
@@ -1072,25 +1054,25 @@ __global__ __launch_bounds__(kTG) void bwd_grad_kernel(BwdArgs a) {
         }
         lds_barrier();   // every read of K, Q, G is done: they take the block results
 #pragma unroll
-        for (int I = 1; I <= 3; ++I)
+        for (int I = 0; I <= 3; ++I)
             if (rows_job)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    sK[(16 * I + 4 * lg + e) * LK + ch] = mrq[I - 1][e];
-                    sG[(16 * I + 4 * lg + e) * LK + ch] = mrk[I - 1][e];
+                    sK[(16 * I + 4 * lg + e) * LK + ch] = mrq[I][e];
+                    sG[(16 * I + 4 * lg + e) * LK + ch] = mrk[I][e];
                 }
 #pragma unroll
-        for (int J = 0; J <= 2; ++J)
+        for (int J = 0; J <= 3; ++J)
             if (cols_job)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) sQ[(16 * J + 4 * lg + e) * LK + ch] = mcc[J][e];
+                for (int e = 0; e < 4; ++e) sQ[(16 * J + 4 * lg + e) * LK + ch] = (J <= 2 ? mcc[J][e] : 0.f) + mcd[J][e];
         lds_barrier();
-        // the same combination for the block results of this thread's row
+        // the block results of this thread's row: rq, rk and cc of its 16 channels
 #pragma unroll
         for (int u = 0; u < CG; u += 4) {
-            const f32x4 x = t >= 16 ? *reinterpret_cast<const f32x4*>(sK + t * LK + c0 + u) : kZero4f();
-            const f32x4 y = t >= 16 ? *reinterpret_cast<const f32x4*>(sG + t * LK + c0 + u) : kZero4f();
-            const f32x4 z = t < 48 ? *reinterpret_cast<const f32x4*>(sQ + t * LK + c0 + u) : kZero4f();
+            const f32x4 x = *reinterpret_cast<const f32x4*>(sK + t * LK + c0 + u);
+            const f32x4 y = *reinterpret_cast<const f32x4*>(sG + t * LK + c0 + u);
+            const f32x4 z = *reinterpret_cast<const f32x4*>(sQ + t * LK + c0 + u);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 dq[u + e] += x[e];
