@@ -958,8 +958,18 @@ __global__ __launch_bounds__(kTG) void bwd_grad_kernel(BwdArgs a) {
             dk[u + e] = accK[u + e] * kbf + bt * xk[u + e] * eg;
             dG[u + e] = accQ[u + e] * q4[e] * eg - accK[u + e] * k4[e] * kbf + bt * xk[u + e] * k4[e] * eg;
             dbeta += xk[u + e] * k4[e] * eg;
-            atomicAdd(&dlgam[c0 + u + e], accK[u + e] * k4[e] * kbf);
+            accK[u + e] *= k4[e] * kbf;   // accK is not needed past this point: it becomes dK- K-
         }
+    }
+    // sum of dK- K- down the rows into dlgam: first over the wave's 8 rows (lanes 8 apart), then one
+    // LDS atomic per channel and wave (an atomic per thread and channel put 64 rows on one address)
+#pragma unroll
+    for (int u = 0; u < CG; ++u) {
+        float v = accK[u];
+        v += __shfl_xor(v, 8);
+        v += __shfl_xor(v, 16);
+        v += __shfl_xor(v, 32);
+        if ((tid & 63) < NGR) atomicAdd(&dlgam[c0 + u], v);
     }
     // pairwise terms, per channel c (E_ij = exp(G_i - G_j), i >= j):
     //   row sums     rq = sum_{j<=t} A_qk[t][j] K_j E_tj,   rk = sum_{j<t} A_kk[t][j] K_j E_tj
