@@ -103,6 +103,22 @@ def test_bf16_8k_workload_all_heads():
     run_and_check("bf16 8k", w.B, w.H, w.T, w.d, w.d, w.dtype)
 
 
+def test_bf16_8k_launch_slow_decay_sampled_heads():
+    """The 8K launch (H=32, T=8192, the plan's own segment count: 8 per lane) under slow decay,
+    log_alpha ~ U[-0.02, 0], with a carried state. With the workload's decay range every affine
+    pair M underflows to zero after a segment; here the entry states reach across all eight
+    segments, so the segment scan's products decide the result. Four heads checked end to end."""
+    w = synth.PREFILL_BF16_8K
+    say("8k launch slow decay: B=%d H=%d T=%d" % (w.B, w.H, w.T))
+    q, k, v, la, beta, S0 = synth.prefill_inputs(w.B, w.H, w.T, w.d, w.d, w.dtype, device=DEV, seed_base=4700,
+                                                 s0_std=0.3, log_alpha_range=(-0.02, 0.0))
+    o, S_T = kda.chunk_fwd(q, k, v, la, beta, S0)
+    torch.cuda.synchronize()
+    heads = [0, 9, 22, 31]
+    o_ref, S_ref = oracle_prefill(q, k, v, la, beta, S0, lanes=heads)
+    assert_close("8k slow decay", BF16, host32(o[0, heads]), o_ref, host32(S_T[0, heads]), S_ref)
+
+
 def test_prefix_64k_workload_sampled_lanes():
     """B=4, H=32, T=65536 with S0 ~ N(0, 0.02): the full launch; 6 lanes checked end to end."""
     w = synth.PREFILL_BF16_PREFIX_64K
