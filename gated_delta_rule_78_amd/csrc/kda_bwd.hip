@@ -356,20 +356,22 @@ __global__ __launch_bounds__(kTP) void bwd_prep_kernel(BwdArgs a) {
 // (16x16x4 MFMA). Per chunk, walking backwards:
 //     dV~ = K- Gx + A_qk^T dO                     (64 x NB; wave w owns rows 16w .. 16w + 15)
 //     Gx  <- Diag(gamma) Gx + Q~^T dO - W^T dV~   (DK x NB; wave w owns rows DK/4 w ..)
-// Gx lives in the waves' accumulator registers for the whole pass. Every MFMA operand sits in LDS
-// with the contraction index contiguous (K- as is; Q~, W, A_qk, dO and dV~ transposed while
-// staged or stored), so a lane fetches its next four k values of an operand in one 16-byte read.
-// In a 16x16x4 step lane l = r + 16 g supplies row (or column) r at k = g; the k values a lane
-// walks through are assigned as kb + 4 g + q for step q of a block of 16, the same on both sides.
+// Gx lives in the waves' accumulator registers for the whole pass. K-, dO and dV~ sit in LDS with
+// the contraction index contiguous (dO and dV~ transposed while staged or stored), so a lane
+// fetches its next four k values in one 16-byte read; Q~, -W and A_qk stay in their row-major
+// layout, where the contraction index is the row, and a lane reads its four values one by one
+// (consecutive lanes take consecutive columns). In a 16x16x4 step lane l = r + 16 g supplies row
+// (or column) r at k = g; the k values a lane walks through are assigned as kb + 4 g + q for step
+// q of a block of 16, the same on both sides.
 // The chunk before the current one is loaded into registers while the current one computes; the
 // barriers order LDS only, so that load stays in flight across them.
 template <int DK, int NB>
 struct __align__(16) StateSmem {
     static constexpr int LK = DK + 4, LS = kC + 4;
     float KB[kC][LK];     // K- [t][ch]
-    float QTT[DK][LS];    // Q~^T [ch][s]
-    float WTN[DK][LS];    // -W^T [ch][s]
-    float AQT[kC][LS];    // A_qk^T [t][s]
+    float QT[kC][LK];     // Q~ [s][ch]
+    float WN[kC][LK];     // -W [s][ch]
+    float AQ[kC][LS];     // A_qk [s][t]
     float dOT[NB][LS];    // dO^T [j][s]
     float dVT[NB][LS];    // dV~^T [j][s]
     float GxT[NB][LK];    // Gx^T [j][ch]
@@ -377,9 +379,11 @@ struct __align__(16) StateSmem {
 };
 
 // one thread's share of a chunk's state-pass operands, held in registers between the global load
-// and the LDS store. A [64][n] factor is read in blocks of 16 rows x 16 columns, one block per
-// wave and instruction: lane l takes row 16 (b mod 4) + (l mod 16) and the four columns from
-// 16 (b / 4) + 4 (l / 16), so the transposed LDS stores of a half-wave fall in distinct banks.
+// and the LDS store. Each factor is read as one contiguous array: float4 number tid + 256 u, so a
+// wave's load instruction covers 1 KiB of whole cache lines, and the LDS stores keep the layout
+// (16-byte stores, no transposition). Reading the factors in 16 x 16 blocks instead (half cache
+// lines per row, for transposed LDS stores) made the loads costlier to issue: 8K backward
+// 2.272-2.278 ms against 2.224-2.231 ms.
 template <int DK, typename TO, int NB>
 struct StateFetch {
     static constexpr int NF = kC * DK / 4 / kT;   // float4s of one [64][DK] factor
@@ -390,9 +394,6 @@ struct StateFetch {
     f32x4 gam;
     TO dO[ND];     // raw, converted when stored to LDS
     int nrows;
-
-    static __device__ __forceinline__ int blk_row(int u) { return 16 * (((threadIdx.x >> 6) + 4 * u) & 3) + (threadIdx.x & 15); }
-    static __device__ __forceinline__ int blk_col(int u) { return 16 * (((threadIdx.x >> 6) + 4 * u) >> 2) + 4 * ((threadIdx.x >> 4) & 3); }
 
     // The loads of one chunk as a flat list: [0, NF) K-, [NF, 2NF) Q~, [2NF, 3NF) W, then A_qk,
     // gamma and dO. load_part issues entries [LO, HI); a chunk's loads go out in three parts
@@ -406,12 +407,12 @@ struct StateFetch {
         for (int i = LO; i < (HI < NLD ? HI : NLD); ++i) {
             if (i < 3 * NF) {
                 const int u = i % NF, f = i / NF;
-                const int off = blk_row(u) * DK + blk_col(u);
+                const int off = 4 * ((int)threadIdx.x + kT * u);
                 const f32x4 x = *reinterpret_cast<const f32x4*>(sc + (f == 0 ? L::KB : (f == 1 ? L::QT : L::W)) + off);
                 if (f == 0) kb[u] = x; else if (f == 1) qt[u] = x; else w[u] = x;
             } else if (i < 3 * NF + NA) {
                 const int u = i - 3 * NF;
-                aqk[u] = *reinterpret_cast<const f32x4*>(sc + L::AQK + blk_row(u) * kC + blk_col(u));
+                aqk[u] = *reinterpret_cast<const f32x4*>(sc + L::AQK + 4 * ((int)threadIdx.x + kT * u));
             } else if (i == 3 * NF + NA) {
                 if ((int)threadIdx.x < DK / 4) gam = *reinterpret_cast<const f32x4*>(sc + L::GAM + threadIdx.x * 4);
             } else {
@@ -432,19 +433,15 @@ struct StateFetch {
     __device__ __forceinline__ void store(SS& sm) const {
 #pragma unroll
         for (int u = 0; u < NF; ++u) {
-            const int r = blk_row(u), c = blk_col(u);
+            const int e = (int)threadIdx.x + kT * u, r = e / (DK / 4), c = 4 * (e % (DK / 4));
             *reinterpret_cast<f32x4*>(&sm.KB[r][c]) = kb[u];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                sm.QTT[c + i][r] = qt[u][i];
-                sm.WTN[c + i][r] = -w[u][i];
-            }
+            *reinterpret_cast<f32x4*>(&sm.QT[r][c]) = qt[u];
+            *reinterpret_cast<f32x4*>(&sm.WN[r][c]) = -w[u];
         }
 #pragma unroll
         for (int u = 0; u < NA; ++u) {
-            const int r = blk_row(u), c = blk_col(u);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) sm.AQT[c + i][r] = aqk[u][i];
+            const int e = (int)threadIdx.x + kT * u;
+            *reinterpret_cast<f32x4*>(&sm.AQ[e / (kC / 4)][4 * (e % (kC / 4))]) = aqk[u];
         }
         if ((int)threadIdx.x < DK / 4) *reinterpret_cast<f32x4*>(&sm.gam[threadIdx.x * 4]) = gam;
 #pragma unroll
@@ -519,8 +516,10 @@ __global__ __launch_bounds__(kT) void bwd_state_kernel(BwdArgs a) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
                     gst[(gr0 + 16 * rt + 4 * lg + i) * DV + j0 + 16 * ct + lr] = gx[rt][ct][i];
-        // the next chunk's operands travel while this one computes, in three parts
-        constexpr int P1 = F::NLD / 3, P2 = 2 * F::NLD / 3;
+        // the next chunk's operands travel while this one computes, in three parts: a quarter before
+        // barrier B, a quarter after the dV~ products, half after the Gx products (8K backward:
+        // 2.195 ms; thirds 2.224, an eighth / eighth / rest 2.293, nothing / quarter / rest 2.263)
+        constexpr int P1 = F::NLD / 4, P2 = F::NLD / 2;
         const float* nsc = a.prep + (lane * a.nchunks + c - 1) * L::PREP;
         const int64_t norow = lane * a.T + (c - 1) * kC;
         const int nrows_next = c > 0 ? chunk_rows(c - 1) : 1;
@@ -543,7 +542,9 @@ __global__ __launch_bounds__(kT) void bwd_state_kernel(BwdArgs a) {
                     for (int ct = 0; ct < CT; ++ct) dv[ct] = mfma4(x[q], y[ct][q], dv[ct]);
             }
             for (int kb = t0; kb < kC; kb += 16) {
-                const f32x4 x = *reinterpret_cast<const f32x4*>(&sm.AQT[t0 + lr][kb + 4 * lg]);
+                f32x4 x;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) x[q] = sm.AQ[kb + 4 * lg + q][t0 + lr];
                 f32x4 y[CT];
 #pragma unroll
                 for (int ct = 0; ct < CT; ++ct) y[ct] = *reinterpret_cast<const f32x4*>(&sm.dOT[16 * ct + lr][kb + 4 * lg]);
@@ -572,8 +573,11 @@ __global__ __launch_bounds__(kT) void bwd_state_kernel(BwdArgs a) {
             f32x4 xq[RT], xw[RT];
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt) {
-                xq[rt] = *reinterpret_cast<const f32x4*>(&sm.QTT[gr0 + 16 * rt + lr][kb + 4 * lg]);
-                xw[rt] = *reinterpret_cast<const f32x4*>(&sm.WTN[gr0 + 16 * rt + lr][kb + 4 * lg]);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    xq[rt][q] = sm.QT[kb + 4 * lg + q][gr0 + 16 * rt + lr];
+                    xw[rt][q] = sm.WN[kb + 4 * lg + q][gr0 + 16 * rt + lr];
+                }
             }
             f32x4 o[CT], v[CT];
 #pragma unroll
