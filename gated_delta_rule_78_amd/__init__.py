@@ -11,6 +11,7 @@ library is missing or fails, the call raises.
     chunk_bwd(q, k, v, log_alpha, beta, S0, dO, dS_T) -> grads    backward of chunkwise prefill
     decode_step(q, k, v, log_alpha, beta, S) -> o                 one token, S updated in place
 """
+import contextlib
 import ctypes
 import os
 
@@ -101,6 +102,37 @@ def _stream(device, stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def _alloc_on(stream):
+    """Context in which the binding allocates outputs and workspace: the caller's ``stream`` when
+    one is given, so that the caching allocator ties those blocks to the stream the kernels run
+    on (a block freed on return is then reused only behind them), else a no-op."""
+    return torch.cuda.stream(stream) if stream is not None else contextlib.nullcontext()
+
+
+def _check_device(fn, dev):
+    if dev.type != "cuda":
+        raise ValueError("%s runs on the GPU; got a tensor on %s" % (fn, dev))
+
+
+def _check_workspace(workspace, dev):
+    """A caller's workspace must be a contiguous tensor on ``dev``: a wrong device or a strided view
+    is a ValueError here, not an out-of-range access in the kernels."""
+    if workspace is not None and (workspace.device != dev or not workspace.is_contiguous()):
+        raise ValueError("workspace must be a contiguous tensor on %s (got %s, contiguous=%s)"
+                         % (dev, workspace.device, workspace.is_contiguous()))
+
+
+def _workspace(need, workspace, dev):
+    """The caller's (checked) workspace when it holds ``need`` bytes, else a new one."""
+    if workspace is not None and workspace.numel() * workspace.element_size() >= need:
+        return workspace
+    return torch.empty(need, device=dev, dtype=torch.uint8) if need else workspace
+
+
+def _nbytes(t):
+    return 0 if t is None else t.numel() * t.element_size()
+
+
 def _check(fn, status):
     if status != 0:
         raise KDAError(fn, status, library().kda_status_string(status).decode())
@@ -128,35 +160,40 @@ def chunk_fwd(q, k, v, log_alpha, beta, S0=None, *, out_dtype=None, segments=0, 
 
     q, k, log_alpha: [B,H,T,dk]; v: [B,H,T,dv]; beta: [B,H,T] (all bf16 or all fp32);
     S0: [B,H,dk,dv] fp32 or None. Returns (o [B,H,T,dv], S_T [B,H,dk,dv] fp32 or None).
+    Caller-supplied o, S_T (may be S0) and workspace are checked like the inputs. Outputs and
+    workspace the binding allocates are allocated on ``stream`` (default: the current stream).
     """
     dev = q.device
-    if dev.type != "cuda":
-        raise ValueError("chunk_fwd runs on the GPU; got a tensor on %s" % dev)
     B, H, T, dk = q.shape
     dv = v.shape[-1]
     dt = q.dtype
     if dt not in _DTYPES:
         raise ValueError("unsupported input dtype %s" % dt)
     out_dtype = out_dtype or dt
+    if out_dtype not in _DTYPES:
+        raise ValueError("unsupported output dtype %s" % out_dtype)
     for name, t, shape in (("q", q, (B, H, T, dk)), ("k", k, (B, H, T, dk)), ("log_alpha", log_alpha, (B, H, T, dk)),
                            ("v", v, (B, H, T, dv)), ("beta", beta, (B, H, T))):
         _check_tensor(name, t, dev, dt, shape)
     if S0 is not None:
         _check_tensor("S0", S0, dev, torch.float32, (B, H, dk, dv))
-    if o is None:
-        o = torch.empty(B, H, T, dv, device=dev, dtype=out_dtype)
-    else:
+    if o is not None:
         _check_tensor("o", o, dev, out_dtype, (B, H, T, dv))
-    if S_T is None and store_state:
-        S_T = torch.empty(B, H, dk, dv, device=dev, dtype=torch.float32)
+    if S_T is not None:
+        _check_tensor("S_T", S_T, dev, torch.float32, (B, H, dk, dv))
+    _check_workspace(workspace, dev)
+    _check_device("chunk_fwd", dev)
     desc = _chunk_desc(q, v, segments, out_dtype)
     lib = library()
     need = int(lib.kda_chunk_fwd_workspace_bytes(ctypes.byref(desc)))
-    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
-        workspace = torch.empty(need, device=dev, dtype=torch.uint8)
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = lib.kda_chunk_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S0),
-                           _ptr(o), _ptr(S_T), _ptr(workspace), ws_bytes, _stream(dev, stream))
+    with _alloc_on(stream):
+        if o is None:
+            o = torch.empty(B, H, T, dv, device=dev, dtype=out_dtype)
+        if S_T is None and store_state:
+            S_T = torch.empty(B, H, dk, dv, device=dev, dtype=torch.float32)
+        workspace = _workspace(need, workspace, dev)
+        st = lib.kda_chunk_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S0),
+                               _ptr(o), _ptr(S_T), _ptr(workspace), _nbytes(workspace), _stream(dev, stream))
     _check("kda_chunk_fwd", st)
     return o, S_T
 
@@ -202,20 +239,22 @@ def chunk_fwd_varlen(q, k, v, log_alpha, beta, cu_seqlens=None, S0=None, *, max_
     Equal lengths (``cu_seqlens`` None): tensors [N,H,T,...] as ``chunk_fwd``.
     S0, S_T: [N,H,dk,dv] fp32. With ``ckpt_every`` = E > 0, the state after every E tokens of each
     sequence goes to S_ckpt[ckpt_offsets[s] + j - 1, h] (S_ckpt: [K, H, dk, dv] fp32 with
-    K = T // E packed or N * (T // E) otherwise) and ckpt_offsets (int32 [N+1]) is written.
+    K >= T // E packed or N * (T // E) otherwise) and ckpt_offsets (int32 [N+1]) is written.
     Returns (o, S_T, S_ckpt, ckpt_offsets); the last two are None when E = 0. S_ckpt is returned
-    at its capacity K; its first ckpt_offsets[N] entries are written (the count is only known on
-    the device, and reading it would synchronise).
+    at its capacity T // E (packed) or N * (T // E); its first ckpt_offsets[N] entries are written
+    (the count is only known on the device, and reading it would synchronise).
     Fused prologue: with ``z`` (shape of log_alpha, which may then be None) and ``A_log`` [H] fp32,
     the log decay is g_min * sigmoid(exp(A_log[h]) * z). Fused epilogue: with ``gate`` (shape of
     v), o receives sigmoid(gate) * norm_weight * o / sqrt(mean(o^2) + eps).
+    Caller-supplied outputs and workspace are checked like the inputs; the ones the binding
+    allocates are allocated on ``stream``.
     """
     dev = q.device
-    if dev.type != "cuda":
-        raise ValueError("chunk_fwd_varlen runs on the GPU; got a tensor on %s" % dev)
     if q.dtype != torch.bfloat16:
         raise ValueError("chunk_fwd_varlen takes bf16 inputs (got %s)" % q.dtype)
     out_dtype = out_dtype or q.dtype
+    if out_dtype not in _DTYPES:
+        raise ValueError("unsupported output dtype %s" % out_dtype)
     packed = cu_seqlens is not None
     dk, dv = q.shape[-1], v.shape[-1]
     if packed:
@@ -240,28 +279,40 @@ def chunk_fwd_varlen(q, k, v, log_alpha, beta, cu_seqlens=None, S0=None, *, max_
     gating = _gating(dev, H, dv, torch.bfloat16, lead, z, A_log, g_min, gate, norm_weight, eps)
     if S0 is not None:
         _check_tensor("S0", S0, dev, torch.float32, slead + (dk, dv))
-    if o is None:
-        o = torch.empty(lead + (dv,), device=dev, dtype=out_dtype)
-    else:
+    if o is not None:
         _check_tensor("o", o, dev, out_dtype, lead + (dv,))
-    if S_T is None and store_state:
-        S_T = torch.empty(slead + (dk, dv), device=dev, dtype=torch.float32)
+    if S_T is not None:
+        _check_tensor("S_T", S_T, dev, torch.float32, slead + (dk, dv))
     if ckpt_every:
-        if S_ckpt is None:
-            S_ckpt = torch.empty(max(n_ck, 1), H, dk, dv, device=dev, dtype=torch.float32)
-        if ckpt_offsets is None:
-            ckpt_offsets = torch.empty(N + 1, device=dev, dtype=torch.int32)
+        if S_ckpt is not None:
+            if (S_ckpt.device != dev or S_ckpt.dtype != torch.float32 or not S_ckpt.is_contiguous()
+                    or S_ckpt.dim() != 4 or tuple(S_ckpt.shape[1:]) != (H, dk, dv) or S_ckpt.shape[0] < n_ck):
+                raise ValueError("S_ckpt must be a contiguous float32 tensor [K, %d, %d, %d] with K >= %d on %s "
+                                 "(got %s %s %s)" % (H, dk, dv, n_ck, dev, S_ckpt.dtype, tuple(S_ckpt.shape),
+                                                     S_ckpt.device))
+        if ckpt_offsets is not None:
+            _check_tensor("ckpt_offsets", ckpt_offsets, dev, torch.int32, (N + 1,))
+    _check_workspace(workspace, dev)
+    _check_device("chunk_fwd_varlen", dev)
     desc = _varlen_desc(N, H, T, max_len, dk, dv, out_dtype, segments, ckpt_every, packed)
     lib = library()
     need = int(lib.kda_chunk_fwd_varlen_workspace_bytes(ctypes.byref(desc)))
-    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
-        workspace = torch.empty(need, device=dev, dtype=torch.uint8)
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = lib.kda_chunk_fwd_varlen(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
-                                  _ptr(cu_seqlens), _ptr(S0), _ptr(o), _ptr(S_T),
-                                  _ptr(S_ckpt if ckpt_every else None), _ptr(ckpt_offsets if ckpt_every else None),
-                                  None if gating is None else ctypes.byref(gating),
-                                  _ptr(workspace), ws_bytes, _stream(dev, stream))
+    with _alloc_on(stream):
+        if o is None:
+            o = torch.empty(lead + (dv,), device=dev, dtype=out_dtype)
+        if S_T is None and store_state:
+            S_T = torch.empty(slead + (dk, dv), device=dev, dtype=torch.float32)
+        if ckpt_every:
+            if S_ckpt is None:
+                S_ckpt = torch.empty(max(n_ck, 1), H, dk, dv, device=dev, dtype=torch.float32)
+            if ckpt_offsets is None:
+                ckpt_offsets = torch.empty(N + 1, device=dev, dtype=torch.int32)
+        workspace = _workspace(need, workspace, dev)
+        st = lib.kda_chunk_fwd_varlen(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
+                                      _ptr(cu_seqlens), _ptr(S0), _ptr(o), _ptr(S_T),
+                                      _ptr(S_ckpt if ckpt_every else None), _ptr(ckpt_offsets if ckpt_every else None),
+                                      None if gating is None else ctypes.byref(gating),
+                                      _ptr(workspace), _nbytes(workspace), _stream(dev, stream))
     _check("kda_chunk_fwd_varlen", st)
     if not ckpt_every:
         return o, S_T, None, None
@@ -277,10 +328,9 @@ def chunk_bwd(q, k, v, log_alpha, beta, S0, dO, dS_T=None, *, segments=0, worksp
     """Backward of chunkwise prefill through ``kda_chunk_bwd`` (bf16 inputs).
 
     Inputs as ``chunk_fwd``; dO [B,H,T,dv] (bf16 or fp32: the forward's output type), dS_T
-    [B,H,dk,dv] fp32 or None. Returns fp32 (dq, dk, dv, dlog_alpha, dbeta, dS0)."""
+    [B,H,dk,dv] fp32 or None. Returns fp32 (dq, dk, dv, dlog_alpha, dbeta, dS0), allocated on
+    ``stream``."""
     dev = q.device
-    if dev.type != "cuda":
-        raise ValueError("chunk_bwd runs on the GPU; got a tensor on %s" % dev)
     B, H, T, dk = q.shape
     dv = v.shape[-1]
     if q.dtype != torch.bfloat16:
@@ -295,20 +345,21 @@ def chunk_bwd(q, k, v, log_alpha, beta, S0, dO, dS_T=None, *, segments=0, worksp
     _check_tensor("dO", dO, dev, dO.dtype, (B, H, T, dv))
     if dS_T is not None:
         _check_tensor("dS_T", dS_T, dev, torch.float32, (B, H, dk, dv))
-    f32 = dict(device=dev, dtype=torch.float32)
-    dq, dk_, dla = (torch.empty(B, H, T, dk, **f32) for _ in range(3))
-    dv_ = torch.empty(B, H, T, dv, **f32)
-    dbeta = torch.empty(B, H, T, **f32)
-    dS0 = torch.empty(B, H, dk, dv, **f32)
+    _check_workspace(workspace, dev)
+    _check_device("chunk_bwd", dev)
     desc = _chunk_desc(q, v, segments, dO.dtype)
     lib = library()
     need = int(lib.kda_chunk_bwd_workspace_bytes(ctypes.byref(desc)))
-    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
-        workspace = torch.empty(need, device=dev, dtype=torch.uint8)
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = lib.kda_chunk_bwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S0),
-                           _ptr(dO), _ptr(dS_T), _ptr(dq), _ptr(dk_), _ptr(dv_), _ptr(dla), _ptr(dbeta), _ptr(dS0),
-                           _ptr(workspace), ws_bytes, _stream(dev, stream))
+    f32 = dict(device=dev, dtype=torch.float32)
+    with _alloc_on(stream):
+        dq, dk_, dla = (torch.empty(B, H, T, dk, **f32) for _ in range(3))
+        dv_ = torch.empty(B, H, T, dv, **f32)
+        dbeta = torch.empty(B, H, T, **f32)
+        dS0 = torch.empty(B, H, dk, dv, **f32)
+        workspace = _workspace(need, workspace, dev)
+        st = lib.kda_chunk_bwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S0),
+                               _ptr(dO), _ptr(dS_T), _ptr(dq), _ptr(dk_), _ptr(dv_), _ptr(dla), _ptr(dbeta), _ptr(dS0),
+                               _ptr(workspace), _nbytes(workspace), _stream(dev, stream))
     _check("kda_chunk_bwd", st)
     return dq, dk_, dv_, dla, dbeta, dS0
 
@@ -317,17 +368,18 @@ def decode_step(q, k, v, log_alpha, beta, S, *, out_dtype=None, o=None, z=None, 
                 norm_weight=None, eps=1e-6, stream=None):
     """One KDA decode step through ``kda_decode_step``; S ([N,H,dk,dv] fp32) is updated in place.
 
-    q, k, log_alpha: [N,H,dk]; v: [N,H,dv]; beta: [N,H]. Returns o [N,H,dv]. With ``z`` or
-    ``gate``, the fused prologue / epilogue of ``chunk_fwd_varlen`` (``kda_decode_step_gated``)."""
+    q, k, log_alpha: [N,H,dk]; v: [N,H,dv]; beta: [N,H]. Returns o [N,H,dv] (allocated on ``stream``
+    when not given). With ``z`` or ``gate``, the fused prologue / epilogue of ``chunk_fwd_varlen``
+    (``kda_decode_step_gated``)."""
     dev = q.device
-    if dev.type != "cuda":
-        raise ValueError("decode_step runs on the GPU; got a tensor on %s" % dev)
     N, H, dk = q.shape
     dv = v.shape[-1]
     dt = q.dtype
     if dt not in _DTYPES:
         raise ValueError("unsupported input dtype %s" % dt)
     out_dtype = out_dtype or dt
+    if out_dtype not in _DTYPES:
+        raise ValueError("unsupported output dtype %s" % out_dtype)
     for name, t, shape in (("q", q, (N, H, dk)), ("k", k, (N, H, dk)), ("log_alpha", log_alpha, (N, H, dk)),
                            ("v", v, (N, H, dv)), ("beta", beta, (N, H))):
         if t is None and name == "log_alpha" and z is not None:
@@ -335,18 +387,21 @@ def decode_step(q, k, v, log_alpha, beta, S, *, out_dtype=None, o=None, z=None, 
         _check_tensor(name, t, dev, dt, shape)
     gating = _gating(dev, H, dv, dt, (N, H), z, A_log, g_min, gate, norm_weight, eps)
     _check_tensor("S", S, dev, torch.float32, (N, H, dk, dv))
-    if o is None:
-        o = torch.empty(N, H, dv, device=dev, dtype=out_dtype)
-    else:
+    if o is not None:
         _check_tensor("o", o, dev, out_dtype, (N, H, dv))
+    _check_device("decode_step", dev)
     desc = DecodeDesc(N, H, dk, dv, _DTYPES[dt], _DTYPES[out_dtype])
-    if gating is None:
-        st = library().kda_decode_step(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
-                                       _ptr(S), _ptr(o), _stream(dev, stream))
-        _check("kda_decode_step", st)
-    else:
-        st = library().kda_decode_step_gated(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha),
-                                             _ptr(beta), ctypes.byref(gating), _ptr(S), _ptr(o),
-                                             _stream(dev, stream))
-        _check("kda_decode_step_gated", st)
+    with _alloc_on(stream):
+        if o is None:
+            o = torch.empty(N, H, dv, device=dev, dtype=out_dtype)
+        if gating is None:
+            st = library().kda_decode_step(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
+                                           _ptr(S), _ptr(o), _stream(dev, stream))
+            fn = "kda_decode_step"
+        else:
+            st = library().kda_decode_step_gated(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha),
+                                                 _ptr(beta), ctypes.byref(gating), _ptr(S), _ptr(o),
+                                                 _stream(dev, stream))
+            fn = "kda_decode_step_gated"
+    _check(fn, st)
     return o

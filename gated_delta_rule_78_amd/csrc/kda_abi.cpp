@@ -200,8 +200,9 @@ kda_status kda_chunk_fwd(const kda_chunk_desc* d, const void* q, const void* k, 
     const Range rin[] = {range_of(q, lanes * d->T * d->dk * ein), range_of(k, lanes * d->T * d->dk * ein),
                          range_of(v, lanes * d->T * d->dv * ein), range_of(log_alpha, lanes * d->T * d->dk * ein),
                          range_of(beta, lanes * d->T * ein)};
+    const Range rst = range_of(S_T, S_T ? state_bytes : 0);
     for (const Range& r : rin)
-        if (overlaps(ro, r)) return KDA_ERR_INVALID_ARG;
+        if (overlaps(ro, r) || overlaps(rst, r)) return KDA_ERR_INVALID_ARG;
     if (S0 && overlaps(ro, range_of(S0, state_bytes))) return KDA_ERR_INVALID_ARG;
     if (S_T && overlaps(ro, range_of(S_T, state_bytes))) return KDA_ERR_INVALID_ARG;
 
@@ -299,7 +300,7 @@ kda_status kda_chunk_fwd_varlen(const kda_varlen_desc* d, const void* q, const v
                          range_of(z ? gating->A_log : nullptr, z ? d->H * 4 : 0),
                          range_of(gate ? gating->norm_weight : nullptr, gate && gating->norm_weight ? d->dv * 4 : 0)};
     for (const Range& r : rin)
-        if (overlaps(ro, r) || overlaps(rck, r) || overlaps(rcko, r)) return KDA_ERR_INVALID_ARG;
+        if (overlaps(ro, r) || overlaps(rck, r) || overlaps(rcko, r) || overlaps(rst, r)) return KDA_ERR_INVALID_ARG;
     if (overlaps(ro, rs0) || overlaps(ro, rst) || overlaps(ro, rck) || overlaps(ro, rcko)) return KDA_ERR_INVALID_ARG;
 
     if (!workspace || workspace_bytes < plan.ws_bytes) return KDA_ERR_WORKSPACE;
@@ -361,8 +362,12 @@ kda_status kda_chunk_bwd(const kda_chunk_desc* d, const void* q, const void* k, 
     }
     if (!q || !k || !v || !log_alpha || !beta || !dO || !dq || !dk || !dv || !dlog_alpha || !dbeta)
         return KDA_ERR_INVALID_ARG;
-    const void* ins[] = {q, k, v, log_alpha, dO, dq, dk, dv, dlog_alpha, dbeta};
+    // the forward recompute reads q, k, v, log_alpha with the 16-byte loads kda_chunk_fwd needs
+    const void* ins[] = {q, k, v, log_alpha, dO};
     for (const void* p : ins)
+        if (!aligned(p, 16)) return KDA_ERR_INVALID_ARG;
+    const void* outs[] = {dq, dk, dv, dlog_alpha, dbeta};
+    for (const void* p : outs)
         if (!aligned(p, 4)) return KDA_ERR_INVALID_ARG;
     if (!aligned(beta, 2)) return KDA_ERR_INVALID_ARG;
     const int64_t nk = lanes * d->T * d->dk, nv = lanes * d->T * d->dv, nt = lanes * d->T;

@@ -629,7 +629,12 @@ struct GradArena {
                          P3_END = P3_G + kC * LK;
     static constexpr int SMALL = (P1_END > P2B_END ? (P1_END > P3_END ? P1_END : P3_END)
                                                    : (P2B_END > P3_END ? P2B_END : P3_END));
-    static constexpr int BETA = SMALL, DLGAM = BETA + kC, DB = DLGAM + DK, TOTAL = DB + kC;
+    // BETA: beta per row; DLGAM: gamma dgamma per channel; DB: dX_V . V per row from each of the
+    // two waves that share a row block (summed in that order); DLP: each wave's sum of dK- K- over
+    // its 8 rows per channel (summed in wave order). Fixed-order sums: the gradients are the same
+    // bit for bit from run to run.
+    static constexpr int BETA = SMALL, DLGAM = BETA + kC, DB = DLGAM + DK, DLP = DB + 2 * kC,
+                         TOTAL = DLP + (kTG / 64) * DK;
     static_assert(P2A_END <= TOTAL && TOTAL * 4 <= 160 * 1024, "arena fits the LDS of a CU");
 };
 
@@ -645,8 +650,9 @@ __global__ __launch_bounds__(kTG) void bwd_grad_kernel(BwdArgs a) {
     extern __shared__ __align__(16) unsigned char smem_raw[];
     float* ar = reinterpret_cast<float*>(smem_raw);
     float* beta = ar + A::BETA;
-    float* dlgam = ar + A::DLGAM;     // gamma dgamma + sum_t dK-_t K-_t (joins row 63 of dG)
-    float* sdb = ar + A::DB;          // dX_V . V per row (joins dbeta)
+    float* dlgam = ar + A::DLGAM;     // gamma dgamma per channel (joins row 63 of dG)
+    float* sdb = ar + A::DB;          // [2][kC] dX_V . V per row, by column half (joins dbeta)
+    float* dlp = ar + A::DLP;         // [waves][DK] per-wave sums of dK- K- (join row 63 of dG)
     const int64_t lane = blockIdx.x / a.nchunks, c = blockIdx.x % a.nchunks;
     const int64_t row0 = lane * a.T + c * kC;
     const int nrows = (int)(a.T - c * kC < kC ? a.T - c * kC : kC);
@@ -824,7 +830,6 @@ __global__ __launch_bounds__(kTG) void bwd_grad_kernel(BwdArgs a) {
     tdv2.store_t(sdVT, LA);
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) *reinterpret_cast<f32x4*>(sdWT + (cm + 16 * ct + lr) * LA + t0 + 4 * lg) = -mw[ct];
-    if (tid < kC) sdb[tid] = 0.f;
     lds_barrier();
     F32Tile<kC, DK, kTG> tw2;
     F32Tile<kC, DV, kTG> tu;
@@ -850,7 +855,8 @@ __global__ __launch_bounds__(kTG) void bwd_grad_kernel(BwdArgs a) {
             for (int ct = 0; ct < NXV; ++ct) mxv[ct] = mfma4(x[q], yv[ct][q], mxv[ct]);
         }
     }
-    {   // dv = beta dX_V; dbeta gets dX_V . V (row sums over the 16 lanes of a tile, then LDS)
+    {   // dv = beta dX_V; dbeta gets dX_V . V (row sums over the 16 lanes of a tile, then one LDS
+        // slot per row and column half: waves w and w + 4 share rows t0 .. t0 + 15)
         float pb[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ct = 0; ct < NXV; ++ct)
@@ -866,7 +872,7 @@ __global__ __launch_bounds__(kTG) void bwd_grad_kernel(BwdArgs a) {
         for (int i = 0; i < 4; ++i) {
 #pragma unroll
             for (int m = 1; m < 16; m <<= 1) pb[i] += __shfl_xor(pb[i], m);
-            if (lr == 0) atomicAdd(&sdb[t0 + 4 * lg + i], pb[i]);
+            if (lr == 0) sdb[(wv >> 2) * kC + t0 + 4 * lg + i] = pb[i];
         }
     }
     lds_barrier();   // T^T, dW^T, dV~^T are done; the dA_kk operands take their place
@@ -965,15 +971,16 @@ __global__ __launch_bounds__(kTG) void bwd_grad_kernel(BwdArgs a) {
             accK[u + e] *= k4[e] * kbf;   // accK is not needed past this point: it becomes dK- K-
         }
     }
-    // sum of dK- K- down the rows into dlgam: first over the wave's 8 rows (lanes 8 apart), then one
-    // LDS atomic per channel and wave (an atomic per thread and channel put 64 rows on one address)
+    // sum of dK- K- down the rows: over the wave's 8 rows (lanes 8 apart) here, into the wave's
+    // own LDS slot per channel; the eight wave sums are added in wave order where row 63 of dG
+    // takes them
 #pragma unroll
     for (int u = 0; u < CG; ++u) {
         float v = accK[u];
         v += __shfl_xor(v, 8);
         v += __shfl_xor(v, 16);
         v += __shfl_xor(v, 32);
-        if ((tid & 63) < NGR) atomicAdd(&dlgam[c0 + u], v);
+        if ((tid & 63) < NGR) dlp[wv * DK + c0 + u] = v;
     }
     // pairwise terms, per channel c (E_ij = exp(G_i - G_j), i >= j):
     //   row sums     rq = sum_{j<=t} A_qk[t][j] K_j E_tj,   rk = sum_{j<t} A_kk[t][j] K_j E_tj
@@ -1102,7 +1109,13 @@ __global__ __launch_bounds__(kTG) void bwd_grad_kernel(BwdArgs a) {
     // so that all three leave in whole rows below.
 #pragma unroll
     for (int u = 0; u < CG; ++u) {
-        sQ[t * LK + c0 + u] = dG[u] + (t == kC - 1 ? dlgam[c0 + u] : 0.f);
+        float last = 0.f;   // row 63: gamma dgamma + sum_t dK-_t K-_t, in a fixed order
+        if (t == kC - 1) {
+            last = dlgam[c0 + u];
+#pragma unroll
+            for (int w = 0; w < kTG / 64; ++w) last += dlp[w * DK + c0 + u];
+        }
+        sQ[t * LK + c0 + u] = dG[u] + last;
         sK[t * LK + c0 + u] = dq[u];
         sG[t * LK + c0 + u] = dk[u];
     }
@@ -1114,7 +1127,7 @@ __global__ __launch_bounds__(kTG) void bwd_grad_kernel(BwdArgs a) {
     lds_barrier();
 #pragma unroll
     for (int m = 1; m < NGR; m <<= 1) dbeta += __shfl_xor(dbeta, m);
-    if (t < nrows && gi == 0) a.dbeta[row0 + t] = dbeta + sdb[t];
+    if (t < nrows && gi == 0) a.dbeta[row0 + t] = dbeta + (sdb[t] + sdb[kC + t]);
     // dq, dk, dlog_alpha row by row: consecutive lanes write consecutive channels, so every store
     // instruction covers whole rows (thread-per-(row, channel group) stores scattered 4-byte words
     // over 8 rows and took about a fifth of the kernel's time)

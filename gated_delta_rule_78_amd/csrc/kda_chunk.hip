@@ -1,5 +1,6 @@
-// KDA chunkwise prefill for gfx950: generic fused chunk loop (used for fp32 inputs), segment
-// scan, state copy. bf16 inputs use the register-resident kernel in kda_prefill_bf16.hip.
+// KDA chunkwise prefill for gfx950, fp32 inputs (dk = 64): one fused chunk loop per (lane, block of
+// value columns) on the fp32 MFMA, and the state copy used by T = 0 calls. bf16 inputs take the
+// two-kernel path instead (intra-chunk records in kda_intra.hip, state pass in kda_inter.hip).
 //
 // Mathematics (Kimi K3 reading notes, liuzhao09.github.io/papers/kimi-k3.html, section 2.2,
 // chunk equations; the pieces the page leaves unprinted are derived by unrolling the
@@ -10,13 +11,10 @@
 //   V~ = (I + A_kk)^{-1} Diag(beta) (V - K~ S)          (= U - W S of the UT transform)
 //   O  = Q~ S + A_qk V~
 //   S' = Diag(gamma_C) S + K-bar^T V~
-// Section 2.5 (affine pair): a run of chunks maps S_in to S~ + M S_in. SUMMARY blocks run
-// the same loop on the augmented state [S~ | M], entry [0 | I], with zero values for the M
-// columns; a scan composes the pairs into exact entry states; FINISH blocks rerun each segment
-// from its exact entry state and write o.
+// The fp32 path is planned without a sequence split: each workgroup walks all chunks of its lane.
 //
 // Work decomposition. Value columns are independent given the key-side quantities, so a
-// workgroup owns a lane (b,h), a segment of chunks and NW*16 state columns; each wave owns 16
+// workgroup owns a lane (b,h) and NW*16 state columns; each wave owns 16
 // of those columns (its slice of S lives in MFMA accumulators, fp32) and a 1/NW share of the
 // key channels for the per-chunk key-side preparation. Per chunk:
 //   A  (wave-local) load rows of q,k,log_alpha,v (prefetched one chunk ahead), cumulative
@@ -78,38 +76,18 @@ __global__ __launch_bounds__(NW * 64) void chunk_kernel(ChunkLaunch p) {
     const int W = NW * 16;
     const int64_t DV = p.dv;
 
-    // ---- which lane / segment / column block this workgroup owns -------------------------
+    // ---- which lane and column block this workgroup owns ---------------------------------
     int64_t bid = blockIdx.x;
     const int64_t nblk = gridDim.x;
     if ((nblk & 7) == 0) bid = (bid & 7) * (nblk >> 3) + (bid >> 3);  // siblings share an XCD
-    const int ncb_fin = (int)(DV / W);
-    const int ncb_sum = (int)((DV + DK) / W);
-    const int64_t n_fin = p.lanes * p.fin_nseg * ncb_fin;
-    bool summary;
-    int cb, seg;
-    int64_t lane;
-    if (bid < n_fin) {
-        summary = false;
-        cb = (int)(bid % ncb_fin);
-        const int64_t r = bid / ncb_fin;
-        seg = p.fin_seg_lo + (int)(r % p.fin_nseg);
-        lane = r / p.fin_nseg;
-    } else {
-        summary = true;
-        const int64_t b2 = bid - n_fin;
-        cb = (int)(b2 % ncb_sum);
-        const int64_t r = b2 / ncb_sum;
-        seg = p.sum_seg_lo + (int)(r % p.sum_nseg);
-        lane = r / p.sum_nseg;
-    }
+    const int ncb = (int)(DV / W);
+    const int cb = (int)(bid % ncb);
+    const int64_t lane = bid / ncb;
     const int64_t T = p.T;
-    const int64_t nchunks = (T + kC - 1) / kC;
-    const int64_t c_begin = (int64_t)seg * p.chunks_per_seg;
-    const int64_t c_end = c_begin + p.chunks_per_seg < nchunks ? c_begin + p.chunks_per_seg : nchunks;
+    const int64_t c_begin = 0;
+    const int64_t c_end = (T + kC - 1) / kC;
 
     const int col0 = cb * W + 16 * w;                  // first column of this wave
-    const bool m_cols = summary && col0 >= DV;         // identity-started M columns
-    const bool has_v = !m_cols;
     const int ch0 = w * CPW;                           // first key channel this wave prepares
 
     const TIn* qg = (const TIn*)p.q + lane * T * DK;
@@ -121,11 +99,7 @@ __global__ __launch_bounds__(NW * 64) void chunk_kernel(ChunkLaunch p) {
     // ---- entry state into accumulators and into the wave's S^T operand tile ---------------
     f32x4 Sacc[NM];
     {
-        const float* entry = nullptr;
-        if (!summary) {
-            if (seg > 0) entry = p.ws_entry + ((lane * p.nseg + seg) * DK) * DV;
-            else if (p.S0) entry = p.S0 + lane * DK * DV;
-        }
+        const float* entry = p.S0 ? p.S0 + lane * DK * DV : nullptr;
         if (entry) {
             // all loads issued together, one wait
             const float* e = entry + col0 + l16;
@@ -134,11 +108,8 @@ __global__ __launch_bounds__(NW * 64) void chunk_kernel(ChunkLaunch p) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) Sacc[M][r] = e[(int64_t)(16 * M + 4 * lq + r) * DV];
         } else {
-            const int diag = m_cols ? col0 - (int)DV + l16 : -1;  // identity columns of M
 #pragma unroll
-            for (int M = 0; M < NM; ++M)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) Sacc[M][r] = (16 * M + 4 * lq + r == diag) ? 1.f : 0.f;
+            for (int M = 0; M < NM; ++M) Sacc[M] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
 #pragma unroll
         for (int M = 0; M < NM; ++M)
@@ -165,7 +136,7 @@ __global__ __launch_bounds__(NW * 64) void chunk_kernel(ChunkLaunch p) {
         }
 #pragma unroll
         for (int i = 0; i < NVV; ++i)
-            pv[i] = (ok && has_v) ? *reinterpret_cast<const uint4*>(vg + row * DV + col0 + i * EPV)
+            pv[i] = ok ? *reinterpret_cast<const uint4*>(vg + row * DV + col0 + i * EPV)
                                   : make_uint4(0, 0, 0, 0);
         if (w == 0) pb = ok ? ld_f(bg + row) : 0.f;
     };
@@ -238,10 +209,8 @@ __global__ __launch_bounds__(NW * 64) void chunk_kernel(ChunkLaunch p) {
             for (int I = 0; I < 4; ++I) {
                 const auto a = Op::load32(&sm.k[(16 * I + l16) * LDK + 32 * ks + 8 * lq]);
                 Y[I] = Op::mma32(a, sf, Y[I]);
-                if (!summary) {
-                    const auto b = Op::load32(&sm.q[(16 * I + l16) * LDK + 32 * ks + 8 * lq]);
-                    Ot[I] = Op::mma32(sf, b, Ot[I]);
-                }
+                const auto b = Op::load32(&sm.q[(16 * I + l16) * LDK + 32 * ks + 8 * lq]);
+                Ot[I] = Op::mma32(sf, b, Ot[I]);
             }
         }
         if (w == 0) {
@@ -291,8 +260,8 @@ __global__ __launch_bounds__(NW * 64) void chunk_kernel(ChunkLaunch p) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) sm.td[(lq * 16 + i) * LDT + l16] = Op::cvt(tc[i]);
         } else {
-            // off-diagonal A_kk blocks (6), then A_qk blocks (10, FINISH only)
-            const int ntiles = summary ? 6 : 16;
+            // off-diagonal A_kk blocks (6), then A_qk blocks (10)
+            const int ntiles = 16;
             for (int idx = w - 1; idx < ntiles; idx += NW - 1) {
                 int I, J;
                 const bool is_kk = idx < 6;
@@ -368,7 +337,7 @@ __global__ __launch_bounds__(NW * 64) void chunk_kernel(ChunkLaunch p) {
                 wave_lds_sync();
             }
         }
-        if (!summary) {
+        {
             TOut* og = (TOut*)p.o + lane * T * DV;
 #pragma unroll
             for (int I = 0; I < 4; ++I) {
@@ -402,21 +371,12 @@ __global__ __launch_bounds__(NW * 64) void chunk_kernel(ChunkLaunch p) {
     }
 
     // ---- exit state ------------------------------------------------------------------------
-    float* dst = nullptr;
-    int64_t ld_dst = DV;
-    if (summary) {
-        dst = p.ws_pair + (lane * p.nseg + seg) * DK * (DV + DK);
-        ld_dst = DV + DK;
-    } else if (seg == p.nseg - 1) {
-        dst = p.S_T ? p.S_T + lane * DK * DV : nullptr;
-    } else if (seg == 0) {
-        dst = p.ws_entry + ((lane * p.nseg + 1) * DK) * DV;
-    }
-    if (dst) {
+    if (p.S_T) {
+        float* dst = p.S_T + lane * DK * DV;
 #pragma unroll
         for (int M = 0; M < NM; ++M)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) dst[(int64_t)(16 * M + 4 * lq + r) * ld_dst + col0 + l16] = Sacc[M][r];
+            for (int r = 0; r < 4; ++r) dst[(int64_t)(16 * M + 4 * lq + r) * DV + col0 + l16] = Sacc[M][r];
     }
 }
 
@@ -428,7 +388,7 @@ __global__ void copy_or_zero_kernel(float* dst, const float* src, int64_t n) {
 template <class Op, typename TIn, typename TOut, int DK, int NW>
 static hipError_t launch_t(const ChunkLaunch& a, hipStream_t st) {
     const int W = NW * 16;
-    const int64_t blocks = a.lanes * ((int64_t)a.fin_nseg * (a.dv / W) + (int64_t)a.sum_nseg * ((a.dv + DK) / W));
+    const int64_t blocks = a.lanes * (a.dv / W);
     if (blocks <= 0) return hipSuccess;
     hipLaunchKernelGGL((chunk_kernel<Op, TIn, TOut, DK, NW>), dim3((unsigned)blocks), dim3(NW * 64), 0, st, a);
     return hipGetLastError();

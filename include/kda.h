@@ -102,7 +102,7 @@ size_t kda_chunk_fwd_workspace_bytes(const kda_chunk_desc* desc);
  *                     may be the same pointer as S0 (in-place update), must not partially
  *                     overlap it
  *   workspace       : at least kda_chunk_fwd_workspace_bytes(desc) bytes (may be NULL if 0)
- * o must not overlap any input. T == 0 writes S_T = S0 (or zeros) and touches nothing else.
+ * Neither o nor S_T may overlap an input. T == 0 writes S_T = S0 (or zeros) and touches nothing else.
  * Source: section 2.2 (recurrence and chunk equations) and section 2.5 (affine pair,
  * in-device sequence split) of the Kimi K3 reading notes.
  */
@@ -223,6 +223,9 @@ size_t kda_chunk_bwd_workspace_bytes(const kda_chunk_desc* desc);
  *   workspace       : at least kda_chunk_bwd_workspace_bytes(desc) bytes, 256-byte aligned
  * The call recomputes the forward (with a state checkpoint after every chunk) and then runs the
  * reverse pass; gradient outputs must not overlap each other, the inputs or the workspace.
+ * q, k, v, log_alpha and dO need 16-byte aligned bases (the forward's loads), beta its element
+ * alignment, the fp32 outputs 4 bytes. Every reduction runs in a fixed order: the same inputs give
+ * the same gradients bit for bit on every call.
  * Source: the pages print no backward; section 2.2 of the Kimi K3 reading notes gives the
  * recurrence and chunk equations this differentiates, and says training uses chunkwise KDA.
  */

@@ -61,3 +61,26 @@ def assert_close(tag, dtype, o_gpu, o_ref, S_gpu=None, S_ref=None):
         ok = ok and es <= TOL_S[dtype]
     say(msg)
     assert ok, msg
+
+
+def check_lanes_streamed(tag, dtype, q, k, v, la, beta, S0, o, S_T, lanes, group=2):
+    """Oracle parity on the given flat lanes (b*H + h) of one launch, `group` lanes at a time so that
+    host memory stays bounded: every output row and the final state of each lane are compared.
+    Returns (max|o - o_ref|, max rel-L2 of S) over the lanes; asserts the tolerances."""
+    flat = lambda t: t.reshape((-1,) + tuple(t.shape[2:]))
+    fq, fk, fv, fla, fb, fo, fS = (flat(x) for x in (q, k, v, la, beta, o, S_T))
+    fS0 = None if S0 is None else flat(S0)
+    worst_o, worst_s = 0.0, 0.0
+    for i in range(0, len(lanes), group):
+        sel = list(lanes[i:i + group])
+        host = lambda t: None if t is None else t[sel].float().cpu().numpy()
+        o_ref, S_ref = native.kda_fwd(host(fq), host(fk), host(fv), host(fla), host(fb), host(fS0))
+        eo = max_abs(host(fo), o_ref)
+        es = rel_l2_per_lane(host(fS), S_ref)
+        worst_o, worst_s = max(worst_o, eo), max(worst_s, es)
+        say("%s: lanes %s max|o-o_ref| = %.3e relL2(S) = %.3e" % (tag, sel, eo, es))
+        del o_ref, S_ref
+        assert eo <= TOL_O[dtype] and es <= TOL_S[dtype], "%s: lanes %s out of tolerance" % (tag, sel)
+    say("%s: %d lanes, every row: max|o-o_ref| = %.3e (tol %.0e), max relL2(S) = %.3e (tol %.0e)"
+        % (tag, len(lanes), worst_o, TOL_O[dtype], worst_s, TOL_S[dtype]))
+    return worst_o, worst_s

@@ -226,3 +226,74 @@ def test_backward_rejects_bad_arguments(lib):
     assert call(d, base, ws_bytes=need - 1) == WORKSPACE
     assert call(d, base, ws=FAKE + (20 << 30) + 16, ws_bytes=need) == INVALID   # 256-byte alignment
     assert lib.kda_chunk_bwd_workspace_bytes(ctypes.byref(_desc(T=0))) == 0
+
+
+def test_final_state_must_not_overlap_inputs(lib):
+    """S_T is written by the state pass's last segment while other workgroups may still read the
+    inputs: an S_T range that overlaps any input is rejected (S_T == S0 stays allowed)."""
+    d = _desc(B=1, H=2, T=128)
+    need = lib.kda_chunk_fwd_workspace_bytes(ctypes.byref(d))
+    ws = FAKE + (7 << 30)
+    assert _chunk(lib, d, ST=FAKE + 256, ws=ws, ws_bytes=need) == INVALID              # S_T inside q
+    assert _chunk(lib, d, ST=FAKE + (4 << 30), ws=ws, ws_bytes=need) == INVALID        # S_T on beta
+    vd = _vdesc()
+    assert _varlen(lib, vd, ST=FAKE + (2 << 30) + 512) == INVALID                      # S_T inside v
+    assert _varlen(lib, vd, ST=FAKE + (3 << 30)) == INVALID                            # S_T on log_alpha
+
+
+def test_backward_needs_the_forward_alignment(lib):
+    """The backward reruns the forward's 16-byte loads on q, k, v, log_alpha (and reads dO the same
+    way): 4-byte aligned inputs that kda_chunk_fwd refuses are refused here too."""
+    d = _desc(B=1, H=2, T=256)
+    P = ctypes.c_void_p
+    base = [FAKE + (i << 30) for i in range(14)]
+
+    def call(ptrs):
+        return lib.kda_chunk_bwd(ctypes.byref(d), *[P(p) for p in ptrs], P(FAKE + (20 << 30)), 1 << 40, None)
+    for i in (0, 1, 2, 3, 6):   # q k v log_alpha dO
+        bad = list(base)
+        bad[i] = base[i] + 4
+        assert call(bad) == INVALID, i
+    bad = list(base)
+    bad[4] = base[4] + 1          # beta at an odd byte address
+    assert call(bad) == INVALID
+    bad = list(base)
+    bad[4] = base[4] + 2          # beta only needs its element alignment
+    assert call(bad) != INVALID
+
+
+def test_binding_checks_caller_buffers():
+    """The binding checks caller-supplied outputs and workspace like the inputs (shape, dtype,
+    contiguity) before any device work; with CPU tensors the checks run and only then the call
+    refuses to run off the GPU."""
+    import torch
+    B, H, T, d = 1, 2, 70, 64
+    bf = torch.bfloat16
+    q = torch.zeros(B, H, T, d, dtype=bf)
+    beta = torch.zeros(B, H, T, dtype=bf)
+    with pytest.raises(ValueError, match="S_T"):
+        kda.chunk_fwd(q, q, q, q, beta, S_T=torch.zeros(B, H, d, d + 1))
+    with pytest.raises(ValueError, match="S_T"):
+        kda.chunk_fwd(q, q, q, q, beta, S_T=torch.zeros(B, H, d, d, dtype=torch.float64))
+    with pytest.raises(ValueError, match="o must"):
+        kda.chunk_fwd(q, q, q, q, beta, o=torch.zeros(B, H, T, d + 2, dtype=bf)[..., :d])   # strided view
+    with pytest.raises(ValueError, match="workspace"):
+        kda.chunk_fwd(q, q, q, q, beta, workspace=torch.zeros(64, 64, dtype=torch.uint8)[:, ::2])
+    with pytest.raises(ValueError, match="runs on the GPU"):
+        kda.chunk_fwd(q, q, q, q, beta, S_T=torch.zeros(B, H, d, d))
+    # packed batch: S_ckpt with a wrong head count, ckpt_offsets with a wrong length, S_T shape
+    pq = torch.zeros(H, 256, d, dtype=bf)
+    pb = torch.zeros(H, 256, dtype=bf)
+    cu = torch.tensor([0, 100, 256], dtype=torch.int32)
+    with pytest.raises(ValueError, match="S_ckpt"):
+        kda.chunk_fwd_varlen(pq, pq, pq, pq, pb, cu, ckpt_every=64, S_ckpt=torch.zeros(4, H + 1, d, d))
+    with pytest.raises(ValueError, match="S_ckpt"):
+        kda.chunk_fwd_varlen(pq, pq, pq, pq, pb, cu, ckpt_every=64, S_ckpt=torch.zeros(2, H, d, d))
+    with pytest.raises(ValueError, match="ckpt_offsets"):
+        kda.chunk_fwd_varlen(pq, pq, pq, pq, pb, cu, ckpt_every=64, ckpt_offsets=torch.zeros(2, dtype=torch.int32))
+    with pytest.raises(ValueError, match="S_T"):
+        kda.chunk_fwd_varlen(pq, pq, pq, pq, pb, cu, S_T=torch.zeros(1, H, d, d))
+    with pytest.raises(ValueError, match="runs on the GPU"):
+        kda.chunk_fwd_varlen(pq, pq, pq, pq, pb, cu, ckpt_every=64, S_ckpt=torch.zeros(4, H, d, d))
+    with pytest.raises(ValueError, match="workspace"):
+        kda.chunk_bwd(q, q, q, q, beta, None, q, workspace=torch.zeros(8, 8, dtype=torch.uint8).t())

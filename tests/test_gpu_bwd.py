@@ -130,3 +130,22 @@ def test_bwd_empty_sequence():
     dq, dk, dv, dla, db, dS0 = kda.chunk_bwd(q, k, v, la, beta, S0, dO, dST)
     torch.cuda.synchronize()
     assert torch.equal(dS0, dST) and dq.numel() == 0
+
+
+@pytest.mark.parametrize("dk,dv", [(128, 128), (64, 64)])
+def test_bwd_run_to_run_bitwise(dk, dv):
+    """Every reduction of the backward runs in a fixed order (no float atomics): two calls on the
+    same inputs give the same gradients bit for bit, across several chunks and lanes."""
+    B, H, T = 1, 6, 64 * 9 + 13
+    say("bwd determinism: B=%d H=%d T=%d dk=%d dv=%d" % (B, H, T, dk, dv))
+    q, k, v, la, beta, S0 = synth.prefill_inputs(B, H, T, dk, dv, BF16, device=DEV, seed_base=7900 + dk,
+                                                 s0_std=0.3)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(7901)
+    dO = torch.randn(B, H, T, dv, generator=g, device=DEV).to(BF16)
+    dST = torch.randn(B, H, dk, dv, generator=g, device=DEV) * 0.1
+    a = kda.chunk_bwd(q, k, v, la, beta, S0, dO, dST)
+    b = kda.chunk_bwd(q, k, v, la, beta, S0, dO, dST)
+    torch.cuda.synchronize()
+    for name, x, y in zip(("dq", "dk", "dv", "dlog_alpha", "dbeta", "dS0"), a, b):
+        assert torch.equal(x, y), name

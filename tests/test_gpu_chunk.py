@@ -6,7 +6,8 @@ import torch
 
 import gated_delta_rule_78_amd as kda
 from gated_delta_rule_78_amd import synth
-from tests.parity import TOL_O, TOL_S, assert_close, host32, oracle_prefill, rel_l2_per_lane, say
+from tests.parity import (TOL_O, TOL_S, assert_close, check_lanes_streamed, host32, oracle_prefill,
+                          rel_l2_per_lane, say)
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0") if torch.cuda.is_available() else None
@@ -35,6 +36,12 @@ def test_fp32_small_workload():
 @pytest.mark.parametrize("T", [1, 15, 16, 17, 63, 64, 65, 127, 130, 200])
 def test_ragged_lengths_bf16(T):
     run_and_check("ragged", 1, 3, T, 128, 128, BF16, seed=2000 + T)
+
+
+def test_fp32_decay_contract_edge():
+    """fp32 path at the edge of its decay contract: log_alpha in [-1.25, -1], so a 64-token chunk's
+    per-channel sum reaches -80 and its factors e^{-G} reach e^80 (tolerance 1e-4)."""
+    run_and_check("fp32 decay edge", 1, 2, 64 * 7 + 19, 64, 64, F32, s0_std=0.3, la_range=(-1.25, -1.0), seed=2200)
 
 
 @pytest.mark.parametrize("T", [1, 65, 200])
@@ -119,34 +126,50 @@ def test_bf16_8k_launch_slow_decay_sampled_heads():
     assert_close("8k slow decay", BF16, host32(o[0, heads]), o_ref, host32(S_T[0, heads]), S_ref)
 
 
-def test_prefix_64k_workload_sampled_lanes():
-    """B=4, H=32, T=65536 with S0 ~ N(0, 0.02): the full launch; 6 lanes checked end to end."""
+def test_prefix_64k_workload_lanes():
+    """B=4, H=32, T=65536 with S0 ~ N(0, 0.02): the full launch in the library's plan; 16 lanes,
+    four of every batch index, checked on every output row and the final state."""
     w = synth.PREFILL_BF16_PREFIX_64K
     say("prefix 64k: B=%d H=%d T=%d" % (w.B, w.H, w.T))
     q, k, v, la, beta, S0 = synth.workload_inputs(w, device=DEV)
     o, S_T = kda.chunk_fwd(q, k, v, la, beta, S0)
     torch.cuda.synchronize()
-    lanes = [0, 31, 32, 77, 100, 127]
-    bh = lambda t: t.reshape((w.B * w.H,) + tuple(t.shape[2:]))[lanes]
-    o_ref, S_ref = oracle_prefill(bh(q)[:, None], bh(k)[:, None], bh(v)[:, None], bh(la)[:, None],
-                                  bh(beta)[:, None], bh(S0)[:, None])
-    assert_close("prefix 64k", BF16, host32(bh(o)), o_ref, host32(bh(S_T)), S_ref)
+    lanes = [b * w.H + h for b in range(w.B) for h in (0, 9 + 5 * b, 20 + 3 * b, 31)]
+    check_lanes_streamed("prefix 64k", BF16, q, k, v, la, beta, S0, o, S_T, lanes, group=4)
 
 
-def test_long_1m_workload_sampled():
-    """B=1, H=32, T=1,048,576 (sequence split across CUs): the full launch; two heads checked
-    (final state, and outputs on the last 2048 tokens plus 64 spread rows)."""
+def test_prefix_64k_launch_slow_decay():
+    """The 64K launch with a carried state under slow decay, log_alpha ~ U[-0.02, 0]: the entry
+    state of every segment reaches across the split. Eight lanes, two per batch index."""
+    w = synth.PREFILL_BF16_PREFIX_64K
+    say("prefix 64k slow decay: B=%d H=%d T=%d" % (w.B, w.H, w.T))
+    q, k, v, la, beta, S0 = synth.workload_inputs(w, device=DEV, seed_base=8100, log_alpha_range=(-0.02, 0.0))
+    o, S_T = kda.chunk_fwd(q, k, v, la, beta, S0)
+    torch.cuda.synchronize()
+    lanes = [b * w.H + h for b in range(w.B) for h in (3 + 7 * b, 30 - 2 * b)]
+    check_lanes_streamed("prefix 64k slow decay", BF16, q, k, v, la, beta, S0, o, S_T, lanes, group=4)
+
+
+def test_long_1m_workload_all_heads():
+    """B=1, H=32, T=1,048,576 (sequence split across CUs): the full launch; all 32 heads checked
+    on every output row and the final state, streamed two heads at a time through the oracle."""
     w = synth.PREFILL_BF16_1M
     say("long 1M: H=%d T=%d" % (w.H, w.T))
     q, k, v, la, beta, _ = synth.workload_inputs(w, device=DEV)
     o, S_T = kda.chunk_fwd(q, k, v, la, beta)
     torch.cuda.synchronize()
-    heads = [3, 30]
-    rows = sorted(set(list(range(0, w.T, w.T // 64)) + list(range(w.T - 2048, w.T))))
-    o_ref, S_ref = oracle_prefill(q[:, heads], k[:, heads], v[:, heads], la[:, heads], beta[:, heads], None,
-                                  rows=rows)
-    o_gpu = host32(o[0, heads][:, rows])
-    assert_close("long 1M", BF16, o_gpu, o_ref, host32(S_T[0, heads]), S_ref)
+    check_lanes_streamed("long 1M", BF16, q, k, v, la, beta, None, o, S_T, list(range(w.H)), group=2)
+
+
+def test_long_1m_launch_slow_decay_sampled_heads():
+    """The 1M launch under slow decay, log_alpha ~ U[-0.02, 0]: state carried across every
+    segment boundary of the split. Four heads, every row."""
+    w = synth.PREFILL_BF16_1M
+    say("long 1M slow decay: H=%d T=%d" % (w.H, w.T))
+    q, k, v, la, beta, _ = synth.workload_inputs(w, device=DEV, seed_base=8200, log_alpha_range=(-0.02, 0.0))
+    o, S_T = kda.chunk_fwd(q, k, v, la, beta)
+    torch.cuda.synchronize()
+    check_lanes_streamed("long 1M slow decay", BF16, q, k, v, la, beta, None, o, S_T, [0, 11, 22, 31], group=2)
 
 
 def test_split_resume_at_prefix_hit():
