@@ -34,10 +34,17 @@ bool overlaps(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi && a.hi > a.
 bool valid_dtype(int32_t d) { return d == KDA_F32 || d == KDA_BF16; }
 int64_t elem_bytes(int32_t d) { return d == KDA_BF16 ? 2 : 4; }
 
-Geometry fixed_geometry(const kda_chunk_desc* d) {
+// The plan (and so the workspace) depends on the compute-unit count of the device: a call plans
+// for its stream's device, a workspace query for the current device.
+int64_t current_cus() {
+    int dev = 0;
+    return kda::compute_units(hipGetDevice(&dev) == hipSuccess ? dev : 0);
+}
+
+Geometry fixed_geometry(const kda_chunk_desc* d, int64_t cus) {
     const int64_t nchunks = ceil_div(d->T, kChunk);
     return Geometry{d->B * d->H, nchunks, d->B * d->H * nchunks, d->dk, d->dv, d->in_dtype, d->segments, 0,
-                    d->B * d->H};
+                    d->B * d->H, cus};
 }
 
 kda_status check_chunk_desc(const kda_chunk_desc* d) {
@@ -108,11 +115,11 @@ kda_status check_varlen_desc(const kda_varlen_desc* d) {
 
 // Packed batch: T/64 + N record slots per head (the lengths are only known on the device).
 // Equal lengths: the fixed-length geometry with B = N.
-Geometry varlen_geometry(const kda_varlen_desc* d) {
+Geometry varlen_geometry(const kda_varlen_desc* d, int64_t cus) {
     if (!d->packed) {
         const int64_t nchunks = ceil_div(d->T, kChunk);
         return Geometry{d->N * d->H, nchunks, d->N * d->H * nchunks, d->dk, d->dv, d->in_dtype, d->segments, 0,
-                        d->N * d->H};
+                        d->N * d->H, cus};
     }
     const int64_t max_len = d->max_len < d->T ? d->max_len : d->T;
     const int64_t max_chunks = ceil_div(max_len, kChunk);
@@ -122,7 +129,7 @@ Geometry varlen_geometry(const kda_varlen_desc* d) {
     // lane (measured: 12 sequences x 32 heads, 8192 tokens, longest 2500: 0.31 ms unsplit,
     // 0.39 ms in 3 segments).
     return Geometry{d->N * d->H, max_chunks, d->H * slots, d->dk, d->dv, d->in_dtype, d->segments, slots,
-                    d->N * d->H};
+                    d->N * d->H, cus};
 }
 
 // Backward workspace, in order: the forward's own workspace (records, pairs, entries), every
@@ -133,9 +140,9 @@ struct BwdPlan {
     size_t ckpt_off, o_off, prep_off, gst_off, dvt_off, ws_bytes;
 };
 
-BwdPlan make_bwd_plan(const kda_chunk_desc* d) {
+BwdPlan make_bwd_plan(const kda_chunk_desc* d, int64_t cus) {
     BwdPlan b{};
-    b.fwd = make_plan(fixed_geometry(d));
+    b.fwd = make_plan(fixed_geometry(d, cus));
     const int64_t lanes = d->B * d->H;
     const int64_t nchunks = ceil_div(d->T, kChunk);
     const size_t chunks = (size_t)(lanes * nchunks);
@@ -169,7 +176,7 @@ const char* kda_version(void) { return "kda-gfx950 0.1.0"; }
 
 size_t kda_chunk_fwd_workspace_bytes(const kda_chunk_desc* d) {
     if (check_chunk_desc(d) != KDA_OK) return 0;
-    return make_plan(fixed_geometry(d)).ws_bytes;
+    return make_plan(fixed_geometry(d, current_cus())).ws_bytes;
 }
 
 kda_status kda_chunk_fwd(const kda_chunk_desc* d, const void* q, const void* k, const void* v,
@@ -206,7 +213,7 @@ kda_status kda_chunk_fwd(const kda_chunk_desc* d, const void* q, const void* k, 
     if (S0 && overlaps(ro, range_of(S0, state_bytes))) return KDA_ERR_INVALID_ARG;
     if (S_T && overlaps(ro, range_of(S_T, state_bytes))) return KDA_ERR_INVALID_ARG;
 
-    const Plan plan = make_plan(fixed_geometry(d));
+    const Plan plan = make_plan(fixed_geometry(d, kda::compute_units(kda::stream_device(st))));
     if (plan.ws_bytes > 0) {
         if (!workspace || workspace_bytes < plan.ws_bytes) return KDA_ERR_WORKSPACE;
         if (!aligned(workspace, 16)) return KDA_ERR_INVALID_ARG;
@@ -235,7 +242,7 @@ kda_status kda_chunk_fwd(const kda_chunk_desc* d, const void* q, const void* k, 
 
 size_t kda_chunk_fwd_varlen_workspace_bytes(const kda_varlen_desc* d) {
     if (check_varlen_desc(d) != KDA_OK) return 0;
-    return make_plan(varlen_geometry(d)).ws_bytes;
+    return make_plan(varlen_geometry(d, current_cus())).ws_bytes;
 }
 
 kda_status kda_chunk_fwd_varlen(const kda_varlen_desc* d, const void* q, const void* k, const void* v,
@@ -276,7 +283,7 @@ kda_status kda_chunk_fwd_varlen(const kda_varlen_desc* d, const void* q, const v
         if (overlaps(r, rs0) || overlaps(r, rst) || overlaps(r, rcu)) return KDA_ERR_INVALID_ARG;
     if (overlaps(rck, rcko) || overlaps(rcu, rst)) return KDA_ERR_INVALID_ARG;
 
-    const Geometry g = varlen_geometry(d);
+    const Geometry g = varlen_geometry(d, kda::compute_units(kda::stream_device(st)));
     const Plan plan = make_plan(g);
     kda::VarlenPrep vp{};
     vp.cu = cu_seqlens; vp.N = d->N; vp.rows = d->T; vp.max_len = packed ? d->max_len : d->T;
@@ -337,7 +344,7 @@ kda_status kda_chunk_fwd_varlen(const kda_varlen_desc* d, const void* q, const v
 
 size_t kda_chunk_bwd_workspace_bytes(const kda_chunk_desc* d) {
     if (check_chunk_desc(d) != KDA_OK || d->in_dtype != KDA_BF16 || d->T == 0) return 0;
-    return make_bwd_plan(d).ws_bytes;
+    return make_bwd_plan(d, current_cus()).ws_bytes;
 }
 
 kda_status kda_chunk_bwd(const kda_chunk_desc* d, const void* q, const void* k, const void* v,
@@ -381,7 +388,7 @@ kda_status kda_chunk_bwd(const kda_chunk_desc* d, const void* q, const void* k, 
         for (int j = i + 1; j < 6; ++j)
             if (overlaps(rout[i], rout[j])) return KDA_ERR_INVALID_ARG;
     }
-    const BwdPlan bp = make_bwd_plan(d);
+    const BwdPlan bp = make_bwd_plan(d, kda::compute_units(kda::stream_device(st)));
     if (!workspace || workspace_bytes < bp.ws_bytes) return KDA_ERR_WORKSPACE;
     if (!aligned(workspace, 256)) return KDA_ERR_INVALID_ARG;
     const Range rw = range_of(workspace, (int64_t)bp.ws_bytes);

@@ -1148,7 +1148,7 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t st) {
     const int64_t chunks = a.lanes * a.nchunks;
     if (chunks <= 0) return hipSuccess;
     // state pass: blocks of 16 value columns when blocks of 32 would leave compute units idle
-    const bool narrow = a.lanes * (DV / 32) < resident_workgroups() / 2;
+    const bool narrow = a.lanes * (DV / 32) < compute_units(stream_device(st));
     const size_t prep_smem = sizeof(PrepSmem<DK, DV>);
     const size_t state_smem = narrow ? sizeof(StateSmem<DK, 16>) : sizeof(StateSmem<DK, 32>);
     const void* state_fn = narrow ? (const void*)bwd_state_kernel<DK, DV, TO, 16> : (const void*)bwd_state_kernel<DK, DV, TO, 32>;

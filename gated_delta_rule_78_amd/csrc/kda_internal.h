@@ -118,9 +118,10 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t st);
 hipError_t launch_chunk(const ChunkLaunch& a, hipStream_t st);
 // bf16-input prefill: records of every chunk, then the inter-chunk state pass.
 hipError_t launch_intra(const IntraArgs& a, hipStream_t st);
-// workgroups that fit on the current device at once at the forward kernels' LDS budget
-// (two per compute unit), cached per device
-int resident_workgroups();
+// The device a stream launches on (the current device for the null stream), and the number of
+// compute units of a device (cached per device; 256 if the runtime cannot tell).
+int stream_device(hipStream_t st);
+int compute_units(int dev);
 hipError_t launch_inter(const ChunkLaunch& a, hipStream_t st);
 // entry_{s+1} = S~_s + M_s entry_s for s in [1, nseg-1), entry_1 already stored.
 hipError_t launch_segment_scan(const ChunkLaunch& a, hipStream_t st);

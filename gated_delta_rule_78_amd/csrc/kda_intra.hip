@@ -28,8 +28,6 @@
 //   3. blocked forward substitution (I + A_kk) [W | U] = Diag(beta) [K~ | V] on the MFMA, 16
 //      columns per tile, right-hand sides and results in registers; U goes to the record, -W is
 //      transposed through LDS into fragment order.
-#include <atomic>
-
 #include "kda_internal.h"
 #include "kda_mfma.h"
 #include "kda_record.h"
@@ -582,7 +580,8 @@ template <int DK, int DV>
 hipError_t launch_dd(const IntraArgs& a, hipStream_t st) {
     int64_t blocks = a.slot_tab ? a.map.H * a.map.slots : a.lanes * a.nchunks;
     if (blocks <= 0) return hipSuccess;
-    if (blocks > resident_workgroups()) blocks = resident_workgroups();
+    const int64_t resident = 2 * (int64_t)compute_units(stream_device(st));   // two per CU (the LDS budget)
+    if (blocks > resident) blocks = resident;
     const dim3 grid((unsigned)blocks), block(256);
     if (a.slot_tab) {
         if (a.gt.z) hipLaunchKernelGGL((intra_kernel<DK, DV, true, true>), grid, block, 0, st, a);
@@ -595,22 +594,6 @@ hipError_t launch_dd(const IntraArgs& a, hipStream_t st) {
 }
 
 }  // namespace
-
-// Resident workgroups for the persistent grid: two per compute unit (the LDS budget). Cached
-// per device; concurrent first calls from several host threads store the same value.
-int resident_workgroups() {
-    static std::atomic<int> cached[64];
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 512;
-    int n = cached[dev].load(std::memory_order_relaxed);
-    if (n == 0) {
-        int cus = 0;
-        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
-        n = 2 * cus;
-        cached[dev].store(n, std::memory_order_relaxed);
-    }
-    return n;
-}
 
 hipError_t launch_intra(const IntraArgs& a, hipStream_t st) {
     if (a.dk == 128) return a.dv == 128 ? launch_dd<128, 128>(a, st) : launch_dd<128, 64>(a, st);

@@ -3,25 +3,44 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+
 #include "kda_record.h"
 
 namespace kda {
 
-constexpr int64_t kTargetBlocks = 256;  // one state-pass workgroup per compute unit
+int stream_device(hipStream_t st) {
+    int dev = 0;
+    if (hipStreamGetDevice(st, &dev) == hipSuccess) return dev;
+    return hipGetDevice(&dev) == hipSuccess ? dev : 0;
+}
+
+// Cached per device; concurrent first calls from several host threads store the same value.
+int compute_units(int dev) {
+    static std::atomic<int> cached[64];
+    if (dev < 0 || dev >= 64) return 256;
+    int n = cached[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cached[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
 
 // Sequence split of the bf16 state pass. One state-pass workgroup occupies a compute unit; with
 // n segments, pass 1 runs segment 0 plus n - 2 summaries per lane, pass 2 the n - 1 later
-// segments, each pass taking chunks_per_seg steps per round of kTargetBlocks workgroups. Pick the
-// n with the fewest sequential chunk steps (the segment scan adds about two per segment).
-static int64_t auto_segments(int64_t lanes, int64_t nchunks) {
+// segments, each pass taking chunks_per_seg steps per round of `cus` workgroups (one per compute
+// unit). Pick the n with the fewest sequential chunk steps (the segment scan adds about two per
+// segment).
+static int64_t auto_segments(int64_t lanes, int64_t nchunks, int64_t cus) {
     int64_t best = 1;
-    int64_t best_cost = nchunks * ceil_div(lanes, kTargetBlocks);
+    int64_t best_cost = nchunks * ceil_div(lanes, cus);
     const int64_t nmax = nchunks / 4 < 64 ? nchunks / 4 : 64;
     for (int64_t n = 3; n <= nmax; ++n) {
         const int64_t cps = ceil_div(nchunks, n);
         const int64_t nn = ceil_div(nchunks, cps);
         if (nn < 3) continue;
-        const int64_t rounds = ceil_div(lanes * (nn - 1), kTargetBlocks);
+        const int64_t rounds = ceil_div(lanes * (nn - 1), cus);
         const int64_t cost = cps * 2 * rounds + 2 * (nn - 2);
         if (cost < best_cost) { best_cost = cost; best = nn; }
     }
@@ -33,7 +52,7 @@ Plan make_plan(const Geometry& g) {
     const int64_t nchunks = g.max_chunks;
     p.nchunks = nchunks;
     int64_t nseg = 1;
-    if (g.in_dtype == KDA_BF16 && nchunks > 0) nseg = g.segments > 0 ? g.segments : auto_segments(g.long_lanes, nchunks);
+    if (g.in_dtype == KDA_BF16 && nchunks > 0) nseg = g.segments > 0 ? g.segments : auto_segments(g.long_lanes, nchunks, g.cus > 0 ? g.cus : 256);
     if (nseg > nchunks) nseg = nchunks > 0 ? nchunks : 1;
     int64_t cps = nchunks > 0 ? ceil_div(nchunks, nseg) : 1;
     if (cps < 1) cps = 1;

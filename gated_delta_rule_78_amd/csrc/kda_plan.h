@@ -23,6 +23,7 @@ struct Geometry {
     int32_t in_dtype, segments;
     int64_t tab_slots;   // slot-table entries (packed batches), 0 otherwise
     int64_t long_lanes;  // lanes that can have max_chunks chunks (plans the sequence split)
+    int64_t cus;         // compute units of the device the call runs on
 };
 
 // Segments per lane, chunks per segment and workspace of a prefill call.
