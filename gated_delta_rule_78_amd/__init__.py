@@ -6,6 +6,8 @@ Every step of the computation runs in the library's HIP kernels. There is no fal
 library is missing or fails, the call raises.
 
     chunk_fwd(q, k, v, log_alpha, beta, S0=None) -> (o, S_T)     chunkwise prefill
+    chunk_fwd_noalloc(q, k, v, log_alpha, beta, S0=None)          the same, workspace from the
+        -> (o, S_T)                                               library's fixed scratch
     chunk_fwd_varlen(q, k, v, log_alpha, beta, cu_seqlens, ...)   packed variable-length batch,
         -> (o, S_T, S_ckpt, ckpt_offsets)                         state checkpoints every E tokens
     chunk_bwd(q, k, v, log_alpha, beta, S0, dO, dS_T) -> grads    backward of chunkwise prefill
@@ -17,7 +19,7 @@ import os
 
 import torch
 
-__all__ = ["chunk_fwd", "chunk_fwd_varlen", "chunk_bwd", "chunk_bwd_workspace_bytes", "decode_step", "chunk_workspace_bytes", "varlen_workspace_bytes",
+__all__ = ["chunk_fwd", "chunk_fwd_noalloc", "SCRATCH_BYTES", "chunk_fwd_varlen", "chunk_bwd", "chunk_bwd_workspace_bytes", "decode_step", "chunk_workspace_bytes", "varlen_workspace_bytes",
            "library", "KDAError", "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkda.so")
@@ -71,6 +73,8 @@ def library():
         lib.kda_chunk_fwd_workspace_bytes.restype = ctypes.c_size_t
         lib.kda_chunk_fwd.argtypes = [ctypes.POINTER(ChunkDesc), P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
         lib.kda_chunk_fwd.restype = ctypes.c_int32
+        lib.kda_chunk_fwd_noalloc.argtypes = [ctypes.POINTER(ChunkDesc), P, P, P, P, P, P, P, P, P]
+        lib.kda_chunk_fwd_noalloc.restype = ctypes.c_int32
         lib.kda_chunk_fwd_varlen_workspace_bytes.argtypes = [ctypes.POINTER(VarlenDesc)]
         lib.kda_chunk_fwd_varlen_workspace_bytes.restype = ctypes.c_size_t
         lib.kda_chunk_fwd_varlen.argtypes = [ctypes.POINTER(VarlenDesc), P, P, P, P, P, P, P, P, P, P, P,
@@ -196,6 +200,47 @@ def chunk_fwd(q, k, v, log_alpha, beta, S0=None, *, out_dtype=None, segments=0, 
                                _ptr(o), _ptr(S_T), _ptr(workspace), _nbytes(workspace), _stream(dev, stream))
     _check("kda_chunk_fwd", st)
     return o, S_T
+
+
+def chunk_fwd_noalloc(q, k, v, log_alpha, beta, S0=None, *, out_dtype=None, o=None, S_T=None, store_state=True,
+                      stream=None):
+    """``chunk_fwd`` through ``kda_chunk_fwd_noalloc``: the library takes the workspace from its own
+    fixed scratch (``SCRATCH_BYTES`` per device) instead of an argument, so the C call allocates
+    nothing; pass ``o`` (and ``S_T``) to keep the binding from allocating them. Calls that overlap
+    in time on one device share that scratch and race. Raises KDAError (KDA_ERR_SCRATCH) when the
+    call needs more workspace than the scratch holds."""
+    dev = q.device
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    dt = q.dtype
+    if dt not in _DTYPES:
+        raise ValueError("unsupported input dtype %s" % dt)
+    out_dtype = out_dtype or dt
+    if out_dtype not in _DTYPES:
+        raise ValueError("unsupported output dtype %s" % out_dtype)
+    for name, t, shape in (("q", q, (B, H, T, dk)), ("k", k, (B, H, T, dk)), ("log_alpha", log_alpha, (B, H, T, dk)),
+                           ("v", v, (B, H, T, dv)), ("beta", beta, (B, H, T))):
+        _check_tensor(name, t, dev, dt, shape)
+    if S0 is not None:
+        _check_tensor("S0", S0, dev, torch.float32, (B, H, dk, dv))
+    if o is not None:
+        _check_tensor("o", o, dev, out_dtype, (B, H, T, dv))
+    if S_T is not None:
+        _check_tensor("S_T", S_T, dev, torch.float32, (B, H, dk, dv))
+    _check_device("chunk_fwd_noalloc", dev)
+    desc = _chunk_desc(q, v, 0, out_dtype)
+    with _alloc_on(stream):
+        if o is None:
+            o = torch.empty(B, H, T, dv, device=dev, dtype=out_dtype)
+        if S_T is None and store_state:
+            S_T = torch.empty(B, H, dk, dv, device=dev, dtype=torch.float32)
+        st = library().kda_chunk_fwd_noalloc(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha),
+                                             _ptr(beta), _ptr(S0), _ptr(o), _ptr(S_T), _stream(dev, stream))
+    _check("kda_chunk_fwd_noalloc", st)
+    return o, S_T
+
+
+SCRATCH_BYTES = 192 << 20   # KDA_NOALLOC_SCRATCH_BYTES of include/kda.h
 
 
 def _gating(dev, H, dv, dtype, lead, z, A_log, g_min, gate, norm_weight, eps):

@@ -168,6 +168,9 @@ const char* kda_status_string(int32_t status) {
         case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED: shape or type not implemented";
         case KDA_ERR_WORKSPACE: return "KDA_ERR_WORKSPACE: workspace missing or too small";
         case KDA_ERR_HIP: return "KDA_ERR_HIP: the HIP runtime reported an error";
+        case KDA_ERR_SCRATCH:
+            return "KDA_ERR_SCRATCH: the call needs more workspace than the library's fixed scratch "
+                   "(KDA_NOALLOC_SCRATCH_BYTES); use kda_chunk_fwd with a workspace";
         default: return "unknown kda_status";
     }
 }
@@ -182,6 +185,19 @@ size_t kda_chunk_fwd_workspace_bytes(const kda_chunk_desc* d) {
 kda_status kda_chunk_fwd(const kda_chunk_desc* d, const void* q, const void* k, const void* v,
                          const void* log_alpha, const void* beta, const float* S0, void* o, float* S_T,
                          void* workspace, size_t workspace_bytes, void* stream) {
+    return kda::chunk_fwd_impl(d, q, k, v, log_alpha, beta, S0, o, S_T, workspace, workspace_bytes, stream, nullptr);
+}
+
+}  // extern "C"
+
+namespace kda {
+
+// kda_chunk_fwd, or with `scratch_of` set kda_chunk_fwd_noalloc: the workspace is then the fixed
+// scratch of the stream's device, looked up only once every argument has passed validation and
+// the plan is known to fit it.
+kda_status chunk_fwd_impl(const kda_chunk_desc* d, const void* q, const void* k, const void* v,
+                          const void* log_alpha, const void* beta, const float* S0, void* o, float* S_T,
+                          void* workspace, size_t workspace_bytes, void* stream, void* (*scratch_of)(int)) {
     const kda_status ds = check_chunk_desc(d);
     if (ds != KDA_OK) return ds;
     const int64_t lanes = d->B * d->H;
@@ -213,7 +229,14 @@ kda_status kda_chunk_fwd(const kda_chunk_desc* d, const void* q, const void* k, 
     if (S0 && overlaps(ro, range_of(S0, state_bytes))) return KDA_ERR_INVALID_ARG;
     if (S_T && overlaps(ro, range_of(S_T, state_bytes))) return KDA_ERR_INVALID_ARG;
 
-    const Plan plan = make_plan(fixed_geometry(d, kda::compute_units(kda::stream_device(st))));
+    const int dev = kda::stream_device(st);
+    const Plan plan = make_plan(fixed_geometry(d, kda::compute_units(dev)));
+    if (scratch_of && plan.ws_bytes > 0) {
+        if (plan.ws_bytes > (size_t)KDA_NOALLOC_SCRATCH_BYTES) return KDA_ERR_SCRATCH;
+        workspace = scratch_of(dev);
+        if (!workspace) return KDA_ERR_HIP;
+        workspace_bytes = (size_t)KDA_NOALLOC_SCRATCH_BYTES;
+    }
     if (plan.ws_bytes > 0) {
         if (!workspace || workspace_bytes < plan.ws_bytes) return KDA_ERR_WORKSPACE;
         if (!aligned(workspace, 16)) return KDA_ERR_INVALID_ARG;
@@ -239,6 +262,10 @@ kda_status kda_chunk_fwd(const kda_chunk_desc* d, const void* q, const void* k, 
     }
     return run_bf16(a, plan, static_cast<unsigned char*>(workspace), st);
 }
+
+}  // namespace kda
+
+extern "C" {
 
 size_t kda_chunk_fwd_varlen_workspace_bytes(const kda_varlen_desc* d) {
     if (check_varlen_desc(d) != KDA_OK) return 0;

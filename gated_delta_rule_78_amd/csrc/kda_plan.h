@@ -43,4 +43,10 @@ Plan make_plan(const Geometry& g);
 // workspace of `plan` (at least plan.ws_bytes). Returns KDA_ERR_HIP if a launch fails.
 kda_status run_bf16(ChunkLaunch& a, const Plan& plan, unsigned char* ws, hipStream_t st);
 
+// kda_chunk_fwd (scratch_of == NULL) or kda_chunk_fwd_noalloc (scratch_of returns the device address
+// of a device's fixed scratch, KDA_NOALLOC_SCRATCH_BYTES long, or NULL on failure).
+kda_status chunk_fwd_impl(const kda_chunk_desc* d, const void* q, const void* k, const void* v,
+                          const void* log_alpha, const void* beta, const float* S0, void* o, float* S_T,
+                          void* workspace, size_t workspace_bytes, void* stream, void* (*scratch_of)(int));
+
 }  // namespace kda

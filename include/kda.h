@@ -46,7 +46,9 @@ typedef enum kda_status {
     KDA_ERR_INVALID_ARG = -1, /* null/negative/misaligned/overlapping argument            */
     KDA_ERR_UNSUPPORTED = -2, /* well-formed but not implemented (e.g. dk not in {64,128}) */
     KDA_ERR_WORKSPACE = -3,   /* workspace missing or smaller than the query reports      */
-    KDA_ERR_HIP = -4          /* the HIP runtime reported an error while enqueuing        */
+    KDA_ERR_HIP = -4,         /* the HIP runtime reported an error while enqueuing        */
+    KDA_ERR_SCRATCH = -5      /* kda_chunk_fwd_noalloc: the call needs more workspace than
+                                 the library's fixed scratch (KDA_NOALLOC_SCRATCH_BYTES)  */
 } kda_status;
 
 typedef enum kda_dtype {
@@ -111,6 +113,25 @@ kda_status kda_chunk_fwd(const kda_chunk_desc* desc,
                          const void* log_alpha, const void* beta,
                          const float* S0, void* o, float* S_T,
                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * kda_chunk_fwd without a workspace argument, for callers that cannot allocate device memory
+ * (code under stream capture, tight serving loops, harnesses that forbid allocation). Same
+ * arguments, layouts, validation and results as kda_chunk_fwd (the same kernels and plan); the
+ * workspace kda_chunk_fwd_workspace_bytes(desc) reports is taken from a scratch array of
+ * KDA_NOALLOC_SCRATCH_BYTES that the library owns: one copy per device, allocated when the
+ * library's code is loaded on that device and held until the process ends. The call allocates
+ * nothing. A call that needs more returns KDA_ERR_SCRATCH (about 2,700 chunk records at
+ * d = 128: e.g. 32 heads x 5,500 tokens, or 8 heads x 22,000 tokens, with the library's plan).
+ * Every call on one device shares that device's scratch: calls that overlap in time on one
+ * device (two streams, or two host threads) race and give undefined results; serialise them.
+ * No part of the scratch needs clearing: each call writes every scratch byte it reads first.
+ */
+#define KDA_NOALLOC_SCRATCH_BYTES (192u << 20)
+kda_status kda_chunk_fwd_noalloc(const kda_chunk_desc* desc,
+                                 const void* q, const void* k, const void* v,
+                                 const void* log_alpha, const void* beta,
+                                 const float* S0, void* o, float* S_T, void* stream);
 
 /*
  * Optional fused prologue and epilogue around the KDA core (section 2.2 of the Kimi K3 reading

@@ -31,7 +31,7 @@ def lib():
 
 def test_header_declares_the_boundary():
     assert declared_functions() == ["kda_chunk_bwd", "kda_chunk_bwd_workspace_bytes", "kda_chunk_fwd",
-                                    "kda_chunk_fwd_varlen", "kda_chunk_fwd_varlen_workspace_bytes",
+                                    "kda_chunk_fwd_noalloc", "kda_chunk_fwd_varlen", "kda_chunk_fwd_varlen_workspace_bytes",
                                     "kda_chunk_fwd_workspace_bytes", "kda_decode_step", "kda_decode_step_gated",
                                     "kda_status_string", "kda_version"]
 
@@ -297,3 +297,22 @@ def test_binding_checks_caller_buffers():
         kda.chunk_fwd_varlen(pq, pq, pq, pq, pb, cu, ckpt_every=64, S_ckpt=torch.zeros(4, H, d, d))
     with pytest.raises(ValueError, match="workspace"):
         kda.chunk_bwd(q, q, q, q, beta, None, q, workspace=torch.zeros(8, 8, dtype=torch.uint8).t())
+
+
+def test_noalloc_rejects_calls_beyond_its_scratch(lib):
+    """kda_chunk_fwd_noalloc refuses, before any device work, a call whose workspace would not fit
+    the library's fixed scratch, and validates its arguments like kda_chunk_fwd."""
+    P = ctypes.c_void_p
+    call = lambda d, q=FAKE, o=FAKE + (5 << 30): lib.kda_chunk_fwd_noalloc(
+        None if d is None else ctypes.byref(d), P(q), P(FAKE + (1 << 30)), P(FAKE + (2 << 30)), P(FAKE + (3 << 30)),
+        P(FAKE + (4 << 30)), None, P(o), None, None)
+    SCRATCH_ERR = -5
+    assert kda.SCRATCH_BYTES == 192 << 20
+    big = _desc(B=1, H=32, T=8192)
+    assert lib.kda_chunk_fwd_workspace_bytes(ctypes.byref(big)) > kda.SCRATCH_BYTES
+    assert call(big) == SCRATCH_ERR
+    assert lib.kda_status_string(SCRATCH_ERR).decode().startswith("KDA_ERR_SCRATCH")
+    assert call(None) == INVALID
+    assert call(_desc(dk=96)) == UNSUPPORTED
+    assert call(_desc(), q=0) == INVALID
+    assert call(_desc(), o=FAKE + 64) == INVALID   # o overlaps q
