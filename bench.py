@@ -1,21 +1,25 @@
 """Benchmark of the KDA hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload prefill_8k|prefill_64k|prefill_1m|fp32_small]
-                    [--decode-steps 1000] [--no-cpu-baseline] [--no-packed] [--copy-probe-mib M]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload prefill_1m|prefill_8k|prefill_64k|fp32_small]
+                    [--decode-steps 1000] [--no-cpu-baseline] [--no-packed] [--no-backward] [--no-sub]
+                    [--copy-probe-mib M]
 
-One step = one kda_chunk_fwd call over the named prefill workload (default: bf16, B=1, H=32,
-T=8192, d=128, C=64, S0=0), inputs already resident in HBM. The decode regime is measured in
-the same run: `--decode-steps` chained kda_decode_step calls over 256 sequences x 32 heads
-(fp32 state, bf16 tokens, each step its own pre-generated tokens), and so is a packed batch of
-12 variable-length sequences (8192 tokens per head, 32 heads) with state checkpoints every 512
-tokens (kda_chunk_fwd_varlen). Times come from HIP events recorded on the stream the library
-launches on.
+One step = one kda_chunk_fwd call over the named prefill workload (default: the long-context
+workload, bf16, B=1, H=32, T=1,048,576, d=128, C=64, S0=0, split across the GPU by the library's
+plan), inputs already resident in HBM. The same run also times, each as a sub-object of the line:
+the 8K workload (B=1, H=32, T=8192) and the 64K workload with a carried state (B=4, H=32,
+T=65536, S0); a packed batch of 12 variable-length sequences (8192 tokens per head, 32 heads) with
+state checkpoints every 512 tokens (kda_chunk_fwd_varlen), with and without the fused gating; the
+backward of the 8K workload; and the decode regime: `--decode-steps` chained kda_decode_step calls
+over 256 sequences x 32 heads (fp32 state, bf16 tokens, each step its own pre-generated tokens).
+Times come from HIP events recorded on the stream the library launches on.
 
-Prints one JSON line. `value` is prefill tokens/s (B*T / seconds per call). `roofline` is the
-prefill call (all of its kernels: intra-chunk records, state passes, segment scan) against HBM
-bandwidth with algorithmic bytes; its `traffic` is the HBM bytes per call that rocprofv3 counters
-measured on the same sources (profiles/), null when the sources changed since. `decode` carries
-the decode figures and its own roofline; `cpu_baseline` is the fp64 oracle timed on this host.
+Prints one JSON line. `value` is prefill tokens/s, B*T / `ms_per_step` (the timed loop of K calls
+between two events, divided by K). `roofline` is the prefill call (all of its kernels) against HBM
+bandwidth with algorithmic bytes, over `call_ms`, the mean of per-call event pairs; its `traffic`
+is the HBM bytes per call that rocprofv3 counters measured on the same sources (profiles/), null
+when the sources changed since. `cpu_baseline` is the fp64 oracle timed on this host on a stated
+sample of the workload's lanes, scaled to the whole workload (lanes are independent).
 """
 import argparse
 import json
@@ -32,7 +36,9 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 FP32_PEAK_TFLOPS = 157.3       # MI355X fp32 vector/matrix, published
 
 # Algorithmic work per token-head of chunkwise prefill (C = 64, dk = dv = d):
-#   flops  6*dk*dv + C*(3*dk + 2*dv) + C^2/3      (state products, Gram/UT/causal halves)
+#   flops  6*dk*dv + C*(3*dk + 2*dv) + C^2/3      (state products; Gram/UT/causal products over
+#                                                   their causal halves only)
+#   dense  6*dk*dv + 2*C*(3*dk + 2*dv)            (the same with the C x C products counted whole)
 #   bytes  q,k,log_alpha,v (4*d elements in) + beta (1) + o (d elements out)
 # plus one fp32 state read (S0, when given) and one fp32 state write (S_T) per head.
 def prefill_alg(B, H, T, d, in_bytes, out_bytes, has_s0, C=64):
@@ -40,6 +46,10 @@ def prefill_alg(B, H, T, d, in_bytes, out_bytes, has_s0, C=64):
     bytes_tok = 4 * d * in_bytes + in_bytes + d * out_bytes
     state = d * d * 4 * (2 if has_s0 else 1)
     return B * H * T * flops_tok, B * H * (T * bytes_tok + state)
+
+
+def prefill_dense_flops(B, H, T, d, C=64):
+    return B * H * T * (6 * d * d + 2 * C * (5 * d))
 
 
 # Decode per (sequence, head): fp32 state read + write, q,k,log_alpha,v in, beta, o out.
@@ -50,8 +60,9 @@ def decode_alg(N, H, d, in_bytes=2, out_bytes=2):
 
 
 # Measured HBM traffic (rocprofv3 FETCH_SIZE / WRITE_SIZE, calibrated) comes from the committed
-# profile summary; a figure is used only while the kernel sources it was taken on are unchanged.
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_prefill_8k_and_decode.md")
+# profile summaries; a figure is used only while the kernel sources it was taken on are unchanged.
+TRAFFIC_FILES = [os.path.join(ROOT, "profiles", f) for f in ("hbm_traffic_prefill_1m.md",
+                                                             "hbm_traffic_prefill_8k_and_decode.md")]
 PREFILL_SOURCES = ["kda_intra.hip", "kda_inter.hip", "kda_scan.hip", "kda_record.h", "kda_mfma.h", "kda_device.h",
                    "kda_plan.h", "kda_plan.cpp"]
 DECODE_SOURCES = ["kda_decode.hip", "kda_device.h"]
@@ -67,16 +78,17 @@ def sources_hash(files):
 
 
 def measured_traffic(kind, workload_name, files):
-    """Bytes per call/step recorded in the profile summary for this workload, or None."""
+    """Bytes per call/step recorded in a profile summary for this workload, or None."""
     import re
-    try:
-        text = open(TRAFFIC_FILE).read()
-    except OSError:
-        return None
     pat = r"traffic_bytes_per_%s\[(.*?)\] = (\d+) sources=([0-9a-f]+)" % kind
-    for name, value, src in re.findall(pat, text):
-        if name == workload_name and src == sources_hash(files):
-            return int(value)
+    for path in TRAFFIC_FILES:
+        try:
+            text = open(path).read()
+        except OSError:
+            continue
+        for name, value, src in re.findall(pat, text):
+            if name == workload_name and src == sources_hash(files):
+                return int(value)
     return None
 
 
@@ -88,18 +100,86 @@ WORKLOADS = {
 }
 
 
+def log(msg):
+    print("bench: " + msg, file=sys.stderr, flush=True)
+
+
+def time_prefill(kda, synth, torch, np, w, steps, warmup, segments, stream, keep_lanes=0):
+    """Time `steps` kda_chunk_fwd calls over workload `w` after `warmup` untimed ones. Returns the
+    figures and, with keep_lanes > 0, host copies of the first keep_lanes lanes' inputs (for the
+    CPU baseline) taken before the device tensors are freed."""
+    dev = stream.device
+    log("generating %s" % w.name)
+    q, k, v, la, beta, S0 = synth.workload_inputs(w, device=dev)
+    o = torch.empty(w.B, w.H, w.T, w.d, device=dev, dtype=w.dtype)
+    S_T = torch.empty(w.B, w.H, w.d, w.d, device=dev, dtype=torch.float32)
+    nbytes = kda.chunk_workspace_bytes(q, v, segments=segments)
+    ws = torch.empty(max(nbytes, 16), device=dev, dtype=torch.uint8)
+
+    def step():
+        kda.chunk_fwd(q, k, v, la, beta, S0, out_dtype=w.dtype, segments=segments, o=o, S_T=S_T, workspace=ws,
+                      stream=stream)
+
+    log("timing %s: %d warm-up + %d timed calls" % (w.name, warmup, steps))
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = t_start.elapsed_time(t_end) / steps
+    call_ms = float(np.mean([a.elapsed_time(b) for a, b in zip(starts, ends)]))
+    in_b = 2 if w.dtype == torch.bfloat16 else 4
+    flops, abytes = prefill_alg(w.B, w.H, w.T, w.d, in_b, in_b, S0 is not None)
+    dense = prefill_dense_flops(w.B, w.H, w.T, w.d)
+    mm_peak = BF16_PEAK_TFLOPS if w.dtype == torch.bfloat16 else FP32_PEAK_TFLOPS
+    gbs = abytes / (call_ms * 1e-3) / 1e9
+    res = {
+        "workload": w.name, "value": w.B * w.T / (ms_per_step * 1e-3), "unit": "tokens/s",
+        "ms_per_step": ms_per_step, "call_ms": call_ms, "steps": steps, "warmup": warmup,
+        "tokens_per_s_from_call_ms": w.B * w.T / (call_ms * 1e-3),
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "T": w.T, "dk": w.d, "dv": w.d, "chunk": 64,
+                   "s0": S0 is not None, "segments": segments or "auto", "workspace_bytes": nbytes},
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbs / HBM_PEAK_GBS, "traffic": measured_traffic("call", w.name, PREFILL_SOURCES)},
+        "mfma": {"alg_tflops": flops / (call_ms * 1e-3) / 1e12, "dense_tile_tflops": dense / (call_ms * 1e-3) / 1e12,
+                 "peak_tflops": mm_peak, "frac": flops / (call_ms * 1e-3) / 1e12 / mm_peak,
+                 "dense_tile_frac": dense / (call_ms * 1e-3) / 1e12 / mm_peak},
+        "alg_bytes_per_call": abytes, "alg_flops_per_call": flops, "dense_tile_flops_per_call": dense,
+    }
+    sample = None
+    if keep_lanes:
+        L = min(keep_lanes, w.B * w.H)
+        f = lambda x: x.reshape((-1,) + tuple(x.shape[2:]))[:L].float().cpu().numpy()
+        sample = ([f(q), f(k), f(v), f(la), f(beta)], None if S0 is None else f(S0), L)
+    del q, k, v, la, beta, S0, o, S_T, ws
+    torch.cuda.empty_cache()
+    return res, sample
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="prefill_8k", choices=sorted(WORKLOADS))
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="prefill_1m", choices=sorted(WORKLOADS))
     ap.add_argument("--segments", type=int, default=0, help="0 = the library's plan")
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-packed", action="store_true", help="skip the packed variable-length batch")
-    ap.add_argument("--no-backward", action="store_true", help="skip the backward of the prefill workload")
-    ap.add_argument("--cpu-lanes", type=int, default=32, help="lanes of the CPU-baseline sample")
+    ap.add_argument("--no-backward", action="store_true", help="skip the backward of the 8K workload")
+    ap.add_argument("--no-sub", action="store_true", help="skip the 8K and 64K prefill sub-objects")
+    ap.add_argument("--cpu-lanes", type=int, default=0,
+                    help="lanes of the CPU-baseline sample (0: about 2M lane-tokens of the workload)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run one plain device copy of this size (counter calibration)")
     args = ap.parse_args()
@@ -118,42 +198,9 @@ def main():
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream(dev)
     w = getattr(synth, WORKLOADS[args.workload])
-    print("bench: generating %s" % w.name, file=sys.stderr, flush=True)
-    q, k, v, la, beta, S0 = synth.workload_inputs(w, device=dev)
-    out_dtype = w.dtype
-    o = torch.empty(w.B, w.H, w.T, w.d, device=dev, dtype=out_dtype)
-    S_T = torch.empty(w.B, w.H, w.d, w.d, device=dev, dtype=torch.float32)
-    nbytes = kda.chunk_workspace_bytes(q, v, segments=args.segments)
-    ws = torch.empty(max(nbytes, 16), device=dev, dtype=torch.uint8)
-
-    def step():
-        kda.chunk_fwd(q, k, v, la, beta, S0, out_dtype=out_dtype, segments=args.segments, o=o, S_T=S_T,
-                      workspace=ws, stream=stream)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_start.record(stream)
-    for i in range(args.steps):
-        starts[i].record(stream)
-        step()
-        ends[i].record(stream)
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    total_ms = t_start.elapsed_time(t_end)
-    ms_per_step = total_ms / args.steps
-    call_ms = float(np.mean([s.elapsed_time(e) for s, e in zip(starts, ends)]))
-    tokens = w.B * w.T
-    in_b = 2 if w.dtype == torch.bfloat16 else 4
-    flops, abytes = prefill_alg(w.B, w.H, w.T, w.d, in_b, in_b, S0 is not None)
-    achieved_gbs = abytes / (call_ms * 1e-3) / 1e9
-    tflops = flops / (call_ms * 1e-3) / 1e12
-    mm_peak = BF16_PEAK_TFLOPS if w.dtype == torch.bfloat16 else FP32_PEAK_TFLOPS
+    cpu_lanes = args.cpu_lanes or max(1, min(w.B * w.H, (2 << 20) // w.T))
+    main_res, sample = time_prefill(kda, synth, torch, np, w, args.steps, args.warmup, args.segments, stream,
+                                    keep_lanes=0 if args.no_cpu_baseline else cpu_lanes)
 
     if args.copy_probe_mib:
         n = args.copy_probe_mib * (1 << 20) // 4
@@ -163,13 +210,22 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    # ---------------- the other prefill workloads ----------------
+    subs = {}
+    if not args.no_sub:
+        for key in ("prefill_8k", "prefill_64k"):
+            if key != args.workload:
+                sw = getattr(synth, WORKLOADS[key])
+                n = max(3, args.steps) if key == "prefill_64k" else max(20, args.steps)
+                subs[key], _ = time_prefill(kda, synth, torch, np, sw, n, max(3, args.warmup), 0, stream)
+
     # ---------------- packed variable-length batch with checkpoints ----------------
     packed = None
     if not args.no_packed:
         pw = synth.PACKED_BF16_8K
         lens = synth.PACKED_BF16_8K_LENS
         E = 512
-        print("bench: packed %s" % pw.name, file=sys.stderr, flush=True)
+        log("packed %s" % pw.name)
         pq, pk, pv, pla, pbeta, cu, _ = synth.packed_inputs(lens, pw.H, pw.d, pw.d, pw.dtype, device=dev)
         N = len(lens)
         n_ck = sum(n // E for n in lens)
@@ -232,26 +288,27 @@ def main():
                                    "alg_bytes_per_call": fby}}
         del pq, pk, pv, pla, pbeta, po, pws
 
-    # ---------------- backward (training) of the same prefill workload ----------------
+    # ---------------- backward (training) of the 8K workload ----------------
     bwd = None
-    if not args.no_backward and w.dtype == torch.bfloat16:
-        print("bench: backward %s" % w.name, file=sys.stderr, flush=True)
+    if not args.no_backward:
+        bw = synth.PREFILL_BF16_8K   # a 1M-token backward would need its per-chunk scratch for 0.5M chunks
+        log("backward %s" % bw.name)
+        q, k, v, la, beta, S0 = synth.workload_inputs(bw, device=dev)
         g = torch.Generator(device=dev)
         g.manual_seed(17)
-        dO = torch.randn(w.B, w.H, w.T, w.d, generator=g, device=dev).to(out_dtype)
-        dST = torch.randn(w.B, w.H, w.d, w.d, generator=g, device=dev) * 0.1
-        bws = torch.empty(max(kda.chunk_bwd_workspace_bytes(q, v, args.segments, out_dtype), 16), device=dev,
-                          dtype=torch.uint8)
+        dO = torch.randn(bw.B, bw.H, bw.T, bw.d, generator=g, device=dev).to(bw.dtype)
+        dST = torch.randn(bw.B, bw.H, bw.d, bw.d, generator=g, device=dev) * 0.1
+        bws = torch.empty(max(kda.chunk_bwd_workspace_bytes(q, v, 0, bw.dtype), 16), device=dev, dtype=torch.uint8)
 
         def bstep():
-            kda.chunk_bwd(q, k, v, la, beta, S0, dO, dST, segments=args.segments, workspace=bws, stream=stream)
+            kda.chunk_bwd(q, k, v, la, beta, S0, dO, dST, workspace=bws, stream=stream)
 
-        for _ in range(max(1, args.warmup)):
+        for _ in range(max(1, min(args.warmup, 5))):
             bstep()
         torch.cuda.synchronize()
         b0 = torch.cuda.Event(enable_timing=True)
         b1 = torch.cuda.Event(enable_timing=True)
-        nb = max(1, args.steps // 4)
+        nb = max(5, args.steps // 4)
         b0.record(stream)
         for _ in range(nb):
             bstep()
@@ -259,20 +316,21 @@ def main():
         torch.cuda.synchronize()
         bms = b0.elapsed_time(b1) / nb
         # bytes: the forward's inputs, dO in, fp32 gradients of q, k, v, log_alpha, beta out, states
-        bby = w.B * w.H * (w.T * (4 * w.d * in_b + in_b + w.d * in_b + 4 * w.d * 4 + 4) + 3 * w.d * w.d * 4)
+        bby = bw.B * bw.H * (bw.T * (4 * bw.d * 2 + 2 + bw.d * 2 + 4 * bw.d * 4 + 4) + 3 * bw.d * bw.d * 4)
         bgbs = bby / (bms * 1e-3) / 1e9
-        bwd = {"workload": w.name + ", backward (forward recompute included)", "metric": "KDA backward tokens/s",
-               "value": tokens / (bms * 1e-3), "unit": "tokens/s", "ms_per_step": bms, "steps": nb,
+        bwd = {"workload": bw.name + ", backward (forward recompute included)", "metric": "KDA backward tokens/s",
+               "value": bw.B * bw.T / (bms * 1e-3), "unit": "tokens/s", "ms_per_step": bms, "steps": nb,
                "roofline": {"bound": "hbm", "achieved": bgbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                             "frac": bgbs / HBM_PEAK_GBS, "traffic": None},
                "alg_bytes_per_call": bby, "workspace_bytes": int(bws.numel())}
-        del dO, bws
+        del q, k, v, la, beta, S0, dO, dST, bws
+        torch.cuda.empty_cache()
 
     # ---------------- decode regime ----------------
     decode = None
     if args.decode_steps > 0:
         dw = synth.DECODE_BF16_256x32
-        print("bench: decode %s" % dw.name, file=sys.stderr, flush=True)
+        log("decode %s" % dw.name)
         S = synth.decode_state(dw.N, dw.H, dw.d, dw.d, dw.s_std, device=dev)
         toks = [synth.decode_tokens(dw.N, dw.H, dw.d, dw.d, dw.dtype, device=dev, seed=4000 + i)
                 for i in range(min(args.decode_steps, 1000))]
@@ -299,39 +357,34 @@ def main():
         del toks
 
     cpu = None
-    if not args.no_cpu_baseline:
+    if sample is not None:
         from oracle import native
-        L = min(args.cpu_lanes, w.B * w.H)
-        print("bench: cpu baseline (oracle) on %d lanes x %d tokens" % (L, w.T), file=sys.stderr, flush=True)
-        f = lambda x: x.reshape((-1,) + tuple(x.shape[2:]))[:L].float().cpu().numpy()
-        a = [f(q), f(k), f(v), f(la), f(beta)]
-        s0 = None if S0 is None else f(S0)
+        arrays, s0, L = sample
+        log("cpu baseline (oracle) on %d lanes x %d tokens" % (L, w.T))
         threads = native.default_threads()
         # repeat the sample until about 10 s of CPU work has been timed (bounded: at most 200 runs)
         runs, t0 = 0, time.perf_counter()
         while True:
-            native.kda_fwd(*a, s0, threads=threads)
+            native.kda_fwd(*arrays, s0, threads=threads)
             runs += 1
             if time.perf_counter() - t0 >= 10.0 or runs >= 200:
                 break
         dt = (time.perf_counter() - t0) / runs
         whole_s = dt * (w.B * w.H) / L          # lanes are independent: scale the sample to the workload
         cpu = {"value": w.B * w.T / whole_s, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-               "sample": "%d of %d lanes x %d tokens (fp64 token loop), %d runs, %.3f s each"
-                         % (L, w.B * w.H, w.T, runs, dt)}
+               "sample": "%d of %d lanes x %d tokens (fp64 token loop), %d runs, %.3f s each; scaled by %d / %d lanes"
+                         % (L, w.B * w.H, w.T, runs, dt, w.B * w.H, L)}
 
     line = {
-        "metric": "KDA prefill tokens/s", "value": tokens / (call_ms * 1e-3), "unit": "tokens/s",
-        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "metric": "KDA prefill tokens/s", "value": main_res["value"], "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": main_res["ms_per_step"],
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16" if w.dtype == torch.bfloat16 else "f32", "data": "synthetic",
-        "config": {"workload": w.name, "B": w.B, "H": w.H, "T": w.T, "dk": w.d, "dv": w.d, "chunk": 64,
-                   "s0": S0 is not None, "segments": args.segments or "auto", "workspace_bytes": nbytes},
-        "roofline": {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved_gbs / HBM_PEAK_GBS,
-                     "traffic": measured_traffic("call", w.name, PREFILL_SOURCES)},
-        "mfma": {"alg_tflops": tflops, "peak_tflops": mm_peak, "frac": tflops / mm_peak},
-        "alg_bytes_per_call": abytes, "alg_flops_per_call": flops, "call_ms": call_ms,
+        "config": main_res["config"], "roofline": main_res["roofline"], "mfma": main_res["mfma"],
+        "call_ms": main_res["call_ms"], "tokens_per_s_from_call_ms": main_res["tokens_per_s_from_call_ms"],
+        "alg_bytes_per_call": main_res["alg_bytes_per_call"], "alg_flops_per_call": main_res["alg_flops_per_call"],
+        "dense_tile_flops_per_call": main_res["dense_tile_flops_per_call"],
+        "prefill_8k": subs.get("prefill_8k"), "prefill_64k": subs.get("prefill_64k"),
         "decode": decode, "packed": packed, "backward": bwd, "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
