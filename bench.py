@@ -63,6 +63,7 @@ def decode_alg(N, H, d, in_bytes=2, out_bytes=2):
 # profile summaries; a figure is used only while the kernel sources it was taken on are unchanged.
 TRAFFIC_FILES = [os.path.join(ROOT, "profiles", f) for f in ("hbm_traffic_prefill_1m.md",
                                                              "hbm_traffic_prefill_8k_and_decode.md")]
+MFMA_FILES = [os.path.join(ROOT, "profiles", "mfma_counters_prefill_1m.md")]
 PREFILL_SOURCES = ["kda_intra.hip", "kda_inter.hip", "kda_scan.hip", "kda_record.h", "kda_mfma.h", "kda_device.h",
                    "kda_plan.h", "kda_plan.cpp"]
 DECODE_SOURCES = ["kda_decode.hip", "kda_device.h"]
@@ -77,11 +78,12 @@ def sources_hash(files):
     return h.hexdigest()[:16]
 
 
-def measured_traffic(kind, workload_name, files):
-    """Bytes per call/step recorded in a profile summary for this workload, or None."""
+def measured_traffic(kind, workload_name, files, what="traffic_bytes", paths=None):
+    """Bytes (or, with what="mfma_flops", executed MFMA flops) per call/step recorded in a profile
+    summary for this workload, or None."""
     import re
-    pat = r"traffic_bytes_per_%s\[(.*?)\] = (\d+) sources=([0-9a-f]+)" % kind
-    for path in TRAFFIC_FILES:
+    pat = r"%s_per_%s\[(.*?)\] = (\d+) sources=([0-9a-f]+)" % (what, kind)
+    for path in paths or TRAFFIC_FILES:
         try:
             text = open(path).read()
         except OSError:
@@ -143,6 +145,8 @@ def time_prefill(kda, synth, torch, np, w, steps, warmup, segments, stream, keep
     dense = prefill_dense_flops(w.B, w.H, w.T, w.d)
     mm_peak = BF16_PEAK_TFLOPS if w.dtype == torch.bfloat16 else FP32_PEAK_TFLOPS
     gbs = abytes / (call_ms * 1e-3) / 1e9
+    # MFMA flops the kernels executed per call (rocprofv3 SQ_INSTS_VALU_MFMA_MOPS_* x 512, profiles/)
+    executed = measured_traffic("call", w.name, PREFILL_SOURCES, what="mfma_flops", paths=MFMA_FILES)
     res = {
         "workload": w.name, "value": w.B * w.T / (ms_per_step * 1e-3), "unit": "tokens/s",
         "ms_per_step": ms_per_step, "call_ms": call_ms, "steps": steps, "warmup": warmup,
@@ -153,7 +157,8 @@ def time_prefill(kda, synth, torch, np, w, steps, warmup, segments, stream, keep
                      "frac": gbs / HBM_PEAK_GBS, "traffic": measured_traffic("call", w.name, PREFILL_SOURCES)},
         "mfma": {"alg_tflops": flops / (call_ms * 1e-3) / 1e12, "dense_tile_tflops": dense / (call_ms * 1e-3) / 1e12,
                  "peak_tflops": mm_peak, "frac": flops / (call_ms * 1e-3) / 1e12 / mm_peak,
-                 "dense_tile_frac": dense / (call_ms * 1e-3) / 1e12 / mm_peak},
+                 "dense_tile_frac": dense / (call_ms * 1e-3) / 1e12 / mm_peak,
+                 "executed_tflops_counter": None if executed is None else executed / (call_ms * 1e-3) / 1e12},
         "alg_bytes_per_call": abytes, "alg_flops_per_call": flops, "dense_tile_flops_per_call": dense,
     }
     sample = None
