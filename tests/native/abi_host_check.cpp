@@ -1,0 +1,183 @@
+// Host-side check of the C ABI's validation and planning layer (kda_abi.cpp, kda_plan.cpp) under
+// AddressSanitizer and UndefinedBehaviorSanitizer. Both files are built for the host only; the
+// kernel launchers and the three HIP runtime queries they use are replaced here by stubs that
+// record what would have been enqueued. Built and run by tests/test_host_sanitizers.py: no GPU,
+// no device memory; every data pointer is a fake address that nothing dereferences.
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "kda.h"
+#include "kda_internal.h"
+#include "kda_plan.h"
+
+namespace {
+int g_intra, g_inter, g_scan, g_chunk, g_copy, g_prep, g_bwd, g_decode;
+kda::ChunkLaunch g_last;
+void reset() { g_intra = g_inter = g_scan = g_chunk = g_copy = g_prep = g_bwd = g_decode = 0; }
+}  // namespace
+
+namespace kda {
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t) { ++g_decode; return a.S && a.o ? hipSuccess : hipErrorInvalidValue; }
+hipError_t launch_chunk(const ChunkLaunch& a, hipStream_t) { ++g_chunk; g_last = a; return hipSuccess; }
+hipError_t launch_intra(const IntraArgs& a, hipStream_t) { ++g_intra; return a.rec ? hipSuccess : hipErrorInvalidValue; }
+hipError_t launch_inter(const ChunkLaunch& a, hipStream_t) { ++g_inter; g_last = a; return hipSuccess; }
+hipError_t launch_segment_scan(const ChunkLaunch&, hipStream_t) { ++g_scan; return hipSuccess; }
+hipError_t launch_varlen_prep(const VarlenPrep&, hipStream_t) { ++g_prep; return hipSuccess; }
+hipError_t launch_copy_or_zero(float* dst, const float*, int64_t n, hipStream_t) { ++g_copy; return dst && n > 0 ? hipSuccess : hipErrorInvalidValue; }
+hipError_t launch_bwd(const BwdArgs& a, hipStream_t) { ++g_bwd; return a.ckpt || a.T < 64 ? hipSuccess : hipErrorInvalidValue; }
+size_t bwd_prep_floats(int64_t dk, int64_t dv) { return (size_t)(64 * (3 * dk + dv) + 64 * 64 + dk); }
+}  // namespace kda
+
+extern "C" {
+hipError_t hipGetDevice(int* d) { *d = 0; return hipSuccess; }
+hipError_t hipStreamGetDevice(hipStream_t, hipDevice_t* d) { *d = 0; return hipSuccess; }
+hipError_t hipDeviceGetAttribute(int* v, hipDeviceAttribute_t, int) { *v = 256; return hipSuccess; }
+}
+
+#define CHECK(cond)                                                               \
+    do {                                                                          \
+        if (!(cond)) {                                                            \
+            fprintf(stderr, "FAIL %s:%d: %s\n", __FILE__, __LINE__, #cond);       \
+            return 1;                                                             \
+        }                                                                         \
+    } while (0)
+
+static const uintptr_t FAKE = 0x7F0000000000ull;
+static void* P(uintptr_t off) { return reinterpret_cast<void*>(FAKE + off); }
+static const uintptr_t GB = 1ull << 30;
+
+static kda_chunk_desc cdesc(int64_t B, int64_t H, int64_t T, int64_t dk = 128, int64_t dv = 128, int32_t ind = KDA_BF16,
+                            int32_t seg = 0) {
+    kda_chunk_desc d;
+    memset(&d, 0, sizeof(d));
+    d.B = B; d.H = H; d.T = T; d.dk = dk; d.dv = dv; d.chunk = 64; d.in_dtype = ind; d.out_dtype = KDA_BF16; d.segments = seg;
+    return d;
+}
+
+static kda_status fwd(const kda_chunk_desc* d, void* ws, size_t wsb, void* S0 = nullptr, void* ST = nullptr,
+                      void* o = P(5 * GB), void* q = P(0)) {
+    return kda_chunk_fwd(d, q, P(1 * GB), P(2 * GB), P(3 * GB), P(4 * GB), (const float*)S0, o, (float*)ST, ws, wsb, nullptr);
+}
+
+static void* scratch_stub(int) { return P(40 * GB); }
+
+static int check_status_strings() {
+    for (int s = 0; s >= -5; --s) CHECK(strncmp(kda_status_string(s), "KDA_", 4) == 0);
+    CHECK(strcmp(kda_status_string(1234), "unknown kda_status") == 0);
+    CHECK(strncmp(kda_version(), "kda-gfx950", 10) == 0);
+    return 0;
+}
+
+static int check_chunk() {
+    kda_chunk_desc d = cdesc(1, 2, 128);
+    CHECK(kda_chunk_fwd_workspace_bytes(nullptr) == 0);
+    CHECK(fwd(nullptr, nullptr, 0) == KDA_ERR_INVALID_ARG);
+    kda_chunk_desc bad = d; bad.B = 0; CHECK(fwd(&bad, nullptr, 0) == KDA_ERR_INVALID_ARG);
+    bad = d; bad.T = -1; CHECK(fwd(&bad, nullptr, 0) == KDA_ERR_INVALID_ARG);
+    bad = d; bad.chunk = 32; CHECK(fwd(&bad, nullptr, 0) == KDA_ERR_UNSUPPORTED);
+    bad = d; bad.dk = 96; CHECK(fwd(&bad, nullptr, 0) == KDA_ERR_UNSUPPORTED);
+    bad = d; bad.in_dtype = 9; CHECK(fwd(&bad, nullptr, 0) == KDA_ERR_INVALID_ARG);
+    bad = cdesc(1, 1, (int64_t)1 << 23); CHECK(fwd(&bad, nullptr, 0) == KDA_ERR_UNSUPPORTED);   // 32-bit row offsets
+    const size_t need = kda_chunk_fwd_workspace_bytes(&d);
+    CHECK(need > 0);
+    reset();
+    CHECK(fwd(&d, nullptr, 0) == KDA_ERR_WORKSPACE);
+    CHECK(fwd(&d, P(7 * GB), need - 1) == KDA_ERR_WORKSPACE);
+    CHECK(fwd(&d, P(7 * GB + 8), need) == KDA_ERR_INVALID_ARG);        // misaligned workspace
+    CHECK(fwd(&d, P(64), need) == KDA_ERR_INVALID_ARG);                // workspace overlaps q
+    CHECK(fwd(&d, P(7 * GB), need, nullptr, P(256)) == KDA_ERR_INVALID_ARG);          // S_T inside q
+    CHECK(fwd(&d, P(7 * GB), need, P(6 * GB), P(6 * GB + 1024)) == KDA_ERR_INVALID_ARG);  // partial S0 / S_T overlap
+    CHECK(fwd(&d, P(7 * GB), need, nullptr, nullptr, P(64)) == KDA_ERR_INVALID_ARG);  // o overlaps q
+    CHECK(fwd(&d, P(7 * GB), need, nullptr, nullptr, P(5 * GB), P(8)) == KDA_ERR_INVALID_ARG);  // misaligned q
+    CHECK(g_intra == 0 && g_inter == 0);                                // nothing enqueued on an error
+    // valid calls: one pass, a forced split (intra, pass 1, scan, pass 2), in-place state, T = 0, fp32
+    CHECK(fwd(&d, P(7 * GB), need, P(6 * GB), P(6 * GB)) == KDA_OK);
+    CHECK(g_intra == 1 && g_inter >= 1);
+    kda_chunk_desc s4 = cdesc(1, 2, 64 * 40, 128, 128, KDA_BF16, 4);
+    const size_t need4 = kda_chunk_fwd_workspace_bytes(&s4);
+    reset();
+    CHECK(fwd(&s4, P(7 * GB), need4, nullptr, P(6 * GB)) == KDA_OK);
+    CHECK(g_intra == 1 && g_inter == 2 && g_scan == 1 && g_last.nseg == 4 && g_last.fin_seg_lo == 1);
+    kda_chunk_desc z = cdesc(1, 2, 0);
+    reset();
+    CHECK(fwd(&z, nullptr, 0, nullptr, P(6 * GB)) == KDA_OK && g_copy == 1);
+    kda_chunk_desc f = cdesc(1, 1, 256, 64, 64, KDA_F32);
+    CHECK(kda_chunk_fwd_workspace_bytes(&f) == 0);
+    reset();
+    CHECK(fwd(&f, nullptr, 0) == KDA_OK && g_chunk == 1 && g_intra == 0);
+    // the no-allocation variant: scratch looked up only after validation, too-large calls refused
+    reset();
+    CHECK(kda::chunk_fwd_impl(&d, P(0), P(GB), P(2 * GB), P(3 * GB), P(4 * GB), nullptr, P(5 * GB), nullptr, nullptr, 0,
+                              nullptr, scratch_stub) == KDA_OK);
+    kda_chunk_desc big = cdesc(1, 32, 8192);
+    CHECK(kda::chunk_fwd_impl(&big, P(0), P(GB), P(2 * GB), P(3 * GB), P(4 * GB), nullptr, P(5 * GB), nullptr, nullptr, 0,
+                              nullptr, scratch_stub) == KDA_ERR_SCRATCH);
+    CHECK(kda::chunk_fwd_impl(&d, nullptr, P(GB), P(2 * GB), P(3 * GB), P(4 * GB), nullptr, P(5 * GB), nullptr, nullptr,
+                              0, nullptr, scratch_stub) == KDA_ERR_INVALID_ARG);
+    return 0;
+}
+
+static int check_varlen() {
+    kda_varlen_desc d;
+    memset(&d, 0, sizeof(d));
+    d.N = 3; d.H = 2; d.T = 640; d.max_len = 512; d.dk = 128; d.dv = 128; d.chunk = 64; d.in_dtype = KDA_BF16;
+    d.out_dtype = KDA_BF16; d.ckpt_every = 128; d.packed = 1;
+    const size_t need = kda_chunk_fwd_varlen_workspace_bytes(&d);
+    CHECK(need > 0);
+    auto call = [&](const kda_varlen_desc* dd, void* cu, void* ck, void* cko, const kda_gating* g, void* ws, size_t wsb,
+                    void* la = P(3 * GB)) {
+        return kda_chunk_fwd_varlen(dd, P(0), P(GB), P(2 * GB), la, P(4 * GB), (const int32_t*)cu, nullptr, P(5 * GB),
+                                    (float*)P(6 * GB), (float*)ck, (int32_t*)cko, g, ws, wsb, nullptr);
+    };
+    reset();
+    CHECK(call(&d, P(8 * GB), P(9 * GB), P(10 * GB), nullptr, P(11 * GB), need) == KDA_OK);
+    CHECK(g_prep == 1 && g_intra == 1 && g_inter >= 1);
+    CHECK(call(&d, nullptr, P(9 * GB), P(10 * GB), nullptr, P(11 * GB), need) == KDA_ERR_INVALID_ARG);   // packed needs cu
+    CHECK(call(&d, P(8 * GB), P(9 * GB), nullptr, nullptr, P(11 * GB), need) == KDA_ERR_INVALID_ARG);   // needs offsets
+    CHECK(call(&d, P(8 * GB), P(9 * GB), P(9 * GB + 64), nullptr, P(11 * GB), need) == KDA_ERR_INVALID_ARG);  // overlap
+    CHECK(call(&d, P(8 * GB), P(9 * GB), P(10 * GB), nullptr, P(11 * GB), need - 1) == KDA_ERR_WORKSPACE);
+    kda_varlen_desc e = d; e.ckpt_every = 100; CHECK(call(&e, P(8 * GB), P(9 * GB), P(10 * GB), nullptr, P(11 * GB), need) == KDA_ERR_INVALID_ARG);
+    kda_gating g;
+    memset(&g, 0, sizeof(g));
+    g.z = P(12 * GB); g.A_log = (const float*)P(13 * GB); g.g_min = -5.f; g.gate = P(14 * GB); g.eps = 1e-6f;
+    reset();
+    CHECK(call(&d, P(8 * GB), P(9 * GB), P(10 * GB), &g, P(11 * GB), need, nullptr) == KDA_OK && g_intra == 1);
+    g.g_min = 0.f;
+    CHECK(call(&d, P(8 * GB), P(9 * GB), P(10 * GB), &g, P(11 * GB), need, nullptr) == KDA_ERR_INVALID_ARG);
+    return 0;
+}
+
+static int check_bwd_and_decode() {
+    kda_chunk_desc d = cdesc(1, 2, 256);
+    const size_t need = kda_chunk_bwd_workspace_bytes(&d);
+    CHECK(need > kda_chunk_fwd_workspace_bytes(&d));
+    auto bwd = [&](void* q, void* ws, size_t wsb) {
+        return kda_chunk_bwd(&d, q, P(GB), P(2 * GB), P(3 * GB), P(4 * GB), nullptr, P(5 * GB), nullptr, (float*)P(6 * GB),
+                             (float*)P(7 * GB), (float*)P(8 * GB), (float*)P(9 * GB), (float*)P(10 * GB),
+                             (float*)P(11 * GB), ws, wsb, nullptr);
+    };
+    reset();
+    CHECK(bwd(P(0), P(12 * GB), need) == KDA_OK && g_bwd == 1 && g_intra == 1);
+    CHECK(bwd(P(4), P(12 * GB), need) == KDA_ERR_INVALID_ARG);          // 16-byte alignment of q
+    CHECK(bwd(P(0), P(12 * GB + 16), need) == KDA_ERR_INVALID_ARG);     // 256-byte workspace alignment
+    CHECK(bwd(P(0), P(12 * GB), need - 1) == KDA_ERR_WORKSPACE);
+    kda_decode_desc dd;
+    memset(&dd, 0, sizeof(dd));
+    dd.N = 4; dd.H = 2; dd.dk = 128; dd.dv = 128; dd.in_dtype = KDA_BF16; dd.out_dtype = KDA_BF16;
+    reset();
+    CHECK(kda_decode_step(&dd, P(0), P(GB), P(2 * GB), P(3 * GB), P(4 * GB), (float*)P(5 * GB), P(6 * GB), nullptr) == KDA_OK);
+    CHECK(g_decode == 1);
+    CHECK(kda_decode_step(&dd, P(0), P(GB), P(2 * GB), P(3 * GB), P(4 * GB), (float*)P(5 * GB), P(5 * GB + 64), nullptr) ==
+          KDA_ERR_INVALID_ARG);                                          // o overlaps S
+    dd.dk = 80;
+    CHECK(kda_decode_step(&dd, P(0), P(GB), P(2 * GB), P(3 * GB), P(4 * GB), (float*)P(5 * GB), P(6 * GB), nullptr) ==
+          KDA_ERR_UNSUPPORTED);
+    return 0;
+}
+
+int main() {
+    if (check_status_strings() || check_chunk() || check_varlen() || check_bwd_and_decode()) return 1;
+    printf("abi host check: ok\n");
+    return 0;
+}
