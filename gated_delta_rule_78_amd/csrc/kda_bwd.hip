@@ -645,8 +645,6 @@ __global__ __launch_bounds__(kTG) void bwd_grad_kernel(BwdArgs a) {
     constexpr int NH = A::NH, LH = A::LH, LK = A::LK, LV = A::LV, LA = A::LA;
     constexpr int NGR = kTG / kC;     // threads per row
     constexpr int CG = DK / NGR;      // channels per thread: thread = (row t, channel group)
-    constexpr int VG = DV / NGR;      // value columns per thread
-    constexpr int JG = kC / NGR;      // columns of A_qk / A_kk per thread
     extern __shared__ __align__(16) unsigned char smem_raw[];
     float* ar = reinterpret_cast<float*>(smem_raw);
     float* beta = ar + A::BETA;
@@ -667,7 +665,6 @@ __global__ __launch_bounds__(kTG) void bwd_grad_kernel(BwdArgs a) {
     const int t = tid / NGR;                 // row of this thread in the (row, group) tiles
     const int gi = tid % NGR;
     const int c0 = gi * CG;                  // its channels
-    const int j0 = gi * VG;                  // its value columns
     if (tid < kC) beta[tid] = tid < nrows ? ldin((const bf16_t*)a.beta, row0 + tid) : 0.f;
 
     // ---------------- phase 1: V~ = U - W S, and the products over the value columns ----------
@@ -718,7 +715,7 @@ __global__ __launch_bounds__(kTG) void bwd_grad_kernel(BwdArgs a) {
     // the two halves are written out (no loop) so that the registers a prefetch fills are the ones
     // the next half reads, with no copies that would wait for the loads
     auto half = [&](auto hc) {
-        constexpr int h = decltype(hc)::value, jh = h * NH;
+        constexpr int h = decltype(hc)::value;
         ts.store(sS, LH, S != nullptr);
         tgx.store(sGx, LH);
         tdv.store(sdVt, LH);
