@@ -62,7 +62,7 @@ def decode_alg(N, H, d, in_bytes=2, out_bytes=2):
 # Measured HBM traffic (rocprofv3 FETCH_SIZE / WRITE_SIZE, calibrated) comes from the committed
 # profile summaries; a figure is used only while the kernel sources it was taken on are unchanged.
 TRAFFIC_FILES = [os.path.join(ROOT, "profiles", f) for f in ("hbm_traffic_prefill_1m.md",
-                                                             "hbm_traffic_prefill_8k_and_decode.md")]
+                                                             "hbm_traffic_prefill_8k_64k_packed.md")]
 MFMA_FILES = [os.path.join(ROOT, "profiles", "mfma_counters_prefill_1m.md")]
 PREFILL_SOURCES = ["kda_intra.hip", "kda_inter.hip", "kda_scan.hip", "kda_record.h", "kda_mfma.h", "kda_device.h",
                    "kda_plan.h", "kda_plan.cpp"]
@@ -284,12 +284,15 @@ def main():
                   "value": pw.T / (pms * 1e-3), "unit": "tokens/s", "ms_per_step": pms, "ckpt_every": E,
                   "checkpoints_per_call": n_ck,
                   "roofline": {"bound": "hbm", "achieved": pgbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                               "frac": pgbs / HBM_PEAK_GBS, "traffic": None},
+                               "frac": pgbs / HBM_PEAK_GBS,
+                               "traffic": measured_traffic("call", pw.name, PREFILL_SOURCES)},
                   "alg_bytes_per_call": pby,
                   "fused_gating": {"what": "decay from z (g = -5 sigmoid(e^A z)) and y = sigmoid(gate) RMSNorm(o)",
                                    "value": pw.T / (fms * 1e-3), "unit": "tokens/s", "ms_per_step": fms,
                                    "roofline": {"bound": "hbm", "achieved": fgbs, "peak": HBM_PEAK_GBS,
-                                                "unit": "GB/s", "frac": fgbs / HBM_PEAK_GBS, "traffic": None},
+                                                "unit": "GB/s", "frac": fgbs / HBM_PEAK_GBS,
+                                                "traffic": measured_traffic("call", pw.name + ", fused gating",
+                                                                            PREFILL_SOURCES)},
                                    "alg_bytes_per_call": fby}}
         del pq, pk, pv, pla, pbeta, po, pws
 
