@@ -23,6 +23,9 @@
 //   FINISH  columns [0, dv): exact entry state in, o written, exit state stored as asked.
 //   SUMMARY columns [0, dv + dk) = [S~ | M] with entry [0 | I] and U = 0 on the M columns: the
 //           affine pair S_out = S~ + M S_in of the segment, no o.
+//   WINDOW  the SUMMARY role over the last few chunks before a segment boundary (SplitPass). A
+//           decay strong enough to drive M to exactly zero in fp32 within the window makes S~
+//           the exact state at the boundary: everything earlier reaches it only through M.
 #include "kda_internal.h"
 #include "kda_mfma.h"
 #include "kda_record.h"
@@ -48,6 +51,7 @@ template <int DK, int DV>
 struct __align__(16) InterSmem {
     unsigned char rec[2][RecordLayout<DK, DV>::BYTES];
     float ssq[2][4][64];    // fused epilogue: per-wave partial sums of o^2 per token, by chunk parity
+    int nonzero[4];         // WINDOW: per wave, whether its share of M has a nonzero entry
 };
 
 // Store two 16-column output tiles of one token row (accumulator layout: lane (lq, l16) holds
@@ -260,6 +264,9 @@ __device__ __forceinline__ void run_segment(const ChunkLaunch& p, InterSmem<DK, 
     int64_t c_end = seg == p.nseg - 1 ? nchunks : c_begin + p.chunks_per_seg;
     if (c_end > nchunks) c_end = nchunks;
     if (c_begin > c_end) c_begin = c_end;
+    // WINDOW: the last win_chunks chunks up to the segment's end, across earlier segments if need be
+    const bool window = !FIN && p.split == kPassWindow;
+    if (window) c_begin = c_end > p.win_chunks ? c_end - p.win_chunks : 0;
     const int col0 = w * 16 * NT;   // FINISH: in [0, dv); SUMMARY: in [0, dv + dk)
 
     // ---- entry state: S[nt][M] holds rows 16M + 4lq + r, column col0 + 16nt + l16 ----------
@@ -277,13 +284,19 @@ __device__ __forceinline__ void run_segment(const ChunkLaunch& p, InterSmem<DK, 
                     for (int r = 0; r < 4; ++r)
                         S[nt][M][r] = entry ? entry[(16 * M + 4 * lq + r) * DVl + col0 + 16 * nt + l16] : 0.f;
         } else {
+            // a window from the lane's first chunk starts from S0 on the S~ columns
+            const float* s0 = window && c_begin == 0 && p.S0 ? p.S0 + lane * DK * DVl : nullptr;
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) {
-                const int diag = col0 + 16 * nt + l16 - DV;   // M column -> its unit row
+                const int col = col0 + 16 * nt + l16;
+                const int diag = col - DV;   // M column -> its unit row
 #pragma unroll
                 for (int M = 0; M < NM; ++M)
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) S[nt][M][r] = (16 * M + 4 * lq + r == diag) ? 1.f : 0.f;
+                    for (int r = 0; r < 4; ++r) {
+                        const int row = 16 * M + 4 * lq + r;
+                        S[nt][M][r] = (row == diag) ? 1.f : (s0 && col < DV ? s0[row * DVl + col] : 0.f);
+                    }
             }
         }
     }
@@ -435,6 +448,30 @@ __device__ __forceinline__ void run_segment(const ChunkLaunch& p, InterSmem<DK, 
 
 #undef KDA_CKPT_STORE
     // ---- exit state --------------------------------------------------------------------------
+    if (window) {
+        // S~ is the next segment's entry state; the flag says whether it is exact
+        float* dst = p.ws_entry + ((lane * p.nseg + seg + 1) * DK) * DVl;
+        int nz = 0;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            const int col = col0 + 16 * nt + l16;
+#pragma unroll
+            for (int M = 0; M < NM; ++M)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    if (col < DV) dst[(int64_t)(16 * M + 4 * lq + r) * DVl + col] = S[nt][M][r];
+                    else nz |= S[nt][M][r] != 0.f;   // NaN counts as nonzero
+                }
+        }
+        const bool wave_nz = __ballot(nz) != 0;
+        if (l == 0) sm.nonzero[w] = wave_nz ? 1 : 0;
+        __syncthreads();
+        if (tid == 0) {
+            const int any = sm.nonzero[0] | sm.nonzero[1] | sm.nonzero[2] | sm.nonzero[3];
+            p.ws_flag[lane * p.nseg + seg] = (c_begin == 0 || !any) ? 1 : 0;
+        }
+        return;
+    }
     float* dst = nullptr;
     int64_t ld_dst = DVl;
     if (!FIN) {
@@ -442,7 +479,8 @@ __device__ __forceinline__ void run_segment(const ChunkLaunch& p, InterSmem<DK, 
         ld_dst = DVl + DK;
     } else if (seg == p.nseg - 1) {
         dst = p.S_T ? p.S_T + lane * DK * DVl : nullptr;
-    } else if (seg == 0) {
+    } else if (seg == 0 && p.split != kPassFinish) {
+        // (pass 2 runs segment 0 only where the window already stored the next entry state)
         dst = p.ws_entry + ((lane * p.nseg + 1) * DK) * DVl;
     }
     if (dst) {
@@ -464,11 +502,16 @@ __global__ __launch_bounds__(kThreads, 1) void inter_kernel(ChunkLaunch p) {
     if (bid < n_fin) {
         const int64_t lane = uniform64(bid / p.fin_nseg);
         const int seg = (int)uniform64(p.fin_seg_lo + bid % p.fin_nseg);
+        if (p.split == kPassCarry || (p.split == kPassFinish && seg == 0)) {
+            const bool exact = window_split_exact(p.ws_flag + lane * p.nseg, p.nseg);
+            if (exact == (p.split == kPassCarry)) return;
+        }
         run_segment<TOut, DK, DV, DV / 64, true, GATED>(p, sm, lane, seg);
     } else {
         const int64_t b2 = bid - n_fin;
         const int64_t lane = uniform64(b2 / p.sum_nseg);
         const int seg = (int)uniform64(p.sum_seg_lo + b2 % p.sum_nseg);
+        if (p.split == kPassCarry && window_split_exact(p.ws_flag + lane * p.nseg, p.nseg)) return;
         run_segment<TOut, DK, DV, (DV + DK) / 64, false, false>(p, sm, lane, seg);
     }
 }

@@ -70,6 +70,14 @@ __device__ __forceinline__ int64_t uniform64(int64_t x) {
     return (int64_t)(((uint64_t)hi << 32) | lo);
 }
 
+// True when every window flag [0, nseg - 1) of a lane is set: the entry states of all its
+// segments came from the window launch of a sequence split, so its pass 1 and scan are skipped.
+__device__ __forceinline__ bool window_split_exact(const int32_t* flag, int nseg) {
+    int all = 1;
+    for (int s = 0; s + 1 < nseg; ++s) all &= flag[s];
+    return all != 0;
+}
+
 // Broadcast lane 15 of each 16-lane row to the whole row (DPP row_newbcast:15).
 __device__ __forceinline__ float row_bcast15(float x) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x15F, 0xf, 0xf, false));

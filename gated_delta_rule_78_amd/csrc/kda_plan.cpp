@@ -27,23 +27,53 @@ int compute_units(int dev) {
     return n;
 }
 
-// Sequence split of the bf16 state pass. One state-pass workgroup occupies a compute unit; with
-// n segments, pass 1 runs segment 0 plus n - 2 summaries per lane, pass 2 the n - 1 later
-// segments, each pass taking chunks_per_seg steps per round of `cus` workgroups (one per compute
-// unit). Pick the n with the fewest sequential chunk steps (the segment scan adds about two per
-// segment).
-static int64_t auto_segments(int64_t lanes, int64_t nchunks, int64_t cus) {
-    int64_t best = 1;
-    int64_t best_cost = nchunks * ceil_div(lanes, cus);
-    const int64_t nmax = nchunks / 4 < 64 ? nchunks / 4 : 64;
-    for (int64_t n = 3; n <= nmax; ++n) {
-        const int64_t cps = ceil_div(nchunks, n);
-        const int64_t nn = ceil_div(nchunks, cps);
-        if (nn < 3) continue;
-        const int64_t rounds = ceil_div(lanes * (nn - 1), cus);
-        const int64_t cost = cps * 2 * rounds + 2 * (nn - 2);
-        if (cost < best_cost) { best_cost = cost; best = nn; }
+// Sequence split of the bf16 state pass, with n segments per lane (SplitPass): a window launch
+// of kWindowChunks steps over lanes * (n - 1) workgroups, then either (every window exact, the
+// usual case) one FINISH pass over lanes * n workgroups, or pass 1 (segment 0 and n - 2
+// summaries per lane), the segment scan and pass 2 (n - 1 FINISH segments per lane).
+//
+// Modelled time of one state-pass launch, in microseconds: `cps` chunk steps per round of `cus`
+// workgroups. A step takes the longer of the chunk's dependent chain (about 3.2 us) and the
+// record bytes the round's workgroups move at about 5 TB/s: 87 KiB per FINISH step (record and
+// output rows), 49 KiB per SUMMARY step (fitted to kernel traces of 8K, 64K and 1M calls).
+static double pass_us(int64_t cps, int64_t fin, int64_t sum, int64_t cus) {
+    double t = 0.0;
+    for (int64_t left = fin + sum; left > 0;) {
+        const int64_t r = left < cus ? left : cus;
+        const int64_t f = fin < r ? fin : r;
+        const double bw = (87.0 * (double)f + 49.0 * (double)(r - f)) / 5000.0;
+        t += (double)cps * (bw > 3.2 ? bw : 3.2);
+        fin -= f;
+        left -= r;
     }
+    return t;
+}
+
+// Pick n: the shortest state pass when every window is exact, among the n whose fallback (a
+// window that is not exact: slow decay) stays within 20 % of the best fallback plan.
+static int64_t auto_segments(int64_t lanes, int64_t nchunks, int64_t cus) {
+    const int64_t nmax = nchunks < 64 ? nchunks : 64;
+    double fast[65], fallback[65];
+    bool valid[65] = {};
+    double best_fallback = 0.0;
+    for (int64_t n = 1; n <= nmax; ++n) {
+        const int64_t cps = ceil_div(nchunks, n);
+        if (ceil_div(nchunks, cps) != n) continue;   // the same split as a smaller n
+        if (n == 1) {
+            fast[n] = fallback[n] = pass_us(nchunks, lanes, 0, cus);
+        } else {
+            const int64_t w = kWindowChunks < nchunks ? kWindowChunks : nchunks;
+            const double window = pass_us(w, 0, lanes * (n - 1), cus);
+            const double scan = n > 2 ? 16.0 + 2.0 * (double)(n - 2) : 0.0;
+            fast[n] = window + 6.0 + pass_us(cps, lanes * n, 0, cus);
+            fallback[n] = window + pass_us(cps, lanes, lanes * (n - 2), cus) + scan + pass_us(cps, lanes * (n - 1), 0, cus);
+        }
+        valid[n] = true;
+        if (n == 1 || fallback[n] < best_fallback) best_fallback = fallback[n];
+    }
+    int64_t best = 1;
+    for (int64_t n = 2; n <= nmax; ++n)
+        if (valid[n] && fallback[n] <= 1.2 * best_fallback && fast[n] < fast[best]) best = n;
     return best;
 }
 
@@ -59,21 +89,22 @@ Plan make_plan(const Geometry& g) {
     nseg = nchunks > 0 ? ceil_div(nchunks, cps) : 1;  // no segment past the longest lane
     p.nseg = (int)nseg;
     p.chunks_per_seg = cps;
+    p.win_chunks = kWindowChunks;   // also past a shorter segment's start: a shorter window is never exact
     if (g.in_dtype == KDA_BF16 && nchunks > 0) {
         p.rec_bytes = (size_t)g.slots * (size_t)record_bytes(g.dk, g.dv);
         if (nseg > 1) {
             p.pair_bytes = (size_t)g.lanes * (size_t)nseg * (size_t)(g.dk * (g.dv + g.dk)) * sizeof(float);
             p.entry_bytes = (size_t)g.lanes * (size_t)nseg * (size_t)(g.dk * g.dv) * sizeof(float);
+            p.flag_bytes = (size_t)g.lanes * (size_t)nseg * sizeof(int32_t);
         }
         p.tab_bytes = (size_t)g.tab_slots * sizeof(SlotEntry);
     }
-    p.ws_bytes = p.rec_bytes + p.pair_bytes + p.entry_bytes + p.tab_bytes;
+    p.ws_bytes = p.rec_bytes + p.pair_bytes + p.entry_bytes + p.tab_bytes + p.flag_bytes;
     return p;
 }
 
 // bf16 prefill after validation: records of every chunk (state independent, fully parallel),
-// then the sequential state pass, split in two passes around the segment scan when the plan
-// has more than one segment per lane.
+// then the sequential state pass, split as above when the plan has more than one segment.
 kda_status run_bf16(ChunkLaunch& a, const Plan& plan, unsigned char* ws, hipStream_t st) {
     IntraArgs ia{};
     ia.lanes = a.lanes; ia.T = a.T; ia.nchunks = a.nchunks; ia.dk = a.dk; ia.dv = a.dv;
@@ -81,23 +112,32 @@ kda_status run_bf16(ChunkLaunch& a, const Plan& plan, unsigned char* ws, hipStre
     ia.rec = ws;
     ia.map = a.map;
     ia.gt = a.gt;
-    ia.slot_tab = a.map.cu ? reinterpret_cast<const SlotEntry*>(ws + plan.rec_bytes + plan.pair_bytes + plan.entry_bytes)
-                           : nullptr;
+    const size_t tab_off = plan.rec_bytes + plan.pair_bytes + plan.entry_bytes;
+    ia.slot_tab = a.map.cu ? reinterpret_cast<const SlotEntry*>(ws + tab_off) : nullptr;
     if (launch_intra(ia, st) != hipSuccess) return KDA_ERR_HIP;
     a.rec = ws;
     a.ws_pair = plan.pair_bytes ? reinterpret_cast<float*>(ws + plan.rec_bytes) : nullptr;
     a.ws_entry = plan.entry_bytes ? reinterpret_cast<float*>(ws + plan.rec_bytes + plan.pair_bytes) : nullptr;
+    a.ws_flag = plan.flag_bytes ? reinterpret_cast<int32_t*>(ws + tab_off + plan.tab_bytes) : nullptr;
+    a.win_chunks = plan.win_chunks;
     if (plan.nseg == 1) {
+        a.split = kPassAll;
         a.fin_seg_lo = 0; a.fin_nseg = 1; a.sum_seg_lo = 0; a.sum_nseg = 0;
         return launch_inter(a, st) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
     }
-    // pass 1: segment 0 from the known entry state; summaries of the middle segments
+    // windows: the entry state of every later segment, exact where the decay allows
+    a.split = kPassWindow;
+    a.fin_seg_lo = 0; a.fin_nseg = 0; a.sum_seg_lo = 0; a.sum_nseg = plan.nseg - 1;
+    if (launch_inter(a, st) != hipSuccess) return KDA_ERR_HIP;
+    // lanes with an inexact window: pass 1 (segment 0 from the known entry state, summaries of
+    // the middle segments), then the exact entry states from the segment scan
+    a.split = kPassCarry;
     a.fin_seg_lo = 0; a.fin_nseg = 1; a.sum_seg_lo = 1; a.sum_nseg = plan.nseg - 2;
     if (launch_inter(a, st) != hipSuccess) return KDA_ERR_HIP;
-    // exact entry state of every later segment
     if (launch_segment_scan(a, st) != hipSuccess) return KDA_ERR_HIP;
-    // pass 2: every later segment from its exact entry state
-    a.fin_seg_lo = 1; a.fin_nseg = plan.nseg - 1; a.sum_seg_lo = 0; a.sum_nseg = 0;
+    // pass 2: every segment from its exact entry state (segment 0 where pass 1 skipped it)
+    a.split = kPassFinish;
+    a.fin_seg_lo = 0; a.fin_nseg = plan.nseg; a.sum_seg_lo = 0; a.sum_nseg = 0;
     return launch_inter(a, st) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 

@@ -26,21 +26,30 @@ struct Geometry {
     int64_t cus;         // compute units of the device the call runs on
 };
 
-// Segments per lane, chunks per segment and workspace of a prefill call.
+// Chunks in the window that looks for an exact segment entry state (SplitPass): a decay of
+// about e^-16 per chunk per key channel (log alpha averaging -0.25 per token) leaves nothing of
+// the state 7 chunks back in fp32.
+constexpr int64_t kWindowChunks = 8;
+
+// Segments per lane, chunks per segment and workspace of a prefill call. The workspace holds,
+// in this order: records, affine pairs, entry states, slot table, window flags.
 struct Plan {
     int nseg;
     int64_t nchunks, chunks_per_seg;
+    int64_t win_chunks;  // chunks per window (nseg > 1), kWindowChunks
     size_t rec_bytes;    // intra-chunk records (bf16 path): one per slot
     size_t pair_bytes;   // affine pairs [lanes][nseg][dk][dv + dk] (nseg > 1)
     size_t entry_bytes;  // entry states [lanes][nseg][dk][dv] (nseg > 1)
     size_t tab_bytes;    // slot table (packed batches)
+    size_t flag_bytes;   // window flags [lanes][nseg] int32 (nseg > 1)
     size_t ws_bytes;
 };
 
 Plan make_plan(const Geometry& g);
 
 // Launch a validated bf16 prefill on `st`: `a` carries the call's tensors and geometry, `ws` the
-// workspace of `plan` (at least plan.ws_bytes). Returns KDA_ERR_HIP if a launch fails.
+// workspace of `plan` (at least plan.ws_bytes). Every workspace byte a launch reads was written
+// earlier in the same call. Returns KDA_ERR_HIP if a launch fails.
 kda_status run_bf16(ChunkLaunch& a, const Plan& plan, unsigned char* ws, hipStream_t st);
 
 // kda_chunk_fwd (scratch_of == NULL) or kda_chunk_fwd_noalloc (scratch_of returns the device address

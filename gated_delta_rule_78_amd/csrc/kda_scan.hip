@@ -2,7 +2,7 @@
 // section 2.5: a segment acts on the state as the affine map S_out = S~ + M S_in, and such maps
 // compose associatively). Given entry_1 (the exit state of segment 0) and the pairs (S~_s, M_s)
 // of the middle segments, it forms the exact entry states entry_{s+1} = S~_s + M_s entry_s for
-// s = 1 .. nseg - 2, in fp32.
+// s = 1 .. nseg - 2, in fp32. Lanes whose window flags are all set (see SplitPass) are skipped.
 //
 // One workgroup per (lane, 16 state columns), one wave per 16-row output tile (8 waves at dk = 128,
 // two per SIMD, so that one wave's operand-load issue overlaps the other's products). The current
@@ -50,6 +50,8 @@ __global__ __launch_bounds__(DK == 128 ? 512 : 256) void segment_scan_kernel(Chu
     const int lq = l >> 4;
     const int64_t col = 16 * cb + l16;
     const int nseg = p.nseg;
+    // a lane whose entry states all came from the window launch has nothing to scan
+    if (window_split_exact(p.ws_flag + lane * nseg, nseg)) return;
 
     // entry tile: every load issued before the first LDS store (one memory round trip)
     const float* e1 = p.ws_entry + (lane * nseg + 1) * DK * DV;

@@ -90,7 +90,11 @@ typedef struct kda_decode_desc {
  *    log_alpha together;
  *  - with more than one sequence segment per lane, per-segment affine pairs (M, S~) with
  *    S_out = S~ + M S_in and the exact entry state of each segment (section 2.5: segment
- *    transforms compose associatively, and a prefix scan gives every segment its entry state).
+ *    transforms compose associatively, and a prefix scan gives every segment its entry state),
+ *    then one 4-byte flag per (lane, segment). The library first runs each segment boundary's
+ *    last 8 chunks from a zero state; where the decay drives that window's M to exactly zero
+ *    in fp32, the window's S~ is the boundary's exact state and the lane needs neither the
+ *    full-length affine pairs nor the scan.
  * The fp32 path needs no workspace.
  */
 size_t kda_chunk_fwd_workspace_bytes(const kda_chunk_desc* desc);
@@ -179,10 +183,10 @@ typedef struct kda_varlen_desc {
 } kda_varlen_desc;
 
 /* Bytes of device workspace kda_chunk_fwd_varlen needs for `desc` (0 for an invalid desc).
- * The same records, affine pairs and entry states as kda_chunk_fwd's workspace; a packed
+ * The same records, affine pairs, entry states and flags as kda_chunk_fwd's workspace; a packed
  * batch lays out records in T/64 + N chunk slots per head (sequence s's chunk c in slot
  * cu_seqlens[s]/64 + s + c, which never collide whatever the lengths) and adds a table of
- * 8 bytes per slot. */
+ * 8 bytes per slot (before the flags). */
 size_t kda_chunk_fwd_varlen_workspace_bytes(const kda_varlen_desc* desc);
 
 /*

@@ -14,6 +14,7 @@
 namespace {
 int g_intra, g_inter, g_scan, g_chunk, g_copy, g_prep, g_bwd, g_decode;
 kda::ChunkLaunch g_last;
+kda::ChunkLaunch g_inter_seq[8];   // the first state-pass launches since reset(), in order
 void reset() { g_intra = g_inter = g_scan = g_chunk = g_copy = g_prep = g_bwd = g_decode = 0; }
 }  // namespace
 
@@ -21,7 +22,11 @@ namespace kda {
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t) { ++g_decode; return a.S && a.o ? hipSuccess : hipErrorInvalidValue; }
 hipError_t launch_chunk(const ChunkLaunch& a, hipStream_t) { ++g_chunk; g_last = a; return hipSuccess; }
 hipError_t launch_intra(const IntraArgs& a, hipStream_t) { ++g_intra; return a.rec ? hipSuccess : hipErrorInvalidValue; }
-hipError_t launch_inter(const ChunkLaunch& a, hipStream_t) { ++g_inter; g_last = a; return hipSuccess; }
+hipError_t launch_inter(const ChunkLaunch& a, hipStream_t) {
+    if (g_inter < 8) g_inter_seq[g_inter] = a;
+    ++g_inter; g_last = a;
+    return hipSuccess;
+}
 hipError_t launch_segment_scan(const ChunkLaunch&, hipStream_t) { ++g_scan; return hipSuccess; }
 hipError_t launch_varlen_prep(const VarlenPrep&, hipStream_t) { ++g_prep; return hipSuccess; }
 hipError_t launch_copy_or_zero(float* dst, const float*, int64_t n, hipStream_t) { ++g_copy; return dst && n > 0 ? hipSuccess : hipErrorInvalidValue; }
@@ -98,7 +103,17 @@ static int check_chunk() {
     const size_t need4 = kda_chunk_fwd_workspace_bytes(&s4);
     reset();
     CHECK(fwd(&s4, P(7 * GB), need4, nullptr, P(6 * GB)) == KDA_OK);
-    CHECK(g_intra == 1 && g_inter == 2 && g_scan == 1 && g_last.nseg == 4 && g_last.fin_seg_lo == 1);
+    // windows (3 boundaries, 8 chunks each), pass 1 with its scan, pass 2 over all 4 segments;
+    // the flags are the workspace's last 2 x 4 int32
+    CHECK(g_intra == 1 && g_inter == 3 && g_scan == 1);
+    const kda::ChunkLaunch& w0 = g_inter_seq[0];
+    const kda::ChunkLaunch& w1 = g_inter_seq[1];
+    const kda::ChunkLaunch& w2 = g_inter_seq[2];
+    CHECK(w0.split == kda::kPassWindow && w0.fin_nseg == 0 && w0.sum_seg_lo == 0 && w0.sum_nseg == 3 && w0.win_chunks == 8);
+    CHECK(w1.split == kda::kPassCarry && w1.fin_seg_lo == 0 && w1.fin_nseg == 1 && w1.sum_seg_lo == 1 && w1.sum_nseg == 2);
+    CHECK(w2.split == kda::kPassFinish && w2.fin_seg_lo == 0 && w2.fin_nseg == 4 && w2.sum_nseg == 0 && w2.nseg == 4);
+    CHECK(w0.ws_flag == (int32_t*)((char*)P(7 * GB) + need4 - 2 * 4 * sizeof(int32_t)) && w2.ws_flag == w0.ws_flag);
+    CHECK((char*)w0.ws_entry + 2 * 4 * 128 * 128 * sizeof(float) == (char*)w0.ws_flag);
     kda_chunk_desc z = cdesc(1, 2, 0);
     reset();
     CHECK(fwd(&z, nullptr, 0, nullptr, P(6 * GB)) == KDA_OK && g_copy == 1);

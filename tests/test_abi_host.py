@@ -93,7 +93,9 @@ def test_workspace_query_and_check(lib):
     lanes, dk, dv, nchunks, nseg = 2, 128, 128, 40, 4
     d = _desc(B=1, H=lanes, T=64 * nchunks, seg=nseg)
     need = lib.kda_chunk_fwd_workspace_bytes(ctypes.byref(d))
-    assert need == lanes * nchunks * record_bytes(dk, dv) + lanes * nseg * dk * (2 * dv + dk) * 4
+    # records, then per (lane, segment) an affine pair [dk x (dv + dk)], an entry state [dk x dv]
+    # and a 4-byte window flag
+    assert need == lanes * nchunks * record_bytes(dk, dv) + lanes * nseg * (dk * (2 * dv + dk) + 1) * 4
     assert _chunk(lib, d) == WORKSPACE
     assert _chunk(lib, d, ws=FAKE + (7 << 30), ws_bytes=need - 1) == WORKSPACE
     assert _chunk(lib, d, ws=FAKE + (7 << 30) + 8, ws_bytes=need) == INVALID   # misaligned workspace
@@ -166,9 +168,10 @@ def test_varlen_workspace_query_and_check(lib):
     need = lib.kda_chunk_fwd_varlen_workspace_bytes(ctypes.byref(d))
     slots = T // 64 + N   # chunk slots per head: sequence s's chunk c sits in slot cu[s]/64 + s + c
     assert need == H * slots * record_bytes(dk, dv) + slots * 8
-    # with a split of the longest sequence (8 chunks) into 4 segments: affine pairs and entries per lane
+    # with a split of the longest sequence (8 chunks) into 4 segments: affine pairs, entries and
+    # window flags per lane
     d4 = _vdesc(N=N, H=H, T=T, max_len=512, seg=4)
-    assert lib.kda_chunk_fwd_varlen_workspace_bytes(ctypes.byref(d4)) == need + N * H * 4 * dk * (2 * dv + dk) * 4
+    assert lib.kda_chunk_fwd_varlen_workspace_bytes(ctypes.byref(d4)) == need + N * H * 4 * (dk * (2 * dv + dk) + 1) * 4
     assert _varlen(lib, d, ws=None, ws_bytes=0) == WORKSPACE
     assert _varlen(lib, d, ws_bytes=need - 1) == WORKSPACE
     assert _varlen(lib, d, ws=FAKE + (8 << 30) + 8, ws_bytes=need) == INVALID
