@@ -93,3 +93,39 @@ def test_window_split_dk64_dv128_fp32_out():
     assert_close("window dk64", BF16, host32(o).reshape(B * H, T, 128), o_ref, host32(S_T).reshape(B * H, 64, 128),
                  S_ref)
     assert (flags == 1).all(), flags
+
+
+def _random_cases(n, seed):
+    """Seeded fixed-length cases around the split's edges: T near multiples of 64 and of the window,
+    forced segment counts up to past the chunk count, decay per head from three ranges."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        dk, dv = [(128, 128), (64, 128), (128, 64), (64, 64)][int(rng.integers(0, 4))]
+        nch = int(rng.integers(1, 41))
+        T = max(1, 64 * nch - int(rng.choice([0, 0, 1, 17, 63])))
+        seg = int(rng.choice([0, 2, 3, 4, 5, 7, 9, 16, 64]))
+        cases.append((i, int(rng.integers(1, 3)), int(rng.integers(1, 4)), T, dk, dv, seg,
+                      bool(rng.integers(0, 2)), [int(x) for x in rng.integers(0, 3, 3)]))
+    return cases
+
+
+@pytest.mark.parametrize("case", _random_cases(24, 8500), ids=lambda c: "c%d" % c[0])
+def test_split_random_shapes(case):
+    """24 seeded shapes: every lane against the oracle, with each head's decay drawn from the
+    workload range, slow decay or the full domain, so that window, fallback and mixed launches all
+    occur at ragged lengths and forced segment counts."""
+    i, B, H, T, dk, dv, seg, s0, kinds = case
+    ranges = [synth.LOG_ALPHA_RANGE, SLOW, (-5.0, 0.0)]
+    say("random split %d: B=%d H=%d T=%d dk=%d dv=%d segments=%d S0=%s decay kinds %s" % (i, B, H, T, dk, dv, seg, s0, kinds[:H]))
+    q, k, v, la, beta, S0 = synth.prefill_inputs(B, H, T, dk, dv, BF16, device=DEV, seed_base=8600 + 10 * i,
+                                                 s0_std=0.3 if s0 else None)
+    for h in range(H):
+        lr = ranges[kinds[h]]
+        la[:, h] = synth.prefill_inputs(B, H, T, dk, dv, BF16, device=DEV, seed_base=8700 + 10 * i + h,
+                                        log_alpha_range=lr)[3][:, h]
+    o, S_T = kda.chunk_fwd(q, k, v, la, beta, S0, segments=seg)
+    torch.cuda.synchronize()
+    o_ref, S_ref = oracle_prefill(q, k, v, la, beta, S0)
+    assert_close("random split %d" % i, BF16, host32(o).reshape(B * H, T, dv), o_ref,
+                 host32(S_T).reshape(B * H, dk, dv), S_ref)
