@@ -23,9 +23,11 @@
 //   FINISH  columns [0, dv): exact entry state in, o written, exit state stored as asked.
 //   SUMMARY columns [0, dv + dk) = [S~ | M] with entry [0 | I] and U = 0 on the M columns: the
 //           affine pair S_out = S~ + M S_in of the segment, no o.
-//   WINDOW  the SUMMARY role over the last few chunks before a segment boundary (SplitPass). A
-//           decay strong enough to drive M to exactly zero in fp32 within the window makes S~
-//           the exact state at the boundary: everything earlier reaches it only through M.
+//   WINDOW  (the start of a FINISH segment s > 0 in the first launch of a split, SplitPass) the
+//           SUMMARY products over the last few chunks before the segment, on this wave's FINISH
+//           columns of S~ and its share of M's columns. A decay strong enough to drive M to exactly
+//           zero in fp32 within the window makes S~ the exact entry state (everything earlier
+//           reaches the boundary only through M), and the segment goes on from it at once.
 #include "kda_internal.h"
 #include "kda_mfma.h"
 #include "kda_record.h"
@@ -117,17 +119,18 @@ __device__ __forceinline__ void copy_record(__amdgpu_buffer_rsrc_t rsrc, uint32_
     }
 }
 
-// One chunk for state tiles G0 .. G0 + NTG - 1 of this wave (columns col0 + 16 nt + l16).
+// One chunk for state tiles G0 .. G0 + NTG - 1 of this wave. Tile nt < nu is value-column tile
+// col0 / 16 + nt (U added); the tiles from nu on are columns of M (U = 0; SUMMARY and WINDOW).
 // The next chunk's record copy (when `copy`) is issued in parts, one after each k step of the
 // first products: issued in one piece before them, its stalls (the copies queue behind the
 // record stream) kept the wave from starting the products for about a microsecond per chunk.
 template <typename TOut, int DK, int DV, int NT, int G0, int NTG, bool FIN>
-__device__ __forceinline__ void chunk_step(const unsigned char* rbuf, f32x4 (&S)[NT][DK / 16], int col0,
+__device__ __forceinline__ void chunk_step(const unsigned char* rbuf, f32x4 (&S)[NT][DK / 16], int col0, int nu,
                                            f32x4 (&Opend)[NT][4], bool copy, __amdgpu_buffer_rsrc_t crs,
                                            unsigned char* cdst, int w) {
     typedef CopyPlan<DK, DV, FIN> CP;
     typedef RecordLayout<DK, DV> R;
-    constexpr int NKS = R::NKS, NM = R::NM, NV = R::NV;
+    constexpr int NKS = R::NKS, NM = R::NM;
     const int l = threadIdx.x & 63;
     const int lq = l >> 4;
     const unsigned char* rb = rbuf + l * 16;
@@ -140,7 +143,7 @@ __device__ __forceinline__ void chunk_step(const unsigned char* rbuf, f32x4 (&S)
 #pragma unroll
     for (int nt = 0; nt < NTG; ++nt) {
         const int n = col0 / 16 + G0 + nt;
-        if (FIN || n < NV) {
+        if (FIN || G0 + nt < nu) {
             const bf16x8 u0 = KDA_FRAG(R::u(n, 0));
             const bf16x8 u1 = KDA_FRAG(R::u(n, 1));
             Vt[nt][0] = unpack4f(lo4(u0)); Vt[nt][1] = unpack4f(hi4(u0));
@@ -221,6 +224,66 @@ __device__ __forceinline__ void chunk_step(const unsigned char* rbuf, f32x4 (&S)
 #undef KDA_FRAG
 }
 
+// WINDOW ahead of FINISH segment seg > 0 of a lane: chunks [wb, we) with we = the segment's first
+// chunk and wb = max(0, we - win_chunks), from S~ = 0 (S0 when wb = 0) on this wave's FINISH columns
+// and M = I on its share of M's columns (16 MT consecutive ones). Stores the lane's flag for the
+// boundary and returns whether the window is exact (M = 0 in fp32, or wb = 0); then S holds S~.
+template <typename TOut, int DK, int DV, int NT>
+__device__ __forceinline__ bool window_entry(const ChunkLaunch& p, InterSmem<DK, DV>& sm, int64_t lane, int seg,
+                                             const unsigned char* rec0, int64_t we, int col0, f32x4 (&S)[NT][DK / 16]) {
+    typedef RecordLayout<DK, DV> R;
+    constexpr int NM = R::NM;
+    constexpr int BYTES = R::BYTES;
+    constexpr int MT = DK / 64;
+    constexpr int NW = NT + MT;
+    const int tid = threadIdx.x;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l = tid & 63;
+    const int l16 = l & 15;
+    const int lq = l >> 4;
+    const int64_t DVl = DV;
+    const int64_t wb = we > p.win_chunks ? we - p.win_chunks : 0;
+    const float* s0 = wb == 0 && p.S0 ? p.S0 + lane * DK * DVl : nullptr;
+    f32x4 X[NW][NM];
+#pragma unroll
+    for (int nt = 0; nt < NW; ++nt) {
+        const int mc = 16 * MT * w + 16 * (nt - NT) + l16;   // M column of an M tile
+#pragma unroll
+        for (int M = 0; M < NM; ++M)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = 16 * M + 4 * lq + r;
+                X[nt][M][r] = nt < NT ? (s0 ? s0[row * DVl + col0 + 16 * nt + l16] : 0.f) : (row == mc ? 1.f : 0.f);
+            }
+    }
+    f32x4 unused[NW][4];   // (no output rows: written only by FINISH products)
+    if (wb < we) copy_record<DK, DV, false>(make_rsrc(rec0 + wb * BYTES, BYTES), 0u, sm.rec[0], w, l);
+    for (int64_t c = wb; c < we; ++c) {
+        const int buf = (int)((c - wb) & 1);
+        __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0): this wave's copies of chunk c landed
+        __syncthreads();                        // ... and everyone's; buffer buf^1 is free again
+        chunk_step<TOut, DK, DV, NW, 0, NW, false>(sm.rec[buf], X, col0, NT, unused, c + 1 < we,
+                                                  make_rsrc(rec0 + (c + 1) * BYTES, BYTES), sm.rec[buf ^ 1], w);
+    }
+    int nz = 0;
+#pragma unroll
+    for (int j = 0; j < MT; ++j)
+#pragma unroll
+        for (int M = 0; M < NM; ++M)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) nz |= X[NT + j][M][r] != 0.f;   // NaN counts as nonzero
+    const bool wave_nz = __ballot(nz) != 0;
+    if (l == 0) sm.nonzero[w] = wave_nz ? 1 : 0;
+    __syncthreads();   // also: every wave is done with both record buffers
+    const bool exact = wb == 0 || !(sm.nonzero[0] | sm.nonzero[1] | sm.nonzero[2] | sm.nonzero[3]);
+    if (tid == 0) p.ws_flag[lane * p.nseg + seg - 1] = exact ? 1 : 0;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int M = 0; M < NM; ++M) S[nt][M] = X[nt][M];
+    return exact;
+}
+
 template <typename TOut, int DK, int DV, int NT, bool FIN, bool GATED>
 __device__ __forceinline__ void run_segment(const ChunkLaunch& p, InterSmem<DK, DV>& sm, int64_t lane, int seg) {
     typedef RecordLayout<DK, DV> R;
@@ -264,14 +327,16 @@ __device__ __forceinline__ void run_segment(const ChunkLaunch& p, InterSmem<DK, 
     int64_t c_end = seg == p.nseg - 1 ? nchunks : c_begin + p.chunks_per_seg;
     if (c_end > nchunks) c_end = nchunks;
     if (c_begin > c_end) c_begin = c_end;
-    // WINDOW: the last win_chunks chunks up to the segment's end, across earlier segments if need be
-    const bool window = !FIN && p.split == kPassWindow;
-    if (window) c_begin = c_end > p.win_chunks ? c_end - p.win_chunks : 0;
     const int col0 = w * 16 * NT;   // FINISH: in [0, dv); SUMMARY: in [0, dv + dk)
+    // one descriptor per chunk record: a lane's records may exceed 32-bit offsets
+    const unsigned char* rec0 = p.rec + slot0 * (int64_t)BYTES;
 
     // ---- entry state: S[nt][M] holds rows 16M + 4lq + r, column col0 + 16nt + l16 ----------
     f32x4 S[NT][NM];
-    {
+    if (FIN && p.split == kPassWindowFinish && seg > 0) {
+        // from the window before the segment; an inexact one leaves the segment to the fallback
+        if (!window_entry<TOut, DK, DV, NT>(p, sm, lane, seg, rec0, c_begin, col0, S)) return;
+    } else {
         if (FIN) {
             const float* entry = nullptr;
             if (seg > 0) entry = p.ws_entry + ((lane * p.nseg + seg) * DK) * DVl;
@@ -284,25 +349,17 @@ __device__ __forceinline__ void run_segment(const ChunkLaunch& p, InterSmem<DK, 
                     for (int r = 0; r < 4; ++r)
                         S[nt][M][r] = entry ? entry[(16 * M + 4 * lq + r) * DVl + col0 + 16 * nt + l16] : 0.f;
         } else {
-            // a window from the lane's first chunk starts from S0 on the S~ columns
-            const float* s0 = window && c_begin == 0 && p.S0 ? p.S0 + lane * DK * DVl : nullptr;
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) {
-                const int col = col0 + 16 * nt + l16;
-                const int diag = col - DV;   // M column -> its unit row
+                const int diag = col0 + 16 * nt + l16 - DV;   // M column -> its unit row
 #pragma unroll
                 for (int M = 0; M < NM; ++M)
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int row = 16 * M + 4 * lq + r;
-                        S[nt][M][r] = (row == diag) ? 1.f : (s0 && col < DV ? s0[row * DVl + col] : 0.f);
-                    }
+                    for (int r = 0; r < 4; ++r) S[nt][M][r] = (16 * M + 4 * lq + r == diag) ? 1.f : 0.f;
             }
         }
     }
 
-    // one descriptor per chunk record: a lane's records may exceed 32-bit offsets
-    const unsigned char* rec0 = p.rec + slot0 * (int64_t)BYTES;
     const __amdgpu_buffer_rsrc_t ro =
         make_rsrc(FIN ? (const TOut*)p.o + row_base * DVl : nullptr, FIN ? (uint32_t)(len * DVl * sizeof(TOut)) : 0u);
     // State checkpoint after chunk cc when it closes a checkpoint interval inside the lane
@@ -430,7 +487,7 @@ __device__ __forceinline__ void run_segment(const ChunkLaunch& p, InterSmem<DK, 
             KDA_STORE_O(c - 1);
         }
         KDA_LOAD_GATE(c);
-        chunk_step<TOut, DK, DV, NT, 0, NT, FIN>(sm.rec[buf], S, col0, Opend, c + 1 < c_end,
+        chunk_step<TOut, DK, DV, NT, 0, NT, FIN>(sm.rec[buf], S, col0, (int)(DV / 16) - col0 / 16, Opend, c + 1 < c_end,
                                                  make_rsrc(rec0 + (c + 1) * BYTES, BYTES), sm.rec[buf ^ 1], w);
         if (gated) KDA_EPI_PARTIAL(c);
     }
@@ -448,30 +505,6 @@ __device__ __forceinline__ void run_segment(const ChunkLaunch& p, InterSmem<DK, 
 
 #undef KDA_CKPT_STORE
     // ---- exit state --------------------------------------------------------------------------
-    if (window) {
-        // S~ is the next segment's entry state; the flag says whether it is exact
-        float* dst = p.ws_entry + ((lane * p.nseg + seg + 1) * DK) * DVl;
-        int nz = 0;
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-            const int col = col0 + 16 * nt + l16;
-#pragma unroll
-            for (int M = 0; M < NM; ++M)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    if (col < DV) dst[(int64_t)(16 * M + 4 * lq + r) * DVl + col] = S[nt][M][r];
-                    else nz |= S[nt][M][r] != 0.f;   // NaN counts as nonzero
-                }
-        }
-        const bool wave_nz = __ballot(nz) != 0;
-        if (l == 0) sm.nonzero[w] = wave_nz ? 1 : 0;
-        __syncthreads();
-        if (tid == 0) {
-            const int any = sm.nonzero[0] | sm.nonzero[1] | sm.nonzero[2] | sm.nonzero[3];
-            p.ws_flag[lane * p.nseg + seg] = (c_begin == 0 || !any) ? 1 : 0;
-        }
-        return;
-    }
     float* dst = nullptr;
     int64_t ld_dst = DVl;
     if (!FIN) {
@@ -479,8 +512,7 @@ __device__ __forceinline__ void run_segment(const ChunkLaunch& p, InterSmem<DK, 
         ld_dst = DVl + DK;
     } else if (seg == p.nseg - 1) {
         dst = p.S_T ? p.S_T + lane * DK * DVl : nullptr;
-    } else if (seg == 0 && p.split != kPassFinish) {
-        // (pass 2 runs segment 0 only where the window already stored the next entry state)
+    } else if (seg == 0) {   // segment 1's entry state, for the fallback's scan
         dst = p.ws_entry + ((lane * p.nseg + 1) * DK) * DVl;
     }
     if (dst) {
@@ -502,10 +534,8 @@ __global__ __launch_bounds__(kThreads, 1) void inter_kernel(ChunkLaunch p) {
     if (bid < n_fin) {
         const int64_t lane = uniform64(bid / p.fin_nseg);
         const int seg = (int)uniform64(p.fin_seg_lo + bid % p.fin_nseg);
-        if (p.split == kPassCarry || (p.split == kPassFinish && seg == 0)) {
-            const bool exact = window_split_exact(p.ws_flag + lane * p.nseg, p.nseg);
-            if (exact == (p.split == kPassCarry)) return;
-        }
+        // the fallback's pass 2 finishes only the segments whose window was not exact
+        if (p.split == kPassFinish && p.ws_flag[lane * p.nseg + seg - 1] != 0) return;
         run_segment<TOut, DK, DV, DV / 64, true, GATED>(p, sm, lane, seg);
     } else {
         const int64_t b2 = bid - n_fin;

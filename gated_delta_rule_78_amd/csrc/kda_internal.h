@@ -45,17 +45,17 @@ struct SlotEntry {
 };
 
 // Launches of a sequence split (ChunkLaunch::split; kda_plan.cpp runs them in this order):
-//   kPassWindow  one block per (lane, segment s < nseg - 1): the SUMMARY role over the last
-//                win_chunks chunks of the lane that end where segment s ends (from the lane's
-//                first chunk, with S0, if the window reaches it). When the window's transition
-//                M is exactly zero in fp32 (or the window starts at chunk 0), its S~ is the entry
-//                state of segment s + 1; it goes to ws_entry and flag [lane][s] is set to 1.
-//   kPassCarry   pass 1 (segment 0 and the SUMMARY roles): skipped by lanes whose flags are all set.
+//   kPassWindowFinish  FINISH of every segment of every lane. A segment s > 0 first runs the
+//                SUMMARY products over the last win_chunks chunks of the lane before it (from the
+//                lane's first chunk, with S0, if the window reaches it). When the window's
+//                transition M is exactly zero in fp32 (or the window starts at chunk 0), its S~ is
+//                the segment's exact entry state and the segment goes on from it; flag [lane][s - 1]
+//                says which. Segment 0 also stores its exit state (segment 1's entry) for the scan.
+//   kPassCarry   SUMMARY of segments 1 .. nseg - 2, skipped by lanes whose flags are all set.
 //   (segment scan, skipped by those lanes too)
-//   kPassFinish  pass 2, FINISH of segments [0, nseg): segment 0 only in lanes whose flags are all
-//                set (the others ran it in pass 1), without storing its exit state.
+//   kPassFinish  FINISH of segments 1 .. nseg - 1 whose flag is 0, from the scanned entry states.
 // kPassAll is a single-segment call (and the fp32 path).
-enum SplitPass { kPassAll = 0, kPassWindow = 1, kPassCarry = 2, kPassFinish = 3 };
+enum SplitPass { kPassAll = 0, kPassWindowFinish = 1, kPassCarry = 2, kPassFinish = 3 };
 
 // One launch of the chunk kernels. Blocks [0, n_fin) run FINISH work (exact entry state, write
 // o and, for the last segment, S_T); the following n_sum blocks run SUMMARY work (affine pair
@@ -78,7 +78,7 @@ struct ChunkLaunch {
     float* ws_entry;        // [lanes][nseg][dk][dv]        exact entry state of each segment
     int32_t* ws_flag;       // [lanes][nseg]                window flags (see SplitPass)
     int split;              // SplitPass of this launch
-    int64_t win_chunks;     // kPassWindow: chunks per window
+    int64_t win_chunks;     // kPassWindowFinish: chunks per window
     SeqMap map;
     // State checkpoints (bf16 path): after every ck_chunks chunks of a lane (s, h), the state
     // goes to ckpt[(ck_off[s] + j - 1) * H + h] (packed) or ckpt[(s * ck_per_lane + j - 1) * H + h]

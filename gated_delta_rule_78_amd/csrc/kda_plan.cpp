@@ -27,34 +27,42 @@ int compute_units(int dev) {
     return n;
 }
 
-// Sequence split of the bf16 state pass, with n segments per lane (SplitPass): a window launch
-// of kWindowChunks steps over lanes * (n - 1) workgroups, then either (every window exact, the
-// usual case) one FINISH pass over lanes * n workgroups, or pass 1 (segment 0 and n - 2
-// summaries per lane), the segment scan and pass 2 (n - 1 FINISH segments per lane).
+// Sequence split of the bf16 state pass, with n segments per lane (SplitPass): one FINISH launch
+// over lanes * n workgroups in which segments 1 .. n - 1 first run a kWindowChunks-chunk window,
+// then, only for lanes with an inexact window (slow decay), pass 1 (n - 2 summaries per lane), the
+// segment scan and pass 2 (the inexact segments).
 //
 // Modelled time of one state-pass launch, in microseconds: `cps` chunk steps per round of `cus`
-// workgroups. A step takes the longer of the chunk's dependent chain (about 3.2 us) and the
-// record bytes the round's workgroups move at about 5 TB/s: 87 KiB per FINISH step (record and
-// output rows), 49 KiB per SUMMARY step (fitted to kernel traces of 8K, 64K and 1M calls).
+// workgroups. A step takes the longer of the chunk's dependent chain (about 3.5 us with FINISH
+// workgroups in the round, 3.2 us with SUMMARY ones only) and the record bytes the round's
+// workgroups move at about 5 TB/s: 87 KiB per FINISH step (record and output rows), 49 KiB per
+// SUMMARY step (fitted to kernel traces of 8K, 64K and 1M calls; at 1M, 192 FINISH workgroups
+// took 3.47 us per step and 256 took 4.45 us).
 static double pass_us(int64_t cps, int64_t fin, int64_t sum, int64_t cus) {
     double t = 0.0;
     for (int64_t left = fin + sum; left > 0;) {
         const int64_t r = left < cus ? left : cus;
         const int64_t f = fin < r ? fin : r;
         const double bw = (87.0 * (double)f + 49.0 * (double)(r - f)) / 5000.0;
-        t += (double)cps * (bw > 3.2 ? bw : 3.2);
+        const double chain = f > 0 ? 3.5 : 3.2;
+        t += (double)cps * (bw > chain ? bw : chain);
         fin -= f;
         left -= r;
     }
     return t;
 }
 
-// Pick n: the shortest state pass when every window is exact, among the n whose fallback (a
-// window that is not exact: slow decay) stays within 20 % of the best fallback plan.
+// Pick n: the most segments whose FINISH workgroups (lanes * n) still run in one round on the
+// device's compute units, among the n whose fallback (a window that is not exact: slow decay)
+// stays within 20 % of the best fallback plan, unless one unsplit pass is modelled faster. (The
+// model's step times alone do not rank the splits: with fewer workgroups than compute units a
+// step is shorter, but at 8K the sweep n = 6, 7, 8 measured 0.2228, 0.2187, 0.2117 ms, and at 1M
+// n = 6 lost 1.3 % to n = 8.)
 static int64_t auto_segments(int64_t lanes, int64_t nchunks, int64_t cus) {
-    const int64_t nmax = nchunks < 64 ? nchunks : 64;
-    double fast[65], fallback[65];
-    bool valid[65] = {};
+    constexpr int64_t kMaxSeg = 256;
+    const int64_t nmax = nchunks < kMaxSeg ? nchunks : kMaxSeg;
+    double fast[kMaxSeg + 1], fallback[kMaxSeg + 1];
+    bool valid[kMaxSeg + 1] = {};
     double best_fallback = 0.0;
     for (int64_t n = 1; n <= nmax; ++n) {
         const int64_t cps = ceil_div(nchunks, n);
@@ -63,18 +71,19 @@ static int64_t auto_segments(int64_t lanes, int64_t nchunks, int64_t cus) {
             fast[n] = fallback[n] = pass_us(nchunks, lanes, 0, cus);
         } else {
             const int64_t w = kWindowChunks < nchunks ? kWindowChunks : nchunks;
-            const double window = pass_us(w, 0, lanes * (n - 1), cus);
+            const double empty = 4.5;   // a launch whose workgroups all return at once
             const double scan = n > 2 ? 16.0 + 2.0 * (double)(n - 2) : 0.0;
-            fast[n] = window + 6.0 + pass_us(cps, lanes * n, 0, cus);
-            fallback[n] = window + pass_us(cps, lanes, lanes * (n - 2), cus) + scan + pass_us(cps, lanes * (n - 1), 0, cus);
+            fast[n] = pass_us(cps + w, lanes * n, 0, cus) + (n > 2 ? 3.0 : 1.0) * empty;
+            fallback[n] = pass_us(cps > w ? cps : w, lanes * n, 0, cus) + pass_us(cps, 0, lanes * (n - 2), cus) + scan +
+                          pass_us(cps, lanes * (n - 1), 0, cus);
         }
         valid[n] = true;
         if (n == 1 || fallback[n] < best_fallback) best_fallback = fallback[n];
     }
     int64_t best = 1;
     for (int64_t n = 2; n <= nmax; ++n)
-        if (valid[n] && fallback[n] <= 1.2 * best_fallback && fast[n] < fast[best]) best = n;
-    return best;
+        if (valid[n] && lanes * n <= cus && fallback[n] <= 1.2 * best_fallback) best = n;
+    return fast[best] < fast[1] ? best : 1;
 }
 
 Plan make_plan(const Geometry& g) {
@@ -125,19 +134,18 @@ kda_status run_bf16(ChunkLaunch& a, const Plan& plan, unsigned char* ws, hipStre
         a.fin_seg_lo = 0; a.fin_nseg = 1; a.sum_seg_lo = 0; a.sum_nseg = 0;
         return launch_inter(a, st) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
     }
-    // windows: the entry state of every later segment, exact where the decay allows
-    a.split = kPassWindow;
-    a.fin_seg_lo = 0; a.fin_nseg = 0; a.sum_seg_lo = 0; a.sum_nseg = plan.nseg - 1;
+    // every segment, the later ones from the window before them where it is exact
+    a.split = kPassWindowFinish;
+    a.fin_seg_lo = 0; a.fin_nseg = plan.nseg; a.sum_seg_lo = 0; a.sum_nseg = 0;
     if (launch_inter(a, st) != hipSuccess) return KDA_ERR_HIP;
-    // lanes with an inexact window: pass 1 (segment 0 from the known entry state, summaries of
-    // the middle segments), then the exact entry states from the segment scan
+    // lanes with an inexact window: summaries of the middle segments, the exact entry states
+    // from the segment scan, then the segments whose window was inexact
     a.split = kPassCarry;
-    a.fin_seg_lo = 0; a.fin_nseg = 1; a.sum_seg_lo = 1; a.sum_nseg = plan.nseg - 2;
+    a.fin_seg_lo = 0; a.fin_nseg = 0; a.sum_seg_lo = 1; a.sum_nseg = plan.nseg - 2;
     if (launch_inter(a, st) != hipSuccess) return KDA_ERR_HIP;
     if (launch_segment_scan(a, st) != hipSuccess) return KDA_ERR_HIP;
-    // pass 2: every segment from its exact entry state (segment 0 where pass 1 skipped it)
     a.split = kPassFinish;
-    a.fin_seg_lo = 0; a.fin_nseg = plan.nseg; a.sum_seg_lo = 0; a.sum_nseg = 0;
+    a.fin_seg_lo = 1; a.fin_nseg = plan.nseg - 1; a.sum_seg_lo = 0; a.sum_nseg = 0;
     return launch_inter(a, st) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 

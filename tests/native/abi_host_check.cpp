@@ -103,15 +103,17 @@ static int check_chunk() {
     const size_t need4 = kda_chunk_fwd_workspace_bytes(&s4);
     reset();
     CHECK(fwd(&s4, P(7 * GB), need4, nullptr, P(6 * GB)) == KDA_OK);
-    // windows (3 boundaries, 8 chunks each), pass 1 with its scan, pass 2 over all 4 segments;
+    // FINISH of all 4 segments (windows of 8 chunks before segments 1..3), then the fallback:
+    // summaries of segments 1..2, the scan, FINISH of segments 1..3 whose window was inexact;
     // the flags are the workspace's last 2 x 4 int32
     CHECK(g_intra == 1 && g_inter == 3 && g_scan == 1);
     const kda::ChunkLaunch& w0 = g_inter_seq[0];
     const kda::ChunkLaunch& w1 = g_inter_seq[1];
     const kda::ChunkLaunch& w2 = g_inter_seq[2];
-    CHECK(w0.split == kda::kPassWindow && w0.fin_nseg == 0 && w0.sum_seg_lo == 0 && w0.sum_nseg == 3 && w0.win_chunks == 8);
-    CHECK(w1.split == kda::kPassCarry && w1.fin_seg_lo == 0 && w1.fin_nseg == 1 && w1.sum_seg_lo == 1 && w1.sum_nseg == 2);
-    CHECK(w2.split == kda::kPassFinish && w2.fin_seg_lo == 0 && w2.fin_nseg == 4 && w2.sum_nseg == 0 && w2.nseg == 4);
+    CHECK(w0.split == kda::kPassWindowFinish && w0.fin_seg_lo == 0 && w0.fin_nseg == 4 && w0.sum_nseg == 0 &&
+          w0.win_chunks == 8);
+    CHECK(w1.split == kda::kPassCarry && w1.fin_nseg == 0 && w1.sum_seg_lo == 1 && w1.sum_nseg == 2);
+    CHECK(w2.split == kda::kPassFinish && w2.fin_seg_lo == 1 && w2.fin_nseg == 3 && w2.sum_nseg == 0 && w2.nseg == 4);
     CHECK(w0.ws_flag == (int32_t*)((char*)P(7 * GB) + need4 - 2 * 4 * sizeof(int32_t)) && w2.ws_flag == w0.ws_flag);
     CHECK((char*)w0.ws_entry + 2 * 4 * 128 * 128 * sizeof(float) == (char*)w0.ws_flag);
     kda_chunk_desc z = cdesc(1, 2, 0);
