@@ -27,7 +27,8 @@
 //           SUMMARY products over the last few chunks before the segment, on this wave's FINISH
 //           columns of S~ and its share of M's columns. A decay strong enough to drive M to exactly
 //           zero in fp32 within the window makes S~ the exact entry state (everything earlier
-//           reaches the boundary only through M), and the segment goes on from it at once.
+//           reaches the boundary only through M), and the segment goes on from it at once;
+//           otherwise the workgroup computes the segment's SUMMARY for the fallback instead.
 #include "kda_internal.h"
 #include "kda_mfma.h"
 #include "kda_record.h"
@@ -284,8 +285,10 @@ __device__ __forceinline__ bool window_entry(const ChunkLaunch& p, InterSmem<DK,
     return exact;
 }
 
+// One segment of one lane in the given role. Returns false when a FINISH segment's window was not
+// exact (nothing of the segment was written then).
 template <typename TOut, int DK, int DV, int NT, bool FIN, bool GATED>
-__device__ __forceinline__ void run_segment(const ChunkLaunch& p, InterSmem<DK, DV>& sm, int64_t lane, int seg) {
+__device__ __forceinline__ bool run_segment(const ChunkLaunch& p, InterSmem<DK, DV>& sm, int64_t lane, int seg) {
     typedef RecordLayout<DK, DV> R;
     constexpr int NM = R::NM;
     constexpr int BYTES = R::BYTES;
@@ -335,7 +338,7 @@ __device__ __forceinline__ void run_segment(const ChunkLaunch& p, InterSmem<DK, 
     f32x4 S[NT][NM];
     if (FIN && p.split == kPassWindowFinish && seg > 0) {
         // from the window before the segment; an inexact one leaves the segment to the fallback
-        if (!window_entry<TOut, DK, DV, NT>(p, sm, lane, seg, rec0, c_begin, col0, S)) return;
+        if (!window_entry<TOut, DK, DV, NT>(p, sm, lane, seg, rec0, c_begin, col0, S)) return false;
     } else {
         if (FIN) {
             const float* entry = nullptr;
@@ -524,6 +527,7 @@ __device__ __forceinline__ void run_segment(const ChunkLaunch& p, InterSmem<DK, 
                 for (int r = 0; r < 4; ++r)
                     dst[(int64_t)(16 * M + 4 * lq + r) * ld_dst + col0 + 16 * nt + l16] = S[nt][M][r];
     }
+    return true;
 }
 
 template <typename TOut, int DK, int DV, bool GATED>
@@ -536,12 +540,20 @@ __global__ __launch_bounds__(kThreads, 1) void inter_kernel(ChunkLaunch p) {
         const int seg = (int)uniform64(p.fin_seg_lo + bid % p.fin_nseg);
         // the fallback's pass 2 finishes only the segments whose window was not exact
         if (p.split == kPassFinish && p.ws_flag[lane * p.nseg + seg - 1] != 0) return;
-        run_segment<TOut, DK, DV, DV / 64, true, GATED>(p, sm, lane, seg);
+        // A segment whose window was not exact computes its own affine pair instead (a middle
+        // segment; the scan needs no pair for the last one), so that under slow decay the
+        // summaries run beside segment 0 as in a plain two-pass split.
+        if (!run_segment<TOut, DK, DV, DV / 64, true, GATED>(p, sm, lane, seg) && seg < p.nseg - 1)
+            run_segment<TOut, DK, DV, (DV + DK) / 64, false, false>(p, sm, lane, seg);
     } else {
         const int64_t b2 = bid - n_fin;
         const int64_t lane = uniform64(b2 / p.sum_nseg);
         const int seg = (int)uniform64(p.sum_seg_lo + b2 % p.sum_nseg);
-        if (p.split == kPassCarry && window_split_exact(p.ws_flag + lane * p.nseg, p.nseg)) return;
+        // pass 1 of the fallback: the pairs the first launch did not compute (segments whose
+        // window was exact, in lanes where another window was not)
+        if (p.split == kPassCarry &&
+            (window_split_exact(p.ws_flag + lane * p.nseg, p.nseg) || p.ws_flag[lane * p.nseg + seg - 1] == 0))
+            return;
         run_segment<TOut, DK, DV, (DV + DK) / 64, false, false>(p, sm, lane, seg);
     }
 }

@@ -49,10 +49,11 @@ struct SlotEntry {
 //                SUMMARY products over the last win_chunks chunks of the lane before it (from the
 //                lane's first chunk, with S0, if the window reaches it). When the window's
 //                transition M is exactly zero in fp32 (or the window starts at chunk 0), its S~ is
-//                the segment's exact entry state and the segment goes on from it; flag [lane][s - 1]
-//                says which. Segment 0 also stores its exit state (segment 1's entry) for the scan.
-//   kPassCarry   SUMMARY of segments 1 .. nseg - 2, skipped by lanes whose flags are all set.
-//   (segment scan, skipped by those lanes too)
+//                the segment's exact entry state and the segment goes on from it; otherwise the
+//                workgroup computes the segment's affine pair (s < nseg - 1). Flag [lane][s - 1]
+//                says which (1: exact). Segment 0 also stores its exit state (segment 1's entry).
+//   kPassCarry   SUMMARY of segments 1 .. nseg - 2 whose flag is 1, in lanes with a flag 0.
+//   (segment scan, skipped by lanes whose flags are all 1)
 //   kPassFinish  FINISH of segments 1 .. nseg - 1 whose flag is 0, from the scanned entry states.
 // kPassAll is a single-segment call (and the fp32 path).
 enum SplitPass { kPassAll = 0, kPassWindowFinish = 1, kPassCarry = 2, kPassFinish = 3 };

@@ -28,9 +28,9 @@ int compute_units(int dev) {
 }
 
 // Sequence split of the bf16 state pass, with n segments per lane (SplitPass): one FINISH launch
-// over lanes * n workgroups in which segments 1 .. n - 1 first run a kWindowChunks-chunk window,
-// then, only for lanes with an inexact window (slow decay), pass 1 (n - 2 summaries per lane), the
-// segment scan and pass 2 (the inexact segments).
+// over lanes * n workgroups in which segments 1 .. n - 1 first run a kWindowChunks-chunk window
+// (and, where it is inexact under slow decay, compute their affine pair instead); then, only for
+// lanes with an inexact window, the missing pairs, the segment scan and the inexact segments.
 //
 // Modelled time of one state-pass launch, in microseconds: `cps` chunk steps per round of `cus`
 // workgroups. A step takes the longer of the chunk's dependent chain (about 3.5 us with FINISH
@@ -74,8 +74,8 @@ static int64_t auto_segments(int64_t lanes, int64_t nchunks, int64_t cus) {
             const double empty = 4.5;   // a launch whose workgroups all return at once
             const double scan = n > 2 ? 16.0 + 2.0 * (double)(n - 2) : 0.0;
             fast[n] = pass_us(cps + w, lanes * n, 0, cus) + (n > 2 ? 3.0 : 1.0) * empty;
-            fallback[n] = pass_us(cps > w ? cps : w, lanes * n, 0, cus) + pass_us(cps, 0, lanes * (n - 2), cus) + scan +
-                          pass_us(cps, lanes * (n - 1), 0, cus);
+            // (segments 1 .. n - 2 compute their pairs in the first launch, beside segment 0)
+            fallback[n] = pass_us(cps + w, lanes, lanes * (n - 1), cus) + empty + scan + pass_us(cps, lanes * (n - 1), 0, cus);
         }
         valid[n] = true;
         if (n == 1 || fallback[n] < best_fallback) best_fallback = fallback[n];
@@ -138,8 +138,8 @@ kda_status run_bf16(ChunkLaunch& a, const Plan& plan, unsigned char* ws, hipStre
     a.split = kPassWindowFinish;
     a.fin_seg_lo = 0; a.fin_nseg = plan.nseg; a.sum_seg_lo = 0; a.sum_nseg = 0;
     if (launch_inter(a, st) != hipSuccess) return KDA_ERR_HIP;
-    // lanes with an inexact window: summaries of the middle segments, the exact entry states
-    // from the segment scan, then the segments whose window was inexact
+    // lanes with an inexact window: the pairs of middle segments whose window was exact, the
+    // exact entry states from the segment scan, then the segments whose window was inexact
     a.split = kPassCarry;
     a.fin_seg_lo = 0; a.fin_nseg = 0; a.sum_seg_lo = 1; a.sum_nseg = plan.nseg - 2;
     if (launch_inter(a, st) != hipSuccess) return KDA_ERR_HIP;
