@@ -129,3 +129,23 @@ def test_split_random_shapes(case):
     o_ref, S_ref = oracle_prefill(q, k, v, la, beta, S0)
     assert_close("random split %d" % i, BF16, host32(o).reshape(B * H, T, dv), o_ref,
                  host32(S_T).reshape(B * H, dk, dv), S_ref)
+
+
+@pytest.mark.parametrize("order", ["fast_then_slow", "slow_then_fast"])
+def test_window_split_decay_changes_along_the_sequence(order):
+    """One lane's decay changes halfway (41 chunks in 4 segments of 11): some of its windows are
+    exact and some not. Fast then slow: segment 1 finishes from its window in the first launch and
+    the fallback's pass 1 computes its affine pair for the scan; slow then fast: the middle
+    segments compute their pairs in the first launch and the last segment finishes from its window."""
+    B, H, T, d = 1, 2, 64 * 40 + 17, 128
+    say("window decay change %s: B=%d H=%d T=%d" % (order, B, H, T))
+    q, k, v, la, beta, S0 = synth.prefill_inputs(B, H, T, d, d, BF16, device=DEV, seed_base=8900, s0_std=0.3)
+    la_slow = synth.prefill_inputs(B, H, T, d, d, BF16, device=DEV, seed_base=8950, log_alpha_range=SLOW)[3]
+    half = 64 * 20
+    if order == "fast_then_slow":
+        la[:, :, half:] = la_slow[:, :, half:]
+    else:
+        la[:, :, :half] = la_slow[:, :, :half]
+    flags = run_with_flags("window decay change " + order, q, k, v, la, beta, S0, segments=4)
+    expect = [1, 0, 0] if order == "fast_then_slow" else [0, 0, 1]
+    assert (flags == np.array(expect)).all(), flags
