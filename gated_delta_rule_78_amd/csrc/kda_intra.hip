@@ -433,9 +433,10 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs p) {
     }
     // the next chunk's rows load during the Gram phase: issued here rather than right after this
     // chunk's staging, they no longer queue behind the previous chunk's record stores at the top of
-    // the chunk, and their registers stay free through the decay phase
-    KDA_INTRA_LOAD(t + G < total, hn, jn);
+    // the chunk, and their registers stay free through the decay phase; issued after the barrier
+    // rather than before it, a wave stalled on issuing them no longer holds up the other three
     __syncthreads();
+    KDA_INTRA_LOAD(t + G < total, hn, jn);
 
     // ================= phase 2: Gram tiles ====================================================
     if (w == 0) {
