@@ -149,3 +149,24 @@ def test_window_split_decay_changes_along_the_sequence(order):
     flags = run_with_flags("window decay change " + order, q, k, v, la, beta, S0, segments=4)
     expect = [1, 0, 0] if order == "fast_then_slow" else [0, 0, 1]
     assert (flags == np.array(expect)).all(), flags
+
+
+def _random_packed(n, seed):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        N = int(rng.integers(1, 7))
+        lens = [int(x) for x in rng.choice([0, 1, 63, 64, 65, 300, 700, 1300, 2100], N)]
+        out.append((i, lens, int(rng.integers(1, 4)), int(rng.choice([0, 2, 3, 5, 9])), int(rng.choice([0, 64, 512])),
+                    int(rng.integers(0, 3))))
+    return out
+
+
+@pytest.mark.parametrize("case", _random_packed(10, 9100), ids=lambda c: "p%d" % c[0])
+def test_split_random_packed(case):
+    """10 seeded packed batches (lengths from empty to 33 chunks, 1-6 sequences, forced or planned
+    segment counts, checkpoints off, every 64 or every 512 tokens, one decay range per case): every
+    lane, final state and checkpoint against the oracle."""
+    i, lens, H, seg, E, kind = case
+    la_range = [synth.LOG_ALPHA_RANGE, SLOW, (-5.0, 0.0)][kind]
+    run_packed("random packed %d" % i, lens, H, 128, 128, E, segments=seg, seed=9200 + 10 * i, la_range=la_range)
