@@ -67,6 +67,8 @@ MFMA_FILES = [os.path.join(ROOT, "profiles", "mfma_counters_prefill_1m.md")]
 PREFILL_SOURCES = ["kda_intra.hip", "kda_inter.hip", "kda_scan.hip", "kda_record.h", "kda_mfma.h", "kda_device.h",
                    "kda_plan.h", "kda_plan.cpp"]
 DECODE_SOURCES = ["kda_decode.hip", "kda_device.h"]
+BACKWARD_SOURCES = PREFILL_SOURCES + ["kda_bwd.hip"]   # the backward reruns the forward first
+BWD_SUFFIX = ", backward (forward recompute included)"
 
 
 def sources_hash(files):
@@ -326,10 +328,11 @@ def main():
         # bytes: the forward's inputs, dO in, fp32 gradients of q, k, v, log_alpha, beta out, states
         bby = bw.B * bw.H * (bw.T * (4 * bw.d * 2 + 2 + bw.d * 2 + 4 * bw.d * 4 + 4) + 3 * bw.d * bw.d * 4)
         bgbs = bby / (bms * 1e-3) / 1e9
-        bwd = {"workload": bw.name + ", backward (forward recompute included)", "metric": "KDA backward tokens/s",
+        bwd = {"workload": bw.name + BWD_SUFFIX, "metric": "KDA backward tokens/s",
                "value": bw.B * bw.T / (bms * 1e-3), "unit": "tokens/s", "ms_per_step": bms, "steps": nb,
                "roofline": {"bound": "hbm", "achieved": bgbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                            "frac": bgbs / HBM_PEAK_GBS, "traffic": None},
+                            "frac": bgbs / HBM_PEAK_GBS,
+                            "traffic": measured_traffic("call", bw.name + BWD_SUFFIX, BACKWARD_SOURCES)},
                "alg_bytes_per_call": bby, "workspace_bytes": int(bws.numel())}
         del q, k, v, la, beta, S0, dO, dST, bws
         torch.cuda.empty_cache()
