@@ -64,8 +64,8 @@ def decode_alg(N, H, d, in_bytes=2, out_bytes=2):
 TRAFFIC_FILES = [os.path.join(ROOT, "profiles", f) for f in ("hbm_traffic_prefill_1m.md",
                                                              "hbm_traffic_prefill_8k_64k_packed.md")]
 MFMA_FILES = [os.path.join(ROOT, "profiles", "mfma_counters_prefill_1m.md")]
-PREFILL_SOURCES = ["kda_intra.hip", "kda_inter.hip", "kda_scan.hip", "kda_record.h", "kda_mfma.h", "kda_device.h",
-                   "kda_plan.h", "kda_plan.cpp"]
+PREFILL_SOURCES = ["kda_intra.hip", "kda_intra_chunk.h", "kda_inter.hip", "kda_step.h", "kda_fused.hip", "kda_scan.hip",
+                   "kda_record.h", "kda_mfma.h", "kda_device.h", "kda_plan.h", "kda_plan.cpp"]
 DECODE_SOURCES = ["kda_decode.hip", "kda_device.h"]
 BACKWARD_SOURCES = PREFILL_SOURCES + ["kda_bwd.hip"]   # the backward reruns the forward first
 BWD_SUFFIX = ", backward (forward recompute included)"
@@ -108,7 +108,7 @@ def log(msg):
     print("bench: " + msg, file=sys.stderr, flush=True)
 
 
-def time_prefill(kda, synth, torch, np, w, steps, warmup, segments, stream, keep_lanes=0):
+def time_prefill(kda, synth, torch, np, w, steps, warmup, segments, stream, keep_lanes=0, state_pass=0):
     """Time `steps` kda_chunk_fwd calls over workload `w` after `warmup` untimed ones. Returns the
     figures and, with keep_lanes > 0, host copies of the first keep_lanes lanes' inputs (for the
     CPU baseline) taken before the device tensors are freed."""
@@ -117,12 +117,12 @@ def time_prefill(kda, synth, torch, np, w, steps, warmup, segments, stream, keep
     q, k, v, la, beta, S0 = synth.workload_inputs(w, device=dev)
     o = torch.empty(w.B, w.H, w.T, w.d, device=dev, dtype=w.dtype)
     S_T = torch.empty(w.B, w.H, w.d, w.d, device=dev, dtype=torch.float32)
-    nbytes = kda.chunk_workspace_bytes(q, v, segments=segments)
+    nbytes = kda.chunk_workspace_bytes(q, v, segments=segments, state_pass=state_pass)
     ws = torch.empty(max(nbytes, 16), device=dev, dtype=torch.uint8)
 
     def step():
-        kda.chunk_fwd(q, k, v, la, beta, S0, out_dtype=w.dtype, segments=segments, o=o, S_T=S_T, workspace=ws,
-                      stream=stream)
+        kda.chunk_fwd(q, k, v, la, beta, S0, out_dtype=w.dtype, segments=segments, state_pass=state_pass, o=o, S_T=S_T,
+                      workspace=ws, stream=stream)
 
     log("timing %s: %d warm-up + %d timed calls" % (w.name, warmup, steps))
     for _ in range(warmup):
@@ -154,7 +154,8 @@ def time_prefill(kda, synth, torch, np, w, steps, warmup, segments, stream, keep
         "ms_per_step": ms_per_step, "call_ms": call_ms, "steps": steps, "warmup": warmup,
         "tokens_per_s_from_call_ms": w.B * w.T / (call_ms * 1e-3),
         "config": {"workload": w.name, "B": w.B, "H": w.H, "T": w.T, "dk": w.d, "dv": w.d, "chunk": 64,
-                   "s0": S0 is not None, "segments": segments or "auto", "workspace_bytes": nbytes},
+                   "s0": S0 is not None, "segments": segments or "auto",
+                   "state_pass": {0: "auto", 1: "two kernels", 2: "fused"}[state_pass], "workspace_bytes": nbytes},
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": gbs / HBM_PEAK_GBS, "traffic": measured_traffic("call", w.name, PREFILL_SOURCES)},
         "mfma": {"alg_tflops": flops / (call_ms * 1e-3) / 1e12, "dense_tile_tflops": dense / (call_ms * 1e-3) / 1e12,
@@ -180,6 +181,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="prefill_1m", choices=sorted(WORKLOADS))
     ap.add_argument("--segments", type=int, default=0, help="0 = the library's plan")
+    ap.add_argument("--state-pass", type=int, default=0, choices=[0, 1, 2],
+                    help="kda_chunk_desc::state_pass of the main workload: 0 = the library's plan, 1 = two kernels, "
+                         "2 = fused")
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-packed", action="store_true", help="skip the packed variable-length batch")
@@ -207,7 +211,7 @@ def main():
     w = getattr(synth, WORKLOADS[args.workload])
     cpu_lanes = args.cpu_lanes or max(1, min(w.B * w.H, (2 << 20) // w.T))
     main_res, sample = time_prefill(kda, synth, torch, np, w, args.steps, args.warmup, args.segments, stream,
-                                    keep_lanes=0 if args.no_cpu_baseline else cpu_lanes)
+                                    keep_lanes=0 if args.no_cpu_baseline else cpu_lanes, state_pass=args.state_pass)
 
     if args.copy_probe_mib:
         n = args.copy_probe_mib * (1 << 20) // 4

@@ -31,7 +31,11 @@ _DTYPES = {torch.float32: KDA_F32, torch.bfloat16: KDA_BF16}
 class ChunkDesc(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int64), ("H", ctypes.c_int64), ("T", ctypes.c_int64), ("dk", ctypes.c_int64),
                 ("dv", ctypes.c_int64), ("chunk", ctypes.c_int32), ("in_dtype", ctypes.c_int32),
-                ("out_dtype", ctypes.c_int32), ("segments", ctypes.c_int32)]
+                ("out_dtype", ctypes.c_int32), ("segments", ctypes.c_int32), ("state_pass", ctypes.c_int32)]
+
+
+# kda_chunk_desc::state_pass
+STATE_PASS_AUTO, STATE_PASS_TWO_KERNELS, STATE_PASS_FUSED = 0, 1, 2
 
 
 class VarlenDesc(ctypes.Structure):
@@ -142,13 +146,14 @@ def _check(fn, status):
         raise KDAError(fn, status, library().kda_status_string(status).decode())
 
 
-def _chunk_desc(q, v, segments, out_dtype):
+def _chunk_desc(q, v, segments, out_dtype, state_pass=STATE_PASS_AUTO):
     B, H, T, dk = q.shape
-    return ChunkDesc(B, H, T, dk, v.shape[-1], 64, _DTYPES[q.dtype], _DTYPES[out_dtype], int(segments))
+    return ChunkDesc(B, H, T, dk, v.shape[-1], 64, _DTYPES[q.dtype], _DTYPES[out_dtype], int(segments),
+                     int(state_pass))
 
 
-def chunk_workspace_bytes(q, v, segments=0, out_dtype=None):
-    d = _chunk_desc(q, v, segments, out_dtype or q.dtype)
+def chunk_workspace_bytes(q, v, segments=0, out_dtype=None, state_pass=STATE_PASS_AUTO):
+    d = _chunk_desc(q, v, segments, out_dtype or q.dtype, state_pass)
     return int(library().kda_chunk_fwd_workspace_bytes(ctypes.byref(d)))
 
 
@@ -158,12 +163,13 @@ def _check_tensor(name, t, device, dtype, shape):
                          % (name, dtype, tuple(shape), device, t.dtype, tuple(t.shape), t.device))
 
 
-def chunk_fwd(q, k, v, log_alpha, beta, S0=None, *, out_dtype=None, segments=0, o=None, S_T=None,
-              store_state=True, workspace=None, stream=None):
+def chunk_fwd(q, k, v, log_alpha, beta, S0=None, *, out_dtype=None, segments=0, state_pass=STATE_PASS_AUTO, o=None,
+              S_T=None, store_state=True, workspace=None, stream=None):
     """Chunkwise KDA prefill through ``kda_chunk_fwd``.
 
     q, k, log_alpha: [B,H,T,dk]; v: [B,H,T,dv]; beta: [B,H,T] (all bf16 or all fp32);
     S0: [B,H,dk,dv] fp32 or None. Returns (o [B,H,T,dv], S_T [B,H,dk,dv] fp32 or None).
+    ``segments`` and ``state_pass`` are kda_chunk_desc's (0: the library's choice).
     Caller-supplied o, S_T (may be S0) and workspace are checked like the inputs. Outputs and
     workspace the binding allocates are allocated on ``stream`` (default: the current stream).
     """
@@ -187,7 +193,7 @@ def chunk_fwd(q, k, v, log_alpha, beta, S0=None, *, out_dtype=None, segments=0, 
         _check_tensor("S_T", S_T, dev, torch.float32, (B, H, dk, dv))
     _check_workspace(workspace, dev)
     _check_device("chunk_fwd", dev)
-    desc = _chunk_desc(q, v, segments, out_dtype)
+    desc = _chunk_desc(q, v, segments, out_dtype, state_pass)
     lib = library()
     need = int(lib.kda_chunk_fwd_workspace_bytes(ctypes.byref(desc)))
     with _alloc_on(stream):

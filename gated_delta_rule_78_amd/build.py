@@ -12,7 +12,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libkda.so")
-SOURCES = ["kda_abi.cpp", "kda_plan.cpp", "kda_decode.hip", "kda_chunk.hip", "kda_intra.hip", "kda_inter.hip", "kda_scan.hip", "kda_varlen.hip", "kda_bwd.hip", "kda_noalloc.hip"]
+SOURCES = ["kda_abi.cpp", "kda_plan.cpp", "kda_decode.hip", "kda_chunk.hip", "kda_intra.hip", "kda_inter.hip", "kda_fused.hip", "kda_scan.hip", "kda_varlen.hip", "kda_bwd.hip", "kda_noalloc.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 COMMON = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",

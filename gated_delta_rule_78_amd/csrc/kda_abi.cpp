@@ -41,20 +41,26 @@ int64_t current_cus() {
     return kda::compute_units(hipGetDevice(&dev) == hipSuccess ? dev : 0);
 }
 
-Geometry fixed_geometry(const kda_chunk_desc* d, int64_t cus) {
+// `forward`: a kda_chunk_fwd call (the fused kernel may take it); else the backward's recompute.
+Geometry fixed_geometry(const kda_chunk_desc* d, int64_t cus, bool forward = true) {
     const int64_t nchunks = ceil_div(d->T, kChunk);
-    return Geometry{d->B * d->H, nchunks, d->B * d->H * nchunks, d->dk, d->dv, d->in_dtype, d->segments, 0,
-                    d->B * d->H, cus};
+    Geometry g{d->B * d->H, nchunks, d->B * d->H * nchunks, d->dk, d->dv, d->in_dtype, d->segments, 0,
+               d->B * d->H, cus};
+    g.state_pass = forward ? d->state_pass : 1;
+    g.fused_ok = forward && d->in_dtype == KDA_BF16 && d->dk == 128 && d->dv == 128;
+    return g;
 }
 
 kda_status check_chunk_desc(const kda_chunk_desc* d) {
     if (!d) return KDA_ERR_INVALID_ARG;
-    if (d->B < 1 || d->H < 1 || d->T < 0 || d->dk < 1 || d->dv < 1 || d->segments < 0)
+    if (d->B < 1 || d->H < 1 || d->T < 0 || d->dk < 1 || d->dv < 1 || d->segments < 0 || d->state_pass < 0 ||
+        d->state_pass > 2)
         return KDA_ERR_INVALID_ARG;
     if (!valid_dtype(d->in_dtype) || !valid_dtype(d->out_dtype)) return KDA_ERR_INVALID_ARG;
     if (d->chunk != kChunk) return KDA_ERR_UNSUPPORTED;
     if ((d->dk != 64 && d->dk != 128) || (d->dv != 64 && d->dv != 128)) return KDA_ERR_UNSUPPORTED;
     if (d->in_dtype == KDA_F32 && d->dk != 64) return KDA_ERR_UNSUPPORTED;
+    if (d->in_dtype == KDA_BF16 && d->state_pass == 2 && (d->dk != 128 || d->dv != 128)) return KDA_ERR_UNSUPPORTED;
     // the bf16 kernel addresses one lane's rows with 32-bit buffer offsets
     if (d->in_dtype == KDA_BF16 && d->T * (d->dk > d->dv ? d->dk : d->dv) * 4 >= ((int64_t)1 << 31))
         return KDA_ERR_UNSUPPORTED;
@@ -142,7 +148,7 @@ struct BwdPlan {
 
 BwdPlan make_bwd_plan(const kda_chunk_desc* d, int64_t cus) {
     BwdPlan b{};
-    b.fwd = make_plan(fixed_geometry(d, cus));
+    b.fwd = make_plan(fixed_geometry(d, cus, false));
     const int64_t lanes = d->B * d->H;
     const int64_t nchunks = ceil_div(d->T, kChunk);
     const size_t chunks = (size_t)(lanes * nchunks);
@@ -380,7 +386,7 @@ kda_status kda_chunk_bwd(const kda_chunk_desc* d, const void* q, const void* k, 
                          float* dS0, void* workspace, size_t workspace_bytes, void* stream) {
     const kda_status ds = check_chunk_desc(d);
     if (ds != KDA_OK) return ds;
-    if (d->in_dtype != KDA_BF16) return KDA_ERR_UNSUPPORTED;
+    if (d->in_dtype != KDA_BF16 || d->state_pass == 2) return KDA_ERR_UNSUPPORTED;
     const int64_t lanes = d->B * d->H;
     const int64_t eout = elem_bytes(d->out_dtype);
     const int64_t state_bytes = lanes * d->dk * d->dv * 4;

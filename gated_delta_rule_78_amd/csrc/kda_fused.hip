@@ -1,0 +1,200 @@
+// KDA fused prefill for gfx950, bf16 inputs: the intra-chunk work and the state step of every
+// chunk in one kernel, so that a chunk's record (kda_record.h) never leaves the compute unit
+// (Kimi K3 reading notes, liuzhao09.github.io/papers/kimi-k3.html, section 2.2 chunk equations;
+// section 2.5 for the sequence split that gives each workgroup its own segment).
+//
+// One 8-wave workgroup per (lane, segment). Waves 0-3 (producer) build chunk c's record in an LDS
+// buffer with the intra-chunk kernel's per-wave code (intra::ChunkWave: decay factors, Gram
+// tiles, UT solve); waves 4-7 (consumer) hold the fp32 state in MFMA accumulators, 16 * DV/64
+// columns each, and run the state step on chunk c - 1's record while the producer works on
+// chunk c:
+//   epoch c:  producer: decay factors of chunk c      | consumer: state step of chunk c - 1
+//             ---- barrier 1: the consumer is done with the record buffer ----
+//             producer: record pieces held back, loads | consumer: o rows of chunk c - 1
+//                       of chunk c + 1, Gram tiles
+//             ---- barrier 2 ----
+//             producer: UT solve (W, U)
+//             ---- barrier 3: chunk c's record is complete ----
+// The two roles run separate loops with the same barriers (every barrier orders LDS only), so
+// the registers of one role are free for the other. Per chunk the kernel reads q, k, v,
+// log_alpha and beta and writes o: the two-kernel path also writes and reads the record
+// (71 KiB per chunk at d = 128) through HBM.
+//
+// Entry states: S0 for segment 0, else the window's S~ (ChunkLaunch::ws_entry, from a kPassWindow
+// launch); a lane with an inexact window (ws_flag) is left to the two-kernel fallback.
+#include "kda_intra_chunk.h"
+#include "kda_step.h"
+
+namespace kda {
+namespace {
+
+using intra::ChunkWave;
+using intra::IntraSmem;
+using intra::kC;
+
+constexpr int kThreads = 512;
+
+template <int DK, int DV>
+struct __align__(16) FusedSmem {
+    IntraSmem<DK, DV> ip;                              // the producer's stages
+    unsigned char rec[RecordLayout<DK, DV>::BYTES];    // the record of the chunk in flight
+};
+
+// Barrier over the whole workgroup that orders LDS accesses only (global loads stay in flight).
+__device__ __forceinline__ void epoch_barrier() { lds_barrier(); }
+
+template <int DK, int DV>
+__device__ __forceinline__ void producer(const ChunkLaunch& p, FusedSmem<DK, DV>& sm, int64_t row_base, int64_t cb,
+                                         int64_t ce) {
+    ChunkWave<DK, DV, false> cw(sm.ip);
+    unsigned char* rec = sm.rec;
+    const int64_t T = p.T;
+    auto load = [&](int64_t c) {
+        uint32_t n = 0;
+        if (c < ce) n = (uint32_t)(T - c * kC < kC ? T - c * kC : kC);
+        cw.load(p.q, p.k, p.la, p.v, p.beta, row_base + (c < ce ? c : 0) * kC, n);
+    };
+    load(cb);
+    cw.pin_inputs();
+    for (int64_t c = cb; c < ce; ++c) {
+        cw.template decay<true>(rec, 0.f, 0.f, kC);
+        epoch_barrier();   // 1
+        cw.publish(rec);
+        load(c + 1);
+        cw.gram(rec);
+        epoch_barrier();   // 2
+        cw.pin_inputs();
+        cw.solve(rec);
+        epoch_barrier();   // 3
+    }
+    // the consumer's last chunk
+    epoch_barrier();
+    epoch_barrier();
+    epoch_barrier();
+}
+
+template <typename TOut, int DK, int DV>
+__device__ __forceinline__ void consumer(const ChunkLaunch& p, FusedSmem<DK, DV>& sm, int64_t lane, int seg,
+                                         int64_t cb, int64_t ce) {
+    constexpr int NT = DV / 64;
+    constexpr int NM = DK / 16;
+    const int tid = threadIdx.x;
+    const int w = __builtin_amdgcn_readfirstlane((tid >> 6) & 3);
+    const int l = tid & 63;
+    const int l16 = l & 15;
+    const int lq = l >> 4;
+    const int64_t DVl = DV;
+    const int col0 = w * 16 * NT;
+    // S[nt][M] holds rows 16M + 4lq + r, column col0 + 16nt + l16
+    f32x4 S[NT][NM];
+    const float* entry = seg > 0 ? p.ws_entry + ((lane * p.nseg + seg) * DK) * DVl : (p.S0 ? p.S0 + lane * DK * DVl : nullptr);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int M = 0; M < NM; ++M)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                S[nt][M][r] = entry ? entry[(16 * M + 4 * lq + r) * DVl + col0 + 16 * nt + l16] : 0.f;
+    const __amdgpu_buffer_rsrc_t ro = make_rsrc((const TOut*)p.o + lane * p.T * DVl, (uint32_t)(p.T * DVl * sizeof(TOut)));
+    constexpr bool PAIRED = sizeof(TOut) == 2 && NT % 2 == 0;
+    f32x4 O[NT][4];
+    for (int64_t c = cb; c <= ce; ++c) {
+        const bool work = c > cb;   // chunk c - 1's record is in the buffer
+        if (work)
+            chunk_step<TOut, DK, DV, NT, 0, NT, true>(sm.rec, S, col0, DV / 16 - col0 / 16, O, false, ro, nullptr, w);
+        epoch_barrier();   // 1
+        if (work) {
+#pragma unroll
+            for (int I = 0; I < 4; ++I) {
+                const uint32_t row = (uint32_t)((c - 1) * kC + 16 * I + l16);
+                if constexpr (PAIRED) {
+#pragma unroll
+                    for (int np = 0; np < NT / 2; ++np) {
+                        f32x4 a, b;
+                        swap_pair(O[2 * np][I], O[2 * np + 1][I], a, b);
+                        store_bf16x8(ro, row * (uint32_t)DV + (uint32_t)(col0 + 32 * np) + pair_col(lq), a, b);
+                    }
+                } else {
+#pragma unroll
+                    for (int nt = 0; nt < NT; ++nt)
+                        store_out(ro, (row * (uint32_t)DV + col0 + 16 * nt + 4 * lq) * (uint32_t)sizeof(TOut), O[nt][I],
+                                  (TOut*)nullptr);
+                }
+            }
+        }
+        epoch_barrier();   // 2
+        epoch_barrier();   // 3
+    }
+    if (seg == p.nseg - 1 && p.S_T) {
+        float* dst = p.S_T + lane * DK * DVl;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+            for (int M = 0; M < NM; ++M)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) dst[(16 * M + 4 * lq + r) * DVl + col0 + 16 * nt + l16] = S[nt][M][r];
+    }
+}
+
+template <typename TOut, int DK, int DV>
+__global__ __launch_bounds__(kThreads, 1) void fused_kernel(ChunkLaunch p) {
+    __shared__ FusedSmem<DK, DV> sm;
+    const int64_t lane = uniform64(blockIdx.x / p.nseg);
+    const int seg = (int)uniform64(blockIdx.x % p.nseg);
+    if (p.nseg > 1 && !window_split_exact(p.ws_flag + lane * p.nseg, p.nseg)) return;   // the fallback's lane
+    int64_t cb = (int64_t)seg * p.chunks_per_seg;
+    int64_t ce = seg == p.nseg - 1 ? p.nchunks : cb + p.chunks_per_seg;
+    if (ce > p.nchunks) ce = p.nchunks;
+    if (cb > ce) cb = ce;
+    cb = uniform64(cb);
+    ce = uniform64(ce);
+    // the role split is wave-uniform (a scalar branch), so each wave runs only its own loop
+    if (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) < 4)
+        producer<DK, DV>(p, sm, lane * p.T, cb, ce);
+    else
+        consumer<TOut, DK, DV>(p, sm, lane, seg, cb, ce);
+}
+
+// One workgroup: the lanes whose flags are not all 1, in increasing order (a block-wide prefix
+// count per 1024 lanes).
+__global__ __launch_bounds__(1024, 1) void fallback_lanes_kernel(const int32_t* flag, int64_t lanes, int nseg,
+                                                                 int32_t* list, int32_t* count) {
+    __shared__ int32_t pre[1024];
+    int32_t base = 0;
+    for (int64_t l0 = 0; l0 < lanes; l0 += 1024) {
+        const int64_t lane = l0 + threadIdx.x;
+        const int32_t need = lane < lanes && !window_split_exact(flag + lane * nseg, nseg) ? 1 : 0;
+        pre[threadIdx.x] = need;
+        __syncthreads();
+        for (int d = 1; d < 1024; d <<= 1) {   // inclusive Hillis-Steele scan
+            const int32_t x = threadIdx.x >= (unsigned)d ? pre[threadIdx.x - d] : 0;
+            __syncthreads();
+            pre[threadIdx.x] += x;
+            __syncthreads();
+        }
+        if (need) list[base + pre[threadIdx.x] - 1] = (int32_t)lane;
+        base += pre[1023];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) *count = base;
+}
+
+}  // namespace
+
+hipError_t launch_fused(const ChunkLaunch& a, hipStream_t st) {
+    const int64_t blocks = a.lanes * (int64_t)a.nseg;
+    if (blocks <= 0) return hipSuccess;
+    if (a.out_bf16)
+        hipLaunchKernelGGL((fused_kernel<bf16_t, 128, 128>), dim3((unsigned)blocks), dim3(kThreads), 0, st, a);
+    else
+        hipLaunchKernelGGL((fused_kernel<float, 128, 128>), dim3((unsigned)blocks), dim3(kThreads), 0, st, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_fallback_lanes(const int32_t* flag, int64_t lanes, int nseg, int32_t* list, int32_t* count,
+                                 hipStream_t st) {
+    hipLaunchKernelGGL(fallback_lanes_kernel, dim3(1), dim3(1024), 0, st, flag, lanes, nseg, list, count);
+    return hipGetLastError();
+}
+
+}  // namespace kda

@@ -56,7 +56,12 @@ struct SlotEntry {
 //   (segment scan, skipped by lanes whose flags are all 1)
 //   kPassFinish  FINISH of segments 1 .. nseg - 1 whose flag is 0, from the scanned entry states.
 // kPassAll is a single-segment call (and the fp32 path).
-enum SplitPass { kPassAll = 0, kPassWindowFinish = 1, kPassCarry = 2, kPassFinish = 3 };
+// The fused plan (launch_fused) runs the windows first, on their own: kPassWindow runs the window
+// before each boundary s = 1 .. nseg - 1 (the FINISH blocks of segments 1 .. nseg - 1), stores its
+// flag and S~ (the segment's entry state where the flag is 1) and nothing else. The fused kernel
+// then finishes every lane whose flags are all 1, and the launches above run the other lanes
+// (ChunkLaunch::skip_flag).
+enum SplitPass { kPassAll = 0, kPassWindowFinish = 1, kPassCarry = 2, kPassFinish = 3, kPassWindow = 4 };
 
 // One launch of the chunk kernels. Blocks [0, n_fin) run FINISH work (exact entry state, write
 // o and, for the last segment, S_T); the following n_sum blocks run SUMMARY work (affine pair
@@ -79,7 +84,10 @@ struct ChunkLaunch {
     float* ws_entry;        // [lanes][nseg][dk][dv]        exact entry state of each segment
     int32_t* ws_flag;       // [lanes][nseg]                window flags (see SplitPass)
     int split;              // SplitPass of this launch
-    int64_t win_chunks;     // kPassWindowFinish: chunks per window
+    int64_t win_chunks;     // kPassWindowFinish, kPassWindow: chunks per window
+    // [lanes][nseg] flags of a kPassWindow launch, or NULL: lanes whose flags there are all 1 were
+    // finished by the fused kernel, and the launches of a two-kernel split skip them.
+    const int32_t* skip_flag;
     SeqMap map;
     // State checkpoints (bf16 path): after every ck_chunks chunks of a lane (s, h), the state
     // goes to ckpt[(ck_off[s] + j - 1) * H + h] (packed) or ckpt[(s * ck_per_lane + j - 1) * H + h]
@@ -100,6 +108,14 @@ struct IntraArgs {
     const SlotEntry* slot_tab;  // [map.slots] for a packed batch, NULL for a fixed one
     SeqMap map;
     Gating gt;              // the prologue fields are read by the intra-chunk kernel
+    // Subsets of a fixed-length batch's chunks (both off: every chunk). With win_chunks > 0, only
+    // the chunks of the windows before segment boundaries 1 .. nseg - 1 (chunks_per_seg chunks per
+    // segment; see SplitPass). With lane_list set, only the lanes lane_list[0 .. *lane_count)
+    // (both device memory).
+    int64_t win_chunks, chunks_per_seg;
+    int nseg;
+    const int32_t* lane_list;
+    const int32_t* lane_count;
 };
 
 // Slot table and checkpoint offsets of a packed batch.
@@ -140,6 +156,14 @@ hipError_t launch_intra(const IntraArgs& a, hipStream_t st);
 int stream_device(hipStream_t st);
 int compute_units(int dev);
 hipError_t launch_inter(const ChunkLaunch& a, hipStream_t st);
+// The fused single-pass prefill (bf16, dk = dv = 128, fixed length, no checkpoints or gating): one
+// workgroup per (lane, segment) builds each chunk's record in LDS and runs the state step on it;
+// segments s > 0 start from ws_entry (a kPassWindow launch), and lanes with an inexact window
+// (ws_flag) are left alone.
+hipError_t launch_fused(const ChunkLaunch& a, hipStream_t st);
+// The lanes whose flags [lanes][nseg] are not all 1, in increasing order: list[0 .. *count).
+hipError_t launch_fallback_lanes(const int32_t* flag, int64_t lanes, int nseg, int32_t* list, int32_t* count,
+                                 hipStream_t st);
 // entry_{s+1} = S~_s + M_s entry_s for s in [1, nseg-1), entry_1 already stored.
 hipError_t launch_segment_scan(const ChunkLaunch& a, hipStream_t st);
 hipError_t launch_varlen_prep(const VarlenPrep& a, hipStream_t st);

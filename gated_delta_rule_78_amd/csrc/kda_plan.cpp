@@ -58,8 +58,9 @@ static double pass_us(int64_t cps, int64_t fin, int64_t sum, int64_t cus) {
 // model's step times alone do not rank the splits: with fewer workgroups than compute units a
 // step is shorter, but at 8K the sweep n = 6, 7, 8 measured 0.2228, 0.2187, 0.2117 ms, and at 1M
 // n = 6 lost 1.3 % to n = 8.)
-static int64_t auto_segments(int64_t lanes, int64_t nchunks, int64_t cus) {
-    constexpr int64_t kMaxSeg = 256;
+constexpr int64_t kMaxSeg = 256;
+
+static int64_t auto_segments(int64_t lanes, int64_t nchunks, int64_t cus, double* us) {
     const int64_t nmax = nchunks < kMaxSeg ? nchunks : kMaxSeg;
     double fast[kMaxSeg + 1], fallback[kMaxSeg + 1];
     bool valid[kMaxSeg + 1] = {};
@@ -83,15 +84,70 @@ static int64_t auto_segments(int64_t lanes, int64_t nchunks, int64_t cus) {
     int64_t best = 1;
     for (int64_t n = 2; n <= nmax; ++n)
         if (valid[n] && lanes * n <= cus && fallback[n] <= 1.2 * best_fallback) best = n;
-    return fast[best] < fast[1] ? best : 1;
+    if (fast[best] >= fast[1]) best = 1;
+    *us = fast[best];
+    return best;
+}
+
+// Modelled time of the intra-chunk kernel over `slots` chunks: two workgroups per compute unit at
+// about 14 us per chunk and workgroup (8K: 8 chunks per workgroup in 120 us; 1M: 1,024 chunks in
+// 13.9 ms, where the record bytes at the device's copy rate bind as much).
+static double intra_us(int64_t slots, int64_t cus) { return 14.0 * (double)ceil_div(slots, 2 * cus); }
+
+// Modelled time of the two-kernel state pass with n segments (n = 0: the plan's choice).
+static double two_kernel_state_us(int64_t lanes, int64_t nchunks, int64_t cus, int64_t n) {
+    double us = 0.0;
+    if (n <= 0) {
+        auto_segments(lanes, nchunks, cus, &us);
+        return us;
+    }
+    const int64_t cps = ceil_div(nchunks, n);
+    n = ceil_div(nchunks, cps);
+    if (n == 1) return pass_us(nchunks, lanes, 0, cus);
+    const int64_t w = kWindowChunks < nchunks ? kWindowChunks : nchunks;
+    return pass_us(cps + w, lanes * n, 0, cus) + (n > 2 ? 3.0 : 1.0) * 4.5;
+}
+
+// The fused plan: one 8-wave workgroup per (lane, segment) and compute unit, each chunk a
+// dependent step of about kFusedStepUs; n = the most segments whose workgroups run in one round
+// (n = 1 when the lanes alone fill the device). With n > 1 the windows come first: the intra-chunk
+// kernel over their (n - 1) * min(8, cps) chunks per lane and the window launch (about 27 us plus
+// 2.4 us per window step), and after the fused kernel the fallback's six launches return at once.
+constexpr double kFusedStepUs = 9.0;
+static int64_t fused_segments(int64_t lanes, int64_t nchunks, int64_t cus, int64_t forced, double* us) {
+    int64_t n = forced > 0 ? forced : (lanes < cus ? cus / lanes : 1);
+    if (n > kMaxSeg) n = kMaxSeg;
+    if (n > nchunks) n = nchunks;
+    const int64_t cps = ceil_div(nchunks, n);
+    n = ceil_div(nchunks, cps);
+    double t = (double)ceil_div(lanes * n, cus) * (double)cps * kFusedStepUs;
+    if (n > 1) {
+        const int64_t w = kWindowChunks < cps ? kWindowChunks : cps;
+        t += intra_us(lanes * (n - 1) * w, cus) + 27.0 + 2.4 * (double)w + 6.0 * 4.5;
+    }
+    *us = t;
+    return n;
 }
 
 Plan make_plan(const Geometry& g) {
     Plan p{};
     const int64_t nchunks = g.max_chunks;
     p.nchunks = nchunks;
+    const int64_t cus = g.cus > 0 ? g.cus : 256;
     int64_t nseg = 1;
-    if (g.in_dtype == KDA_BF16 && nchunks > 0) nseg = g.segments > 0 ? g.segments : auto_segments(g.long_lanes, nchunks, g.cus > 0 ? g.cus : 256);
+    if (g.in_dtype == KDA_BF16 && nchunks > 0) {
+        double two_us = 0.0, fused_us = 0.0;
+        if (g.segments > 0) nseg = g.segments;
+        else nseg = auto_segments(g.long_lanes, nchunks, cus, &two_us);
+        if (g.fused_ok && g.state_pass != 1) {
+            const int64_t nf = fused_segments(g.lanes, nchunks, cus, g.segments, &fused_us);
+            if (g.state_pass == 0) two_us = intra_us(g.slots, cus) + two_kernel_state_us(g.lanes, nchunks, cus, g.segments);
+            if (g.state_pass == 2 || fused_us < two_us) {
+                p.fused = true;
+                nseg = nf;
+            }
+        }
+    }
     if (nseg > nchunks) nseg = nchunks > 0 ? nchunks : 1;
     int64_t cps = nchunks > 0 ? ceil_div(nchunks, nseg) : 1;
     if (cps < 1) cps = 1;
@@ -105,11 +161,45 @@ Plan make_plan(const Geometry& g) {
             p.pair_bytes = (size_t)g.lanes * (size_t)nseg * (size_t)(g.dk * (g.dv + g.dk)) * sizeof(float);
             p.entry_bytes = (size_t)g.lanes * (size_t)nseg * (size_t)(g.dk * g.dv) * sizeof(float);
             p.flag_bytes = (size_t)g.lanes * (size_t)nseg * sizeof(int32_t);
+            if (p.fused) {
+                p.pre_bytes = p.flag_bytes;
+                p.list_bytes = ((size_t)(g.lanes + 1) * sizeof(int32_t) + 15) & ~(size_t)15;
+            }
         }
         p.tab_bytes = (size_t)g.tab_slots * sizeof(SlotEntry);
     }
-    p.ws_bytes = p.rec_bytes + p.pair_bytes + p.entry_bytes + p.tab_bytes + p.flag_bytes;
+    p.ws_bytes = p.rec_bytes + p.pair_bytes + p.entry_bytes + p.tab_bytes + p.flag_bytes + p.pre_bytes + p.list_bytes;
     return p;
+}
+
+// The fused plan: the windows' records and the window launch (n > 1), the fused kernel for every
+// lane whose windows are all exact, then the two-kernel window split below for the other lanes
+// (their full records, first), each launch of which skips the fused lanes.
+static kda_status run_fused(ChunkLaunch& a, const Plan& plan, const IntraArgs& ia, unsigned char* ws, hipStream_t st) {
+    if (plan.nseg == 1) {
+        a.split = kPassAll;
+        return launch_fused(a, st) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+    }
+    const size_t pre_off = plan.rec_bytes + plan.pair_bytes + plan.entry_bytes + plan.tab_bytes + plan.flag_bytes;
+    int32_t* pre = reinterpret_cast<int32_t*>(ws + pre_off);
+    int32_t* list = reinterpret_cast<int32_t*>(ws + pre_off + plan.pre_bytes);
+    int32_t* count = list + a.lanes;
+    IntraArgs iw = ia;   // the window chunks of every lane
+    iw.win_chunks = plan.win_chunks; iw.chunks_per_seg = plan.chunks_per_seg; iw.nseg = plan.nseg;
+    if (launch_intra(iw, st) != hipSuccess) return KDA_ERR_HIP;
+    ChunkLaunch w = a;   // their flags and S~
+    w.split = kPassWindow; w.ws_flag = pre;
+    w.fin_seg_lo = 1; w.fin_nseg = plan.nseg - 1; w.sum_seg_lo = 0; w.sum_nseg = 0;
+    if (launch_inter(w, st) != hipSuccess) return KDA_ERR_HIP;
+    ChunkLaunch f = a;
+    f.split = kPassAll; f.ws_flag = pre;
+    if (launch_fused(f, st) != hipSuccess) return KDA_ERR_HIP;
+    if (launch_fallback_lanes(pre, a.lanes, plan.nseg, list, count, st) != hipSuccess) return KDA_ERR_HIP;
+    IntraArgs il = ia;   // the fallback lanes' records
+    il.lane_list = list; il.lane_count = count;
+    if (launch_intra(il, st) != hipSuccess) return KDA_ERR_HIP;
+    a.skip_flag = pre;
+    return KDA_OK;
 }
 
 // bf16 prefill after validation: records of every chunk (state independent, fully parallel),
@@ -123,12 +213,17 @@ kda_status run_bf16(ChunkLaunch& a, const Plan& plan, unsigned char* ws, hipStre
     ia.gt = a.gt;
     const size_t tab_off = plan.rec_bytes + plan.pair_bytes + plan.entry_bytes;
     ia.slot_tab = a.map.cu ? reinterpret_cast<const SlotEntry*>(ws + tab_off) : nullptr;
-    if (launch_intra(ia, st) != hipSuccess) return KDA_ERR_HIP;
     a.rec = ws;
     a.ws_pair = plan.pair_bytes ? reinterpret_cast<float*>(ws + plan.rec_bytes) : nullptr;
     a.ws_entry = plan.entry_bytes ? reinterpret_cast<float*>(ws + plan.rec_bytes + plan.pair_bytes) : nullptr;
     a.ws_flag = plan.flag_bytes ? reinterpret_cast<int32_t*>(ws + tab_off + plan.tab_bytes) : nullptr;
     a.win_chunks = plan.win_chunks;
+    if (plan.fused) {
+        const kda_status fs = run_fused(a, plan, ia, ws, st);
+        if (fs != KDA_OK || plan.nseg == 1) return fs;
+    } else if (launch_intra(ia, st) != hipSuccess) {
+        return KDA_ERR_HIP;
+    }
     if (plan.nseg == 1) {
         a.split = kPassAll;
         a.fin_seg_lo = 0; a.fin_nseg = 1; a.sum_seg_lo = 0; a.sum_nseg = 0;

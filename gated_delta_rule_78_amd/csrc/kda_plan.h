@@ -24,6 +24,8 @@ struct Geometry {
     int64_t tab_slots;   // slot-table entries (packed batches), 0 otherwise
     int64_t long_lanes;  // lanes that can have max_chunks chunks (plans the sequence split)
     int64_t cus;         // compute units of the device the call runs on
+    int32_t state_pass;  // kda_chunk_desc::state_pass (0 = choose, 1 = two kernels, 2 = fused)
+    bool fused_ok;       // the call can take the fused kernel (see launch_fused)
 };
 
 // Chunks in the window that looks for an exact segment entry state (SplitPass): a decay of
@@ -32,8 +34,11 @@ struct Geometry {
 constexpr int64_t kWindowChunks = 8;
 
 // Segments per lane, chunks per segment and workspace of a prefill call. The workspace holds,
-// in this order: records, affine pairs, entry states, slot table, window flags.
+// in this order: records, affine pairs, entry states, slot table, window flags and, for the
+// fused plan, the window launch's flags and the list of lanes left to the two-kernel fallback.
 struct Plan {
+    bool fused;          // the fused kernel (with the two-kernel path as the fallback of lanes
+                         // with an inexact window)
     int nseg;
     int64_t nchunks, chunks_per_seg;
     int64_t win_chunks;  // chunks per window (nseg > 1), kWindowChunks
@@ -42,6 +47,8 @@ struct Plan {
     size_t entry_bytes;  // entry states [lanes][nseg][dk][dv] (nseg > 1)
     size_t tab_bytes;    // slot table (packed batches)
     size_t flag_bytes;   // window flags [lanes][nseg] int32 (nseg > 1)
+    size_t pre_bytes;    // fused plan, nseg > 1: the window launch's flags [lanes][nseg] int32
+    size_t list_bytes;   // fused plan, nseg > 1: fallback lanes [lanes] int32, then their count
     size_t ws_bytes;
 };
 

@@ -50,7 +50,9 @@ __global__ __launch_bounds__(DK == 128 ? 512 : 256) void segment_scan_kernel(Chu
     const int lq = l >> 4;
     const int64_t col = 16 * cb + l16;
     const int nseg = p.nseg;
-    // a lane whose entry states all came from the window launch has nothing to scan
+    // a lane that the fused kernel finished, or whose entry states all came from the window
+    // launch, has nothing to scan
+    if (p.skip_flag && window_split_exact(p.skip_flag + lane * nseg, nseg)) return;
     if (window_split_exact(p.ws_flag + lane * nseg, nseg)) return;
 
     // entry tile: every load issued before the first LDS store (one memory round trip)

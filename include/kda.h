@@ -68,6 +68,10 @@ typedef struct kda_chunk_desc {
     int32_t in_dtype;   /* kda_dtype of q,k,v,log_alpha,beta (KDA_F32 needs dk == 64)    */
     int32_t out_dtype;  /* kda_dtype of o                                                */
     int32_t segments;   /* sequence segments per lane: 0 = library's choice, n >= 1 = n  */
+    int32_t state_pass; /* bf16 inputs: 0 = library's choice; 1 = two kernels (every chunk's
+                           factors through the workspace); 2 = the fused kernel (dk = dv =
+                           128 only, else KDA_ERR_UNSUPPORTED). kda_chunk_bwd uses 1 for its
+                           forward and accepts 0 or 1. The fp32 path ignores it.         */
 } kda_chunk_desc;
 
 /* Shape and types of one decode step over N independent sequences. */

@@ -12,22 +12,35 @@
 #include "kda_plan.h"
 
 namespace {
-int g_intra, g_inter, g_scan, g_chunk, g_copy, g_prep, g_bwd, g_decode;
+int g_intra, g_inter, g_scan, g_chunk, g_copy, g_prep, g_bwd, g_decode, g_fused, g_lanes;
 kda::ChunkLaunch g_last;
 kda::ChunkLaunch g_inter_seq[8];   // the first state-pass launches since reset(), in order
-void reset() { g_intra = g_inter = g_scan = g_chunk = g_copy = g_prep = g_bwd = g_decode = 0; }
+kda::IntraArgs g_intra_seq[4];     // the first intra-chunk launches since reset()
+kda::ChunkLaunch g_fused_last;
+int g_order[16], g_norder;          // launch kinds in order: 1 intra, 2 inter, 3 scan, 4 fused, 5 lane list
+void note(int kind) { if (g_norder < 16) g_order[g_norder++] = kind; }
+void reset() { g_intra = g_inter = g_scan = g_chunk = g_copy = g_prep = g_bwd = g_decode = g_fused = g_lanes = g_norder = 0; }
 }  // namespace
 
 namespace kda {
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t) { ++g_decode; return a.S && a.o ? hipSuccess : hipErrorInvalidValue; }
 hipError_t launch_chunk(const ChunkLaunch& a, hipStream_t) { ++g_chunk; g_last = a; return hipSuccess; }
-hipError_t launch_intra(const IntraArgs& a, hipStream_t) { ++g_intra; return a.rec ? hipSuccess : hipErrorInvalidValue; }
+hipError_t launch_intra(const IntraArgs& a, hipStream_t) {
+    if (g_intra < 4) g_intra_seq[g_intra] = a;
+    ++g_intra; note(1);
+    return a.rec ? hipSuccess : hipErrorInvalidValue;
+}
 hipError_t launch_inter(const ChunkLaunch& a, hipStream_t) {
     if (g_inter < 8) g_inter_seq[g_inter] = a;
-    ++g_inter; g_last = a;
+    ++g_inter; g_last = a; note(2);
     return hipSuccess;
 }
-hipError_t launch_segment_scan(const ChunkLaunch&, hipStream_t) { ++g_scan; return hipSuccess; }
+hipError_t launch_segment_scan(const ChunkLaunch&, hipStream_t) { ++g_scan; note(3); return hipSuccess; }
+hipError_t launch_fused(const ChunkLaunch& a, hipStream_t) { ++g_fused; g_fused_last = a; note(4); return hipSuccess; }
+hipError_t launch_fallback_lanes(const int32_t* flag, int64_t lanes, int nseg, int32_t* list, int32_t* count, hipStream_t) {
+    ++g_lanes; note(5);
+    return flag && list && count && lanes > 0 && nseg > 1 ? hipSuccess : hipErrorInvalidValue;
+}
 hipError_t launch_varlen_prep(const VarlenPrep&, hipStream_t) { ++g_prep; return hipSuccess; }
 hipError_t launch_copy_or_zero(float* dst, const float*, int64_t n, hipStream_t) { ++g_copy; return dst && n > 0 ? hipSuccess : hipErrorInvalidValue; }
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t) { ++g_bwd; return a.ckpt || a.T < 64 ? hipSuccess : hipErrorInvalidValue; }
@@ -116,6 +129,59 @@ static int check_chunk() {
     CHECK(w2.split == kda::kPassFinish && w2.fin_seg_lo == 1 && w2.fin_nseg == 3 && w2.sum_nseg == 0 && w2.nseg == 4);
     CHECK(w0.ws_flag == (int32_t*)((char*)P(7 * GB) + need4 - 2 * 4 * sizeof(int32_t)) && w2.ws_flag == w0.ws_flag);
     CHECK((char*)w0.ws_entry + 2 * 4 * 128 * 128 * sizeof(float) == (char*)w0.ws_flag);
+    CHECK(w0.skip_flag == nullptr && w2.skip_flag == nullptr);
+    // the fused plan, forced: the windows' records and the window launch, the fused kernel, the
+    // fallback lane list and those lanes' records, then the window split above for those lanes.
+    // Its workspace adds the window launch's flags and the lane list (2 lanes + count, 16 bytes).
+    kda_chunk_desc s5 = s4;
+    s5.state_pass = 2;
+    const size_t need5 = kda_chunk_fwd_workspace_bytes(&s5);
+    CHECK(need5 == need4 + 2 * 4 * sizeof(int32_t) + 16);
+    reset();
+    CHECK(fwd(&s5, P(7 * GB), need5 - 1, nullptr, P(6 * GB)) == KDA_ERR_WORKSPACE);
+    CHECK(fwd(&s5, P(7 * GB), need5, nullptr, P(6 * GB)) == KDA_OK);
+    const int order[9] = {1, 2, 4, 5, 1, 2, 2, 3, 2};
+    CHECK(g_norder == 9 && memcmp(g_order, order, sizeof(order)) == 0);
+    const int32_t* pre = (const int32_t*)((char*)P(7 * GB) + need4);
+    CHECK(g_intra_seq[0].win_chunks == 8 && g_intra_seq[0].chunks_per_seg == 10 && g_intra_seq[0].nseg == 4 &&
+          !g_intra_seq[0].lane_list);
+    CHECK(g_intra_seq[1].win_chunks == 0 && g_intra_seq[1].lane_list == pre + 2 * 4 &&
+          g_intra_seq[1].lane_count == g_intra_seq[1].lane_list + 2);
+    const kda::ChunkLaunch& v0 = g_inter_seq[0];
+    CHECK(v0.split == kda::kPassWindow && v0.fin_seg_lo == 1 && v0.fin_nseg == 3 && v0.sum_nseg == 0 && v0.ws_flag == pre &&
+          v0.skip_flag == nullptr && v0.win_chunks == 8);
+    CHECK(g_fused_last.ws_flag == pre && g_fused_last.nseg == 4 && g_fused_last.chunks_per_seg == 10 &&
+          g_fused_last.ws_entry == v0.ws_entry && g_fused_last.S_T == P(6 * GB));
+    CHECK(g_inter_seq[1].split == kda::kPassWindowFinish && g_inter_seq[1].skip_flag == pre &&
+          g_inter_seq[1].ws_flag == pre - 2 * 4);
+    CHECK(g_inter_seq[2].split == kda::kPassCarry && g_inter_seq[2].skip_flag == pre);
+    CHECK(g_inter_seq[3].split == kda::kPassFinish && g_inter_seq[3].skip_flag == pre);
+    // forced with one segment: the fused kernel alone
+    kda_chunk_desc s1 = cdesc(1, 2, 64 * 40, 128, 128, KDA_BF16, 1);
+    s1.state_pass = 2;
+    reset();
+    CHECK(fwd(&s1, P(7 * GB), kda_chunk_fwd_workspace_bytes(&s1), nullptr, P(6 * GB)) == KDA_OK);
+    CHECK(g_fused == 1 && g_intra == 0 && g_inter == 0 && g_fused_last.nseg == 1);
+    // forced two kernels; the fused kernel takes dk = dv = 128 only; state_pass outside 0..2
+    kda_chunk_desc s2 = s4;
+    s2.state_pass = 1;
+    CHECK(kda_chunk_fwd_workspace_bytes(&s2) == need4);
+    kda_chunk_desc s6 = cdesc(1, 2, 128, 64, 128);
+    s6.state_pass = 2;
+    CHECK(fwd(&s6, P(7 * GB), GB) == KDA_ERR_UNSUPPORTED);
+    bad = d; bad.state_pass = 3; CHECK(fwd(&bad, nullptr, 0) == KDA_ERR_INVALID_ARG);
+    bad = d; bad.state_pass = -1; CHECK(fwd(&bad, nullptr, 0) == KDA_ERR_INVALID_ARG);
+    // the library's choice: the fused plan for 32 heads x 1M tokens (8 segments per lane, one
+    // workgroup per compute unit), two kernels for 32 heads x 8K tokens
+    kda::Geometry g1m{32, 16384, 32 * 16384, 128, 128, KDA_BF16, 0, 0, 32, 256};
+    g1m.fused_ok = true;
+    const kda::Plan p1m = kda::make_plan(g1m);
+    CHECK(p1m.fused && p1m.nseg == 8 && p1m.chunks_per_seg == 2048);
+    kda::Geometry g8k{32, 128, 32 * 128, 128, 128, KDA_BF16, 0, 0, 32, 256};
+    g8k.fused_ok = true;
+    CHECK(!kda::make_plan(g8k).fused);
+    g1m.fused_ok = false;
+    CHECK(!kda::make_plan(g1m).fused);
     kda_chunk_desc z = cdesc(1, 2, 0);
     reset();
     CHECK(fwd(&z, nullptr, 0, nullptr, P(6 * GB)) == KDA_OK && g_copy == 1);
@@ -179,6 +245,11 @@ static int check_bwd_and_decode() {
     CHECK(bwd(P(4), P(12 * GB), need) == KDA_ERR_INVALID_ARG);          // 16-byte alignment of q
     CHECK(bwd(P(0), P(12 * GB + 16), need) == KDA_ERR_INVALID_ARG);     // 256-byte workspace alignment
     CHECK(bwd(P(0), P(12 * GB), need - 1) == KDA_ERR_WORKSPACE);
+    d.state_pass = 1;
+    CHECK(kda_chunk_bwd_workspace_bytes(&d) == need && bwd(P(0), P(12 * GB), need) == KDA_OK);
+    d.state_pass = 2;   // the backward's forward keeps its checkpoints: two kernels only
+    CHECK(bwd(P(0), P(12 * GB), need) == KDA_ERR_UNSUPPORTED);
+    d.state_pass = 0;
     kda_decode_desc dd;
     memset(&dd, 0, sizeof(dd));
     dd.N = 4; dd.H = 2; dd.dk = 128; dd.dv = 128; dd.in_dtype = KDA_BF16; dd.out_dtype = KDA_BF16;

@@ -1,0 +1,147 @@
+"""GPU parity of the fused prefill (kda_chunk_desc::state_pass = 2): one kernel builds every chunk's
+factors in LDS and runs the state step on them (section 2.2 chunk equations of the Kimi K3 reading
+notes), its segments starting from the window states of section 2.5's sequence split, and lanes
+with an inexact window falling back to the two-kernel path within the same call. Each case is
+checked against the fp64 oracle; where the two paths split a lane the same way, the fused output
+must also equal the two-kernel output bit for bit (the same per-chunk arithmetic in the same
+order: only where the factors live differs)."""
+import numpy as np
+import pytest
+import torch
+
+import gated_delta_rule_78_amd as kda
+from gated_delta_rule_78_amd import synth
+from tests.parity import assert_close, host32, oracle_prefill, say
+
+pytestmark = pytest.mark.gpu
+DEV = torch.device("cuda:0") if torch.cuda.is_available() else None
+BF16 = torch.bfloat16
+FUSED, TWO = kda.STATE_PASS_FUSED, kda.STATE_PASS_TWO_KERNELS
+SLOW = (-0.02, 0.0)
+
+
+def inputs(B, H, T, seed, s0_std=0.3, la_range=synth.LOG_ALPHA_RANGE):
+    return synth.prefill_inputs(B, H, T, 128, 128, BF16, device=DEV, seed_base=seed, s0_std=s0_std,
+                                log_alpha_range=la_range)
+
+
+def check(tag, q, k, v, la, beta, S0, segments, out_dtype=None, same_as_two=True):
+    B, H, T, _ = q.shape
+    o, S_T = kda.chunk_fwd(q, k, v, la, beta, S0, out_dtype=out_dtype, segments=segments, state_pass=FUSED)
+    torch.cuda.synchronize()
+    o_ref, S_ref = oracle_prefill(q, k, v, la, beta, S0)
+    assert_close(tag, BF16, host32(o).reshape(B * H, T, 128), o_ref, host32(S_T).reshape(B * H, 128, 128), S_ref)
+    if same_as_two:
+        o2, S2 = kda.chunk_fwd(q, k, v, la, beta, S0, out_dtype=out_dtype, segments=segments, state_pass=TWO)
+        torch.cuda.synchronize()
+        assert torch.equal(o, o2) and torch.equal(S_T, S2), "%s: fused and two-kernel outputs differ" % tag
+        say("%s: bit-identical to the two-kernel path" % tag)
+    return o, S_T
+
+
+@pytest.mark.parametrize("T", [1, 63, 64, 65, 64 * 9 + 37])
+def test_fused_one_segment_ragged(T):
+    """One segment per lane (the fused kernel alone, no windows): ragged lengths, a prefix state."""
+    say("fused one segment: B=2 H=3 T=%d" % T)
+    q, k, v, la, beta, S0 = inputs(2, 3, T, 9400 + T)
+    check("fused T=%d" % T, q, k, v, la, beta, S0, segments=1)
+
+
+def test_fused_fp32_output_zero_state():
+    say("fused fp32 out: B=1 H=2 T=1000 S0=None")
+    q, k, v, la, beta, _ = inputs(1, 2, 1000, 9450, s0_std=None)
+    check("fused fp32 out", q, k, v, la, beta, None, segments=3, out_dtype=torch.float32)
+
+
+@pytest.mark.parametrize("segments", [2, 4, 7])
+def test_fused_segments_from_windows(segments):
+    """Forced splits at the workload decay: every window is exact, so every lane is fused."""
+    T = 64 * 40 + 17
+    say("fused segments=%d: B=1 H=4 T=%d" % (segments, T))
+    q, k, v, la, beta, S0 = inputs(1, 4, T, 9500 + segments)
+    check("fused segments=%d" % segments, q, k, v, la, beta, S0, segments=segments)
+
+
+def test_fused_short_segments():
+    """Segments of 2 chunks, shorter than the 8-chunk window: the windows reach back over several
+    segments (and to chunk 0 and S0)."""
+    T = 64 * 12 + 5
+    say("fused short segments: B=1 H=2 T=%d segments=6" % T)
+    q, k, v, la, beta, S0 = inputs(1, 2, T, 9550)
+    check("fused short segments", q, k, v, la, beta, S0, segments=6)
+
+
+def test_fused_slow_decay_falls_back():
+    """Slow decay: no window is exact, every lane takes the two-kernel fallback inside the call."""
+    T = 64 * 30 + 9
+    say("fused slow decay: B=1 H=3 T=%d segments=4" % T)
+    q, k, v, la, beta, S0 = inputs(1, 3, T, 9600, la_range=SLOW)
+    check("fused slow decay", q, k, v, la, beta, S0, segments=4)
+
+
+def test_fused_mixed_lanes():
+    """Heads 1 and 3 at slow decay fall back; heads 0 and 2 are fused, in the same call."""
+    T = 64 * 40 + 17
+    say("fused mixed lanes: B=1 H=4 T=%d segments=4" % T)
+    q, k, v, la, beta, S0 = inputs(1, 4, T, 9650)
+    la_slow = inputs(1, 4, T, 9660, la_range=SLOW)[3]
+    la[:, 1::2] = la_slow[:, 1::2]
+    check("fused mixed lanes", q, k, v, la, beta, S0, segments=4)
+
+
+@pytest.mark.parametrize("order", ["fast_then_slow", "slow_then_fast"])
+def test_fused_decay_changes_along_the_sequence(order):
+    """A lane with some exact windows and some inexact ones falls back as a whole."""
+    T = 64 * 40 + 17
+    say("fused decay change %s: B=1 H=2 T=%d" % (order, T))
+    q, k, v, la, beta, S0 = inputs(1, 2, T, 9700)
+    la_slow = inputs(1, 2, T, 9710, la_range=SLOW)[3]
+    half = 64 * 20
+    if order == "fast_then_slow":
+        la[:, :, half:] = la_slow[:, :, half:]
+    else:
+        la[:, :, :half] = la_slow[:, :, :half]
+    check("fused decay change " + order, q, k, v, la, beta, S0, segments=4)
+
+
+def test_fused_in_place_state():
+    """S_T written over S0 (the last segment writes it; every reader of S0 comes first)."""
+    T = 64 * 20 + 3
+    say("fused in place: B=2 H=2 T=%d segments=3" % T)
+    q, k, v, la, beta, S0 = inputs(2, 2, T, 9750)
+    o_ref, S_ref = oracle_prefill(q, k, v, la, beta, S0)
+    S = S0.clone()
+    o, S_T = kda.chunk_fwd(q, k, v, la, beta, S, segments=3, state_pass=FUSED, S_T=S)
+    torch.cuda.synchronize()
+    assert S_T.data_ptr() == S.data_ptr()
+    assert_close("fused in place", BF16, host32(o).reshape(4, T, 128), o_ref, host32(S).reshape(4, 128, 128), S_ref)
+
+
+def _random_cases(n, seed):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        nch = int(rng.integers(1, 49))
+        T = max(1, 64 * nch - int(rng.choice([0, 0, 1, 31, 63])))
+        out.append((i, int(rng.integers(1, 3)), int(rng.integers(1, 4)), T, int(rng.choice([0, 1, 2, 3, 5, 8, 16])),
+                    bool(rng.integers(0, 2)), [int(x) for x in rng.integers(0, 3, 3)]))
+    return out
+
+
+@pytest.mark.parametrize("case", _random_cases(16, 9800), ids=lambda c: "f%d" % c[0])
+def test_fused_random_shapes(case):
+    """16 seeded shapes: ragged T up to 48 chunks, forced or planned segment counts, each head's
+    decay from the workload range, slow decay or the full domain (fused, fallback and mixed)."""
+    i, B, H, T, seg, s0, kinds = case
+    say("fused random %d: B=%d H=%d T=%d segments=%d S0=%s decay kinds %s" % (i, B, H, T, seg, s0, kinds[:H]))
+    q, k, v, la, beta, S0 = inputs(B, H, T, 9900 + 10 * i, s0_std=0.3 if s0 else None)
+    ranges = [synth.LOG_ALPHA_RANGE, SLOW, (-5.0, 0.0)]
+    for h in range(H):
+        la[:, h] = inputs(B, H, T, 9905 + 10 * i + h, la_range=ranges[kinds[h]])[3][:, h]
+    check("fused random %d" % i, q, k, v, la, beta, S0, segments=seg)
+
+
+def test_fused_refused_for_dk64():
+    q, k, v, la, beta, S0 = synth.prefill_inputs(1, 1, 128, 64, 128, BF16, device=DEV, seed_base=9990)
+    with pytest.raises(kda.KDAError):
+        kda.chunk_fwd(q, k, v, la, beta, S0, state_pass=FUSED)

@@ -21,9 +21,12 @@ BF16 = torch.bfloat16
 SLOW = (-0.02, 0.0)
 
 
+TWO = kda.STATE_PASS_TWO_KERNELS
+
+
 def window_flags(ws, need, lanes, T, segments):
-    """Flags [lanes, nseg - 1] of a fixed-length call with a forced segment count: the workspace's
-    last lanes * nseg int32 (no slot table in a fixed-length call)."""
+    """Flags [lanes, nseg - 1] of a fixed-length two-kernel call with a forced segment count: the
+    workspace's last lanes * nseg int32 (no slot table in a fixed-length call)."""
     nchunks = (T + 63) // 64
     cps = (nchunks + segments - 1) // segments
     nseg = (nchunks + cps - 1) // cps
@@ -34,9 +37,9 @@ def window_flags(ws, need, lanes, T, segments):
 def run_with_flags(tag, q, k, v, la, beta, S0, segments):
     B, H, T, dk = q.shape
     dv = v.shape[-1]
-    need = kda.chunk_workspace_bytes(q, v, segments=segments)
+    need = kda.chunk_workspace_bytes(q, v, segments=segments, state_pass=TWO)
     ws = torch.empty(need, device=DEV, dtype=torch.uint8)
-    o, S_T = kda.chunk_fwd(q, k, v, la, beta, S0, segments=segments, workspace=ws)
+    o, S_T = kda.chunk_fwd(q, k, v, la, beta, S0, segments=segments, state_pass=TWO, workspace=ws)
     torch.cuda.synchronize()
     flags = window_flags(ws, need, B * H, T, segments)
     say("%s: window flags per lane %s" % (tag, flags.tolist()))
