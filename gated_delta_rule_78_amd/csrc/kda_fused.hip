@@ -3,22 +3,25 @@
 // (Kimi K3 reading notes, liuzhao09.github.io/papers/kimi-k3.html, section 2.2 chunk equations;
 // section 2.5 for the sequence split that gives each workgroup its own segment).
 //
-// One 8-wave workgroup per (lane, segment). Waves 0-3 (producer) build chunk c's record in an LDS
-// buffer with the intra-chunk kernel's per-wave code (intra::ChunkWave: decay factors, Gram
-// tiles, UT solve); waves 4-7 (consumer) hold the fp32 state in MFMA accumulators, 16 * DV/64
-// columns each, and run the state step on chunk c - 1's record while the producer works on
-// chunk c:
-//   epoch c:  producer: decay factors of chunk c      | consumer: state step of chunk c - 1
+// One 8-wave workgroup per (lane, segment). Waves 0-3 (producer) run the key side of the
+// intra-chunk work with the intra-chunk kernel's per-wave code (intra::ChunkWave, SPLIT): decay
+// factors, the off-diagonal Gram tiles and A_qk, the W half of the UT solve, into an LDS record
+// buffer. Waves 4-7 (consumer) hold the fp32 state in MFMA accumulators, 32 columns each, and
+// take the value side (intra::ValueWave): their V rows, A_kk's diagonal block and its inverse,
+// the U half of the solve (U stays in their registers), then the state step. Chunk c's record is
+// built while the consumer steps through chunk c - 1's:
+//   epoch c:  producer: decay factors of chunk c        | consumer: state step of chunk c - 1
 //             ---- barrier 1: the consumer is done with the record buffer ----
-//             producer: record pieces held back, loads | consumer: o rows of chunk c - 1
-//                       of chunk c + 1, Gram tiles
+//             producer: record pieces held back, loads  | consumer: o rows of chunk c - 1, V of
+//                       of chunk c + 1, Gram tiles      |   chunk c staged, diagonal inverses
 //             ---- barrier 2 ----
-//             producer: UT solve (W, U)
+//             producer: W                               | consumer: U of chunk c
 //             ---- barrier 3: chunk c's record is complete ----
 // The two roles run separate loops with the same barriers (every barrier orders LDS only), so
 // the registers of one role are free for the other. Per chunk the kernel reads q, k, v,
 // log_alpha and beta and writes o: the two-kernel path also writes and reads the record
-// (71 KiB per chunk at d = 128) through HBM.
+// (71 KiB per chunk at d = 128) through HBM. Every product is the two-kernel path's, in the same
+// order, so the outputs are the same bit for bit.
 //
 // Entry states: S0 for segment 0, else the window's S~ (ChunkLaunch::ws_entry, from a kPassWindow
 // launch); a lane with an inexact window (ws_flag) is left to the two-kernel fallback.
@@ -30,14 +33,24 @@ namespace {
 
 using intra::ChunkWave;
 using intra::IntraSmem;
+using intra::ValueWave;
 using intra::kC;
 
 constexpr int kThreads = 512;
 
+// The record buffer's U blocks are never written (U stays with the consumer): the consumer's V
+// stages live there, the fourth one after the record.
 template <int DK, int DV>
 struct __align__(16) FusedSmem {
+    typedef RecordLayout<DK, DV> R;
+    static constexpr int VSTAGE = kC * intra::IntraCfg<DK, DV>::LDVS * 2;
+    static_assert(3 * VSTAGE <= 2 * R::NV * 1024, "three V stages fit the U blocks");
     IntraSmem<DK, DV> ip;                              // the producer's stages
-    unsigned char rec[RecordLayout<DK, DV>::BYTES];    // the record of the chunk in flight
+    unsigned char rec[R::BYTES];                       // the record of the chunk in flight
+    unsigned char vst3[VSTAGE];                        // the fourth consumer wave's V stage
+    __device__ __forceinline__ bf16_t* vstage(int cw) {
+        return reinterpret_cast<bf16_t*>(cw < 3 ? rec + R::U * 1024 + cw * VSTAGE : vst3);
+    }
 };
 
 // Barrier over the whole workgroup that orders LDS accesses only (global loads stay in flight).
@@ -46,7 +59,7 @@ __device__ __forceinline__ void epoch_barrier() { lds_barrier(); }
 template <int DK, int DV>
 __device__ __forceinline__ void producer(const ChunkLaunch& p, FusedSmem<DK, DV>& sm, int64_t row_base, int64_t cb,
                                          int64_t ce) {
-    ChunkWave<DK, DV, false> cw(sm.ip);
+    ChunkWave<DK, DV, false, true> cw(sm.ip);
     unsigned char* rec = sm.rec;
     const int64_t T = p.T;
     auto load = [&](int64_t c) {
@@ -84,7 +97,15 @@ __device__ __forceinline__ void consumer(const ChunkLaunch& p, FusedSmem<DK, DV>
     const int l16 = l & 15;
     const int lq = l >> 4;
     const int64_t DVl = DV;
+    const int64_t T = p.T;
     const int col0 = w * 16 * NT;
+    ValueWave<DK, DV> vw(sm.ip, sm.vstage(w), w);
+    auto load = [&](int64_t c) {
+        uint32_t n = 0;
+        if (c < ce) n = (uint32_t)(T - c * kC < kC ? T - c * kC : kC);
+        vw.load(p.v, lane * T + (c < ce ? c : 0) * kC, n);
+    };
+    load(cb);
     // S[nt][M] holds rows 16M + 4lq + r, column col0 + 16nt + l16
     f32x4 S[NT][NM];
     const float* entry = seg > 0 ? p.ws_entry + ((lane * p.nseg + seg) * DK) * DVl : (p.S0 ? p.S0 + lane * DK * DVl : nullptr);
@@ -95,15 +116,17 @@ __device__ __forceinline__ void consumer(const ChunkLaunch& p, FusedSmem<DK, DV>
 #pragma unroll
             for (int r = 0; r < 4; ++r)
                 S[nt][M][r] = entry ? entry[(16 * M + 4 * lq + r) * DVl + col0 + 16 * nt + l16] : 0.f;
-    const __amdgpu_buffer_rsrc_t ro = make_rsrc((const TOut*)p.o + lane * p.T * DVl, (uint32_t)(p.T * DVl * sizeof(TOut)));
+    const __amdgpu_buffer_rsrc_t ro = make_rsrc((const TOut*)p.o + lane * T * DVl, (uint32_t)(T * DVl * sizeof(TOut)));
     constexpr bool PAIRED = sizeof(TOut) == 2 && NT % 2 == 0;
     f32x4 O[NT][4];
+    i16x4 U[NT][4];   // U of the chunk the next state step takes
     for (int64_t c = cb; c <= ce; ++c) {
-        const bool work = c > cb;   // chunk c - 1's record is in the buffer
-        if (work)
-            chunk_step<TOut, DK, DV, NT, 0, NT, true>(sm.rec, S, col0, DV / 16 - col0 / 16, O, false, ro, nullptr, w);
+        const bool prev = c > cb;   // chunk c - 1's record is in the buffer
+        const bool cur = c < ce;    // chunk c is being built
+        if (prev)
+            chunk_step<TOut, DK, DV, NT, 0, NT, true>(sm.rec, S, col0, DV / 16 - col0 / 16, O, false, ro, nullptr, w, U);
         epoch_barrier();   // 1
-        if (work) {
+        if (prev) {
 #pragma unroll
             for (int I = 0; I < 4; ++I) {
                 const uint32_t row = (uint32_t)((c - 1) * kC + 16 * I + l16);
@@ -122,7 +145,14 @@ __device__ __forceinline__ void consumer(const ChunkLaunch& p, FusedSmem<DK, DV>
                 }
             }
         }
+        if (cur) {
+            vw.pin_inputs();
+            vw.stage();
+            load(c + 1);
+            vw.diag_inverse();
+        }
         epoch_barrier();   // 2
+        if (cur) vw.solve(U);
         epoch_barrier();   // 3
     }
     if (seg == p.nseg - 1 && p.S_T) {

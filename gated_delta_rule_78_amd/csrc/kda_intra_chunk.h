@@ -123,11 +123,127 @@ struct __align__(16) IntraSmem {
     bf16_t fij[6][DK];          // exp(G_ref(I) - G_ref(J)) per channel for the pairs I > J
 };
 
+// LDS fragment block of tensor X (0 Q~, 1 K~, 2 K^), token block I, of the wave owning key
+// channels 32ks .. 32ks + 31 (block-relative factors; see ChunkWave::decay).
+template <int DK, int DV>
+__device__ __forceinline__ unsigned char* lds_block(IntraSmem<DK, DV>& sm, int ks, int X, int I) {
+    return sm.region[ks] + IntraCfg<DK, DV>::STAGE_A + (X * 4 + I) * 1024;
+}
+
+// Diagonal block I of A_kk = Diag(beta) StrictTril(K~ K^^T), rows i = 16I + 4lq + r and column
+// m = 16I + l16, in fp32 into sm.ld[I] (column-major).
+template <int DK, int DV>
+__device__ __forceinline__ void diag_akk_block(IntraSmem<DK, DV>& sm, int I, int l) {
+    const int l16 = l & 15, lq = l >> 4;
+    f32x4 acc = kZero4;
+#pragma unroll
+    for (int ks = 0; ks < DK / 32; ++ks)
+        acc = mma32(read16(lds_block(sm, ks, 1, I) + l * 16), read16(lds_block(sm, ks, 2, I) + l * 16), acc);
+    const float4 b4 = *reinterpret_cast<const float4*>(&sm.beta[16 * I + 4 * lq]);
+    f32x4 o;
+    o[0] = (l16 < 4 * lq + 0) ? b4.x * acc[0] : 0.f;
+    o[1] = (l16 < 4 * lq + 1) ? b4.y * acc[1] : 0.f;
+    o[2] = (l16 < 4 * lq + 2) ? b4.z * acc[2] : 0.f;
+    o[3] = (l16 < 4 * lq + 3) ? b4.w * acc[3] : 0.f;
+    *reinterpret_cast<f32x4*>(&sm.ld[I][l16 * 16 + 4 * lq]) = o;   // column m = l16
+}
+
+// Row i of T = (I + L)^{-1} for the strictly lower block L = sm.ld[b], from T (I + L) = I:
+// t[m] = -sum_{n > m} t[n] L[n][m] for m < i, t[i] = 1, t[m > i] = 0; stored to sm.tinv[b] as bf16
+// when `store`.
+template <int DK, int DV>
+__device__ __forceinline__ void invert_row(IntraSmem<DK, DV>& sm, int b, int i, bool store) {
+    const float* Lc = sm.ld[b];
+    float t[16];
+#pragma unroll
+    for (int n = 0; n < 16; ++n) t[n] = (n == i) ? 1.f : 0.f;
+#pragma unroll
+    for (int m = 14; m >= 0; --m) {
+        float s = 0.f;
+#pragma unroll
+        for (int nb = (m + 1) / 4; nb < 4; ++nb) {
+            const float4 L4 = *reinterpret_cast<const float4*>(&Lc[m * 16 + 4 * nb]);
+            s += L4.x * t[4 * nb] + L4.y * t[4 * nb + 1] + L4.z * t[4 * nb + 2] + L4.w * t[4 * nb + 3];
+        }
+        if (m < i) t[m] = -s;
+    }
+    uint4 r0, r1;
+    r0.x = pack_bf16x2(t[0], t[1]);   r0.y = pack_bf16x2(t[2], t[3]);
+    r0.z = pack_bf16x2(t[4], t[5]);   r0.w = pack_bf16x2(t[6], t[7]);
+    r1.x = pack_bf16x2(t[8], t[9]);   r1.y = pack_bf16x2(t[10], t[11]);
+    r1.z = pack_bf16x2(t[12], t[13]); r1.w = pack_bf16x2(t[14], t[15]);
+    if (store) {
+        *reinterpret_cast<uint4*>(&sm.tinv[b][i * 24]) = r0;
+        *reinterpret_cast<uint4*>(&sm.tinv[b][i * 24 + 8]) = r1;
+    }
+}
+
+// Off-diagonal block pair (I > J): K^_J rescaled once by f_IJ and used for both the A_kk block
+// (bf16, beta-scaled, to sm.akk) and the A_qk block (to the record). Transposed: the lane holds
+// X[16I + l16][16J + 4lq + r], so the A_kk blocks are K16 A operands as computed and the A_qk
+// blocks are record halves (record block A(I, h) holds J = 2h in bytes 0..7 and J = 2h + 1 in
+// bytes 8..15 of each lane's 16).
+template <int DK, int DV>
+__device__ __forceinline__ void gram_pair(IntraSmem<DK, DV>& sm, unsigned char* rec, int I, int J, int l) {
+    typedef RecordLayout<DK, DV> R;
+    const int l16 = l & 15, lq = l >> 4;
+    const bf16_t* f = sm.fij[pair_index(I, J)];
+    f32x4 akk = kZero4, aqk = kZero4;
+#pragma unroll
+    for (int ks = 0; ks < DK / 32; ++ks) {
+        const bf16x8 a = scale_frag(read16(lds_block(sm, ks, 2, J) + l * 16), f, ks, lq);
+        akk = mma32(a, read16(lds_block(sm, ks, 1, I) + l * 16), akk);
+        aqk = mma32(a, read16(lds_block(sm, ks, 0, I) + l * 16), aqk);
+    }
+    *reinterpret_cast<i16x4*>(&sm.akk[pair_index(I, J)][l * 4]) = cvt4(akk * sm.beta[16 * I + l16]);
+    *reinterpret_cast<i16x4*>(rec + R::a(I, J >> 1) * 1024 + l * 16 + 8 * (J & 1)) = cvt4(aqk);
+}
+
+// Diagonal A_qk block I (j <= i kept) to the record; for I = 0 (I = 2) also the zero J = 1 (J = 3)
+// half of record block A(0,0) (A(2,1)).
+template <int DK, int DV>
+__device__ __forceinline__ void diag_aqk_block(IntraSmem<DK, DV>& sm, unsigned char* rec, int I, int l) {
+    typedef RecordLayout<DK, DV> R;
+    const int l16 = l & 15, lq = l >> 4;
+    f32x4 acc = kZero4;
+#pragma unroll
+    for (int ks = 0; ks < DK / 32; ++ks)
+        acc = mma32(read16(lds_block(sm, ks, 2, I) + l * 16), read16(lds_block(sm, ks, 0, I) + l * 16), acc);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[r] = (4 * lq + r <= l16) ? acc[r] : 0.f;
+    unsigned char* b = rec + R::a(I, I >> 1) * 1024 + l * 16;
+    *reinterpret_cast<i16x4*>(b + 8 * (I & 1)) = cvt4(acc);
+    if ((I & 1) == 0) *reinterpret_cast<uint2*>(b + 8) = make_uint2(0u, 0u);
+}
+
+// Operands of the blocked substitution, from the Gram phase's LDS results.
+template <int DK, int DV>
+__device__ __forceinline__ SolveOps solve_ops(const IntraSmem<DK, DV>& sm, int l) {
+    const int l16 = l & 15, lq = l >> 4;
+    SolveOps ops;
+    ops.a10 = read8(&sm.akk[0][l * 4]);
+    ops.a2 = cat(read8(&sm.akk[1][l * 4]), read8(&sm.akk[2][l * 4]));
+    ops.a3 = cat(read8(&sm.akk[3][l * 4]), read8(&sm.akk[4][l * 4]));
+    ops.a32 = read8(&sm.akk[5][l * 4]);
+    ops.t0 = read8(&sm.tinv[0][l16 * 24 + 4 * lq]);
+    ops.t1 = read8(&sm.tinv[1][l16 * 24 + 4 * lq]);
+    ops.t2 = read8(&sm.tinv[2][l16 * 24 + 4 * lq]);
+    ops.t3 = read8(&sm.tinv[3][l16 * 24 + 4 * lq]);
+    ops.b0 = *reinterpret_cast<const f32x4*>(&sm.beta[0 + 4 * lq]);
+    ops.b1 = *reinterpret_cast<const f32x4*>(&sm.beta[16 + 4 * lq]);
+    ops.b2 = *reinterpret_cast<const f32x4*>(&sm.beta[32 + 4 * lq]);
+    ops.b3 = *reinterpret_cast<const f32x4*>(&sm.beta[48 + 4 * lq]);
+    return ops;
+}
+
 // The wave's part of one chunk. `rec` (global or LDS memory) receives the chunk's record
 // (kda_record.h). With DEFER, decay() keeps the record pieces it forms (Q~, K-, gamma) in
 // registers and in the wave's LDS stage, and publish() writes them: the fused kernel's consumer
 // waves may still be reading the previous chunk's record while decay() runs.
-template <int DK, int DV, bool ZPRO>
+// With SPLIT (the fused kernel's producer) the value side and the diagonal blocks of A_kk belong
+// to other waves (ValueWave): decay() loads and stages no V, gram() spreads the off-diagonal pairs
+// and the diagonal A_qk blocks over all four waves, and solve() solves the W tiles only.
+template <int DK, int DV, bool ZPRO, bool SPLIT = false>
 struct ChunkWave {
     typedef IntraCfg<DK, DV> Cfg;
     typedef RecordLayout<DK, DV> R;
@@ -157,7 +273,7 @@ struct ChunkWave {
         l16 = l & 15;
         lq = l >> 4;
         kw = NKS == 4 || w < NKS;
-        vw = Cfg::has_v(w);
+        vw = !SPLIT && Cfg::has_v(w);
         vc0 = 16 * Cfg::vt0(w);
         // Lane's 16-byte slice of a q/k row: rows (lq = 0, 1) and (2, 3) then trade halves with one
         // permlane16 swap per dword pair, which leaves each lane its fragment channels
@@ -169,9 +285,7 @@ struct ChunkWave {
     }
     __device__ __forceinline__ unsigned char* region() const { return sm.region[w]; }
     // LDS block of tensor X (0 Q~, 1 K~, 2 K^), token block I, of the wave owning channels 32ks..
-    __device__ __forceinline__ unsigned char* lblk(int ks, int X, int I) const {
-        return sm.region[ks] + Cfg::STAGE_A + (X * 4 + I) * 1024;
-    }
+    __device__ __forceinline__ unsigned char* lblk(int ks, int X, int I) const { return lds_block(sm, ks, X, I); }
 
     // Issue the loads of one chunk: rows row0 .. row0 + n - 1 of the bf16 row-major inputs q, k,
     // g (the decay rows: log_alpha, or the pre-activation z of the fused prologue), v and beta
@@ -401,105 +515,38 @@ struct ChunkWave {
         store_kbar(rec);
     }
 
-    // Phase 2: Gram tiles from every wave's LDS blocks.
+    // Phase 2: Gram tiles from every wave's LDS blocks. Wave 0 forms the four diagonal blocks of
+    // A_kk and inverts I + A_kk,II (lane: block lq, row l16); waves 1-3 take two off-diagonal pairs
+    // each, then the diagonal A_qk blocks. SPLIT: no diagonal A_kk work; the six pairs and the four
+    // diagonal A_qk blocks spread over the four waves.
     __device__ __forceinline__ void gram(unsigned char* rec) {
-        auto blk = [&](int b) -> unsigned char* { return rec + b * 1024 + l * 16; };
+        if (SPLIT) {
+            if (w == 0) { gram_pair(sm, rec, 1, 0, l); gram_pair(sm, rec, 2, 0, l); }
+            if (w == 1) { gram_pair(sm, rec, 2, 1, l); gram_pair(sm, rec, 3, 0, l); }
+            if (w == 2) { gram_pair(sm, rec, 3, 1, l); diag_aqk_block(sm, rec, 0, l); diag_aqk_block(sm, rec, 1, l); }
+            if (w == 3) { gram_pair(sm, rec, 3, 2, l); diag_aqk_block(sm, rec, 2, l); diag_aqk_block(sm, rec, 3, l); }
+            return;
+        }
         if (w == 0) {
-            // diagonal blocks, rows i = 16I + 4lq + r, column m = 16I + l16; wave 0 then inverts them
 #pragma unroll
-            for (int I = 0; I < 4; ++I) {
-                f32x4 acc = kZero4;
-#pragma unroll
-                for (int ks = 0; ks < NKS; ++ks)
-                    acc = mma32(read16(lblk(ks, 1, I) + l * 16), read16(lblk(ks, 2, I) + l * 16), acc);
-                const float4 b4 = *reinterpret_cast<const float4*>(&sm.beta[16 * I + 4 * lq]);
-                f32x4 o;
-                o[0] = (l16 < 4 * lq + 0) ? b4.x * acc[0] : 0.f;
-                o[1] = (l16 < 4 * lq + 1) ? b4.y * acc[1] : 0.f;
-                o[2] = (l16 < 4 * lq + 2) ? b4.z * acc[2] : 0.f;
-                o[3] = (l16 < 4 * lq + 3) ? b4.w * acc[3] : 0.f;
-                *reinterpret_cast<f32x4*>(&sm.ld[I][l16 * 16 + 4 * lq]) = o;   // column m = l16
-            }
+            for (int I = 0; I < 4; ++I) diag_akk_block(sm, I, l);
             wave_lds_sync();
-            // Lane (block lq, row i = l16): row i of T = (I + L)^{-1} from T (I + L) = I, i.e.
-            // t[m] = -sum_{n > m} t[n] L[n][m] for m < i, t[i] = 1, t[m > i] = 0.
-            const float* Lc = sm.ld[lq];
-            const int i = l16;
-            float t[16];
-#pragma unroll
-            for (int n = 0; n < 16; ++n) t[n] = (n == i) ? 1.f : 0.f;
-#pragma unroll
-            for (int m = 14; m >= 0; --m) {
-                float s = 0.f;
-#pragma unroll
-                for (int nb = (m + 1) / 4; nb < 4; ++nb) {
-                    const float4 L4 = *reinterpret_cast<const float4*>(&Lc[m * 16 + 4 * nb]);
-                    s += L4.x * t[4 * nb] + L4.y * t[4 * nb + 1] + L4.z * t[4 * nb + 2] + L4.w * t[4 * nb + 3];
-                }
-                if (m < i) t[m] = -s;
-            }
-            uint4 r0, r1;
-            r0.x = pack_bf16x2(t[0], t[1]);   r0.y = pack_bf16x2(t[2], t[3]);
-            r0.z = pack_bf16x2(t[4], t[5]);   r0.w = pack_bf16x2(t[6], t[7]);
-            r1.x = pack_bf16x2(t[8], t[9]);   r1.y = pack_bf16x2(t[10], t[11]);
-            r1.z = pack_bf16x2(t[12], t[13]); r1.w = pack_bf16x2(t[14], t[15]);
-            *reinterpret_cast<uint4*>(&sm.tinv[lq][i * 24]) = r0;
-            *reinterpret_cast<uint4*>(&sm.tinv[lq][i * 24 + 8]) = r1;
+            invert_row(sm, lq, l16, true);
         } else {
-            // Waves 1-3: two off-diagonal block pairs (I > J) each, with K^_J rescaled once per pair
-            // and used for both A_kk and A_qk (transposed: the lane holds X[16I + l16][16J + 4lq + r],
-            // so the A_kk blocks are K16 A operands as computed and the A_qk blocks are record
-            // halves); then the diagonal A_qk blocks (j <= i kept). Record block A(I, h) holds
-            // J = 2h in bytes 0..7 and J = 2h + 1 in bytes 8..15 of each lane's 16.
             const int I0 = w == 1 ? 1 : (w == 2 ? 2 : 3), J0 = w == 1 ? 0 : (w == 2 ? 1 : 1);
             const int I1 = w == 1 ? 2 : 3, J1 = w == 1 ? 0 : (w == 2 ? 0 : 2);
-#pragma unroll
-            for (int pr = 0; pr < 2; ++pr) {
-                const int I = pr ? I1 : I0, J = pr ? J1 : J0;
-                const bf16_t* f = sm.fij[pair_index(I, J)];
-                f32x4 akk = kZero4, aqk = kZero4;
-#pragma unroll
-                for (int ks = 0; ks < NKS; ++ks) {
-                    const bf16x8 a = scale_frag(read16(lblk(ks, 2, J) + l * 16), f, ks, lq);
-                    akk = mma32(a, read16(lblk(ks, 1, I) + l * 16), akk);
-                    aqk = mma32(a, read16(lblk(ks, 0, I) + l * 16), aqk);
-                }
-                *reinterpret_cast<i16x4*>(&sm.akk[pair_index(I, J)][l * 4]) = cvt4(akk * sm.beta[16 * I + l16]);
-                *reinterpret_cast<i16x4*>(blk(R::a(I, J >> 1)) + 8 * (J & 1)) = cvt4(aqk);
-            }
-            // diagonal A_qk blocks: wave 1 takes I = 0, 1, wave 2 I = 2, wave 3 I = 3; the wave that
-            // writes I = 0 (I = 2) also zeroes the J = 1 (J = 3) half of record block A(0,0) (A(2,1))
+            gram_pair(sm, rec, I0, J0, l);
+            gram_pair(sm, rec, I1, J1, l);
+            // diagonal A_qk blocks: wave 1 takes I = 0, 1, wave 2 I = 2, wave 3 I = 3
             const int nd = w == 1 ? 2 : 1;
-            for (int d = 0; d < nd; ++d) {
-                const int I = w == 1 ? d : w;
-                f32x4 acc = kZero4;
-#pragma unroll
-                for (int ks = 0; ks < NKS; ++ks)
-                    acc = mma32(read16(lblk(ks, 2, I) + l * 16), read16(lblk(ks, 0, I) + l * 16), acc);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) acc[r] = (4 * lq + r <= l16) ? acc[r] : 0.f;
-                *reinterpret_cast<i16x4*>(blk(R::a(I, I >> 1)) + 8 * (I & 1)) = cvt4(acc);
-                if ((I & 1) == 0) *reinterpret_cast<uint2*>(blk(R::a(I, I >> 1)) + 8) = make_uint2(0u, 0u);
-            }
+            for (int d = 0; d < nd; ++d) diag_aqk_block(sm, rec, w == 1 ? d : w, l);
         }
     }
 
     // Phase 3: (I + A_kk) [W | U] = Diag(beta) [K~ | V]; U and -W to the record.
     __device__ __forceinline__ void solve(unsigned char* rec) {
         auto blk = [&](int b) -> unsigned char* { return rec + b * 1024 + l * 16; };
-        SolveOps ops;
-        ops.a10 = read8(&sm.akk[0][l * 4]);
-        ops.a2 = cat(read8(&sm.akk[1][l * 4]), read8(&sm.akk[2][l * 4]));
-        ops.a3 = cat(read8(&sm.akk[3][l * 4]), read8(&sm.akk[4][l * 4]));
-        ops.a32 = read8(&sm.akk[5][l * 4]);
-        ops.t0 = read8(&sm.tinv[0][l16 * 24 + 4 * lq]);
-        ops.t1 = read8(&sm.tinv[1][l16 * 24 + 4 * lq]);
-        ops.t2 = read8(&sm.tinv[2][l16 * 24 + 4 * lq]);
-        ops.t3 = read8(&sm.tinv[3][l16 * 24 + 4 * lq]);
-        ops.b0 = *reinterpret_cast<const f32x4*>(&sm.beta[0 + 4 * lq]);
-        ops.b1 = *reinterpret_cast<const f32x4*>(&sm.beta[16 + 4 * lq]);
-        ops.b2 = *reinterpret_cast<const f32x4*>(&sm.beta[32 + 4 * lq]);
-        ops.b3 = *reinterpret_cast<const f32x4*>(&sm.beta[48 + 4 * lq]);
+        const SolveOps ops = solve_ops(sm, l);
         if (vw) {
 #pragma unroll
             for (int j = 0; j < VPW; ++j) {
@@ -528,6 +575,72 @@ struct ChunkWave {
                 const bf16_t* b0 = &wt[(4 * lq + (l16 >> 2)) * LDW + 16 * I + 4 * (l16 & 3)];
                 *reinterpret_cast<bf16x8*>(blk(R::w(I, w))) = cat(tr_read(b0), tr_read(b0 + 16 * LDW));
             }
+        }
+    }
+};
+
+// The value side of one chunk for a wave that owns value tiles 2 vw, 2 vw + 1 (dv = 128) and key
+// block I = vw of A_kk's diagonal, next to four ChunkWave<..., SPLIT> waves (the fused kernel's
+// consumer): V rows loaded one chunk ahead, staged in LDS into accumulator layout; the diagonal
+// block and its inverse (for every wave's solve); and U = (I + A_kk)^{-1} Diag(beta) V for its
+// tiles, kept in registers as the bf16 values a record would hold.
+template <int DK, int DV>
+struct ValueWave {
+    typedef IntraCfg<DK, DV> Cfg;
+    static constexpr int LDVS = Cfg::LDVS;
+    static_assert(DV == 128 && Cfg::VPW == 2, "two value tiles per wave");
+    IntraSmem<DK, DV>& sm;
+    bf16_t* vst;      // this wave's V stage: 64 rows of LDVS elements
+    int vw, l, l16, lq;
+    uint32_t v_voff;
+    uint4 pv[4];      // V rows of the chunk being loaded
+    i16x4 vacc[2][4]; // V rows 16I + 4lq + e, column 32 vw + 16j + l16
+
+    __device__ __forceinline__ ValueWave(IntraSmem<DK, DV>& s, bf16_t* stage, int wave) : sm(s), vst(stage), vw(wave) {
+        l = threadIdx.x & 63;
+        l16 = l & 15;
+        lq = l >> 4;
+        v_voff = ((l / 4) * DV + 32 * vw + 8 * (l % 4)) * 2;
+    }
+    // rows row0 .. row0 + n - 1 of v (zeros from n on; n = 0 moves no data)
+    __device__ __forceinline__ void load(const void* v, int64_t row0, uint32_t n) {
+        const __amdgpu_buffer_rsrc_t rv = make_rsrc((const bf16_t*)v + row0 * DV, n * (DV * 2));
+        uint32_t vo = v_voff;
+        asm volatile("" : "+v"(vo));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pv[i] = buf_load16(rv, vo + i * 16 * DV * 2);
+    }
+    __device__ __forceinline__ void pin_inputs() {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pin(pv[i]);
+    }
+    // the loaded rows into accumulator layout through the stage
+    __device__ __forceinline__ void stage() {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(&vst[(i * 16 + l / 4) * LDVS + 8 * (l % 4)]) = pv[i];
+        wave_lds_sync();
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int I = 0; I < 4; ++I)
+                vacc[j][I] = tr_read(&vst[(16 * I + 4 * lq + (l16 >> 2)) * LDVS + 16 * j + 4 * (l16 & 3)]);
+    }
+    // diagonal block vw of A_kk and the inverse of I + A_kk,vw (the lanes of row group lq = 0 store it)
+    __device__ __forceinline__ void diag_inverse() {
+        diag_akk_block(sm, vw, l);
+        wave_lds_sync();
+        invert_row(sm, vw, l16, lq == 0);
+    }
+    // U of this wave's two tiles, in the record's rounding
+    __device__ __forceinline__ void solve(i16x4 (&U)[2][4]) {
+        const SolveOps ops = solve_ops(sm, l);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            f32x4 X[4];
+            ut_solve(ops, unpack4f(vacc[j][0]), unpack4f(vacc[j][1]), unpack4f(vacc[j][2]), unpack4f(vacc[j][3]), X[0],
+                     X[1], X[2], X[3]);
+#pragma unroll
+            for (int I = 0; I < 4; ++I) U[j][I] = cvt4(X[I]);
         }
     }
 };

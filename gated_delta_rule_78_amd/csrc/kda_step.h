@@ -80,10 +80,12 @@ __device__ __forceinline__ void copy_record(__amdgpu_buffer_rsrc_t rsrc, uint32_
 // The next chunk's record copy (when `copy`) is issued in parts, one after each k step of the
 // first products: issued in one piece before them, its stalls (the copies queue behind the
 // record stream) kept the wave from starting the products for about a microsecond per chunk.
+// With `ureg`, the U tiles come from registers (ureg[nt][I]: the record's bf16 U values of tile
+// G0 + nt, rows 16I + 4lq + r) instead of the record.
 template <typename TOut, int DK, int DV, int NT, int G0, int NTG, bool FIN>
 __device__ __forceinline__ void chunk_step(const unsigned char* rbuf, f32x4 (&S)[NT][DK / 16], int col0, int nu,
                                            f32x4 (&Opend)[NT][4], bool copy, __amdgpu_buffer_rsrc_t crs,
-                                           unsigned char* cdst, int w) {
+                                           unsigned char* cdst, int w, const i16x4 (*ureg)[4] = nullptr) {
     typedef CopyPlan<DK, DV, FIN> CP;
     typedef RecordLayout<DK, DV> R;
     constexpr int NKS = R::NKS, NM = R::NM;
@@ -99,7 +101,10 @@ __device__ __forceinline__ void chunk_step(const unsigned char* rbuf, f32x4 (&S)
 #pragma unroll
     for (int nt = 0; nt < NTG; ++nt) {
         const int n = col0 / 16 + G0 + nt;
-        if (FIN || G0 + nt < nu) {
+        if (ureg) {
+#pragma unroll
+            for (int I = 0; I < 4; ++I) Vt[nt][I] = unpack4f(ureg[G0 + nt][I]);
+        } else if (FIN || G0 + nt < nu) {
             const bf16x8 u0 = KDA_FRAG(R::u(n, 0));
             const bf16x8 u1 = KDA_FRAG(R::u(n, 1));
             Vt[nt][0] = unpack4f(lo4(u0)); Vt[nt][1] = unpack4f(hi4(u0));
