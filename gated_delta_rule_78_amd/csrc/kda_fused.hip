@@ -13,7 +13,9 @@
 //   epoch c:  producer: decay factors of chunk c        | consumer: state step of chunk c - 1
 //             ---- barrier 1: the consumer is done with the record buffer ----
 //             producer: record pieces held back, loads  | consumer: o rows of chunk c - 1, V of
-//                       of chunk c + 1, Gram tiles      |   chunk c staged, diagonal inverses
+//                       of chunk c + 1, Gram tiles      |   chunk c staged, loads of V of chunk
+//                                                       |   c + 1, A_kk's diagonal blocks and
+//                                                       |   their inverses
 //             ---- barrier 2 ----
 //             producer: W                               | consumer: U of chunk c
 //             ---- barrier 3: chunk c's record is complete ----

@@ -116,7 +116,7 @@ template <int DK, int DV>
 struct __align__(16) IntraSmem {
     typedef IntraCfg<DK, DV> Cfg;
     unsigned char region[4][Cfg::REGION];
-    float ld[4][16 * 16];       // beta-scaled strictly lower diagonal blocks of A_kk, column-major
+    float ld[4][16 * 16];       // beta-scaled strictly lower diagonal blocks of A_kk, row-major
     bf16_t akk[6][256];         // off-diagonal blocks (I, J), I > J, as K16 A fragments
     bf16_t tinv[4][16 * 24];    // (I + A_kk,II)^{-1}, row-major, 24-element rows
     float beta[kC];
@@ -131,7 +131,7 @@ __device__ __forceinline__ unsigned char* lds_block(IntraSmem<DK, DV>& sm, int k
 }
 
 // Diagonal block I of A_kk = Diag(beta) StrictTril(K~ K^^T), rows i = 16I + 4lq + r and column
-// m = 16I + l16, in fp32 into sm.ld[I] (column-major).
+// m = 16I + l16, in fp32 into sm.ld[I] (row-major).
 template <int DK, int DV>
 __device__ __forceinline__ void diag_akk_block(IntraSmem<DK, DV>& sm, int I, int l) {
     const int l16 = l & 15, lq = l >> 4;
@@ -140,32 +140,36 @@ __device__ __forceinline__ void diag_akk_block(IntraSmem<DK, DV>& sm, int I, int
     for (int ks = 0; ks < DK / 32; ++ks)
         acc = mma32(read16(lds_block(sm, ks, 1, I) + l * 16), read16(lds_block(sm, ks, 2, I) + l * 16), acc);
     const float4 b4 = *reinterpret_cast<const float4*>(&sm.beta[16 * I + 4 * lq]);
-    f32x4 o;
-    o[0] = (l16 < 4 * lq + 0) ? b4.x * acc[0] : 0.f;
-    o[1] = (l16 < 4 * lq + 1) ? b4.y * acc[1] : 0.f;
-    o[2] = (l16 < 4 * lq + 2) ? b4.z * acc[2] : 0.f;
-    o[3] = (l16 < 4 * lq + 3) ? b4.w * acc[3] : 0.f;
-    *reinterpret_cast<f32x4*>(&sm.ld[I][l16 * 16 + 4 * lq]) = o;   // column m = l16
+    const float bb[4] = {b4.x, b4.y, b4.z, b4.w};
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sm.ld[I][(4 * lq + r) * 16 + l16] = (l16 < 4 * lq + r) ? bb[r] * acc[r] : 0.f;
 }
 
 // Row i of T = (I + L)^{-1} for the strictly lower block L = sm.ld[b], from T (I + L) = I:
 // t[m] = -sum_{n > m} t[n] L[n][m] for m < i, t[i] = 1, t[m > i] = 0; stored to sm.tinv[b] as bf16
-// when `store`.
+// when `store`. Right-looking: once t[n] is final, every partial sum of a column m < n takes its
+// term at once, so the dependent chain is one multiply-add per row (16) rather than one per term.
 template <int DK, int DV>
 __device__ __forceinline__ void invert_row(IntraSmem<DK, DV>& sm, int b, int i, bool store) {
-    const float* Lc = sm.ld[b];
-    float t[16];
+    const float* L = sm.ld[b];
+    float t[16], s[16];
 #pragma unroll
-    for (int n = 0; n < 16; ++n) t[n] = (n == i) ? 1.f : 0.f;
+    for (int m = 0; m < 16; ++m) s[m] = 0.f;
 #pragma unroll
-    for (int m = 14; m >= 0; --m) {
-        float s = 0.f;
+    for (int n = 15; n >= 0; --n) {
+        t[n] = n == i ? 1.f : (n < i ? -s[n] : 0.f);
+        // row n's address depends (in form only) on t[n + 4]: its loads go out at most four rows
+        // ahead, instead of all 36 at the top, which would hold about 140 registers
+        int off = n * 16;
+        if (n + 4 <= 15) asm volatile("" : "+v"(off) : "v"(t[n + 4]));
 #pragma unroll
-        for (int nb = (m + 1) / 4; nb < 4; ++nb) {
-            const float4 L4 = *reinterpret_cast<const float4*>(&Lc[m * 16 + 4 * nb]);
-            s += L4.x * t[4 * nb] + L4.y * t[4 * nb + 1] + L4.z * t[4 * nb + 2] + L4.w * t[4 * nb + 3];
+        for (int mb = 0; 4 * mb < n; ++mb) {
+            const float4 L4 = *reinterpret_cast<const float4*>(&L[off + 4 * mb]);   // L[n][4mb ..]
+            if (4 * mb + 0 < n) s[4 * mb + 0] += L4.x * t[n];
+            if (4 * mb + 1 < n) s[4 * mb + 1] += L4.y * t[n];
+            if (4 * mb + 2 < n) s[4 * mb + 2] += L4.z * t[n];
+            if (4 * mb + 3 < n) s[4 * mb + 3] += L4.w * t[n];
         }
-        if (m < i) t[m] = -s;
     }
     uint4 r0, r1;
     r0.x = pack_bf16x2(t[0], t[1]);   r0.y = pack_bf16x2(t[2], t[3]);
