@@ -108,22 +108,25 @@ static double two_kernel_state_us(int64_t lanes, int64_t nchunks, int64_t cus, i
     return pass_us(cps + w, lanes * n, 0, cus) + (n > 2 ? 3.0 : 1.0) * 4.5;
 }
 
-// The fused plan: one 8-wave workgroup per (lane, segment) and compute unit, each chunk a
-// dependent step of about kFusedStepUs; n = the most segments whose workgroups run in one round
-// (n = 1 when the lanes alone fill the device). With n > 1 the windows come first: the intra-chunk
-// kernel over their (n - 1) * min(8, cps) chunks per lane and the window launch (about 27 us plus
-// 2.4 us per window step), and after the fused kernel the fallback's six launches return at once.
-constexpr double kFusedStepUs = 9.0;
+// The fused plan: one 8-wave workgroup per (lane, segment) and compute unit; each chunk is a
+// dependent step of about kFusedStepUs (kernel traces: 7.45 us at 64K, 6.9 us at 1M), plus one
+// step to fill the pipeline and a few microseconds for the entry and exit states. n = the most
+// segments whose workgroups run in one round (n = 1 when the lanes alone fill the device). With
+// n > 1 the windows come first: the intra-chunk kernel over their (n - 1) * min(8, cps) chunks per
+// lane and the window launch (about 6 us plus 2.4 us per window step), and after the fused kernel
+// six launches that return at once (about 4.5 us each). At 8K (32 heads, 16 chunks per segment)
+// this models 235 us against 232 us for the two-kernel path, measured 240 and 235.
+constexpr double kFusedStepUs = 7.0;
 static int64_t fused_segments(int64_t lanes, int64_t nchunks, int64_t cus, int64_t forced, double* us) {
     int64_t n = forced > 0 ? forced : (lanes < cus ? cus / lanes : 1);
     if (n > kMaxSeg) n = kMaxSeg;
     if (n > nchunks) n = nchunks;
     const int64_t cps = ceil_div(nchunks, n);
     n = ceil_div(nchunks, cps);
-    double t = (double)ceil_div(lanes * n, cus) * (double)cps * kFusedStepUs;
+    double t = (double)ceil_div(lanes * n, cus) * ((double)(cps + 1) * kFusedStepUs + 8.0);
     if (n > 1) {
         const int64_t w = kWindowChunks < cps ? kWindowChunks : cps;
-        t += intra_us(lanes * (n - 1) * w, cus) + 27.0 + 2.4 * (double)w + 6.0 * 4.5;
+        t += intra_us(lanes * (n - 1) * w, cus) + 6.0 + 2.4 * (double)w + 6.0 * 4.5;
     }
     *us = t;
     return n;

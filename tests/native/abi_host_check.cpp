@@ -172,11 +172,16 @@ static int check_chunk() {
     bad = d; bad.state_pass = 3; CHECK(fwd(&bad, nullptr, 0) == KDA_ERR_INVALID_ARG);
     bad = d; bad.state_pass = -1; CHECK(fwd(&bad, nullptr, 0) == KDA_ERR_INVALID_ARG);
     // the library's choice: the fused plan for 32 heads x 1M tokens (8 segments per lane, one
-    // workgroup per compute unit), two kernels for 32 heads x 8K tokens
+    // workgroup per compute unit) and 4 x 32 lanes x 64K tokens (2 segments), two kernels for 32
+    // heads x 8K tokens
     kda::Geometry g1m{32, 16384, 32 * 16384, 128, 128, KDA_BF16, 0, 0, 32, 256};
     g1m.fused_ok = true;
     const kda::Plan p1m = kda::make_plan(g1m);
     CHECK(p1m.fused && p1m.nseg == 8 && p1m.chunks_per_seg == 2048);
+    kda::Geometry g64k{128, 1024, 128 * 1024, 128, 128, KDA_BF16, 0, 0, 128, 256};   // B = 4, H = 32, T = 65536
+    g64k.fused_ok = true;
+    const kda::Plan p64k = kda::make_plan(g64k);
+    CHECK(p64k.fused && p64k.nseg == 2);
     kda::Geometry g8k{32, 128, 32 * 128, 128, 128, KDA_BF16, 0, 0, 32, 256};
     g8k.fused_ok = true;
     CHECK(!kda::make_plan(g8k).fused);
