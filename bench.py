@@ -1,8 +1,8 @@
 """Benchmark of the KDA hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload prefill_1m|prefill_8k|prefill_64k|fp32_small]
-                    [--decode-steps 1000] [--no-cpu-baseline] [--no-packed] [--no-backward] [--no-sub]
-                    [--copy-probe-mib M]
+                    [--segments N] [--state-pass 0|1|2] [--decode-steps 1000] [--no-cpu-baseline] [--no-packed]
+                    [--no-backward] [--no-sub] [--copy-probe-mib M]
 
 One step = one kda_chunk_fwd call over the named prefill workload (default: the long-context
 workload, bf16, B=1, H=32, T=1,048,576, d=128, C=64, S0=0, split across the GPU by the library's
