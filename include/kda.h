@@ -98,7 +98,12 @@ typedef struct kda_decode_desc {
  *    then one 4-byte flag per (lane, segment). The library first runs each segment boundary's
  *    last 8 chunks from a zero state; where the decay drives that window's M to exactly zero
  *    in fp32, the window's S~ is the boundary's exact state and the lane needs neither the
- *    full-length affine pairs nor the scan.
+ *    full-length affine pairs nor the scan;
+ *  - with the fused kernel (state_pass, or the library's choice for long lanes) and more than one
+ *    segment, the window launch's own flags (4 bytes per lane and segment) and the list of lanes
+ *    with an inexact window (4 bytes per lane, then the count; 16-byte multiple). The fused kernel
+ *    keeps every chunk's factors in on-chip memory; the records are still reserved, for the lanes
+ *    that fall back to the two-kernel path, and only the windows' chunks are written otherwise.
  * The fp32 path needs no workspace.
  */
 size_t kda_chunk_fwd_workspace_bytes(const kda_chunk_desc* desc);
