@@ -42,7 +42,7 @@ class VarlenDesc(ctypes.Structure):
     _fields_ = [("N", ctypes.c_int64), ("H", ctypes.c_int64), ("T", ctypes.c_int64), ("max_len", ctypes.c_int64),
                 ("dk", ctypes.c_int64), ("dv", ctypes.c_int64), ("chunk", ctypes.c_int32), ("in_dtype", ctypes.c_int32),
                 ("out_dtype", ctypes.c_int32), ("segments", ctypes.c_int32), ("ckpt_every", ctypes.c_int32),
-                ("packed", ctypes.c_int32)]
+                ("packed", ctypes.c_int32), ("state_pass", ctypes.c_int32)]
 
 
 class Gating(ctypes.Structure):
@@ -267,20 +267,20 @@ def _gating(dev, H, dv, dtype, lead, z, A_log, g_min, gate, norm_weight, eps):
                   _ptr(norm_weight) if gate is not None else None)
 
 
-def _varlen_desc(N, H, T, max_len, dk, dv, out_dtype, segments, ckpt_every, packed):
+def _varlen_desc(N, H, T, max_len, dk, dv, out_dtype, segments, ckpt_every, packed, state_pass=STATE_PASS_AUTO):
     return VarlenDesc(N, H, T, max_len, dk, dv, 64, KDA_BF16, _DTYPES[out_dtype], int(segments), int(ckpt_every),
-                      int(packed))
+                      int(packed), int(state_pass))
 
 
 def varlen_workspace_bytes(N, H, T, max_len, dk, dv, *, segments=0, ckpt_every=0, packed=True,
-                           out_dtype=torch.bfloat16):
-    d = _varlen_desc(N, H, T, max_len, dk, dv, out_dtype, segments, ckpt_every, packed)
+                           out_dtype=torch.bfloat16, state_pass=STATE_PASS_AUTO):
+    d = _varlen_desc(N, H, T, max_len, dk, dv, out_dtype, segments, ckpt_every, packed, state_pass)
     return int(library().kda_chunk_fwd_varlen_workspace_bytes(ctypes.byref(d)))
 
 
 def chunk_fwd_varlen(q, k, v, log_alpha, beta, cu_seqlens=None, S0=None, *, max_len=None, N=None, ckpt_every=0,
-                     out_dtype=None, segments=0, o=None, S_T=None, S_ckpt=None, ckpt_offsets=None,
-                     z=None, A_log=None, g_min=-5.0, gate=None, norm_weight=None, eps=1e-6,
+                     out_dtype=None, segments=0, state_pass=STATE_PASS_AUTO, o=None, S_T=None, S_ckpt=None,
+                     ckpt_offsets=None, z=None, A_log=None, g_min=-5.0, gate=None, norm_weight=None, eps=1e-6,
                      store_state=True, workspace=None, stream=None):
     """KDA prefill over a batch of sequences with state checkpoints, through ``kda_chunk_fwd_varlen``.
 
@@ -297,6 +297,7 @@ def chunk_fwd_varlen(q, k, v, log_alpha, beta, cu_seqlens=None, S0=None, *, max_
     Fused prologue: with ``z`` (shape of log_alpha, which may then be None) and ``A_log`` [H] fp32,
     the log decay is g_min * sigmoid(exp(A_log[h]) * z). Fused epilogue: with ``gate`` (shape of
     v), o receives sigmoid(gate) * norm_weight * o / sqrt(mean(o^2) + eps).
+    ``segments`` and ``state_pass`` are kda_varlen_desc's (0: the library's choice).
     Caller-supplied outputs and workspace are checked like the inputs; the ones the binding
     allocates are allocated on ``stream``.
     """
@@ -345,7 +346,7 @@ def chunk_fwd_varlen(q, k, v, log_alpha, beta, cu_seqlens=None, S0=None, *, max_
             _check_tensor("ckpt_offsets", ckpt_offsets, dev, torch.int32, (N + 1,))
     _check_workspace(workspace, dev)
     _check_device("chunk_fwd_varlen", dev)
-    desc = _varlen_desc(N, H, T, max_len, dk, dv, out_dtype, segments, ckpt_every, packed)
+    desc = _varlen_desc(N, H, T, max_len, dk, dv, out_dtype, segments, ckpt_every, packed, state_pass)
     lib = library()
     need = int(lib.kda_chunk_fwd_varlen_workspace_bytes(ctypes.byref(desc)))
     with _alloc_on(stream):

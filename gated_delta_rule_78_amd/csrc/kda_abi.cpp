@@ -99,13 +99,14 @@ kda::Gating to_gating(const kda_gating* g) {
 kda_status check_varlen_desc(const kda_varlen_desc* d) {
     if (!d) return KDA_ERR_INVALID_ARG;
     if (d->N < 1 || d->H < 1 || d->T < 0 || d->max_len < 0 || d->dk < 1 || d->dv < 1 || d->segments < 0 ||
-        d->ckpt_every < 0 || (d->packed != 0 && d->packed != 1))
+        d->ckpt_every < 0 || (d->packed != 0 && d->packed != 1) || d->state_pass < 0 || d->state_pass > 2)
         return KDA_ERR_INVALID_ARG;
     if (d->ckpt_every % kChunk != 0) return KDA_ERR_INVALID_ARG;
     if (!valid_dtype(d->in_dtype) || !valid_dtype(d->out_dtype)) return KDA_ERR_INVALID_ARG;
     if (d->chunk != kChunk) return KDA_ERR_UNSUPPORTED;
     if ((d->dk != 64 && d->dk != 128) || (d->dv != 64 && d->dv != 128)) return KDA_ERR_UNSUPPORTED;
     if (d->in_dtype != KDA_BF16) return KDA_ERR_UNSUPPORTED;
+    if (d->state_pass == 2 && (d->packed || d->dk != 128 || d->dv != 128)) return KDA_ERR_UNSUPPORTED;
     // the state pass addresses one sequence's output rows with 32-bit offsets; slot rows are int32
     const int64_t dmax = d->dk > d->dv ? d->dk : d->dv;
     const int64_t longest = d->packed ? d->max_len : d->T;
@@ -124,8 +125,11 @@ kda_status check_varlen_desc(const kda_varlen_desc* d) {
 Geometry varlen_geometry(const kda_varlen_desc* d, int64_t cus) {
     if (!d->packed) {
         const int64_t nchunks = ceil_div(d->T, kChunk);
-        return Geometry{d->N * d->H, nchunks, d->N * d->H * nchunks, d->dk, d->dv, d->in_dtype, d->segments, 0,
-                        d->N * d->H, cus};
+        Geometry g{d->N * d->H, nchunks, d->N * d->H * nchunks, d->dk, d->dv, d->in_dtype, d->segments, 0,
+                   d->N * d->H, cus};
+        g.state_pass = d->state_pass;
+        g.fused_ok = d->dk == 128 && d->dv == 128;
+        return g;
     }
     const int64_t max_len = d->max_len < d->T ? d->max_len : d->T;
     const int64_t max_chunks = ceil_div(max_len, kChunk);

@@ -26,7 +26,9 @@
 // order, so the outputs are the same bit for bit.
 //
 // Entry states: S0 for segment 0, else the window's S~ (ChunkLaunch::ws_entry, from a kPassWindow
-// launch); a lane with an inexact window (ws_flag) is left to the two-kernel fallback.
+// launch); a lane with an inexact window (ws_flag) is left to the two-kernel fallback. Lanes of
+// an equal-length batch only; state checkpoints, the fused decay prologue (producer) and the gated
+// RMSNorm epilogue (consumer) as in the two-kernel path.
 #include "kda_intra_chunk.h"
 #include "kda_step.h"
 
@@ -50,6 +52,8 @@ struct __align__(16) FusedSmem {
     IntraSmem<DK, DV> ip;                              // the producer's stages
     unsigned char rec[R::BYTES];                       // the record of the chunk in flight
     unsigned char vst3[VSTAGE];                        // the fourth consumer wave's V stage
+    float ssq[4][kC];                                  // gated epilogue: per-wave sums of o^2 per token
+    float norm_w[DV];                                  // gated epilogue: the RMSNorm weight
     __device__ __forceinline__ bf16_t* vstage(int cw) {
         return reinterpret_cast<bf16_t*>(cw < 3 ? rec + R::U * 1024 + cw * VSTAGE : vst3);
     }
@@ -58,21 +62,40 @@ struct __align__(16) FusedSmem {
 // Barrier over the whole workgroup that orders LDS accesses only (global loads stay in flight).
 __device__ __forceinline__ void epoch_barrier() { lds_barrier(); }
 
-template <int DK, int DV>
-__device__ __forceinline__ void producer(const ChunkLaunch& p, FusedSmem<DK, DV>& sm, int64_t row_base, int64_t cb,
+// A consumer wave's columns col0 .. col0 + 16 NT - 1 of a dk x dv fp32 state at dst, through a
+// buffer descriptor: the lane's offset in a register, each (nt, M, r) offset a scalar constant
+// (64-bit addresses per element would hold dozens of registers in the chunk loop).
+template <int DK, int DV, int NT>
+__device__ __forceinline__ void store_state(float* dst, const f32x4 (&S)[NT][DK / 16], int col0, int lq, int l16) {
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(dst, (uint32_t)(DK * DV * 4));
+    const int lane_off = (4 * lq * DV + col0 + l16) * 4;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int M = 0; M < DK / 16; ++M)
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr)
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(S[nt][M][rr]), r, lane_off,
+                                                      ((16 * M + rr) * DV + 16 * nt) * 4, 0);
+}
+
+template <int DK, int DV, bool ZPRO>
+__device__ __forceinline__ void producer(const ChunkLaunch& p, FusedSmem<DK, DV>& sm, int64_t lane, int64_t cb,
                                          int64_t ce) {
-    ChunkWave<DK, DV, false, true> cw(sm.ip);
+    ChunkWave<DK, DV, ZPRO, true> cw(sm.ip);
     unsigned char* rec = sm.rec;
     const int64_t T = p.T;
+    const int64_t row_base = lane * T;
+    auto rows_of = [&](int64_t c) -> uint32_t { return c < ce ? (uint32_t)(T - c * kC < kC ? T - c * kC : kC) : 0u; };
     auto load = [&](int64_t c) {
-        uint32_t n = 0;
-        if (c < ce) n = (uint32_t)(T - c * kC < kC ? T - c * kC : kC);
-        cw.load(p.q, p.k, p.la, p.v, p.beta, row_base + (c < ce ? c : 0) * kC, n);
+        cw.load(p.q, p.k, ZPRO ? p.gt.z : p.la, p.v, p.beta, row_base + (c < ce ? c : 0) * kC, rows_of(c));
     };
+    // the fused decay prologue: exp(A_h) of the lane's head (lane = b * H + h)
+    const float eA = ZPRO ? __builtin_amdgcn_exp2f(p.gt.A_log[lane % p.map.H] * kLog2e) : 0.f;
     load(cb);
     cw.pin_inputs();
     for (int64_t c = cb; c < ce; ++c) {
-        cw.template decay<true>(rec, 0.f, 0.f, kC);
+        cw.template decay<true>(rec, eA, ZPRO ? p.gt.g_min : 0.f, rows_of(c));
         epoch_barrier();   // 1
         cw.publish(rec);
         load(c + 1);
@@ -88,7 +111,7 @@ __device__ __forceinline__ void producer(const ChunkLaunch& p, FusedSmem<DK, DV>
     epoch_barrier();
 }
 
-template <typename TOut, int DK, int DV>
+template <typename TOut, int DK, int DV, bool GATED, bool CKPT>
 __device__ __forceinline__ void consumer(const ChunkLaunch& p, FusedSmem<DK, DV>& sm, int64_t lane, int seg,
                                          int64_t cb, int64_t ce) {
     constexpr int NT = DV / 64;
@@ -120,30 +143,134 @@ __device__ __forceinline__ void consumer(const ChunkLaunch& p, FusedSmem<DK, DV>
                 S[nt][M][r] = entry ? entry[(16 * M + 4 * lq + r) * DVl + col0 + 16 * nt + l16] : 0.f;
     const __amdgpu_buffer_rsrc_t ro = make_rsrc((const TOut*)p.o + lane * T * DVl, (uint32_t)(T * DVl * sizeof(TOut)));
     constexpr bool PAIRED = sizeof(TOut) == 2 && NT % 2 == 0;
+    constexpr int NP = NT / 2 > 0 ? NT / 2 : 1;
+
+    // State checkpoints of an equal-length batch: sequence s = lane / H has its checkpoints at
+    // rows s * ck_per_lane + j - 1 of H states each (ChunkLaunch::ckpt).
+    int64_t ck_base = 0, ck_stride = 1;
+    if (CKPT) {
+        ck_base = uniform64((lane / p.map.H) * p.ck_per_lane * p.map.H + lane % p.map.H);
+        ck_stride = p.map.H;
+    }
+    // Gated epilogue: the gate rows of chunk c load after the V of chunk c is staged, wait in
+    // registers through the U solve and then sit in the wave's V stage (free until the next V)
+    // until chunk c's o rows are stored, in the layout of those stores; per-token sums of o^2 meet
+    // across the four consumer waves in LDS.
+    const __amdgpu_buffer_rsrc_t rgt =
+        make_rsrc(GATED ? (const bf16_t*)p.gt.gate + lane * T * DVl : nullptr, GATED ? (uint32_t)(T * DVl * 2) : 0u);
+    uint2 gpend[NT][4];
+    uint4 gq[NP][4];
+    if (GATED) {   // the weights (ones when absent) in LDS: read at each use, held in no register
+        for (int i = l; i < 16 * NT; i += 64) sm.norm_w[col0 + i] = p.gt.norm_w ? p.gt.norm_w[col0 + i] : 1.f;
+        wave_lds_sync();
+    }
+    auto weights = [&](int c0) -> f32x4 { return *reinterpret_cast<const f32x4*>(&sm.norm_w[c0]); };
+    unsigned char* gstage = reinterpret_cast<unsigned char*>(sm.vstage(w)) + l * 16;   // lane-private
+    auto load_gate = [&](int64_t c) {
+        if (!GATED) return;
+        const uint32_t r0 = (uint32_t)(c * kC);
+#pragma unroll
+        for (int I = 0; I < 4; ++I) {
+            if constexpr (PAIRED) {
+#pragma unroll
+                for (int np = 0; np < NP; ++np)
+                    gq[np][I] = buf_load16(rgt, ((r0 + 16 * I + l16) * (uint32_t)DV + col0 + 32 * np + pair_col(lq)) * 2u);
+            } else {
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt)
+                    gpend[nt][I] = buf_load8(rgt, ((r0 + 16 * I + l16) * (uint32_t)DV + col0 + 16 * nt + 4 * lq) * 2u);
+            }
+        }
+    };
+    // (4 KiB of lane-private 16-byte slots in the 5 KiB stage)
+    auto gate_to_stage = [&]() {
+#pragma unroll
+        for (int I = 0; I < 4; ++I) {
+            if constexpr (PAIRED) {
+#pragma unroll
+                for (int np = 0; np < NP; ++np) *reinterpret_cast<uint4*>(gstage + (I * NP + np) * 1024) = gq[np][I];
+            } else {
+#pragma unroll
+                for (int nt = 0; nt < NT; nt += 2)
+                    *reinterpret_cast<uint4*>(gstage + (I * NP + nt / 2) * 1024) =
+                        make_uint4(gpend[nt][I].x, gpend[nt][I].y, gpend[nt + 1][I].x, gpend[nt + 1][I].y);
+            }
+        }
+    };
+    auto gate_from_stage = [&]() {
+#pragma unroll
+        for (int I = 0; I < 4; ++I) {
+            if constexpr (PAIRED) {
+#pragma unroll
+                for (int np = 0; np < NP; ++np) gq[np][I] = *reinterpret_cast<const uint4*>(gstage + (I * NP + np) * 1024);
+            } else {
+#pragma unroll
+                for (int nt = 0; nt < NT; nt += 2) {
+                    const uint4 g = *reinterpret_cast<const uint4*>(gstage + (I * NP + nt / 2) * 1024);
+                    gpend[nt][I] = make_uint2(g.x, g.y);
+                    gpend[nt + 1][I] = make_uint2(g.z, g.w);
+                }
+            }
+        }
+    };
+    static_assert(!GATED || NT % 2 == 0, "gate slots hold two tiles");
+    const float inv_dv = 1.f / (float)DV;
+
     f32x4 O[NT][4];
     i16x4 U[NT][4];   // U of the chunk the next state step takes
     for (int64_t c = cb; c <= ce; ++c) {
         const bool prev = c > cb;   // chunk c - 1's record is in the buffer
         const bool cur = c < ce;    // chunk c is being built
-        if (prev)
+        if (prev) {
             chunk_step<TOut, DK, DV, NT, 0, NT, true>(sm.rec, S, col0, DV / 16 - col0 / 16, O, false, ro, nullptr, w, U);
+            if (CKPT && c % p.ck_chunks == 0 && c * kC <= T) {   // S is the state after chunk c - 1
+                const int64_t idx = ck_base + (c / p.ck_chunks - 1) * ck_stride;
+                if (idx < p.ck_cap) store_state<DK, DV, NT>(p.ckpt + idx * DK * DVl, S, col0, lq, l16);
+            }
+            if (GATED) {   // this wave's part of each token's sum of o^2
+#pragma unroll
+                for (int I = 0; I < 4; ++I) {
+                    float ss = 0.f;
+#pragma unroll
+                    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) ss += O[nt][I][r] * O[nt][I][r];
+                    ss += __shfl_xor(ss, 16);
+                    ss += __shfl_xor(ss, 32);
+                    if (lq == 0) sm.ssq[w][16 * I + l16] = ss;
+                }
+            }
+        }
         epoch_barrier();   // 1
         if (prev) {
+            if (GATED) gate_from_stage();
 #pragma unroll
             for (int I = 0; I < 4; ++I) {
                 const uint32_t row = (uint32_t)((c - 1) * kC + 16 * I + l16);
+                float rstd = 0.f;
+                if (GATED)
+                    rstd = __builtin_amdgcn_rsqf((sm.ssq[0][16 * I + l16] + sm.ssq[1][16 * I + l16] + sm.ssq[2][16 * I + l16] +
+                                                  sm.ssq[3][16 * I + l16]) * inv_dv + p.gt.eps);
                 if constexpr (PAIRED) {
 #pragma unroll
-                    for (int np = 0; np < NT / 2; ++np) {
+                    for (int np = 0; np < NP; ++np) {
                         f32x4 a, b;
                         swap_pair(O[2 * np][I], O[2 * np + 1][I], a, b);
+                        if (GATED) {
+                            const int wc = col0 + 32 * np + (int)pair_col(lq);
+                            a = gated_norm(a, make_uint2(gq[np][I].x, gq[np][I].y), weights(wc), rstd);
+                            b = gated_norm(b, make_uint2(gq[np][I].z, gq[np][I].w), weights(wc + 4), rstd);
+                        }
                         store_bf16x8(ro, row * (uint32_t)DV + (uint32_t)(col0 + 32 * np) + pair_col(lq), a, b);
                     }
                 } else {
 #pragma unroll
-                    for (int nt = 0; nt < NT; ++nt)
-                        store_out(ro, (row * (uint32_t)DV + col0 + 16 * nt + 4 * lq) * (uint32_t)sizeof(TOut), O[nt][I],
+                    for (int nt = 0; nt < NT; ++nt) {
+                        const f32x4 y = GATED ? gated_norm(O[nt][I], gpend[nt][I], weights(col0 + 16 * nt + 4 * lq), rstd)
+                                              : O[nt][I];
+                        store_out(ro, (row * (uint32_t)DV + col0 + 16 * nt + 4 * lq) * (uint32_t)sizeof(TOut), y,
                                   (TOut*)nullptr);
+                    }
                 }
             }
         }
@@ -152,23 +279,19 @@ __device__ __forceinline__ void consumer(const ChunkLaunch& p, FusedSmem<DK, DV>
             vw.stage();
             load(c + 1);
             vw.diag_inverse();
+            load_gate(c);
         }
         epoch_barrier();   // 2
-        if (cur) vw.solve(U);
+        if (cur) {
+            vw.solve(U);
+            if (GATED) gate_to_stage();   // (the stage's V reads are done)
+        }
         epoch_barrier();   // 3
     }
-    if (seg == p.nseg - 1 && p.S_T) {
-        float* dst = p.S_T + lane * DK * DVl;
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-            for (int M = 0; M < NM; ++M)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) dst[(16 * M + 4 * lq + r) * DVl + col0 + 16 * nt + l16] = S[nt][M][r];
-    }
+    if (seg == p.nseg - 1 && p.S_T) store_state<DK, DV, NT>(p.S_T + lane * DK * DVl, S, col0, lq, l16);
 }
 
-template <typename TOut, int DK, int DV>
+template <typename TOut, int DK, int DV, bool ZPRO, bool GATED, bool CKPT>
 __global__ __launch_bounds__(kThreads, 1) void fused_kernel(ChunkLaunch p) {
     __shared__ FusedSmem<DK, DV> sm;
     const int64_t lane = uniform64(blockIdx.x / p.nseg);
@@ -182,9 +305,9 @@ __global__ __launch_bounds__(kThreads, 1) void fused_kernel(ChunkLaunch p) {
     ce = uniform64(ce);
     // the role split is wave-uniform (a scalar branch), so each wave runs only its own loop
     if (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) < 4)
-        producer<DK, DV>(p, sm, lane * p.T, cb, ce);
+        producer<DK, DV, ZPRO>(p, sm, lane, cb, ce);
     else
-        consumer<TOut, DK, DV>(p, sm, lane, seg, cb, ce);
+        consumer<TOut, DK, DV, GATED, CKPT>(p, sm, lane, seg, cb, ce);
 }
 
 // One workgroup: the lanes whose flags are not all 1, in increasing order (a block-wide prefix
@@ -213,13 +336,30 @@ __global__ __launch_bounds__(1024, 1) void fallback_lanes_kernel(const int32_t* 
 
 }  // namespace
 
+template <typename TOut, bool ZPRO, bool GATED>
+void launch_g(const ChunkLaunch& a, int64_t blocks, hipStream_t st) {
+    if (a.ckpt)
+        hipLaunchKernelGGL((fused_kernel<TOut, 128, 128, ZPRO, GATED, true>), dim3((unsigned)blocks), dim3(kThreads), 0, st, a);
+    else
+        hipLaunchKernelGGL((fused_kernel<TOut, 128, 128, ZPRO, GATED, false>), dim3((unsigned)blocks), dim3(kThreads), 0, st, a);
+}
+
+template <typename TOut>
+void launch_o(const ChunkLaunch& a, int64_t blocks, hipStream_t st) {
+    if (a.gt.z) {
+        if (a.gt.gate) launch_g<TOut, true, true>(a, blocks, st);
+        else launch_g<TOut, true, false>(a, blocks, st);
+    } else {
+        if (a.gt.gate) launch_g<TOut, false, true>(a, blocks, st);
+        else launch_g<TOut, false, false>(a, blocks, st);
+    }
+}
+
 hipError_t launch_fused(const ChunkLaunch& a, hipStream_t st) {
     const int64_t blocks = a.lanes * (int64_t)a.nseg;
     if (blocks <= 0) return hipSuccess;
-    if (a.out_bf16)
-        hipLaunchKernelGGL((fused_kernel<bf16_t, 128, 128>), dim3((unsigned)blocks), dim3(kThreads), 0, st, a);
-    else
-        hipLaunchKernelGGL((fused_kernel<float, 128, 128>), dim3((unsigned)blocks), dim3(kThreads), 0, st, a);
+    if (a.out_bf16) launch_o<bf16_t>(a, blocks, st);
+    else launch_o<float>(a, blocks, st);
     return hipGetLastError();
 }
 

@@ -47,17 +47,6 @@ struct __align__(16) InterSmem {
     int nonzero[4];         // WINDOW: per wave, whether its share of M has a nonzero entry
 };
 
-// Fused epilogue of one output tile: y = sigmoid(gate) * w * o * rstd for 4 columns of a token.
-__device__ __forceinline__ f32x4 gated_norm(f32x4 o, uint2 g, f32x4 w, float rstd) {
-    const float gv[4] = {__uint_as_float(g.x << 16), __uint_as_float(g.x & 0xffff0000u),
-                         __uint_as_float(g.y << 16), __uint_as_float(g.y & 0xffff0000u)};
-    f32x4 y;
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-        y[r] = o[r] * rstd * w[r] * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-gv[r] * kLog2e));
-    return y;
-}
-
 // WINDOW ahead of FINISH segment seg > 0 of a lane: chunks [wb, we) with we = the segment's first
 // chunk and wb = max(0, we - win_chunks), from S~ = 0 (S0 when wb = 0) on this wave's FINISH columns
 // and M = I on its share of M's columns (16 MT consecutive ones). Stores the lane's flag for the

@@ -156,8 +156,9 @@ hipError_t launch_intra(const IntraArgs& a, hipStream_t st);
 int stream_device(hipStream_t st);
 int compute_units(int dev);
 hipError_t launch_inter(const ChunkLaunch& a, hipStream_t st);
-// The fused single-pass prefill (bf16, dk = dv = 128, fixed length, no checkpoints or gating): one
-// workgroup per (lane, segment) builds each chunk's record in LDS and runs the state step on it;
+// The fused single-pass prefill (bf16, dk = dv = 128, lanes of equal length; checkpoints and the
+// fused gating as ChunkLaunch says): one workgroup per (lane, segment) builds each chunk's record
+// in LDS and runs the state step on it;
 // segments s > 0 start from ws_entry (a kPassWindow launch), and lanes with an inexact window
 // (ws_flag) are left alone.
 hipError_t launch_fused(const ChunkLaunch& a, hipStream_t st);

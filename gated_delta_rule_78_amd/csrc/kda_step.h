@@ -45,6 +45,17 @@ __device__ __forceinline__ void store_bf16x8(__amdgpu_buffer_rsrc_t r, uint32_t 
 }
 
 
+// Fused epilogue of one output tile: y = sigmoid(gate) * w * o * rstd for 4 columns of a token.
+__device__ __forceinline__ f32x4 gated_norm(f32x4 o, uint2 g, f32x4 w, float rstd) {
+    const float gv[4] = {__uint_as_float(g.x << 16), __uint_as_float(g.x & 0xffff0000u),
+                         __uint_as_float(g.y << 16), __uint_as_float(g.y & 0xffff0000u)};
+    f32x4 y;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+        y[r] = o[r] * rstd * w[r] * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-gv[r] * kLog2e));
+    return y;
+}
+
 // Copy this wave's share (blocks w, w + 4, ...) of the blocks of one chunk record that a role
 // reads (FINISH: all; SUMMARY: all but Q~ and A_qk) into an LDS buffer: one direct-to-LDS buffer
 // load per 1 KiB block; the descriptor covers the chunk's record, offsets stay scalar. Every wave

@@ -233,6 +233,19 @@ static int check_varlen() {
     CHECK(call(&d, P(8 * GB), P(9 * GB), P(10 * GB), &g, P(11 * GB), need, nullptr) == KDA_OK && g_intra == 1);
     g.g_min = 0.f;
     CHECK(call(&d, P(8 * GB), P(9 * GB), P(10 * GB), &g, P(11 * GB), need, nullptr) == KDA_ERR_INVALID_ARG);
+    g.g_min = -5.f;
+    // the fused kernel takes equal-length batches (checkpoints and gating included), not packed ones
+    kda_varlen_desc f = d;
+    f.state_pass = 2;
+    CHECK(call(&f, P(8 * GB), P(9 * GB), P(10 * GB), nullptr, P(11 * GB), need) == KDA_ERR_UNSUPPORTED);
+    f.packed = 0; f.segments = 2;
+    const size_t needf = kda_chunk_fwd_varlen_workspace_bytes(&f);
+    reset();
+    CHECK(call(&f, nullptr, P(9 * GB), P(10 * GB), &g, P(11 * GB), needf, nullptr) == KDA_OK);
+    CHECK(g_fused == 1 && g_fused_last.ckpt == (float*)P(9 * GB) && g_fused_last.ck_chunks == 2 &&
+          g_fused_last.gt.z == P(12 * GB) && g_fused_last.gt.gate == P(14 * GB) && g_fused_last.nseg == 2);
+    f.state_pass = 3;
+    CHECK(call(&f, nullptr, P(9 * GB), P(10 * GB), &g, P(11 * GB), needf, nullptr) == KDA_ERR_INVALID_ARG);
     return 0;
 }
 

@@ -1,7 +1,8 @@
 """GPU parity of the fused prefill (kda_chunk_desc::state_pass = 2): one kernel builds every chunk's
 factors in LDS and runs the state step on them (section 2.2 chunk equations of the Kimi K3 reading
 notes), its segments starting from the window states of section 2.5's sequence split, and lanes
-with an inexact window falling back to the two-kernel path within the same call. Each case is
+with an inexact window falling back to the two-kernel path within the same call; with state
+checkpoints and the fused gating through kda_chunk_fwd_varlen (equal lengths). Each case is
 checked against the fp64 oracle; where the two paths split a lane the same way, the fused output
 must also equal the two-kernel output bit for bit (the same per-chunk arithmetic in the same
 order: only where the factors live differs)."""
@@ -11,7 +12,9 @@ import torch
 
 import gated_delta_rule_78_amd as kda
 from gated_delta_rule_78_amd import synth
-from tests.parity import assert_close, host32, oracle_prefill, say
+from oracle import gating, native
+from tests.parity import TOL_S, assert_close, host32, oracle_prefill, rel_l2_per_lane, say
+from tests.test_gpu_gating import EPS, G_MIN, check_gated
 
 pytestmark = pytest.mark.gpu
 DEV = torch.device("cuda:0") if torch.cuda.is_available() else None
@@ -145,3 +148,70 @@ def test_fused_refused_for_dk64():
     q, k, v, la, beta, S0 = synth.prefill_inputs(1, 1, 128, 64, 128, BF16, device=DEV, seed_base=9990)
     with pytest.raises(kda.KDAError):
         kda.chunk_fwd(q, k, v, la, beta, S0, state_pass=FUSED)
+
+
+def _equal_length_ckpt_ref(q, k, v, la, beta, S0, E):
+    N, H, T, d = q.shape
+    f = lambda t: host32(t).reshape((N * H,) + tuple(t.shape[2:]))
+    o_ref, S_ref, ck_ref = native.kda_fwd(f(q), f(k), f(v), f(la), f(beta), None if S0 is None else f(S0), ckpt_every=E)
+    n = T // E
+    return o_ref, S_ref, ck_ref.reshape(N, H, n, d, d).transpose(0, 2, 1, 3, 4).reshape(N * n, H, d, d)
+
+
+@pytest.mark.parametrize("E", [64, 512])
+def test_fused_checkpoints_equal_lengths(E):
+    """State checkpoints every E tokens (kda_chunk_fwd_varlen, equal lengths) from the fused kernel,
+    one head at slow decay falling back: bit-identical to the two-kernel path, and against the
+    oracle's prefix states."""
+    N, H, T = 2, 3, 64 * 40 + 17
+    say("fused checkpoints: N=%d H=%d T=%d E=%d segments=4" % (N, H, T, E))
+    q, k, v, la, beta, S0 = inputs(N, H, T, 9600 + E)
+    la[:, 2] = inputs(N, H, T, 9610 + E, la_range=SLOW)[3][:, 2]
+    outs = {}
+    for sp in (FUSED, TWO):
+        outs[sp] = kda.chunk_fwd_varlen(q, k, v, la, beta, None, S0, ckpt_every=E, segments=4, state_pass=sp)
+    torch.cuda.synchronize()
+    for a, b in zip(outs[FUSED], outs[TWO]):
+        assert torch.equal(a, b), "fused and two-kernel checkpoint calls differ"
+    o, S_T, ck, offs = outs[FUSED]
+    o_ref, S_ref, ck_ref = _equal_length_ckpt_ref(q, k, v, la, beta, S0, E)
+    assert_close("fused checkpoints E=%d" % E, BF16, host32(o).reshape(N * H, T, 128), o_ref,
+                 host32(S_T).reshape(N * H, 128, 128), S_ref)
+    n = T // E
+    assert np.array_equal(offs.cpu().numpy(), [s * n for s in range(N + 1)])
+    es = rel_l2_per_lane(host32(ck[:N * n]).reshape(N * n * H, -1), ck_ref.reshape(N * n * H, -1))
+    say("fused checkpoints E=%d: %d x %d states, relL2 = %.3e" % (E, N * n, H, es))
+    assert es <= TOL_S[BF16]
+
+
+@pytest.mark.parametrize("z_on,gate_on,odt", [(True, False, BF16), (False, True, BF16), (True, True, BF16),
+                                               (True, True, torch.float32)])
+def test_fused_gating_equal_lengths(z_on, gate_on, odt):
+    """The fused decay prologue and gated RMSNorm epilogue in the fused kernel: bit-identical to
+    the two-kernel path (which the gating tests hold to the oracle), and the gated output against
+    the oracle's epilogue of the oracle's core output."""
+    N, H, T, E = 1, 4, 64 * 24 + 5, 512
+    say("fused gating: z=%s gate=%s out=%s N=%d H=%d T=%d" % (z_on, gate_on, odt, N, H, T))
+    q, k, v, la, beta, S0 = inputs(N, H, T, 9700 + 2 * z_on + gate_on)
+    z, A_log, gate, w = synth.gating_inputs((N, H, T), H, 128, 128, BF16, device=DEV, seed=9720 + 2 * z_on + gate_on)
+    kw = dict(ckpt_every=E, segments=3, out_dtype=odt)
+    if z_on:
+        kw.update(z=z, A_log=A_log, g_min=G_MIN)
+    if gate_on:
+        kw.update(gate=gate, norm_weight=w, eps=EPS)
+    outs = {sp: kda.chunk_fwd_varlen(q, k, v, None if z_on else la, beta, None, S0, state_pass=sp, **kw)
+            for sp in (FUSED, TWO)}
+    torch.cuda.synchronize()
+    for a, b in zip(outs[FUSED], outs[TWO]):
+        assert torch.equal(a, b), "fused and two-kernel gated calls differ"
+    o, S_T = outs[FUSED][0], outs[FUSED][1]
+    g = gating.log_decay(host32(z), host32(A_log)[None, :, None, None], G_MIN).astype(np.float32) if z_on else host32(la)
+    f = lambda t: np.asarray(t).reshape((N * H,) + tuple(np.asarray(t).shape[2:]))
+    o_ref, S_ref = native.kda_fwd(f(host32(q)), f(host32(k)), f(host32(v)), f(g), f(host32(beta)), f(host32(S0)))
+    if gate_on:
+        check_gated("fused gating", o.reshape(N * H, T, 128), o_ref, gate.reshape(N * H, T, 128), w, odt)
+        es = rel_l2_per_lane(host32(S_T).reshape(N * H, -1), S_ref.reshape(N * H, -1))
+        assert es <= TOL_S[BF16]
+    else:
+        assert_close("fused prologue", BF16, host32(o).reshape(N * H, T, 128), o_ref, host32(S_T).reshape(N * H, 128, 128),
+                     S_ref)
