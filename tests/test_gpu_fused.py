@@ -215,3 +215,12 @@ def test_fused_gating_equal_lengths(z_on, gate_on, odt):
     else:
         assert_close("fused prologue", BF16, host32(o).reshape(N * H, T, 128), o_ref, host32(S_T).reshape(N * H, 128, 128),
                      S_ref)
+
+
+@pytest.mark.parametrize("segments", [1, 2])
+def test_fused_more_workgroups_than_compute_units(segments):
+    """300 lanes (x segments) of workgroups, more than one per compute unit: several rounds."""
+    B, H, T = 3, 100, 64 * 6 + 11
+    say("fused many lanes: B=%d H=%d T=%d segments=%d" % (B, H, T, segments))
+    q, k, v, la, beta, S0 = inputs(B, H, T, 9950 + segments)
+    check("fused many lanes segments=%d" % segments, q, k, v, la, beta, S0, segments=segments)
