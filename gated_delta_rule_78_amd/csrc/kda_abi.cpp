@@ -106,7 +106,7 @@ kda_status check_varlen_desc(const kda_varlen_desc* d) {
     if (d->chunk != kChunk) return KDA_ERR_UNSUPPORTED;
     if ((d->dk != 64 && d->dk != 128) || (d->dv != 64 && d->dv != 128)) return KDA_ERR_UNSUPPORTED;
     if (d->in_dtype != KDA_BF16) return KDA_ERR_UNSUPPORTED;
-    if (d->state_pass == 2 && (d->packed || d->dk != 128 || d->dv != 128)) return KDA_ERR_UNSUPPORTED;
+    if (d->state_pass == 2 && (d->dk != 128 || d->dv != 128)) return KDA_ERR_UNSUPPORTED;
     // the state pass addresses one sequence's output rows with 32-bit offsets; slot rows are int32
     const int64_t dmax = d->dk > d->dv ? d->dk : d->dv;
     const int64_t longest = d->packed ? d->max_len : d->T;
@@ -138,8 +138,10 @@ Geometry varlen_geometry(const kda_varlen_desc* d, int64_t cus) {
     // split would shorten their chain, but the scan and the summary pass still run over every
     // lane (measured: 12 sequences x 32 heads, 8192 tokens, longest 2500: 0.31 ms unsplit,
     // 0.39 ms in 3 segments).
-    return Geometry{d->N * d->H, max_chunks, d->H * slots, d->dk, d->dv, d->in_dtype, d->segments, slots,
-                    d->N * d->H, cus};
+    Geometry g{d->N * d->H, max_chunks, d->H * slots, d->dk, d->dv, d->in_dtype, d->segments, slots, d->N * d->H, cus};
+    g.state_pass = d->state_pass;
+    g.fused_ok = d->dk == 128 && d->dv == 128;
+    return g;
 }
 
 // Backward workspace, in order: the forward's own workspace (records, pairs, entries), every

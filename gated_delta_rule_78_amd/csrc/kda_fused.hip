@@ -27,8 +27,8 @@
 //
 // Entry states: S0 for segment 0, else the window's S~ (ChunkLaunch::ws_entry, from a kPassWindow
 // launch); a lane with an inexact window (ws_flag) is left to the two-kernel fallback. Lanes of
-// an equal-length batch only; state checkpoints, the fused decay prologue (producer) and the gated
-// RMSNorm epilogue (consumer) as in the two-kernel path.
+// equal-length and packed batches (LaneSpan); state checkpoints, the fused decay prologue
+// (producer) and the gated RMSNorm epilogue (consumer) as in the two-kernel path.
 #include "kda_intra_chunk.h"
 #include "kda_step.h"
 
@@ -80,17 +80,17 @@ __device__ __forceinline__ void store_state(float* dst, const f32x4 (&S)[NT][DK 
 }
 
 template <int DK, int DV, bool ZPRO>
-__device__ __forceinline__ void producer(const ChunkLaunch& p, FusedSmem<DK, DV>& sm, int64_t lane, int64_t cb,
-                                         int64_t ce) {
+__device__ __forceinline__ void producer(const ChunkLaunch& p, FusedSmem<DK, DV>& sm, int64_t lane, const LaneSpan& span,
+                                         int64_t cb, int64_t ce) {
     ChunkWave<DK, DV, ZPRO, true> cw(sm.ip);
     unsigned char* rec = sm.rec;
-    const int64_t T = p.T;
-    const int64_t row_base = lane * T;
+    const int64_t T = span.len;
+    const int64_t row_base = span.row_base;
     auto rows_of = [&](int64_t c) -> uint32_t { return c < ce ? (uint32_t)(T - c * kC < kC ? T - c * kC : kC) : 0u; };
     auto load = [&](int64_t c) {
         cw.load(p.q, p.k, ZPRO ? p.gt.z : p.la, p.v, p.beta, row_base + (c < ce ? c : 0) * kC, rows_of(c));
     };
-    // the fused decay prologue: exp(A_h) of the lane's head (lane = b * H + h)
+    // the fused decay prologue: exp(A_h) of the lane's head (lane = b * H + h, or s * H + h packed)
     const float eA = ZPRO ? __builtin_amdgcn_exp2f(p.gt.A_log[lane % p.map.H] * kLog2e) : 0.f;
     load(cb);
     cw.pin_inputs();
@@ -113,7 +113,7 @@ __device__ __forceinline__ void producer(const ChunkLaunch& p, FusedSmem<DK, DV>
 
 template <typename TOut, int DK, int DV, bool GATED, bool CKPT>
 __device__ __forceinline__ void consumer(const ChunkLaunch& p, FusedSmem<DK, DV>& sm, int64_t lane, int seg,
-                                         int64_t cb, int64_t ce) {
+                                         const LaneSpan& span, int64_t cb, int64_t ce) {
     constexpr int NT = DV / 64;
     constexpr int NM = DK / 16;
     const int tid = threadIdx.x;
@@ -122,13 +122,14 @@ __device__ __forceinline__ void consumer(const ChunkLaunch& p, FusedSmem<DK, DV>
     const int l16 = l & 15;
     const int lq = l >> 4;
     const int64_t DVl = DV;
-    const int64_t T = p.T;
+    const int64_t T = span.len;
+    const int64_t row_base = span.row_base;
     const int col0 = w * 16 * NT;
     ValueWave<DK, DV> vw(sm.ip, sm.vstage(w), w);
     auto load = [&](int64_t c) {
         uint32_t n = 0;
         if (c < ce) n = (uint32_t)(T - c * kC < kC ? T - c * kC : kC);
-        vw.load(p.v, lane * T + (c < ce ? c : 0) * kC, n);
+        vw.load(p.v, row_base + (c < ce ? c : 0) * kC, n);
     };
     load(cb);
     // S[nt][M] holds rows 16M + 4lq + r, column col0 + 16nt + l16
@@ -141,23 +142,18 @@ __device__ __forceinline__ void consumer(const ChunkLaunch& p, FusedSmem<DK, DV>
 #pragma unroll
             for (int r = 0; r < 4; ++r)
                 S[nt][M][r] = entry ? entry[(16 * M + 4 * lq + r) * DVl + col0 + 16 * nt + l16] : 0.f;
-    const __amdgpu_buffer_rsrc_t ro = make_rsrc((const TOut*)p.o + lane * T * DVl, (uint32_t)(T * DVl * sizeof(TOut)));
+    const __amdgpu_buffer_rsrc_t ro = make_rsrc((const TOut*)p.o + row_base * DVl, (uint32_t)(T * DVl * sizeof(TOut)));
     constexpr bool PAIRED = sizeof(TOut) == 2 && NT % 2 == 0;
     constexpr int NP = NT / 2 > 0 ? NT / 2 : 1;
 
-    // State checkpoints of an equal-length batch: sequence s = lane / H has its checkpoints at
-    // rows s * ck_per_lane + j - 1 of H states each (ChunkLaunch::ckpt).
-    int64_t ck_base = 0, ck_stride = 1;
-    if (CKPT) {
-        ck_base = uniform64((lane / p.map.H) * p.ck_per_lane * p.map.H + lane % p.map.H);
-        ck_stride = p.map.H;
-    }
+    // State checkpoints (ChunkLaunch::ckpt): the lane's j-th at ck_base + (j - 1) ck_stride.
+    const int64_t ck_base = span.ck_base, ck_stride = span.ck_stride;
     // Gated epilogue: the gate rows of chunk c load after the V of chunk c is staged, wait in
     // registers through the U solve and then sit in the wave's V stage (free until the next V)
     // until chunk c's o rows are stored, in the layout of those stores; per-token sums of o^2 meet
     // across the four consumer waves in LDS.
     const __amdgpu_buffer_rsrc_t rgt =
-        make_rsrc(GATED ? (const bf16_t*)p.gt.gate + lane * T * DVl : nullptr, GATED ? (uint32_t)(T * DVl * 2) : 0u);
+        make_rsrc(GATED ? (const bf16_t*)p.gt.gate + row_base * DVl : nullptr, GATED ? (uint32_t)(T * DVl * 2) : 0u);
     uint2 gpend[NT][4];
     uint4 gq[NP][4];
     if (GATED) {   // the weights (ones when absent) in LDS: read at each use, held in no register
@@ -297,17 +293,21 @@ __global__ __launch_bounds__(kThreads, 1) void fused_kernel(ChunkLaunch p) {
     const int64_t lane = uniform64(blockIdx.x / p.nseg);
     const int seg = (int)uniform64(blockIdx.x % p.nseg);
     if (p.nseg > 1 && !window_split_exact(p.ws_flag + lane * p.nseg, p.nseg)) return;   // the fallback's lane
+    const LaneSpan span = lane_span(p, lane);
+    // the last segment runs to the lane's last chunk (a packed batch plans with its longest
+    // sequence); segments past a short lane's end are empty
+    const int64_t nch = (span.len + kC - 1) / kC;
     int64_t cb = (int64_t)seg * p.chunks_per_seg;
-    int64_t ce = seg == p.nseg - 1 ? p.nchunks : cb + p.chunks_per_seg;
-    if (ce > p.nchunks) ce = p.nchunks;
+    int64_t ce = seg == p.nseg - 1 ? nch : cb + p.chunks_per_seg;
+    if (ce > nch) ce = nch;
     if (cb > ce) cb = ce;
     cb = uniform64(cb);
     ce = uniform64(ce);
     // the role split is wave-uniform (a scalar branch), so each wave runs only its own loop
     if (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) < 4)
-        producer<DK, DV, ZPRO>(p, sm, lane, cb, ce);
+        producer<DK, DV, ZPRO>(p, sm, lane, span, cb, ce);
     else
-        consumer<TOut, DK, DV, GATED, CKPT>(p, sm, lane, seg, cb, ce);
+        consumer<TOut, DK, DV, GATED, CKPT>(p, sm, lane, seg, span, cb, ce);
 }
 
 // One workgroup: the lanes whose flags are not all 1, in increasing order (a block-wide prefix

@@ -122,29 +122,9 @@ __device__ __forceinline__ bool run_segment(const ChunkLaunch& p, InterSmem<DK, 
     const int64_t DVl = DV;
 
     // ---- where the lane's rows, records and checkpoints are (see SeqMap) ---------------------
-    int64_t row_base, len, slot0, ck_base = 0, ck_stride = 1;
-    if (p.map.cu) {
-        const int64_t s = uniform64(lane / p.map.H), h = uniform64(lane % p.map.H);
-        const int64_t rows = p.map.rows;
-        int64_t c0 = p.map.cu[s], c1 = p.map.cu[s + 1];
-        c0 = c0 < 0 ? 0 : (c0 > rows ? rows : c0);
-        c1 = c1 < c0 ? c0 : (c1 > rows ? rows : c1);
-        len = c1 - c0 < p.map.max_len ? c1 - c0 : p.map.max_len;
-        row_base = h * rows + c0;
-        slot0 = h * p.map.slots + (c0 >> 6) + s;
-        if (p.ckpt) { ck_base = (int64_t)p.ck_off[s] * p.map.H + h; ck_stride = p.map.H; }
-    } else {
-        len = p.T;
-        row_base = lane * p.T;
-        slot0 = lane * p.nchunks;
-        if (p.ckpt) {   // sequence s = lane / H has its checkpoints at rows s * ck_per_lane + j - 1
-            const int64_t s = uniform64(lane / p.map.H), h = uniform64(lane % p.map.H);
-            ck_base = s * p.ck_per_lane * p.map.H + h;
-            ck_stride = p.map.H;
-        }
-    }
-    row_base = uniform64(row_base); len = uniform64(len); slot0 = uniform64(slot0);
-    ck_base = uniform64(ck_base); ck_stride = uniform64(ck_stride);
+    const LaneSpan span = lane_span(p, lane);
+    const int64_t row_base = span.row_base, len = span.len, slot0 = span.slot0;
+    const int64_t ck_base = span.ck_base, ck_stride = span.ck_stride;
     const int64_t nchunks = (len + kC - 1) / kC;
     // the last segment runs to the lane's last chunk (a packed batch plans with its longest
     // sequence); segments past a short lane's end are empty

@@ -116,7 +116,25 @@ struct IntraArgs {
     int nseg;
     const int32_t* lane_list;
     const int32_t* lane_count;
+    // Packed batch: with slot_list set, only the record slots slot_list[0 .. *slot_count) (global
+    // indices h * slots + j). With run_if set, the launch does nothing when *run_if is 0.
+    const int32_t* slot_list;
+    const int32_t* slot_count;
+    const int32_t* run_if;
 };
+
+// The record slots of a packed batch that the windows before segment boundaries 1 .. nseg - 1
+// read (kPassWindow; every window ends at its segment's first chunk, clamped to the sequence's
+// chunks), each once, in increasing (lane, boundary, chunk) order: list[0 .. *count).
+struct WindowSlots {
+    const int32_t* cu;
+    int64_t N, H, rows, max_len, slots;
+    int nseg;
+    int64_t chunks_per_seg, win_chunks;
+    int32_t* list;
+    int32_t* count;
+};
+hipError_t launch_window_slots(const WindowSlots& a, hipStream_t st);
 
 // Slot table and checkpoint offsets of a packed batch.
 struct VarlenPrep {

@@ -51,7 +51,9 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs p) {
     // window chunks per boundary: the whole previous segment when a segment is shorter than the window
     const uint32_t wspan = !PACKED && p.win_chunks > 0 ? (uint32_t)(p.win_chunks < p.chunks_per_seg ? p.win_chunks : p.chunks_per_seg) : 0u;
     const uint32_t per_lane = wspan ? (uint32_t)(p.nseg - 1) * wspan : slots;
-    const uint32_t total = PACKED ? (uint32_t)(p.map.H * (int64_t)slots) : nl * per_lane;
+    if (p.run_if && *p.run_if == 0) return;
+    const uint32_t total = PACKED ? (p.slot_list ? (uint32_t)*p.slot_count : (uint32_t)(p.map.H * (int64_t)slots))
+                                  : nl * per_lane;
     const int64_t nheads = p.map.H > 0 ? p.map.H : 1;
 
     // First row and valid rows of item (h, j) in the row-major inputs; no rows (zeros, no
@@ -81,7 +83,12 @@ __global__ __launch_bounds__(256, 2) void intra_kernel(IntraArgs p) {
     // boundary s = r / wspan + 1 ends at chunk s * chunks_per_seg).
     const uint32_t G = gridDim.x;
     auto item_of = [&](uint32_t u, uint32_t& h, uint32_t& j) {
-        if (PACKED) { h = u / slots; j = u % slots; return; }
+        if (PACKED) {
+            const uint32_t e = p.slot_list ? (uint32_t)p.slot_list[u] : u;
+            h = e / slots;
+            j = e % slots;
+            return;
+        }
         h = u % nl;
         const uint32_t r = u / nl;
         j = wspan ? (r / wspan + 1u) * (uint32_t)p.chunks_per_seg - wspan + r % wspan : slots - 1u - r;

@@ -167,17 +167,21 @@ Plan make_plan(const Geometry& g) {
             if (p.fused) {
                 p.pre_bytes = p.flag_bytes;
                 p.list_bytes = ((size_t)(g.lanes + 1) * sizeof(int32_t) + 15) & ~(size_t)15;
+                if (g.tab_slots > 0)
+                    p.wlist_bytes = ((size_t)(g.lanes * (nseg - 1) * kWindowChunks + 1) * sizeof(int32_t) + 15) & ~(size_t)15;
             }
         }
         p.tab_bytes = (size_t)g.tab_slots * sizeof(SlotEntry);
     }
-    p.ws_bytes = p.rec_bytes + p.pair_bytes + p.entry_bytes + p.tab_bytes + p.flag_bytes + p.pre_bytes + p.list_bytes;
+    p.ws_bytes = p.rec_bytes + p.pair_bytes + p.entry_bytes + p.tab_bytes + p.flag_bytes + p.pre_bytes + p.list_bytes +
+                 p.wlist_bytes;
     return p;
 }
 
 // The fused plan: the windows' records and the window launch (n > 1), the fused kernel for every
 // lane whose windows are all exact, then the two-kernel window split below for the other lanes
-// (their full records, first), each launch of which skips the fused lanes.
+// (their full records first: in a packed batch, every record when any lane falls back), each
+// launch of which skips the fused lanes.
 static kda_status run_fused(ChunkLaunch& a, const Plan& plan, const IntraArgs& ia, unsigned char* ws, hipStream_t st) {
     if (plan.nseg == 1) {
         a.split = kPassAll;
@@ -188,7 +192,18 @@ static kda_status run_fused(ChunkLaunch& a, const Plan& plan, const IntraArgs& i
     int32_t* list = reinterpret_cast<int32_t*>(ws + pre_off + plan.pre_bytes);
     int32_t* count = list + a.lanes;
     IntraArgs iw = ia;   // the window chunks of every lane
-    iw.win_chunks = plan.win_chunks; iw.chunks_per_seg = plan.chunks_per_seg; iw.nseg = plan.nseg;
+    if (a.map.cu) {      // packed: their slots, listed on the device from cu_seqlens
+        int32_t* wlist = reinterpret_cast<int32_t*>(ws + pre_off + plan.pre_bytes + plan.list_bytes);
+        WindowSlots wsl{};
+        wsl.cu = a.map.cu; wsl.N = a.lanes / a.map.H; wsl.H = a.map.H; wsl.rows = a.map.rows;
+        wsl.max_len = a.map.max_len; wsl.slots = a.map.slots; wsl.nseg = plan.nseg;
+        wsl.chunks_per_seg = plan.chunks_per_seg; wsl.win_chunks = plan.win_chunks;
+        wsl.list = wlist; wsl.count = wlist + a.lanes * (plan.nseg - 1) * plan.win_chunks;
+        if (launch_window_slots(wsl, st) != hipSuccess) return KDA_ERR_HIP;
+        iw.slot_list = wsl.list; iw.slot_count = wsl.count;
+    } else {
+        iw.win_chunks = plan.win_chunks; iw.chunks_per_seg = plan.chunks_per_seg; iw.nseg = plan.nseg;
+    }
     if (launch_intra(iw, st) != hipSuccess) return KDA_ERR_HIP;
     ChunkLaunch w = a;   // their flags and S~
     w.split = kPassWindow; w.ws_flag = pre;
@@ -198,8 +213,9 @@ static kda_status run_fused(ChunkLaunch& a, const Plan& plan, const IntraArgs& i
     f.split = kPassAll; f.ws_flag = pre;
     if (launch_fused(f, st) != hipSuccess) return KDA_ERR_HIP;
     if (launch_fallback_lanes(pre, a.lanes, plan.nseg, list, count, st) != hipSuccess) return KDA_ERR_HIP;
-    IntraArgs il = ia;   // the fallback lanes' records
-    il.lane_list = list; il.lane_count = count;
+    IntraArgs il = ia;   // the fallback lanes' records (packed: every record, when any lane falls back)
+    if (a.map.cu) il.run_if = count;
+    else { il.lane_list = list; il.lane_count = count; }
     if (launch_intra(il, st) != hipSuccess) return KDA_ERR_HIP;
     a.skip_flag = pre;
     return KDA_OK;

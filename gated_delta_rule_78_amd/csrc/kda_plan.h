@@ -35,7 +35,8 @@ constexpr int64_t kWindowChunks = 8;
 
 // Segments per lane, chunks per segment and workspace of a prefill call. The workspace holds,
 // in this order: records, affine pairs, entry states, slot table, window flags and, for the
-// fused plan, the window launch's flags and the list of lanes left to the two-kernel fallback.
+// fused plan, the window launch's flags, the list of lanes left to the two-kernel fallback and
+// (packed batches) the list of the windows' record slots.
 struct Plan {
     bool fused;          // the fused kernel (with the two-kernel path as the fallback of lanes
                          // with an inexact window)
@@ -49,6 +50,7 @@ struct Plan {
     size_t flag_bytes;   // window flags [lanes][nseg] int32 (nseg > 1)
     size_t pre_bytes;    // fused plan, nseg > 1: the window launch's flags [lanes][nseg] int32
     size_t list_bytes;   // fused plan, nseg > 1: fallback lanes [lanes] int32, then their count
+    size_t wlist_bytes;  // fused plan of a packed batch, nseg > 1: the windows' slots, then their count
     size_t ws_bytes;
 };
 

@@ -6,10 +6,45 @@
 // Internal to the library.
 #pragma once
 
+#include "kda_internal.h"
 #include "kda_mfma.h"
 #include "kda_record.h"
 
 namespace kda {
+
+// Where a lane's rows, records and checkpoints are (SeqMap): its first row in the row-major
+// tensors, its length, its first record slot, and the index of its first checkpoint and the
+// stride between its checkpoints (ChunkLaunch::ckpt). Packed lengths are clamped into the rows
+// and to max_len, so malformed lengths give wrong numbers but no access outside the tensors.
+struct LaneSpan {
+    int64_t row_base, len, slot0, ck_base, ck_stride;
+};
+__device__ __forceinline__ LaneSpan lane_span(const ChunkLaunch& p, int64_t lane) {
+    LaneSpan r{0, 0, 0, 0, 1};
+    if (p.map.cu) {
+        const int64_t s = uniform64(lane / p.map.H), h = uniform64(lane % p.map.H);
+        const int64_t rows = p.map.rows;
+        int64_t c0 = p.map.cu[s], c1 = p.map.cu[s + 1];
+        c0 = c0 < 0 ? 0 : (c0 > rows ? rows : c0);
+        c1 = c1 < c0 ? c0 : (c1 > rows ? rows : c1);
+        r.len = c1 - c0 < p.map.max_len ? c1 - c0 : p.map.max_len;
+        r.row_base = h * rows + c0;
+        r.slot0 = h * p.map.slots + (c0 >> 6) + s;
+        if (p.ckpt) { r.ck_base = (int64_t)p.ck_off[s] * p.map.H + h; r.ck_stride = p.map.H; }
+    } else {
+        r.len = p.T;
+        r.row_base = lane * p.T;
+        r.slot0 = lane * p.nchunks;
+        if (p.ckpt) {   // sequence s = lane / H has its checkpoints at rows s * ck_per_lane + j - 1
+            const int64_t s = uniform64(lane / p.map.H), h = uniform64(lane % p.map.H);
+            r.ck_base = s * p.ck_per_lane * p.map.H + h;
+            r.ck_stride = p.map.H;
+        }
+    }
+    r.row_base = uniform64(r.row_base); r.len = uniform64(r.len); r.slot0 = uniform64(r.slot0);
+    r.ck_base = uniform64(r.ck_base); r.ck_stride = uniform64(r.ck_stride);
+    return r;
+}
 
 // Four output values in storage form (bf16: 8 bytes; fp32: 16 bytes) and their buffer store.
 __device__ __forceinline__ void store_out(__amdgpu_buffer_rsrc_t r, uint32_t off, f32x4 x, bf16_t*) {

@@ -83,7 +83,55 @@ __global__ __launch_bounds__(kThreads) void varlen_prep_kernel(VarlenPrep p) {
     p.slot_tab[j] = e;
 }
 
+// One workgroup: the window slots of every lane (WindowSlots). Candidate u = ((lane * (nseg - 1)
+// + b - 1) * win + r) is chunk cb_b - win + r of the lane's sequence, cb_b = min(b * cps, n_s) the
+// first chunk of segment b clamped to the sequence's n_s chunks; it is kept when it is >= 0 and
+// not already in boundary b - 1's window (>= cb_{b-1}).
+__global__ __launch_bounds__(1024, 1) void window_slots_kernel(WindowSlots p) {
+    __shared__ int32_t pre[1024];
+    const int64_t lanes = p.N * p.H;
+    const int64_t per_lane = (int64_t)(p.nseg - 1) * p.win_chunks;
+    const int64_t total = lanes * per_lane;
+    VarlenPrep vp{};
+    vp.cu = p.cu; vp.rows = p.rows; vp.max_len = p.max_len;
+    int32_t base = 0;
+    for (int64_t u0 = 0; u0 < total; u0 += 1024) {
+        const int64_t u = u0 + threadIdx.x;
+        int32_t slot = -1;
+        if (u < total) {
+            const int64_t lane = u / per_lane, rest = u % per_lane;
+            const int64_t b = 1 + rest / p.win_chunks, r = rest % p.win_chunks;
+            const int64_t s = lane / p.H, h = lane % p.H;
+            int64_t c0, len;
+            seq_rows(vp, s, c0, len);
+            const int64_t n = (len + 63) / 64;
+            const int64_t cb = b * p.chunks_per_seg < n ? b * p.chunks_per_seg : n;
+            const int64_t cp = (b - 1) * p.chunks_per_seg < n ? (b - 1) * p.chunks_per_seg : n;
+            const int64_t c = cb - p.win_chunks + r;
+            if (c >= 0 && (b == 1 || c >= cp)) slot = (int32_t)(h * p.slots + (c0 >> 6) + s + c);
+        }
+        const int32_t need = slot >= 0 ? 1 : 0;
+        pre[threadIdx.x] = need;
+        __syncthreads();
+        for (int d = 1; d < 1024; d <<= 1) {   // inclusive Hillis-Steele scan
+            const int32_t x = threadIdx.x >= (unsigned)d ? pre[threadIdx.x - d] : 0;
+            __syncthreads();
+            pre[threadIdx.x] += x;
+            __syncthreads();
+        }
+        if (need) p.list[base + pre[threadIdx.x] - 1] = slot;
+        base += pre[1023];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) *p.count = base;
+}
+
 }  // namespace
+
+hipError_t launch_window_slots(const WindowSlots& a, hipStream_t st) {
+    hipLaunchKernelGGL(window_slots_kernel, dim3(1), dim3(1024), 0, st, a);
+    return hipGetLastError();
+}
 
 hipError_t launch_varlen_prep(const VarlenPrep& a, hipStream_t st) {
     const int64_t blocks = 1 + (a.slots + kThreads - 1) / kThreads;

@@ -190,7 +190,7 @@ typedef struct kda_varlen_desc {
     int32_t packed;     /* 1: sequences packed along T, described by cu_seqlens;
                            0: N sequences of T tokens in kda_chunk_fwd's layout (B = N)   */
     int32_t state_pass; /* as kda_chunk_desc::state_pass; 2 (the fused kernel) needs
-                           packed = 0 and dk = dv = 128, else KDA_ERR_UNSUPPORTED         */
+                           dk = dv = 128, else KDA_ERR_UNSUPPORTED                        */
 } kda_varlen_desc;
 
 /* Bytes of device workspace kda_chunk_fwd_varlen needs for `desc` (0 for an invalid desc).

@@ -17,7 +17,9 @@ kda::ChunkLaunch g_last;
 kda::ChunkLaunch g_inter_seq[8];   // the first state-pass launches since reset(), in order
 kda::IntraArgs g_intra_seq[4];     // the first intra-chunk launches since reset()
 kda::ChunkLaunch g_fused_last;
-int g_order[16], g_norder;          // launch kinds in order: 1 intra, 2 inter, 3 scan, 4 fused, 5 lane list
+int g_order[16], g_norder;          // launch kinds in order: 1 intra, 2 inter, 3 scan, 4 fused, 5 lane list,
+                                    // 6 window slot list
+kda::WindowSlots g_wslots;
 void note(int kind) { if (g_norder < 16) g_order[g_norder++] = kind; }
 void reset() { g_intra = g_inter = g_scan = g_chunk = g_copy = g_prep = g_bwd = g_decode = g_fused = g_lanes = g_norder = 0; }
 }  // namespace
@@ -42,6 +44,10 @@ hipError_t launch_fallback_lanes(const int32_t* flag, int64_t lanes, int nseg, i
     return flag && list && count && lanes > 0 && nseg > 1 ? hipSuccess : hipErrorInvalidValue;
 }
 hipError_t launch_varlen_prep(const VarlenPrep&, hipStream_t) { ++g_prep; return hipSuccess; }
+hipError_t launch_window_slots(const WindowSlots& a, hipStream_t) {
+    g_wslots = a; note(6);
+    return a.cu && a.list && a.count && a.nseg > 1 ? hipSuccess : hipErrorInvalidValue;
+}
 hipError_t launch_copy_or_zero(float* dst, const float*, int64_t n, hipStream_t) { ++g_copy; return dst && n > 0 ? hipSuccess : hipErrorInvalidValue; }
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t) { ++g_bwd; return a.ckpt || a.T < 64 ? hipSuccess : hipErrorInvalidValue; }
 size_t bwd_prep_floats(int64_t dk, int64_t dv) { return (size_t)(64 * (3 * dk + dv) + 64 * 64 + dk); }
@@ -234,11 +240,36 @@ static int check_varlen() {
     g.g_min = 0.f;
     CHECK(call(&d, P(8 * GB), P(9 * GB), P(10 * GB), &g, P(11 * GB), need, nullptr) == KDA_ERR_INVALID_ARG);
     g.g_min = -5.f;
-    // the fused kernel takes equal-length batches (checkpoints and gating included), not packed ones
+    // the fused kernel on a packed batch (3 segments of 4 chunks): the slot table, the list of the
+    // windows' slots and their records, the window launch, the fused kernel, the lane list, every
+    // record when a lane falls back, then the two-kernel passes skipping the fused lanes
     kda_varlen_desc f = d;
-    f.state_pass = 2;
-    CHECK(call(&f, P(8 * GB), P(9 * GB), P(10 * GB), nullptr, P(11 * GB), need) == KDA_ERR_UNSUPPORTED);
-    f.packed = 0; f.segments = 2;
+    f.state_pass = 2; f.segments = 3; f.max_len = 768; f.T = 1536;
+    const size_t needp = kda_chunk_fwd_varlen_workspace_bytes(&f);
+    kda_varlen_desc f1 = f; f1.state_pass = 1;
+    CHECK(needp > kda_chunk_fwd_varlen_workspace_bytes(&f1));
+    reset();
+    CHECK(call(&f, P(8 * GB), P(9 * GB), P(10 * GB), nullptr, P(11 * GB), needp - 1) == KDA_ERR_WORKSPACE);
+    CHECK(call(&f, P(8 * GB), P(9 * GB), P(10 * GB), nullptr, P(11 * GB), needp) == KDA_OK);
+    {
+        const int want[] = {6, 1, 2, 4, 5, 1, 2, 2, 3, 2};
+        CHECK(g_norder == 10 && g_prep == 1);
+        for (int i = 0; i < 10; ++i) CHECK(g_order[i] == want[i]);
+        const unsigned char* w0 = (const unsigned char*)P(11 * GB);
+        const unsigned char* wend = w0 + needp;
+        CHECK(g_wslots.N == 3 && g_wslots.H == 2 && g_wslots.nseg == 3 && g_wslots.chunks_per_seg == 4 &&
+              g_wslots.win_chunks == 8 && g_wslots.max_len == 768 && g_wslots.rows == 1536);
+        CHECK((const unsigned char*)g_wslots.list > w0 && (const unsigned char*)(g_wslots.count + 1) <= wend &&
+              g_wslots.count == g_wslots.list + 6 * 2 * 8);
+        CHECK(g_intra_seq[0].slot_list == g_wslots.list && g_intra_seq[0].slot_count == g_wslots.count &&
+              g_intra_seq[0].slot_tab != nullptr && g_intra_seq[0].run_if == nullptr);
+        CHECK(g_intra_seq[1].slot_list == nullptr && g_intra_seq[1].lane_list == nullptr && g_intra_seq[1].run_if &&
+              (const unsigned char*)g_intra_seq[1].run_if < (const unsigned char*)g_wslots.list);
+        CHECK(g_inter_seq[0].split == kda::kPassWindow && g_inter_seq[0].map.cu == P(8 * GB));
+        CHECK(g_fused_last.map.cu == P(8 * GB) && g_fused_last.ws_flag == g_inter_seq[0].ws_flag && g_fused_last.nseg == 3);
+        for (int i = 1; i < 4; ++i) CHECK(g_inter_seq[i].skip_flag == g_inter_seq[0].ws_flag);
+    }
+    f.packed = 0; f.segments = 2; f.max_len = 512; f.T = 640;
     const size_t needf = kda_chunk_fwd_varlen_workspace_bytes(&f);
     reset();
     CHECK(call(&f, nullptr, P(9 * GB), P(10 * GB), &g, P(11 * GB), needf, nullptr) == KDA_OK);

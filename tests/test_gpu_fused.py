@@ -224,3 +224,117 @@ def test_fused_more_workgroups_than_compute_units(segments):
     say("fused many lanes: B=%d H=%d T=%d segments=%d" % (B, H, T, segments))
     q, k, v, la, beta, S0 = inputs(B, H, T, 9950 + segments)
     check("fused many lanes segments=%d" % segments, q, k, v, la, beta, S0, segments=segments)
+
+
+def _packed_pair(tag, lens, H, E, segments, seed, slow_heads=(), max_len=None, s0_std=0.3, odt=BF16, **gkw):
+    """One packed batch through the fused plan and the two-kernel plan with the same split: every
+    output equal bit for bit; returns the inputs and the fused outputs."""
+    say("%s: lens=%s H=%d E=%d segments=%d slow heads=%s max_len=%s" % (tag, list(lens), H, E, segments,
+                                                                        list(slow_heads), max_len))
+    q, k, v, la, beta, cu, S0 = synth.packed_inputs(lens, H, 128, 128, BF16, device=DEV, seed_base=seed,
+                                                    s0_std=s0_std)
+    for h in slow_heads:
+        la[h] = synth.packed_inputs(lens, H, 128, 128, BF16, device=DEV, seed_base=seed + 50,
+                                    log_alpha_range=SLOW)[3][h]
+    outs = {sp: kda.chunk_fwd_varlen(q, k, v, la if "z" not in gkw else None, beta, cu, S0, max_len=max_len,
+                                     ckpt_every=E, segments=segments, state_pass=sp, out_dtype=odt, **gkw)
+            for sp in (FUSED, TWO)}
+    torch.cuda.synchronize()
+    _same_packed(tag, outs[FUSED], outs[TWO])
+    return (q, k, v, la, beta, cu, S0), outs[FUSED]
+
+
+def _same_packed(tag, a, b):
+    """o, S_T and the checkpoint offsets equal bit for bit, and the checkpoints written (the first
+    offsets[N] of the buffer: the rest of its capacity is never written)."""
+    for x, y in zip(a[:2], b[:2]):
+        assert torch.equal(x, y), "%s: fused and two-kernel packed calls differ" % tag
+    if a[3] is not None:
+        assert torch.equal(a[3], b[3]), "%s: checkpoint offsets differ" % tag
+        n = int(a[3][-1])
+        assert torch.equal(a[2][:n], b[2][:n]), "%s: checkpoints differ" % tag
+    say("%s: bit-identical to the two-kernel path" % tag)
+
+
+def _check_packed_oracle(tag, ins, outs, E, N, H):
+    q, k, v, la, beta, cu, S0 = ins
+    o, S_T, ck, offs = outs
+    ref = native.kda_varlen(host32(q), host32(k), host32(v), host32(la), host32(beta), cu.cpu().numpy(),
+                            None if S0 is None else host32(S0), ckpt_every=E)
+    assert_close(tag, BF16, host32(o), ref[0], host32(S_T).reshape(N * H, 128, 128), ref[1].reshape(N * H, 128, 128))
+    if E:
+        assert np.array_equal(offs.cpu().numpy(), np.asarray(ref[3]))
+        n = int(ref[3][-1])
+        if n:
+            es = rel_l2_per_lane(host32(ck[:n]).reshape(n * H, -1), ref[2].reshape(n * H, -1))
+            say("%s: %d checkpoints x %d heads, relL2 = %.3e" % (tag, n, H, es))
+            assert es <= TOL_S[BF16]
+
+
+PACKED_MIXES = {
+    "ragged": [1000, 64, 0, 1, 513, 700, 130, 77],
+    "one_long": [40, 2600, 17],
+    "boundaries": [64 * 12, 64 * 12 - 1, 64 * 12 + 1, 64 * 4, 64 * 8],
+}
+
+
+@pytest.mark.parametrize("segments", [1, 3, 5])
+@pytest.mark.parametrize("mix", list(PACKED_MIXES))
+def test_fused_packed_mixes(mix, segments):
+    """Packed sequences of mixed lengths (empty, one token, chunk multiples, the longest well past
+    the others) with checkpoints every 128 tokens: segments past a short sequence's end are empty,
+    and its windows are clamped to its chunks."""
+    lens, H, E = PACKED_MIXES[mix], 3, 128
+    ins, outs = _packed_pair("fused packed %s" % mix, lens, H, E, segments, 12000 + 10 * segments + len(mix))
+    _check_packed_oracle("fused packed %s segments=%d" % (mix, segments), ins, outs, E, len(lens), H)
+
+
+def test_fused_packed_slow_heads_fall_back():
+    """Slow decay on two of four heads: their lanes' windows are inexact, every record is then
+    built and the two-kernel passes finish those lanes; the other lanes stay fused."""
+    lens, H, E = [64 * 30 + 9, 300, 64 * 17], 4, 256
+    ins, outs = _packed_pair("fused packed slow", lens, H, E, 4, 12500, slow_heads=(1, 3))
+    _check_packed_oracle("fused packed slow", ins, outs, E, len(lens), H)
+
+
+def test_fused_packed_max_len_and_empty():
+    """max_len above the longest sequence (the plan's chunk count), and a batch of empty sequences."""
+    lens, H = [700, 64 * 10, 5], 2
+    ins, outs = _packed_pair("fused packed max_len", lens, H, 64, 3, 12600, max_len=64 * 16)
+    _check_packed_oracle("fused packed max_len", ins, outs, 64, len(lens), H)
+    ins, outs = _packed_pair("fused packed empty", [0, 0, 0], 2, 0, 2, 12700, s0_std=0.2)
+    o, S_T = outs[0], outs[1]
+    assert o.numel() == 0 and torch.equal(S_T, ins[6])
+
+
+def test_fused_packed_many_short_sequences():
+    """Sixty sequences of at most three chunks under a 3-segment plan of a longer one: most lanes
+    have all their chunks in segment 0, and their windows start at chunk 0."""
+    g = np.random.default_rng(12800)
+    lens = [int(x) for x in g.integers(0, 64 * 3, 60)] + [64 * 20 + 3]
+    ins, outs = _packed_pair("fused packed many", lens, 2, 64, 3, 12800, s0_std=None)
+    _check_packed_oracle("fused packed many", ins, outs, 64, len(lens), 2)
+
+
+@pytest.mark.parametrize("odt", [BF16, torch.float32])
+def test_fused_packed_gating(odt):
+    """The decay prologue and gated RMSNorm epilogue on a packed batch in the fused kernel:
+    bit-identical to the two-kernel path; the gated output against the oracle's epilogue."""
+    lens, H, E = [64 * 14 + 30, 0, 200, 64 * 9], 3, 256
+    z_seed = 12900 + (odt == BF16)
+    q, k, v, la, beta, cu, S0 = synth.packed_inputs(lens, H, 128, 128, BF16, device=DEV, seed_base=z_seed, s0_std=0.3)
+    T = int(cu[-1])
+    z, A_log, gate, w = synth.gating_inputs((H, T), H, 128, 128, BF16, device=DEV, seed=z_seed + 1)
+    kw = dict(z=z, A_log=A_log, g_min=G_MIN, gate=gate, norm_weight=w, eps=EPS, ckpt_every=E, segments=3,
+              out_dtype=odt)
+    say("fused packed gating: lens=%s H=%d out=%s" % (lens, H, odt))
+    outs = {sp: kda.chunk_fwd_varlen(q, k, v, None, beta, cu, S0, state_pass=sp, **kw) for sp in (FUSED, TWO)}
+    torch.cuda.synchronize()
+    _same_packed("fused packed gating", outs[FUSED], outs[TWO])
+    o, S_T = outs[FUSED][0], outs[FUSED][1]
+    g = gating.log_decay(host32(z), host32(A_log)[:, None, None], G_MIN).astype(np.float32)
+    ref = native.kda_varlen(host32(q), host32(k), host32(v), g, host32(beta), cu.cpu().numpy(), host32(S0))
+    check_gated("fused packed gating", o, ref[0], gate, w, odt)
+    N = len(lens)
+    es = rel_l2_per_lane(host32(S_T).reshape(N * H, -1), ref[1].reshape(N * H, -1))
+    assert es <= TOL_S[BF16]
