@@ -113,7 +113,7 @@ __device__ __forceinline__ void producer(const ChunkLaunch& p, FusedSmem<DK, DV>
 
 template <typename TOut, int DK, int DV, bool GATED, bool CKPT>
 __device__ __forceinline__ void consumer(const ChunkLaunch& p, FusedSmem<DK, DV>& sm, int64_t lane, int seg,
-                                         const LaneSpan& span, int64_t cb, int64_t ce) {
+                                         bool last, const LaneSpan& span, int64_t cb, int64_t ce) {
     constexpr int NT = DV / 64;
     constexpr int NM = DK / 16;
     const int tid = threadIdx.x;
@@ -284,7 +284,7 @@ __device__ __forceinline__ void consumer(const ChunkLaunch& p, FusedSmem<DK, DV>
         }
         epoch_barrier();   // 3
     }
-    if (seg == p.nseg - 1 && p.S_T) store_state<DK, DV, NT>(p.S_T + lane * DK * DVl, S, col0, lq, l16);
+    if (last && p.S_T) store_state<DK, DV, NT>(p.S_T + lane * DK * DVl, S, col0, lq, l16);
 }
 
 template <typename TOut, int DK, int DV, bool ZPRO, bool GATED, bool CKPT>
@@ -294,11 +294,13 @@ __global__ __launch_bounds__(kThreads, 1) void fused_kernel(ChunkLaunch p) {
     const int seg = (int)uniform64(blockIdx.x % p.nseg);
     if (p.nseg > 1 && !window_split_exact(p.ws_flag + lane * p.nseg, p.nseg)) return;   // the fallback's lane
     const LaneSpan span = lane_span(p, lane);
-    // the last segment runs to the lane's last chunk (a packed batch plans with its longest
-    // sequence); segments past a short lane's end are empty
+    // the lane's last live segment runs to its last chunk and stores S_T; the ones past it (a
+    // packed lane shorter than the plan's longest) do nothing
     const int64_t nch = (span.len + kC - 1) / kC;
+    const int live = live_segments(p, nch);
+    if (seg >= live) return;
     int64_t cb = (int64_t)seg * p.chunks_per_seg;
-    int64_t ce = seg == p.nseg - 1 ? nch : cb + p.chunks_per_seg;
+    int64_t ce = seg == live - 1 ? nch : cb + p.chunks_per_seg;
     if (ce > nch) ce = nch;
     if (cb > ce) cb = ce;
     cb = uniform64(cb);
@@ -307,7 +309,7 @@ __global__ __launch_bounds__(kThreads, 1) void fused_kernel(ChunkLaunch p) {
     if (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6) < 4)
         producer<DK, DV, ZPRO>(p, sm, lane, span, cb, ce);
     else
-        consumer<TOut, DK, DV, GATED, CKPT>(p, sm, lane, seg, span, cb, ce);
+        consumer<TOut, DK, DV, GATED, CKPT>(p, sm, lane, seg, seg == live - 1, span, cb, ce);
 }
 
 // One workgroup: the lanes whose flags are not all 1, in increasing order (a block-wide prefix

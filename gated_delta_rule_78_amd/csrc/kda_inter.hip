@@ -126,10 +126,17 @@ __device__ __forceinline__ bool run_segment(const ChunkLaunch& p, InterSmem<DK, 
     const int64_t row_base = span.row_base, len = span.len, slot0 = span.slot0;
     const int64_t ck_base = span.ck_base, ck_stride = span.ck_stride;
     const int64_t nchunks = (len + kC - 1) / kC;
-    // the last segment runs to the lane's last chunk (a packed batch plans with its longest
-    // sequence); segments past a short lane's end are empty
+    // the lane's last live segment runs to its last chunk; a segment past it does nothing, and
+    // the window passes mark its boundary exact (no SUMMARY is needed for the last live one: the
+    // scan stops before it)
+    const int live = live_segments(p, nchunks);
+    if (seg >= live || (!FIN && seg == live - 1)) {
+        if (FIN && (p.split == kPassWindow || p.split == kPassWindowFinish) && tid == 0)
+            p.ws_flag[lane * p.nseg + seg - 1] = 1;
+        return true;
+    }
     int64_t c_begin = (int64_t)seg * p.chunks_per_seg;
-    int64_t c_end = seg == p.nseg - 1 ? nchunks : c_begin + p.chunks_per_seg;
+    int64_t c_end = seg == live - 1 ? nchunks : c_begin + p.chunks_per_seg;
     if (c_end > nchunks) c_end = nchunks;
     if (c_begin > c_end) c_begin = c_end;
     const int col0 = w * 16 * NT;   // FINISH: in [0, dv); SUMMARY: in [0, dv + dk)
@@ -327,7 +334,7 @@ __device__ __forceinline__ bool run_segment(const ChunkLaunch& p, InterSmem<DK, 
     if (!FIN) {
         dst = p.ws_pair + (lane * p.nseg + seg) * DK * (DVl + DK);
         ld_dst = DVl + DK;
-    } else if (seg == p.nseg - 1) {
+    } else if (seg == live - 1) {
         dst = p.S_T ? p.S_T + lane * DK * DVl : nullptr;
     } else if (seg == 0) {   // segment 1's entry state, for the fallback's scan
         dst = p.ws_entry + ((lane * p.nseg + 1) * DK) * DVl;

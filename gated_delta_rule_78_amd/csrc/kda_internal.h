@@ -64,9 +64,11 @@ struct SlotEntry {
 enum SplitPass { kPassAll = 0, kPassWindowFinish = 1, kPassCarry = 2, kPassFinish = 3, kPassWindow = 4 };
 
 // One launch of the chunk kernels. Blocks [0, n_fin) run FINISH work (exact entry state, write
-// o and, for the last segment, S_T); the following n_sum blocks run SUMMARY work (affine pair
-// of a segment, no o). Every segment covers `chunks_per_seg` chunks of 64 tokens; the last
-// segment of a lane runs to the lane's last chunk.
+// o and, for the lane's last segment, S_T); the following n_sum blocks run SUMMARY work (affine
+// pair of a segment, no o). Every segment covers `chunks_per_seg` chunks of 64 tokens; the last
+// segment of a lane runs to the lane's last chunk. A packed lane shorter than the plan's longest
+// has fewer segments (ceil(chunks / chunks_per_seg), at least 1): the later ones do nothing,
+// and their window flags are set (exact).
 struct ChunkLaunch {
     int64_t lanes, T, dk, dv;
     int64_t nchunks;
@@ -124,8 +126,9 @@ struct IntraArgs {
 };
 
 // The record slots of a packed batch that the windows before segment boundaries 1 .. nseg - 1
-// read (kPassWindow; every window ends at its segment's first chunk, clamped to the sequence's
-// chunks), each once, in increasing (lane, boundary, chunk) order: list[0 .. *count).
+// read (kPassWindow; every window ends at its segment's first chunk, and a boundary at or past
+// the sequence's last chunk has none), each once, in increasing (lane, boundary, chunk) order:
+// list[0 .. *count).
 struct WindowSlots {
     const int32_t* cu;
     int64_t N, H, rows, max_len, slots;

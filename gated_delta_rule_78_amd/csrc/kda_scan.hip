@@ -2,7 +2,8 @@
 // section 2.5: a segment acts on the state as the affine map S_out = S~ + M S_in, and such maps
 // compose associatively). Given entry_1 (the exit state of segment 0) and the pairs (S~_s, M_s)
 // of the middle segments, it forms the exact entry states entry_{s+1} = S~_s + M_s entry_s for
-// s = 1 .. nseg - 2, in fp32. Lanes whose window flags are all set (see SplitPass) are skipped.
+// s = 1 .. live - 2, in fp32 (live: the lane's segments that hold chunks, nseg but for a packed
+// lane shorter than the longest). Lanes whose window flags are all set (see SplitPass) are skipped.
 //
 // One workgroup per (lane, 16 state columns), one wave per 16-row output tile (8 waves at dk = 128,
 // two per SIMD, so that one wave's operand-load issue overlaps the other's products). The current
@@ -14,6 +15,7 @@
 // instruction touch four times as many cache lines).
 #include "kda_internal.h"
 #include "kda_mfma.h"
+#include "kda_step.h"
 
 namespace kda {
 namespace {
@@ -54,6 +56,9 @@ __global__ __launch_bounds__(DK == 128 ? 512 : 256) void segment_scan_kernel(Chu
     // launch, has nothing to scan
     if (p.skip_flag && window_split_exact(p.skip_flag + lane * nseg, nseg)) return;
     if (window_split_exact(p.ws_flag + lane * nseg, nseg)) return;
+    const int64_t nch = (lane_span(p, lane).len + 63) / 64;   // the lane's chunks of 64 tokens
+    const int ns = live_segments(p, nch);   // steps s = 1 .. ns - 2
+    if (ns <= 2) return;
 
     // entry tile: every load issued before the first LDS store (one memory round trip)
     const float* e1 = p.ws_entry + (lane * nseg + 1) * DK * DV;
@@ -90,8 +95,8 @@ __global__ __launch_bounds__(DK == 128 ? 512 : 256) void segment_scan_kernel(Chu
     // this step's MFMA chain runs. The loop is unrolled by three so that no buffer is ever copied
     // (a register copy would wait for the loads filling its source).
     f32x4 a1[TPW][KJ / 4], st1[TPW], a2[TPW][KJ / 4], st2[TPW];
-    if (nseg > 2) load_step(1, a, st);
-    if (nseg > 3) load_step(2, a1, st1);
+    load_step(1, a, st);
+    if (ns > 3) load_step(2, a1, st1);
     // Barriers below order the LDS tile only: a full barrier would also wait for the operand
     // loads in flight for later steps. The entry states stored here are read by a later kernel.
     lds_barrier();
@@ -99,7 +104,7 @@ __global__ __launch_bounds__(DK == 128 ? 512 : 256) void segment_scan_kernel(Chu
 #define KDA_SCAN_STEP(S_, A_, ST_, NA_, NST_)                                                       \
     do {                                                                                            \
         const int s_ = (S_);                                                                        \
-        if (s_ + 3 < nseg) load_step(s_ + 2, NA_, NST_);                                            \
+        if (s_ + 3 < ns) load_step(s_ + 2, NA_, NST_);                                              \
         f32x4 acc[TPW];                                                                             \
         _Pragma("unroll") for (int t = 0; t < TPW; ++t) acc[t] = ST_[t];                            \
         _Pragma("unroll") for (int j4 = 0; j4 < KJ / 4; ++j4) {                                     \
@@ -118,10 +123,10 @@ __global__ __launch_bounds__(DK == 128 ? 512 : 256) void segment_scan_kernel(Chu
         }                                                                                           \
         lds_barrier();                                                                              \
     } while (0)
-    for (int s = 1; s + 1 < nseg; s += 3) {
+    for (int s = 1; s + 1 < ns; s += 3) {
         KDA_SCAN_STEP(s, a, st, a2, st2);
-        if (s + 2 < nseg) KDA_SCAN_STEP(s + 1, a1, st1, a, st);
-        if (s + 3 < nseg) KDA_SCAN_STEP(s + 2, a2, st2, a1, st1);
+        if (s + 2 < ns) KDA_SCAN_STEP(s + 1, a1, st1, a, st);
+        if (s + 3 < ns) KDA_SCAN_STEP(s + 2, a2, st2, a1, st1);
     }
 #undef KDA_SCAN_STEP
 }

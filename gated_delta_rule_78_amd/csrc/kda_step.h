@@ -46,6 +46,15 @@ __device__ __forceinline__ LaneSpan lane_span(const ChunkLaunch& p, int64_t lane
     return r;
 }
 
+// The segments that hold a lane's nch chunks: [0, live), live >= 1. A packed batch plans its
+// segments for its longest sequence, so a shorter lane ends in an earlier segment, which then
+// finishes the lane (S_T); the boundaries past it have no window and count as exact. (Equal
+// lengths: live = nseg.)
+__device__ __forceinline__ int live_segments(const ChunkLaunch& p, int64_t nch) {
+    const int64_t n = (nch + p.chunks_per_seg - 1) / p.chunks_per_seg;
+    return (int)uniform64(n < 1 ? 1 : (n > p.nseg ? p.nseg : n));
+}
+
 // Four output values in storage form (bf16: 8 bytes; fp32: 16 bytes) and their buffer store.
 __device__ __forceinline__ void store_out(__amdgpu_buffer_rsrc_t r, uint32_t off, f32x4 x, bf16_t*) {
     typedef __attribute__((ext_vector_type(2))) unsigned u32x2;

@@ -84,9 +84,10 @@ __global__ __launch_bounds__(kThreads) void varlen_prep_kernel(VarlenPrep p) {
 }
 
 // One workgroup: the window slots of every lane (WindowSlots). Candidate u = ((lane * (nseg - 1)
-// + b - 1) * win + r) is chunk cb_b - win + r of the lane's sequence, cb_b = min(b * cps, n_s) the
-// first chunk of segment b clamped to the sequence's n_s chunks; it is kept when it is >= 0 and
-// not already in boundary b - 1's window (>= cb_{b-1}).
+// + b - 1) * win + r) is chunk b * cps - win + r of the lane's sequence; it is kept when boundary b
+// lies inside the sequence's n_s chunks (b * cps < n_s: the boundaries past a shorter sequence's
+// end have no window), when it is >= 0, and when it is not already in boundary b - 1's window
+// (>= (b - 1) * cps).
 __global__ __launch_bounds__(1024, 1) void window_slots_kernel(WindowSlots p) {
     __shared__ int32_t pre[1024];
     const int64_t lanes = p.N * p.H;
@@ -105,10 +106,9 @@ __global__ __launch_bounds__(1024, 1) void window_slots_kernel(WindowSlots p) {
             int64_t c0, len;
             seq_rows(vp, s, c0, len);
             const int64_t n = (len + 63) / 64;
-            const int64_t cb = b * p.chunks_per_seg < n ? b * p.chunks_per_seg : n;
-            const int64_t cp = (b - 1) * p.chunks_per_seg < n ? (b - 1) * p.chunks_per_seg : n;
+            const int64_t cb = b * p.chunks_per_seg, cp = cb - p.chunks_per_seg;
             const int64_t c = cb - p.win_chunks + r;
-            if (c >= 0 && (b == 1 || c >= cp)) slot = (int32_t)(h * p.slots + (c0 >> 6) + s + c);
+            if (cb < n && c >= 0 && c >= cp) slot = (int32_t)(h * p.slots + (c0 >> 6) + s + c);
         }
         const int32_t need = slot >= 0 ? 1 : 0;
         pre[threadIdx.x] = need;
