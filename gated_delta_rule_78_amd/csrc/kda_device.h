@@ -95,6 +95,16 @@ __device__ __forceinline__ float lane_value(float x, int lane) {
 }
 
 // Order this wave's LDS writes before its later LDS reads (all lanes of the wave).
+// The lane's index in its wave, computed where it is used: a volatile asm is neither hoisted out
+// of a loop nor merged with another, so the addresses a phase derives from it are rebuilt (a few
+// ALU operations) instead of being held in registers across a long loop, where the register
+// allocator would spill them and reload them behind waits on the memory queue.
+__device__ __forceinline__ int fresh_lane() {
+    int x;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(x));
+    return x;
+}
+
 __device__ __forceinline__ void wave_lds_sync() {
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     __builtin_amdgcn_wave_barrier();

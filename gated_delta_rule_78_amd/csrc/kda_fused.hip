@@ -142,74 +142,56 @@ __device__ __forceinline__ void consumer(const ChunkLaunch& p, FusedSmem<DK, DV>
 #pragma unroll
             for (int r = 0; r < 4; ++r)
                 S[nt][M][r] = entry ? entry[(16 * M + 4 * lq + r) * DVl + col0 + 16 * nt + l16] : 0.f;
+    // wait for the entry state here: left to its first use, the wait would sit at the top of the
+    // chunk loop and, run every chunk, also wait for the stores and loads in flight there
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int M = 0; M < NM; ++M)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                float x = S[nt][M][r];
+                asm volatile("" : "+v"(x));
+                S[nt][M][r] = x;
+            }
     const __amdgpu_buffer_rsrc_t ro = make_rsrc((const TOut*)p.o + row_base * DVl, (uint32_t)(T * DVl * sizeof(TOut)));
     constexpr bool PAIRED = sizeof(TOut) == 2 && NT % 2 == 0;
     constexpr int NP = NT / 2 > 0 ? NT / 2 : 1;
 
     // State checkpoints (ChunkLaunch::ckpt): the lane's j-th at ck_base + (j - 1) ck_stride.
     const int64_t ck_base = span.ck_base, ck_stride = span.ck_stride;
-    // Gated epilogue: the gate rows of chunk c load after the V of chunk c is staged, wait in
-    // registers through the U solve and then sit in the wave's V stage (free until the next V)
-    // until chunk c's o rows are stored, in the layout of those stores; per-token sums of o^2 meet
-    // across the four consumer waves in LDS.
+    // Gated epilogue: the gate rows of chunk c are loaded into registers after chunk c's U solve,
+    // in the layout of chunk c's o stores, and wait there through the next state step (a whole
+    // step to arrive) until those rows are stored; per-token sums of o^2 meet across the four
+    // consumer waves in LDS. The loads are issued on every path, like the V loads (past the last
+    // chunk the rows lie beyond the lane and read as zeros). The row goes in the range-checked
+    // vector offset, rebuilt at each use from fresh_lane().
     const __amdgpu_buffer_rsrc_t rgt =
         make_rsrc(GATED ? (const bf16_t*)p.gt.gate + row_base * DVl : nullptr, GATED ? (uint32_t)(T * DVl * 2) : 0u);
-    uint2 gpend[NT][4];
-    uint4 gq[NP][4];
+    uint2 gpend[NT][4];   // fp32 output: gate values of columns col0 + 16nt + 4lq .. + 3, row 16I + l16
+    uint4 gq[NP][4];      // bf16 output: columns col0 + 32np + pair_col(lq) .. + 7, row 16I + l16
     if (GATED) {   // the weights (ones when absent) in LDS: read at each use, held in no register
         for (int i = l; i < 16 * NT; i += 64) sm.norm_w[col0 + i] = p.gt.norm_w ? p.gt.norm_w[col0 + i] : 1.f;
         wave_lds_sync();
     }
     auto weights = [&](int c0) -> f32x4 { return *reinterpret_cast<const f32x4*>(&sm.norm_w[c0]); };
-    unsigned char* gstage = reinterpret_cast<unsigned char*>(sm.vstage(w)) + l * 16;   // lane-private
     auto load_gate = [&](int64_t c) {
         if (!GATED) return;
-        const uint32_t r0 = (uint32_t)(c * kC);
+        const int fl = fresh_lane();
+        const uint32_t vo =
+            (uint32_t)(((uint32_t)(c * kC) + (uint32_t)(fl & 15)) * (uint32_t)DV + (uint32_t)col0 +
+                       (PAIRED ? pair_col(fl >> 4) : 4u * (uint32_t)(fl >> 4))) * 2u;
 #pragma unroll
         for (int I = 0; I < 4; ++I) {
             if constexpr (PAIRED) {
 #pragma unroll
-                for (int np = 0; np < NP; ++np)
-                    gq[np][I] = buf_load16(rgt, ((r0 + 16 * I + l16) * (uint32_t)DV + col0 + 32 * np + pair_col(lq)) * 2u);
+                for (int np = 0; np < NP; ++np) gq[np][I] = buf_load16(rgt, vo + (uint32_t)(16 * I * DV + 32 * np) * 2u);
             } else {
 #pragma unroll
-                for (int nt = 0; nt < NT; ++nt)
-                    gpend[nt][I] = buf_load8(rgt, ((r0 + 16 * I + l16) * (uint32_t)DV + col0 + 16 * nt + 4 * lq) * 2u);
+                for (int nt = 0; nt < NT; ++nt) gpend[nt][I] = buf_load8(rgt, vo + (uint32_t)(16 * I * DV + 16 * nt) * 2u);
             }
         }
     };
-    // (4 KiB of lane-private 16-byte slots in the 5 KiB stage)
-    auto gate_to_stage = [&]() {
-#pragma unroll
-        for (int I = 0; I < 4; ++I) {
-            if constexpr (PAIRED) {
-#pragma unroll
-                for (int np = 0; np < NP; ++np) *reinterpret_cast<uint4*>(gstage + (I * NP + np) * 1024) = gq[np][I];
-            } else {
-#pragma unroll
-                for (int nt = 0; nt < NT; nt += 2)
-                    *reinterpret_cast<uint4*>(gstage + (I * NP + nt / 2) * 1024) =
-                        make_uint4(gpend[nt][I].x, gpend[nt][I].y, gpend[nt + 1][I].x, gpend[nt + 1][I].y);
-            }
-        }
-    };
-    auto gate_from_stage = [&]() {
-#pragma unroll
-        for (int I = 0; I < 4; ++I) {
-            if constexpr (PAIRED) {
-#pragma unroll
-                for (int np = 0; np < NP; ++np) gq[np][I] = *reinterpret_cast<const uint4*>(gstage + (I * NP + np) * 1024);
-            } else {
-#pragma unroll
-                for (int nt = 0; nt < NT; nt += 2) {
-                    const uint4 g = *reinterpret_cast<const uint4*>(gstage + (I * NP + nt / 2) * 1024);
-                    gpend[nt][I] = make_uint2(g.x, g.y);
-                    gpend[nt + 1][I] = make_uint2(g.z, g.w);
-                }
-            }
-        }
-    };
-    static_assert(!GATED || NT % 2 == 0, "gate slots hold two tiles");
     const float inv_dv = 1.f / (float)DV;
 
     f32x4 O[NT][4];
@@ -239,7 +221,6 @@ __device__ __forceinline__ void consumer(const ChunkLaunch& p, FusedSmem<DK, DV>
         }
         epoch_barrier();   // 1
         if (prev) {
-            if (GATED) gate_from_stage();
 #pragma unroll
             for (int I = 0; I < 4; ++I) {
                 const uint32_t row = (uint32_t)((c - 1) * kC + 16 * I + l16);
@@ -270,18 +251,17 @@ __device__ __forceinline__ void consumer(const ChunkLaunch& p, FusedSmem<DK, DV>
                 }
             }
         }
+        // V of chunk c into the stage (its wait also covers the o stores just issued: measured
+        // faster than staging V before the stores), the next V rows, the diagonal inverse
         if (cur) {
             vw.pin_inputs();
             vw.stage();
             load(c + 1);
             vw.diag_inverse();
-            load_gate(c);
         }
         epoch_barrier();   // 2
-        if (cur) {
-            vw.solve(U);
-            if (GATED) gate_to_stage();   // (the stage's V reads are done)
-        }
+        if (cur) vw.solve(U);
+        load_gate(c);
         epoch_barrier();   // 3
     }
     if (last && p.S_T) store_state<DK, DV, NT>(p.S_T + lane * DK * DVl, S, col0, lq, l16);

@@ -524,11 +524,12 @@ struct ChunkWave {
     // each, then the diagonal A_qk blocks. SPLIT: no diagonal A_kk work; the six pairs and the four
     // diagonal A_qk blocks spread over the four waves.
     __device__ __forceinline__ void gram(unsigned char* rec) {
-        if (SPLIT) {
-            if (w == 0) { gram_pair(sm, rec, 1, 0, l); gram_pair(sm, rec, 2, 0, l); }
-            if (w == 1) { gram_pair(sm, rec, 2, 1, l); gram_pair(sm, rec, 3, 0, l); }
-            if (w == 2) { gram_pair(sm, rec, 3, 1, l); diag_aqk_block(sm, rec, 0, l); diag_aqk_block(sm, rec, 1, l); }
-            if (w == 3) { gram_pair(sm, rec, 3, 2, l); diag_aqk_block(sm, rec, 2, l); diag_aqk_block(sm, rec, 3, l); }
+        if (SPLIT) {   // (each wave's own addresses, rebuilt per chunk)
+            const int fl = fresh_lane();
+            if (w == 0) { gram_pair(sm, rec, 1, 0, fl); gram_pair(sm, rec, 2, 0, fl); }
+            if (w == 1) { gram_pair(sm, rec, 2, 1, fl); gram_pair(sm, rec, 3, 0, fl); }
+            if (w == 2) { gram_pair(sm, rec, 3, 1, fl); diag_aqk_block(sm, rec, 0, fl); diag_aqk_block(sm, rec, 1, fl); }
+            if (w == 3) { gram_pair(sm, rec, 3, 2, fl); diag_aqk_block(sm, rec, 2, fl); diag_aqk_block(sm, rec, 3, fl); }
             return;
         }
         if (w == 0) {
@@ -595,22 +596,18 @@ struct ValueWave {
     static_assert(DV == 128 && Cfg::VPW == 2, "two value tiles per wave");
     IntraSmem<DK, DV>& sm;
     bf16_t* vst;      // this wave's V stage: 64 rows of LDVS elements
-    int vw, l, l16, lq;
-    uint32_t v_voff;
+    int vw;
     uint4 pv[4];      // V rows of the chunk being loaded
     i16x4 vacc[2][4]; // V rows 16I + 4lq + e, column 32 vw + 16j + l16
+    // (each phase derives its lane offsets from fresh_lane(): the wave runs beside the state step,
+    // whose registers leave none to hold them across the chunk loop)
 
-    __device__ __forceinline__ ValueWave(IntraSmem<DK, DV>& s, bf16_t* stage, int wave) : sm(s), vst(stage), vw(wave) {
-        l = threadIdx.x & 63;
-        l16 = l & 15;
-        lq = l >> 4;
-        v_voff = ((l / 4) * DV + 32 * vw + 8 * (l % 4)) * 2;
-    }
+    __device__ __forceinline__ ValueWave(IntraSmem<DK, DV>& s, bf16_t* stage, int wave) : sm(s), vst(stage), vw(wave) {}
     // rows row0 .. row0 + n - 1 of v (zeros from n on; n = 0 moves no data)
     __device__ __forceinline__ void load(const void* v, int64_t row0, uint32_t n) {
         const __amdgpu_buffer_rsrc_t rv = make_rsrc((const bf16_t*)v + row0 * DV, n * (DV * 2));
-        uint32_t vo = v_voff;
-        asm volatile("" : "+v"(vo));
+        const int l = fresh_lane();
+        const uint32_t vo = (uint32_t)(((l / 4) * DV + 32 * vw + 8 * (l % 4)) * 2);
 #pragma unroll
         for (int i = 0; i < 4; ++i) pv[i] = buf_load16(rv, vo + i * 16 * DV * 2);
     }
@@ -620,6 +617,7 @@ struct ValueWave {
     }
     // the loaded rows into accumulator layout through the stage
     __device__ __forceinline__ void stage() {
+        const int l = fresh_lane(), l16 = l & 15, lq = l >> 4;
 #pragma unroll
         for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(&vst[(i * 16 + l / 4) * LDVS + 8 * (l % 4)]) = pv[i];
         wave_lds_sync();
@@ -631,13 +629,14 @@ struct ValueWave {
     }
     // diagonal block vw of A_kk and the inverse of I + A_kk,vw (the lanes of row group lq = 0 store it)
     __device__ __forceinline__ void diag_inverse() {
+        const int l = fresh_lane(), l16 = l & 15, lq = l >> 4;
         diag_akk_block(sm, vw, l);
         wave_lds_sync();
         invert_row(sm, vw, l16, lq == 0);
     }
     // U of this wave's two tiles, in the record's rounding
     __device__ __forceinline__ void solve(i16x4 (&U)[2][4]) {
-        const SolveOps ops = solve_ops(sm, l);
+        const SolveOps ops = solve_ops(sm, fresh_lane());
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             f32x4 X[4];
