@@ -134,11 +134,15 @@ Geometry varlen_geometry(const kda_varlen_desc* d, int64_t cus) {
     const int64_t max_len = d->max_len < d->T ? d->max_len : d->T;
     const int64_t max_chunks = ceil_div(max_len, kChunk);
     const int64_t slots = d->T / kChunk + d->N;
-    // The split is planned as if every lane had max_chunks chunks: with few long sequences a
-    // split would shorten their chain, but the scan and the summary pass still run over every
-    // lane (measured: 12 sequences x 32 heads, 8192 tokens, longest 2500: 0.31 ms unsplit,
-    // 0.39 ms in 3 segments).
-    Geometry g{d->N * d->H, max_chunks, d->H * slots, d->dk, d->dv, d->in_dtype, d->segments, slots, d->N * d->H, cus};
+    // The split is planned for the lanes that can have max_chunks chunks: at most T / max_len
+    // sequences reach max_len (a shorter lane has fewer live segments, and the launches' workgroups
+    // of its dead ones return at once). Measured on 12 sequences x 32 heads, 8192 tokens, longest
+    // 2500 (96 such lanes: 2 segments): 0.263 ms unsplit, 0.237 ms in 2 segments, 0.242 in 3.
+    int64_t can_be_long = max_len > 0 ? d->T / max_len : d->N;
+    if (can_be_long < 1) can_be_long = 1;
+    if (can_be_long > d->N) can_be_long = d->N;
+    Geometry g{d->N * d->H, max_chunks, d->H * slots, d->dk, d->dv, d->in_dtype, d->segments, slots, can_be_long * d->H,
+               cus};
     g.state_pass = d->state_pass;
     g.fused_ok = d->dk == 128 && d->dv == 128;
     return g;

@@ -75,8 +75,13 @@ static int64_t auto_segments(int64_t lanes, int64_t nchunks, int64_t cus, double
             const double empty = 4.5;   // a launch whose workgroups all return at once
             const double scan = n > 2 ? 16.0 + 2.0 * (double)(n - 2) : 0.0;
             fast[n] = pass_us(cps + w, lanes * n, 0, cus) + (n > 2 ? 3.0 : 1.0) * empty;
-            // (segments 1 .. n - 2 compute their pairs in the first launch, beside segment 0)
-            fallback[n] = pass_us(cps + w, lanes, lanes * (n - 1), cus) + empty + scan + pass_us(cps, lanes * (n - 1), 0, cus);
+            // (segments 1 .. n - 2 compute their pairs in the first launch, beside segment 0; with
+            // n = 2 the last segment needs no pair and its workgroups stop after the window, so
+            // the fallback is segment 0, then segment 1 from its exit state)
+            if (n == 2)
+                fallback[n] = pass_us(cps, lanes, lanes, cus) + empty + pass_us(cps, lanes, 0, cus);
+            else
+                fallback[n] = pass_us(cps + w, lanes, lanes * (n - 1), cus) + empty + scan + pass_us(cps, lanes * (n - 1), 0, cus);
         }
         valid[n] = true;
         if (n == 1 || fallback[n] < best_fallback) best_fallback = fallback[n];
@@ -144,7 +149,7 @@ Plan make_plan(const Geometry& g) {
         else nseg = auto_segments(g.long_lanes, nchunks, cus, &two_us);
         if (g.fused_ok && g.state_pass != 1) {
             const int64_t nf = fused_segments(g.lanes, nchunks, cus, g.segments, &fused_us);
-            if (g.state_pass == 0) two_us = intra_us(g.slots, cus) + two_kernel_state_us(g.lanes, nchunks, cus, g.segments);
+            if (g.state_pass == 0) two_us = intra_us(g.slots, cus) + two_kernel_state_us(g.long_lanes, nchunks, cus, g.segments);
             if (g.state_pass == 2 || fused_us < two_us) {
                 p.fused = true;
                 nseg = nf;

@@ -240,6 +240,16 @@ static int check_varlen() {
     g.g_min = 0.f;
     CHECK(call(&d, P(8 * GB), P(9 * GB), P(10 * GB), &g, P(11 * GB), need, nullptr) == KDA_ERR_INVALID_ARG);
     g.g_min = -5.f;
+    // the plan of a packed batch splits for the lanes that can be long: 12 sequences x 32 heads,
+    // 8192 tokens, longest 2500 (40 chunks; at most 3 sequences that long): 2 segments
+    {
+        kda_varlen_desc pk = d;
+        pk.N = 12; pk.H = 32; pk.T = 8192; pk.max_len = 2500; pk.ckpt_every = 512;
+        const size_t needk = kda_chunk_fwd_varlen_workspace_bytes(&pk);
+        reset();
+        CHECK(call(&pk, P(8 * GB), P(9 * GB), P(10 * GB), nullptr, P(11 * GB), needk) == KDA_OK);
+        CHECK(g_fused == 0 && g_inter >= 1 && g_inter_seq[0].nseg == 2 && g_inter_seq[0].chunks_per_seg == 20);
+    }
     // the fused kernel on a packed batch (3 segments of 4 chunks): the slot table, the list of the
     // windows' slots and their records, the window launch, the fused kernel, the lane list, every
     // record when a lane falls back, then the two-kernel passes skipping the fused lanes
