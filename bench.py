@@ -63,7 +63,7 @@ def decode_alg(N, H, d, in_bytes=2, out_bytes=2):
 # profile summaries; a figure is used only while the kernel sources it was taken on are unchanged.
 TRAFFIC_FILES = [os.path.join(ROOT, "profiles", f) for f in ("hbm_traffic_prefill_1m.md",
                                                              "hbm_traffic_prefill_8k_64k_packed.md")]
-MFMA_FILES = [os.path.join(ROOT, "profiles", "mfma_counters_prefill_1m.md")]
+MFMA_FILES = [os.path.join(ROOT, "profiles", f) for f in ("mfma_counters_prefill_1m.md", "mfma_counters_backward_8k.md")]
 PREFILL_SOURCES = ["kda_intra.hip", "kda_intra_chunk.h", "kda_inter.hip", "kda_step.h", "kda_fused.hip", "kda_scan.hip",
                    "kda_record.h", "kda_mfma.h", "kda_device.h", "kda_plan.h", "kda_plan.cpp"]
 DECODE_SOURCES = ["kda_decode.hip", "kda_device.h"]
@@ -332,11 +332,17 @@ def main():
         # bytes: the forward's inputs, dO in, fp32 gradients of q, k, v, log_alpha, beta out, states
         bby = bw.B * bw.H * (bw.T * (4 * bw.d * 2 + 2 + bw.d * 2 + 4 * bw.d * 4 + 4) + 3 * bw.d * bw.d * 4)
         bgbs = bby / (bms * 1e-3) / 1e9
+        # the three backward kernels run on the fp32 matrix cores: their executed fp32 MFMA flops per
+        # call (rocprofv3 counters, profiles/) against the fp32 peak
+        f32 = measured_traffic("call", bw.name + BWD_SUFFIX, BACKWARD_SOURCES, what="mfma_fp32_flops", paths=MFMA_FILES)
         bwd = {"workload": bw.name + BWD_SUFFIX, "metric": "KDA backward tokens/s",
                "value": bw.B * bw.T / (bms * 1e-3), "unit": "tokens/s", "ms_per_step": bms, "steps": nb,
                "roofline": {"bound": "hbm", "achieved": bgbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                             "frac": bgbs / HBM_PEAK_GBS,
                             "traffic": measured_traffic("call", bw.name + BWD_SUFFIX, BACKWARD_SOURCES)},
+               "mfma_fp32": None if f32 is None else {
+                   "executed_tflops_counter": f32 / (bms * 1e-3) / 1e12, "peak_tflops": FP32_PEAK_TFLOPS,
+                   "frac": f32 / (bms * 1e-3) / 1e12 / FP32_PEAK_TFLOPS, "executed_flops_per_call": f32},
                "alg_bytes_per_call": bby, "workspace_bytes": int(bws.numel())}
         del q, k, v, la, beta, S0, dO, dST, bws
         torch.cuda.empty_cache()
