@@ -339,6 +339,20 @@ struct ChunkWave {
     // the chunk's valid rows feed the fused decay prologue only (padded rows must not decay there).
     template <bool DEFER>
     __device__ __forceinline__ void decay(unsigned char* rec, float eA, float g_min, uint32_t nrows) {
+        if constexpr (DK < 128) {
+            // dk = 64: the lane's offsets rebuilt for this phase (the compiler otherwise holds a
+            // dozen LDS addresses across the chunk loop and spills them, each reload waiting for
+            // the prefetch)
+            const int sl = l, sl16 = l16, slq = lq;
+            l = fresh_lane(); l16 = l & 15; lq = l >> 4;
+            decay_body<DEFER>(rec, eA, g_min, nrows);
+            l = sl; l16 = sl16; lq = slq;
+        } else {
+            decay_body<DEFER>(rec, eA, g_min, nrows);
+        }
+    }
+    template <bool DEFER>
+    __device__ __forceinline__ void decay_body(unsigned char* rec, float eA, float g_min, uint32_t nrows) {
         unsigned char* reg = region();
         bf16_t* stA = reinterpret_cast<bf16_t*>(reg);                    // g, then K- (token-major)
         unsigned char* stB = reg + Cfg::STAGE_A;                         // v, then blocks
