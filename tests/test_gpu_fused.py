@@ -338,3 +338,30 @@ def test_fused_packed_gating(odt):
     N = len(lens)
     es = rel_l2_per_lane(host32(S_T).reshape(N * H, -1), ref[1].reshape(N * H, -1))
     assert es <= TOL_S[BF16]
+
+
+@pytest.mark.parametrize("segments", [2, 3])
+def test_fused_packed_workload_sampled_heads(segments):
+    """The packed 8K workload (12 sequences of 27 to 2500 tokens, 32 heads, checkpoints every 512)
+    forced onto the fused path: bit-identical to the two-kernel path with the same split, and the
+    oracle checks 3 heads of every sequence."""
+    w = synth.PACKED_BF16_8K
+    lens = synth.PACKED_BF16_8K_LENS
+    say("fused packed workload: segments=%d" % segments)
+    q, k, v, la, beta, cu, S0 = synth.packed_inputs(lens, w.H, w.d, w.d, BF16, device=DEV)
+    outs = {sp: kda.chunk_fwd_varlen(q, k, v, la, beta, cu, None, max_len=max(lens), ckpt_every=512, segments=segments,
+                                     state_pass=sp) for sp in (FUSED, TWO)}
+    torch.cuda.synchronize()
+    _same_packed("fused packed workload", outs[FUSED], outs[TWO])
+    o, S_T, ck, offs = outs[FUSED]
+    heads = [0, 13, 31]
+    sub = lambda x: host32(x[heads])
+    ref = native.kda_varlen(sub(q), sub(k), sub(v), sub(la), sub(beta), cu.cpu().numpy(), None, ckpt_every=512)
+    N = len(lens)
+    assert_close("fused packed workload (3 heads)", BF16, host32(o[heads]), ref[0],
+                 host32(S_T[:, heads]).reshape(N * 3, w.d, w.d), ref[1].reshape(N * 3, w.d, w.d))
+    assert np.array_equal(offs.cpu().numpy(), np.asarray(ref[3]))
+    n = int(ref[3][-1])
+    es = rel_l2_per_lane(host32(ck[:n][:, heads]).reshape(n * 3, -1), ref[2].reshape(n * 3, -1))
+    say("fused packed workload: %d checkpoints x 3 heads, relL2 = %.3e" % (n, es))
+    assert es <= TOL_S[BF16]
