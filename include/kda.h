@@ -197,7 +197,10 @@ typedef struct kda_varlen_desc {
  * The same records, affine pairs, entry states and flags as kda_chunk_fwd's workspace; a packed
  * batch lays out records in T/64 + N chunk slots per head (sequence s's chunk c in slot
  * cu_seqlens[s]/64 + s + c, which never collide whatever the lengths) and adds a table of
- * 8 bytes per slot (before the flags). */
+ * 8 bytes per slot (before the flags). A packed batch on the fused kernel with more than one
+ * segment also lists the record slots of the windows (4 bytes per lane, boundary and window
+ * chunk, then the count; at the end). The segments are planned for the longest sequence
+ * (max_len); a shorter sequence ends in an earlier segment, which finishes it. */
 size_t kda_chunk_fwd_varlen_workspace_bytes(const kda_varlen_desc* desc);
 
 /*
