@@ -110,6 +110,7 @@ struct IntraCfg {
     static constexpr int REGION = STAGE_A + STAGE_B; // after the Gram: W^T stage
     static_assert(kC * LDVS * 2 <= STAGE_B, "v stage fits");
     static_assert(32 * LDW * 2 <= REGION, "W^T stage fits");
+    static_assert(LDG * 2 >= 64 + 16 && kC >= 24, "the decay's P table fits the g stage padding");
 };
 
 template <int DK, int DV>
@@ -476,26 +477,31 @@ struct ChunkWave {
                     *reinterpret_cast<uint2*>(&stA[(16 * I + l16) * LDG + 16 * h + 4 * lq]) =
                         __builtin_bit_cast(uint2, cvt4(ob));
                 }
-                // P_I of channel 32w + 16h + l16 (the accumulator-layout column of the solve):
-                // P_I of local channel 16h + 4lq' + r' sits in every lane of row lq'
-                {
-                    const int src = ((l16 >> 2) << 4) * 4;   // byte address of lane 16 (l16 / 4)
-                    pcol[h][0] = 1.f;
+                // P_I (I > 0) of local channel 16h + 4lq + r (every lane of row lq holds it), fp32,
+                // into the g stage's padding columns, stage row (I - 1) 8 + 4h + lq: the solve's
+                // accumulator layout wants it for channel 16h + l16, read back after the sync below
+                // (a cross-row permute here would wait for this phase's LDS writes)
+                if (l16 == 0) {
 #pragma unroll
-                    for (int I = 1; I < 4; ++I) {
-                        float v[4];
-#pragma unroll
-                        for (int r = 0; r < 4; ++r)
-                            v[r] = __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(P[I][r])));
-                        const int rr = l16 & 3;
-                        pcol[h][I] = rr == 0 ? v[0] : (rr == 1 ? v[1] : (rr == 2 ? v[2] : v[3]));
-                    }
+                    for (int I = 1; I < 4; ++I)
+                        *reinterpret_cast<f32x4*>(reinterpret_cast<unsigned char*>(stA) +
+                                                  ((I - 1) * 8 + 4 * h + lq) * (LDG * 2) + 64) = P[I];
                 }
                 // one 16-channel tile at a time: interleaving the two would double the live set
                 __builtin_amdgcn_sched_barrier(0);
             }
             wave_lds_sync();
             if (!DEFER) store_kbar(rec);
+            // P_I of the lane's column channel 32w + 16h + l16 (P_0 = 1), from the stage padding
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                pcol[h][0] = 1.f;
+#pragma unroll
+                for (int I = 1; I < 4; ++I)
+                    pcol[h][I] = *reinterpret_cast<const float*>(reinterpret_cast<const unsigned char*>(stA) +
+                                                                 ((I - 1) * 8 + 4 * h + (l16 >> 2)) * (LDG * 2) + 64 +
+                                                                 (l16 & 3) * 4);
+            }
             // K~ in accumulator layout from its own blocks: the 8-byte chunk addressed by lane
             // (lq, l16) is K~[16I + 4lq + l16/4][32w + 16h + 4(l16%4) ..], i.e. block lane
             // (l16 % 4, 4lq + l16/4), half h.
