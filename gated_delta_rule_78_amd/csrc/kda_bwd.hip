@@ -190,7 +190,8 @@ __global__ __launch_bounds__(kTP) void bwd_prep_kernel(BwdArgs a) {
     float* sc = a.prep + (int64_t)blockIdx.x * L::PREP;
     const int tid = threadIdx.x;
     // K, Q, log_alpha and V of the chunk in one round trip; V stays in registers until its LDS
-    // place is free
+    // place is free (a persistent grid that loads the next chunk's rows during the current one's
+    // last phase was 3 % slower: its loop holds twice the registers)
     InTile<kC, DK, kTP, bf16_t> tk, tq, tg;
     InTile<kC, DV, kTP, bf16_t> tv;
     tk.load((const bf16_t*)a.k + row0 * DK, DK, nrows);
@@ -220,48 +221,54 @@ __global__ __launch_bounds__(kTP) void bwd_prep_kernel(BwdArgs a) {
         const int i = tid >> 3;
         for (int j = (i & ~15) + 16 + (tid & 7); j < kC; j += 8) sc[L::AQK + i * kC + j] = 0.f;
     }
-    {   // 16 x 16 blocks (I, J), I >= J, on the fp32 MFMA: the six off-diagonal blocks on waves 0 .. 5,
-        // the four diagonal blocks two each on waves 6 and 7. Inside a diagonal block the second
-        // factor exp(G_r - G_j) is >= 1 but at most e^{15 * 5}, far inside the fp32 range; the
-        // entries above the diagonal (whose product is not bounded) are masked out.
-        const int wv = tid >> 6, lr = tid & 15, lg = (tid >> 4) & 3;
-        const int njobs = wv < 6 ? 1 : 2;
-        for (int jn = 0; jn < njobs; ++jn) {
-            int I, J;
-            if (wv < 6) { I = wv < 1 ? 1 : (wv < 3 ? 2 : 3); J = wv - (I * (I - 1)) / 2; }
-            else { I = 2 * (wv - 6) + jn; J = I; }
-            const int r = 16 * I, ia = r + lr, jb = 16 * J + lr;
-            f32x4 ckk = kZero4f(), cqk = kZero4f();
-            for (int kb = 0; kb < DK; kb += 16) {
-                const int k0 = kb + 4 * lg;
-                const f32x4 ka = *reinterpret_cast<const f32x4*>(&sm.K[ia][k0]);
-                const f32x4 qa = *reinterpret_cast<const f32x4*>(&sm.Q[ia][k0]);
-                const f32x4 ga = *reinterpret_cast<const f32x4*>(&sm.G[ia][k0]);
-                const f32x4 gr = *reinterpret_cast<const f32x4*>(&sm.G[r][k0]);
-                const f32x4 kbv = *reinterpret_cast<const f32x4*>(&sm.K[jb][k0]);
-                const f32x4 gbv = *reinterpret_cast<const f32x4*>(&sm.G[jb][k0]);
+    const int wv = tid >> 6, lr = tid & 15, lg = (tid >> 4) & 3;
+    // One 16 x 16 block (I, J), I >= J, of A_kk and A_qk on the fp32 MFMA (one wave). Inside a
+    // diagonal block the second factor exp(G_r - G_j) is >= 1 but at most e^{15 * 5}, far inside
+    // the fp32 range; the entries above the diagonal (whose product is not bounded) are masked out.
+    auto gram_block = [&](int I, int J) {
+        const int r = 16 * I, ia = r + lr, jb = 16 * J + lr;
+        f32x4 ckk = kZero4f(), cqk = kZero4f();
+        for (int kb = 0; kb < DK; kb += 16) {
+            const int k0 = kb + 4 * lg;
+            const f32x4 ka = *reinterpret_cast<const f32x4*>(&sm.K[ia][k0]);
+            const f32x4 qa = *reinterpret_cast<const f32x4*>(&sm.Q[ia][k0]);
+            const f32x4 ga = *reinterpret_cast<const f32x4*>(&sm.G[ia][k0]);
+            const f32x4 gr = *reinterpret_cast<const f32x4*>(&sm.G[r][k0]);
+            const f32x4 kbv = *reinterpret_cast<const f32x4*>(&sm.K[jb][k0]);
+            const f32x4 gbv = *reinterpret_cast<const f32x4*>(&sm.G[jb][k0]);
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const float fa = fexp(ga[q] - gr[q]), fb = kbv[q] * fexp(gr[q] - gbv[q]);
-                    ckk = mfma4(ka[q] * fa, fb, ckk);
-                    cqk = mfma4(qa[q] * fa, fb, cqk);
-                }
-            }
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int row = r + 4 * lg + e, col = 16 * J + lr;
-                sm.A[row][col] = col < row ? sm.beta[row] * ckk[e] : 0.f;   // always true off the diagonal
-                sc[L::AQK + row * kC + col] = col <= row ? cqk[e] : 0.f;
+            for (int q = 0; q < 4; ++q) {
+                const float fa = fexp(ga[q] - gr[q]), fb = kbv[q] * fexp(gr[q] - gbv[q]);
+                ckk = mfma4(ka[q] * fa, fb, ckk);
+                cqk = mfma4(qa[q] * fa, fb, cqk);
             }
         }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int row = r + 4 * lg + e, col = 16 * J + lr;
+            sm.A[row][col] = col < row ? sm.beta[row] * ckk[e] : 0.f;   // always true off the diagonal
+            sc[L::AQK + row * kC + col] = col <= row ? cqk[e] : 0.f;
+        }
+    };
+    // One block per wave: the six off-diagonal blocks on waves 0 .. 5, diagonal blocks 0 and 1 on
+    // waves 6 and 7. Diagonal blocks 2 and 3 go to waves 2 and 3 in the next phase, right before
+    // they invert them (two blocks on one wave here made that wave the phase's critical path).
+    if (wv < 6) {
+        const int I = wv < 1 ? 1 : (wv < 3 ? 2 : 3);
+        gram_block(I, wv - (I * (I - 1)) / 2);
+    } else {
+        gram_block(wv - 6, wv - 6);
     }
     lds_barrier();
     // T = (I + A_kk)^{-1} (unit lower triangular) by 16 x 16 blocks: waves 0-3 invert the diagonal
     // blocks (one column per lane in registers, rows in order) while waves 4-7 write Q~, K- and
     // gamma; then block forward substitution T_IJ = -T_II sum_{J <= K < I} A_IK T_KJ, one level
     // of I - J at a time, on the fp32 MFMA.
-    const int wv = tid >> 6, lr = tid & 15, lg = (tid >> 4) & 3;
     if (wv < 4) {
+        if (wv >= 2) {   // this wave's diagonal block of A_kk and A_qk first
+            gram_block(wv, wv);
+            wave_lds_sync();
+        }
         const int o = 16 * wv, j = lr;
         float col[16];
 #pragma unroll
@@ -276,11 +283,21 @@ __global__ __launch_bounds__(kTP) void bwd_prep_kernel(BwdArgs a) {
             for (int i = 0; i < 16; ++i) sm.T[o + i][o + j] = col[i];
         for (int e = tid & 63; e < 16 * (kC - o - 16); e += 64) sm.T[o + e / (kC - o - 16)][o + 16 + e % (kC - o - 16)] = 0.f;
     } else {
-        // Q~ = Q e^G, K- = K e^{G_63 - G}, gamma
-        for (int e = tid - 256; e < kC * DK; e += kTP - 256) {
-            const int t = e / DK, ch = e % DK;
-            sc[L::QT + e] = sm.Q[t][ch] * fexp(sm.G[t][ch]);
-            sc[L::KB + e] = sm.K[t][ch] * fexp(sm.G[kC - 1][ch] - sm.G[t][ch]);
+        // Q~ = Q e^G, K- = K e^{G_63 - G}, gamma: four channels per thread and step
+        for (int e = tid - 256; e < kC * DK / 4; e += kTP - 256) {
+            const int t = e / (DK / 4), ch = 4 * (e % (DK / 4));
+            const f32x4 q4 = *reinterpret_cast<const f32x4*>(&sm.Q[t][ch]);
+            const f32x4 k4 = *reinterpret_cast<const f32x4*>(&sm.K[t][ch]);
+            const f32x4 g4 = *reinterpret_cast<const f32x4*>(&sm.G[t][ch]);
+            const f32x4 gl = *reinterpret_cast<const f32x4*>(&sm.G[kC - 1][ch]);
+            f32x4 qt, kb;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                qt[i] = q4[i] * fexp(g4[i]);
+                kb[i] = k4[i] * fexp(gl[i] - g4[i]);
+            }
+            *reinterpret_cast<f32x4*>(sc + L::QT + t * DK + ch) = qt;
+            *reinterpret_cast<f32x4*>(sc + L::KB + t * DK + ch) = kb;
         }
         for (int ch = tid - 256; ch < DK; ch += kTP - 256) sc[L::GAM + ch] = fexp(sm.G[kC - 1][ch]);
     }
@@ -313,41 +330,55 @@ __global__ __launch_bounds__(kTP) void bwd_prep_kernel(BwdArgs a) {
     // right-hand sides in place: K <- Diag(beta) K e^G, and Diag(beta) V over Q (or its own
     // array when dv > dk), rows of DV floats
     float* Vs = DV <= DK ? &sm.Q[0][0] : &sm.Vx[0][0];
-    for (int e = tid; e < kC * DK; e += kTP) {
-        const int t = e / DK, ch = e % DK;
-        sm.K[t][ch] *= sm.beta[t] * fexp(sm.G[t][ch]);
+    for (int e = tid; e < kC * DK / 4; e += kTP) {
+        const int t = e / (DK / 4), ch = 4 * (e % (DK / 4));
+        f32x4& k4 = *reinterpret_cast<f32x4*>(&sm.K[t][ch]);
+        const f32x4 g4 = *reinterpret_cast<const f32x4*>(&sm.G[t][ch]);
+        const float b = sm.beta[t];
+        f32x4 x = k4;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[i] *= b * fexp(g4[i]);
+        k4 = x;
     }
     tv.store(Vs, DV, sm.beta);
-    for (int e = tid; e < kC * kC; e += kTP) sc[L::T + e] = sm.T[e / kC][e % kC];
+    for (int e = tid; e < kC * kC / 4; e += kTP) {
+        const int t = e / (kC / 4), m = 4 * (e % (kC / 4));
+        *reinterpret_cast<f32x4*>(sc + L::T + t * kC + m) = *reinterpret_cast<const f32x4*>(&sm.T[t][m]);
+    }
     lds_barrier();
-    // W = T (beta K e^G), U = T (beta V) as 16x16x4 MFMA tiles: wave w takes rows 16 (w mod 4) and
-    // half of the columns of each (T[t][m] = 0 past the diagonal block, so m stops there)
+    // W = T (beta K e^G), U = T (beta V) as 16x16x4 MFMA tiles. Row block b costs b + 1 steps
+    // (T[t][m] = 0 past the diagonal block, so m stops there): wave w takes row blocks {0, 3}
+    // (w even) or {1, 2} (w odd), five steps either way, and a quarter of the columns of W and U.
     {
-        constexpr int NWT = DK / 32, NUT = DV / 32;
-        const int rb = 16 * (wv & 3), cw = (DK / 2) * (wv >> 2), cu = (DV / 2) * (wv >> 2);
-        f32x4 aw[NWT], au[NUT];
+        constexpr int NWT = DK / 64, NUT = DV / 64;
+        const int cw = (DK / 4) * (wv >> 1), cu = (DV / 4) * (wv >> 1);
 #pragma unroll
-        for (int ct = 0; ct < NWT; ++ct) aw[ct] = kZero4f();
+        for (int h = 0; h < 2; ++h) {
+            const int rb = 16 * ((wv & 1) ? 1 + h : 3 * h);
+            f32x4 aw[NWT], au[NUT];
 #pragma unroll
-        for (int ct = 0; ct < NUT; ++ct) au[ct] = kZero4f();
-        for (int kb = 0; kb <= rb; kb += 16) {
-            const f32x4 x = *reinterpret_cast<const f32x4*>(&sm.T[rb + lr][kb + 4 * lg]);
+            for (int ct = 0; ct < NWT; ++ct) aw[ct] = kZero4f();
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int m = kb + 4 * lg + q;
+            for (int ct = 0; ct < NUT; ++ct) au[ct] = kZero4f();
+            for (int kb = 0; kb <= rb; kb += 16) {
+                const f32x4 x = *reinterpret_cast<const f32x4*>(&sm.T[rb + lr][kb + 4 * lg]);
 #pragma unroll
-                for (int ct = 0; ct < NWT; ++ct) aw[ct] = mfma4(x[q], sm.K[m][cw + 16 * ct + lr], aw[ct]);
+                for (int q = 0; q < 4; ++q) {
+                    const int m = kb + 4 * lg + q;
 #pragma unroll
-                for (int ct = 0; ct < NUT; ++ct) au[ct] = mfma4(x[q], Vs[m * DV + cu + 16 * ct + lr], au[ct]);
+                    for (int ct = 0; ct < NWT; ++ct) aw[ct] = mfma4(x[q], sm.K[m][cw + 16 * ct + lr], aw[ct]);
+#pragma unroll
+                    for (int ct = 0; ct < NUT; ++ct) au[ct] = mfma4(x[q], Vs[m * DV + cu + 16 * ct + lr], au[ct]);
+                }
             }
-        }
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int t = rb + 4 * lg + e;
+            for (int e = 0; e < 4; ++e) {
+                const int t = rb + 4 * lg + e;
 #pragma unroll
-            for (int ct = 0; ct < NWT; ++ct) sc[L::W + t * DK + cw + 16 * ct + lr] = aw[ct][e];
+                for (int ct = 0; ct < NWT; ++ct) sc[L::W + t * DK + cw + 16 * ct + lr] = aw[ct][e];
 #pragma unroll
-            for (int ct = 0; ct < NUT; ++ct) sc[L::U + t * DV + cu + 16 * ct + lr] = au[ct][e];
+                for (int ct = 0; ct < NUT; ++ct) sc[L::U + t * DV + cu + 16 * ct + lr] = au[ct][e];
+            }
         }
     }
 }
@@ -517,8 +548,10 @@ __global__ __launch_bounds__(kT) void bwd_state_kernel(BwdArgs a) {
                 for (int i = 0; i < 4; ++i)
                     gst[(gr0 + 16 * rt + 4 * lg + i) * DV + j0 + 16 * ct + lr] = gx[rt][ct][i];
         // the next chunk's operands travel while this one computes, in three parts: a quarter before
-        // barrier B, a quarter after the dV~ products, half after the Gx products (8K backward:
-        // 2.195 ms; thirds 2.224, an eighth / eighth / rest 2.293, nothing / quarter / rest 2.263)
+        // barrier B, a quarter after the dV~ products, half after the first of the four blocks of
+        // the Gx products (8K backward: 2.134 ms; half after all of them 2.150, half before them
+        // 2.170, a quarter before and a quarter after 2.159; thirds, an eighth / eighth / rest and
+        // nothing / quarter / rest were slower still)
         constexpr int P1 = F::NLD / 4, P2 = F::NLD / 2;
         const float* nsc = a.prep + (lane * a.nchunks + c - 1) * L::PREP;
         const int64_t norow = lane * a.T + (c - 1) * kC;
@@ -569,8 +602,10 @@ __global__ __launch_bounds__(kT) void bwd_state_kernel(BwdArgs a) {
 #pragma unroll
             for (int ct = 0; ct < CT; ++ct) gx[rt][ct] *= g4;
         }
+#pragma unroll
         for (int kb = 0; kb < kC; kb += 16) {
             f32x4 xq[RT], xw[RT];
+            if (kb == 16 && c > 0) f.template load_part<L, P2, F::NLD>(nsc, dO, norow, nrows_next, j0, DV);
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt) {
 #pragma unroll
@@ -595,7 +630,6 @@ __global__ __launch_bounds__(kT) void bwd_state_kernel(BwdArgs a) {
                     for (int ct = 0; ct < CT; ++ct) gx[rt][ct] = mfma4(xw[rt][q], v[ct][q], gx[rt][ct]);
                 }
         }
-        if (c > 0) f.template load_part<L, P2, F::NLD>(nsc, dO, norow, nrows_next, j0, DV);
         put_gxt();   // nothing reads Gx^T between the dV~ products above and the next chunk's
     }
     if (a.dS0)
