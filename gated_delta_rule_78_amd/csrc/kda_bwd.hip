@@ -699,7 +699,12 @@ __global__ __launch_bounds__(kTG) void bwd_grad_kernel(BwdArgs a) {
     const int t = tid / NGR;                 // row of this thread in the (row, group) tiles
     const int gi = tid % NGR;
     const int c0 = gi * CG;                  // its channels
-    if (tid < kC) beta[tid] = tid < nrows ? ldin((const bf16_t*)a.beta, row0 + tid) : 0.f;
+    // beta of the chunk's rows, loaded ahead of the first tiles and written to LDS after them by
+    // every thread (thread tid writes row tid mod 64; the eight writers of a row store the same
+    // value). A store under a branch would take the load into the branch with it, where the load
+    // is waited for at once, ahead of the tile loads.
+    const int brow = tid & (kC - 1);
+    const bf16_t beta_raw = ((const bf16_t*)a.beta)[row0 + (brow < nrows ? brow : nrows - 1)];
 
     // ---------------- phase 1: V~ = U - W S, and the products over the value columns ----------
     // fp32 16x16x4 MFMA tiles (lane l = lr + 16 lg supplies row / column lr at k = lg; the k
@@ -746,6 +751,7 @@ __global__ __launch_bounds__(kTG) void bwd_grad_kernel(BwdArgs a) {
     tdo.load(dO + row0 * DV, DV, nrows);
     load_uin(0);
     tw.store(sW, LK);
+    beta[brow] = brow < nrows ? bf16_bits_to_f32(beta_raw) : 0.f;
     // the two halves are written out (no loop) so that the registers a prefetch fills are the ones
     // the next half reads, with no copies that would wait for the loads
     auto half = [&](auto hc) {
@@ -871,6 +877,16 @@ __global__ __launch_bounds__(kTG) void bwd_grad_kernel(BwdArgs a) {
     for (int ct = 0; ct < NCT; ++ct) mxk[ct] = kZero4f();
 #pragma unroll
     for (int ct = 0; ct < NXV; ++ct) mxv[ct] = kZero4f();
+    // V of this wave's dX_V entries, for dbeta: loaded before the products (rows past the end read
+    // the last row; no branch, so nothing waits for them until they are used)
+    bf16_t vdb[NXV][4];
+#pragma unroll
+    for (int ct = 0; ct < NXV; ++ct)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = t0 + 4 * lg + i, rr = r < nrows ? r : nrows - 1;
+            vdb[ct][i] = ((const bf16_t*)a.v)[(row0 + rr) * DV + xb + 16 * ct + lr];
+        }
     for (int kb = t0; kb < kC; kb += 16) {   // T^T[t][m] = 0 for m < t
         const f32x4 x = *reinterpret_cast<const f32x4*>(sTT + (t0 + lr) * LA + kb + 4 * lg);
         f32x4 yw[NCT], yv[NXV];
@@ -896,7 +912,7 @@ __global__ __launch_bounds__(kTG) void bwd_grad_kernel(BwdArgs a) {
                 const int r = t0 + 4 * lg + i, j = xb + 16 * ct + lr;
                 if (r < nrows) {
                     a.dv_[(row0 + r) * DV + j] = beta[r] * mxv[ct][i];
-                    pb[i] += mxv[ct][i] * ldin((const bf16_t*)a.v, (row0 + r) * DV + j);
+                    pb[i] += mxv[ct][i] * bf16_bits_to_f32(vdb[ct][i]);
                 }
             }
 #pragma unroll
@@ -933,37 +949,54 @@ __global__ __launch_bounds__(kTG) void bwd_grad_kernel(BwdArgs a) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) xk[u + e] = x4[e];
     }
-    {   // dA_kk tiles (rows t0 .., columns sb + 16 ct) = -(dX_K W^T + dX_V U^T), kept for j < i
-        f32x4 akk[2] = {kZero4f(), kZero4f()};
+    {   // dA_kk = -(dX_K W^T + dX_V U^T) below the diagonal: the ten 16 x 16 tiles (R, C), C <= R,
+        // as tile codes 4 R + C, one per wave and a second on waves 0 and 1 (three tiles per SIMD
+        // at most: waves w and w + 4 share one); waves 2-7 also zero one tile above the diagonal
+        // each. The tiles of a wave run interleaved, each one accumulation chain in step order.
+        const int codeA = (int)((0xEC84D950u >> (4 * wv)) & 15u), codeB = (int)((0xAFu >> (4 * wv)) & 15u);
+        const bool two = wv < 2;
+        const int rA = 16 * (codeA >> 2), cA = 16 * (codeA & 3), rB = 16 * (codeB >> 2), cB = 16 * (codeB & 3);
+        f32x4 akA = kZero4f(), akB = kZero4f();
 #pragma unroll 2
         for (int kb = 0; kb < DK; kb += 16) {
-            const f32x4 x = *reinterpret_cast<const f32x4*>(sXK + (t0 + lr) * LK + kb + 4 * lg);
-            const f32x4 y0 = *reinterpret_cast<const f32x4*>(sW2 + (sb + lr) * LK + kb + 4 * lg);
-            const f32x4 y1 = *reinterpret_cast<const f32x4*>(sW2 + (sb + 16 + lr) * LK + kb + 4 * lg);
+            const f32x4 x = *reinterpret_cast<const f32x4*>(sXK + (rA + lr) * LK + kb + 4 * lg);
+            const f32x4 y = *reinterpret_cast<const f32x4*>(sW2 + (cA + lr) * LK + kb + 4 * lg);
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                akk[0] = mfma4(x[q], y0[q], akk[0]);
-                akk[1] = mfma4(x[q], y1[q], akk[1]);
+            for (int q = 0; q < 4; ++q) akA = mfma4(x[q], y[q], akA);
+            if (two) {
+                const f32x4 xb = *reinterpret_cast<const f32x4*>(sXK + (rB + lr) * LK + kb + 4 * lg);
+                const f32x4 yb = *reinterpret_cast<const f32x4*>(sW2 + (cB + lr) * LK + kb + 4 * lg);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) akB = mfma4(xb[q], yb[q], akB);
             }
         }
 #pragma unroll 2
         for (int kb = 0; kb < DV; kb += 16) {
-            const f32x4 x = *reinterpret_cast<const f32x4*>(sXV + (t0 + lr) * LV + kb + 4 * lg);
-            const f32x4 y0 = *reinterpret_cast<const f32x4*>(sU + (sb + lr) * LV + kb + 4 * lg);
-            const f32x4 y1 = *reinterpret_cast<const f32x4*>(sU + (sb + 16 + lr) * LV + kb + 4 * lg);
+            const f32x4 x = *reinterpret_cast<const f32x4*>(sXV + (rA + lr) * LV + kb + 4 * lg);
+            const f32x4 y = *reinterpret_cast<const f32x4*>(sU + (cA + lr) * LV + kb + 4 * lg);
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                akk[0] = mfma4(x[q], y0[q], akk[0]);
-                akk[1] = mfma4(x[q], y1[q], akk[1]);
+            for (int q = 0; q < 4; ++q) akA = mfma4(x[q], y[q], akA);
+            if (two) {
+                const f32x4 xb = *reinterpret_cast<const f32x4*>(sXV + (rB + lr) * LV + kb + 4 * lg);
+                const f32x4 yb = *reinterpret_cast<const f32x4*>(sU + (cB + lr) * LV + kb + 4 * lg);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) akB = mfma4(xb[q], yb[q], akB);
             }
         }
         lds_barrier();   // everyone has read dX / W / U before dA_qk and K, Q, G land on them
+        const int codeZ = (int)((0xB7632100u >> (4 * wv)) & 15u), rZ = 16 * (codeZ >> 2), cZ = 16 * (codeZ & 3);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int r = 4 * lg + e, col = lr;
+            sAkk[(rA + r) * LA + cA + col] = cA + col < rA + r ? -akA[e] : 0.f;
+            if (two) sAkk[(rB + r) * LA + cB + col] = cB + col < rB + r ? -akB[e] : 0.f;
+            else sAkk[(rZ + r) * LA + cZ + col] = 0.f;
+        }
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int r = t0 + 4 * lg + e, col = sb + 16 * ct + lr;
-                sAkk[r * LA + col] = col < r ? -akk[ct][e] : 0.f;
                 ar[A::AQK + r * LA + col] = col <= r ? mqk[ct][e] : 0.f;
             }
     }
